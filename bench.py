@@ -1,0 +1,215 @@
+"""Benchmark: 35B-tier batch-1 decode through the full 40-layer MoE stack.
+
+One step = one decode token through all 40 layers (layer_step over [0, 40)):
+per layer the attention stand-in and RMSNorm, routing (own router on layers
+0-6 and 39, the previous token's prediction on 7-38), the int4 routed
+experts and the shared expert with its unmerged LoRA, the residual, and on
+layers 6-38 the prerouter head that predicts the next layer's routing for the
+next token. Weights are synthetic, seeded, and resident in HBM; inputs of all
+timed tokens are resident before the timed region starts.
+
+Prints one JSON line (rank 0) with tokens/s as `value`, layer-steps/s, the
+algorithmic HBM GB/s against the 8 TB/s peak, and the scalar fp64 oracle
+timed on the host cores as a CPU baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "35B-tier decode layer-steps/s & tokens/s at B=1; HBM GB/s as % of MI355X peak"
+
+
+def algorithmic_bytes(dm: dict, roles: list[dict]) -> dict:
+    """Weight bytes one decode token must read (activations, < 20 KB, ignored).
+
+    Routed: K experts x (gate + up + down) packed nibbles + fp16 scales.
+    Shared expert likewise, plus its LoRA A/B (fp16). Head: dense fc1/lin
+    columns over d, fc2, and only the 2K gathered one-hot columns of fc1 and
+    lin. Router: fp16 [E, d] on layers that run their own router.
+    """
+    d, E, K, I, Is, P, G, r = (dm[k] for k in ("d", "E", "K", "I", "Is", "P", "G", "r"))
+    expert = 3 * (I * d // 2) + 3 * 2 * (I * d // G)
+    shared = 3 * (Is * d // 2) + 3 * 2 * (Is * d // G)
+    lora = 2 * (r * d + Is * r) * 2 + (r * Is + d * r) * 2
+    head = 2 * (P * d + E * d + E * P) + 2 * (2 * K) * (P + E)
+    router = 2 * E * d
+    n_heads = sum(1 for x in roles if x["head"])
+    n_router = sum(1 for x in roles if x["router"])
+    L = len(roles)
+    parts = dict(routed=L * K * expert, shared=L * shared, lora=L * lora, heads=n_heads * head,
+                 routers=n_router * router)
+    parts["total"] = sum(parts.values())
+    return parts
+
+
+def cpu_baseline(tier: str, seed: int, roles, host_layers, toks, idx0, w0, n_tokens: int):
+    """The fp64 oracle (single thread) on the first tokens of the same workload."""
+    import oracle
+    from sparse_moe_decode_amd import synth
+    dm = synth.dims(tier)
+    L = len(roles)
+    los = [oracle.LayerOracle(dm, host_layers[l]) for l in range(L)]
+    pred_idx = {l: idx0[l] for l in range(L)}
+    pred_w = {l: w0[l].astype(np.float64) for l in range(L)}
+    prev = [None] * L
+    t0 = time.perf_counter()
+    for t in range(n_tokens):
+        h16 = toks[t]
+        new_pred = {}
+        for l in range(L):
+            out = los[l].step(h16, pred_idx[l], pred_w[l], prev[l])
+            prev[l] = out["exec_idx"].copy()
+            if roles[l]["head"] and l + 1 < L:
+                new_pred[l + 1] = (out["pred_idx"].copy(), out["pred_w"].copy())
+            h16 = out["h_out"].astype(np.float16)
+        for l, (pi, pw) in new_pred.items():
+            pred_idx[l], pred_w[l] = pi, pw
+    dt = time.perf_counter() - t0
+    return dict(value=n_tokens / dt, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"first {n_tokens} decode tokens of the same 40-layer workload "
+                       f"({n_tokens * L} layer-steps, single thread, {dt:.1f} s)")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--seed", type=int, default=3)
+    ap.add_argument("--rho", type=float, default=0.5)
+    ap.add_argument("--cpu-tokens", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_moe_decode_amd import api, synth
+    from sparse_moe_decode_amd import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    tier = "35b"
+    dm = synth.dims(tier)
+    roles = synth.stack_roles(tier)
+    L = len(roles)
+    T = args.warmup + args.steps
+
+    keep_host = not args.no_cpu_baseline
+    host_layers = {}
+    layers = []
+    t_build = time.perf_counter()
+    for l, role in enumerate(roles):
+        lw = synth.layer(args.seed, l, dm, role, zero_mean=True)
+        layers.append(dict(routed=wl.tree_to_dev(lw["routed"]), shared=wl.tree_to_dev(lw["shared"]),
+                           attn=wl.to_dev(lw["attn"]),
+                           router=None if lw["router"] is None else wl.to_dev(lw["router"]),
+                           router_bias=None, head=wl.tree_to_dev(lw["head"])))
+        if keep_host:
+            host_layers[l] = lw
+        print(f"[bench] layer {l + 1}/{L} resident", file=sys.stderr, flush=True)
+    t_build = time.perf_counter() - t_build
+
+    ctx = api.Context(dm, max_tokens=1)
+    model = api.Model(ctx, layers)
+    state = api.State(dm, L, head_logits=False)
+    idx0, w0 = wl.initial_routing(tier, args.seed, L)
+    state.route_idx[0].copy_(torch.from_numpy(idx0))
+    state.route_w[0].copy_(torch.from_numpy(w0))
+    toks = wl.token_inputs(tier, args.seed, T, args.rho)
+    h_all = torch.zeros((T, L + 1, dm["d"]), dtype=torch.float16, device="cuda")
+    h_all[:, 0].copy_(torch.from_numpy(toks))
+    exec_hist = torch.zeros((T, L, dm["K"]), dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    for t in range(args.warmup):
+        api.layer_step(ctx, model, 0, L, state, t, h_all[t], stream)
+        exec_hist[t].copy_(state.exec_idx[t & 1])
+    rc = api.device_status(ctx)
+    assert rc == 0, f"device status {rc}"
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for t in range(args.warmup, T):
+        api.layer_step(ctx, model, 0, L, state, t, h_all[t], stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    rc = api.device_status(ctx)
+    assert rc == 0, f"device status {rc}"
+
+    # Adjacent-token overlap of the executed sets on predicted layers (warmup tokens).
+    eh = exec_hist[: args.warmup].cpu().numpy()
+    cons = [l for l, r in enumerate(roles) if not r["router"]]
+    ov = [len(set(eh[t, l]) & set(eh[t - 1, l])) / dm["K"]
+          for t in range(1, args.warmup) for l in cons]
+    overlap = float(np.mean(ov)) if ov else None
+
+    ab = algorithmic_bytes(dm, roles)
+    gbs = ab["total"] / (ms * 1e-3) / 1e9
+    tok_s = 1000.0 / ms
+    cpu = None
+    if keep_host:
+        cpu = cpu_baseline(tier, args.seed, roles, host_layers, toks, idx0, w0, args.cpu_tokens)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tok_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 weights x fp16 activations, fp32 accumulate",
+        "data": "synthetic (seeded; random-init weights of the 35B-tier shapes)",
+        "config": {
+            "workload": "35B-tier full decode stack, batch 1: 40 MoE layers (d=2048, E=256, "
+                        "K=4, I=512, shared I=512 with LoRA r=16), prerouter heads on layers "
+                        "6-38, own fp16 router on layers 0-6 and 39, attention replaced by a "
+                        "fixed fp16 residual update",
+            "tokens_timed": args.steps, "layers": L, "batch": 1,
+            "weights_resident_GB": round(sum(
+                sum(v.numel() * v.element_size() for v in part.values())
+                if isinstance(part, dict) else 0
+                for lay in layers for part in lay.values()) / 1e9, 2),
+        },
+        "layer_steps_per_s": round(tok_s * L, 1),
+        "hbm_gb_per_s": round(gbs, 1),
+        "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes_per_token": ab["total"],
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "layer_step (one decode token, all 40 layers)",
+            "achieved": round(gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "adjacent_set_overlap": None if overlap is None else round(overlap, 3),
+        "cpu_baseline": cpu,
+        "build_s": round(t_build, 1),
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -445,10 +445,13 @@ struct orc_layer {
   int P;
 };
 
-int orc_layer_step(const orc_layer* L, const uint16_t* h16, const int32_t* route_idx,
-                   const float* route_w, const int32_t* prev_idx, double* h_out,
-                   uint16_t* x_out, int32_t* exec_idx, double* exec_w, double* router_logits,
-                   double* head_logits, int32_t* pred_idx, double* pred_w) {
+// x_in (nullable): an fp16 rounding of RMSNorm(h_attn) to use instead of the
+// oracle's own; x_out always receives the oracle's own rounding.
+int orc_layer_step(const orc_layer* L, const uint16_t* h16, const uint16_t* x_in,
+                   const int32_t* route_idx, const float* route_w, const int32_t* prev_idx,
+                   double* h_out, uint16_t* x_out, int32_t* exec_idx, double* exec_w,
+                   double* router_logits, double* head_logits, int32_t* pred_idx,
+                   double* pred_w) {
   const int d = L->moe.d, E = L->moe.E, K = L->moe.K;
   std::vector<double> ha(d), xn(d), x(d), y(d);
   for (int i = 0; i < d; ++i) ha[i] = f16_to_f64(h16[i]) + (L->attn ? f16_to_f64(L->attn[i]) : 0.0);
@@ -457,6 +460,8 @@ int orc_layer_step(const orc_layer* L, const uint16_t* h16, const int32_t* route
   for (int i = 0; i < d; ++i) x16[i] = f64_to_f16(xn[i]);
   if (x_out)
     for (int i = 0; i < d; ++i) x_out[i] = x16[i];
+  if (x_in)
+    for (int i = 0; i < d; ++i) x16[i] = x_in[i];
   for (int i = 0; i < d; ++i) x[i] = f16_to_f64(x16[i]);
   std::vector<double> w(K);
   if (L->router) {

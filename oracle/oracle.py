@@ -99,7 +99,7 @@ def _declare(lib):
     lib.orc_head_logits.restype = _i
     lib.orc_route.argtypes = [C.POINTER(OrcRouting), _p, _p, _p, _p]
     lib.orc_route.restype = _i
-    lib.orc_layer_step.argtypes = [C.POINTER(OrcLayer)] + [_p] * 12
+    lib.orc_layer_step.argtypes = [C.POINTER(OrcLayer)] + [_p] * 13
     lib.orc_layer_step.restype = _i
     lib.orc_slot_policy.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _p]
     lib.orc_slot_policy.restype = _i
@@ -356,9 +356,12 @@ class LayerOracle:
         self.has_head = head is not None
         self.has_router = layer.get("router") is not None
 
-    def step(self, h16, route_idx=None, route_w=None, prev_idx=None) -> dict:
+    def step(self, h16, route_idx=None, route_w=None, prev_idx=None, x16=None) -> dict:
+        """One layer-step. x16 (optional) replaces the oracle's own fp16 rounding of
+        the normed activation (out['x16'] is always the oracle's own)."""
         d, E, K = self.dims["d"], self.dims["E"], self.dims["K"]
         h16 = _u16(h16)
+        xin = _u16(x16)
         ri = _i32(route_idx) if route_idx is not None else np.zeros(K, np.int32)
         rw = _c(route_w, np.float32) if route_w is not None else np.zeros(K, np.float32)
         pv = _i32(prev_idx)
@@ -366,7 +369,8 @@ class LayerOracle:
                    exec_idx=np.empty(K, np.int32), exec_w=np.empty(K, np.float64),
                    router_logits=np.full(E, np.nan), head_logits=np.full(E, np.nan),
                    pred_idx=np.full(K, -1, np.int32), pred_w=np.full(K, np.nan))
-        rc = load().orc_layer_step(C.byref(self.L), _ptr(h16), _ptr(ri), _ptr(rw), _ptr(pv),
+        rc = load().orc_layer_step(C.byref(self.L), _ptr(h16), _ptr(xin), _ptr(ri), _ptr(rw),
+                                   _ptr(pv),
                                    _ptr(out["h_out"]), _ptr(out["x16"]), _ptr(out["exec_idx"]),
                                    _ptr(out["exec_w"]), _ptr(out["router_logits"]),
                                    _ptr(out["head_logits"]), _ptr(out["pred_idx"]),

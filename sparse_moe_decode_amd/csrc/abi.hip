@@ -1,0 +1,526 @@
+// C-ABI entry points: argument validation, device scratch, and the launch
+// sequences of the decode step. Declarations and documentation are in
+// include/sparse_moe_decode.h.
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+namespace smd {
+bool q4_shape_ok(int cols);
+}  // namespace smd
+
+using namespace smd;
+
+namespace {
+
+thread_local std::string g_err = "no error";
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(E0_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+struct e0_ctx {
+  e0_spec spec;
+  Dims dm;
+  int device;
+  Scratch s;
+  void* block;
+};
+
+struct e0_model {
+  e0_ctx* ctx;
+  std::vector<e0_layer> layers;
+  void* dev_table;  // device copy of the layer table (persistent kernel)
+};
+
+extern "C" {
+
+const char* e0_last_error(void) { return g_err.c_str(); }
+
+int e0_create(const e0_spec* spec, int32_t max_tokens, e0_ctx** out) {
+  if (!spec || !out) return fail(E0_ERR_ARG, "e0_create: null argument");
+  *out = nullptr;
+  const e0_spec& p = *spec;
+  if (p.d_model <= 0 || p.n_experts <= 0 || p.top_k < 1 || p.top_k > 8 ||
+      p.top_k > p.n_experts || p.inter <= 0 || p.group <= 0 || max_tokens < 1 ||
+      max_tokens > 256)
+    return fail(E0_ERR_ARG, "e0_create: bad dimensions");
+  if (p.group % 32 || p.d_model % p.group || p.inter % p.group)
+    return fail(E0_ERR_SHAPE, "e0_create: group %d must be a multiple of 32 dividing d and I",
+                p.group);
+  if (!q4_shape_ok(p.d_model) || !q4_shape_ok(p.inter))
+    return fail(E0_ERR_SHAPE, "e0_create: d=%d or I=%d not supported by the int4 kernels",
+                p.d_model, p.inter);
+  if (p.shared_inter != 0 && p.shared_inter != p.inter)
+    return fail(E0_ERR_SHAPE, "e0_create: shared_inter must be 0 or equal to inter");
+  if (p.lora_rank < 0 || p.lora_rank > 64) return fail(E0_ERR_SHAPE, "e0_create: rank > 64");
+  if (p.n_experts > 512) return fail(E0_ERR_SHAPE, "e0_create: more than 512 experts");
+  if (p.head_hidden < 0 || p.head_hidden % 8 || (p.d_model + 2 * p.n_experts) % 8)
+    return fail(E0_ERR_SHAPE, "e0_create: head dims must be multiples of 8");
+  if (p.router_kind == E0_ROUTER_SIGMOID_GROUP) {
+    if (p.n_groups < 1 || p.n_groups > 64 || p.n_experts % p.n_groups ||
+        p.n_experts / p.n_groups < 2 || p.topk_groups < 1 || p.topk_groups > p.n_groups ||
+        p.top_k > p.topk_groups * (p.n_experts / p.n_groups))
+      return fail(E0_ERR_SHAPE, "e0_create: bad sigmoid-group parameters");
+  } else if (p.router_kind != E0_ROUTER_SOFTMAX_TOPK) {
+    return fail(E0_ERR_ARG, "e0_create: unknown router kind");
+  }
+  e0_ctx* c = new e0_ctx();
+  c->spec = p;
+  Dims& dm = c->dm;
+  dm.d = p.d_model; dm.E = p.n_experts; dm.K = p.top_k; dm.I = p.inter; dm.Is = p.shared_inter;
+  dm.P = p.head_hidden; dm.G = p.group; dm.r = p.lora_rank;
+  dm.lora_scale = p.lora_rank > 0 ? p.lora_alpha / (float)p.lora_rank : 0.0f;
+  dm.router_kind = p.router_kind; dm.norm_topk = p.norm_topk; dm.n_groups = p.n_groups;
+  dm.topk_groups = p.topk_groups; dm.route_scale = p.route_scale;
+  dm.eps = p.rms_eps > 0 ? p.rms_eps : 1e-6f;
+  hipGetDevice(&c->device);
+
+  const int B = max_tokens;
+  const int imax = dm.I > dm.Is ? dm.I : dm.Is;
+  const int rmax = dm.r > 1 ? dm.r : 1;
+  const size_t n_gu = (size_t)B * (dm.K + 1) * imax;
+  const size_t n_ax = (size_t)B * 3 * rmax;
+  const size_t n_d = (size_t)B * dm.d;
+  const size_t n_p = (size_t)B * (dm.P > 0 ? dm.P : 1);
+  const size_t n_e = (size_t)B * dm.E;
+  auto up = [](size_t bytes) { return (bytes + 255) & ~(size_t)255; };
+  const size_t bytes = up(n_gu * 4) + up(n_ax * 4) + up(n_d * 4) + up(n_d * 2) + up(n_p * 4) +
+                       2 * up(n_e * 4) + 2 * up((size_t)B * dm.K * 4) + up(N_FLAGS * 4);
+  hipError_t e = hipMalloc(&c->block, bytes);
+  if (e != hipSuccess) {
+    delete c;
+    return hip_fail(e, "e0_create: hipMalloc");
+  }
+  hipMemset(c->block, 0, bytes);
+  char* q = (char*)c->block;
+  Scratch& s = c->s;
+  s.max_tokens = B;
+  s.gu = (float*)q; q += up(n_gu * 4);
+  s.ax = (float*)q; q += up(n_ax * 4);
+  s.hattn = (float*)q; q += up(n_d * 4);
+  s.xn = (uint16_t*)q; q += up(n_d * 2);
+  s.hact = (float*)q; q += up(n_p * 4);
+  s.hlin = (float*)q; q += up(n_e * 4);
+  s.logits = (float*)q; q += up(n_e * 4);
+  s.sink_idx = (int32_t*)q; q += up((size_t)B * dm.K * 4);
+  s.sink_w = (float*)q; q += up((size_t)B * dm.K * 4);
+  s.flags = (int32_t*)q;
+  *out = c;
+  return E0_OK;
+}
+
+void e0_destroy(e0_ctx* ctx) {
+  if (!ctx) return;
+  hipFree(ctx->block);
+  delete ctx;
+}
+
+int e0_device_status(e0_ctx* ctx, void* stream) {
+  if (!ctx) return fail(E0_ERR_ARG, "e0_device_status: null ctx");
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "e0_device_status: sync");
+  int32_t flags[N_FLAGS];
+  e = hipMemcpy(flags, ctx->s.flags, sizeof(flags), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "e0_device_status: copy");
+  e = hipMemset(ctx->s.flags, 0, sizeof(flags));
+  if (e != hipSuccess) return hip_fail(e, "e0_device_status: clear");
+  if (flags[FLAG_SYNC]) return fail(E0_ERR_SYNC, "a device-side wait hit its spin limit");
+  if (flags[FLAG_RANGE]) return fail(E0_ERR_RANGE, "an expert id or slot was out of range");
+  return E0_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+int check_q4(const e0_q4& m, const char* what) {
+  if (!m.q || !m.s) return fail(E0_ERR_ARG, "%s: null int4 matrix", what);
+  if (!aligned(m.q, 16) || !aligned(m.s, 2))
+    return fail(E0_ERR_ALIGN, "%s: packed words must be 16-byte aligned", what);
+  return E0_OK;
+}
+
+int make_pool(const e0_ctx* ctx, const e0_experts* ex, const int32_t* slot_of, Pool& p) {
+  if (!ex) return fail(E0_ERR_ARG, "routed pool is null");
+  int rc;
+  if ((rc = check_q4(ex->gate, "routed gate")) || (rc = check_q4(ex->up, "routed up")) ||
+      (rc = check_q4(ex->down, "routed down")))
+    return rc;
+  const Dims& dm = ctx->dm;
+  p.gate = {ex->gate.q, ex->gate.s};
+  p.up = {ex->up.q, ex->up.s};
+  p.down = {ex->down.q, ex->down.s};
+  p.stride_q = ex->stride_q ? ex->stride_q : (int64_t)dm.I * dm.d / 2;
+  p.stride_s = ex->stride_s ? ex->stride_s : (int64_t)2 * dm.I * (dm.d / dm.G);
+  if (p.stride_q % 16 || p.stride_s % 2) return fail(E0_ERR_ALIGN, "pool strides misaligned");
+  p.count = ex->count;
+  if (p.count < 1) return fail(E0_ERR_ARG, "routed pool count must be >= 1");
+  p.slot_of = slot_of;
+  return E0_OK;
+}
+
+int make_shared(const e0_ctx* ctx, const e0_shared* sh, SharedW& w) {
+  std::memset(&w, 0, sizeof(w));
+  if (!sh) return E0_OK;
+  if (ctx->dm.Is == 0) return fail(E0_ERR_ARG, "shared expert given but shared_inter = 0");
+  int rc;
+  if ((rc = check_q4(sh->gate, "shared gate")) || (rc = check_q4(sh->up, "shared up")) ||
+      (rc = check_q4(sh->down, "shared down")))
+    return rc;
+  w.gate = {sh->gate.q, sh->gate.s};
+  w.up = {sh->up.q, sh->up.s};
+  w.down = {sh->down.q, sh->down.s};
+  const bool lg = sh->lgate.a && sh->lgate.b, lu = sh->lup.a && sh->lup.b,
+             ld = sh->ldown.a && sh->ldown.b;
+  if ((lg || lu || ld) && ctx->dm.r == 0) return fail(E0_ERR_ARG, "LoRA given but rank = 0");
+  if (lg != lu) return fail(E0_ERR_ARG, "gate and up LoRA must be given together");
+  for (const uint16_t* a : {sh->lgate.a, sh->lup.a, sh->ldown.a})
+    if (a && !aligned(a, 16)) return fail(E0_ERR_ALIGN, "LoRA A must be 16-byte aligned");
+  if (lg) { w.ag = sh->lgate.a; w.bg = sh->lgate.b; w.au = sh->lup.a; w.bu = sh->lup.b; }
+  if (ld) { w.ad = sh->ldown.a; w.bd = sh->ldown.b; }
+  w.present = 1;
+  return E0_OK;
+}
+
+// Shared-expert LoRA A products for the gate/up (input x fp16).
+hipError_t lora_a_x(const e0_ctx* ctx, const SharedW& sh, const uint16_t* x, int B,
+                    hipStream_t st) {
+  if (!sh.present || !sh.ag) return hipSuccess;
+  const int rmax = ctx->dm.r > 1 ? ctx->dm.r : 1;
+  const uint16_t* A[2] = {sh.ag, sh.au};
+  const int slots[2] = {0, rmax};
+  return launch_lora_a(2, A, slots, ctx->dm.d, ctx->dm.r, x, nullptr, ctx->dm.d, B, ctx->s.ax,
+                       3 * rmax, st);
+}
+
+// Down LoRA A product on the shared expert's fp32 SwiGLU output.
+hipError_t lora_a_down(const e0_ctx* ctx, const SharedW& sh, int B, hipStream_t st) {
+  if (!sh.present || !sh.ad) return hipSuccess;
+  const Dims& dm = ctx->dm;
+  const int rmax = dm.r > 1 ? dm.r : 1;
+  const int imax = dm.I > dm.Is ? dm.I : dm.Is;
+  const uint16_t* A[1] = {sh.ad};
+  const int slots[1] = {2 * rmax};
+  return launch_lora_a(1, A, slots, dm.Is, dm.r, nullptr, ctx->s.gu + (int64_t)dm.K * imax,
+                       (int64_t)(dm.K + 1) * imax, B, ctx->s.ax, 3 * rmax, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_int4_decode(e0_ctx* ctx, const e0_experts* routed, const int32_t* slot_of,
+                    const e0_shared* shared, const uint16_t* x, const int32_t* idx,
+                    const float* w, int32_t n_tokens, uint16_t* y, void* stream) {
+  if (!ctx || !x || !idx || !w || !y) return fail(E0_ERR_ARG, "moe_int4_decode: null argument");
+  if (n_tokens == 0) return E0_OK;
+  if (n_tokens < 0 || n_tokens > ctx->s.max_tokens)
+    return fail(E0_ERR_ARG, "moe_int4_decode: n_tokens %d outside [0, %d]", n_tokens,
+                ctx->s.max_tokens);
+  Pool pool;
+  SharedW sh;
+  int rc;
+  if ((rc = make_pool(ctx, routed, slot_of, pool)) || (rc = make_shared(ctx, shared, sh)))
+    return rc;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if ((e = lora_a_x(ctx, sh, x, n_tokens, st)) != hipSuccess) return hip_fail(e, "lora A");
+  if ((e = launch_gate_up(ctx->dm, pool, sh, x, idx, n_tokens, ctx->s, st)) != hipSuccess)
+    return hip_fail(e, "gate/up");
+  if ((e = lora_a_down(ctx, sh, n_tokens, st)) != hipSuccess) return hip_fail(e, "lora A down");
+  if ((e = launch_down(ctx->dm, pool, sh, idx, w, n_tokens, nullptr, y, ctx->s, st)) !=
+      hipSuccess)
+    return hip_fail(e, "down");
+  return E0_OK;
+}
+
+int lora_delta(e0_ctx* ctx, const uint16_t* A, const uint16_t* Bm, int32_t in_dim,
+               int32_t out_dim, int32_t rank, float scale, const uint16_t* x, float* y_acc,
+               int32_t n_tokens, void* stream) {
+  if (!ctx || !A || !Bm || !x || !y_acc) return fail(E0_ERR_ARG, "lora_delta: null argument");
+  if (n_tokens == 0) return E0_OK;
+  if (n_tokens < 0 || n_tokens > ctx->s.max_tokens)
+    return fail(E0_ERR_ARG, "lora_delta: n_tokens out of range");
+  if (rank < 1 || rank > 64 || in_dim < 8 || in_dim % 8 || out_dim < 1)
+    return fail(E0_ERR_SHAPE, "lora_delta: rank in [1, 64], in_dim a multiple of 8");
+  if (!aligned(A, 16) || !aligned(x, 16))
+    return fail(E0_ERR_ALIGN, "lora_delta: A and x must be 16-byte aligned");
+  const int rmax = ctx->dm.r > 1 ? ctx->dm.r : 1;
+  if (rank > 3 * rmax) return fail(E0_ERR_SHAPE, "lora_delta: rank larger than the context's");
+  hipStream_t st = (hipStream_t)stream;
+  const int slots[1] = {0};
+  hipError_t e = launch_lora_a(1, &A, slots, in_dim, rank, x, nullptr, in_dim, n_tokens,
+                               ctx->s.ax, 3 * rmax, st);
+  if (e != hipSuccess) return hip_fail(e, "lora_delta A");
+  e = launch_lora_b(Bm, out_dim, rank, scale, ctx->s.ax, 3 * rmax, y_acc, n_tokens, st);
+  if (e != hipSuccess) return hip_fail(e, "lora_delta B");
+  return E0_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+int check_head(const e0_ctx* ctx, const e0_head* hd) {
+  if (!hd || !hd->fc1 || !hd->fc2 || !hd->lin) return fail(E0_ERR_ARG, "head: null weights");
+  if (ctx->dm.P <= 0) return fail(E0_ERR_SHAPE, "head: head_hidden is 0");
+  if (!aligned(hd->fc1, 16) || !aligned(hd->fc2, 16) || !aligned(hd->lin, 16))
+    return fail(E0_ERR_ALIGN, "head: weights must be 16-byte aligned");
+  return E0_OK;
+}
+
+// fc1 (+GELU) and lin on [x; onehot(cur); onehot(prev)], then fc2 + lin,
+// then routing. logits_out may alias the scratch logits.
+hipError_t head_launch(const e0_ctx* ctx, const e0_head* hd, const uint16_t* x,
+                       const int32_t* cur, const int32_t* prev, int B, float* logits_out,
+                       int32_t* out_idx, float* out_w, hipStream_t st) {
+  const Dims& dm = ctx->dm;
+  const Scratch& s = ctx->s;
+  const int64_t F = (int64_t)dm.d + 2 * dm.E;
+  hipError_t e = launch_gemv16(hd->fc1, dm.P, dm.d, F, x, nullptr, dm.d, B, cur, prev, dm.K,
+                               dm.E, dm.d, 1, nullptr, s.hact, dm.P, st);
+  if (e != hipSuccess) return e;
+  e = launch_gemv16(hd->lin, dm.E, dm.d, F, x, nullptr, dm.d, B, cur, prev, dm.K, dm.E, dm.d, 0,
+                    nullptr, s.hlin, dm.E, st);
+  if (e != hipSuccess) return e;
+  float* lg = logits_out ? logits_out : s.logits;
+  e = launch_gemv16(hd->fc2, dm.E, dm.P, dm.P, nullptr, s.hact, dm.P, B, nullptr, nullptr, 0,
+                    0, 0, 2, s.hlin, lg, dm.E, st);
+  if (e != hipSuccess) return e;
+  return launch_route(dm, lg, hd->bias, B, out_idx, out_w, s.flags, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int prerouter_forward(e0_ctx* ctx, const e0_head* head, const uint16_t* x,
+                      const int32_t* cur_idx, const int32_t* prev_idx, int32_t n_tokens,
+                      float* logits, int32_t* out_idx, float* out_w, void* stream) {
+  if (!ctx || !x || !cur_idx || !out_idx || !out_w)
+    return fail(E0_ERR_ARG, "prerouter_forward: null argument");
+  int rc = check_head(ctx, head);
+  if (rc) return rc;
+  if (n_tokens == 0) return E0_OK;
+  if (n_tokens < 0 || n_tokens > ctx->s.max_tokens)
+    return fail(E0_ERR_ARG, "prerouter_forward: n_tokens out of range");
+  if (!aligned(x, 16)) return fail(E0_ERR_ALIGN, "prerouter_forward: x must be 16-byte aligned");
+  hipError_t e = head_launch(ctx, head, x, cur_idx, prev_idx, n_tokens, logits, out_idx, out_w,
+                             (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "prerouter_forward");
+  return E0_OK;
+}
+
+int e0_model_create(e0_ctx* ctx, const e0_layer* layers, int32_t n_layers, e0_model** out) {
+  if (!ctx || !layers || !out || n_layers < 1)
+    return fail(E0_ERR_ARG, "e0_model_create: bad argument");
+  *out = nullptr;
+  for (int l = 0; l < n_layers; ++l) {
+    const e0_layer& L = layers[l];
+    Pool p;
+    SharedW sw;
+    int rc;
+    if ((rc = make_pool(ctx, &L.experts, L.slot_of, p)) ||
+        (rc = make_shared(ctx, L.shared.gate.q ? &L.shared : nullptr, sw)))
+      return fail(rc, "layer %d: %s", l, g_err.c_str());
+    if (L.head.fc1 && (rc = check_head(ctx, &L.head)))
+      return fail(rc, "layer %d: %s", l, g_err.c_str());
+    if (L.router && !aligned(L.router, 16))
+      return fail(E0_ERR_ALIGN, "layer %d: router must be 16-byte aligned", l);
+  }
+  e0_model* m = new e0_model();
+  m->ctx = ctx;
+  m->layers.assign(layers, layers + n_layers);
+  m->dev_table = nullptr;
+  *out = m;
+  return E0_OK;
+}
+
+void e0_model_destroy(e0_model* model) {
+  if (!model) return;
+  if (model->dev_table) hipFree(model->dev_table);
+  delete model;
+}
+
+int layer_step(e0_ctx* ctx, e0_model* model, int32_t layer_begin, int32_t layer_end,
+               const e0_state* state, int32_t token, uint16_t* h, void* stream) {
+  if (!ctx || !model || !state || !h) return fail(E0_ERR_ARG, "layer_step: null argument");
+  const int L = (int)model->layers.size();
+  if (layer_begin < 0 || layer_end > L || layer_begin >= layer_end || token < 0)
+    return fail(E0_ERR_ARG, "layer_step: bad layer range or token");
+  if (!state->route_idx || !state->route_w || !state->exec_idx || !state->exec_w)
+    return fail(E0_ERR_ARG, "layer_step: state buffers are null");
+  if (!aligned(h, 16) || (ctx->dm.d * 2) % 16)
+    return fail(E0_ERR_ALIGN, "layer_step: h must be 16-byte aligned");
+  const Dims& dm = ctx->dm;
+  const Scratch& s = ctx->s;
+  hipStream_t st = (hipStream_t)stream;
+  const int K = dm.K;
+  const int cur = token & 1, nxt = (token + 1) & 1;
+  for (int l = layer_begin; l < layer_end; ++l) {
+    const e0_layer& Ly = model->layers[l];
+    Pool pool;
+    SharedW sh;
+    make_pool(ctx, &Ly.experts, Ly.slot_of, pool);
+    make_shared(ctx, Ly.shared.gate.q ? &Ly.shared : nullptr, sh);
+    const uint16_t* hin = h + (int64_t)(l - layer_begin) * dm.d;
+    uint16_t* hout = h + (int64_t)(l - layer_begin + 1) * dm.d;
+    int32_t* eidx = state->exec_idx + ((int64_t)cur * L + l) * K;
+    float* ew = state->exec_w + ((int64_t)cur * L + l) * K;
+    const int32_t* ridx = state->route_idx + ((int64_t)cur * L + l) * K;
+    const float* rw = state->route_w + ((int64_t)cur * L + l) * K;
+    hipError_t e;
+    const bool routed_here = Ly.router != nullptr;
+    uint16_t* xn = state->x_trace ? state->x_trace + (int64_t)l * dm.d : s.xn;
+    e = launch_prep(dm, hin, Ly.attn, 1, s.hattn, xn, routed_here ? nullptr : ridx,
+                    routed_here ? nullptr : rw, eidx, ew, st);
+    if (e != hipSuccess) return hip_fail(e, "layer_step prep");
+    if (routed_here) {
+      e = launch_gemv16(Ly.router, dm.E, dm.d, dm.d, xn, nullptr, dm.d, 1, nullptr, nullptr,
+                        0, 0, 0, 0, nullptr, s.logits, dm.E, st);
+      if (e == hipSuccess) e = launch_route(dm, s.logits, Ly.router_bias, 1, eidx, ew, s.flags, st);
+      if (e != hipSuccess) return hip_fail(e, "layer_step router");
+    }
+    if ((e = lora_a_x(ctx, sh, xn, 1, st)) != hipSuccess) return hip_fail(e, "lora A");
+    if ((e = launch_gate_up(dm, pool, sh, xn, eidx, 1, s, st)) != hipSuccess)
+      return hip_fail(e, "gate/up");
+    if ((e = lora_a_down(ctx, sh, 1, st)) != hipSuccess) return hip_fail(e, "lora A down");
+    if ((e = launch_down(dm, pool, sh, eidx, ew, 1, s.hattn, hout, s, st)) != hipSuccess)
+      return hip_fail(e, "down");
+    if (Ly.head.fc1) {
+      const int32_t* prev = token > 0 ? state->exec_idx + ((int64_t)nxt * L + l) * K : nullptr;
+      float* lg = state->head_logits ? state->head_logits + (int64_t)l * dm.E : nullptr;
+      int32_t* pidx;
+      float* pw;
+      if (l + 1 < L) {
+        pidx = state->route_idx + ((int64_t)nxt * L + l + 1) * K;
+        pw = state->route_w + ((int64_t)nxt * L + l + 1) * K;
+      } else {
+        // The last layer's head has no consumer; its routing goes to a sink.
+        pidx = s.sink_idx;
+        pw = s.sink_w;
+      }
+      e = head_launch(ctx, &Ly.head, xn, eidx, prev, 1, lg, pidx, pw, st);
+      if (e != hipSuccess) return hip_fail(e, "layer_step head");
+    }
+  }
+  return E0_OK;
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------- staging --
+
+struct e0_stager {
+  e0_ctx* ctx;
+  const char* host_dev;  // device-side address of the pinned host pool
+  int32_t L, n_slots;
+  char* hbm;
+  int32_t* slot_of;
+  int32_t* slot_expert;
+  int64_t bundle;
+  int32_t* copy_list;  // [L][2*8]
+  int32_t* n_copies;   // [L]
+};
+
+extern "C" {
+
+int64_t e0_bundle_bytes(const e0_spec* spec) {
+  if (!spec || spec->group <= 0) return -1;
+  const int64_t Id = (int64_t)spec->inter * spec->d_model;
+  return 3 * (Id / 2) + 3 * 2 * (Id / spec->group);
+}
+
+int e0_stager_create(e0_ctx* ctx, const void* host_pool, int32_t n_layers, int32_t n_slots,
+                     void* hbm_slots, int32_t* slot_of, int32_t* slot_expert,
+                     e0_stager** out) {
+  if (!ctx || !host_pool || !hbm_slots || !slot_of || !slot_expert || !out)
+    return fail(E0_ERR_ARG, "e0_stager_create: null argument");
+  *out = nullptr;
+  const Dims& dm = ctx->dm;
+  if (n_layers < 1 || n_slots < 2 * dm.K || n_slots > 64)
+    return fail(E0_ERR_ARG, "e0_stager_create: need 2K <= n_slots <= 64 and n_layers >= 1");
+  if (!aligned(host_pool, 16) || !aligned(hbm_slots, 16))
+    return fail(E0_ERR_ALIGN, "e0_stager_create: pools must be 16-byte aligned");
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, host_pool);
+  if (e != hipSuccess || attr.type != hipMemoryTypeHost) {
+    (void)hipGetLastError();
+    return fail(E0_ERR_ARG, "e0_stager_create: host pool is not pinned host memory");
+  }
+  void* dev = nullptr;
+  e = hipHostGetDevicePointer(&dev, const_cast<void*>(host_pool), 0);
+  if (e != hipSuccess || !dev) return hip_fail(e, "e0_stager_create: device address of pool");
+  e0_stager* s = new e0_stager();
+  s->ctx = ctx;
+  s->host_dev = (const char*)dev;
+  s->L = n_layers;
+  s->n_slots = n_slots;
+  s->hbm = (char*)hbm_slots;
+  s->slot_of = slot_of;
+  s->slot_expert = slot_expert;
+  s->bundle = e0_bundle_bytes(&ctx->spec);
+  e = hipMalloc(&s->copy_list, (size_t)n_layers * 16 * sizeof(int32_t));
+  if (e == hipSuccess) e = hipMalloc(&s->n_copies, (size_t)n_layers * sizeof(int32_t));
+  if (e == hipSuccess) e = hipMemset(slot_of, 0xFF, (size_t)n_layers * dm.E * sizeof(int32_t));
+  if (e == hipSuccess)
+    e = hipMemset(slot_expert, 0xFF, (size_t)n_layers * n_slots * sizeof(int32_t));
+  if (e == hipSuccess) e = hipMemset(s->n_copies, 0, (size_t)n_layers * sizeof(int32_t));
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    e0_stager_destroy(s);
+    return hip_fail(e, "e0_stager_create");
+  }
+  *out = s;
+  return E0_OK;
+}
+
+void e0_stager_destroy(e0_stager* st) {
+  if (!st) return;
+  if (st->copy_list) hipFree(st->copy_list);
+  if (st->n_copies) hipFree(st->n_copies);
+  delete st;
+}
+
+int stage_experts(e0_stager* st, int32_t layer, const int32_t* new_idx,
+                  const int32_t* in_use_idx, void* side_stream, void* done_event) {
+  if (!st || !new_idx) return fail(E0_ERR_ARG, "stage_experts: null argument");
+  if (layer < 0 || layer >= st->L) return fail(E0_ERR_ARG, "stage_experts: bad layer");
+  const Dims& dm = st->ctx->dm;
+  hipStream_t ss = (hipStream_t)side_stream;
+  hipError_t e = launch_stage(
+      dm.E, st->n_slots, dm.K, st->slot_of + (int64_t)layer * dm.E,
+      st->slot_expert + (int64_t)layer * st->n_slots, in_use_idx, new_idx,
+      st->copy_list + (int64_t)layer * 16, st->n_copies + layer,
+      st->host_dev + (int64_t)layer * dm.E * st->bundle,
+      st->hbm + (int64_t)layer * st->n_slots * st->bundle, st->bundle, st->ctx->s.flags, ss);
+  if (e != hipSuccess) return hip_fail(e, "stage_experts");
+  if (done_event) {
+    e = hipEventRecord((hipEvent_t)done_event, ss);
+    if (e != hipSuccess) return hip_fail(e, "stage_experts: event");
+  }
+  return E0_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,121 @@
+// Device helpers for gfx950 (CDNA4, wave64): fp16 conversion, int4 dot
+// products with in-register dequantisation, lane-group reductions, top-K.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smd {
+
+typedef _Float16 f16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(f16, b); }
+// fp32 -> fp16, round-to-nearest-even (the hardware default rounding mode).
+__device__ __forceinline__ uint16_t f2h(float v) { return __builtin_bit_cast(uint16_t, (f16)v); }
+
+__device__ __forceinline__ f16x2 as_h2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
+
+__device__ __forceinline__ float dot2(f16x2 a, f16x2 b, float c) {
+  return __builtin_amdgcn_fdot2(a, b, c, false);
+}
+
+// Eight int4 weights of one packed word against eight activations.
+//
+// The word holds two's-complement nibbles n_0..n_7 (n_j at bits 4j). XOR with
+// 0x8 per nibble gives the offset-binary u_j = q_j + 8 in [0, 15]. OR-ing a
+// nibble into the mantissa of fp16 1024.0 (0x6400) yields 1024 + u exactly;
+// nibbles sitting 4 bits higher yield 1024 + 16u. One packed fp16 subtract
+// (or multiply-add by 1/16) then gives q exactly, two values per register:
+//   p0 = (q0, q4)   p1 = (q1, q5)   p2 = (q2, q6)   p3 = (q3, q7)
+// so the activations must be supplied pair-permuted as
+//   xp[0] = (x0, x4)  xp[1] = (x1, x5)  xp[2] = (x2, x6)  xp[3] = (x3, x7).
+// q and x are exact in fp16; v_dot2_f32_f16 accumulates the products in fp32.
+__device__ __forceinline__ float q4_dot8(uint32_t w, const f16x2* xp, float acc) {
+  const uint32_t u = w ^ 0x88888888u;
+  const uint32_t v = u >> 8;
+  const f16x2 k1032 = {(f16)1032.0f, (f16)1032.0f};
+  const f16x2 k16 = {(f16)0.0625f, (f16)0.0625f};
+  const f16x2 k72 = {(f16)72.0f, (f16)72.0f};
+  f16x2 p0 = as_h2((u & 0x000F000Fu) | 0x64006400u) - k1032;
+  f16x2 p1 = as_h2((u & 0x00F000F0u) | 0x64006400u) * k16 - k72;
+  f16x2 p2 = as_h2((v & 0x000F000Fu) | 0x64006400u) - k1032;
+  f16x2 p3 = as_h2((v & 0x00F000F0u) | 0x64006400u) * k16 - k72;
+  acc = dot2(p0, xp[0], acc);
+  acc = dot2(p1, xp[1], acc);
+  acc = dot2(p2, xp[2], acc);
+  acc = dot2(p3, xp[3], acc);
+  return acc;
+}
+
+// Position of element i inside its 8-element block after the pair
+// permutation q4_dot8 expects: [x0 x4 x1 x5 x2 x6 x3 x7].
+__device__ __forceinline__ int perm8(int i) {
+  int j = i & 7;
+  return (i & ~7) | (j < 4 ? 2 * j : 2 * (j - 4) + 1);
+}
+
+// DPP lane moves within a 16-lane row (bound_ctrl off, all lanes active).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of LG lanes (LG in {1, 2, 4, 8, 16}); every lane of
+// the group receives the group sum. quad_perm swaps, then half-row and row
+// mirrors, so partner lanes never leave the group.
+template <int LG>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (LG >= 2) v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  if constexpr (LG >= 4) v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  if constexpr (LG >= 8) v += dpp_f<0x141>(v);  // row_half_mirror
+  if constexpr (LG >= 16) v += dpp_f<0x140>(v); // row_mirror
+  return v;
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+__device__ __forceinline__ float gelu_erf(float z) {
+  return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
+}
+
+// Order-preserving map of fp32 to uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t f2key(float v) {
+  uint32_t b = __builtin_bit_cast(uint32_t, v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Wave-wide maximum of a 64-bit key (xor butterfly over the 64 lanes).
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t lo = __shfl_xor((uint32_t)k, off);
+    uint32_t hi = __shfl_xor((uint32_t)(k >> 32), off);
+    uint64_t o = ((uint64_t)hi << 32) | lo;
+    k = o > k ? o : k;
+  }
+  return k;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+// Split an fp32 vector value into fp16 hi + lo after scaling by 2^-e, so that
+// dot products against fp16 weights keep ~22 bits of the activation:
+// x * 2^-e = hi + lo + O(2^-22 |x|).
+__device__ __forceinline__ void split_hilo(float v, float inv_scale, f16& hi, f16& lo) {
+  float t = v * inv_scale;
+  hi = (f16)t;
+  lo = (f16)(t - (float)hi);
+}
+
+}  // namespace smd

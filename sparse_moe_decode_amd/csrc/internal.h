@@ -1,0 +1,109 @@
+// Internal types shared by the HIP kernels and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/sparse_moe_decode.h"
+
+namespace smd {
+
+// Device view of one int4 matrix.
+struct Q4 {
+  const uint32_t* q;
+  const uint16_t* s;
+};
+
+// Device view of a routed pool: entry j of projection p sits at
+// p.q + j*stride_q bytes (scales p.s + j*stride_s). Expert ids map to
+// entries directly, or through slot_of when it is set.
+struct Pool {
+  Q4 gate, up, down;
+  int64_t stride_q, stride_s;
+  int32_t count;
+  const int32_t* slot_of;
+};
+
+struct SharedW {
+  Q4 gate, up, down;
+  const uint16_t *ag, *bg, *au, *bu, *ad, *bd;  // LoRA A/B per projection, nullable
+  int32_t present;
+};
+
+struct HeadW {
+  const uint16_t *fc1, *fc2, *lin;
+  const float* bias;
+};
+
+// Tier dimensions as the kernels use them.
+struct Dims {
+  int32_t d, E, K, I, Is, P, G, r;
+  float lora_scale;  // alpha / r
+  int32_t router_kind, norm_topk, n_groups, topk_groups;
+  float route_scale, eps;
+};
+
+// Flags the kernels raise (device int32 array).
+enum { FLAG_RANGE = 0, FLAG_SYNC = 1, N_FLAGS = 4 };
+
+// Per-context device scratch, sized for max_tokens tokens.
+struct Scratch {
+  int32_t max_tokens;
+  float* gu;      // [B][K+1][Imax] SwiGLU outputs (routed experts, then shared)
+  float* ax;      // [B][3][rmax]   LoRA A products: gate, up, down
+  float* hattn;   // [B][d]         h + attention update (fp32)
+  uint16_t* xn;   // [B][d]         fp16 RMS-normed activation
+  float* hact;    // [B][P]         head hidden activation erf_gelu(fc1 f)
+  float* hlin;    // [B][E]         head linear path lin f
+  float* logits;  // [B][E]         router / head logits
+  int32_t* sink_idx;  // [B][K]     prediction with no consumer layer
+  float* sink_w;      // [B][K]
+  int32_t* flags; // [N_FLAGS]
+};
+
+// ---- launchers (kernels.hip) ------------------------------------------------
+// All return hipSuccess or the launch error; shapes are validated by callers.
+
+// SwiGLU gate/up for the K routed experts of each token (expert k reads
+// routing idx[b*K + k]) and, when sh.present, the shared expert (slot K).
+hipError_t launch_gate_up(const Dims& dm, const Pool& pool, const SharedW& sh,
+                          const uint16_t* x, const int32_t* idx, int B, const Scratch& s,
+                          hipStream_t st);
+// Down projections + weighted combine + shared expert + down LoRA.
+// Output y16[b][d] = fp16(resid[b][d] + y) (resid may be null).
+hipError_t launch_down(const Dims& dm, const Pool& pool, const SharedW& sh,
+                       const int32_t* idx, const float* w, int B, const float* resid,
+                       uint16_t* y16, const Scratch& s, hipStream_t st);
+// LoRA A products: ax[b][slot][t] = sum_i A[t][i] x[b][i] for up to 3 A's.
+// x is fp16 ([B][in], stride x_stride) or fp32 when xf32 != nullptr.
+hipError_t launch_lora_a(int n_mats, const uint16_t* const* A, const int* slots, int in_dim,
+                         int r, const uint16_t* x16, const float* xf32, int64_t x_stride,
+                         int B, float* ax, int ax_stride, hipStream_t st);
+// y_acc[b][o] += scale * sum_t Bm[o][t] ax[b][t]
+hipError_t launch_lora_b(const uint16_t* Bm, int out_dim, int r, float scale, const float* ax,
+                         int ax_stride, float* y_acc, int B, hipStream_t st);
+// Dense fp16 GEMV: y[b][o] = W[o, 0:cols] . x[b] (+ gathered one-hot columns
+// W[o, gcol0 + cur[b][k]] and W[o, gcol0 + E + prev[b][k]]) with epilogue:
+// epi 0 none, 1 erf-GELU, 2 add addv[b][o]. x is fp16, or fp32 if xf32.
+hipError_t launch_gemv16(const uint16_t* W, int rows, int cols, int64_t ld,
+                         const uint16_t* x16, const float* xf32, int64_t x_stride, int B,
+                         const int32_t* cur, const int32_t* prev, int K, int E, int gcol0,
+                         int epi, const float* addv, float* y, int64_t y_stride,
+                         hipStream_t st);
+// Routing of fp32 logits [B][E] with the tier's family -> idx/w [B][K].
+hipError_t launch_route(const Dims& dm, const float* logits, const float* bias, int B,
+                        int32_t* idx, float* w, int32_t* flags, hipStream_t st);
+// h_attn = h + attn, xn = fp16(RMSNorm(h_attn)); optionally copies a routing
+// (cidx/cw [B][K]) into exec (eidx/ew).
+hipError_t launch_prep(const Dims& dm, const uint16_t* h, const uint16_t* attn, int B,
+                       float* hattn, uint16_t* xn, const int32_t* cidx, const float* cw,
+                       int32_t* eidx, float* ew, hipStream_t st);
+
+// Staging: device-side slot policy for one layer, then a gather-copy of the
+// missing bundles from (device-mapped) pinned host memory into HBM slots.
+hipError_t launch_stage(int E, int n_slots, int K, int32_t* slot_of, int32_t* slot_expert,
+                        const int32_t* in_use, const int32_t* next, int32_t* copy_list,
+                        int32_t* n_copies, const char* host_layer, char* hbm_layer,
+                        int64_t bundle, int32_t* flags, hipStream_t st);
+
+}  // namespace smd

@@ -1,0 +1,743 @@
+// Per-phase HIP kernels of the decode step (gfx950, wave64).
+//
+// GEMV scheme shared by every weight-streaming kernel: a row of the weight
+// matrix is owned by an aligned group of LG lanes; each lane reads 16-byte
+// chunks at stride LG (so one wave instruction covers 64/LG rows with fully
+// used cache lines), keeps the matching activations in registers, and the
+// group is reduced with DPP at the end. Int4 rows are dequantised in
+// registers (q4_dot8); fp16 rows use v_dot2_f32_f16 directly. All sums are
+// fp32; fp32 activations meet fp16 weights as an fp16 hi/lo pair.
+//
+// Page tags: [MW] "The Other Half of the Memory Wall: Serving 35B MoEs from
+// SSD with Trained Routing Prediction"; [CB] "Edge0 streams a 35B MoE off
+// SSD. I counted the bytes it can't stream."; [IE] "Inside Edge0-35B".
+
+#include "device.h"
+#include "internal.h"
+
+namespace smd {
+
+namespace {
+
+constexpr int kBlock = 128;  // threads per block of the GEMV kernels (2 waves)
+
+__device__ __forceinline__ const void* entry_ptr(const void* base, int64_t entry, int64_t stride) {
+  return (const char*)base + entry * stride;
+}
+
+// Resolve routed expert id -> pool entry (through the slot table if any);
+// -1 if the id or the slot is out of range.
+__device__ __forceinline__ int64_t resolve_entry(const Pool& p, int E, int e) {
+  if (e < 0 || e >= E) return -1;
+  int64_t ent = e;
+  if (p.slot_of) ent = p.slot_of[e];
+  if (ent < 0 || ent >= p.count) return -1;
+  return ent;
+}
+
+// Load the pair-permuted fp16 activation chunk c (32 elements) from LDS.
+__device__ __forceinline__ void load_xchunk(const uint16_t* xs, int c, f16x2* xr) {
+  const uint4* src = reinterpret_cast<const uint4*>(xs + 32 * c);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    uint4 v = src[m];
+    xr[4 * m + 0] = as_h2(v.x);
+    xr[4 * m + 1] = as_h2(v.y);
+    xr[4 * m + 2] = as_h2(v.z);
+    xr[4 * m + 3] = as_h2(v.w);
+  }
+}
+
+// One 16-byte chunk (32 int4 weights) against 32 activations.
+__device__ __forceinline__ float q4_dot32(uint4 wv, const f16x2* xr) {
+  float p = 0.0f;
+  p = q4_dot8(wv.x, xr + 0, p);
+  p = q4_dot8(wv.y, xr + 4, p);
+  p = q4_dot8(wv.z, xr + 8, p);
+  p = q4_dot8(wv.w, xr + 12, p);
+  return p;
+}
+
+// Same with an fp16 hi/lo activation pair (dequantises each word once).
+__device__ __forceinline__ float q4_dot8_hl(uint32_t w, const f16x2* xh, const f16x2* xl,
+                                            float acc) {
+  const uint32_t u = w ^ 0x88888888u;
+  const uint32_t v = u >> 8;
+  const f16x2 k1032 = {(f16)1032.0f, (f16)1032.0f};
+  const f16x2 k16 = {(f16)0.0625f, (f16)0.0625f};
+  const f16x2 k72 = {(f16)72.0f, (f16)72.0f};
+  f16x2 p0 = as_h2((u & 0x000F000Fu) | 0x64006400u) - k1032;
+  f16x2 p1 = as_h2((u & 0x00F000F0u) | 0x64006400u) * k16 - k72;
+  f16x2 p2 = as_h2((v & 0x000F000Fu) | 0x64006400u) - k1032;
+  f16x2 p3 = as_h2((v & 0x00F000F0u) | 0x64006400u) * k16 - k72;
+  acc = dot2(p0, xh[0], acc);
+  acc = dot2(p1, xh[1], acc);
+  acc = dot2(p2, xh[2], acc);
+  acc = dot2(p3, xh[3], acc);
+  acc = dot2(p0, xl[0], acc);
+  acc = dot2(p1, xl[1], acc);
+  acc = dot2(p2, xl[2], acc);
+  acc = dot2(p3, xl[3], acc);
+  return acc;
+}
+
+__device__ __forceinline__ float q4_dot32_hl(uint4 wv, const f16x2* xh, const f16x2* xl) {
+  float p = 0.0f;
+  p = q4_dot8_hl(wv.x, xh + 0, xl + 0, p);
+  p = q4_dot8_hl(wv.y, xh + 4, xl + 4, p);
+  p = q4_dot8_hl(wv.z, xh + 8, xl + 8, p);
+  p = q4_dot8_hl(wv.w, xh + 12, xl + 12, p);
+  return p;
+}
+
+// Block-wide max of |v| over a strided range (kBlock threads).
+__device__ float block_absmax(const float* v, int n, float* red) {
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) m = fmaxf(m, fabsf(v[i]));
+  m = wave_max(m);
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = m;
+  __syncthreads();
+  float r = 0.0f;
+  for (int j = 0; j < nw; ++j) r = fmaxf(r, red[j]);
+  return r;
+}
+
+// Power-of-two exponent e with max|v| * 2^-e < 2^14 (0 for an all-zero vector).
+__device__ __forceinline__ int hilo_exponent(float absmax) {
+  if (!(absmax > 0.0f)) return 0;
+  int ex;
+  frexpf(absmax, &ex);  // absmax < 2^ex
+  return ex - 14;
+}
+
+// ------------------------------------------------------------- gate / up --
+
+struct GateUpArgs {
+  Dims dm;
+  Pool pool;
+  SharedW sh;
+  const uint16_t* x;  // [B][d]
+  const int32_t* idx; // [B][K]
+  float* gu;          // [B][K+1][imax]
+  const float* ax;    // [B][3][rmax]
+  int imax, rmax;
+  int32_t* flags;
+};
+
+// SwiGLU gate/up of one expert slot (routed k < K, shared k == K) for one
+// token: h[row] = silu(Wg[row] . x (+ LoRA)) * (Wu[row] . x (+ LoRA))
+// [MW §3.1 Math contract; IE "Architectural Deep Dive"]. grid = (row blocks,
+// K+1, B).
+template <int LG, int CPL>
+__global__ __launch_bounds__(kBlock) void k_gate_up(GateUpArgs a) {
+  extern __shared__ uint16_t xs[];
+  const Dims& dm = a.dm;
+  const int b = blockIdx.z, k = blockIdx.y;
+  const bool shared = (k == dm.K);
+  if (shared && !a.sh.present) return;
+  const int rows = shared ? dm.Is : dm.I;
+  const int d = dm.d;
+
+  const uint32_t *gq, *uq;
+  const uint16_t *gs, *us;
+  if (shared) {
+    gq = a.sh.gate.q; gs = a.sh.gate.s; uq = a.sh.up.q; us = a.sh.up.s;
+  } else {
+    const int64_t ent = resolve_entry(a.pool, dm.E, a.idx[b * dm.K + k]);
+    if (ent < 0) {
+      if (threadIdx.x == 0 && blockIdx.x == 0) atomicOr(&a.flags[FLAG_RANGE], 1);
+      return;
+    }
+    gq = (const uint32_t*)entry_ptr(a.pool.gate.q, ent, a.pool.stride_q);
+    uq = (const uint32_t*)entry_ptr(a.pool.up.q, ent, a.pool.stride_q);
+    gs = (const uint16_t*)entry_ptr(a.pool.gate.s, ent, a.pool.stride_s);
+    us = (const uint16_t*)entry_ptr(a.pool.up.s, ent, a.pool.stride_s);
+  }
+
+  const uint16_t* xb = a.x + (int64_t)b * d;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) xs[perm8(i)] = xb[i];
+  __syncthreads();
+
+  constexpr int kRowsPerWave = 64 / LG;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane % LG, grp = lane / LG;
+  const int row = blockIdx.x * (kBlock / 64) * kRowsPerWave + wave * kRowsPerWave + grp;
+  if (row >= rows) return;  // whole aligned lane groups leave together
+
+  const int wpr = d / 8, spr = d / dm.G;
+  const uint32_t* grow = gq + (int64_t)row * wpr;
+  const uint32_t* urow = uq + (int64_t)row * wpr;
+  const uint16_t* gsr = gs + (int64_t)row * spr;
+  const uint16_t* usr = us + (int64_t)row * spr;
+
+  uint4 wg[CPL], wu[CPL];
+  uint16_t sg[CPL], su[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = li + LG * j;
+    wg[j] = *reinterpret_cast<const uint4*>(grow + 4 * c);
+    wu[j] = *reinterpret_cast<const uint4*>(urow + 4 * c);
+    sg[j] = gsr[(32 * c) / dm.G];
+    su[j] = usr[(32 * c) / dm.G];
+  }
+  float ag = 0.0f, au = 0.0f;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    f16x2 xr[16];
+    load_xchunk(xs, li + LG * j, xr);
+    ag += h2f(sg[j]) * q4_dot32(wg[j], xr);
+    au += h2f(su[j]) * q4_dot32(wu[j], xr);
+  }
+  if (shared && a.sh.bg) {
+    const float* axb = a.ax + (int64_t)b * 3 * a.rmax;
+    float lg = 0.0f, lu = 0.0f;
+    for (int t = li; t < dm.r; t += LG) {
+      lg += h2f(a.sh.bg[(int64_t)row * dm.r + t]) * axb[t];
+      lu += h2f(a.sh.bu[(int64_t)row * dm.r + t]) * axb[a.rmax + t];
+    }
+    ag += dm.lora_scale * lg;
+    au += dm.lora_scale * lu;
+  }
+  ag = group_sum<LG>(ag);
+  au = group_sum<LG>(au);
+  if (li == 0) a.gu[((int64_t)b * (dm.K + 1) + k) * a.imax + row] = silu(ag) * au;
+}
+
+// ------------------------------------------------------------------ down --
+
+struct DownArgs {
+  Dims dm;
+  Pool pool;
+  SharedW sh;
+  const int32_t* idx;  // [B][K]
+  const float* w;      // [B][K]
+  const float* gu;     // [B][K+1][imax]
+  int imax;
+  const float* ax;     // [B][3][rmax]
+  int rmax;
+  const float* resid;  // [B][d] or null
+  uint16_t* y;         // [B][d]
+  int32_t* flags;
+};
+
+// Down projections with the weighted combine and the shared expert:
+// y[row] = sum_k w_k Wd_k[row] . h_k + Wd_s[row] . h_s (+ down LoRA)
+// [MW §3.1 Math contract; CB "The mechanism" (shared_experts = 1)].
+// Output fp16(resid + y). grid = (row blocks of d, B).
+template <int LG, int CPL>
+__global__ __launch_bounds__(kBlock) void k_down(DownArgs a) {
+  extern __shared__ uint16_t hs[];  // [nexp][2][I] pair-permuted hi / lo
+  __shared__ float coef[16];
+  __shared__ int64_t ent_s[16];
+  __shared__ float red[4];
+  const Dims& dm = a.dm;
+  const int b = blockIdx.y;
+  const int I = dm.I, d = dm.d;
+  const int nexp = dm.K + (a.sh.present ? 1 : 0);
+
+  for (int k = 0; k < nexp; ++k) {
+    const float* src = a.gu + ((int64_t)b * (dm.K + 1) + k) * a.imax;
+    const float m = block_absmax(src, I, red);
+    const int e = hilo_exponent(m);
+    const float inv = ldexpf(1.0f, -e);
+    uint16_t* hh = hs + (int64_t)k * 2 * I;
+    for (int i = threadIdx.x; i < I; i += blockDim.x) {
+      f16 hi, lo;
+      split_hilo(src[i], inv, hi, lo);
+      hh[perm8(i)] = __builtin_bit_cast(uint16_t, hi);
+      hh[I + perm8(i)] = __builtin_bit_cast(uint16_t, lo);
+    }
+    if (threadIdx.x == 0) {
+      if (k < dm.K) {
+        const int64_t ent = resolve_entry(a.pool, dm.E, a.idx[b * dm.K + k]);
+        if (ent < 0 && blockIdx.x == 0) atomicOr(&a.flags[FLAG_RANGE], 1);
+        ent_s[k] = ent;
+        coef[k] = ent < 0 ? 0.0f : a.w[b * dm.K + k] * ldexpf(1.0f, e);
+      } else {
+        ent_s[k] = 0;
+        coef[k] = ldexpf(1.0f, e);
+      }
+    }
+  }
+  __syncthreads();
+
+  constexpr int kRowsPerWave = 64 / LG;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane % LG, grp = lane / LG;
+  const int row = blockIdx.x * (kBlock / 64) * kRowsPerWave + wave * kRowsPerWave + grp;
+  if (row >= d) return;
+
+  const int wpr = I / 8, spr = I / dm.G;
+  float acc = 0.0f;
+  for (int k = 0; k < nexp; ++k) {
+    if (k < dm.K && ent_s[k] < 0) continue;
+    const uint32_t* q;
+    const uint16_t* s;
+    if (k < dm.K) {
+      q = (const uint32_t*)entry_ptr(a.pool.down.q, ent_s[k], a.pool.stride_q);
+      s = (const uint16_t*)entry_ptr(a.pool.down.s, ent_s[k], a.pool.stride_s);
+    } else {
+      q = a.sh.down.q;
+      s = a.sh.down.s;
+    }
+    const uint32_t* qrow = q + (int64_t)row * wpr;
+    const uint16_t* srow = s + (int64_t)row * spr;
+    uint4 wv[CPL];
+    uint16_t sv[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = li + LG * j;
+      wv[j] = *reinterpret_cast<const uint4*>(qrow + 4 * c);
+      sv[j] = srow[(32 * c) / dm.G];
+    }
+    const uint16_t* hh = hs + (int64_t)k * 2 * I;
+    float part = 0.0f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      f16x2 xh[16], xl[16];
+      load_xchunk(hh, li + LG * j, xh);
+      load_xchunk(hh + I, li + LG * j, xl);
+      part += h2f(sv[j]) * q4_dot32_hl(wv[j], xh, xl);
+    }
+    acc += coef[k] * part;
+  }
+  if (a.sh.present && a.sh.bd) {
+    const float* axd = a.ax + (int64_t)b * 3 * a.rmax + 2 * a.rmax;
+    float l = 0.0f;
+    for (int t = li; t < dm.r; t += LG) l += h2f(a.sh.bd[(int64_t)row * dm.r + t]) * axd[t];
+    acc += dm.lora_scale * l;
+  }
+  acc = group_sum<LG>(acc);
+  if (li == 0) {
+    const float base = a.resid ? a.resid[(int64_t)b * d + row] : 0.0f;
+    a.y[(int64_t)b * d + row] = f2h(base + acc);
+  }
+}
+
+// ------------------------------------------------------------ fp16 GEMV --
+
+struct Gemv16Args {
+  const uint16_t* W;
+  int rows, cols;
+  int64_t ld;
+  const uint16_t* x16;
+  const float* xf;
+  int64_t x_stride;
+  const int32_t *cur, *prev;
+  int K, E, gcol0;
+  int epi;
+  const float* addv;
+  float* y;
+  int64_t y_stride;
+};
+
+// y[b][row] = W[row, :cols] . x[b] (+ one-hot gathered columns) with an
+// epilogue. Used for the router, the LoRA A products and the three head
+// matrices [MW §3.2 Head; CB "The mechanism" (PrerouterHead)].
+// grid = (row blocks, B); 16 lanes per row.
+template <bool XF32>
+__global__ __launch_bounds__(kBlock) void k_gemv16(Gemv16Args a) {
+  extern __shared__ uint16_t xs16[];  // [cols] or hi [cols] + lo [cols]
+  __shared__ float red[4];
+  const int b = blockIdx.y;
+  const int cols = a.cols;
+  float scale = 1.0f;
+  if constexpr (XF32) {
+    const float* xb = a.xf + (int64_t)b * a.x_stride;
+    const int e = hilo_exponent(block_absmax(xb, cols, red));
+    const float inv = ldexpf(1.0f, -e);
+    scale = ldexpf(1.0f, e);
+    for (int i = threadIdx.x; i < cols; i += blockDim.x) {
+      f16 hi, lo;
+      split_hilo(xb[i], inv, hi, lo);
+      xs16[i] = __builtin_bit_cast(uint16_t, hi);
+      xs16[cols + i] = __builtin_bit_cast(uint16_t, lo);
+    }
+  } else {
+    const uint16_t* xb = a.x16 + (int64_t)b * a.x_stride;
+    for (int i = threadIdx.x; i < cols; i += blockDim.x) xs16[i] = xb[i];
+  }
+  __syncthreads();
+
+  constexpr int LG = 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane % LG, grp = lane / LG;
+  const int row = blockIdx.x * (kBlock / LG) + wave * (64 / LG) + grp;
+  if (row >= a.rows) return;
+
+  const uint16_t* wrow = a.W + (int64_t)row * a.ld;
+  float acc = 0.0f;
+  const int nch = cols / 8;
+  for (int c = li; c < nch; c += LG) {
+    const uint4 wv = *reinterpret_cast<const uint4*>(wrow + 8 * c);
+    const uint4 xv = *reinterpret_cast<const uint4*>(xs16 + 8 * c);
+    acc = dot2(as_h2(wv.x), as_h2(xv.x), acc);
+    acc = dot2(as_h2(wv.y), as_h2(xv.y), acc);
+    acc = dot2(as_h2(wv.z), as_h2(xv.z), acc);
+    acc = dot2(as_h2(wv.w), as_h2(xv.w), acc);
+    if constexpr (XF32) {
+      const uint4 xl = *reinterpret_cast<const uint4*>(xs16 + cols + 8 * c);
+      acc = dot2(as_h2(wv.x), as_h2(xl.x), acc);
+      acc = dot2(as_h2(wv.y), as_h2(xl.y), acc);
+      acc = dot2(as_h2(wv.z), as_h2(xl.z), acc);
+      acc = dot2(as_h2(wv.w), as_h2(xl.w), acc);
+    }
+  }
+  acc *= scale;
+  if (a.cur) {
+    // One-hot blocks of the head feature: each selected expert adds one
+    // weight column (the one-hot entry is exactly 1).
+    for (int kk = li; kk < 2 * a.K; kk += LG) {
+      int col = -1;
+      if (kk < a.K) {
+        const int e = a.cur[(int64_t)b * a.K + kk];
+        if (e >= 0 && e < a.E) col = a.gcol0 + e;
+      } else if (a.prev) {
+        const int e = a.prev[(int64_t)b * a.K + kk - a.K];
+        if (e >= 0 && e < a.E) col = a.gcol0 + a.E + e;
+      }
+      if (col >= 0) acc += h2f(wrow[col]);
+    }
+  }
+  acc = group_sum<LG>(acc);
+  if (li == 0) {
+    float v = acc;
+    if (a.epi == 1) v = gelu_erf(v);
+    else if (a.epi == 2) v += a.addv[(int64_t)b * a.y_stride + row];
+    a.y[(int64_t)b * a.y_stride + row] = v;
+  }
+}
+
+// ------------------------------------------------------------ LoRA B ------
+
+__global__ __launch_bounds__(256) void k_lora_b(const uint16_t* Bm, int out_dim, int r,
+                                                float scale, const float* ax, int ax_stride,
+                                                float* y_acc) {
+  const int b = blockIdx.y;
+  const int o = blockIdx.x * blockDim.x + threadIdx.x;
+  if (o >= out_dim) return;
+  const float* axb = ax + (int64_t)b * ax_stride;
+  float s = 0.0f;
+  for (int t = 0; t < r; ++t) s += h2f(Bm[(int64_t)o * r + t]) * axb[t];
+  y_acc[(int64_t)b * out_dim + o] += scale * s;
+}
+
+// --------------------------------------------------------------- routing --
+
+struct RouteArgs {
+  Dims dm;
+  const float* logits;  // [B][E]
+  const float* bias;    // [E] or null (sigmoid-group)
+  int32_t* idx;         // [B][K]
+  float* w;             // [B][K]
+  int32_t* flags;
+};
+
+constexpr int kMaxE = 512;
+
+// Routing of one token's fp32 logits by the tier's family [MW App. A]:
+// softmax-top-K (select the K largest logits, which are the K largest
+// probabilities; weights renormalised over the K) or sigmoid-group (biased
+// scores, top-2-sum group ranking, top-K inside surviving groups, weights
+// s * sigma / (sum sigma + 1e-20)). Ties go to the lower id. One wave per
+// token.
+__global__ __launch_bounds__(64) void k_route(RouteArgs a) {
+  __shared__ float sel_s[kMaxE];
+  __shared__ float gsc_s[64];
+  __shared__ int keep_s[64];
+  const Dims& dm = a.dm;
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int E = dm.E, K = dm.K;
+  constexpr int kPer = kMaxE / 64;
+  const float* lg = a.logits + (int64_t)b * E;
+
+  float v[kPer], sig[kPer];
+  bool ok[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = lane + 64 * j;
+    ok[j] = e < E;
+    v[j] = ok[j] ? lg[e] : 0.0f;
+    sig[j] = 0.0f;
+  }
+  if (dm.router_kind == E0_ROUTER_SIGMOID_GROUP) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int e = lane + 64 * j;
+      if (!ok[j]) continue;
+      sig[j] = 1.0f / (1.0f + expf(-v[j]));
+      v[j] = sig[j] + (a.bias ? a.bias[e] : 0.0f);
+      sel_s[e] = v[j];
+    }
+    __syncthreads();
+    const int per = E / dm.n_groups;
+    if (lane < dm.n_groups) {
+      float m1 = -INFINITY, m2 = -INFINITY;
+      for (int i = 0; i < per; ++i) {
+        const float s = sel_s[lane * per + i];
+        if (s > m1) { m2 = m1; m1 = s; } else if (s > m2) { m2 = s; }
+      }
+      gsc_s[lane] = m1 + m2;
+      keep_s[lane] = 0;
+    }
+    __syncthreads();
+    if (lane == 0) {
+      for (int t = 0; t < dm.topk_groups; ++t) {
+        int best = -1;
+        for (int g = 0; g < dm.n_groups; ++g)
+          if (!keep_s[g] && (best < 0 || gsc_s[g] > gsc_s[best])) best = g;
+        keep_s[best] = 1;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int e = lane + 64 * j;
+      if (ok[j]) ok[j] = keep_s[e / per] != 0;
+    }
+  }
+
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (lane + 64 * j < E) mx = fmaxf(mx, lg[lane + 64 * j]);
+  mx = wave_max(mx);
+
+  float wsel[8];
+  int isel[8];
+  float denom = 0.0f;
+  for (int k = 0; k < K; ++k) {
+    uint64_t key = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      if (!ok[j]) continue;
+      const uint32_t e = lane + 64 * j;
+      const uint64_t kk = ((uint64_t)f2key(v[j]) << 32) | (0xFFFFFFFFu - e);
+      key = kk > key ? kk : key;
+    }
+    key = wave_max_u64(key);
+    if (key == 0) {  // no candidate left (rejected shapes make this unreachable)
+      if (lane == 0) atomicOr(&a.flags[FLAG_RANGE], 4);
+      key = 0xFFFFFFFFull;  // decodes to expert 0
+    }
+    const int e = (int)(0xFFFFFFFFu - (uint32_t)key);
+    isel[k] = e;
+    if (dm.router_kind == E0_ROUTER_SIGMOID_GROUP) {
+      wsel[k] = 1.0f / (1.0f + expf(-lg[e]));
+    } else {
+      wsel[k] = expf(lg[e] - mx);
+    }
+    denom += wsel[k];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (lane + 64 * j == e) ok[j] = false;
+  }
+  if (dm.router_kind == E0_ROUTER_SIGMOID_GROUP) {
+    denom += 1e-20f;
+  } else if (!dm.norm_topk) {
+    float z = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (lane + 64 * j < E) z += expf(lg[lane + 64 * j] - mx);
+    denom = wave_sum(z);
+  }
+  if (lane == 0) {
+    for (int k = 0; k < K; ++k) {
+      a.idx[(int64_t)b * K + k] = isel[k];
+      const float ww = wsel[k] / denom;
+      a.w[(int64_t)b * K + k] =
+          dm.router_kind == E0_ROUTER_SIGMOID_GROUP ? dm.route_scale * ww : ww;
+    }
+  }
+}
+
+// --------------------------------------------------------------- prepare --
+
+struct PrepArgs {
+  Dims dm;
+  const uint16_t* h;
+  const uint16_t* attn;
+  float* hattn;
+  uint16_t* xn;
+  const int32_t* cidx;
+  const float* cw;
+  int32_t* eidx;
+  float* ew;
+};
+
+// h_a = h + attn (fp32), x = fp16(h_a / sqrt(mean(h_a^2) + eps)): the
+// post-attention RMSNorm the head and the experts read [MW §3.2 Motivation].
+__global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
+  __shared__ float red[4];
+  const int b = blockIdx.x, d = a.dm.d;
+  const uint16_t* hb = a.h + (int64_t)b * d;
+  float ss = 0.0f;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) {
+    const float v = h2f(hb[i]) + (a.attn ? h2f(a.attn[i]) : 0.0f);
+    a.hattn[(int64_t)b * d + i] = v;
+    ss += v * v;
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.0f;
+  for (int j = 0; j < (int)(blockDim.x >> 6); ++j) tot += red[j];
+  const float inv = 1.0f / sqrtf(tot / d + a.dm.eps);
+  for (int i = threadIdx.x; i < d; i += blockDim.x)
+    a.xn[(int64_t)b * d + i] = f2h(a.hattn[(int64_t)b * d + i] * inv);
+  if (a.cidx && threadIdx.x < a.dm.K) {
+    a.eidx[(int64_t)b * a.dm.K + threadIdx.x] = a.cidx[(int64_t)b * a.dm.K + threadIdx.x];
+    a.ew[(int64_t)b * a.dm.K + threadIdx.x] = a.cw[(int64_t)b * a.dm.K + threadIdx.x];
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------- launchers --
+
+static bool q4_shape(int cols, int& lg, int& cpl) {
+  if (cols % 32) return false;
+  const int nch = cols / 32;
+  if (nch % 16 == 0 && nch / 16 <= 8) {
+    lg = 16;
+    cpl = nch / 16;
+  } else if (nch <= 8) {
+    lg = 1;
+    cpl = nch;
+  } else {
+    return false;
+  }
+  return cpl == 1 || cpl == 2 || cpl == 3 || cpl == 4 || cpl == 6 || cpl == 8;
+}
+
+bool q4_shape_ok(int cols) {
+  int lg, cpl;
+  return q4_shape(cols, lg, cpl);
+}
+
+// Calls Op<LG, CPL>::run(args...) for the supported instantiations.
+template <template <int, int> class Op, typename... A>
+static hipError_t q4_dispatch(int lg, int cpl, A&&... args) {
+  if (lg == 16) {
+    switch (cpl) {
+      case 1: Op<16, 1>::run(args...); break;
+      case 2: Op<16, 2>::run(args...); break;
+      case 3: Op<16, 3>::run(args...); break;
+      case 4: Op<16, 4>::run(args...); break;
+      case 6: Op<16, 6>::run(args...); break;
+      case 8: Op<16, 8>::run(args...); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (cpl) {
+      case 1: Op<1, 1>::run(args...); break;
+      case 2: Op<1, 2>::run(args...); break;
+      case 3: Op<1, 3>::run(args...); break;
+      case 4: Op<1, 4>::run(args...); break;
+      case 6: Op<1, 6>::run(args...); break;
+      case 8: Op<1, 8>::run(args...); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipGetLastError();
+}
+
+template <int LG, int CPL>
+struct GateUpOp {
+  static void run(dim3 grid, size_t lds, hipStream_t st, const GateUpArgs& a) {
+    k_gate_up<LG, CPL><<<grid, kBlock, lds, st>>>(a);
+  }
+};
+
+template <int LG, int CPL>
+struct DownOp {
+  static void run(dim3 grid, size_t lds, hipStream_t st, const DownArgs& a) {
+    k_down<LG, CPL><<<grid, kBlock, lds, st>>>(a);
+  }
+};
+
+static int imax_of(const Dims& dm) { return dm.I > dm.Is ? dm.I : dm.Is; }
+static int rmax_of(const Dims& dm) { return dm.r > 1 ? dm.r : 1; }
+
+hipError_t launch_gate_up(const Dims& dm, const Pool& pool, const SharedW& sh,
+                          const uint16_t* x, const int32_t* idx, int B, const Scratch& s,
+                          hipStream_t st) {
+  int lg, cpl;
+  if (!q4_shape(dm.d, lg, cpl)) return hipErrorInvalidValue;
+  GateUpArgs a{dm, pool, sh, x, idx, s.gu, s.ax, imax_of(dm), rmax_of(dm), s.flags};
+  const int rows = imax_of(dm);
+  const int rpb = (kBlock / 64) * (64 / lg);
+  dim3 grid((rows + rpb - 1) / rpb, dm.K + 1, B);
+  const size_t lds = (size_t)dm.d * sizeof(uint16_t);
+  return q4_dispatch<GateUpOp>(lg, cpl, grid, lds, st, a);
+}
+
+hipError_t launch_down(const Dims& dm, const Pool& pool, const SharedW& sh,
+                       const int32_t* idx, const float* w, int B, const float* resid,
+                       uint16_t* y16, const Scratch& s, hipStream_t st) {
+  int lg, cpl;
+  if (!q4_shape(dm.I, lg, cpl)) return hipErrorInvalidValue;
+  DownArgs a{dm, pool, sh, idx, w, s.gu, imax_of(dm), s.ax, rmax_of(dm), resid, y16, s.flags};
+  const int rpb = (kBlock / 64) * (64 / lg);
+  dim3 grid((dm.d + rpb - 1) / rpb, B);
+  const int nexp = dm.K + (sh.present ? 1 : 0);
+  const size_t lds = (size_t)nexp * 2 * dm.I * sizeof(uint16_t);
+  return q4_dispatch<DownOp>(lg, cpl, grid, lds, st, a);
+}
+
+hipError_t launch_gemv16(const uint16_t* W, int rows, int cols, int64_t ld,
+                         const uint16_t* x16, const float* xf32, int64_t x_stride, int B,
+                         const int32_t* cur, const int32_t* prev, int K, int E, int gcol0,
+                         int epi, const float* addv, float* y, int64_t y_stride,
+                         hipStream_t st) {
+  if (cols % 8 || ld % 8) return hipErrorInvalidValue;
+  Gemv16Args a{W, rows, cols, ld, x16, xf32, x_stride, cur, prev, K, E, gcol0, epi, addv, y,
+               y_stride};
+  dim3 grid((rows + (kBlock / 16) - 1) / (kBlock / 16), B);
+  if (xf32) {
+    hipLaunchKernelGGL(k_gemv16<true>, grid, dim3(kBlock), (size_t)cols * 4, st, a);
+  } else {
+    hipLaunchKernelGGL(k_gemv16<false>, grid, dim3(kBlock), (size_t)cols * 2, st, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_a(int n_mats, const uint16_t* const* A, const int* slots, int in_dim,
+                         int r, const uint16_t* x16, const float* xf32, int64_t x_stride,
+                         int B, float* ax, int ax_stride, hipStream_t st) {
+  for (int m = 0; m < n_mats; ++m) {
+    hipError_t e = launch_gemv16(A[m], r, in_dim, in_dim, x16, xf32, x_stride, B, nullptr,
+                                 nullptr, 0, 0, 0, 0, nullptr, ax + slots[m], ax_stride, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_lora_b(const uint16_t* Bm, int out_dim, int r, float scale, const float* ax,
+                         int ax_stride, float* y_acc, int B, hipStream_t st) {
+  dim3 grid((out_dim + 255) / 256, B);
+  hipLaunchKernelGGL(k_lora_b, grid, dim3(256), 0, st, Bm, out_dim, r, scale, ax, ax_stride,
+                     y_acc);
+  return hipGetLastError();
+}
+
+hipError_t launch_route(const Dims& dm, const float* logits, const float* bias, int B,
+                        int32_t* idx, float* w, int32_t* flags, hipStream_t st) {
+  if (dm.E > kMaxE || dm.K > 8 || dm.n_groups > 64) return hipErrorInvalidValue;
+  RouteArgs a{dm, logits, bias, idx, w, flags};
+  hipLaunchKernelGGL(k_route, dim3(B), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep(const Dims& dm, const uint16_t* h, const uint16_t* attn, int B,
+                       float* hattn, uint16_t* xn, const int32_t* cidx, const float* cw,
+                       int32_t* eidx, float* ew, hipStream_t st) {
+  PrepArgs a{dm, h, attn, hattn, xn, cidx, cw, eidx, ew};
+  hipLaunchKernelGGL(k_prep, dim3(B), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace smd

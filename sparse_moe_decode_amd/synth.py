@@ -67,8 +67,8 @@ def stack_roles(tier: str) -> list[dict]:
 
 
 def rng_for(seed: int, *path: int) -> np.random.Generator:
-    """Independent generator for a (seed, layer, ...) path."""
-    return np.random.default_rng(np.random.SeedSequence([seed, *path]))
+    """Independent generator (SFC64 bit stream) for a (seed, layer, ...) path."""
+    return np.random.Generator(np.random.SFC64(np.random.SeedSequence([seed, *path])))
 
 
 # ------------------------------------------------------------ primitives --
@@ -76,7 +76,26 @@ def rng_for(seed: int, *path: int) -> np.random.Generator:
 def random_words(rng, shape) -> np.ndarray:
     """uint32 words with eight independent uniform nibbles each."""
     n = int(np.prod(shape))
-    return np.frombuffer(rng.bytes(4 * n), dtype=np.uint32).reshape(shape).copy()
+    raw = rng.bit_generator.random_raw((n + 1) // 2).view(np.uint32)
+    return (raw if raw.size == n else raw[:n].copy()).reshape(shape)
+
+
+def fold_min_code(words: np.ndarray) -> np.ndarray:
+    """In place: every nibble holding code 0b1000 (-8) becomes 0.
+
+    Uniform nibbles read as two's complement have mean -0.5; after the fold
+    the codes are symmetric in [-7, 7] with mean 0. A nibble is 0b1000 when
+    its top bit is set and its low three bits are zero; adding 0b0111 to the
+    low three bits sets bit 3 exactly when they are non-zero (no carry leaves
+    the nibble), which gives a per-nibble test with whole-word operations.
+    """
+    lo = np.bitwise_and(words, np.uint32(0x77777777))
+    np.add(lo, np.uint32(0x77777777), out=lo)
+    np.bitwise_and(lo, np.uint32(0x88888888), out=lo)       # bit 3 set: low bits != 0
+    np.bitwise_xor(lo, np.uint32(0x88888888), out=lo)       # bit 3 set: low bits == 0
+    np.bitwise_and(lo, words, out=lo)                       # ... and top bit set
+    np.bitwise_xor(words, lo, out=words)                    # clear it: 0b1000 -> 0
+    return words
 
 
 def group_scales(rng, shape) -> np.ndarray:
@@ -87,30 +106,34 @@ def f16_normal(rng, shape, std=1.0) -> np.ndarray:
     return rng.normal(0.0, std, size=shape).astype(np.float16)
 
 
-def q4_matrix(rng, rows, cols, G, lead=()):
-    """Packed int4 matrix: (uint32 [*lead, rows, cols/8], fp16 [*lead, rows, cols/G])."""
+def q4_matrix(rng, rows, cols, G, lead=(), zero_mean=False):
+    """Packed int4 matrix: (uint32 [*lead, rows, cols/8], fp16 [*lead, rows, cols/G]).
+
+    zero_mean folds the -8 code to 0 (see fold_min_code)."""
     assert cols % 8 == 0 and cols % G == 0
-    return (random_words(rng, (*lead, rows, cols // 8)),
-            group_scales(rng, (*lead, rows, cols // G)))
+    q = random_words(rng, (*lead, rows, cols // 8))
+    if zero_mean:
+        fold_min_code(q)
+    return q, group_scales(rng, (*lead, rows, cols // G))
 
 
 # ----------------------------------------------------------- layer parts --
 
-def routed_pool(rng, dm: dict, n: int | None = None) -> dict:
+def routed_pool(rng, dm: dict, n: int | None = None, zero_mean: bool = False) -> dict:
     """n experts (default E) stacked: gate/up [n, I, d/8], down [n, d, I/8]."""
     n = dm["E"] if n is None else n
     d, I, G = dm["d"], dm["I"], dm["G"]
-    gq, gs = q4_matrix(rng, I, d, G, (n,))
-    uq, us = q4_matrix(rng, I, d, G, (n,))
-    dq, ds = q4_matrix(rng, d, I, G, (n,))
+    gq, gs = q4_matrix(rng, I, d, G, (n,), zero_mean)
+    uq, us = q4_matrix(rng, I, d, G, (n,), zero_mean)
+    dq, ds = q4_matrix(rng, d, I, G, (n,), zero_mean)
     return dict(gate_q=gq, gate_s=gs, up_q=uq, up_s=us, down_q=dq, down_s=ds)
 
 
-def shared_expert(rng, dm: dict, lora: bool = True) -> dict:
+def shared_expert(rng, dm: dict, lora: bool = True, zero_mean: bool = False) -> dict:
     d, Is, G, r = dm["d"], dm["Is"], dm["G"], dm["r"]
-    gq, gs = q4_matrix(rng, Is, d, G)
-    uq, us = q4_matrix(rng, Is, d, G)
-    dq, ds = q4_matrix(rng, d, Is, G)
+    gq, gs = q4_matrix(rng, Is, d, G, zero_mean=zero_mean)
+    uq, us = q4_matrix(rng, Is, d, G, zero_mean=zero_mean)
+    dq, ds = q4_matrix(rng, d, Is, G, zero_mean=zero_mean)
     out = dict(gate_q=gq, gate_s=gs, up_q=uq, up_s=us, down_q=dq, down_s=ds)
     if lora and r > 0:
         out.update(a_gate=f16_normal(rng, (r, d), 0.01), b_gate=f16_normal(rng, (Is, r), 0.01),
@@ -138,10 +161,16 @@ def router(rng, dm: dict):
     return W, b
 
 
-def layer(seed: int, l: int, dm: dict, role: dict, lora: bool = True) -> dict:
-    """All weights of layer l of a stack (or of a single layer with l = 0)."""
+def layer(seed: int, l: int, dm: dict, role: dict, lora: bool = True,
+          zero_mean: bool = False) -> dict:
+    """All weights of layer l of a stack (or of a single layer with l = 0).
+
+    zero_mean=True draws zero-mean int4 codes; the stacked workloads use it so
+    the residual stream does not drift through the layers (uniform codes have
+    mean -0.5, which RMSNorm feeds back as a growing common mode)."""
     rng = rng_for(seed, l)
-    out = dict(routed=routed_pool(rng, dm), shared=shared_expert(rng, dm, lora),
+    out = dict(routed=routed_pool(rng, dm, zero_mean=zero_mean),
+               shared=shared_expert(rng, dm, lora, zero_mean=zero_mean),
                attn=f16_normal(rng, dm["d"], 1.0), router=None, router_bias=None, head=None)
     rrng = rng_for(seed, l, 1)
     if role.get("router"):

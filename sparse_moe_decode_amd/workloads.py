@@ -1,0 +1,64 @@
+"""Device-resident synthetic workloads for tests and the benchmark.
+
+Uploads the seeded inputs of ``synth`` to the GPU in the layouts the C ABI
+takes. Pure plumbing: no step of the decode arithmetic happens here.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import synth
+
+
+def to_dev(a: np.ndarray, device="cuda") -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint32:
+        a = a.view(np.int32)
+    return torch.from_numpy(a).to(device)
+
+
+def tree_to_dev(d, device="cuda"):
+    if d is None:
+        return None
+    return {k: (to_dev(v, device) if isinstance(v, np.ndarray) else v) for k, v in d.items()}
+
+
+def layer_roles(tier: str, n_layers: int | None = None) -> list[dict]:
+    roles = synth.stack_roles(tier)
+    return roles if n_layers is None else roles[:n_layers]
+
+
+def build_stack(tier: str, seed: int, device="cuda", n_layers: int | None = None,
+                lora: bool = True) -> dict:
+    """All layers of a stack on the device (weights resident in HBM); zero-mean
+    int4 codes keep the residual stream of the deep stack bounded."""
+    dm = synth.dims(tier)
+    roles = layer_roles(tier, n_layers)
+    layers = []
+    for l, role in enumerate(roles):
+        lw = synth.layer(seed, l, dm, role, lora=lora, zero_mean=True)
+        layers.append(dict(routed=tree_to_dev(lw["routed"], device),
+                           shared=tree_to_dev(lw["shared"], device),
+                           attn=to_dev(lw["attn"], device),
+                           router=None if lw["router"] is None else to_dev(lw["router"], device),
+                           router_bias=(None if lw["router_bias"] is None
+                                        else to_dev(lw["router_bias"], device)),
+                           head=tree_to_dev(lw["head"], device)))
+        del lw
+    return dict(dims=dm, roles=roles, layers=layers, seed=seed)
+
+
+def initial_routing(tier: str, seed: int, n_layers: int):
+    """Routing consumed at the first token: a random K-set with Dirichlet weights."""
+    dm = synth.dims(tier)
+    rng = synth.rng_for(seed, 10_000)
+    idx = np.stack([synth.random_set(rng, dm["E"], dm["K"]) for _ in range(n_layers)])
+    w = np.stack([synth.random_weights(rng, dm["K"]) for _ in range(n_layers)])
+    return idx, w
+
+
+def token_inputs(tier: str, seed: int, T: int, rho: float = 0.5) -> np.ndarray:
+    dm = synth.dims(tier)
+    return synth.ar1_tokens(synth.rng_for(seed, 20_000), T, dm["d"], rho)

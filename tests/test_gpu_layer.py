@@ -1,0 +1,98 @@
+"""GPU parity of layer_step: single layers of every tier and the full stacks.
+
+Runs tokens through layer_step exactly as the benchmark does (one call per
+token over the layer range) and checks every (token, layer) step against the
+oracle, re-anchored on the GPU's own inputs (see stack_check.py).
+"""
+
+import numpy as np
+import pytest
+
+from gpu_util import announce, dev, host
+from stack_check import StackChecker
+from sparse_moe_decode_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def api():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_moe_decode_amd import api as _api
+    return _api
+
+
+def _run_and_check(api, orc, tier, roles, seed, T, check_layers, rho=0.5, zero_mean=False):
+    import torch
+    from sparse_moe_decode_amd import workloads as wl
+    dm = synth.dims(tier)
+    L = len(roles)
+    layers, keep = [], {}
+    for l, role in enumerate(roles):
+        lw = synth.layer(seed, l, dm, role, zero_mean=zero_mean)
+        if l in check_layers:
+            keep[l] = lw
+        if L > 2:
+            announce("upload", tier, f"layer {l}/{L}")
+        layers.append(dict(routed=wl.tree_to_dev(lw["routed"]), shared=wl.tree_to_dev(lw["shared"]),
+                           attn=dev(lw["attn"]),
+                           router=None if lw["router"] is None else dev(lw["router"]),
+                           router_bias=(None if lw["router_bias"] is None
+                                        else dev(lw["router_bias"])),
+                           head=wl.tree_to_dev(lw["head"])))
+    ctx = api.Context(dm, max_tokens=4)
+    model = api.Model(ctx, layers)
+    state = api.State(dm, L)
+    idx0, w0 = wl.initial_routing(tier, seed, L)
+    state.route_idx[0].copy_(torch.from_numpy(idx0))
+    state.route_w[0].copy_(torch.from_numpy(w0))
+    toks = wl.token_inputs(tier, seed, T, rho)
+    checker = StackChecker(orc, tier, seed, roles, check_layers, keep, zero_mean)
+    prev_exec = None
+    h = torch.empty((L + 1, dm["d"]), dtype=torch.float16, device="cuda")
+    for t in range(T):
+        announce("layer_step", tier, f"L={L}", f"token {t}")
+        h[0].copy_(torch.from_numpy(toks[t]))
+        api.layer_step(ctx, model, 0, L, state, t, h)
+        assert api.device_status(ctx) == 0
+        cur, nxt = t & 1, (t + 1) & 1
+        exec_idx = host(state.exec_idx[cur]).copy()
+        checker.check(t, host(h).copy(), host(state.x_trace).copy(), exec_idx,
+                      host(state.exec_w[cur]).copy(),
+                      prev_exec, host(state.route_idx[cur]).copy(),
+                      host(state.route_w[cur]).copy(), host(state.route_idx[nxt]).copy(),
+                      host(state.route_w[nxt]).copy(),
+                      host(state.head_logits).copy())
+        prev_exec = exec_idx
+    print(f"{tier} L={L}: {checker.steps} layer-steps checked, worst error ratio "
+          f"{checker.worst:.3f}, re-anchored router sets {checker.reanchored}, "
+          f"x elements one ulp off {checker.x_ulp_diffs}")
+    model.close()
+    ctx.close()
+    return checker
+
+
+@pytest.mark.parametrize("tier,T", [("tiny", 24), ("8b", 5), ("35b", 5)])
+def test_layer_step_two_layers(api, orc, tier, T):
+    """Layer 0 runs its router and owns a head predicting layer 1; layer 1
+    consumes that prediction and owns a head with no consumer."""
+    roles = [dict(router=True, head=True), dict(router=False, head=True)]
+    _run_and_check(api, orc, tier, roles, seed=31, T=T, check_layers=[0, 1])
+
+
+@pytest.mark.timeout(900)
+def test_layer_step_stack_35b(api, orc):
+    """Full 35B stack (40 layers, heads on 6-38) in the benchmark's launch
+    configuration; every layer-step of the first tokens is checked."""
+    roles = synth.stack_roles("35b")
+    _run_and_check(api, orc, "35b", roles, seed=3, T=3, check_layers=list(range(40)),
+                   zero_mean=True)
+
+
+@pytest.mark.timeout(600)
+def test_layer_step_stack_8b(api, orc):
+    roles = synth.stack_roles("8b")
+    _run_and_check(api, orc, "8b", roles, seed=5, T=3, check_layers=list(range(24)),
+                   zero_mean=True)
