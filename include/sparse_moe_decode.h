@@ -206,6 +206,23 @@ typedef struct e0_model e0_model;
 int e0_model_create(e0_ctx* ctx, const e0_layer* layers, int32_t n_layers, e0_model** out);
 void e0_model_destroy(e0_model* model);
 
+/* How layer_step executes: E0_PATH_AUTO (default) uses the persistent
+ * whole-token kernel when the shapes allow it (d a multiple of 512 up to
+ * 2048, I = 512), else one kernel per phase; E0_PATH_PHASES and
+ * E0_PATH_PERSISTENT force one (the latter fails with E0_ERR_SHAPE when the
+ * shapes are not supported). Both compute the same step. */
+enum { E0_PATH_AUTO = 0, E0_PATH_PHASES = 1, E0_PATH_PERSISTENT = 2 };
+int e0_model_set_path(e0_model* model, int32_t path);
+
+/* Phase tracing of the persistent kernel (observability; off by default).
+ * trace: device uint64 [grid][L][points] (shape from e0_model_trace_shape),
+ * or NULL to turn tracing off. Thread 0 of each workgroup writes the 100 MHz
+ * wall clock at each phase boundary of each layer it runs: layer start, h
+ * gathered, x normed, routed, gate/up done, head fc1 done, SwiGLU outputs
+ * gathered, shared expert done, down done, layer end. */
+int e0_model_set_trace(e0_model* model, uint64_t* trace);
+int32_t e0_model_trace_shape(e0_model* model, int32_t* grid, int32_t* points);
+
 /* Device-resident decode state, caller-owned, L = number of model layers:
  *   route_idx / route_w  int32 / fp32 [2][L][K]: routing consumed at token t
  *        is read from buffer t&1; a head owned by layer l at token t writes

@@ -83,6 +83,9 @@ _lib.lora_delta.argtypes = [_p, _p, _p, _i32, _i32, _i32, _f, _p, _p, _i32, _p]
 _lib.prerouter_forward.argtypes = [_p, C.POINTER(e0_head), _p, _p, _p, _i32, _p, _p, _p, _p]
 _lib.e0_model_create.argtypes = [_p, C.POINTER(e0_layer), _i32, C.POINTER(_p)]
 _lib.e0_model_destroy.argtypes = [_p]
+_lib.e0_model_set_path.argtypes = [_p, _i32]
+_lib.e0_model_set_trace.argtypes = [_p, _p]
+_lib.e0_model_trace_shape.argtypes = [_p, C.POINTER(_i32), C.POINTER(_i32)]
 _lib.layer_step.argtypes = [_p, _p, _i32, _i32, C.POINTER(e0_state), _i32, _p, _p]
 _lib.e0_bundle_bytes.argtypes = [C.POINTER(e0_spec)]
 _lib.e0_bundle_bytes.restype = _i64
@@ -93,7 +96,9 @@ _lib.stage_experts.argtypes = [_p, _i32, _p, _p, _p, _p]
 EXPORTS = ["e0_create", "e0_destroy", "e0_last_error", "e0_device_status", "moe_int4_decode",
            "lora_delta", "prerouter_forward", "e0_model_create", "e0_model_destroy",
            "layer_step", "e0_bundle_bytes", "e0_stager_create", "e0_stager_destroy",
-           "stage_experts"]
+           "stage_experts", "e0_model_set_path", "e0_model_set_trace", "e0_model_trace_shape"]
+
+PATH_AUTO, PATH_PHASES, PATH_PERSISTENT = 0, 1, 2
 
 
 class E0Error(RuntimeError):
@@ -252,6 +257,23 @@ class Model:
         self.ctx = ctx
         self.n_layers = len(layers)
         self._keep = layers
+
+    def enable_trace(self, on: bool = True):
+        """Allocate (or drop) the phase-trace buffer; returns it ([grid, L, points])."""
+        if not on:
+            _check(_lib.e0_model_set_trace(self.handle, None))
+            self.trace = None
+            return None
+        g, pts = _i32(), _i32()
+        _check(_lib.e0_model_trace_shape(self.handle, C.byref(g), C.byref(pts)))
+        self.trace = torch.zeros((max(g.value, 1), self.n_layers, pts.value), dtype=torch.int64,
+                                 device="cuda")
+        _check(_lib.e0_model_set_trace(self.handle, self.trace.data_ptr()))
+        return self.trace
+
+    def set_path(self, path: int):
+        """PATH_AUTO, PATH_PHASES (one kernel per phase) or PATH_PERSISTENT."""
+        _check(_lib.e0_model_set_path(self.handle, path))
 
     def close(self):
         if getattr(self, "handle", None):

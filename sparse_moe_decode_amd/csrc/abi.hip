@@ -49,7 +49,15 @@ struct e0_ctx {
 struct e0_model {
   e0_ctx* ctx;
   std::vector<e0_layer> layers;
-  void* dev_table;  // device copy of the layer table (persistent kernel)
+  LayerDev* dev_table;  // device copy of the layer table (persistent kernel)
+  void* xbuf;           // exchange words of the persistent kernel (one block)
+  uint64_t *xh, *xg, *xr, *xa, *xl;
+  uint32_t* fl;
+  int32_t ng;
+  uint32_t epoch;
+  int32_t path;
+  int32_t grid;
+  uint64_t* trace;
 };
 
 extern "C" {
@@ -353,6 +361,62 @@ int e0_model_create(e0_ctx* ctx, const e0_layer* layers, int32_t n_layers, e0_mo
   m->ctx = ctx;
   m->layers.assign(layers, layers + n_layers);
   m->dev_table = nullptr;
+  m->xbuf = nullptr;
+  m->xh = m->xg = m->xr = m->xa = m->xl = nullptr;
+  m->fl = nullptr;
+  m->epoch = 0;
+  m->path = E0_PATH_AUTO;
+  m->grid = 0;
+  m->trace = nullptr;
+  const Dims& dm = ctx->dm;
+  // Device table of the layers for the persistent kernel.
+  std::vector<LayerDev> table(n_layers);
+  int ng = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    const e0_layer& L = layers[l];
+    LayerDev& t = table[l];
+    make_pool(ctx, &L.experts, L.slot_of, t.pool);
+    make_shared(ctx, L.shared.gate.q ? &L.shared : nullptr, t.sh);
+    t.router = L.router;
+    t.router_bias = L.router_bias;
+    t.head = HeadW{L.head.fc1, L.head.fc2, L.head.lin, L.head.bias};
+    if (!L.head.fc1) t.head = HeadW{nullptr, nullptr, nullptr, nullptr};
+    t.attn = L.attn;
+    const int Is = t.sh.present ? dm.Is : 0;
+    const int r2 = (t.sh.present && t.sh.ag) ? 2 * dm.r : 0;
+    const int n = dm.K * dm.I + 2 * Is + r2;
+    if (n > ng) ng = n;
+  }
+  m->ng = ng;
+  if (stack_supported(dm)) {
+    hipError_t e = hipMalloc(&m->dev_table, sizeof(LayerDev) * n_layers);
+    if (e == hipSuccess)
+      e = hipMemcpy(m->dev_table, table.data(), sizeof(LayerDev) * n_layers,
+                    hipMemcpyHostToDevice);
+    const size_t wh = (size_t)n_layers * (dm.d / 2), wg = (size_t)n_layers * ng,
+                 wr = (size_t)n_layers * dm.E, wa = (size_t)n_layers * (dm.P + dm.E),
+                 wl = (size_t)n_layers * dm.E;
+    int dev = 0, cus = 0;
+    if (e == hipSuccess) e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const size_t nfl = (size_t)n_layers * kExchanges * (cus > 0 ? cus : 1);
+    const size_t words = wh + wg + wr + wa + wl + (nfl + 1) / 2;
+    if (e == hipSuccess) e = hipMalloc(&m->xbuf, words * 8);
+    if (e == hipSuccess) e = hipMemset(m->xbuf, 0, words * 8);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+      e0_model_destroy(m);
+      return hip_fail(e, "e0_model_create: persistent-kernel buffers");
+    }
+    uint64_t* w = (uint64_t*)m->xbuf;
+    m->xh = w; w += wh;
+    m->xg = w; w += wg;
+    m->xr = w; w += wr;
+    m->xa = w; w += wa;
+    m->xl = w; w += wl;
+    m->fl = (uint32_t*)w;
+    m->grid = cus;
+  }
   *out = m;
   return E0_OK;
 }
@@ -360,7 +424,30 @@ int e0_model_create(e0_ctx* ctx, const e0_layer* layers, int32_t n_layers, e0_mo
 void e0_model_destroy(e0_model* model) {
   if (!model) return;
   if (model->dev_table) hipFree(model->dev_table);
+  if (model->xbuf) hipFree(model->xbuf);
   delete model;
+}
+
+int e0_model_set_trace(e0_model* model, uint64_t* trace) {
+  if (!model) return fail(E0_ERR_ARG, "e0_model_set_trace: null model");
+  model->trace = trace;
+  return E0_OK;
+}
+
+int32_t e0_model_trace_shape(e0_model* model, int32_t* grid, int32_t* points) {
+  if (!model) return fail(E0_ERR_ARG, "e0_model_trace_shape: null model");
+  if (grid) *grid = model->grid;
+  if (points) *points = kTracePoints;
+  return E0_OK;
+}
+
+int e0_model_set_path(e0_model* model, int32_t path) {
+  if (!model || path < E0_PATH_AUTO || path > E0_PATH_PERSISTENT)
+    return fail(E0_ERR_ARG, "e0_model_set_path: bad argument");
+  if (path == E0_PATH_PERSISTENT && !model->dev_table)
+    return fail(E0_ERR_SHAPE, "e0_model_set_path: shapes not supported by the persistent kernel");
+  model->path = path;
+  return E0_OK;
 }
 
 int layer_step(e0_ctx* ctx, e0_model* model, int32_t layer_begin, int32_t layer_end,
@@ -378,6 +465,38 @@ int layer_step(e0_ctx* ctx, e0_model* model, int32_t layer_begin, int32_t layer_
   hipStream_t st = (hipStream_t)stream;
   const int K = dm.K;
   const int cur = token & 1, nxt = (token + 1) & 1;
+  if (model->path != E0_PATH_PHASES && model->dev_table) {
+    StackArgs a;
+    a.dm = dm;
+    a.layers = model->dev_table;
+    a.L = L;
+    a.l0 = layer_begin;
+    a.l1 = layer_end;
+    a.token = token;
+    a.ng = model->ng;
+    a.epoch = ++model->epoch;
+    if (a.epoch == 0) a.epoch = ++model->epoch;  // 0 marks never-written words
+    a.route_idx = state->route_idx;
+    a.route_w = state->route_w;
+    a.exec_idx = state->exec_idx;
+    a.exec_w = state->exec_w;
+    a.head_logits = state->head_logits;
+    a.x_trace = state->x_trace;
+    a.h = h;
+    a.xh = model->xh;
+    a.xg = model->xg;
+    a.xr = model->xr;
+    a.xa = model->xa;
+    a.xl = model->xl;
+    a.fl = model->fl;
+    a.sink_idx = s.sink_idx;
+    a.sink_w = s.sink_w;
+    a.flags = s.flags;
+    a.trace = model->trace;
+    hipError_t e = launch_stack(a, model->grid, st);
+    if (e != hipSuccess) return hip_fail(e, "layer_step (persistent kernel)");
+    return E0_OK;
+  }
   for (int l = layer_begin; l < layer_end; ++l) {
     const e0_layer& Ly = model->layers[l];
     Pool pool;

@@ -16,6 +16,21 @@ __device__ __forceinline__ uint16_t f2h(float v) { return __builtin_bit_cast(uin
 
 __device__ __forceinline__ f16x2 as_h2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
 
+// Load through the global address space. Pointers read out of device tables
+// are generic; a generic (flat) load is also counted by the LDS wait counter,
+// so every LDS wait would stall on it. Weights are always in global memory.
+template <typename T>
+__device__ __forceinline__ T ldg(const T* p) {
+  return *(const __attribute__((address_space(1))) T*)(p);
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 ldg(const uint4* p) {
+  const u32x4 v = *(const __attribute__((address_space(1))) u32x4*)(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ float dot2(f16x2 a, f16x2 b, float c) {
   return __builtin_amdgcn_fdot2(a, b, c, false);
 }

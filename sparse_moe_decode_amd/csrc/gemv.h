@@ -1,0 +1,331 @@
+// Device building blocks shared by the per-phase kernels and the persistent
+// whole-token kernel, so that both compute identical sums in identical order.
+#pragma once
+
+#include "device.h"
+#include "internal.h"
+
+namespace smd {
+
+__device__ __forceinline__ const void* entry_ptr(const void* base, int64_t entry, int64_t stride) {
+  return (const char*)base + entry * stride;
+}
+
+// Resolve routed expert id -> pool entry (through the slot table if any);
+// -1 if the id or the slot is out of range.
+__device__ __forceinline__ int64_t resolve_entry(const Pool& p, int E, int e) {
+  if (e < 0 || e >= E) return -1;
+  int64_t ent = e;
+  if (p.slot_of) ent = ldg(p.slot_of + e);
+  if (ent < 0 || ent >= p.count) return -1;
+  return ent;
+}
+
+// Load the pair-permuted fp16 activation chunk c (32 elements) from LDS.
+__device__ __forceinline__ void load_xchunk(const uint16_t* xs, int c, f16x2* xr) {
+  const uint4* src = reinterpret_cast<const uint4*>(xs + 32 * c);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    uint4 v = src[m];
+    xr[4 * m + 0] = as_h2(v.x);
+    xr[4 * m + 1] = as_h2(v.y);
+    xr[4 * m + 2] = as_h2(v.z);
+    xr[4 * m + 3] = as_h2(v.w);
+  }
+}
+
+// One 16-byte chunk (32 int4 weights) against 32 activations.
+__device__ __forceinline__ float q4_dot32(uint4 wv, const f16x2* xr) {
+  float p = 0.0f;
+  p = q4_dot8(wv.x, xr + 0, p);
+  p = q4_dot8(wv.y, xr + 4, p);
+  p = q4_dot8(wv.z, xr + 8, p);
+  p = q4_dot8(wv.w, xr + 12, p);
+  return p;
+}
+
+// Same with an fp16 hi/lo activation pair (dequantises each word once).
+__device__ __forceinline__ float q4_dot8_hl(uint32_t w, const f16x2* xh, const f16x2* xl,
+                                            float acc) {
+  const uint32_t u = w ^ 0x88888888u;
+  const uint32_t v = u >> 8;
+  const f16x2 k1032 = {(f16)1032.0f, (f16)1032.0f};
+  const f16x2 k16 = {(f16)0.0625f, (f16)0.0625f};
+  const f16x2 k72 = {(f16)72.0f, (f16)72.0f};
+  f16x2 p0 = as_h2((u & 0x000F000Fu) | 0x64006400u) - k1032;
+  f16x2 p1 = as_h2((u & 0x00F000F0u) | 0x64006400u) * k16 - k72;
+  f16x2 p2 = as_h2((v & 0x000F000Fu) | 0x64006400u) - k1032;
+  f16x2 p3 = as_h2((v & 0x00F000F0u) | 0x64006400u) * k16 - k72;
+  acc = dot2(p0, xh[0], acc);
+  acc = dot2(p1, xh[1], acc);
+  acc = dot2(p2, xh[2], acc);
+  acc = dot2(p3, xh[3], acc);
+  acc = dot2(p0, xl[0], acc);
+  acc = dot2(p1, xl[1], acc);
+  acc = dot2(p2, xl[2], acc);
+  acc = dot2(p3, xl[3], acc);
+  return acc;
+}
+
+__device__ __forceinline__ float q4_dot32_hl(uint4 wv, const f16x2* xh, const f16x2* xl) {
+  float p = 0.0f;
+  p = q4_dot8_hl(wv.x, xh + 0, xl + 0, p);
+  p = q4_dot8_hl(wv.y, xh + 4, xl + 4, p);
+  p = q4_dot8_hl(wv.z, xh + 8, xl + 8, p);
+  p = q4_dot8_hl(wv.w, xh + 12, xl + 12, p);
+  return p;
+}
+
+// Block-wide max of |v| over a strided range (kBlock threads).
+__device__ __forceinline__ float block_absmax(const float* v, int n, float* red) {
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) m = fmaxf(m, fabsf(v[i]));
+  m = wave_max(m);
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = m;
+  __syncthreads();
+  float r = 0.0f;
+  for (int j = 0; j < nw; ++j) r = fmaxf(r, red[j]);
+  return r;
+}
+
+// Power-of-two exponent e with max|v| * 2^-e < 2^14 (0 for an all-zero vector).
+__device__ __forceinline__ int hilo_exponent(float absmax) {
+  if (!(absmax > 0.0f)) return 0;
+  int ex;
+  frexpf(absmax, &ex);  // absmax < 2^ex
+  return ex - 14;
+}
+
+
+// ---------------------------------------------------------- row kernels --
+// One aligned group of LG lanes computes one row; li is the lane's index in
+// the group. Each returns the lane's partial sum; the caller reduces over the
+// group with group_sum<LG>.
+
+// Gate and up rows of one expert against the pair-permuted fp16 x in LDS
+// (d = 32 * LG * CPL columns): partial Wg[row] . x and Wu[row] . x.
+template <int LG, int CPL>
+__device__ __forceinline__ void gateup_rowpair(const uint32_t* grow, const uint32_t* urow,
+                                               const uint16_t* gsr, const uint16_t* usr, int G,
+                                               const uint16_t* xs, int li, float& ag,
+                                               float& au) {
+  uint4 wg[CPL], wu[CPL];
+  uint16_t sg[CPL], su[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = li + LG * j;
+    wg[j] = ldg(reinterpret_cast<const uint4*>(grow + 4 * c));
+    wu[j] = ldg(reinterpret_cast<const uint4*>(urow + 4 * c));
+    sg[j] = ldg(gsr + (32 * c) / G);
+    su[j] = ldg(usr + (32 * c) / G);
+  }
+  ag = 0.0f;
+  au = 0.0f;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    f16x2 xr[16];
+    load_xchunk(xs, li + LG * j, xr);
+    ag += h2f(sg[j]) * q4_dot32(wg[j], xr);
+    au += h2f(su[j]) * q4_dot32(wu[j], xr);
+  }
+}
+
+// One int4 row ([I] inputs) against an activation held as pair-permuted fp16
+// hi and lo halves in LDS: partial row . (hi + lo).
+template <int LG, int CPL>
+__device__ __forceinline__ float down_row_hl(const uint32_t* qrow, const uint16_t* srow, int G,
+                                             const uint16_t* hh, const uint16_t* hl, int li) {
+  uint4 wv[CPL];
+  uint16_t sv[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = li + LG * j;
+    wv[j] = ldg(reinterpret_cast<const uint4*>(qrow + 4 * c));
+    sv[j] = ldg(srow + (32 * c) / G);
+  }
+  float part = 0.0f;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    f16x2 xh[16], xl[16];
+    load_xchunk(hh, li + LG * j, xh);
+    load_xchunk(hl, li + LG * j, xl);
+    part += h2f(sv[j]) * q4_dot32_hl(wv[j], xh, xl);
+  }
+  return part;
+}
+
+// fp16 row [cols] against fp16 x (natural order) in LDS: partial dot product
+// over the 8-element chunks li, li + LG, ...
+template <int LG>
+__device__ __forceinline__ float f16_row_dot(const uint16_t* wrow, int cols, const uint16_t* xs,
+                                             int li) {
+  float acc = 0.0f;
+  const int nch = cols / 8;
+  for (int c = li; c < nch; c += LG) {
+    const uint4 wv = ldg(reinterpret_cast<const uint4*>(wrow + 8 * c));
+    const uint4 xv = *reinterpret_cast<const uint4*>(xs + 8 * c);
+    acc = dot2(as_h2(wv.x), as_h2(xv.x), acc);
+    acc = dot2(as_h2(wv.y), as_h2(xv.y), acc);
+    acc = dot2(as_h2(wv.z), as_h2(xv.z), acc);
+    acc = dot2(as_h2(wv.w), as_h2(xv.w), acc);
+  }
+  return acc;
+}
+
+// Same with an fp16 hi/lo activation pair (natural order).
+template <int LG>
+__device__ __forceinline__ float f16_row_dot_hl(const uint16_t* wrow, int cols,
+                                                const uint16_t* xh, const uint16_t* xl, int li) {
+  float acc = 0.0f;
+  const int nch = cols / 8;
+  for (int c = li; c < nch; c += LG) {
+    const uint4 wv = ldg(reinterpret_cast<const uint4*>(wrow + 8 * c));
+    const uint4 a = *reinterpret_cast<const uint4*>(xh + 8 * c);
+    const uint4 b = *reinterpret_cast<const uint4*>(xl + 8 * c);
+    acc = dot2(as_h2(wv.x), as_h2(a.x), acc);
+    acc = dot2(as_h2(wv.y), as_h2(a.y), acc);
+    acc = dot2(as_h2(wv.z), as_h2(a.z), acc);
+    acc = dot2(as_h2(wv.w), as_h2(a.w), acc);
+    acc = dot2(as_h2(wv.x), as_h2(b.x), acc);
+    acc = dot2(as_h2(wv.y), as_h2(b.y), acc);
+    acc = dot2(as_h2(wv.z), as_h2(b.z), acc);
+    acc = dot2(as_h2(wv.w), as_h2(b.w), acc);
+  }
+  return acc;
+}
+
+constexpr int kMaxE = 512;
+
+// LDS written by some lanes of a wave and read by others: the wave's LDS
+// operations complete in issue order, so only compiler reordering must be
+// prevented.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+struct RouteScratch {
+  float sel[kMaxE];
+  float gsc[64];
+  int keep[64];
+};
+
+// Routing of one token's fp32 logits by the tier's family [MW App. A]:
+// softmax-top-K (select the K largest logits, which are the K largest
+// probabilities; weights renormalised over the K) or sigmoid-group (biased
+// scores, top-2-sum group ranking, top-K inside surviving groups, weights
+// s * sigma / (sum sigma + 1e-20)). Ties go to the lower id. Executed by one
+// full wave (lanes 0..63 of the caller); lane 0 writes idx[K] / w[K].
+__device__ __forceinline__ void route_wave(const Dims& dm, const float* lg, const float* bias,
+                                           RouteScratch& rs, int32_t* out_idx, float* out_w,
+                                           int32_t* flags) {
+  float* sel_s = rs.sel;
+  float* gsc_s = rs.gsc;
+  int* keep_s = rs.keep;
+  const int lane = threadIdx.x & 63;
+  const int E = dm.E, K = dm.K;
+  constexpr int kPer = kMaxE / 64;
+
+  float v[kPer], sig[kPer];
+  bool ok[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = lane + 64 * j;
+    ok[j] = e < E;
+    v[j] = ok[j] ? lg[e] : 0.0f;
+    sig[j] = 0.0f;
+  }
+  if (dm.router_kind == E0_ROUTER_SIGMOID_GROUP) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int e = lane + 64 * j;
+      if (!ok[j]) continue;
+      sig[j] = 1.0f / (1.0f + expf(-v[j]));
+      v[j] = sig[j] + (bias ? ldg(bias + e) : 0.0f);
+      sel_s[e] = v[j];
+    }
+    wave_lds_sync();
+    const int per = E / dm.n_groups;
+    if (lane < dm.n_groups) {
+      float m1 = -INFINITY, m2 = -INFINITY;
+      for (int i = 0; i < per; ++i) {
+        const float s = sel_s[lane * per + i];
+        if (s > m1) { m2 = m1; m1 = s; } else if (s > m2) { m2 = s; }
+      }
+      gsc_s[lane] = m1 + m2;
+      keep_s[lane] = 0;
+    }
+    wave_lds_sync();
+    if (lane == 0) {
+      for (int t = 0; t < dm.topk_groups; ++t) {
+        int best = -1;
+        for (int g = 0; g < dm.n_groups; ++g)
+          if (!keep_s[g] && (best < 0 || gsc_s[g] > gsc_s[best])) best = g;
+        keep_s[best] = 1;
+      }
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int e = lane + 64 * j;
+      if (ok[j]) ok[j] = keep_s[e / per] != 0;
+    }
+  }
+
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (lane + 64 * j < E) mx = fmaxf(mx, lg[lane + 64 * j]);
+  mx = wave_max(mx);
+
+  float wsel[8];
+  int isel[8];
+  float denom = 0.0f;
+  for (int k = 0; k < K; ++k) {
+    uint64_t key = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      if (!ok[j]) continue;
+      const uint32_t e = lane + 64 * j;
+      const uint64_t kk = ((uint64_t)f2key(v[j]) << 32) | (0xFFFFFFFFu - e);
+      key = kk > key ? kk : key;
+    }
+    key = wave_max_u64(key);
+    if (key == 0) {  // no candidate left (rejected shapes make this unreachable)
+      if (lane == 0) atomicOr(&flags[FLAG_RANGE], 4);
+      key = 0xFFFFFFFFull;  // decodes to expert 0
+    }
+    const int e = (int)(0xFFFFFFFFu - (uint32_t)key);
+    isel[k] = e;
+    if (dm.router_kind == E0_ROUTER_SIGMOID_GROUP) {
+      wsel[k] = 1.0f / (1.0f + expf(-lg[e]));
+    } else {
+      wsel[k] = expf(lg[e] - mx);
+    }
+    denom += wsel[k];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (lane + 64 * j == e) ok[j] = false;
+  }
+  if (dm.router_kind == E0_ROUTER_SIGMOID_GROUP) {
+    denom += 1e-20f;
+  } else if (!dm.norm_topk) {
+    float z = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (lane + 64 * j < E) z += expf(lg[lane + 64 * j] - mx);
+    denom = wave_sum(z);
+  }
+  if (lane == 0) {
+    for (int k = 0; k < K; ++k) {
+      out_idx[k] = isel[k];
+      const float ww = wsel[k] / denom;
+      out_w[k] = dm.router_kind == E0_ROUTER_SIGMOID_GROUP ? dm.route_scale * ww : ww;
+    }
+  }
+}
+
+}  // namespace smd

@@ -35,6 +35,16 @@ struct HeadW {
   const float* bias;
 };
 
+// One layer of a stack as the persistent kernel reads it (device table).
+struct LayerDev {
+  Pool pool;
+  SharedW sh;
+  const uint16_t* router;
+  const float* router_bias;
+  HeadW head;
+  const uint16_t* attn;
+};
+
 // Tier dimensions as the kernels use them.
 struct Dims {
   int32_t d, E, K, I, Is, P, G, r;
@@ -98,6 +108,35 @@ hipError_t launch_route(const Dims& dm, const float* logits, const float* bias, 
 hipError_t launch_prep(const Dims& dm, const uint16_t* h, const uint16_t* attn, int B,
                        float* hattn, uint16_t* xn, const int32_t* cidx, const float* cw,
                        int32_t* eidx, float* ew, hipStream_t st);
+
+// Persistent whole-token kernel (stack.hip). Exchange buffers hold 8-byte
+// (payload, epoch) words per layer: xh [L][d/2] h_out fp16 pairs, xg [L][ng]
+// SwiGLU outputs + shared bases + LoRA A products, xr [L][E] router logits,
+// xa [L][P+E] head hidden + linear path, xl [L][E] head logits.
+struct StackArgs {
+  Dims dm;
+  const LayerDev* layers;
+  int32_t L, l0, l1, token, ng;
+  uint32_t epoch;
+  int32_t* route_idx;
+  float* route_w;
+  int32_t* exec_idx;
+  float* exec_w;
+  float* head_logits;
+  uint16_t* x_trace;
+  uint16_t* h;
+  uint64_t *xh, *xg, *xr, *xa, *xl;
+  uint32_t* fl;  // arrival flags [L][kExchanges][grid]: epoch of the last post
+  int32_t* sink_idx;
+  float* sink_w;
+  int32_t* flags;
+  uint64_t* trace;  // optional [G][L][kTracePoints] wall-clock stamps (100 MHz)
+};
+constexpr int kTracePoints = 10;
+constexpr int kExchanges = 5;  // h_out, SwiGLU outputs, router logits, head hidden, head logits
+bool stack_supported(const Dims& dm);
+int stack_lds_bytes(const Dims& dm, int ng);
+hipError_t launch_stack(const StackArgs& a, int grid, hipStream_t st);
 
 // Staging: device-side slot policy for one layer, then a gather-copy of the
 // missing bundles from (device-mapped) pinned host memory into HBM slots.

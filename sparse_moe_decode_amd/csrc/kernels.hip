@@ -13,6 +13,7 @@
 // SSD. I counted the bytes it can't stream."; [IE] "Inside Edge0-35B".
 
 #include "device.h"
+#include "gemv.h"
 #include "internal.h"
 
 namespace smd {
@@ -20,97 +21,6 @@ namespace smd {
 namespace {
 
 constexpr int kBlock = 128;  // threads per block of the GEMV kernels (2 waves)
-
-__device__ __forceinline__ const void* entry_ptr(const void* base, int64_t entry, int64_t stride) {
-  return (const char*)base + entry * stride;
-}
-
-// Resolve routed expert id -> pool entry (through the slot table if any);
-// -1 if the id or the slot is out of range.
-__device__ __forceinline__ int64_t resolve_entry(const Pool& p, int E, int e) {
-  if (e < 0 || e >= E) return -1;
-  int64_t ent = e;
-  if (p.slot_of) ent = p.slot_of[e];
-  if (ent < 0 || ent >= p.count) return -1;
-  return ent;
-}
-
-// Load the pair-permuted fp16 activation chunk c (32 elements) from LDS.
-__device__ __forceinline__ void load_xchunk(const uint16_t* xs, int c, f16x2* xr) {
-  const uint4* src = reinterpret_cast<const uint4*>(xs + 32 * c);
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    uint4 v = src[m];
-    xr[4 * m + 0] = as_h2(v.x);
-    xr[4 * m + 1] = as_h2(v.y);
-    xr[4 * m + 2] = as_h2(v.z);
-    xr[4 * m + 3] = as_h2(v.w);
-  }
-}
-
-// One 16-byte chunk (32 int4 weights) against 32 activations.
-__device__ __forceinline__ float q4_dot32(uint4 wv, const f16x2* xr) {
-  float p = 0.0f;
-  p = q4_dot8(wv.x, xr + 0, p);
-  p = q4_dot8(wv.y, xr + 4, p);
-  p = q4_dot8(wv.z, xr + 8, p);
-  p = q4_dot8(wv.w, xr + 12, p);
-  return p;
-}
-
-// Same with an fp16 hi/lo activation pair (dequantises each word once).
-__device__ __forceinline__ float q4_dot8_hl(uint32_t w, const f16x2* xh, const f16x2* xl,
-                                            float acc) {
-  const uint32_t u = w ^ 0x88888888u;
-  const uint32_t v = u >> 8;
-  const f16x2 k1032 = {(f16)1032.0f, (f16)1032.0f};
-  const f16x2 k16 = {(f16)0.0625f, (f16)0.0625f};
-  const f16x2 k72 = {(f16)72.0f, (f16)72.0f};
-  f16x2 p0 = as_h2((u & 0x000F000Fu) | 0x64006400u) - k1032;
-  f16x2 p1 = as_h2((u & 0x00F000F0u) | 0x64006400u) * k16 - k72;
-  f16x2 p2 = as_h2((v & 0x000F000Fu) | 0x64006400u) - k1032;
-  f16x2 p3 = as_h2((v & 0x00F000F0u) | 0x64006400u) * k16 - k72;
-  acc = dot2(p0, xh[0], acc);
-  acc = dot2(p1, xh[1], acc);
-  acc = dot2(p2, xh[2], acc);
-  acc = dot2(p3, xh[3], acc);
-  acc = dot2(p0, xl[0], acc);
-  acc = dot2(p1, xl[1], acc);
-  acc = dot2(p2, xl[2], acc);
-  acc = dot2(p3, xl[3], acc);
-  return acc;
-}
-
-__device__ __forceinline__ float q4_dot32_hl(uint4 wv, const f16x2* xh, const f16x2* xl) {
-  float p = 0.0f;
-  p = q4_dot8_hl(wv.x, xh + 0, xl + 0, p);
-  p = q4_dot8_hl(wv.y, xh + 4, xl + 4, p);
-  p = q4_dot8_hl(wv.z, xh + 8, xl + 8, p);
-  p = q4_dot8_hl(wv.w, xh + 12, xl + 12, p);
-  return p;
-}
-
-// Block-wide max of |v| over a strided range (kBlock threads).
-__device__ float block_absmax(const float* v, int n, float* red) {
-  float m = 0.0f;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) m = fmaxf(m, fabsf(v[i]));
-  m = wave_max(m);
-  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[wave] = m;
-  __syncthreads();
-  float r = 0.0f;
-  for (int j = 0; j < nw; ++j) r = fmaxf(r, red[j]);
-  return r;
-}
-
-// Power-of-two exponent e with max|v| * 2^-e < 2^14 (0 for an all-zero vector).
-__device__ __forceinline__ int hilo_exponent(float absmax) {
-  if (!(absmax > 0.0f)) return 0;
-  int ex;
-  frexpf(absmax, &ex);  // absmax < 2^ex
-  return ex - 14;
-}
 
 // ------------------------------------------------------------- gate / up --
 
@@ -172,24 +82,8 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(GateUpArgs a) {
   const uint16_t* gsr = gs + (int64_t)row * spr;
   const uint16_t* usr = us + (int64_t)row * spr;
 
-  uint4 wg[CPL], wu[CPL];
-  uint16_t sg[CPL], su[CPL];
-#pragma unroll
-  for (int j = 0; j < CPL; ++j) {
-    const int c = li + LG * j;
-    wg[j] = *reinterpret_cast<const uint4*>(grow + 4 * c);
-    wu[j] = *reinterpret_cast<const uint4*>(urow + 4 * c);
-    sg[j] = gsr[(32 * c) / dm.G];
-    su[j] = usr[(32 * c) / dm.G];
-  }
-  float ag = 0.0f, au = 0.0f;
-#pragma unroll
-  for (int j = 0; j < CPL; ++j) {
-    f16x2 xr[16];
-    load_xchunk(xs, li + LG * j, xr);
-    ag += h2f(sg[j]) * q4_dot32(wg[j], xr);
-    au += h2f(su[j]) * q4_dot32(wu[j], xr);
-  }
+  float ag, au;
+  gateup_rowpair<LG, CPL>(grow, urow, gsr, usr, dm.G, xs, li, ag, au);
   if (shared && a.sh.bg) {
     const float* axb = a.ax + (int64_t)b * 3 * a.rmax;
     float lg = 0.0f, lu = 0.0f;
@@ -282,25 +176,9 @@ __global__ __launch_bounds__(kBlock) void k_down(DownArgs a) {
       q = a.sh.down.q;
       s = a.sh.down.s;
     }
-    const uint32_t* qrow = q + (int64_t)row * wpr;
-    const uint16_t* srow = s + (int64_t)row * spr;
-    uint4 wv[CPL];
-    uint16_t sv[CPL];
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const int c = li + LG * j;
-      wv[j] = *reinterpret_cast<const uint4*>(qrow + 4 * c);
-      sv[j] = srow[(32 * c) / dm.G];
-    }
     const uint16_t* hh = hs + (int64_t)k * 2 * I;
-    float part = 0.0f;
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      f16x2 xh[16], xl[16];
-      load_xchunk(hh, li + LG * j, xh);
-      load_xchunk(hh + I, li + LG * j, xl);
-      part += h2f(sv[j]) * q4_dot32_hl(wv[j], xh, xl);
-    }
+    const float part = down_row_hl<LG, CPL>(q + (int64_t)row * wpr, s + (int64_t)row * spr, dm.G,
+                                            hh, hh + I, li);
     acc += coef[k] * part;
   }
   if (a.sh.present && a.sh.bd) {
@@ -368,22 +246,11 @@ __global__ __launch_bounds__(kBlock) void k_gemv16(Gemv16Args a) {
   if (row >= a.rows) return;
 
   const uint16_t* wrow = a.W + (int64_t)row * a.ld;
-  float acc = 0.0f;
-  const int nch = cols / 8;
-  for (int c = li; c < nch; c += LG) {
-    const uint4 wv = *reinterpret_cast<const uint4*>(wrow + 8 * c);
-    const uint4 xv = *reinterpret_cast<const uint4*>(xs16 + 8 * c);
-    acc = dot2(as_h2(wv.x), as_h2(xv.x), acc);
-    acc = dot2(as_h2(wv.y), as_h2(xv.y), acc);
-    acc = dot2(as_h2(wv.z), as_h2(xv.z), acc);
-    acc = dot2(as_h2(wv.w), as_h2(xv.w), acc);
-    if constexpr (XF32) {
-      const uint4 xl = *reinterpret_cast<const uint4*>(xs16 + cols + 8 * c);
-      acc = dot2(as_h2(wv.x), as_h2(xl.x), acc);
-      acc = dot2(as_h2(wv.y), as_h2(xl.y), acc);
-      acc = dot2(as_h2(wv.z), as_h2(xl.z), acc);
-      acc = dot2(as_h2(wv.w), as_h2(xl.w), acc);
-    }
+  float acc;
+  if constexpr (XF32) {
+    acc = f16_row_dot_hl<LG>(wrow, cols, xs16, xs16 + cols, li);
+  } else {
+    acc = f16_row_dot<LG>(wrow, cols, xs16, li);
   }
   acc *= scale;
   if (a.cur) {
@@ -435,123 +302,12 @@ struct RouteArgs {
   int32_t* flags;
 };
 
-constexpr int kMaxE = 512;
-
-// Routing of one token's fp32 logits by the tier's family [MW App. A]:
-// softmax-top-K (select the K largest logits, which are the K largest
-// probabilities; weights renormalised over the K) or sigmoid-group (biased
-// scores, top-2-sum group ranking, top-K inside surviving groups, weights
-// s * sigma / (sum sigma + 1e-20)). Ties go to the lower id. One wave per
-// token.
+// Routing of one token's fp32 logits (one wave per token) [MW App. A].
 __global__ __launch_bounds__(64) void k_route(RouteArgs a) {
-  __shared__ float sel_s[kMaxE];
-  __shared__ float gsc_s[64];
-  __shared__ int keep_s[64];
-  const Dims& dm = a.dm;
+  __shared__ RouteScratch rs;
   const int b = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int E = dm.E, K = dm.K;
-  constexpr int kPer = kMaxE / 64;
-  const float* lg = a.logits + (int64_t)b * E;
-
-  float v[kPer], sig[kPer];
-  bool ok[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int e = lane + 64 * j;
-    ok[j] = e < E;
-    v[j] = ok[j] ? lg[e] : 0.0f;
-    sig[j] = 0.0f;
-  }
-  if (dm.router_kind == E0_ROUTER_SIGMOID_GROUP) {
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int e = lane + 64 * j;
-      if (!ok[j]) continue;
-      sig[j] = 1.0f / (1.0f + expf(-v[j]));
-      v[j] = sig[j] + (a.bias ? a.bias[e] : 0.0f);
-      sel_s[e] = v[j];
-    }
-    __syncthreads();
-    const int per = E / dm.n_groups;
-    if (lane < dm.n_groups) {
-      float m1 = -INFINITY, m2 = -INFINITY;
-      for (int i = 0; i < per; ++i) {
-        const float s = sel_s[lane * per + i];
-        if (s > m1) { m2 = m1; m1 = s; } else if (s > m2) { m2 = s; }
-      }
-      gsc_s[lane] = m1 + m2;
-      keep_s[lane] = 0;
-    }
-    __syncthreads();
-    if (lane == 0) {
-      for (int t = 0; t < dm.topk_groups; ++t) {
-        int best = -1;
-        for (int g = 0; g < dm.n_groups; ++g)
-          if (!keep_s[g] && (best < 0 || gsc_s[g] > gsc_s[best])) best = g;
-        keep_s[best] = 1;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int e = lane + 64 * j;
-      if (ok[j]) ok[j] = keep_s[e / per] != 0;
-    }
-  }
-
-  float mx = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j)
-    if (lane + 64 * j < E) mx = fmaxf(mx, lg[lane + 64 * j]);
-  mx = wave_max(mx);
-
-  float wsel[8];
-  int isel[8];
-  float denom = 0.0f;
-  for (int k = 0; k < K; ++k) {
-    uint64_t key = 0;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      if (!ok[j]) continue;
-      const uint32_t e = lane + 64 * j;
-      const uint64_t kk = ((uint64_t)f2key(v[j]) << 32) | (0xFFFFFFFFu - e);
-      key = kk > key ? kk : key;
-    }
-    key = wave_max_u64(key);
-    if (key == 0) {  // no candidate left (rejected shapes make this unreachable)
-      if (lane == 0) atomicOr(&a.flags[FLAG_RANGE], 4);
-      key = 0xFFFFFFFFull;  // decodes to expert 0
-    }
-    const int e = (int)(0xFFFFFFFFu - (uint32_t)key);
-    isel[k] = e;
-    if (dm.router_kind == E0_ROUTER_SIGMOID_GROUP) {
-      wsel[k] = 1.0f / (1.0f + expf(-lg[e]));
-    } else {
-      wsel[k] = expf(lg[e] - mx);
-    }
-    denom += wsel[k];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j)
-      if (lane + 64 * j == e) ok[j] = false;
-  }
-  if (dm.router_kind == E0_ROUTER_SIGMOID_GROUP) {
-    denom += 1e-20f;
-  } else if (!dm.norm_topk) {
-    float z = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j)
-      if (lane + 64 * j < E) z += expf(lg[lane + 64 * j] - mx);
-    denom = wave_sum(z);
-  }
-  if (lane == 0) {
-    for (int k = 0; k < K; ++k) {
-      a.idx[(int64_t)b * K + k] = isel[k];
-      const float ww = wsel[k] / denom;
-      a.w[(int64_t)b * K + k] =
-          dm.router_kind == E0_ROUTER_SIGMOID_GROUP ? dm.route_scale * ww : ww;
-    }
-  }
+  route_wave(a.dm, a.logits + (int64_t)b * a.dm.E, a.bias, rs, a.idx + (int64_t)b * a.dm.K,
+             a.w + (int64_t)b * a.dm.K, a.flags);
 }
 
 // --------------------------------------------------------------- prepare --

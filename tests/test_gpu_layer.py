@@ -24,7 +24,8 @@ def api():
     return _api
 
 
-def _run_and_check(api, orc, tier, roles, seed, T, check_layers, rho=0.5, zero_mean=False):
+def _run_and_check(api, orc, tier, roles, seed, T, check_layers, rho=0.5, zero_mean=False,
+                   path="auto"):
     import torch
     from sparse_moe_decode_amd import workloads as wl
     dm = synth.dims(tier)
@@ -44,6 +45,8 @@ def _run_and_check(api, orc, tier, roles, seed, T, check_layers, rho=0.5, zero_m
                            head=wl.tree_to_dev(lw["head"])))
     ctx = api.Context(dm, max_tokens=4)
     model = api.Model(ctx, layers)
+    model.set_path({"auto": api.PATH_AUTO, "phases": api.PATH_PHASES,
+                    "persistent": api.PATH_PERSISTENT}[path])
     state = api.State(dm, L)
     idx0, w0 = wl.initial_routing(tier, seed, L)
     state.route_idx[0].copy_(torch.from_numpy(idx0))
@@ -53,7 +56,7 @@ def _run_and_check(api, orc, tier, roles, seed, T, check_layers, rho=0.5, zero_m
     prev_exec = None
     h = torch.empty((L + 1, dm["d"]), dtype=torch.float16, device="cuda")
     for t in range(T):
-        announce("layer_step", tier, f"L={L}", f"token {t}")
+        announce("layer_step", tier, path, f"L={L}", f"token {t}")
         h[0].copy_(torch.from_numpy(toks[t]))
         api.layer_step(ctx, model, 0, L, state, t, h)
         assert api.device_status(ctx) == 0
@@ -66,7 +69,7 @@ def _run_and_check(api, orc, tier, roles, seed, T, check_layers, rho=0.5, zero_m
                       host(state.route_w[nxt]).copy(),
                       host(state.head_logits).copy())
         prev_exec = exec_idx
-    print(f"{tier} L={L}: {checker.steps} layer-steps checked, worst error ratio "
+    print(f"{tier} {path} L={L}: {checker.steps} layer-steps checked, worst error ratio "
           f"{checker.worst:.3f}, re-anchored router sets {checker.reanchored}, "
           f"x elements one ulp off {checker.x_ulp_diffs}")
     model.close()
@@ -74,25 +77,29 @@ def _run_and_check(api, orc, tier, roles, seed, T, check_layers, rho=0.5, zero_m
     return checker
 
 
-@pytest.mark.parametrize("tier,T", [("tiny", 24), ("8b", 5), ("35b", 5)])
-def test_layer_step_two_layers(api, orc, tier, T):
+@pytest.mark.parametrize("tier,T,path", [("tiny", 24, "phases"), ("8b", 5, "phases"),
+                                         ("35b", 5, "phases"), ("8b", 5, "persistent"),
+                                         ("35b", 5, "persistent")])
+def test_layer_step_two_layers(api, orc, tier, T, path):
     """Layer 0 runs its router and owns a head predicting layer 1; layer 1
     consumes that prediction and owns a head with no consumer."""
     roles = [dict(router=True, head=True), dict(router=False, head=True)]
-    _run_and_check(api, orc, tier, roles, seed=31, T=T, check_layers=[0, 1])
+    _run_and_check(api, orc, tier, roles, seed=31, T=T, check_layers=[0, 1], path=path)
 
 
 @pytest.mark.timeout(900)
-def test_layer_step_stack_35b(api, orc):
+@pytest.mark.parametrize("path", ["persistent", "phases"])
+def test_layer_step_stack_35b(api, orc, path):
     """Full 35B stack (40 layers, heads on 6-38) in the benchmark's launch
     configuration; every layer-step of the first tokens is checked."""
     roles = synth.stack_roles("35b")
     _run_and_check(api, orc, "35b", roles, seed=3, T=3, check_layers=list(range(40)),
-                   zero_mean=True)
+                   zero_mean=True, path=path)
 
 
 @pytest.mark.timeout(600)
-def test_layer_step_stack_8b(api, orc):
+@pytest.mark.parametrize("path", ["persistent", "phases"])
+def test_layer_step_stack_8b(api, orc, path):
     roles = synth.stack_roles("8b")
     _run_and_check(api, orc, "8b", roles, seed=5, T=3, check_layers=list(range(24)),
-                   zero_mean=True)
+                   zero_mean=True, path=path)
