@@ -215,13 +215,16 @@ enum { E0_PATH_AUTO = 0, E0_PATH_PHASES = 1, E0_PATH_PERSISTENT = 2 };
 int e0_model_set_path(e0_model* model, int32_t path);
 
 /* Phase tracing of the persistent kernel (observability; off by default).
- * trace: device uint64 [grid][L][points] (shape from e0_model_trace_shape),
- * or NULL to turn tracing off. Thread 0 of each workgroup writes the 100 MHz
- * wall clock at each phase boundary of each layer it runs: layer start, h
- * gathered, x normed, routed, gate/up done, head fc1 done, SwiGLU outputs
- * gathered, shared expert done, down done, layer end. */
+ * trace: device uint64 [grid][rows][points] (shape from e0_model_trace_shape;
+ * rows = L + 1), or NULL to turn tracing off. Thread 0 of each workgroup
+ * writes the 100 MHz wall clock at each phase boundary. Row l < L (a layer):
+ * layer start, h gathered, x normed, routed, gate/up published, down and
+ * LoRA loads issued, SwiGLU outputs gathered, shared expert and hi/lo copies
+ * done, h_out published, next layer's loads issued. Row L (the heads, after
+ * the last layer): start, fc1/linear rows published, activations gathered,
+ * fc2 rows published, head routing done. */
 int e0_model_set_trace(e0_model* model, uint64_t* trace);
-int32_t e0_model_trace_shape(e0_model* model, int32_t* grid, int32_t* points);
+int32_t e0_model_trace_shape(e0_model* model, int32_t* grid, int32_t* rows, int32_t* points);
 
 /* Device-resident decode state, caller-owned, L = number of model layers:
  *   route_idx / route_w  int32 / fp32 [2][L][K]: routing consumed at token t

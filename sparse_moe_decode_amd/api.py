@@ -85,7 +85,7 @@ _lib.e0_model_create.argtypes = [_p, C.POINTER(e0_layer), _i32, C.POINTER(_p)]
 _lib.e0_model_destroy.argtypes = [_p]
 _lib.e0_model_set_path.argtypes = [_p, _i32]
 _lib.e0_model_set_trace.argtypes = [_p, _p]
-_lib.e0_model_trace_shape.argtypes = [_p, C.POINTER(_i32), C.POINTER(_i32)]
+_lib.e0_model_trace_shape.argtypes = [_p, C.POINTER(_i32), C.POINTER(_i32), C.POINTER(_i32)]
 _lib.layer_step.argtypes = [_p, _p, _i32, _i32, C.POINTER(e0_state), _i32, _p, _p]
 _lib.e0_bundle_bytes.argtypes = [C.POINTER(e0_spec)]
 _lib.e0_bundle_bytes.restype = _i64
@@ -151,7 +151,8 @@ class Context:
         self.max_tokens = max_tokens
 
     def close(self):
-        if getattr(self, "handle", None):
+        # at interpreter exit the module globals may already be gone
+        if getattr(self, "handle", None) and _lib is not None:
             _lib.e0_destroy(self.handle)
             self.handle = None
 
@@ -259,14 +260,14 @@ class Model:
         self._keep = layers
 
     def enable_trace(self, on: bool = True):
-        """Allocate (or drop) the phase-trace buffer; returns it ([grid, L, points])."""
+        """Allocate (or drop) the phase-trace buffer; returns it ([grid, L + 1, points])."""
         if not on:
             _check(_lib.e0_model_set_trace(self.handle, None))
             self.trace = None
             return None
-        g, pts = _i32(), _i32()
-        _check(_lib.e0_model_trace_shape(self.handle, C.byref(g), C.byref(pts)))
-        self.trace = torch.zeros((max(g.value, 1), self.n_layers, pts.value), dtype=torch.int64,
+        g, rows, pts = _i32(), _i32(), _i32()
+        _check(_lib.e0_model_trace_shape(self.handle, C.byref(g), C.byref(rows), C.byref(pts)))
+        self.trace = torch.zeros((max(g.value, 1), rows.value, pts.value), dtype=torch.int64,
                                  device="cuda")
         _check(_lib.e0_model_set_trace(self.handle, self.trace.data_ptr()))
         return self.trace
@@ -276,7 +277,8 @@ class Model:
         _check(_lib.e0_model_set_path(self.handle, path))
 
     def close(self):
-        if getattr(self, "handle", None):
+        # at interpreter exit the module globals may already be gone
+        if getattr(self, "handle", None) and _lib is not None:
             _lib.e0_model_destroy(self.handle)
             self.handle = None
 
@@ -324,7 +326,8 @@ class Stager:
         self._keep = (host_pool, hbm_slots, slot_of, slot_expert)
 
     def close(self):
-        if getattr(self, "handle", None):
+        # at interpreter exit the module globals may already be gone
+        if getattr(self, "handle", None) and _lib is not None:
             _lib.e0_stager_destroy(self.handle)
             self.handle = None
 

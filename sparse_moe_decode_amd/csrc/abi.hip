@@ -434,9 +434,10 @@ int e0_model_set_trace(e0_model* model, uint64_t* trace) {
   return E0_OK;
 }
 
-int32_t e0_model_trace_shape(e0_model* model, int32_t* grid, int32_t* points) {
+int32_t e0_model_trace_shape(e0_model* model, int32_t* grid, int32_t* rows, int32_t* points) {
   if (!model) return fail(E0_ERR_ARG, "e0_model_trace_shape: null model");
   if (grid) *grid = model->grid;
+  if (rows) *rows = (int32_t)model->layers.size() + 1;
   if (points) *points = kTracePoints;
   return E0_OK;
 }
@@ -467,6 +468,9 @@ int layer_step(e0_ctx* ctx, e0_model* model, int32_t layer_begin, int32_t layer_
   const int cur = token & 1, nxt = (token + 1) & 1;
   if (model->path != E0_PATH_PHASES && model->dev_table) {
     StackArgs a;
+    a.n_heads = 0;
+    for (int l = layer_begin; l < layer_end; ++l)
+      if (model->layers[l].head.fc1) ++a.n_heads;
     a.dm = dm;
     a.layers = model->dev_table;
     a.L = L;
@@ -493,9 +497,13 @@ int layer_step(e0_ctx* ctx, e0_model* model, int32_t layer_begin, int32_t layer_
     a.sink_w = s.sink_w;
     a.flags = s.flags;
     a.trace = model->trace;
-    hipError_t e = launch_stack(a, model->grid, st);
-    if (e != hipSuccess) return hip_fail(e, "layer_step (persistent kernel)");
-    return E0_OK;
+    if (stack_launchable(a, model->grid)) {
+      hipError_t e = launch_stack(a, model->grid, st);
+      if (e != hipSuccess) return hip_fail(e, "layer_step (persistent kernel)");
+      return E0_OK;
+    }
+    if (model->path == E0_PATH_PERSISTENT)
+      return fail(E0_ERR_SHAPE, "layer_step: this layer range does not fit the persistent kernel");
   }
   for (int l = layer_begin; l < layer_end; ++l) {
     const e0_layer& Ly = model->layers[l];

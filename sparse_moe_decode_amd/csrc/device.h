@@ -89,6 +89,63 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+template <int LG>
+__device__ __forceinline__ float group_max(float v) {
+  if constexpr (LG >= 2) v = fmaxf(v, dpp_f<0xB1>(v));
+  if constexpr (LG >= 4) v = fmaxf(v, dpp_f<0x4E>(v));
+  if constexpr (LG >= 8) v = fmaxf(v, dpp_f<0x141>(v));
+  if constexpr (LG >= 16) v = fmaxf(v, dpp_f<0x140>(v));
+  return v;
+}
+
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Wave-wide sum / max without LDS traffic: DPP inside each 16-lane row, then
+// the four row results are read into scalars. The whole wave must be active.
+__device__ __forceinline__ float wave_sum_rows(float v) {
+  v = group_sum<16>(v);
+  return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+}
+
+__device__ __forceinline__ float wave_max_rows(float v) {
+  v = group_max<16>(v);
+  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)),
+               fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ void max_step_u64(uint32_t& hi, uint32_t& lo) {
+  const uint32_t oh = dpp_u<CTRL>(hi), ol = dpp_u<CTRL>(lo);
+  const bool gt = oh > hi || (oh == hi && ol > lo);
+  hi = gt ? oh : hi;
+  lo = gt ? ol : lo;
+}
+
+// Wave-wide maximum of a 64-bit key (same result as wave_max_u64); the whole
+// wave must be active.
+__device__ __forceinline__ uint64_t wave_max_u64_rows(uint64_t k) {
+  uint32_t hi = (uint32_t)(k >> 32), lo = (uint32_t)k;
+  max_step_u64<0xB1>(hi, lo);
+  max_step_u64<0x4E>(hi, lo);
+  max_step_u64<0x141>(hi, lo);
+  max_step_u64<0x140>(hi, lo);
+  uint64_t best = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint64_t v = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, 16 * r) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)lo, 16 * r);
+    best = v > best ? v : best;
+  }
+  return best;
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 __device__ __forceinline__ float gelu_erf(float z) {
   return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));

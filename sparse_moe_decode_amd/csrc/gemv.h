@@ -218,7 +218,7 @@ struct RouteScratch {
 // probabilities; weights renormalised over the K) or sigmoid-group (biased
 // scores, top-2-sum group ranking, top-K inside surviving groups, weights
 // s * sigma / (sum sigma + 1e-20)). Ties go to the lower id. Executed by one
-// full wave (lanes 0..63 of the caller); lane 0 writes idx[K] / w[K].
+// full wave (all 64 lanes active); lane 0 writes idx[K] / w[K].
 __device__ __forceinline__ void route_wave(const Dims& dm, const float* lg, const float* bias,
                                            RouteScratch& rs, int32_t* out_idx, float* out_w,
                                            int32_t* flags) {
@@ -279,7 +279,7 @@ __device__ __forceinline__ void route_wave(const Dims& dm, const float* lg, cons
 #pragma unroll
   for (int j = 0; j < kPer; ++j)
     if (lane + 64 * j < E) mx = fmaxf(mx, lg[lane + 64 * j]);
-  mx = wave_max(mx);
+  mx = wave_max_rows(mx);
 
   float wsel[8];
   int isel[8];
@@ -293,7 +293,7 @@ __device__ __forceinline__ void route_wave(const Dims& dm, const float* lg, cons
       const uint64_t kk = ((uint64_t)f2key(v[j]) << 32) | (0xFFFFFFFFu - e);
       key = kk > key ? kk : key;
     }
-    key = wave_max_u64(key);
+    key = wave_max_u64_rows(key);
     if (key == 0) {  // no candidate left (rejected shapes make this unreachable)
       if (lane == 0) atomicOr(&flags[FLAG_RANGE], 4);
       key = 0xFFFFFFFFull;  // decodes to expert 0
@@ -317,7 +317,7 @@ __device__ __forceinline__ void route_wave(const Dims& dm, const float* lg, cons
 #pragma unroll
     for (int j = 0; j < kPer; ++j)
       if (lane + 64 * j < E) z += expf(lg[lane + 64 * j] - mx);
-    denom = wave_sum(z);
+    denom = wave_sum_rows(z);
   }
   if (lane == 0) {
     for (int k = 0; k < K; ++k) {

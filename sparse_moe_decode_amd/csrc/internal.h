@@ -117,6 +117,7 @@ struct StackArgs {
   Dims dm;
   const LayerDev* layers;
   int32_t L, l0, l1, token, ng;
+  int32_t n_heads;  // layers of [l0, l1) with a head
   uint32_t epoch;
   int32_t* route_idx;
   float* route_w;
@@ -130,12 +131,15 @@ struct StackArgs {
   int32_t* sink_idx;
   float* sink_w;
   int32_t* flags;
-  uint64_t* trace;  // optional [G][L][kTracePoints] wall-clock stamps (100 MHz)
+  uint64_t* trace;  // optional [G][L+1][kTracePoints] wall-clock stamps (100 MHz)
 };
 constexpr int kTracePoints = 10;
 constexpr int kExchanges = 5;  // h_out, SwiGLU outputs, router logits, head hidden, head logits
 bool stack_supported(const Dims& dm);
-int stack_lds_bytes(const Dims& dm, int ng);
+// Whether one launch over [l0, l1) (with a.n_heads head layers) fits the
+// kernel's fixed per-workgroup plans on `grid` workgroups.
+bool stack_launchable(const StackArgs& a, int grid);
+int stack_lds_bytes(const Dims& dm, int ng, int n_layers);
 hipError_t launch_stack(const StackArgs& a, int grid, hipStream_t st);
 
 // Staging: device-side slot policy for one layer, then a gather-copy of the

@@ -11,13 +11,15 @@
 //      the previous token's head wrote;
 //   3. gate/up rows of the routed experts and the shared expert, and the
 //      LoRA A products of the shared gate/up, spread over the chip;
-//   4. head fc1 (erf-GELU) and linear-path rows, spread over the chip;
-//   5. every workgroup gathers the SwiGLU outputs, finishes the shared
-//      expert (LoRA B of gate/up, SwiGLU, LoRA A of down) redundantly;
-//   6. down rows with the weighted combine, shared expert and down LoRA;
-//      h_{l+1} = fp16(h_a + y) is published;
-//   7. head fc2 rows; the routing of the head logits runs after the last
-//      layer and writes the prediction read by the next token.
+//   4. every workgroup gathers the SwiGLU outputs and finishes the shared
+//      expert (LoRA B of gate/up, SwiGLU, LoRA A of down) itself;
+//   5. down rows with the weighted combine, shared expert and down LoRA;
+//      h_{l+1} = fp16(h_a + y) is published.
+// The prerouter heads are not on this chain: a head's output is consumed by
+// the next token only. Each workgroup keeps x_l of the few head layers whose
+// rows it owns; after the last layer every workgroup streams its share of
+// all heads' fc1 and linear-path rows, then of their fc2 rows, and the
+// routing of each head's logits writes the next token's prediction.
 //
 // Cross-workgroup data moves as 8-byte words (32-bit payload, 32-bit epoch)
 // written and polled with agent-scope relaxed atomics (coherent across the
@@ -38,6 +40,13 @@ constexpr int kThreads = 256;
 constexpr int kLG = 16;
 constexpr int kGroups = kThreads / kLG;
 constexpr uint64_t kSpinLimit = 20000000ull;  // 0.2 s of the 100 MHz wall clock
+constexpr int kMaxL = 64;      // layers per launch (routing tables in LDS)
+constexpr int kNR = 4;         // fp16 rows per workgroup per block job (router, LoRA A)
+constexpr int kMaxExp = 9;     // experts per down row: K <= 8 routed + the shared expert
+constexpr int kRank = 16;      // LoRA rank of this kernel (or no LoRA at all)
+constexpr int kHX = 4;         // head layers one workgroup keeps x / fc2 activations of
+constexpr int kF2R = 4;        // fc2 rounds (kGroups rows each) per workgroup
+constexpr int kCPF = 4;        // 16-byte chunks per lane of an fc2 row (P <= 512)
 
 __device__ __forceinline__ uint64_t ld64(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -74,7 +83,7 @@ __device__ __forceinline__ bool wait_expired(uint64_t t0, int32_t* flags, int* a
 
 // All threads of the block gather n words src[0..n) of epoch ep into dst.
 template <int U>
-__device__ void ll_gather(const uint64_t* src, int n, uint32_t ep, uint32_t* dst,
+__device__ __forceinline__ void ll_gather(const uint64_t* src, int n, uint32_t ep, uint32_t* dst,
                           int32_t* flags, int* abort_lds) {
   const uint64_t t0 = wall_clock64();
   uint32_t polls = 0;
@@ -106,10 +115,11 @@ __device__ void ll_gather(const uint64_t* src, int n, uint32_t ep, uint32_t* dst
   }
 }
 
-// Phase timestamp of this workgroup (thread 0) when tracing is on.
-__device__ __forceinline__ void stamp(const StackArgs& a, int l, int k) {
+// Phase timestamp of this workgroup (thread 0) when tracing is on. Rows
+// 0..L-1 are layers, row L the head phase after the last layer.
+__device__ __forceinline__ void stamp(const StackArgs& a, int row, int k) {
   if (a.trace && threadIdx.x == 0)
-    a.trace[((int64_t)blockIdx.x * a.L + l) * kTracePoints + k] = wall_clock64();
+    a.trace[((int64_t)blockIdx.x * (a.L + 1) + row) * kTracePoints + k] = wall_clock64();
 }
 
 enum { XH = 0, XG = 1, XR = 2, XA = 3, XL = 4 };
@@ -160,40 +170,42 @@ __device__ __forceinline__ void wait_all(const StackArgs& a, int l, int x, int* 
   __syncthreads();
 }
 
+// Contiguous share [beg, end) of n items for workgroup c of G (n * G < 2^32).
 __device__ __forceinline__ void split(int n, int G, int c, int& beg, int& end) {
-  beg = (int)((int64_t)n * c / G);
-  end = (int)((int64_t)n * (c + 1) / G);
+  beg = (int)((uint32_t)n * (uint32_t)c / (uint32_t)G);
+  end = (int)((uint32_t)n * (uint32_t)(c + 1) / (uint32_t)G);
 }
 
 // Block-wide sum (all threads return the total).
 __device__ __forceinline__ float block_sum(float v, float* red) {
-  v = wave_sum(v);
+  v = wave_sum_rows(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  float t = 0.0f;
-  for (int j = 0; j < kThreads / 64; ++j) t += red[j];
-  return t;
+  return (red[0] + red[1]) + (red[2] + red[3]);
 }
-
-constexpr int kMaxL = 64;      // layers per launch (routing tables in LDS)
-constexpr int kNR = 4;         // fp16 rows per workgroup per job (router, head, fc2, LoRA A)
-constexpr int kLoraRegs = 12;  // 16-byte chunks per thread of the LoRA matrices (Is*r <= 8192)
 
 // Small per-layer values kept in LDS.
 struct Misc {
   int32_t ridx[8];
   float rw[8];
   int64_t ent[16];
+  // down-projection bases and combine weight of expert slot k (routed k < K,
+  // shared k == K); null / 0 when the slot is unused or its id did not resolve
+  const uint32_t* dq[kMaxExp];
+  const uint16_t* dsc[kMaxExp];
   float coef[16];
-  float emax[16];
-  float ad[64];
+  float csc[kMaxExp][16];      // power-of-two scale of each 32-element hi/lo chunk
+  float ad[kRank];             // A_down . h_shared
+  float red16[kRank][kGroups];
+  float hsc[kHX][16];          // scales of the fc2 activation chunks (per lane)
   float red[4 * kNR];
-  float rows[kNR];   // results of the block fp16 row jobs
-  float gath[kNR * 16];
-  float ha_scale;
+  float rows[kNR];             // results of the block fp16 row jobs
   int abort;
-  uint16_t hstage[512];  // h_out rows of this workgroup (<= 512)
+  int n_heads;
+  uint16_t hstage[512];        // h_out rows of this workgroup (<= 512)
+  int32_t hl_list[kMaxL];      // layer of head h (launch order)
+  int32_t hidx_of[kMaxL];      // head index of layer step s, or -1
   int32_t ridx_all[kMaxL * 8];
   float rw_all[kMaxL * 8];
   int32_t pidx_all[kMaxL * 8];
@@ -203,11 +215,14 @@ struct Misc {
 
 struct Lds {
   // byte offsets into dynamic LDS
-  int hattn, xperm, xnat, land, hk, ha, lora, misc;
+  int hattn, xperm, xnat, land, hk, ha, hx, misc, lay;
   int bytes;
 };
 
-__host__ __device__ inline Lds lds_layout(const Dims& dm, int ng) {
+// nl: layers of the launch; their device-table entries are copied to LDS so
+// that no pointer of the table is read from global memory inside the layer
+// loop (such a read would wait on every load issued before it).
+__host__ __device__ inline Lds lds_layout(const Dims& dm, int ng, int nl) {
   auto up = [](int b) { return (b + 15) & ~15; };
   Lds o;
   int off = 0;
@@ -217,12 +232,13 @@ __host__ __device__ inline Lds lds_layout(const Dims& dm, int ng) {
   int land = ng;
   if (dm.d / 2 > land) land = dm.d / 2;
   if (dm.E > land) land = dm.E;
-  if (dm.P + dm.E > land) land = dm.P + dm.E;
+  if (kHX * (dm.P + dm.E) > land) land = kHX * (dm.P + dm.E);
   o.land = off; off += up(land * 4);
   o.hk = off; off += up((dm.K + 1) * 2 * dm.I * 2);
-  o.ha = off; off += up(dm.P * 2 * 2);
-  o.lora = off; off += up(3 * dm.Is * dm.r * 2);
+  o.ha = off; off += up(kHX * 2 * dm.P * 2);
+  o.hx = off; off += up(kHX * dm.d * 2);
   o.misc = off; off += up((int)sizeof(Misc));
+  o.lay = off; off += up(nl * (int)sizeof(LayerDev));
   o.bytes = off;
   return o;
 }
@@ -258,7 +274,7 @@ __device__ __forceinline__ void block_rows_reduce(float (&p)[NR], int nr, Misc& 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int j = 0; j < NR; ++j)
-    if (j < nr) p[j] = wave_sum(p[j]);
+    if (j < nr) p[j] = wave_sum_rows(p[j]);
   if (lane == 0)
 #pragma unroll
     for (int j = 0; j < NR; ++j) ms.red[wave * NR + j] = p[j];
@@ -280,21 +296,6 @@ __device__ __forceinline__ void f16rows_finish(const F16Rows<NR>& R, int nr, int
   float p[NR];
 #pragma unroll
   for (int j = 0; j < NR; ++j) p[j] = dot8_h(R.w[j], xv, 0.0f);
-  block_rows_reduce<NR>(p, nr, ms);
-}
-
-// rows . (xh + xl) with an fp16 hi/lo activation in LDS.
-template <int NR>
-__device__ __forceinline__ void f16rows_finish_hl(const F16Rows<NR>& R, int nr, int cols,
-                                                  const uint16_t* xh, const uint16_t* xl,
-                                                  Misc& ms) {
-  const int t = threadIdx.x;
-  const bool in = t < cols / 8;
-  const uint4 a = in ? *reinterpret_cast<const uint4*>(xh + 8 * t) : make_uint4(0, 0, 0, 0);
-  const uint4 b = in ? *reinterpret_cast<const uint4*>(xl + 8 * t) : make_uint4(0, 0, 0, 0);
-  float p[NR];
-#pragma unroll
-  for (int j = 0; j < NR; ++j) p[j] = dot8_h(R.w[j], b, dot8_h(R.w[j], a, 0.0f));
   block_rows_reduce<NR>(p, nr, ms);
 }
 
@@ -360,10 +361,10 @@ __device__ __forceinline__ void gu_issue(GuRegs<CPL, IPG>& R, const LayerDev& Ly
 }
 
 template <int CPL, int IPG>
-__device__ __forceinline__ void gu_finish(const GuRegs<CPL, IPG>& R, const LayerDev& Ly,
-                                          const Dims& dm, const Misc& ms, int n_rt, int Is,
-                                          const GuPlan& pl, int grp, int li,
-                                          const uint16_t* xperm, uint64_t* xg, uint32_t ep) {
+__device__ __forceinline__ void gu_finish(const GuRegs<CPL, IPG>& R, const Dims& dm,
+                                          const Misc& ms, int n_rt, int Is, const GuPlan& pl,
+                                          int grp, int li, const uint16_t* xperm, uint64_t* xg,
+                                          uint32_t ep) {
 #pragma unroll
   for (int j = 0; j < IPG; ++j) {
     const int it = pl.ib + grp + kGroups * j;
@@ -394,19 +395,57 @@ __device__ __forceinline__ void gu_finish(const GuRegs<CPL, IPG>& R, const Layer
 }
 
 // ---- down rows: every expert's chunk of one row per lane group ------------
-constexpr int kMaxExp = 9;
-
 struct DownRegs {
   uint4 w[kMaxExp];
   uint16_t s[kMaxExp];
-  uint4 bd[4];  // LoRA B of the down projection, r fp16 = r/8 chunks (r <= 32)
+  uint4 bd[kRank / 8];  // LoRA B of the down projection, row drow (lane 0 of the group)
 };
+
+// Shared-expert LoRA matrices, thread t's part: rows 2t and 2t+1 of B_gate
+// and B_up ([Is, r]), and columns 2t, 2t+1 of A_down ([r, Is]).
+struct LoraRegs {
+  uint4 bg[kRank / 4], bu[kRank / 4];
+  uint32_t ad[kRank];
+};
+
+// B row (kRank fp16 in two 16-byte chunks) . a (kRank fp32 in LDS).
+__device__ __forceinline__ float lora_row(uint4 c0, uint4 c1, const float* a) {
+  const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  float s = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    s += h2f((uint16_t)(w[q] & 0xFFFF)) * a[2 * q];
+    s += h2f((uint16_t)(w[q] >> 16)) * a[2 * q + 1];
+  }
+  return s;
+}
+
+// Lane li of a 16-lane group holds elements 32c + 2li and 32c + 2li + 1 of an
+// I-vector. The group converts chunk c to fp16 hi + lo scaled by a power of
+// two 2^-e chosen from the chunk's max |v|, written pair-permuted to dst (hi
+// at dst[0, I), lo at dst[I, 2I)); returns 2^e. All 16 lanes must be active.
+__device__ __forceinline__ float hilo_pair(float v0, float v1, int c, int li, uint16_t* dst,
+                                           int I) {
+  const float m = group_max<kLG>(fmaxf(fabsf(v0), fabsf(v1)));
+  const int e = hilo_exponent(m);
+  const float inv = ldexpf(1.0f, -e);
+  f16 h0, l0, h1, l1;
+  split_hilo(v0, inv, h0, l0);
+  split_hilo(v1, inv, h1, l1);
+  const int i0 = 32 * c + 2 * li;
+  const int p0 = perm8(i0), p1 = perm8(i0 + 1);
+  dst[p0] = __builtin_bit_cast(uint16_t, h0);
+  dst[p1] = __builtin_bit_cast(uint16_t, h1);
+  dst[I + p0] = __builtin_bit_cast(uint16_t, l0);
+  dst[I + p1] = __builtin_bit_cast(uint16_t, l1);
+  return ldexpf(1.0f, e);
+}
 
 // Pending loads of phase A (before the h exchange).
 template <int CPL, int IPG>
 struct PhaseA {
-  F16Rows<kNR> router, head, ax;
-  int n_router, n_head, n_ax;
+  F16Rows<kNR> router, ax;
+  int n_router, n_ax;
   GuRegs<CPL, IPG> gu;
   bool gu_loaded;
   uint4 attn;  // this thread's 8 elements of the attention update
@@ -414,6 +453,7 @@ struct PhaseA {
 
 template <int CPL_D, int IPG>
 __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
+  constexpr int CPH = 4 * CPL_D;  // 16-byte chunks per lane of a d-wide fp16 head row
   extern __shared__ __align__(16) unsigned char smem[];
   const Dims& dm = a.dm;
   const int d = dm.d, E = dm.E, K = dm.K, I = dm.I, P = dm.P, G = (int)gridDim.x;
@@ -423,18 +463,26 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
   const int li = lane % kLG, grp = t / kLG;
   const uint32_t ep = a.epoch;
   const int cur = a.token & 1, nxt = (a.token + 1) & 1;
-  const Lds lo = lds_layout(dm, a.ng);
+  const int nL = a.l1 - a.l0;
+  const Lds lo = lds_layout(dm, a.ng, nL);
   float* hattn = (float*)(smem + lo.hattn);
   uint16_t* xperm = (uint16_t*)(smem + lo.xperm);
   uint16_t* xnat = (uint16_t*)(smem + lo.xnat);
   uint32_t* land = (uint32_t*)(smem + lo.land);
   uint16_t* hk = (uint16_t*)(smem + lo.hk);
   uint16_t* ha = (uint16_t*)(smem + lo.ha);
-  uint16_t* lora = (uint16_t*)(smem + lo.lora);
+  uint16_t* hx = (uint16_t*)(smem + lo.hx);
   Misc& ms = *(Misc*)(smem + lo.misc);
-  const int nL = a.l1 - a.l0;
+  LayerDev* lay = (LayerDev*)(smem + lo.lay);
   const int F = d + 2 * E;
+  const int PE = P + E;
 
+  {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(a.layers + a.l0);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(lay);
+    const int nw = nL * (int)(sizeof(LayerDev) / 4);
+    for (int i = t; i < nw; i += kThreads) dst[i] = ldg(src + i);
+  }
   // Routing tables of every layer of the launch: the prediction consumed at
   // this token, the previous token's sets, and pool entries of predicted layers.
   if (t == 0) ms.abort = 0;
@@ -445,18 +493,32 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
     ms.pidx_all[i] = a.token > 0 ? a.exec_idx[((int64_t)nxt * a.L + l) * K + k] : -1;
   }
   __syncthreads();
+  if (wave == 0) {  // head list (nL <= 64: one lane per layer)
+    const bool has = lane < nL && lay[lane].head.fc1 != nullptr;
+    const uint64_t m = __ballot(has);
+    const int before = __popcll(m & ((1ull << lane) - 1ull));
+    if (lane < nL) ms.hidx_of[lane] = has ? before : -1;
+    if (has) ms.hl_list[before] = a.l0 + lane;
+    if (lane == 0) ms.n_heads = __popcll(m);
+  }
   for (int i = t; i < nL * K; i += kThreads) {
-    const int l = a.l0 + i / K;
-    ms.ent_all[i] = a.layers[l].router ? 0 : resolve_entry(a.layers[l].pool, E, ms.ridx_all[i]);
+    const int s = i / K;
+    ms.ent_all[i] = lay[s].router ? 0 : resolve_entry(lay[s].pool, E, ms.ridx_all[i]);
   }
   __syncthreads();
+  const int nH = ms.n_heads;
+  // This workgroup's share of the heads' fc1 / linear rows (head-major), and
+  // the heads whose x it keeps for them.
+  int g0, g1;
+  split(nH * PE, G, cu, g0, g1);
+  const int hx0 = g0 / PE, hx1 = g1 > g0 ? (g1 - 1) / PE : -1;
 
   // Issue every load of layer l that does not depend on its activations.
   auto issue_a = [&](int l, PhaseA<CPL_D, IPG>& A) {
-    const LayerDev& Ly = a.layers[l];
+    const LayerDev& Ly = lay[l - a.l0];
     const bool has_sh = Ly.sh.present != 0;
     const int Is = has_sh ? dm.Is : 0;
-    const int r2 = (has_sh && Ly.sh.ag) ? 2 * dm.r : 0;
+    const int r2 = (has_sh && Ly.sh.ag) ? 2 * kRank : 0;
     const uint16_t* rp[kNR];
     int b, e;
     A.n_router = 0;
@@ -470,19 +532,9 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
     A.n_ax = e - b;
     for (int j = 0; j < kNR; ++j) {
       const int tt = b + (j < A.n_ax ? j : 0);
-      rp[j] = (tt < dm.r ? Ly.sh.ag : Ly.sh.au) + (int64_t)(tt % (dm.r > 0 ? dm.r : 1)) * d;
+      rp[j] = (tt < kRank ? Ly.sh.ag : Ly.sh.au) + (int64_t)(tt % kRank) * d;
     }
     if (A.n_ax) f16rows_issue<kNR>(A.ax, rp, A.n_ax, d);
-    A.n_head = 0;
-    if (Ly.head.fc1) {
-      split(P + E, G, cu, b, e);
-      A.n_head = e - b;
-      for (int j = 0; j < kNR; ++j) {
-        const int it = b + (j < A.n_head ? j : 0);
-        rp[j] = it < P ? Ly.head.fc1 + (int64_t)it * F : Ly.head.lin + (int64_t)(it - P) * F;
-      }
-      f16rows_issue<kNR>(A.head, rp, A.n_head, d);
-    }
     A.attn = make_uint4(0, 0, 0, 0);
     if (Ly.attn && t < d / 8) A.attn = ldg(reinterpret_cast<const uint4*>(Ly.attn + 8 * t));
     A.gu_loaded = false;
@@ -501,15 +553,16 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
   issue_a(a.l0, A);
 
   for (int l = a.l0; l < a.l1; ++l) {
-    const LayerDev& Ly = a.layers[l];
+    const LayerDev& Ly = lay[l - a.l0];
     const int step = l - a.l0;
     const bool has_sh = Ly.sh.present != 0;
     const int Is = has_sh ? dm.Is : 0;
-    const int r2 = (has_sh && Ly.sh.ag) ? 2 * dm.r : 0;
-    const int nexp = K + (has_sh ? 1 : 0);
+    const int r2 = (has_sh && Ly.sh.ag) ? 2 * kRank : 0;
+    const bool lora_d = has_sh && Ly.sh.ad != nullptr;
     const int n_rt = K * I;
     uint64_t* xg = a.xg + (int64_t)l * a.ng;
-    const bool head = Ly.head.fc1 != nullptr;
+    const int hid = ms.hidx_of[step];
+    const bool keep_x = hid >= hx0 && hid <= hx1;
 
     // ---- 1. h_l, attention stand-in, RMSNorm ---------------------------
     stamp(a, l, 0);
@@ -556,6 +609,7 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
                                      xv[2] | ((uint32_t)xv[6] << 16), xv[3] | ((uint32_t)xv[7] << 16));
         *reinterpret_cast<uint4*>(xnat + 8 * t) = nat;
         *reinterpret_cast<uint4*>(xperm + 8 * t) = per;
+        if (keep_x) *reinterpret_cast<uint4*>(hx + (hid - hx0) * d + 8 * t) = nat;
         if (cu == 0 && a.x_trace) *reinterpret_cast<uint4*>(a.x_trace + (int64_t)l * d + 8 * t) = nat;
       }
     }
@@ -578,7 +632,10 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
       __syncthreads();
       if (t < 16) {
         int64_t ent = 0;
-        if (t < K) ent = resolve_entry(Ly.pool, E, ms.ridx[t]);
+        if (t < K) {
+          ent = resolve_entry(Ly.pool, E, ms.ridx[t]);
+          ms.ridx_all[step * K + t] = ms.ridx[t];  // the executed set, for this layer's head
+        }
         ms.ent[t] = ent;
         if (ent < 0 && cu == 0) atomicOr(&a.flags[FLAG_RANGE], 1);
       }
@@ -595,6 +652,25 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
       eidx[t] = ms.ridx[t];
       ew[t] = ms.rw[t];
     }
+    if (t < kMaxExp) {
+      const uint32_t* q = nullptr;
+      const uint16_t* sc = nullptr;
+      float cf = 0.0f;
+      if (t < K) {
+        if (ms.ent[t] >= 0) {
+          q = (const uint32_t*)entry_ptr(Ly.pool.down.q, ms.ent[t], Ly.pool.stride_q);
+          sc = (const uint16_t*)entry_ptr(Ly.pool.down.s, ms.ent[t], Ly.pool.stride_s);
+          cf = ms.rw[t];
+        }
+      } else if (t == K && has_sh) {
+        q = Ly.sh.down.q;
+        sc = Ly.sh.down.s;
+        cf = 1.0f;
+      }
+      ms.dq[t] = q;
+      ms.dsc[t] = sc;
+      ms.coef[t] = cf;
+    }
     stamp(a, l, 3);
 
     // ---- 3. gate/up rows, shared bases, LoRA A of gate/up ----------------
@@ -602,7 +678,7 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
       GuPlan pl;
       split(n_rt + Is, G, cu, pl.ib, pl.ie);
       if (!A.gu_loaded) gu_issue<CPL_D, IPG>(A.gu, Ly, dm, ms, n_rt, pl, grp, li);
-      gu_finish<CPL_D, IPG>(A.gu, Ly, dm, ms, n_rt, Is, pl, grp, li, xperm, xg, ep);
+      gu_finish<CPL_D, IPG>(A.gu, dm, ms, n_rt, Is, pl, grp, li, xperm, xg, ep);
       if (A.n_ax) {
         int b, e;
         split(r2, G, cu, b, e);
@@ -613,37 +689,7 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
     }
     stamp(a, l, 4);
 
-    // ---- 4. head fc1 / linear path ----------------------------------------
-    if (head) {
-      int hb, he;
-      split(P + E, G, cu, hb, he);
-      // one-hot columns of the executed set and of the previous token's set
-      if (t < A.n_head * 2 * K) {
-        const int j = t / (2 * K), kk = t % (2 * K);
-        const int it = hb + j;
-        const uint16_t* wrow = it < P ? Ly.head.fc1 + (int64_t)it * F : Ly.head.lin + (int64_t)(it - P) * F;
-        int col = -1;
-        if (kk < K) {
-          const int e = ms.ridx[kk];
-          if (e >= 0 && e < E) col = d + e;
-        } else {
-          const int e = ms.pidx_all[step * K + kk - K];
-          if (e >= 0 && e < E) col = d + E + e;
-        }
-        ms.gath[t] = col >= 0 ? h2f(ldg(wrow + col)) : 0.0f;
-      }
-      f16rows_finish<kNR>(A.head, A.n_head, d, xnat, ms);
-      if (t < A.n_head) {
-        float acc = ms.rows[t];
-        for (int kk = 0; kk < 2 * K; ++kk) acc += ms.gath[t * 2 * K + kk];
-        const int it = hb + t;
-        ll_put(a.xa + (int64_t)l * (P + E) + it, fbits(it < P ? gelu_erf(acc) : acc), ep);
-      }
-      post(a, l, XA);
-    }
-    stamp(a, l, 5);
-
-    // ---- phase B loads: down rows, shared-expert LoRA matrices, fc2 rows ----
+    // ---- phase B loads: down rows and the shared-expert LoRA matrices -------
     int db, de;
     {
       int wb, we;
@@ -655,141 +701,110 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
     const int drow = db + grp;
     if (drow < de) {
       const int wpr = I / 8, spr = I / dm.G;
+      const uint32_t* qp[kMaxExp];
+      const uint16_t* sp[kMaxExp];
+#pragma unroll
+      for (int k = 0; k < kMaxExp; ++k) {
+        qp[k] = ms.dq[k];
+        sp[k] = ms.dsc[k];
+      }
 #pragma unroll
       for (int k = 0; k < kMaxExp; ++k) {
         D.w[k] = make_uint4(0, 0, 0, 0);
         D.s[k] = 0;
-        if (k >= nexp || (k < K && ms.ent[k] < 0)) continue;
-        const uint32_t* q = k < K ? (const uint32_t*)entry_ptr(Ly.pool.down.q, ms.ent[k], Ly.pool.stride_q) : Ly.sh.down.q;
-        const uint16_t* sc = k < K ? (const uint16_t*)entry_ptr(Ly.pool.down.s, ms.ent[k], Ly.pool.stride_s) : Ly.sh.down.s;
-        D.w[k] = ldg(reinterpret_cast<const uint4*>(q + (int64_t)drow * wpr + 4 * li));
-        D.s[k] = ldg(sc + (int64_t)drow * spr + (32 * li) / dm.G);
+        if (!qp[k]) continue;
+        D.w[k] = ldg(reinterpret_cast<const uint4*>(qp[k] + (int64_t)drow * wpr + 4 * li));
+        D.s[k] = ldg(sp[k] + (int64_t)drow * spr + (32 * li) / dm.G);
       }
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < kRank / 8; ++c) {
         D.bd[c] = make_uint4(0, 0, 0, 0);
-        if (has_sh && Ly.sh.bd && c * 8 < dm.r && li == 0)
-          D.bd[c] = ldg(reinterpret_cast<const uint4*>(Ly.sh.bd + (int64_t)drow * dm.r + 8 * c));
+        if (lora_d && li == 0)
+          D.bd[c] = ldg(reinterpret_cast<const uint4*>(Ly.sh.bd + (int64_t)drow * kRank + 8 * c));
       }
     }
-    // LoRA matrices of the shared expert: B_gate, B_up [Is, r], A_down [r, Is]
-    uint4 lr[kLoraRegs];
-    const int n_lora16 = has_sh && dm.r > 0 ? (3 * Is * dm.r) / 8 : 0;
-    const bool lora_gu = has_sh && Ly.sh.bg;
-    const bool lora_d = has_sh && Ly.sh.ad;
+    LoraRegs LR;
 #pragma unroll
-    for (int j = 0; j < kLoraRegs; ++j) {
-      lr[j] = make_uint4(0, 0, 0, 0);
-      const int c = t + kThreads * j;
-      if (c >= n_lora16) continue;
-      const int per = Is * dm.r / 8;  // chunks per matrix
-      const int m = c / per, off = c % per;
-      const uint16_t* src = m == 0 ? Ly.sh.bg : (m == 1 ? Ly.sh.bu : Ly.sh.ad);
-      if ((m < 2 && lora_gu) || (m == 2 && lora_d)) lr[j] = ldg(reinterpret_cast<const uint4*>(src + 8 * off));
+    for (int c = 0; c < kRank / 4; ++c) {
+      LR.bg[c] = make_uint4(0, 0, 0, 0);
+      LR.bu[c] = make_uint4(0, 0, 0, 0);
+      if (r2) {
+        LR.bg[c] = ldg(reinterpret_cast<const uint4*>(Ly.sh.bg + 2 * t * kRank + 8 * c));
+        LR.bu[c] = ldg(reinterpret_cast<const uint4*>(Ly.sh.bu + 2 * t * kRank + 8 * c));
+      }
     }
-    F16Rows<kNR> fc2r;
-    int n_fc2 = 0, fb = 0, fe = 0;
-    if (head) {
-      split(E, G, cu, fb, fe);
-      n_fc2 = fe - fb;
-      const uint16_t* rp[kNR];
-      for (int j = 0; j < kNR; ++j) rp[j] = Ly.head.fc2 + (int64_t)(fb + (j < n_fc2 ? j : 0)) * P;
-      f16rows_issue<kNR>(fc2r, rp, n_fc2, P);
-    }
+#pragma unroll
+    for (int q = 0; q < kRank; ++q)
+      LR.ad[q] = lora_d ? ldg(reinterpret_cast<const uint32_t*>(Ly.sh.ad + q * Is + 2 * t)) : 0u;
+    stamp(a, l, 5);
 
-    // ---- 5. gather SwiGLU outputs; finish the shared expert ----------------
-    stamp(a, l, 6);
+    // ---- 4. gather SwiGLU outputs; finish the shared expert ----------------
     const int ng_l = n_rt + 2 * Is + r2;
     wait_all(a, l, XG, &ms.abort);
     ll_gather<16>(xg, ng_l, ep, land, a.flags, &ms.abort);
-#pragma unroll
-    for (int j = 0; j < kLoraRegs; ++j) {
-      const int c = t + kThreads * j;
-      if (c < n_lora16) *reinterpret_cast<uint4*>(lora + 8 * c) = lr[j];
-    }
     __syncthreads();
-    stamp(a, l, 7);
-    if (has_sh) {
-      const float c = dm.lora_scale;
-      const float* axg = (const float*)land + n_rt + 2 * Is;
-      const int r = dm.r;
-      const uint16_t* Bg = lora;
-      const uint16_t* Bu = lora + Is * r;
-      const uint16_t* Ad = lora + 2 * Is * r;
-      for (int i = t; i < Is; i += kThreads) {
-        float g = bitsf(land[n_rt + i]), u = bitsf(land[n_rt + Is + i]);
+    stamp(a, l, 6);
+    {
+      // fp16 hi/lo copies of every expert's SwiGLU output for the down GEMVs:
+      // lane group grp converts 32-element chunk grp (I / 32 == kGroups).
+      const float* lf = (const float*)land;
+      if (has_sh) {
+        const float cs = dm.lora_scale;
+        const float2 gb = *reinterpret_cast<const float2*>(lf + n_rt + 2 * t);
+        const float2 ub = *reinterpret_cast<const float2*>(lf + n_rt + Is + 2 * t);
+        float g0v = gb.x, g1v = gb.y, u0v = ub.x, u1v = ub.y;
         if (r2) {
-          float lg = 0.0f, lu = 0.0f;
-          for (int q = 0; q < r; ++q) {
-            lg += h2f(Bg[i * r + q]) * axg[q];
-            lu += h2f(Bu[i * r + q]) * axg[r + q];
-          }
-          g += c * lg;
-          u += c * lu;
+          const float* axg = lf + n_rt + 2 * Is;
+          const float* axu = axg + kRank;
+          g0v += cs * lora_row(LR.bg[0], LR.bg[1], axg);
+          g1v += cs * lora_row(LR.bg[2], LR.bg[3], axg);
+          u0v += cs * lora_row(LR.bu[0], LR.bu[1], axu);
+          u1v += cs * lora_row(LR.bu[2], LR.bu[3], axu);
         }
-        land[n_rt + i] = fbits(silu(g) * u);  // the shared SwiGLU output replaces the gate base
+        const float h0 = silu(g0v) * u0v, h1 = silu(g1v) * u1v;
+        const float sc = hilo_pair(h0, h1, grp, li, hk + K * 2 * I, I);
+        if (li == 0) ms.csc[K][grp] = sc;
+        if (lora_d) {
+#pragma unroll
+          for (int q = 0; q < kRank; ++q) {
+            float p = h2f((uint16_t)(LR.ad[q] & 0xFFFF)) * h0 + h2f((uint16_t)(LR.ad[q] >> 16)) * h1;
+            p = group_sum<kLG>(p);
+            if (li == 0) ms.red16[q][grp] = p;
+          }
+        }
+      }
+      for (int k = 0; k < K; ++k) {
+        if (!ms.dq[k]) continue;  // uniform: unresolved expert, contributes nothing
+        const float2 v = *reinterpret_cast<const float2*>(lf + k * I + 32 * grp + 2 * li);
+        const float sc = hilo_pair(v.x, v.y, grp, li, hk + k * 2 * I, I);
+        if (li == 0) ms.csc[k][grp] = sc;
       }
       __syncthreads();
-      if (lora_d) {
-        const float* hsh = (const float*)land + n_rt;
-        for (int q = grp; q < r; q += kGroups) {
-          float acc = 0.0f;
-          for (int i = li; i < Is; i += kLG) acc += h2f(Ad[q * Is + i]) * hsh[i];
-          acc = group_sum<kLG>(acc);
-          if (li == 0) ms.ad[q] = acc;
-        }
+      if (lora_d && t < kRank) {
+        float s = 0.0f;
+        for (int g = 0; g < kGroups; ++g) s += ms.red16[t][g];
+        ms.ad[t] = s;
       }
+      __syncthreads();
     }
-    // fp16 hi/lo copies of each expert's SwiGLU output for the down GEMVs
-    for (int k = wave; k < nexp; k += kThreads / 64) {
-      const float* src = (const float*)land + (k < K ? k * I : n_rt);
-      float m = 0.0f;
-      for (int i = lane; i < I; i += 64) m = fmaxf(m, fabsf(src[i]));
-      m = wave_max(m);
-      if (lane == 0) ms.emax[k] = m;
-    }
-    __syncthreads();
-    for (int idx = t; idx < nexp * (I / 8); idx += kThreads) {
-      const int k = idx / (I / 8), blk = idx % (I / 8);
-      const float* src = (const float*)land + (k < K ? k * I : n_rt) + 8 * blk;
-      const int e = hilo_exponent(ms.emax[k]);
-      const float inv = ldexpf(1.0f, -e);
-      uint16_t hi[8], lo2[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        f16 h_, l_;
-        split_hilo(src[q], inv, h_, l_);
-        hi[q] = __builtin_bit_cast(uint16_t, h_);
-        lo2[q] = __builtin_bit_cast(uint16_t, l_);
-      }
-      uint16_t* hh = hk + (int64_t)k * 2 * I + 8 * blk;
-      *reinterpret_cast<uint4*>(hh) = make_uint4(hi[0] | ((uint32_t)hi[4] << 16), hi[1] | ((uint32_t)hi[5] << 16),
-                                                 hi[2] | ((uint32_t)hi[6] << 16), hi[3] | ((uint32_t)hi[7] << 16));
-      *reinterpret_cast<uint4*>(hh + I) = make_uint4(lo2[0] | ((uint32_t)lo2[4] << 16), lo2[1] | ((uint32_t)lo2[5] << 16),
-                                                     lo2[2] | ((uint32_t)lo2[6] << 16), lo2[3] | ((uint32_t)lo2[7] << 16));
-      if (blk == 0)
-        ms.coef[k] = k < K ? (ms.ent[k] < 0 ? 0.0f : ms.rw[k] * ldexpf(1.0f, e)) : ldexpf(1.0f, e);
-    }
-    __syncthreads();
-    stamp(a, l, 8);
+    stamp(a, l, 7);
 
-    // ---- 6. down rows: combine, shared expert, down LoRA, residual ---------
+    // ---- 5. down rows: combine, shared expert, down LoRA, residual ---------
     if (drow < de) {
       float acc = 0.0f;
 #pragma unroll
       for (int k = 0; k < kMaxExp; ++k) {
-        if (k >= nexp || (k < K && ms.ent[k] < 0)) continue;
+        if (!ms.dq[k]) continue;
         const uint16_t* hh = hk + (int64_t)k * 2 * I;
         f16x2 xh[16], xl[16];
         load_xchunk(hh, li, xh);
         load_xchunk(hh + I, li, xl);
-        acc += ms.coef[k] * (h2f(D.s[k]) * q4_dot32_hl(D.w[k], xh, xl));
+        acc += (ms.coef[k] * ms.csc[k][li]) * (h2f(D.s[k]) * q4_dot32_hl(D.w[k], xh, xl));
       }
-      if (has_sh && Ly.sh.bd && li == 0) {
+      if (lora_d && li == 0) {
         float lsum = 0.0f;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          if (c * 8 >= dm.r) continue;
+        for (int c = 0; c < kRank / 8; ++c) {
           const uint32_t bw[4] = {D.bd[c].x, D.bd[c].y, D.bd[c].z, D.bd[c].w};
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -813,64 +828,191 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
       ll_put(a.xh + (int64_t)l * (d / 2) + j, pr, ep);
     }
     post(a, l, XH);
-    stamp(a, l, 9);
+    stamp(a, l, 8);
 
-    // next layer's activation-independent loads go out before the fc2 work
     if (l + 1 < a.l1) issue_a(l + 1, A);
-
-    // ---- 7. head fc2 rows ----------------------------------------------------
-    if (head) {
-      wait_all(a, l, XA, &ms.abort);
-      ll_gather<4>(a.xa + (int64_t)l * (P + E), P + E, ep, land, a.flags, &ms.abort);
-      __syncthreads();
-      {
-        float m = 0.0f;
-        for (int i = t; i < P; i += kThreads) m = fmaxf(m, fabsf(bitsf(land[i])));
-        m = wave_max(m);
-        if (lane == 0) ms.red[wave] = m;
-        __syncthreads();
-        float mx = 0.0f;
-        for (int j = 0; j < kThreads / 64; ++j) mx = fmaxf(mx, ms.red[j]);
-        const int e = hilo_exponent(mx);
-        const float inv = ldexpf(1.0f, -e);
-        for (int i = t; i < P; i += kThreads) {
-          f16 hi, lo2;
-          split_hilo(bitsf(land[i]), inv, hi, lo2);
-          ha[i] = __builtin_bit_cast(uint16_t, hi);
-          ha[P + i] = __builtin_bit_cast(uint16_t, lo2);
-        }
-        if (t == 0) ms.ha_scale = ldexpf(1.0f, e);
-      }
-      __syncthreads();
-      f16rows_finish_hl<kNR>(fc2r, n_fc2, P, ha, ha + P, ms);
-      if (t < n_fc2) {
-        const int e = fb + t;
-        const float logit = ms.rows[t] * ms.ha_scale + bitsf(land[P + e]);
-        ll_put(a.xl + (int64_t)l * E + e, fbits(logit), ep);
-        if (a.head_logits) a.head_logits[(int64_t)l * E + e] = logit;
-      }
-      post(a, l, XL);
-    }
-    __syncthreads();
+    stamp(a, l, 9);
   }
 
-  // ---- routing of each head's logits: the next token's prediction ----------
-  for (int l = a.l0 + cu; l < a.l1; l += G) {
-    const LayerDev& Ly = a.layers[l];
-    if (!Ly.head.fc1) continue;
-    wait_all(a, l, XL, &ms.abort);
+  if (nH == 0) return;
+
+  // ---- heads: fc1 / linear rows, fc2 rows, routing of the logits ------------
+  const int hrow = a.L;
+  stamp(a, hrow, 0);
+  // fc2 rows of this workgroup (head-major); they do not depend on the
+  // hidden activations, so they are loaded first.
+  int f0, f1;
+  split(nH * E, G, cu, f0, f1);
+  const int nf = f1 - f0;
+  const int cpf = P / 128;
+  uint4 w2[kF2R][kCPF];
+#pragma unroll
+  for (int r = 0; r < kF2R; ++r) {
+    int f = f0 + r * kGroups + grp;
+    f = f < f1 ? f : f1 - 1;
+    const int h = nf > 0 ? f / E : 0, e = nf > 0 ? f % E : 0;
+    const uint16_t* wrow = lay[ms.hl_list[h] - a.l0].head.fc2 + (int64_t)e * P;
+#pragma unroll
+    for (int j = 0; j < kCPF; ++j) {
+      w2[r][j] = make_uint4(0, 0, 0, 0);
+      if (nf > 0 && r * kGroups < nf && j < cpf)
+        w2[r][j] = ldg(reinterpret_cast<const uint4*>(wrow + 8 * (li + kLG * j)));
+    }
+  }
+
+  // fc1 / linear rows: lane group grp takes row g0 + r*kGroups + grp of round
+  // r; two rounds in flight. Lanes li < 2K also fetch the row's one-hot
+  // column of the executed set (li < K) or of the previous token's set.
+  {
+    const int nrow = g1 - g0;
+    const int R1 = (nrow + kGroups - 1) / kGroups;
+    auto h1_issue = [&](uint4 (&w)[CPH], uint16_t& gv, int r) {
+      int g = g0 + r * kGroups + grp;
+      g = g < g1 ? g : g1 - 1;
+      const int h = g / PE, it = g % PE;
+      const int s = ms.hl_list[h] - a.l0;
+      const LayerDev& Lh = lay[s];
+      const uint16_t* wrow = it < P ? Lh.head.fc1 + (int64_t)it * F : Lh.head.lin + (int64_t)(it - P) * F;
+#pragma unroll
+      for (int j = 0; j < CPH; ++j) w[j] = ldg(reinterpret_cast<const uint4*>(wrow + 8 * (li + kLG * j)));
+      int col = d;  // an in-row column whose value is dropped
+      if (li < K) {
+        const int e = ms.ridx_all[s * K + li];
+        if (e >= 0 && e < E) col = d + e;
+      } else if (li < 2 * K) {
+        const int e = ms.pidx_all[s * K + li - K];
+        if (e >= 0 && e < E) col = d + E + e;
+      }
+      gv = ldg(wrow + col);
+    };
+    auto h1_finish = [&](const uint4 (&w)[CPH], uint16_t gv, int r) {
+      const int graw = g0 + r * kGroups + grp;
+      const int g = graw < g1 ? graw : g1 - 1;
+      const int h = g / PE, it = g % PE;
+      const int l = ms.hl_list[h], s = l - a.l0;
+      const uint16_t* xs = hx + (h - hx0) * d;
+      float acc = 0.0f;
+#pragma unroll
+      for (int j = 0; j < CPH; ++j)
+        acc = dot8_h(w[j], *reinterpret_cast<const uint4*>(xs + 8 * (li + kLG * j)), acc);
+      bool use = false;
+      if (li < K) {
+        const int e = ms.ridx_all[s * K + li];
+        use = e >= 0 && e < E;
+      } else if (li < 2 * K) {
+        const int e = ms.pidx_all[s * K + li - K];
+        use = e >= 0 && e < E;
+      }
+      if (use) acc += h2f(gv);
+      acc = group_sum<kLG>(acc);
+      if (li == 0 && graw < g1)
+        ll_put(a.xa + (int64_t)l * PE + it, fbits(it < P ? gelu_erf(acc) : acc), ep);
+    };
+    uint4 wa[CPH], wb[CPH];
+    uint16_t ga = 0, gb = 0;
+    if (nrow > 0) {
+      h1_issue(wa, ga, 0);
+      for (int r = 0; r < R1; r += 2) {
+        if (r + 1 < R1) h1_issue(wb, gb, r + 1);
+        h1_finish(wa, ga, r);
+        if (r + 1 < R1) {
+          if (r + 2 < R1) h1_issue(wa, ga, r + 2);
+          h1_finish(wb, gb, r + 1);
+        }
+      }
+    }
+  }
+  post(a, a.l0, XA);
+  stamp(a, hrow, 1);
+
+  // fc2: hidden activations and linear path of the heads of this workgroup's
+  // fc2 rows, as fp16 hi + lo with a power-of-two scale per lane chunk.
+  wait_all(a, a.l0, XA, &ms.abort);
+  const int hf0 = nf > 0 ? f0 / E : 0, hf1 = nf > 0 ? (f1 - 1) / E : -1;
+  for (int h = hf0; h <= hf1; ++h)
+    ll_gather<4>(a.xa + (int64_t)ms.hl_list[h] * PE, PE, ep, land + (h - hf0) * PE, a.flags,
+                 &ms.abort);
+  __syncthreads();
+  stamp(a, hrow, 2);
+  if (t < (hf1 - hf0 + 1) * kLG) {
+    const int s = t / kLG, lc = t % kLG;
+    const float* act = (const float*)land + s * PE;
+    float m = 0.0f;
+    for (int j = 0; j < cpf; ++j) {
+      const float4 u = *reinterpret_cast<const float4*>(act + 8 * (lc + kLG * j));
+      const float4 v = *reinterpret_cast<const float4*>(act + 8 * (lc + kLG * j) + 4);
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(u.x), fabsf(u.y)), fmaxf(fabsf(u.z), fabsf(u.w))));
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
+    const int e = hilo_exponent(m);
+    const float inv = ldexpf(1.0f, -e);
+    for (int j = 0; j < cpf; ++j) {
+      const int c = lc + kLG * j;
+      uint16_t hi[8], lo2[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        f16 h_, l_;
+        split_hilo(act[8 * c + q], inv, h_, l_);
+        hi[q] = __builtin_bit_cast(uint16_t, h_);
+        lo2[q] = __builtin_bit_cast(uint16_t, l_);
+      }
+      uint16_t* dst = ha + s * 2 * P + 8 * c;
+      *reinterpret_cast<uint4*>(dst) =
+          make_uint4(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16),
+                     hi[4] | ((uint32_t)hi[5] << 16), hi[6] | ((uint32_t)hi[7] << 16));
+      *reinterpret_cast<uint4*>(dst + P) =
+          make_uint4(lo2[0] | ((uint32_t)lo2[1] << 16), lo2[2] | ((uint32_t)lo2[3] << 16),
+                     lo2[4] | ((uint32_t)lo2[5] << 16), lo2[6] | ((uint32_t)lo2[7] << 16));
+    }
+    ms.hsc[s][lc] = ldexpf(1.0f, e);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kF2R; ++r) {
+    if (r * kGroups >= nf) continue;  // uniform
+    const int fraw = f0 + r * kGroups + grp;
+    const int f = fraw < f1 ? fraw : f1 - 1;
+    const int h = f / E, e = f % E, s = h - hf0;
+    const uint16_t* xh_ = ha + s * 2 * P;
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kCPF; ++j) {
+      if (j >= cpf) continue;
+      const int c = li + kLG * j;
+      const uint4 xa = *reinterpret_cast<const uint4*>(xh_ + 8 * c);
+      const uint4 xb = *reinterpret_cast<const uint4*>(xh_ + P + 8 * c);
+      acc = dot8_h(w2[r][j], xb, dot8_h(w2[r][j], xa, acc));
+    }
+    acc *= ms.hsc[s][li];
+    acc = group_sum<kLG>(acc);
+    if (li == 0 && fraw < f1) {
+      const int l = ms.hl_list[h];
+      const float logit = acc + bitsf(land[s * PE + P + e]);
+      ll_put(a.xl + (int64_t)l * E + e, fbits(logit), ep);
+      if (a.head_logits) a.head_logits[(int64_t)l * E + e] = logit;
+    }
+  }
+  post(a, a.l0, XL);
+  stamp(a, hrow, 3);
+
+  // routing of each head's logits: the next token's prediction
+  for (int h = cu; h < nH; h += G) {
+    const int l = ms.hl_list[h];
+    const LayerDev& Lh = lay[l - a.l0];
+    wait_all(a, a.l0, XL, &ms.abort);
     ll_gather<2>(a.xl + (int64_t)l * E, E, ep, land, a.flags, &ms.abort);
     __syncthreads();
     int32_t* pidx = l + 1 < a.L ? a.route_idx + ((int64_t)nxt * a.L + l + 1) * K : a.sink_idx;
     float* pw = l + 1 < a.L ? a.route_w + ((int64_t)nxt * a.L + l + 1) * K : a.sink_w;
-    if (wave == 0) route_wave(dm, (const float*)land, Ly.head.bias, ms.rs, pidx, pw, a.flags);
+    if (wave == 0) route_wave(dm, (const float*)land, Lh.head.bias, ms.rs, pidx, pw, a.flags);
     __syncthreads();
   }
+  stamp(a, hrow, 4);
 }
 
 template <int CPL_D, int IPG>
 hipError_t launch_stack_t(const StackArgs& a, int grid, hipStream_t st) {
-  const Lds lo = lds_layout(a.dm, a.ng);
+  const Lds lo = lds_layout(a.dm, a.ng, a.l1 - a.l0);
   static bool attr_set = false;
   if (!attr_set) {
     hipFuncSetAttribute((const void*)k_stack<CPL_D, IPG>,
@@ -881,29 +1023,48 @@ hipError_t launch_stack_t(const StackArgs& a, int grid, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Largest number of consecutive blocks of size `block` that a contiguous
+// range of at most `per` items can touch.
+int span(int per, int block) { return per <= 0 ? 0 : (per - 1) / block + 2; }
+
 }  // namespace
 
-int stack_lds_bytes(const Dims& dm, int ng) { return lds_layout(dm, ng).bytes; }
-
 bool stack_supported(const Dims& dm) {
-  if (dm.d % 512 || dm.I != 512 || dm.K > 8 || dm.E > kMaxE || dm.r > 16) return false;
+  if (dm.d % 512 || dm.I != 512 || dm.K > 8 || dm.E > kMaxE) return false;
   if (dm.Is != 0 && dm.Is != dm.I) return false;
-  if (3 * dm.Is * dm.r / 8 > kLoraRegs * kThreads) return false;
-  if (dm.P % 8 || dm.P > 2048) return false;
+  if (dm.r != 0 && dm.r != kRank) return false;
+  if (dm.P % 128 || dm.P > 128 * kCPF) return false;
   const int cpl = dm.d / 512;
   return cpl == 3 || cpl == 4;
 }
 
-hipError_t launch_stack(const StackArgs& a, int grid, hipStream_t st) {
+bool stack_launchable(const StackArgs& a, int grid) {
   const Dims& dm = a.dm;
+  const int n_heads = a.n_heads;
+  if (!stack_supported(dm) || a.l1 - a.l0 > kMaxL || a.l1 <= a.l0 || grid < 1 || grid > 512 ||
+      !a.fl)
+    return false;
+  if (lds_layout(dm, a.ng, a.l1 - a.l0).bytes > 160 * 1024) return false;
   // Work per workgroup must fit the fixed per-thread plans.
   const int gu_items = dm.K * dm.I + dm.Is;
   const int ipg = (gu_items + grid - 1) / grid;
-  if (a.l1 - a.l0 > kMaxL || grid < 1 || grid > 512 || !a.fl) return hipErrorInvalidValue;
-  if ((dm.E + grid - 1) / grid > kNR || (dm.P + dm.E + grid - 1) / grid > kNR ||
-      (2 * dm.r + grid - 1) / grid > kNR || 2 * ((dm.d / 2 + grid - 1) / grid) > kGroups ||
-      2 * dm.K * kNR > kNR * 16)
-    return hipErrorInvalidValue;
+  if (ipg > 2 * kGroups) return false;
+  if ((dm.E + grid - 1) / grid > kNR || (2 * dm.r + grid - 1) / grid > kNR ||
+      2 * ((dm.d / 2 + grid - 1) / grid) > kGroups)
+    return false;
+  const int PE = dm.P + dm.E;
+  const int h1 = (n_heads * PE + grid - 1) / grid, f2 = (n_heads * dm.E + grid - 1) / grid;
+  if (span(h1, PE) > kHX || span(f2, dm.E) > kHX || f2 > kF2R * kGroups) return false;
+  return true;
+}
+
+int stack_lds_bytes(const Dims& dm, int ng, int n_layers) { return lds_layout(dm, ng, n_layers).bytes; }
+
+hipError_t launch_stack(const StackArgs& a, int grid, hipStream_t st) {
+  if (!stack_launchable(a, grid)) return hipErrorInvalidValue;
+  const Dims& dm = a.dm;
+  const int gu_items = dm.K * dm.I + dm.Is;
+  const int ipg = (gu_items + grid - 1) / grid;
   const int cpl = dm.d / 512;
   if (ipg <= kGroups) {
     if (cpl == 3) return launch_stack_t<3, 1>(a, grid, st);
