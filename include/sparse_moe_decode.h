@@ -217,12 +217,14 @@ int e0_model_set_path(e0_model* model, int32_t path);
 /* Phase tracing of the persistent kernel (observability; off by default).
  * trace: device uint64 [grid][rows][points] (shape from e0_model_trace_shape;
  * rows = L + 1), or NULL to turn tracing off. Thread 0 of each workgroup
- * writes the 100 MHz wall clock at each phase boundary. Row l < L (a layer):
- * layer start, h gathered, x normed, routed, gate/up published, down and
- * LoRA loads issued, SwiGLU outputs gathered, shared expert and hi/lo copies
- * done, h_out published, next layer's loads issued. Row L (the heads, after
- * the last layer): start, fc1/linear rows published, activations gathered,
- * fc2 rows published, head routing done. */
+ * writes the 100 MHz wall clock at each phase boundary. Row l < L (a layer),
+ * point: 0 layer start, 9 activation-independent loads issued, 1 h gathered,
+ * 2 x normed, 3 routed, 4 gate/up published, 5 down and LoRA loads issued,
+ * 6 SwiGLU outputs gathered, 7 shared expert and hi/lo copies done, 8 h_out
+ * published; a layer with its own router also 10 logits reduced, 11 logits
+ * published, 13 logits gathered, 14 routed. Row L (the heads, after the last
+ * layer): 0 start, 1 fc1/linear rows published, 2 activations gathered, 3 fc2
+ * rows published, 4 head routing done. */
 int e0_model_set_trace(e0_model* model, uint64_t* trace);
 int32_t e0_model_trace_shape(e0_model* model, int32_t* grid, int32_t* rows, int32_t* points);
 

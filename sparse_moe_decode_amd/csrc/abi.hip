@@ -52,7 +52,6 @@ struct e0_model {
   LayerDev* dev_table;  // device copy of the layer table (persistent kernel)
   void* xbuf;           // exchange words of the persistent kernel (one block)
   uint64_t *xh, *xg, *xr, *xa, *xl;
-  uint32_t* fl;
   int32_t ng;
   uint32_t epoch;
   int32_t path;
@@ -363,7 +362,6 @@ int e0_model_create(e0_ctx* ctx, const e0_layer* layers, int32_t n_layers, e0_mo
   m->dev_table = nullptr;
   m->xbuf = nullptr;
   m->xh = m->xg = m->xr = m->xa = m->xl = nullptr;
-  m->fl = nullptr;
   m->epoch = 0;
   m->path = E0_PATH_AUTO;
   m->grid = 0;
@@ -399,8 +397,7 @@ int e0_model_create(e0_ctx* ctx, const e0_layer* layers, int32_t n_layers, e0_mo
     int dev = 0, cus = 0;
     if (e == hipSuccess) e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    const size_t nfl = (size_t)n_layers * kExchanges * (cus > 0 ? cus : 1);
-    const size_t words = wh + wg + wr + wa + wl + (nfl + 1) / 2;
+    const size_t words = wh + wg + wr + wa + wl;
     if (e == hipSuccess) e = hipMalloc(&m->xbuf, words * 8);
     if (e == hipSuccess) e = hipMemset(m->xbuf, 0, words * 8);
     if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -414,7 +411,6 @@ int e0_model_create(e0_ctx* ctx, const e0_layer* layers, int32_t n_layers, e0_mo
     m->xr = w; w += wr;
     m->xa = w; w += wa;
     m->xl = w; w += wl;
-    m->fl = (uint32_t*)w;
     m->grid = cus;
   }
   *out = m;
@@ -492,7 +488,6 @@ int layer_step(e0_ctx* ctx, e0_model* model, int32_t layer_begin, int32_t layer_
     a.xr = model->xr;
     a.xa = model->xa;
     a.xl = model->xl;
-    a.fl = model->fl;
     a.sink_idx = s.sink_idx;
     a.sink_w = s.sink_w;
     a.flags = s.flags;

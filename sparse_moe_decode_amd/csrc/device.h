@@ -128,8 +128,7 @@ __device__ __forceinline__ void max_step_u64(uint32_t& hi, uint32_t& lo) {
   lo = gt ? ol : lo;
 }
 
-// Wave-wide maximum of a 64-bit key (same result as wave_max_u64); the whole
-// wave must be active.
+// Wave-wide maximum of a 64-bit key; the whole wave must be active.
 __device__ __forceinline__ uint64_t wave_max_u64_rows(uint64_t k) {
   uint32_t hi = (uint32_t)(k >> 32), lo = (uint32_t)k;
   max_step_u64<0xB1>(hi, lo);
@@ -155,18 +154,6 @@ __device__ __forceinline__ float gelu_erf(float z) {
 __device__ __forceinline__ uint32_t f2key(float v) {
   uint32_t b = __builtin_bit_cast(uint32_t, v);
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-
-// Wave-wide maximum of a 64-bit key (xor butterfly over the 64 lanes).
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t lo = __shfl_xor((uint32_t)k, off);
-    uint32_t hi = __shfl_xor((uint32_t)(k >> 32), off);
-    uint64_t o = ((uint64_t)hi << 32) | lo;
-    k = o > k ? o : k;
-  }
-  return k;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

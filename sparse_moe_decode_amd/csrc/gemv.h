@@ -208,122 +208,124 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 struct RouteScratch {
-  float sel[kMaxE];
-  float gsc[64];
-  int keep[64];
+  float sel[kMaxE];  // sigmoid-group selection scores
+  int keep[64];      // sigmoid-group: group kept
+  int ksel[8];       // selected ids, in selection order
 };
 
 // Routing of one token's fp32 logits by the tier's family [MW App. A]:
 // softmax-top-K (select the K largest logits, which are the K largest
-// probabilities; weights renormalised over the K) or sigmoid-group (biased
-// scores, top-2-sum group ranking, top-K inside surviving groups, weights
-// s * sigma / (sum sigma + 1e-20)). Ties go to the lower id. Executed by one
-// full wave (all 64 lanes active); lane 0 writes idx[K] / w[K].
+// probabilities; weights renormalised over the K, or the full softmax when
+// norm_topk is 0) or sigmoid-group (biased scores, top-2-sum group ranking,
+// top-K inside surviving groups, weights s * sigma / (sum sigma + 1e-20)).
+// Ties go to the lower id (lower group id for groups).
+//
+// One full wave (all 64 lanes active). Lane l holds candidates l + 64j as
+// 64-bit keys (order-preserving score bits, then the complemented id, so
+// the maximum key is the best score with the lowest id). Each of the K
+// rounds takes the lane-local best, the wave maximum (DPP inside rows,
+// four readlanes) and knocks the winner out. Lane 0 writes idx[K] / w[K].
 __device__ __forceinline__ void route_wave(const Dims& dm, const float* lg, const float* bias,
                                            RouteScratch& rs, int32_t* out_idx, float* out_w,
                                            int32_t* flags) {
-  float* sel_s = rs.sel;
-  float* gsc_s = rs.gsc;
-  int* keep_s = rs.keep;
   const int lane = threadIdx.x & 63;
   const int E = dm.E, K = dm.K;
+  const bool sg = dm.router_kind == E0_ROUTER_SIGMOID_GROUP;
   constexpr int kPer = kMaxE / 64;
+  const int per = (E + 63) >> 6;
 
-  float v[kPer], sig[kPer];
-  bool ok[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int e = lane + 64 * j;
-    ok[j] = e < E;
-    v[j] = ok[j] ? lg[e] : 0.0f;
-    sig[j] = 0.0f;
-  }
-  if (dm.router_kind == E0_ROUTER_SIGMOID_GROUP) {
+  if (sg) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int e = lane + 64 * j;
-      if (!ok[j]) continue;
-      sig[j] = 1.0f / (1.0f + expf(-v[j]));
-      v[j] = sig[j] + (bias ? ldg(bias + e) : 0.0f);
-      sel_s[e] = v[j];
+      if (j < per && e < E)
+        rs.sel[e] = 1.0f / (1.0f + expf(-lg[e])) + (bias ? ldg(bias + e) : 0.0f);
     }
     wave_lds_sync();
-    const int per = E / dm.n_groups;
+    // group score: sum of the two best selection scores of the group
+    const int gsize = E / dm.n_groups;
+    uint64_t gkey = 0;
     if (lane < dm.n_groups) {
       float m1 = -INFINITY, m2 = -INFINITY;
-      for (int i = 0; i < per; ++i) {
-        const float s = sel_s[lane * per + i];
-        if (s > m1) { m2 = m1; m1 = s; } else if (s > m2) { m2 = s; }
+      for (int i = 0; i < gsize; ++i) {
+        const float v = rs.sel[lane * gsize + i];
+        if (v > m1) { m2 = m1; m1 = v; } else if (v > m2) { m2 = v; }
       }
-      gsc_s[lane] = m1 + m2;
-      keep_s[lane] = 0;
+      gkey = ((uint64_t)f2key(m1 + m2) << 32) | (0xFFFFFFFFu - (uint32_t)lane);
     }
-    wave_lds_sync();
-    if (lane == 0) {
-      for (int t = 0; t < dm.topk_groups; ++t) {
-        int best = -1;
-        for (int g = 0; g < dm.n_groups; ++g)
-          if (!keep_s[g] && (best < 0 || gsc_s[g] > gsc_s[best])) best = g;
-        keep_s[best] = 1;
+    bool kept = false;
+    for (int r = 0; r < dm.topk_groups; ++r) {
+      const uint64_t g = wave_max_u64_rows(gkey);
+      if (gkey == g && g != 0) {
+        kept = true;
+        gkey = 0;
       }
     }
+    if (lane < dm.n_groups) rs.keep[lane] = kept ? 1 : 0;
     wave_lds_sync();
+  }
+
+  uint64_t key[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    key[j] = 0;
+    const int e = lane + 64 * j;
+    if (j < per && e < E) {
+      bool ok = true;
+      float score = lg[e];
+      if (sg) {
+        ok = rs.keep[e / (E / dm.n_groups)] != 0;
+        score = rs.sel[e];
+      }
+      if (ok) key[j] = ((uint64_t)f2key(score) << 32) | (0xFFFFFFFFu - (uint32_t)e);
+    }
+  }
+  int first = 0;
+  for (int k = 0; k < K; ++k) {
+    uint64_t b = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (j < per) b = key[j] > b ? key[j] : b;
+    const uint64_t g = wave_max_u64_rows(b);
+    int e = 0;
+    if (g == 0) {  // no candidate left (rejected shapes make this unreachable)
+      if (lane == 0) atomicOr(&flags[FLAG_RANGE], 4);
+    } else {
+      e = (int)(0xFFFFFFFFu - (uint32_t)g);
+    }
+    if (k == 0) first = e;
+    if (lane == 0) rs.ksel[k] = e;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (j < per && key[j] == g) key[j] = 0;
+  }
+  // softmax shift: the largest logit is the first selection
+  const float mx = lg[first];
+  float full = 0.0f;
+  if (!sg && !dm.norm_topk) {
+    float z = 0.0f;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int e = lane + 64 * j;
-      if (ok[j]) ok[j] = keep_s[e / per] != 0;
+      if (j < per && e < E) z += expf(lg[e] - mx);
     }
+    full = wave_sum_rows(z);
   }
-
-  float mx = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j)
-    if (lane + 64 * j < E) mx = fmaxf(mx, lg[lane + 64 * j]);
-  mx = wave_max_rows(mx);
-
-  float wsel[8];
-  int isel[8];
-  float denom = 0.0f;
-  for (int k = 0; k < K; ++k) {
-    uint64_t key = 0;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      if (!ok[j]) continue;
-      const uint32_t e = lane + 64 * j;
-      const uint64_t kk = ((uint64_t)f2key(v[j]) << 32) | (0xFFFFFFFFu - e);
-      key = kk > key ? kk : key;
-    }
-    key = wave_max_u64_rows(key);
-    if (key == 0) {  // no candidate left (rejected shapes make this unreachable)
-      if (lane == 0) atomicOr(&flags[FLAG_RANGE], 4);
-      key = 0xFFFFFFFFull;  // decodes to expert 0
-    }
-    const int e = (int)(0xFFFFFFFFu - (uint32_t)key);
-    isel[k] = e;
-    if (dm.router_kind == E0_ROUTER_SIGMOID_GROUP) {
-      wsel[k] = 1.0f / (1.0f + expf(-lg[e]));
-    } else {
-      wsel[k] = expf(lg[e] - mx);
-    }
-    denom += wsel[k];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j)
-      if (lane + 64 * j == e) ok[j] = false;
-  }
-  if (dm.router_kind == E0_ROUTER_SIGMOID_GROUP) {
-    denom += 1e-20f;
-  } else if (!dm.norm_topk) {
-    float z = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j)
-      if (lane + 64 * j < E) z += expf(lg[lane + 64 * j] - mx);
-    denom = wave_sum_rows(z);
-  }
+  wave_lds_sync();
   if (lane == 0) {
+    float wsel[8];
+    float denom = 0.0f;
     for (int k = 0; k < K; ++k) {
-      out_idx[k] = isel[k];
+      const float l = lg[rs.ksel[k]];
+      wsel[k] = sg ? 1.0f / (1.0f + expf(-l)) : expf(l - mx);
+      denom += wsel[k];
+    }
+    if (sg) denom += 1e-20f;
+    else if (!dm.norm_topk) denom = full;
+    for (int k = 0; k < K; ++k) {
+      out_idx[k] = rs.ksel[k];
       const float ww = wsel[k] / denom;
-      out_w[k] = dm.router_kind == E0_ROUTER_SIGMOID_GROUP ? dm.route_scale * ww : ww;
+      out_w[k] = sg ? dm.route_scale * ww : ww;
     }
   }
 }

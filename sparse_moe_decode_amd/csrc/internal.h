@@ -127,14 +127,12 @@ struct StackArgs {
   uint16_t* x_trace;
   uint16_t* h;
   uint64_t *xh, *xg, *xr, *xa, *xl;
-  uint32_t* fl;  // arrival flags [L][kExchanges][grid]: epoch of the last post
   int32_t* sink_idx;
   float* sink_w;
   int32_t* flags;
   uint64_t* trace;  // optional [G][L+1][kTracePoints] wall-clock stamps (100 MHz)
 };
-constexpr int kTracePoints = 10;
-constexpr int kExchanges = 5;  // h_out, SwiGLU outputs, router logits, head hidden, head logits
+constexpr int kTracePoints = 16;
 bool stack_supported(const Dims& dm);
 // Whether one launch over [l0, l1) (with a.n_heads head layers) fits the
 // kernel's fixed per-workgroup plans on `grid` workgroups.

@@ -25,9 +25,11 @@
 // written and polled with agent-scope relaxed atomics (coherent across the
 // XCDs' L2s without cache write-back or invalidation): an aligned 8-byte
 // access is single-copy atomic, so a word carrying the current launch's epoch
-// carries that launch's payload. Buffers are per layer, so no word is written
-// twice in one launch. Every wait is bounded by a wall-clock limit; on expiry
-// the kernel raises FLAG_SYNC and runs to completion.
+// carries that launch's payload, and a consumer polls the words themselves
+// (no separate arrival flag, so one fabric round trip per exchange). Buffers
+// are per layer, so no word is written twice in one launch. Every wait is
+// bounded by a wall-clock limit; on expiry the kernel raises FLAG_SYNC and
+// runs to completion.
 
 #include "gemv.h"
 #include "internal.h"
@@ -122,52 +124,25 @@ __device__ __forceinline__ void stamp(const StackArgs& a, int row, int k) {
     a.trace[((int64_t)blockIdx.x * (a.L + 1) + row) * kTracePoints + k] = wall_clock64();
 }
 
-enum { XH = 0, XG = 1, XR = 2, XA = 3, XL = 4 };
+// Wait for every outstanding vector memory operation. Placed only where all
+// of them are already known to be complete (their results were consumed),
+// so it costs nothing; it keeps the compiler's conservative tracking of
+// possibly pending loads across the layer loop from adding a wait later at a
+// point where exchange stores or prefetches are in flight (vector memory
+// operations retire in order, so such a wait would stall on all of them).
+__device__ __forceinline__ void vm_drained() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-__device__ __forceinline__ uint32_t* flag_row(const StackArgs& a, int l, int x) {
-  return a.fl + ((int64_t)l * kExchanges + x) * gridDim.x;
-}
 
-// This workgroup has issued its words of exchange x for layer l.
-__device__ __forceinline__ void post(const StackArgs& a, int l, int x) {
-  __syncthreads();
-  if (threadIdx.x == 0)
-    __hip_atomic_store(flag_row(a, l, x) + blockIdx.x, a.epoch, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Wait until every workgroup posted exchange x of layer l. Wave 0 polls the
-// packed flags (a few coalesced loads per round); the others wait at the
-// barrier. The words themselves are still epoch-checked when gathered.
-__device__ __forceinline__ void wait_all(const StackArgs& a, int l, int x, int* abort_lds) {
-  if ((threadIdx.x >> 6) == 0) {
-    const uint32_t* f = flag_row(a, l, x);
-    const int lane = threadIdx.x & 63;
-    const int G = (int)gridDim.x;
-    const uint64_t t0 = wall_clock64();
-    uint32_t polls = 0;
-    uint32_t v[8];
+// A struct of 8-byte fields from global memory by vector loads (per-lane
+// addresses allowed).
+template <typename T>
+__device__ __forceinline__ T ldg_struct(const T* p) {
+  static_assert(sizeof(T) % 8 == 0, "struct size");
+  const uint64_t* w = reinterpret_cast<const uint64_t*>(p);
+  uint64_t buf[sizeof(T) / 8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = lane + 64 * j;
-      v[j] = i < G ? __hip_atomic_load(f + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : a.epoch;
-    }
-    for (;;) {
-      bool ok = true;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) ok = ok && v[j] == a.epoch;
-      if (__all(ok)) break;
-      if (wait_expired(t0, a.flags, abort_lds, polls)) break;
-      __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int i = lane + 64 * j;
-        if (i < G && v[j] != a.epoch)
-          v[j] = __hip_atomic_load(f + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-  }
-  __syncthreads();
+  for (int i = 0; i < (int)(sizeof(T) / 8); ++i) buf[i] = ldg(w + i);
+  return __builtin_bit_cast(T, buf);
 }
 
 // Contiguous share [beg, end) of n items for workgroup c of G (n * G < 2^32).
@@ -205,6 +180,10 @@ struct Misc {
   int n_heads;
   uint16_t hstage[512];        // h_out rows of this workgroup (<= 512)
   int32_t hl_list[kMaxL];      // layer of head h (launch order)
+  const uint16_t* hfc1[kMaxL];  // weights of head h
+  const uint16_t* hlin[kMaxL];
+  const uint16_t* hfc2[kMaxL];
+  const float* hbias[kMaxL];
   int32_t hidx_of[kMaxL];      // head index of layer step s, or -1
   int32_t ridx_all[kMaxL * 8];
   float rw_all[kMaxL * 8];
@@ -395,9 +374,10 @@ __device__ __forceinline__ void gu_finish(const GuRegs<CPL, IPG>& R, const Dims&
 }
 
 // ---- down rows: every expert's chunk of one row per lane group ------------
+template <int NX>
 struct DownRegs {
-  uint4 w[kMaxExp];
-  uint16_t s[kMaxExp];
+  uint4 w[NX];
+  uint16_t s[NX];
   uint4 bd[kRank / 8];  // LoRA B of the down projection, row drow (lane 0 of the group)
 };
 
@@ -441,17 +421,23 @@ __device__ __forceinline__ float hilo_pair(float v0, float v1, int c, int li, ui
   return ldexpf(1.0f, e);
 }
 
-// Pending loads of phase A (before the h exchange).
-template <int CPL, int IPG>
+// Loads of a layer issued ahead of its activations: router and LoRA A rows,
+// attention update, and, once the routing is known, gate/up rows (phase A)
+// and down rows with the shared-expert LoRA matrices (phase B).
+template <int CPL, int IPG, int NX>
 struct PhaseA {
   F16Rows<kNR> router, ax;
   int n_router, n_ax;
   GuRegs<CPL, IPG> gu;
-  bool gu_loaded;
+  bool gu_loaded, b_loaded;
   uint4 attn;  // this thread's 8 elements of the attention update
+  DownRegs<NX> D;
+  LoraRegs LR;
 };
 
-template <int CPL_D, int IPG>
+// CPL_D: 16-byte chunks per lane of a d-wide int4 row; IPG: gate/up items
+// per lane group; NX: expert slots per down row (K routed + shared).
+template <int CPL_D, int IPG, int NX>
 __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
   constexpr int CPH = 4 * CPL_D;  // 16-byte chunks per lane of a d-wide fp16 head row
   extern __shared__ __align__(16) unsigned char smem[];
@@ -494,16 +480,24 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
   }
   __syncthreads();
   if (wave == 0) {  // head list (nL <= 64: one lane per layer)
-    const bool has = lane < nL && lay[lane].head.fc1 != nullptr;
+    const LayerDev* Lm = a.layers + a.l0 + (lane < nL ? lane : 0);
+    const HeadW hw = ldg_struct(&Lm->head);
+    const bool has = lane < nL && hw.fc1 != nullptr;
     const uint64_t m = __ballot(has);
     const int before = __popcll(m & ((1ull << lane) - 1ull));
     if (lane < nL) ms.hidx_of[lane] = has ? before : -1;
-    if (has) ms.hl_list[before] = a.l0 + lane;
+    if (has) {
+      ms.hl_list[before] = a.l0 + lane;
+      ms.hfc1[before] = hw.fc1;
+      ms.hlin[before] = hw.lin;
+      ms.hfc2[before] = hw.fc2;
+      ms.hbias[before] = hw.bias;
+    }
     if (lane == 0) ms.n_heads = __popcll(m);
   }
   for (int i = t; i < nL * K; i += kThreads) {
-    const int s = i / K;
-    ms.ent_all[i] = lay[s].router ? 0 : resolve_entry(lay[s].pool, E, ms.ridx_all[i]);
+    const LayerDev* Ls = a.layers + a.l0 + i / K;
+    ms.ent_all[i] = ldg(&Ls->router) ? 0 : resolve_entry(ldg_struct(&Ls->pool), E, ms.ridx_all[i]);
   }
   __syncthreads();
   const int nH = ms.n_heads;
@@ -513,9 +507,70 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
   split(nH * PE, G, cu, g0, g1);
   const int hx0 = g0 / PE, hx1 = g1 > g0 ? (g1 - 1) / PE : -1;
 
+  // down rows of this workgroup: [db, de), one per lane group
+  int db, de;
+  {
+    int wb, we;
+    split(d / 2, G, cu, wb, we);
+    db = 2 * wb;
+    de = 2 * we;
+  }
+  const int drow = db + grp;
+
+  // Phase B loads of a layer whose routed entries are in ms.ent: down rows
+  // [drow] of every expert slot, LoRA B_down row, the shared-expert LoRA
+  // matrices.
+  auto issue_b = [&](const LayerDev& Ly, PhaseA<CPL_D, IPG, NX>& A) {
+    const bool has_sh = Ly.sh.present != 0;
+    const int Is = has_sh ? dm.Is : 0;
+    const bool lora_gu = has_sh && Ly.sh.ag != nullptr;
+    const bool lora_d = has_sh && Ly.sh.ad != nullptr;
+    if (drow < de) {
+      const int wpr = I / 8, spr = I / dm.G;
+#pragma unroll
+      for (int k = 0; k < NX; ++k) {
+        A.D.w[k] = make_uint4(0, 0, 0, 0);
+        A.D.s[k] = 0;
+        const uint32_t* q = nullptr;
+        const uint16_t* sc = nullptr;
+        if (k < K) {
+          const int64_t ent = ms.ent[k];
+          if (ent >= 0) {
+            q = (const uint32_t*)entry_ptr(Ly.pool.down.q, ent, Ly.pool.stride_q);
+            sc = (const uint16_t*)entry_ptr(Ly.pool.down.s, ent, Ly.pool.stride_s);
+          }
+        } else if (k == K && has_sh) {
+          q = Ly.sh.down.q;
+          sc = Ly.sh.down.s;
+        }
+        if (!q) continue;
+        A.D.w[k] = ldg(reinterpret_cast<const uint4*>(q + (int64_t)drow * wpr + 4 * li));
+        A.D.s[k] = ldg(sc + (int64_t)drow * spr + (32 * li) / dm.G);
+      }
+#pragma unroll
+      for (int c = 0; c < kRank / 8; ++c) {
+        A.D.bd[c] = make_uint4(0, 0, 0, 0);
+        if (lora_d && li == 0)
+          A.D.bd[c] = ldg(reinterpret_cast<const uint4*>(Ly.sh.bd + (int64_t)drow * kRank + 8 * c));
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kRank / 4; ++c) {
+      A.LR.bg[c] = make_uint4(0, 0, 0, 0);
+      A.LR.bu[c] = make_uint4(0, 0, 0, 0);
+      if (lora_gu) {
+        A.LR.bg[c] = ldg(reinterpret_cast<const uint4*>(Ly.sh.bg + 2 * t * kRank + 8 * c));
+        A.LR.bu[c] = ldg(reinterpret_cast<const uint4*>(Ly.sh.bu + 2 * t * kRank + 8 * c));
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kRank; ++q)
+      A.LR.ad[q] = lora_d ? ldg(reinterpret_cast<const uint32_t*>(Ly.sh.ad + q * Is + 2 * t)) : 0u;
+    A.b_loaded = true;
+  };
+
   // Issue every load of layer l that does not depend on its activations.
-  auto issue_a = [&](int l, PhaseA<CPL_D, IPG>& A) {
-    const LayerDev& Ly = lay[l - a.l0];
+  auto issue_a = [&](int l, const LayerDev& Ly, PhaseA<CPL_D, IPG, NX>& A) {
     const bool has_sh = Ly.sh.present != 0;
     const int Is = has_sh ? dm.Is : 0;
     const int r2 = (has_sh && Ly.sh.ag) ? 2 * kRank : 0;
@@ -538,6 +593,7 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
     A.attn = make_uint4(0, 0, 0, 0);
     if (Ly.attn && t < d / 8) A.attn = ldg(reinterpret_cast<const uint4*>(Ly.attn + 8 * t));
     A.gu_loaded = false;
+    A.b_loaded = false;
     if (!Ly.router) {
       // routing known: entries from the tables
       if (t < 16) ms.ent[t] = t < K ? ms.ent_all[(l - a.l0) * K + t] : 0;
@@ -546,14 +602,17 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
       split(K * I + Is, G, cu, pl.ib, pl.ie);
       gu_issue<CPL_D, IPG>(A.gu, Ly, dm, ms, K * I, pl, grp, li);
       A.gu_loaded = true;
+      issue_b(Ly, A);
     }
   };
 
-  PhaseA<CPL_D, IPG> A;
-  issue_a(a.l0, A);
-
   for (int l = a.l0; l < a.l1; ++l) {
+    // Loads of layer l that need no activations go out first; they are in
+    // flight while h_l is gathered (their registers live within one layer).
+    stamp(a, l, 0);
     const LayerDev& Ly = lay[l - a.l0];
+    PhaseA<CPL_D, IPG, NX> A;
+    issue_a(l, Ly, A);
     const int step = l - a.l0;
     const bool has_sh = Ly.sh.present != 0;
     const int Is = has_sh ? dm.Is : 0;
@@ -565,11 +624,11 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
     const bool keep_x = hid >= hx0 && hid <= hx1;
 
     // ---- 1. h_l, attention stand-in, RMSNorm ---------------------------
-    stamp(a, l, 0);
+    stamp(a, l, 9);
     if (step > 0) {
-      wait_all(a, l - 1, XH, &ms.abort);
       ll_gather<4>(a.xh + (int64_t)(l - 1) * (d / 2), d / 2, ep, land, a.flags, &ms.abort);
     }
+    vm_drained();
     __syncthreads();
     stamp(a, l, 1);
     {
@@ -585,7 +644,9 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
           const uint4 hv = *reinterpret_cast<const uint4*>(land + 4 * t);
           hw[0] = hv.x; hw[1] = hv.y; hw[2] = hv.z; hw[3] = hv.w;
         }
-        const uint32_t aw[4] = {A.attn.x, A.attn.y, A.attn.z, A.attn.w};
+        const bool att = Ly.attn != nullptr;
+        const uint32_t aw[4] = {att ? A.attn.x : 0u, att ? A.attn.y : 0u, att ? A.attn.z : 0u,
+                                att ? A.attn.w : 0u};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           v[2 * q] = h2f((uint16_t)(hw[q] & 0xFFFF)) + h2f((uint16_t)(aw[q] & 0xFFFF));
@@ -623,13 +684,15 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
       int rb, re;
       split(E, G, cu, rb, re);
       f16rows_finish<kNR>(A.router, A.n_router, d, xnat, ms);
+      stamp(a, l, 10);
       if (t < A.n_router) ll_put(a.xr + (int64_t)l * E + rb + t, fbits(ms.rows[t]), ep);
-      post(a, l, XR);
-      wait_all(a, l, XR, &ms.abort);
+      stamp(a, l, 11);
       ll_gather<2>(a.xr + (int64_t)l * E, E, ep, land, a.flags, &ms.abort);
       __syncthreads();
+      stamp(a, l, 13);
       if (wave == 0) route_wave(dm, (const float*)land, Ly.router_bias, ms.rs, ms.ridx, ms.rw, a.flags);
       __syncthreads();
+      stamp(a, l, 14);
       if (t < 16) {
         int64_t ent = 0;
         if (t < K) {
@@ -652,7 +715,7 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
       eidx[t] = ms.ridx[t];
       ew[t] = ms.rw[t];
     }
-    if (t < kMaxExp) {
+    if (t < NX) {
       const uint32_t* q = nullptr;
       const uint16_t* sc = nullptr;
       float cf = 0.0f;
@@ -678,6 +741,7 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
       GuPlan pl;
       split(n_rt + Is, G, cu, pl.ib, pl.ie);
       if (!A.gu_loaded) gu_issue<CPL_D, IPG>(A.gu, Ly, dm, ms, n_rt, pl, grp, li);
+      vm_drained();  // gate/up rows, router and LoRA A rows have arrived
       gu_finish<CPL_D, IPG>(A.gu, dm, ms, n_rt, Is, pl, grp, li, xperm, xg, ep);
       if (A.n_ax) {
         int b, e;
@@ -685,63 +749,20 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
         f16rows_finish<kNR>(A.ax, A.n_ax, d, xnat, ms);
         if (t < A.n_ax) ll_put(xg + n_rt + 2 * Is + b + t, fbits(ms.rows[t]), ep);
       }
-      post(a, l, XG);
+      __syncthreads();  // the down-projection table of this layer is visible
     }
     stamp(a, l, 4);
 
-    // ---- phase B loads: down rows and the shared-expert LoRA matrices -------
-    int db, de;
-    {
-      int wb, we;
-      split(d / 2, G, cu, wb, we);
-      db = 2 * wb;
-      de = 2 * we;
-    }
-    DownRegs D;
-    const int drow = db + grp;
-    if (drow < de) {
-      const int wpr = I / 8, spr = I / dm.G;
-      const uint32_t* qp[kMaxExp];
-      const uint16_t* sp[kMaxExp];
-#pragma unroll
-      for (int k = 0; k < kMaxExp; ++k) {
-        qp[k] = ms.dq[k];
-        sp[k] = ms.dsc[k];
-      }
-#pragma unroll
-      for (int k = 0; k < kMaxExp; ++k) {
-        D.w[k] = make_uint4(0, 0, 0, 0);
-        D.s[k] = 0;
-        if (!qp[k]) continue;
-        D.w[k] = ldg(reinterpret_cast<const uint4*>(qp[k] + (int64_t)drow * wpr + 4 * li));
-        D.s[k] = ldg(sp[k] + (int64_t)drow * spr + (32 * li) / dm.G);
-      }
-#pragma unroll
-      for (int c = 0; c < kRank / 8; ++c) {
-        D.bd[c] = make_uint4(0, 0, 0, 0);
-        if (lora_d && li == 0)
-          D.bd[c] = ldg(reinterpret_cast<const uint4*>(Ly.sh.bd + (int64_t)drow * kRank + 8 * c));
-      }
-    }
-    LoraRegs LR;
-#pragma unroll
-    for (int c = 0; c < kRank / 4; ++c) {
-      LR.bg[c] = make_uint4(0, 0, 0, 0);
-      LR.bu[c] = make_uint4(0, 0, 0, 0);
-      if (r2) {
-        LR.bg[c] = ldg(reinterpret_cast<const uint4*>(Ly.sh.bg + 2 * t * kRank + 8 * c));
-        LR.bu[c] = ldg(reinterpret_cast<const uint4*>(Ly.sh.bu + 2 * t * kRank + 8 * c));
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < kRank; ++q)
-      LR.ad[q] = lora_d ? ldg(reinterpret_cast<const uint32_t*>(Ly.sh.ad + q * Is + 2 * t)) : 0u;
+    // ---- phase B loads (layers routed here): down rows, shared-expert LoRA --
+    if (!A.b_loaded) issue_b(Ly, A);
+    const DownRegs<NX>& D = A.D;
+    const LoraRegs& LR = A.LR;
     stamp(a, l, 5);
 
     // ---- 4. gather SwiGLU outputs; finish the shared expert ----------------
     const int ng_l = n_rt + 2 * Is + r2;
-    wait_all(a, l, XG, &ms.abort);
     ll_gather<16>(xg, ng_l, ep, land, a.flags, &ms.abort);
+    vm_drained();
     __syncthreads();
     stamp(a, l, 6);
     {
@@ -793,7 +814,7 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
     if (drow < de) {
       float acc = 0.0f;
 #pragma unroll
-      for (int k = 0; k < kMaxExp; ++k) {
+      for (int k = 0; k < NX; ++k) {
         if (!ms.dq[k]) continue;
         const uint16_t* hh = hk + (int64_t)k * 2 * I;
         f16x2 xh[16], xl[16];
@@ -815,6 +836,7 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
         acc += dm.lora_scale * lsum;
       }
       acc = group_sum<kLG>(acc);
+      vm_drained();
       if (li == 0) {
         const uint16_t hv = f2h(hattn[drow] + acc);
         a.h[(int64_t)(step + 1) * d + drow] = hv;
@@ -827,11 +849,7 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
       const uint32_t pr = (uint32_t)ms.hstage[r0] | ((uint32_t)ms.hstage[r0 + 1] << 16);
       ll_put(a.xh + (int64_t)l * (d / 2) + j, pr, ep);
     }
-    post(a, l, XH);
     stamp(a, l, 8);
-
-    if (l + 1 < a.l1) issue_a(l + 1, A);
-    stamp(a, l, 9);
   }
 
   if (nH == 0) return;
@@ -851,7 +869,7 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
     int f = f0 + r * kGroups + grp;
     f = f < f1 ? f : f1 - 1;
     const int h = nf > 0 ? f / E : 0, e = nf > 0 ? f % E : 0;
-    const uint16_t* wrow = lay[ms.hl_list[h] - a.l0].head.fc2 + (int64_t)e * P;
+    const uint16_t* wrow = ms.hfc2[h] + (int64_t)e * P;
 #pragma unroll
     for (int j = 0; j < kCPF; ++j) {
       w2[r][j] = make_uint4(0, 0, 0, 0);
@@ -871,8 +889,7 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
       g = g < g1 ? g : g1 - 1;
       const int h = g / PE, it = g % PE;
       const int s = ms.hl_list[h] - a.l0;
-      const LayerDev& Lh = lay[s];
-      const uint16_t* wrow = it < P ? Lh.head.fc1 + (int64_t)it * F : Lh.head.lin + (int64_t)(it - P) * F;
+      const uint16_t* wrow = it < P ? ms.hfc1[h] + (int64_t)it * F : ms.hlin[h] + (int64_t)(it - P) * F;
 #pragma unroll
       for (int j = 0; j < CPH; ++j) w[j] = ldg(reinterpret_cast<const uint4*>(wrow + 8 * (li + kLG * j)));
       int col = d;  // an in-row column whose value is dropped
@@ -922,12 +939,11 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
       }
     }
   }
-  post(a, a.l0, XA);
+  __syncthreads();
   stamp(a, hrow, 1);
 
   // fc2: hidden activations and linear path of the heads of this workgroup's
   // fc2 rows, as fp16 hi + lo with a power-of-two scale per lane chunk.
-  wait_all(a, a.l0, XA, &ms.abort);
   const int hf0 = nf > 0 ? f0 / E : 0, hf1 = nf > 0 ? (f1 - 1) / E : -1;
   for (int h = hf0; h <= hf1; ++h)
     ll_gather<4>(a.xa + (int64_t)ms.hl_list[h] * PE, PE, ep, land + (h - hf0) * PE, a.flags,
@@ -992,34 +1008,33 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
       if (a.head_logits) a.head_logits[(int64_t)l * E + e] = logit;
     }
   }
-  post(a, a.l0, XL);
+  __syncthreads();
   stamp(a, hrow, 3);
 
   // routing of each head's logits: the next token's prediction
   for (int h = cu; h < nH; h += G) {
     const int l = ms.hl_list[h];
-    const LayerDev& Lh = lay[l - a.l0];
-    wait_all(a, a.l0, XL, &ms.abort);
     ll_gather<2>(a.xl + (int64_t)l * E, E, ep, land, a.flags, &ms.abort);
     __syncthreads();
     int32_t* pidx = l + 1 < a.L ? a.route_idx + ((int64_t)nxt * a.L + l + 1) * K : a.sink_idx;
     float* pw = l + 1 < a.L ? a.route_w + ((int64_t)nxt * a.L + l + 1) * K : a.sink_w;
-    if (wave == 0) route_wave(dm, (const float*)land, Lh.head.bias, ms.rs, pidx, pw, a.flags);
+    if (wave == 0) route_wave(dm, (const float*)land, ms.hbias[h], ms.rs, pidx, pw, a.flags);
     __syncthreads();
   }
   stamp(a, hrow, 4);
 }
 
-template <int CPL_D, int IPG>
+template <int CPL_D, int IPG, int NX>
 hipError_t launch_stack_t(const StackArgs& a, int grid, hipStream_t st) {
   const Lds lo = lds_layout(a.dm, a.ng, a.l1 - a.l0);
   static bool attr_set = false;
   if (!attr_set) {
-    hipFuncSetAttribute((const void*)k_stack<CPL_D, IPG>,
-                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    (void)hipFuncSetAttribute((const void*)k_stack<CPL_D, IPG, NX>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     attr_set = true;
   }
-  hipLaunchKernelGGL((k_stack<CPL_D, IPG>), dim3(grid), dim3(kThreads), (size_t)lo.bytes, st, a);
+  hipLaunchKernelGGL((k_stack<CPL_D, IPG, NX>), dim3(grid), dim3(kThreads), (size_t)lo.bytes, st,
+                     a);
   return hipGetLastError();
 }
 
@@ -1041,8 +1056,7 @@ bool stack_supported(const Dims& dm) {
 bool stack_launchable(const StackArgs& a, int grid) {
   const Dims& dm = a.dm;
   const int n_heads = a.n_heads;
-  if (!stack_supported(dm) || a.l1 - a.l0 > kMaxL || a.l1 <= a.l0 || grid < 1 || grid > 512 ||
-      !a.fl)
+  if (!stack_supported(dm) || a.l1 - a.l0 > kMaxL || a.l1 <= a.l0 || grid < 1 || grid > 512)
     return false;
   if (lds_layout(dm, a.ng, a.l1 - a.l0).bytes > 160 * 1024) return false;
   // Work per workgroup must fit the fixed per-thread plans.
@@ -1066,12 +1080,14 @@ hipError_t launch_stack(const StackArgs& a, int grid, hipStream_t st) {
   const int gu_items = dm.K * dm.I + dm.Is;
   const int ipg = (gu_items + grid - 1) / grid;
   const int cpl = dm.d / 512;
-  if (ipg <= kGroups) {
-    if (cpl == 3) return launch_stack_t<3, 1>(a, grid, st);
-    if (cpl == 4) return launch_stack_t<4, 1>(a, grid, st);
+  // instantiated shapes: top-4 (5 expert slots) with one gate/up item per
+  // lane group, top-8 (9 slots) with up to two
+  if (dm.K <= 4 && ipg <= kGroups) {
+    if (cpl == 3) return launch_stack_t<3, 1, 5>(a, grid, st);
+    if (cpl == 4) return launch_stack_t<4, 1, 5>(a, grid, st);
   } else if (ipg <= 2 * kGroups) {
-    if (cpl == 3) return launch_stack_t<3, 2>(a, grid, st);
-    if (cpl == 4) return launch_stack_t<4, 2>(a, grid, st);
+    if (cpl == 3) return launch_stack_t<3, 2, 9>(a, grid, st);
+    if (cpl == 4) return launch_stack_t<4, 2, 9>(a, grid, st);
   }
   return hipErrorInvalidValue;
 }
