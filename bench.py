@@ -16,8 +16,10 @@ timed on the host cores as a CPU baseline.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -28,6 +30,43 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "35B-tier decode layer-steps/s & tokens/s at B=1; HBM GB/s as % of MI355X peak"
+KERNEL_SOURCES = ["stack.hip", "gemv.h", "device.h", "internal.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_stack_35b_stack.md")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "sparse_moe_decode_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the persistent kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if it was taken on the current
+    kernel sources (else None)."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9]+)", text)
+    if not m_hash or not m_b or m_hash.group(1) != kernel_source_hash():
+        return None
+    return int(m_b.group(1))
+
+
+def copy_probe(nbytes: int):
+    """A plain device copy of known size (calibrates the PMC byte counters)."""
+    import torch
+    src = torch.empty(nbytes // 2, dtype=torch.float16, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "launches": 3}))
 
 
 def algorithmic_bytes(dm: dict, roles: list[dict]) -> dict:
@@ -90,7 +129,12 @@ def main():
     ap.add_argument("--rho", type=float, default=0.5)
     ap.add_argument("--cpu-tokens", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="only run a plain device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -142,14 +186,21 @@ def main():
     rc = api.device_status(ctx)
     assert rc == 0, f"device status {rc}"
 
+    # Timed region: one persistent-kernel launch per token on `stream`; events
+    # on that stream bracket the whole region and each launch.
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
     torch.cuda.synchronize()
     start.record(stream)
-    for t in range(args.warmup, T):
+    for i, t in enumerate(range(args.warmup, T)):
+        ev[i][0].record(stream)
         api.layer_step(ctx, model, 0, L, state, t, h_all[t], stream)
+        ev[i][1].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
+    kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     rc = api.device_status(ctx)
     assert rc == 0, f"device status {rc}"
 
@@ -162,6 +213,8 @@ def main():
 
     ab = algorithmic_bytes(dm, roles)
     gbs = ab["total"] / (ms * 1e-3) / 1e9
+    kgbs = ab["total"] / (kernel_ms * 1e-3) / 1e9
+    traffic = measured_traffic()
     tok_s = 1000.0 / ms
     cpu = None
     if keep_host:
@@ -197,12 +250,14 @@ def main():
         "algorithmic_bytes_per_token": ab["total"],
         "roofline": {
             "bound": "hbm",
-            "kernel": "layer_step (one decode token, all 40 layers)",
-            "achieved": round(gbs, 1),
+            "kernel": "k_stack (persistent layer_step kernel: one decode token, 40 layers)",
+            "achieved": round(kgbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "frac": round(kgbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel_ms_per_launch": round(kernel_ms, 5),
+            "algorithmic_bytes_per_launch": ab["total"],
         },
         "adjacent_set_overlap": None if overlap is None else round(overlap, 3),
         "cpu_baseline": cpu,
