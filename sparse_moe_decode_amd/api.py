@@ -197,12 +197,13 @@ def head_struct(hd: dict | None) -> e0_head:
 
 
 def moe_int4_decode(ctx: Context, routed: dict, x, idx, w, y=None, shared: dict | None = None,
-                    slot_of=None, count=None, stream=None):
-    """y[b] = sum_k w[b,k] E_{idx[b,k]}(x[b]) + S(x[b]); x fp16 [B, d] on the GPU."""
+                    slot_of=None, count=None, stride: int = 0, stream=None):
+    """y[b] = sum_k w[b,k] E_{idx[b,k]}(x[b]) + S(x[b]); x fp16 [B, d] on the GPU.
+    stride: bytes between pool entries (0 = stacked per projection)."""
     B = x.shape[0]
     if y is None:
         y = torch.empty_like(x)
-    ex = experts_struct(routed, count if count is not None else ctx.dims["E"])
+    ex = experts_struct(routed, count if count is not None else ctx.dims["E"], stride, stride)
     sh = shared_struct(shared)
     _check(_lib.moe_int4_decode(ctx.handle, C.byref(ex), _ptr(slot_of),
                                 C.byref(sh) if sh is not None else None, _ptr(x), _ptr(idx),
@@ -310,6 +311,35 @@ def layer_step(ctx: Context, model: Model, layer_begin: int, layer_end: int, sta
     _check(_lib.layer_step(ctx.handle, model.handle, layer_begin, layer_end,
                            C.byref(state.struct), token, _ptr(h), _stream(stream)))
     return h
+
+
+def bundle_parts(dims: dict) -> list[tuple[str, int]]:
+    """(name, bytes) of one expert bundle in the ABI's order: gate q, up q,
+    down q (packed u32), gate s, up s, down s (fp16)."""
+    qb = dims["I"] * dims["d"] // 2
+    sb = dims["I"] * dims["d"] // dims["G"] * 2
+    return [("gate_q", qb), ("up_q", qb), ("down_q", qb), ("gate_s", sb), ("up_s", sb),
+            ("down_s", sb)]
+
+
+def pack_bundles(pool: dict, dims: dict):
+    """Host numpy pool (gate_q [n, I, d/8] u32 ... down_s [n, d, I/G] fp16) ->
+    uint8 [n, bundle] in the ABI's bundle layout (a byte re-arrangement)."""
+    import numpy as np
+    n = pool["gate_q"].shape[0]
+    cols = [np.ascontiguousarray(pool[name]).view(np.uint8).reshape(n, nb)
+            for name, nb in bundle_parts(dims)]
+    return np.concatenate(cols, axis=1)
+
+
+def bundle_view(base: int, dims: dict) -> dict:
+    """Device addresses of the six parts of bundle 0 of a bundle pool at
+    `base`; with stride = bundle bytes this is an e0_experts view."""
+    view, off = {}, 0
+    for name, nb in bundle_parts(dims):
+        view[name] = base + off
+        off += nb
+    return view
 
 
 class Stager:
