@@ -149,7 +149,11 @@ int e0_device_status(e0_ctx* ctx, void* stream);
  *   idx, w   int32 / fp32 [B, K] routing (ids in [0, E)).
  *   y        fp16 [B, d] output (round-to-nearest-even of the fp32 sum).
  * B <= max_tokens. Internal sums are fp32; q*s is never rounded to fp16 and
- * the SwiGLU intermediate stays fp32. */
+ * the SwiGLU intermediate keeps fp32 precision. B < 16 runs one GEMV per
+ * (token, expert); B >= 16 runs in chunks of up to 32 tokens grouped by
+ * expert, each expert's weights read once per chunk by int4 x fp16 MFMA
+ * tiles (fp32 group scales applied to fp32 partials) [MW §3.1 Executor
+ * paths: batched chunks take the whole-layer path]. Both are deterministic. */
 int moe_int4_decode(e0_ctx* ctx, const e0_experts* routed, const int32_t* slot_of,
                     const e0_shared* shared, const uint16_t* x, const int32_t* idx,
                     const float* w, int32_t n_tokens, uint16_t* y, void* stream);

@@ -18,6 +18,10 @@ using namespace smd;
 
 namespace {
 
+// Token count from which moe_int4_decode groups tokens by expert and runs
+// grouped int4 GEMMs on MFMA (chunks of up to 32 tokens).
+constexpr int kBatchedMin = 16;
+
 thread_local std::string g_err = "no error";
 
 int fail(int code, const char* fmt, ...) {
@@ -100,7 +104,10 @@ int e0_create(const e0_spec* spec, int32_t max_tokens, e0_ctx** out) {
   dm.router_kind = p.router_kind; dm.norm_topk = p.norm_topk; dm.n_groups = p.n_groups;
   dm.topk_groups = p.topk_groups; dm.route_scale = p.route_scale;
   dm.eps = p.rms_eps > 0 ? p.rms_eps : 1e-6f;
-  hipGetDevice(&c->device);
+  if (hipGetDevice(&c->device) != hipSuccess) {
+    delete c;
+    return fail(E0_ERR_HIP, "e0_create: no current HIP device");
+  }
 
   const int B = max_tokens;
   const int imax = dm.I > dm.Is ? dm.I : dm.Is;
@@ -111,14 +118,23 @@ int e0_create(const e0_spec* spec, int32_t max_tokens, e0_ctx** out) {
   const size_t n_p = (size_t)B * (dm.P > 0 ? dm.P : 1);
   const size_t n_e = (size_t)B * dm.E;
   auto up = [](size_t bytes) { return (bytes + 255) & ~(size_t)255; };
+  const size_t n_grp = 1 + 4 * (size_t)B * dm.K;
+  const size_t n_slot = (size_t)B * (dm.K + 1);
   const size_t bytes = up(n_gu * 4) + up(n_ax * 4) + up(n_d * 4) + up(n_d * 2) + up(n_p * 4) +
-                       2 * up(n_e * 4) + 2 * up((size_t)B * dm.K * 4) + up(N_FLAGS * 4);
+                       2 * up(n_e * 4) + 2 * up((size_t)B * dm.K * 4) + up(N_FLAGS * 4) +
+                       up(n_grp * 4) + 2 * up(n_gu * 2) + up(n_slot * 4) +
+                       up(n_slot * dm.d * 4);
   hipError_t e = hipMalloc(&c->block, bytes);
   if (e != hipSuccess) {
     delete c;
     return hip_fail(e, "e0_create: hipMalloc");
   }
-  hipMemset(c->block, 0, bytes);
+  e = hipMemset(c->block, 0, bytes);
+  if (e != hipSuccess) {
+    (void)hipFree(c->block);
+    delete c;
+    return hip_fail(e, "e0_create: hipMemset");
+  }
   char* q = (char*)c->block;
   Scratch& s = c->s;
   s.max_tokens = B;
@@ -131,14 +147,19 @@ int e0_create(const e0_spec* spec, int32_t max_tokens, e0_ctx** out) {
   s.logits = (float*)q; q += up(n_e * 4);
   s.sink_idx = (int32_t*)q; q += up((size_t)B * dm.K * 4);
   s.sink_w = (float*)q; q += up((size_t)B * dm.K * 4);
-  s.flags = (int32_t*)q;
+  s.flags = (int32_t*)q; q += up(N_FLAGS * 4);
+  s.grp = (int32_t*)q; q += up(n_grp * 4);
+  s.hh = (uint16_t*)q; q += up(n_gu * 2);
+  s.hl = (uint16_t*)q; q += up(n_gu * 2);
+  s.hexp = (float*)q; q += up(n_slot * 4);
+  s.yk = (float*)q;
   *out = c;
   return E0_OK;
 }
 
 void e0_destroy(e0_ctx* ctx) {
   if (!ctx) return;
-  hipFree(ctx->block);
+  (void)hipFree(ctx->block);
   delete ctx;
 }
 
@@ -252,6 +273,19 @@ int moe_int4_decode(e0_ctx* ctx, const e0_experts* routed, const int32_t* slot_o
     return rc;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
+  const Dims& dm = ctx->dm;
+  if (n_tokens >= kBatchedMin && batched_supported(dm)) {
+    // chunks of up to 32 tokens through the grouped MFMA path
+    for (int c0 = 0; c0 < n_tokens; c0 += 32) {
+      const int nb = n_tokens - c0 < 32 ? n_tokens - c0 : 32;
+      const uint16_t* xc = x + (int64_t)c0 * dm.d;
+      if ((e = lora_a_x(ctx, sh, xc, nb, st)) != hipSuccess) return hip_fail(e, "lora A");
+      if ((e = launch_batched(dm, pool, sh, xc, idx + (int64_t)c0 * dm.K, w + (int64_t)c0 * dm.K,
+                              nb, y + (int64_t)c0 * dm.d, ctx->s, st)) != hipSuccess)
+        return hip_fail(e, "batched chunk");
+    }
+    return E0_OK;
+  }
   if ((e = lora_a_x(ctx, sh, x, n_tokens, st)) != hipSuccess) return hip_fail(e, "lora A");
   if ((e = launch_gate_up(ctx->dm, pool, sh, x, idx, n_tokens, ctx->s, st)) != hipSuccess)
     return hip_fail(e, "gate/up");
@@ -419,8 +453,8 @@ int e0_model_create(e0_ctx* ctx, const e0_layer* layers, int32_t n_layers, e0_mo
 
 void e0_model_destroy(e0_model* model) {
   if (!model) return;
-  if (model->dev_table) hipFree(model->dev_table);
-  if (model->xbuf) hipFree(model->xbuf);
+  if (model->dev_table) (void)hipFree(model->dev_table);
+  if (model->xbuf) (void)hipFree(model->xbuf);
   delete model;
 }
 
@@ -620,8 +654,8 @@ int e0_stager_create(e0_ctx* ctx, const void* host_pool, int32_t n_layers, int32
 
 void e0_stager_destroy(e0_stager* st) {
   if (!st) return;
-  if (st->copy_list) hipFree(st->copy_list);
-  if (st->n_copies) hipFree(st->n_copies);
+  if (st->copy_list) (void)hipFree(st->copy_list);
+  if (st->n_copies) (void)hipFree(st->n_copies);
   delete st;
 }
 

@@ -69,6 +69,12 @@ struct Scratch {
   int32_t* sink_idx;  // [B][K]     prediction with no consumer layer
   float* sink_w;      // [B][K]
   int32_t* flags; // [N_FLAGS]
+  // batched chunk (16..32 tokens)
+  int32_t* grp;   // [1 + 4 B K]    experts of the chunk and their token runs
+  uint16_t* hh;   // [B][K+1][Imax] SwiGLU outputs, fp16 hi (pair-permuted)
+  uint16_t* hl;   // [B][K+1][Imax] fp16 lo
+  float* hexp;    // [B][K+1]       power-of-two scale of hh/hl
+  float* yk;      // [B][K+1][d]    per-slot down outputs
 };
 
 // ---- launchers (kernels.hip) ------------------------------------------------
@@ -108,6 +114,14 @@ hipError_t launch_route(const Dims& dm, const float* logits, const float* bias, 
 hipError_t launch_prep(const Dims& dm, const uint16_t* h, const uint16_t* attn, int B,
                        float* hattn, uint16_t* xn, const int32_t* cidx, const float* cw,
                        int32_t* eidx, float* ew, hipStream_t st);
+
+// Batched chunk of 1..32 tokens through grouped int4 GEMMs on MFMA
+// (batched.hip): y[b] = fp16(sum_k w[b,k] E_idx(x[b]) + S(x[b])). The LoRA A
+// products of the shared gate/up must already be in s.ax.
+bool batched_supported(const Dims& dm);
+hipError_t launch_batched(const Dims& dm, const Pool& pool, const SharedW& sh, const uint16_t* x,
+                          const int32_t* idx, const float* w, int B, uint16_t* y,
+                          const Scratch& s, hipStream_t st);
 
 // Persistent whole-token kernel (stack.hip). Exchange buffers hold 8-byte
 // (payload, epoch) words per layer: xh [L][d/2] h_out fp16 pairs, xg [L][ng]
