@@ -120,6 +120,148 @@ def cpu_baseline(tier: str, seed: int, roles, host_layers, toks, idx0, w0, n_tok
                        f"({n_tokens * L} layer-steps, single thread, {dt:.1f} s)")
 
 
+def run_chunk(args):
+    """Batched chunk: B=32 tokens, each with a seeded random K-set of the 256
+    experts (K in {2, 4, 8}) and Dirichlet weights, through moe_int4_decode's
+    grouped MFMA path on one 35B-tier layer. Weight bytes = the union of the
+    chunk's experts + the shared expert + its LoRA, each read once per chunk."""
+    import torch
+    from sparse_moe_decode_amd import api, synth
+    from sparse_moe_decode_amd import workloads as wl
+    tier = "35b"
+    B = 32
+    dm0 = synth.dims(tier)
+    rng = synth.rng_for(args.seed, 70)
+    pool = synth.routed_pool(rng, dm0)
+    sh = synth.shared_expert(rng, dm0)
+    dpool, dsh = wl.tree_to_dev(pool), wl.tree_to_dev(sh)
+    x = synth.f16_normal(rng, (B, dm0["d"]))
+    expert = 3 * (dm0["I"] * dm0["d"] // 2) + 3 * 2 * (dm0["I"] * dm0["d"] // dm0["G"])
+    lora = 2 * (dm0["r"] * dm0["d"] + dm0["Is"] * dm0["r"]) * 2 + (dm0["r"] * dm0["Is"] + dm0["d"] * dm0["r"]) * 2
+    lines = []
+    for K in (2, 4, 8):
+        dm = synth.dims(tier, K=K)
+        krng = synth.rng_for(args.seed, 71, K)
+        idx = np.stack([synth.random_set(krng, dm["E"], K) for _ in range(B)])
+        w = np.stack([synth.random_weights(krng, K) for _ in range(B)])
+        ctx = api.Context(dm, max_tokens=B)
+        dx = torch.from_numpy(x).cuda()
+        didx = torch.from_numpy(idx).cuda()
+        dw = torch.from_numpy(w).cuda()
+        y = torch.empty_like(dx)
+        for _ in range(args.warmup):
+            api.moe_int4_decode(ctx, dpool, dx, didx, dw, y=y, shared=dsh)
+        assert api.device_status(ctx) == 0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            api.moe_int4_decode(ctx, dpool, dx, didx, dw, y=y, shared=dsh)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        union = int(len(np.unique(idx)))
+        nbytes = union * expert + expert + lora
+        flops = 2 * B * (K + 1) * 3 * dm0["I"] * dm0["d"]
+        lines.append({"K": K, "union_experts": union, "ms_per_chunk": round(ms, 5),
+                      "tokens_per_s": round(B / ms * 1e3, 1), "weight_bytes": nbytes,
+                      "hbm_gb_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                      "hbm_frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                      "tflops": round(flops / (ms * 1e-3) / 1e12, 2)})
+    print(json.dumps({"workload": "35B-tier batched chunk: B=32 tokens, one layer, grouped int4 "
+                                  "MFMA (moe_int4_decode, B>=16 path)", "steps": args.steps,
+                      "warmup": args.warmup, "results": lines}))
+
+
+def run_staged(args):
+    """Host-staged 35B stack at batch 1 (StagedStack): routed experts of the
+    predicted layers (7-38) live in a pinned host pool, 2K HBM slots per
+    layer, staged on a side stream as soon as the head predicting the layer
+    has run; router layers keep their experts resident."""
+    import torch
+    from sparse_moe_decode_amd import api, pipeline, synth
+    from sparse_moe_decode_amd import workloads as wl
+    tier = "35b"
+    dm = synth.dims(tier)
+    roles = synth.stack_roles(tier)
+    L = len(roles)
+    K, E = dm["K"], dm["E"]
+    n_slots = 2 * K
+    cons = [l for l in range(L) if not roles[l]["router"]]
+    ci = {l: i for i, l in enumerate(cons)}
+    ctx = api.Context(dm, max_tokens=1)
+    bundle = ctx.bundle_bytes()
+    host_pool = torch.empty((len(cons), E, bundle), dtype=torch.uint8, pin_memory=True)
+    slots = torch.zeros((len(cons), n_slots, bundle), dtype=torch.uint8, device="cuda")
+    slot_of = torch.empty((len(cons), E), dtype=torch.int32, device="cuda")
+    slot_expert = torch.empty((len(cons), n_slots), dtype=torch.int32, device="cuda")
+    layers = []
+    t_build = time.perf_counter()
+    for l, role in enumerate(roles):
+        lw = synth.layer(args.seed, l, dm, role, zero_mean=True)
+        lay = dict(shared=wl.tree_to_dev(lw["shared"]), attn=wl.to_dev(lw["attn"]),
+                   router=None if lw["router"] is None else wl.to_dev(lw["router"]),
+                   router_bias=(None if lw["router_bias"] is None
+                                else wl.to_dev(lw["router_bias"])),
+                   head=wl.tree_to_dev(lw["head"]))
+        if l in ci:
+            host_pool[ci[l]].copy_(torch.from_numpy(api.pack_bundles(lw["routed"], dm)))
+            lay.update(routed=api.bundle_view(slots[ci[l]].data_ptr(), dm), count=n_slots,
+                       stride_q=bundle, stride_s=bundle, slot_of=slot_of[ci[l]])
+        else:
+            lay["routed"] = wl.tree_to_dev(lw["routed"])
+        layers.append(lay)
+        del lw
+        print(f"[bench] staged workload: layer {l + 1}/{L} built", file=sys.stderr, flush=True)
+    t_build = time.perf_counter() - t_build
+    stager = api.Stager(ctx, host_pool, len(cons), n_slots, slots, slot_of, slot_expert)
+    model = api.Model(ctx, layers)
+    state = api.State(dm, L, head_logits=False, x_trace=False)
+    idx0, w0 = wl.initial_routing(tier, args.seed, L)
+    state.route_idx[0].copy_(torch.from_numpy(idx0))
+    state.route_w[0].copy_(torch.from_numpy(w0))
+    T = args.warmup + args.steps
+    toks = wl.token_inputs(tier, args.seed, T, args.rho)
+    h_all = torch.zeros((T, L + 1, dm["d"]), dtype=torch.float16, device="cuda")
+    h_all[:, 0].copy_(torch.from_numpy(toks))
+    pipe = pipeline.StagedStack(ctx, model, state, stager, cons, L)
+    main = pipe.main
+    pipe.stage(0, after_token=False)
+    sets = []
+    for t in range(args.warmup):
+        pipe.run_token(t, h_all[t])
+        sets.append(pipe.sets[t & 1].clone())
+    torch.cuda.synchronize()
+    assert api.device_status(ctx) == 0
+    print("[bench] staged workload: warmup done", file=sys.stderr, flush=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(main)
+    for t in range(args.warmup, T):
+        pipe.run_token(t, h_all[t])
+    e1.record(main)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    assert api.device_status(ctx) == 0
+    st = torch.stack(sets).cpu().numpy()[:, cons]          # [warmup, n_cons, K]
+    new_ids = np.array([[len(set(st[t, i]) - set(st[t - 1, i])) for i in range(len(cons))]
+                        for t in range(1, len(st))], np.float64)
+    mean_new = float(new_ids.mean()) if new_ids.size else float("nan")
+    h2d = mean_new * len(cons) * bundle
+    print(json.dumps({
+        "workload": "35B-tier host-staged decode stack, batch 1: experts of the 32 predicted "
+                    "layers streamed from pinned host memory into 2K HBM slots per layer by "
+                    "stage_experts on a side stream; router layers resident",
+        "steps": args.steps, "warmup": args.warmup, "rho": args.rho,
+        "ms_per_token": round(ms, 4), "tokens_per_s": round(1000.0 / ms, 2),
+        "adjacent_set_overlap": round(1.0 - mean_new / K, 3),
+        "new_experts_per_layer_token": round(mean_new, 3),
+        "bundle_bytes": bundle,
+        "h2d_bytes_per_token_est": int(h2d),
+        "h2d_gb_per_s_est": round(h2d / (ms * 1e-3) / 1e9, 1),
+        "pinned_pool_GB": round(host_pool.numel() / 1e9, 2), "build_s": round(t_build, 1)}))
+    stager.close()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -131,9 +273,18 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
+    ap.add_argument("--workload", choices=["stack", "chunk", "staged"], default="stack",
+                    help="stack: the 40-layer resident decode (the bench line); chunk: the "
+                         "B=32 batched chunk; staged: the host-staged stack")
     args = ap.parse_args()
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.workload != "stack":
+        if args.gpus != 1:
+            print("bench.py measures one GPU (run with --gpus 1)", file=sys.stderr)
+            sys.exit(2)
+        (run_chunk if args.workload == "chunk" else run_staged)(args)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:

@@ -1,0 +1,123 @@
+"""GPU parity of the host-staged decode pipeline (pipeline.StagedStack).
+
+Predicted layers read their routed experts through HBM slot pools that
+stage_experts fills from a pinned host pool on a side stream while earlier
+layers of the same token still run. Per token, after the pipeline (including
+the staging of the next token's sets) has drained:
+  * every (token, layer) step matches the oracle, re-anchored on the GPU's
+    own inputs (stack_check.py), exactly as for resident pools;
+  * each predicted layer's slot tables equal the oracle slot policy run on
+    (new = next token's prediction, in use = this token's set), bit-exact;
+  * every held slot holds its expert's host bundle, byte for byte.
+"""
+
+import numpy as np
+import pytest
+
+from gpu_util import announce, dev, host
+from stack_check import StackChecker
+from sparse_moe_decode_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def api():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_moe_decode_amd import api as _api
+    return _api
+
+
+# router + head, three predicted layers (the last without a head), router
+ROLES = [dict(router=True, head=True), dict(router=False, head=True),
+         dict(router=False, head=True), dict(router=False, head=False),
+         dict(router=True, head=False)]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("tier,T", [("35b", 5), ("8b", 4)])
+def test_staged_stack_matches_oracle(api, orc, tier, T):
+    import torch
+    from sparse_moe_decode_amd import pipeline
+    from sparse_moe_decode_amd import workloads as wl
+    dm = synth.dims(tier)
+    E, K, L = dm["E"], dm["K"], len(ROLES)
+    n_slots = 2 * K
+    seed = 41
+    cons = [l for l in range(L) if not ROLES[l]["router"]]
+    ci = {l: i for i, l in enumerate(cons)}
+    ctx = api.Context(dm, max_tokens=1)
+    bundle = ctx.bundle_bytes()
+    host_pool = torch.empty((len(cons), E, bundle), dtype=torch.uint8, pin_memory=True)
+    hbm = torch.zeros((len(cons), n_slots, bundle), dtype=torch.uint8, device="cuda")
+    slot_of = torch.empty((len(cons), E), dtype=torch.int32, device="cuda")
+    slot_expert = torch.empty((len(cons), n_slots), dtype=torch.int32, device="cuda")
+    layers, keep = [], {}
+    for l, role in enumerate(ROLES):
+        announce("upload", tier, f"layer {l}/{L}")
+        lw = synth.layer(seed, l, dm, role, zero_mean=True)
+        keep[l] = lw
+        lay = dict(shared=wl.tree_to_dev(lw["shared"]), attn=dev(lw["attn"]),
+                   router=None if lw["router"] is None else dev(lw["router"]),
+                   router_bias=None if lw["router_bias"] is None else dev(lw["router_bias"]),
+                   head=wl.tree_to_dev(lw["head"]))
+        if l in ci:
+            host_pool[ci[l]].copy_(torch.from_numpy(api.pack_bundles(lw["routed"], dm)))
+            lay.update(routed=api.bundle_view(hbm[ci[l]].data_ptr(), dm), count=n_slots,
+                       stride_q=bundle, stride_s=bundle, slot_of=slot_of[ci[l]])
+        else:
+            lay["routed"] = wl.tree_to_dev(lw["routed"])
+        layers.append(lay)
+    host_dev = host_pool.to("cuda")
+    stager = api.Stager(ctx, host_pool, len(cons), n_slots, hbm, slot_of, slot_expert)
+    model = api.Model(ctx, layers)
+    state = api.State(dm, L)
+    idx0, w0 = wl.initial_routing(tier, seed, L)
+    state.route_idx[0].copy_(torch.from_numpy(idx0))
+    state.route_w[0].copy_(torch.from_numpy(w0))
+    toks = wl.token_inputs(tier, seed, T)
+    checker = StackChecker(orc, tier, seed, ROLES, list(range(L)), keep, zero_mean=True)
+    pipe = pipeline.StagedStack(ctx, model, state, stager, cons, L)
+
+    o_slot_of = np.full((len(cons), E), -1, np.int32)
+    o_slot_exp = np.full((len(cons), n_slots), -1, np.int32)
+    for i, l in enumerate(cons):
+        orc.slot_policy(E, n_slots, K, o_slot_of[i], o_slot_exp[i], None, idx0[l])
+    pipe.stage(0, after_token=False)
+    prev_exec = None
+    h = torch.zeros((L + 1, dm["d"]), dtype=torch.float16, device="cuda")
+    copies = 0
+    for t in range(T):
+        announce("staged layer_step", tier, f"L={L}", f"token {t}")
+        h[0].copy_(torch.from_numpy(toks[t]))
+        pipe.run_token(t, h)
+        torch.cuda.synchronize()
+        assert api.device_status(ctx) == 0
+        cur, nxt = t & 1, (t + 1) & 1
+        exec_idx = host(state.exec_idx[cur]).copy()
+        route_cur = host(state.route_idx[cur]).copy()
+        route_nxt = host(state.route_idx[nxt]).copy()
+        checker.check(t, host(h).copy(), host(state.x_trace).copy(), exec_idx,
+                      host(state.exec_w[cur]).copy(), prev_exec, route_cur,
+                      host(state.route_w[cur]).copy(), route_nxt,
+                      host(state.route_w[nxt]).copy(), host(state.head_logits).copy())
+        prev_exec = exec_idx
+        # the staging of token t+1 has run: compare with the oracle slot policy
+        for i, l in enumerate(cons):
+            copies += len(orc.slot_policy(E, n_slots, K, o_slot_of[i], o_slot_exp[i],
+                                          route_cur[l], route_nxt[l]))
+        g_slot_of, g_slot_exp = host(slot_of), host(slot_expert)
+        assert np.array_equal(g_slot_of, o_slot_of), f"slot_of differs after token {t}"
+        assert np.array_equal(g_slot_exp, o_slot_exp), f"slot_expert differs after token {t}"
+        for i, l in enumerate(cons):
+            assert np.all(g_slot_of[i][route_nxt[l]] >= 0)
+            for s, e in enumerate(g_slot_exp[i]):
+                if e >= 0:
+                    assert torch.equal(hbm[i, s], host_dev[i, e]), f"t={t} l={l} slot {s}"
+    print(f"{tier} staged L={L}: {checker.steps} layer-steps checked, worst error ratio "
+          f"{checker.worst:.3f}, {copies} bundle copies after the first token")
+    stager.close()
+    model.close()
+    ctx.close()
