@@ -121,10 +121,14 @@ def cpu_baseline(tier: str, seed: int, roles, host_layers, toks, idx0, w0, n_tok
 
 
 def run_chunk(args):
-    """Batched chunk: B=32 tokens, each with a seeded random K-set of the 256
-    experts (K in {2, 4, 8}) and Dirichlet weights, through moe_int4_decode's
-    grouped MFMA path on one 35B-tier layer. Weight bytes = the union of the
-    chunk's experts + the shared expert + its LoRA, each read once per chunk."""
+    """Batched chunk: B=32 independent N(0,1) fp16 tokens on one 35B-tier layer
+    (K in {2, 4, 8}), routed by the layer's fp16 router with softmax top-K,
+    then moe_int4_decode's grouped MFMA path. The routing runs on the GPU
+    through prerouter_forward with a head whose fc1 and fc2 are zero and whose
+    linear path is [router | 0 | 0] (its logits are the router's exactly);
+    it is input preparation, outside the timed loop. Weight bytes = the union
+    of the chunk's experts + the shared expert + its LoRA, each read once per
+    chunk."""
     import torch
     from sparse_moe_decode_amd import api, synth
     from sparse_moe_decode_amd import workloads as wl
@@ -134,20 +138,27 @@ def run_chunk(args):
     rng = synth.rng_for(args.seed, 70)
     pool = synth.routed_pool(rng, dm0)
     sh = synth.shared_expert(rng, dm0)
+    router, _ = synth.router(rng, dm0)
     dpool, dsh = wl.tree_to_dev(pool), wl.tree_to_dev(sh)
+    d, E, P = dm0["d"], dm0["E"], dm0["P"]
+    as_head = dict(fc1=torch.zeros((P, d + 2 * E), dtype=torch.float16, device="cuda"),
+                   fc2=torch.zeros((E, P), dtype=torch.float16, device="cuda"),
+                   lin=torch.cat([wl.to_dev(router),
+                                  torch.zeros((E, 2 * E), dtype=torch.float16, device="cuda")],
+                                 dim=1).contiguous())
     x = synth.f16_normal(rng, (B, dm0["d"]))
     expert = 3 * (dm0["I"] * dm0["d"] // 2) + 3 * 2 * (dm0["I"] * dm0["d"] // dm0["G"])
     lora = 2 * (dm0["r"] * dm0["d"] + dm0["Is"] * dm0["r"]) * 2 + (dm0["r"] * dm0["Is"] + dm0["d"] * dm0["r"]) * 2
     lines = []
     for K in (2, 4, 8):
         dm = synth.dims(tier, K=K)
-        krng = synth.rng_for(args.seed, 71, K)
-        idx = np.stack([synth.random_set(krng, dm["E"], K) for _ in range(B)])
-        w = np.stack([synth.random_weights(krng, K) for _ in range(B)])
         ctx = api.Context(dm, max_tokens=B)
         dx = torch.from_numpy(x).cuda()
-        didx = torch.from_numpy(idx).cuda()
-        dw = torch.from_numpy(w).cuda()
+        krng = synth.rng_for(args.seed, 71, K)
+        cur = wl.to_dev(np.stack([synth.random_set(krng, E, K) for _ in range(B)]))
+        didx, dw = api.prerouter_forward(ctx, as_head, dx, cur)
+        torch.cuda.synchronize()
+        idx = didx.cpu().numpy()
         y = torch.empty_like(dx)
         for _ in range(args.warmup):
             api.moe_int4_decode(ctx, dpool, dx, didx, dw, y=y, shared=dsh)
@@ -262,6 +273,103 @@ def run_staged(args):
     stager.close()
 
 
+def layer_step_bytes(dm: dict) -> int:
+    """Algorithmic weight bytes of one predicted layer-step with a head: K
+    routed experts + shared expert + LoRA + head (fc1/lin read over the d dense
+    columns and the 2K gathered one-hot columns, fc2 whole)."""
+    d, E, K, I, Is, P, G, r = (dm[k] for k in ("d", "E", "K", "I", "Is", "P", "G", "r"))
+    expert = 3 * (I * d // 2) + 3 * 2 * (I * d // G)
+    shared = 3 * (Is * d // 2) + 3 * 2 * (Is * d // G)
+    lora = 2 * 2 * (r * d + Is * r) + 2 * (r * Is + d * r)
+    head = 2 * P * (d + 2 * K) + 2 * E * P + 2 * E * (d + 2 * K)
+    return K * expert + shared + lora + head
+
+
+def run_layer(args):
+    """Single-layer decode (one predicted layer with its head, batch 1), 8B and
+    35B tiers: each step is one layer_step launch consuming the next set of a
+    Markov chain (each id kept with probability 0.7) with Dirichlet weights.
+    Warm: one copy of the layer's weights (reused from the caches between
+    steps). Cold: 48 rotated copies, so a step's weights were last touched 47
+    steps earlier (reuse distance beyond the last-level cache)."""
+    import types
+    import torch
+    from sparse_moe_decode_amd import api, synth
+    from sparse_moe_decode_amd import workloads as wl
+    T, R = args.steps, 5
+    results = []
+    for tier in ("8b", "35b"):
+        dm = synth.dims(tier)
+        d, K, E = dm["d"], dm["K"], dm["E"]
+        lw = synth.layer(args.seed, 0, dm, dict(router=False, head=True))
+        base = dict(routed=wl.tree_to_dev(lw["routed"]), shared=wl.tree_to_dev(lw["shared"]),
+                    attn=wl.to_dev(lw["attn"]), router=None, router_bias=None,
+                    head=wl.tree_to_dev(lw["head"]))
+        del lw
+        ctx = api.Context(dm, max_tokens=1)
+        rng = synth.rng_for(args.seed, 30_000)
+        sets = synth.markov_sets(rng, E, K, T + 1, keep=0.7)
+        wts = np.stack([synth.random_weights(rng, K) for _ in range(T + 1)])
+        toks = wl.token_inputs(tier, args.seed, T + 1)
+        for copies in (1, 48):
+            layers = [base] + [{k: ({n: t.clone() for n, t in v.items()} if isinstance(v, dict)
+                                    else (v.clone() if v is not None else None))
+                                for k, v in base.items()} for _ in range(copies - 1)]
+            model = api.Model(ctx, layers)
+            n = copies
+            # per-step private routing / exec blocks [T+1][2][n][K]
+            ri = np.zeros((T + 1, 2, n, K), np.int32)
+            rw = np.zeros((T + 1, 2, n, K), np.float32)
+            ei = np.zeros((T + 1, 2, n, K), np.int32)
+            ew = np.zeros((T + 1, 2, n, K), np.float32)
+            for t in range(T + 1):
+                c = t % n
+                ri[t, t & 1, c] = sets[t]
+                rw[t, t & 1, c] = wts[t]
+                if t > 0:
+                    ei[t, (t + 1) & 1, c] = sets[t - 1]
+                    ew[t, (t + 1) & 1, c] = wts[t - 1]
+            dri, drw, dei, dew = (torch.from_numpy(a).cuda() for a in (ri, rw, ei, ew))
+            states = [types.SimpleNamespace(struct=api.e0_state(
+                dri[t].data_ptr(), drw[t].data_ptr(), dei[t].data_ptr(), dew[t].data_ptr(),
+                None, None)) for t in range(T + 1)]
+            h = torch.zeros((T + 1, 2, d), dtype=torch.float16, device="cuda")
+            h[:, 0].copy_(torch.from_numpy(toks))
+            main = torch.cuda.current_stream()
+            for t in range(min(args.warmup, T)):
+                api.layer_step(ctx, model, t % n, t % n + 1, states[t], t, h[t], main)
+            torch.cuda.synchronize()
+            assert api.device_status(ctx) == 0
+            times = []
+            for _ in range(R):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(main)
+                for t in range(1, T + 1):
+                    api.layer_step(ctx, model, t % n, t % n + 1, states[t], t, h[t], main)
+                e1.record(main)
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1) * 1e3 / T)
+            assert api.device_status(ctx) == 0
+            us = float(np.median(times))
+            nbytes = layer_step_bytes(dm)
+            results.append({"tier": tier, "cache": "warm" if copies == 1 else "cold (48 copies)",
+                            "us_per_layer_step": round(us, 3),
+                            "us_range": [round(min(times), 3), round(max(times), 3)],
+                            "layer_steps_per_s": round(1e6 / us, 1),
+                            "algorithmic_bytes": nbytes,
+                            "gb_per_s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                            "hbm_frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
+            print(json.dumps(results[-1]), file=sys.stderr, flush=True)
+            model.close()
+            del layers, dri, drw, dei, dew, h
+        ctx.close()
+        del base
+        torch.cuda.empty_cache()
+    print(json.dumps({"workload": "single predicted layer-step with head, batch 1, one "
+                                  "layer_step launch per step (8B and 35B tiers)",
+                      "steps": T, "repeats": R, "results": results}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -273,9 +381,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
-    ap.add_argument("--workload", choices=["stack", "chunk", "staged"], default="stack",
+    ap.add_argument("--workload", choices=["stack", "chunk", "staged", "layer"], default="stack",
                     help="stack: the 40-layer resident decode (the bench line); chunk: the "
-                         "B=32 batched chunk; staged: the host-staged stack")
+                         "B=32 batched chunk; staged: the host-staged stack; layer: single "
+                         "layer-steps, warm and cold")
     args = ap.parse_args()
     if args.copy_probe:
         copy_probe(args.copy_probe)
@@ -284,7 +393,7 @@ def main():
         if args.gpus != 1:
             print("bench.py measures one GPU (run with --gpus 1)", file=sys.stderr)
             sys.exit(2)
-        (run_chunk if args.workload == "chunk" else run_staged)(args)
+        dict(chunk=run_chunk, staged=run_staged, layer=run_layer)[args.workload](args)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:

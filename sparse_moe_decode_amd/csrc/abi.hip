@@ -279,7 +279,6 @@ int moe_int4_decode(e0_ctx* ctx, const e0_experts* routed, const int32_t* slot_o
     for (int c0 = 0; c0 < n_tokens; c0 += 32) {
       const int nb = n_tokens - c0 < 32 ? n_tokens - c0 : 32;
       const uint16_t* xc = x + (int64_t)c0 * dm.d;
-      if ((e = lora_a_x(ctx, sh, xc, nb, st)) != hipSuccess) return hip_fail(e, "lora A");
       if ((e = launch_batched(dm, pool, sh, xc, idx + (int64_t)c0 * dm.K, w + (int64_t)c0 * dm.K,
                               nb, y + (int64_t)c0 * dm.d, ctx->s, st)) != hipSuccess)
         return hip_fail(e, "batched chunk");

@@ -34,6 +34,7 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kCols = 32;  // tokens per MFMA column block
+constexpr int kMaxR = 32;  // largest LoRA rank of the shared expert
 
 // Grouping tables in s.grp (int32): [0] union size; then sorted entries
 // (b*K + k) [BK]; expert, first sorted position and run length per union
@@ -50,52 +51,114 @@ __host__ __device__ inline Groups groups(int32_t* g, int BK) {
   return {g, g + 1, g + 1 + BK, g + 1 + 2 * BK, g + 1 + 3 * BK};
 }
 
-__global__ __launch_bounds__(256) void k_mb_group(int E, int K, int B, const int32_t* idx,
-                                                  int32_t* grp, int32_t* flags) {
+struct MbArgs {
+  Dims dm;
+  Pool pool;
+  SharedW sh;
+  int B;
+  const uint16_t* x;     // [B][d] input, natural order
+  uint16_t* xp;          // [B][d] pair-permuted copy
+  int32_t* grp;
+  const int32_t* idx;    // [B][K]
+  const float* w;        // [B][K]
+  float* ax;             // [B][3*rmax] LoRA A products (gate, up, down)
+  int rmax;
+  float* H;              // [B][K+1][imax] SwiGLU outputs
+  uint16_t* hh;          // [B][K+1][imax] fp16 hi, pair-permuted
+  uint16_t* hl;
+  float* hexp;           // [B][K+1] power-of-two scale of hh/hl
+  float* Y;              // [B][K+1][d] per-slot down outputs
+  uint16_t* y;           // [B][d]
+  int32_t* flags;
+};
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int l = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(v, off);
+    if (l >= off) v += t;
+  }
+  return v;
+}
+
+// Block B of k_mb_prep: the chunk's B*K entries sorted by expert (ascending
+// expert id, then entry order), the union of experts and each member's run.
+// Integer counting only, so the result does not depend on thread timing.
+__device__ void group_entries(const MbArgs& a) {
   __shared__ int cnt[kMaxE];
-  __shared__ int off[kMaxE];
-  const int BK = B * K;
-  Groups g = groups(grp, BK);
-  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+  __shared__ __align__(16) int sidx[256];
+  __shared__ int wtot[2][4];
+  const int E = a.dm.E, K = a.dm.K, BK = a.B * K;
+  const Groups g = groups(a.grp, BK);
+  const int t = threadIdx.x;
+  for (int e = t; e < kMaxE; e += blockDim.x) cnt[e] = 0;
   __syncthreads();
-  const int i = threadIdx.x;
   int e = -1;
-  if (i < BK) {
-    e = idx[i];
+  if (t < BK) {
+    e = a.idx[t];
     if (e < 0 || e >= E) {
-      atomicOr(&flags[FLAG_RANGE], 1);
+      atomicOr(&a.flags[FLAG_RANGE], 1);
       e = -1;
     } else {
       atomicAdd(&cnt[e], 1);  // integer counts: order-independent
     }
+    sidx[t] = e;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int o = 0, u = 0;
-    for (int x = 0; x < E; ++x) {
-      off[x] = o;
-      if (cnt[x]) {
-        g.uexp[u] = x;
-        g.ustart[u] = o;
-        g.ucount[u] = cnt[x];
-        ++u;
-      }
-      o += cnt[x];
-    }
-    *g.n_union = u;
+  // thread t owns experts 2t and 2t+1 (E <= 512)
+  const int c0 = cnt[2 * t], c1 = cnt[2 * t + 1];
+  int ps = wave_incl_scan(c0 + c1);
+  int pu = wave_incl_scan((c0 > 0) + (c1 > 0));
+  const int wv = t >> 6;
+  if ((t & 63) == 63) {
+    wtot[0][wv] = ps;
+    wtot[1][wv] = pu;
   }
+  __syncthreads();
+  for (int v = 0; v < wv; ++v) {
+    ps += wtot[0][v];
+    pu += wtot[1][v];
+  }
+  const int off0 = ps - c0 - c1;
+  int u = pu - (c0 > 0) - (c1 > 0);
+  if (c0) {
+    g.uexp[u] = 2 * t;
+    g.ustart[u] = off0;
+    g.ucount[u] = c0;
+    ++u;
+  }
+  if (c1) {
+    g.uexp[u] = 2 * t + 1;
+    g.ustart[u] = off0 + c0;
+    g.ucount[u] = c1;
+  }
+  if (t == blockDim.x - 1) *g.n_union = pu;
+  __syncthreads();
+  // cnt becomes the exclusive offsets
+  cnt[2 * t] = off0;
+  cnt[2 * t + 1] = off0 + c0;
   __syncthreads();
   if (e >= 0) {
     int rank = 0;  // earlier entries routed to the same expert
-    for (int j = 0; j < i; ++j) rank += idx[j] == e;
-    g.sorted[off[e] + rank] = i;
+    const int4* s4 = reinterpret_cast<const int4*>(sidx);
+    int j = 0;
+    for (; j + 4 <= t; j += 4) {
+      const int4 v = s4[j >> 2];
+      rank += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
+    }
+    for (; j < t; ++j) rank += sidx[j] == e;
+    g.sorted[cnt[e] + rank] = t;
   }
 }
 
-__global__ __launch_bounds__(256) void k_mb_xperm(const uint16_t* x, int d, uint16_t* xp) {
-  const int b = blockIdx.x;
+// Blocks 0..B-1 of k_mb_prep: token b's pair-permuted x.
+__device__ void prep_token(const MbArgs& a, int b) {
+  const int d = a.dm.d;
+  const uint16_t* xb = a.x + (int64_t)b * d;
   for (int c = threadIdx.x; c < d / 8; c += blockDim.x) {
-    const uint4 v = ldg(reinterpret_cast<const uint4*>(x + (int64_t)b * d + 8 * c));
+    const uint4 v = ldg(reinterpret_cast<const uint4*>(xb + 8 * c));
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint16_t e[8];
 #pragma unroll
@@ -103,10 +166,48 @@ __global__ __launch_bounds__(256) void k_mb_xperm(const uint16_t* x, int d, uint
       e[2 * q] = (uint16_t)(w[q] & 0xFFFF);
       e[2 * q + 1] = (uint16_t)(w[q] >> 16);
     }
-    *reinterpret_cast<uint4*>(xp + (int64_t)b * d + 8 * c) =
+    *reinterpret_cast<uint4*>(a.xp + (int64_t)b * d + 8 * c) =
         make_uint4(e[0] | ((uint32_t)e[4] << 16), e[1] | ((uint32_t)e[5] << 16),
                    e[2] | ((uint32_t)e[6] << 16), e[3] | ((uint32_t)e[7] << 16));
   }
+}
+
+// LoRA blocks of k_mb_prep: each wave one output o of ax[b] = (A_gate x_b,
+// A_up x_b), o in [0, 2r).
+__device__ void prep_lora(const MbArgs& a, int lb) {
+  const int d = a.dm.d, r = a.dm.r, per = (2 * r + 3) / 4;
+  const int b = lb / per, o = (lb % per) * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (b >= a.B || o >= 2 * r) return;
+  const uint16_t* xb = a.x + (int64_t)b * d;
+  {
+    const uint16_t* A = (o < r ? a.sh.ag : a.sh.au) + (int64_t)(o % r) * d;
+    float s = 0.0f;
+    for (int c = lane; c < d / 8; c += 64) {
+      const uint4 av = ldg(reinterpret_cast<const uint4*>(A + 8 * c));
+      const uint4 xv = ldg(reinterpret_cast<const uint4*>(xb + 8 * c));
+      const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f16x2 ah = as_h2(aw[q]), xh = as_h2(xw[q]);
+        s = fmaf((float)ah.x, (float)xh.x, s);
+        s = fmaf((float)ah.y, (float)xh.y, s);
+      }
+    }
+    s = wave_sum_rows(s);
+    if (lane == 0) a.ax[(int64_t)b * 3 * a.rmax + (o < r ? 0 : a.rmax) + o % r] = s;
+  }
+}
+
+// Grid: B token blocks, one grouping block, then B*ceil(2r/4) LoRA blocks
+// when the shared expert has LoRA.
+__global__ __launch_bounds__(256) void k_mb_prep(MbArgs a) {
+  const int bx = blockIdx.x;
+  if (bx < a.B)
+    prep_token(a, bx);
+  else if (bx == a.B)
+    group_entries(a);
+  else
+    prep_lora(a, bx - a.B - 1);
 }
 
 // Eight int4 weights of one word as exact fp16 integers, in the order
@@ -129,98 +230,126 @@ __device__ __forceinline__ h8 q4_to_h8(uint32_t w) {
 
 __device__ __forceinline__ h8 as_h8(uint4 v) { return __builtin_bit_cast(h8, v); }
 
-// Row held in accumulator register r by a lane of half kh (MFMA 32x32 layout).
-__device__ __forceinline__ int acc_row(int r, int kh) { return 8 * (r >> 2) + 4 * kh + (r & 3); }
+__device__ __forceinline__ uint32_t word(const uint4& v, int j) {
+  return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+}
 
-// One 32-row tile of an int4 matrix against 32 activation columns, over
-// n_in inputs: acc (fp32) += sum over groups of scale[row][group] *
-// (q . x)_group. `act(g, j)` returns the lane's 8 activations (pair-permuted
-// fp16) for MFMA j of input block g (64 inputs).
-template <typename Act>
-__device__ __forceinline__ void tile_mma(const uint32_t* rows, int wpr, const uint16_t* sc_lds,
-                                         int n_groups_s, int G, int n_in, Act act, f32x16& acc) {
-  const int l = threadIdx.x & 63, lm = l & 31, kh = l >> 5;
-  const uint32_t* arow = rows + (int64_t)lm * wpr;
-  for (int g = 0; g < n_in / 64; ++g) {
-    const uint4 wv = ldg(reinterpret_cast<const uint4*>(arow + 8 * g + 4 * kh));
-    const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+// MFMA 32x32x16 layout with the chunk's tokens as operand A and 32 weight rows
+// as operand B: lane l supplies token row l%32 and weight row l%32 over the
+// k-slice 8*(l/32)..+8; accumulator register r of lane l holds token row
+// tok_row(r, l/32) of weight row l%32.
+__device__ __forceinline__ int tok_row(int r, int kh) { return 8 * (r >> 2) + 4 * kh + (r & 3); }
+
+// acc[r] += s * c[r] for the NR registers that can hold a valid token: count
+// tokens occupy rows 0..count-1, i.e. registers r < NR = 4*ceil(count/8).
+template <int NR>
+__device__ __forceinline__ void scale_add(f32x16& acc, const f32x16& c, float s) {
+#pragma unroll
+  for (int r = 0; r < NR; ++r) acc[r] = fmaf(s, c[r], acc[r]);
+}
+
+// Multiply-accumulate of one wave: NG groups of 64 inputs, weights wv (one
+// word per lane per MFMA), activations xv of the lane's token row
+// (pair-permuted fp16), group scales sv.
+template <int NG, int NR>
+__device__ __forceinline__ f32x16 gu_mma(const uint4 (&wv)[NG], const float (&sv)[NG],
+                                         const uint4 (&xv)[NG][4]) {
+  f32x16 acc = {};
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
     f32x16 c = {};
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      c = __builtin_amdgcn_mfma_f32_32x32x16_f16(q4_to_h8(ww[j]), act(g, j), c, 0, 0, 0);
-    const int s = (64 * g) / G;
+      c = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(xv[i][j]), q4_to_h8(word(wv[i], j)), c,
+                                                0, 0, 0);
+    scale_add<NR>(acc, c, sv[i]);
+  }
+  return acc;
+}
+
+// Down multiply-accumulate: hi and lo activation rows (in LDS) through the
+// same dequantised weights.
+template <int NG, int NR>
+__device__ __forceinline__ f32x16 dn_mma(const uint4 (&wq)[NG], const float (&sc)[NG],
+                                         const uint16_t* hrow, const uint16_t* lrow) {
+  f32x16 acc = {};
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] += h2f(sc_lds[s * 32 + acc_row(r, kh)]) * c[r];
+  for (int i = 0; i < NG; ++i) {
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 c = {};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 hv = *reinterpret_cast<const uint4*>(hrow + 64 * i + 8 * j);
+      const uint4 lv = *reinterpret_cast<const uint4*>(lrow + 64 * i + 8 * j);
+      const h8 w8 = q4_to_h8(word(wq[i], j));
+      c = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(hv), w8, c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(lv), w8, c, 0, 0, 0);
+    }
+    scale_add<NR>(acc, c, sc[i]);
   }
-  (void)n_groups_s;
+  return acc;
 }
 
-// Scales of rows [m0, m0+32) of an int4 matrix into LDS as [group][row].
-__device__ __forceinline__ void load_tile_scales(const uint16_t* s, int n_groups_s, int m0,
-                                                 uint16_t* dst) {
-  for (int i = threadIdx.x; i < 32 * n_groups_s; i += blockDim.x) {
-    const int rr = i / n_groups_s, gg = i % n_groups_s;
-    dst[gg * 32 + rr] = ldg(s + (int64_t)(m0 + rr) * n_groups_s + gg);
-  }
-}
-
-struct MbArgs {
-  Dims dm;
-  Pool pool;
-  SharedW sh;
-  int B;
-  const uint16_t* xp;    // [B][d] pair-permuted
-  const int32_t* grp;
-  const int32_t* idx;    // [B][K]
-  const float* w;        // [B][K]
-  const float* ax;       // [B][3*rmax] LoRA A products (gate, up, down)
-  int rmax;
-  float* H;              // [B][K+1][imax] SwiGLU outputs
-  uint16_t* hh;          // [B][K+1][imax] fp16 hi, pair-permuted
-  uint16_t* hl;
-  float* hexp;           // [B][K+1] power-of-two scale of hh/hl
-  float* Y;              // [B][K+1][d] per-slot down outputs
-  float* axd;            // ax, written: A_down . h_shared
-  uint16_t* y;           // [B][d]
-  int32_t* flags;
-};
-
-// Column n of a column block: its token and output slot; `valid` false for
-// padding columns (they compute on token 0 and are not stored).
-__device__ __forceinline__ void column(const MbArgs& a, bool shared, int start, int count, int cb,
-                                       int n, int& b, int& k, bool& valid) {
+// Token and output slot of token row t of a union member's run.
+__device__ __forceinline__ void entry_of(const MbArgs& a, bool shared, int start, int t, int& b,
+                                         int& k) {
   const int K = a.dm.K;
-  const Groups g = groups(const_cast<int32_t*>(a.grp), a.B * K);
-  valid = cb + n < count;
   if (shared) {
-    b = valid ? cb + n : 0;
+    b = t;
     k = K;
   } else {
-    const int ent = g.sorted[start + (valid ? cb + n : 0)];
+    const Groups g = groups(a.grp, a.B * K);
+    const int ent = g.sorted[start + t];
     b = ent / K;
     k = ent % K;
   }
 }
 
-__global__ __launch_bounds__(64) void k_mb_gate_up(MbArgs a) {
-  __shared__ uint16_t sg[32 * 64], su[32 * 64];  // [group][row], d/G <= 64
-  const Dims& dm = a.dm;
-  const int K = dm.K, d = dm.d, I = dm.I;
-  const int imax = dm.I > dm.Is ? dm.I : dm.Is;
-  const Groups gv = groups(const_cast<int32_t*>(a.grp), a.B * K);
+// Member of a grid row: y = 0 is the shared expert (dispatched first, it has
+// the most tokens), y = 1..n_union the union members in ascending expert id.
+__device__ __forceinline__ bool member_of(const MbArgs& a, int y, bool& shared, int& u) {
+  const Groups gv = groups(a.grp, a.B * a.dm.K);
   const int nu = *gv.n_union;
-  const int u = blockIdx.y;
-  const bool shared = u == nu;
-  if (u > nu || (shared && !a.sh.present)) return;
+  shared = y == 0;
+  u = y - 1;
+  if (shared) return a.sh.present != 0;
+  return u < nu;
+}
+
+// Gate/up of one union member (or the shared expert) for 32 rows. Eight
+// waves: waves 0-3 the gate rows, 4-7 the up rows, each over a quarter of
+// the inputs (NG groups); partials meet in LDS. A wave issues all its loads
+// (weight words, scales, activations of its valid token rows) before the
+// first multiply.
+template <int NG>
+__global__ __launch_bounds__(512) void k_mb_gate_up(MbArgs a) {
+  __shared__ float red[2][4][16][64];
+  __shared__ float axs[kCols][2][kMaxR];
+  const Dims& dm = a.dm;
+  const int K = dm.K, d = dm.d;
+  const int imax = dm.I > dm.Is ? dm.I : dm.Is;
+  bool shared;
+  int u;
+  if (!member_of(a, blockIdx.y, shared, u)) return;
   const int m0 = blockIdx.x * 32;
-  const int rows_total = shared ? dm.Is : I;
-  if (m0 >= rows_total) return;
-  const uint32_t *gq, *uq;
-  const uint16_t *gs, *us;
+  if (m0 >= (shared ? dm.Is : dm.I)) return;
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, n = l & 31, kh = l >> 5;
+  const int mat = wave >> 2, quarter = wave & 3;  // 0 gate, 1 up
+  const uint32_t* wq;
+  const uint16_t* ws;
   int start = 0, count = a.B;
+  const bool lora = shared && a.sh.ag;
   if (shared) {
-    gq = a.sh.gate.q; uq = a.sh.up.q; gs = a.sh.gate.s; us = a.sh.up.s;
+    wq = mat ? a.sh.up.q : a.sh.gate.q;
+    ws = mat ? a.sh.up.s : a.sh.gate.s;
+    if (lora) {
+      for (int i = threadIdx.x; i < a.B * 2 * dm.r; i += blockDim.x) {
+        const int b = i / (2 * dm.r), j = i % (2 * dm.r);
+        axs[b][j / dm.r][j % dm.r] = a.ax[(int64_t)b * 3 * a.rmax + (j / dm.r) * a.rmax + j % dm.r];
+      }
+    }
   } else {
+    const Groups gv = groups(a.grp, a.B * K);
     const int e = gv.uexp[u];
     start = gv.ustart[u];
     count = gv.ucount[u];
@@ -229,51 +358,70 @@ __global__ __launch_bounds__(64) void k_mb_gate_up(MbArgs a) {
       if (threadIdx.x == 0) atomicOr(&a.flags[FLAG_RANGE], 1);
       return;
     }
-    gq = (const uint32_t*)entry_ptr(a.pool.gate.q, ent, a.pool.stride_q);
-    uq = (const uint32_t*)entry_ptr(a.pool.up.q, ent, a.pool.stride_q);
-    gs = (const uint16_t*)entry_ptr(a.pool.gate.s, ent, a.pool.stride_s);
-    us = (const uint16_t*)entry_ptr(a.pool.up.s, ent, a.pool.stride_s);
+    const Q4& m = mat ? a.pool.up : a.pool.gate;
+    wq = (const uint32_t*)entry_ptr(m.q, ent, a.pool.stride_q);
+    ws = (const uint16_t*)entry_ptr(m.s, ent, a.pool.stride_s);
   }
-  const int ngs = d / dm.G, wpr = d / 8;
-  load_tile_scales(gs, ngs, m0, sg);
-  load_tile_scales(us, ngs, m0, su);
-  __syncthreads();
-  const int l = threadIdx.x, n = l & 31, kh = l >> 5;
-  const float c = dm.lora_scale;
-  for (int cb = 0; cb < count; cb += kCols) {
-    int b, k;
-    bool valid;
-    column(a, shared, start, count, cb, n, b, k, valid);
-    const uint16_t* xrow = a.xp + (int64_t)b * d + 32 * kh;
-    auto act = [&](int g, int j) {
-      return as_h8(ldg(reinterpret_cast<const uint4*>(xrow + 64 * g + 8 * j)));
-    };
-    f32x16 ag = {}, au = {};
-    tile_mma(gq + (int64_t)m0 * wpr, wpr, sg, ngs, dm.G, d, act, ag);
-    tile_mma(uq + (int64_t)m0 * wpr, wpr, su, ngs, dm.G, d, act, au);
-    if (!valid) continue;
-    float* hrow = a.H + ((int64_t)b * (K + 1) + k) * imax;
+  const int ngs = d / dm.G, g0 = quarter * NG, wpr = d / 8;
+  const int nr = 4 * ((count + 7) >> 3);
+  const uint32_t* qrow = wq + (int64_t)(m0 + n) * wpr + 4 * kh;
+  const uint16_t* srow = ws + (int64_t)(m0 + n) * ngs;
+  // Token rows past count read a valid row (the last one): their outputs
+  // land in accumulator rows that are never stored.
+  int bt, kt;
+  entry_of(a, shared, start, n < count ? n : count - 1, bt, kt);
+  const uint16_t* xrow = a.xp + (int64_t)bt * d + 32 * kh + 64 * g0;
+  uint4 wv[NG];
+  float sv[NG];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = m0 + acc_row(r, kh);
-      float gg = ag[r], uu = au[r];
-      if (shared && a.sh.ag) {
-        const float* axb = a.ax + (int64_t)b * 3 * a.rmax;
-        float lg = 0.0f, lu = 0.0f;
-        for (int q = 0; q < dm.r; ++q) {
-          lg += h2f(ldg(a.sh.bg + (int64_t)row * dm.r + q)) * axb[q];
-          lu += h2f(ldg(a.sh.bu + (int64_t)row * dm.r + q)) * axb[a.rmax + q];
+  for (int i = 0; i < NG; ++i) wv[i] = ldg(reinterpret_cast<const uint4*>(qrow + 8 * (g0 + i)));
+#pragma unroll
+  for (int i = 0; i < NG; ++i) sv[i] = h2f(ldg(srow + g0 + i));
+  uint4 xv[NG][4];
+#pragma unroll
+  for (int i = 0; i < NG; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xv[i][j] = ldg(reinterpret_cast<const uint4*>(xrow + 64 * i + 8 * j));
+  // one variant for all counts: a second (fewer registers scaled) costs the
+  // register allocator more than it saves
+  const f32x16 acc = gu_mma<NG, 16>(wv, sv, xv);
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    if (r < nr) red[mat][quarter][r][l] = acc[r];
+  __syncthreads();
+  // wave w finishes registers r = w, w+8 (fixed summation order)
+  const float c = dm.lora_scale;
+  const int row = m0 + n;
+  for (int r = wave; r < nr; r += 8) {
+    const int t = tok_row(r, kh);
+    if (t >= count) continue;
+    float gg = (red[0][0][r][l] + red[0][1][r][l]) + (red[0][2][r][l] + red[0][3][r][l]);
+    float uu = (red[1][0][r][l] + red[1][1][r][l]) + (red[1][2][r][l] + red[1][3][r][l]);
+    int b, k;
+    entry_of(a, shared, start, t, b, k);
+    if (lora) {
+      float lg = 0.0f, lu = 0.0f;
+      for (int q = 0; q < dm.r; q += 8) {
+        const uint4 bgv = ldg(reinterpret_cast<const uint4*>(a.sh.bg + (int64_t)row * dm.r + q));
+        const uint4 buv = ldg(reinterpret_cast<const uint4*>(a.sh.bu + (int64_t)row * dm.r + q));
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const f16x2 g2 = as_h2(word(bgv, p)), u2 = as_h2(word(buv, p));
+          lg = fmaf((float)g2.x, axs[b][0][q + 2 * p], lg);
+          lg = fmaf((float)g2.y, axs[b][0][q + 2 * p + 1], lg);
+          lu = fmaf((float)u2.x, axs[b][1][q + 2 * p], lu);
+          lu = fmaf((float)u2.y, axs[b][1][q + 2 * p + 1], lu);
         }
-        gg += c * lg;
-        uu += c * lu;
       }
-      hrow[row] = silu(gg) * uu;
+      gg = fmaf(c, lg, gg);
+      uu = fmaf(c, lu, uu);
     }
+    a.H[((int64_t)b * (K + 1) + k) * imax + row] = silu(gg) * uu;
   }
 }
 
-// One wave per (token, slot): hi/lo copies of the SwiGLU output; for the
-// shared slot also A_down . h.
+// One wave per (token, slot): fp16 hi/lo copies of the SwiGLU output under a
+// power-of-two scale; for the shared slot also A_down . h into ax.
 __global__ __launch_bounds__(64) void k_mb_hsplit(MbArgs a) {
   const Dims& dm = a.dm;
   const int K = dm.K;
@@ -288,49 +436,101 @@ __global__ __launch_bounds__(64) void k_mb_hsplit(MbArgs a) {
   }
   if (!valid) return;
   const int lane = threadIdx.x;
-  const float* h = a.H + ((int64_t)b * (K + 1) + k) * imax;
+  const int64_t slot = (int64_t)b * (K + 1) + k;
+  const float* h = a.H + slot * imax;
   float m = 0.0f;
-  for (int i = lane; i < n; i += 64) m = fmaxf(m, fabsf(h[i]));
+  for (int c = lane; c < n / 8; c += 64) {
+    const float4 v0 = *reinterpret_cast<const float4*>(h + 8 * c);
+    const float4 v1 = *reinterpret_cast<const float4*>(h + 8 * c + 4);
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))));
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(v1.x), fabsf(v1.y)), fmaxf(fabsf(v1.z), fabsf(v1.w))));
+  }
   m = wave_max_rows(m);
   const int e = hilo_exponent(m);
   const float inv = ldexpf(1.0f, -e);
-  uint16_t* hh = a.hh + ((int64_t)b * (K + 1) + k) * imax;
-  uint16_t* hl = a.hl + ((int64_t)b * (K + 1) + k) * imax;
-  for (int i = lane; i < n; i += 64) {
-    f16 hi, lo;
-    split_hilo(h[i], inv, hi, lo);
-    hh[perm8(i)] = __builtin_bit_cast(uint16_t, hi);
-    hl[perm8(i)] = __builtin_bit_cast(uint16_t, lo);
+  uint16_t* hh = a.hh + slot * imax;
+  uint16_t* hl = a.hl + slot * imax;
+  for (int c = lane; c < n / 8; c += 64) {
+    const float4 v0 = *reinterpret_cast<const float4*>(h + 8 * c);
+    const float4 v1 = *reinterpret_cast<const float4*>(h + 8 * c + 4);
+    const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    uint16_t hi[8], lo[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      f16 th, tl;
+      split_hilo(v[i], inv, th, tl);
+      hi[i] = __builtin_bit_cast(uint16_t, th);
+      lo[i] = __builtin_bit_cast(uint16_t, tl);
+    }
+    // pair-permuted order [0 4 1 5 2 6 3 7]
+    *reinterpret_cast<uint4*>(hh + 8 * c) =
+        make_uint4(hi[0] | ((uint32_t)hi[4] << 16), hi[1] | ((uint32_t)hi[5] << 16),
+                   hi[2] | ((uint32_t)hi[6] << 16), hi[3] | ((uint32_t)hi[7] << 16));
+    *reinterpret_cast<uint4*>(hl + 8 * c) =
+        make_uint4(lo[0] | ((uint32_t)lo[4] << 16), lo[1] | ((uint32_t)lo[5] << 16),
+                   lo[2] | ((uint32_t)lo[6] << 16), lo[3] | ((uint32_t)lo[7] << 16));
   }
-  if (lane == 0) a.hexp[(int64_t)b * (K + 1) + k] = ldexpf(1.0f, e);
+  if (lane == 0) a.hexp[slot] = ldexpf(1.0f, e);
   if (k == K && a.sh.ad) {
-    for (int q = 0; q < dm.r; ++q) {
-      float s = 0.0f;
-      for (int i = lane; i < n; i += 64) s += h2f(ldg(a.sh.ad + (int64_t)q * n + i)) * h[i];
-      s = wave_sum_rows(s);
-      if (lane == 0) a.axd[(int64_t)b * 3 * a.rmax + 2 * a.rmax + q] = s;
+    const int r = dm.r;
+    for (int q0 = 0; q0 < r; q0 += 16) {
+      float s[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) s[q] = 0.0f;
+      for (int c = lane; c < n / 8; c += 64) {
+        const float4 v0 = *reinterpret_cast<const float4*>(h + 8 * c);
+        const float4 v1 = *reinterpret_cast<const float4*>(h + 8 * c + 4);
+        const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          if (q0 + q < r) {
+            const uint4 av =
+                ldg(reinterpret_cast<const uint4*>(a.sh.ad + (int64_t)(q0 + q) * n + 8 * c));
+            const uint32_t aw[4] = {av.x, av.y, av.z, av.w};
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              const f16x2 ah = as_h2(aw[p]);
+              s[q] = fmaf((float)ah.x, v[2 * p], s[q]);
+              s[q] = fmaf((float)ah.y, v[2 * p + 1], s[q]);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        if (q0 + q < r) {
+          const float t = wave_sum_rows(s[q]);
+          if (lane == 0) a.ax[(int64_t)b * 3 * a.rmax + 2 * a.rmax + q0 + q] = t;
+        }
+      }
     }
   }
 }
 
-__global__ __launch_bounds__(64) void k_mb_down(MbArgs a) {
-  __shared__ uint16_t sd[32 * 64];  // [group][row], I/G <= 64
+// Down projection. A workgroup takes 128 output rows of one union member (or
+// the shared expert); its four waves take 32 rows each over all NG input
+// groups. The member's hi and lo activations (count tokens x NG*64 inputs)
+// are staged once in LDS; hi and lo then go through the same dequantised
+// weights.
+constexpr int kDnPad = 8;  // fp16 padding per staged row (spreads LDS banks)
+
+template <int NG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_mb_down(MbArgs a) {
+  extern __shared__ __align__(16) uint16_t hs[];  // [count][2][NG*64 + kDnPad]
+  constexpr int nin = NG * 64, stride = nin + kDnPad, wpr = NG * 8;
   const Dims& dm = a.dm;
   const int K = dm.K, d = dm.d;
   const int imax = dm.I > dm.Is ? dm.I : dm.Is;
-  const Groups gv = groups(const_cast<int32_t*>(a.grp), a.B * K);
-  const int nu = *gv.n_union;
-  const int u = blockIdx.y;
-  const bool shared = u == nu;
-  if (u > nu || (shared && !a.sh.present)) return;
-  const int m0 = blockIdx.x * 32;
+  bool shared;
+  int u;
+  if (!member_of(a, blockIdx.y, shared, u)) return;
   const uint32_t* dq;
   const uint16_t* ds;
   int start = 0, count = a.B;
-  const int nin = shared ? dm.Is : dm.I;
   if (shared) {
     dq = a.sh.down.q; ds = a.sh.down.s;
   } else {
+    const Groups gv = groups(a.grp, a.B * K);
     const int e = gv.uexp[u];
     start = gv.ustart[u];
     count = gv.ucount[u];
@@ -339,65 +539,104 @@ __global__ __launch_bounds__(64) void k_mb_down(MbArgs a) {
     dq = (const uint32_t*)entry_ptr(a.pool.down.q, ent, a.pool.stride_q);
     ds = (const uint16_t*)entry_ptr(a.pool.down.s, ent, a.pool.stride_s);
   }
-  const int ngs = nin / dm.G, wpr = nin / 8;
-  load_tile_scales(ds, ngs, m0, sd);
-  __syncthreads();
-  const int l = threadIdx.x, n = l & 31, kh = l >> 5;
-  for (int cb = 0; cb < count; cb += kCols) {
-    int b, k;
-    bool valid;
-    column(a, shared, start, count, cb, n, b, k, valid);
-    const int64_t slot = (int64_t)b * (K + 1) + k;
-    const uint16_t* hrow = a.hh + slot * imax + 32 * kh;
-    const uint16_t* lrow = a.hl + slot * imax + 32 * kh;
-    // hi and lo halves go through the same weights: two MFMA passes per block
-    auto act_hi = [&](int g, int j) {
-      return as_h8(ldg(reinterpret_cast<const uint4*>(hrow + 64 * g + 8 * j)));
-    };
-    auto act_lo = [&](int g, int j) {
-      return as_h8(ldg(reinterpret_cast<const uint4*>(lrow + 64 * g + 8 * j)));
-    };
-    f32x16 acc = {};
-    tile_mma(dq + (int64_t)m0 * wpr, wpr, sd, ngs, dm.G, nin, act_hi, acc);
-    tile_mma(dq + (int64_t)m0 * wpr, wpr, sd, ngs, dm.G, nin, act_lo, acc);
-    if (!valid) continue;
-    const float sc = a.hexp[slot];
-    float* yrow = a.Y + slot * d;
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, n = l & 31, kh = l >> 5;
+  const int m0 = (blockIdx.x * 4 + wave) * 32;
+  const bool rows_ok = m0 < d;
+  uint4 wq[NG];
+  float sc[NG];
+  if (rows_ok) {
+    const uint32_t* qrow = dq + (int64_t)(m0 + n) * wpr + 4 * kh;
+    const uint16_t* srow = ds + (int64_t)(m0 + n) * NG;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) yrow[m0 + acc_row(r, kh)] = acc[r] * sc;
+    for (int i = 0; i < NG; ++i) wq[i] = ldg(reinterpret_cast<const uint4*>(qrow + 8 * i));
+#pragma unroll
+    for (int i = 0; i < NG; ++i) sc[i] = h2f(ldg(srow + i));
+  }
+  // stage the activations: 16-byte pieces, [token][hi/lo][piece]
+  constexpr int ppr = nin / 8;
+  for (int p = threadIdx.x; p < count * 2 * ppr; p += blockDim.x) {
+    const int t = p / (2 * ppr), hl = (p / ppr) & 1, c = p % ppr;
+    int b, k;
+    entry_of(a, shared, start, t, b, k);
+    const uint16_t* src = (hl ? a.hl : a.hh) + ((int64_t)b * (K + 1) + k) * imax + 8 * c;
+    *reinterpret_cast<uint4*>(hs + (t * 2 + hl) * stride + 8 * c) =
+        *reinterpret_cast<const uint4*>(src);
+  }
+  __syncthreads();
+  if (!rows_ok) return;
+  const int nr = 4 * ((count + 7) >> 3);
+  // token rows past count read the last valid row (never stored)
+  const int tc = n < count ? n : count - 1;
+  const uint16_t* hrow = hs + (tc * 2) * stride + 32 * kh;
+  const uint16_t* lrow = hrow + stride;
+  f32x16 acc;
+  if (nr == 4)
+    acc = dn_mma<NG, 4>(wq, sc, hrow, lrow);
+  else
+    acc = dn_mma<NG, 16>(wq, sc, hrow, lrow);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int t = tok_row(r, kh);
+    if (r < nr && t < count) {
+      int b, k;
+      entry_of(a, shared, start, t, b, k);
+      const int64_t slot = (int64_t)b * (K + 1) + k;
+      a.Y[slot * d + m0 + n] = acc[r] * a.hexp[slot];
+    }
   }
 }
 
+// y[b] = sum_k w_k y_k + y_shared + down LoRA, in a fixed order (no atomics),
+// rounded to fp16. Grid (B, ceil(d/256)).
 __global__ __launch_bounds__(256) void k_mb_combine(MbArgs a) {
+  __shared__ int ok[8];
   const Dims& dm = a.dm;
   const int K = dm.K, d = dm.d, b = blockIdx.x;
+  if (threadIdx.x < K) ok[threadIdx.x] = resolve_entry(a.pool, dm.E, a.idx[b * K + threadIdx.x]) >= 0;
+  __syncthreads();
+  const int j = blockIdx.y * blockDim.x + threadIdx.x;
+  if (j >= d) return;
   const float c = dm.lora_scale;
-  const float* axb = a.axd + (int64_t)b * 3 * a.rmax + 2 * a.rmax;
-  for (int j = threadIdx.x; j < d; j += blockDim.x) {
-    float acc = 0.0f;
-    for (int k = 0; k < K; ++k) {
-      if (resolve_entry(a.pool, dm.E, a.idx[b * K + k]) < 0) continue;
-      acc += a.w[b * K + k] * a.Y[((int64_t)b * (K + 1) + k) * d + j];
-    }
-    if (a.sh.present) {
-      acc += a.Y[((int64_t)b * (K + 1) + K) * d + j];
-      if (a.sh.bd) {
-        float ls = 0.0f;
-        for (int q = 0; q < dm.r; ++q) ls += h2f(ldg(a.sh.bd + (int64_t)j * dm.r + q)) * axb[q];
-        acc += c * ls;
-      }
-    }
-    a.y[(int64_t)b * d + j] = f2h(acc);
+  float acc = 0.0f;
+  for (int k = 0; k < K; ++k) {
+    if (!ok[k]) continue;
+    acc += a.w[b * K + k] * a.Y[((int64_t)b * (K + 1) + k) * d + j];
   }
+  if (a.sh.present) {
+    acc += a.Y[((int64_t)b * (K + 1) + K) * d + j];
+    if (a.sh.bd) {
+      const float* axb = a.ax + (int64_t)b * 3 * a.rmax + 2 * a.rmax;
+      float ls = 0.0f;
+      for (int q = 0; q < dm.r; ++q) ls = fmaf(h2f(ldg(a.sh.bd + (int64_t)j * dm.r + q)), axb[q], ls);
+      acc += c * ls;
+    }
+  }
+  a.y[(int64_t)b * d + j] = f2h(acc);
 }
 
 }  // namespace
 
 bool batched_supported(const Dims& dm) {
-  return dm.G % 64 == 0 && dm.d % 64 == 0 && dm.I % 64 == 0 && dm.d / dm.G <= 64 &&
-         dm.I / dm.G <= 64 && dm.K * kCols <= 256 && dm.E <= kMaxE &&
-         (dm.Is == 0 || dm.Is == dm.I);
+  const int gu_groups = dm.G > 0 ? dm.d / dm.G : 0, dn_groups = dm.G > 0 ? dm.I / dm.G : 0;
+  return dm.G == 64 && dm.d % 128 == 0 && dm.I % 64 == 0 && gu_groups % 8 == 0 &&
+         gu_groups <= 32 && dn_groups % 2 == 0 && dn_groups <= 8 && dm.K <= 8 &&
+         dm.E <= kMaxE && dm.r % 8 == 0 && dm.r <= kMaxR && (dm.Is == 0 || dm.Is == dm.I);
 }
+
+namespace {
+
+template <int NG>
+void launch_gate_up_ng(const MbArgs& a, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL(k_mb_gate_up<NG>, grid, dim3(512), 0, st, a);
+}
+
+template <int NG>
+void launch_down_ng(const MbArgs& a, dim3 grid, hipStream_t st) {
+  const size_t lds = (size_t)a.B * 2 * (NG * 64 + kDnPad) * sizeof(uint16_t);
+  hipLaunchKernelGGL(k_mb_down<NG>, grid, dim3(256), lds, st, a);
+}
+
+}  // namespace
 
 hipError_t launch_batched(const Dims& dm, const Pool& pool, const SharedW& sh, const uint16_t* x,
                           const int32_t* idx, const float* w, int B, uint16_t* y,
@@ -408,6 +647,7 @@ hipError_t launch_batched(const Dims& dm, const Pool& pool, const SharedW& sh, c
   a.pool = pool;
   a.sh = sh;
   a.B = B;
+  a.x = x;
   a.xp = s.xn;
   a.grp = s.grp;
   a.idx = idx;
@@ -419,17 +659,28 @@ hipError_t launch_batched(const Dims& dm, const Pool& pool, const SharedW& sh, c
   a.hl = s.hl;
   a.hexp = s.hexp;
   a.Y = s.yk;
-  a.axd = s.ax;
   a.y = y;
   a.flags = s.flags;
-  hipLaunchKernelGGL(k_mb_group, dim3(1), dim3(256), 0, st, dm.E, dm.K, B, idx, s.grp, s.flags);
-  hipLaunchKernelGGL(k_mb_xperm, dim3(B), dim3(256), 0, st, x, dm.d, s.xn);
   const int ny = B * dm.K + 1;  // union members + the shared expert
   const int imax = dm.I > dm.Is ? dm.I : dm.Is;
-  hipLaunchKernelGGL(k_mb_gate_up, dim3(imax / 32, ny), dim3(64), 0, st, a);
+  const int lora_blocks = sh.present && sh.ag ? B * ((2 * dm.r + 3) / 4) : 0;
+  hipLaunchKernelGGL(k_mb_prep, dim3(B + 1 + lora_blocks), dim3(256), 0, st, a);
+  const dim3 gu_grid(imax / 32, ny);
+  switch (dm.d / dm.G / 4) {
+    case 2: launch_gate_up_ng<2>(a, gu_grid, st); break;
+    case 4: launch_gate_up_ng<4>(a, gu_grid, st); break;
+    case 6: launch_gate_up_ng<6>(a, gu_grid, st); break;
+    default: launch_gate_up_ng<8>(a, gu_grid, st); break;
+  }
   hipLaunchKernelGGL(k_mb_hsplit, dim3(B * (dm.K + 1)), dim3(64), 0, st, a);
-  hipLaunchKernelGGL(k_mb_down, dim3(dm.d / 32, ny), dim3(64), 0, st, a);
-  hipLaunchKernelGGL(k_mb_combine, dim3(B), dim3(256), 0, st, a);
+  const dim3 dn_grid(dm.d / 128, ny);
+  switch (dm.I / dm.G) {
+    case 2: launch_down_ng<2>(a, dn_grid, st); break;
+    case 4: launch_down_ng<4>(a, dn_grid, st); break;
+    case 6: launch_down_ng<6>(a, dn_grid, st); break;
+    default: launch_down_ng<8>(a, dn_grid, st); break;
+  }
+  hipLaunchKernelGGL(k_mb_combine, dim3(B, (dm.d + 255) / 256), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
