@@ -150,7 +150,7 @@ def run_chunk(args):
     expert = 3 * (dm0["I"] * dm0["d"] // 2) + 3 * 2 * (dm0["I"] * dm0["d"] // dm0["G"])
     lora = 2 * (dm0["r"] * dm0["d"] + dm0["Is"] * dm0["r"]) * 2 + (dm0["r"] * dm0["Is"] + dm0["d"] * dm0["r"]) * 2
     lines = []
-    for K in (2, 4, 8):
+    for K in ((2, 4, 8) if args.chunk_k == 0 else (args.chunk_k,)):
         dm = synth.dims(tier, K=K)
         ctx = api.Context(dm, max_tokens=B)
         dx = torch.from_numpy(x).cuda()
@@ -385,6 +385,8 @@ def main():
                     help="stack: the 40-layer resident decode (the bench line); chunk: the "
                          "B=32 batched chunk; staged: the host-staged stack; layer: single "
                          "layer-steps, warm and cold")
+    ap.add_argument("--chunk-k", type=int, default=0, choices=[0, 2, 4, 8],
+                    help="chunk workload: only this top-K (0 = 2, 4 and 8)")
     args = ap.parse_args()
     if args.copy_probe:
         copy_probe(args.copy_probe)

@@ -122,8 +122,7 @@ int e0_create(const e0_spec* spec, int32_t max_tokens, e0_ctx** out) {
   const size_t n_slot = (size_t)B * (dm.K + 1);
   const size_t bytes = up(n_gu * 4) + up(n_ax * 4) + up(n_d * 4) + up(n_d * 2) + up(n_p * 4) +
                        2 * up(n_e * 4) + 2 * up((size_t)B * dm.K * 4) + up(N_FLAGS * 4) +
-                       up(n_grp * 4) + 2 * up(n_gu * 2) + up(n_slot * 4) +
-                       up(n_slot * dm.d * 4);
+                       up(n_grp * 4) + up(n_slot * dm.d * 4);
   hipError_t e = hipMalloc(&c->block, bytes);
   if (e != hipSuccess) {
     delete c;
@@ -149,9 +148,6 @@ int e0_create(const e0_spec* spec, int32_t max_tokens, e0_ctx** out) {
   s.sink_w = (float*)q; q += up((size_t)B * dm.K * 4);
   s.flags = (int32_t*)q; q += up(N_FLAGS * 4);
   s.grp = (int32_t*)q; q += up(n_grp * 4);
-  s.hh = (uint16_t*)q; q += up(n_gu * 2);
-  s.hl = (uint16_t*)q; q += up(n_gu * 2);
-  s.hexp = (float*)q; q += up(n_slot * 4);
   s.yk = (float*)q;
   *out = c;
   return E0_OK;

@@ -6,22 +6,27 @@
 // quantized kernel computing down(silu(gate(x)) * up(x)) per expert).
 //
 // Steps, all on the caller's stream:
-//   1. k_mb_group: the B*K (token, slot) entries sorted by expert (ascending
-//      expert, then entry order), the union of experts with each expert's run.
-//   2. k_mb_xperm: x copied in the pair-permuted fp16 order the int4 dequant
-//      produces ([x0 x4 x1 x5 x2 x6 x3 x7] per block of 8).
-//   3. k_mb_gate_up: one wave per (expert of the union, 32 rows of I); the
-//      expert's tokens are the 32 columns of v_mfma_f32_32x32x16_f16 tiles.
-//      int4 words are dequantised in registers to exact fp16 integers; each
-//      group of 64 inputs is accumulated on its own and scaled in fp32 by the
-//      row's group scale (q*s is never rounded). SwiGLU in the epilogue. The
-//      shared expert runs as the last "expert" with all tokens, its LoRA B
-//      terms added in the epilogue.
-//   4. k_mb_hsplit: each (token, slot) SwiGLU output -> fp16 hi + lo with a
-//      power-of-two scale (about 22 bits kept); A_down . h of the shared one.
-//   5. k_mb_down: as 3 for the down rows, hi and lo accumulated together.
-//   6. k_mb_combine: y = sum_k w_k y_k + y_shared + down LoRA, in a fixed
+//   1. k_mb_prep: the B*K (token, slot) entries sorted by expert (ascending
+//      expert, then entry order) with the union of experts and each one's run;
+//      x copied in the pair-permuted fp16 order the int4 dequant produces
+//      ([x0 x4 x1 x5 x2 x6 x3 x7] per block of 8); LoRA A.x of the shared
+//      expert's gate and up.
+//   2. k_mb_gate_up: per (union member, 32 rows of I), eight waves: gate and
+//      up rows, each over a quarter of the inputs. On
+//      v_mfma_f32_32x32x16_f16 the member's tokens are operand A (rows) and
+//      32 weight rows operand B, so each lane owns one weight row and its
+//      group scales. int4 words are dequantised in registers to exact fp16
+//      integers; each group of 64 inputs is accumulated on its own and scaled
+//      in fp32 by the row's group scale (q*s is never rounded). SwiGLU and
+//      the shared expert's LoRA B terms in the epilogue; fp32 output.
+//   3. k_mb_down: per (union member, 128 output rows); the member's SwiGLU
+//      outputs are staged in LDS as fp16 hi + lo under a power-of-two scale
+//      per token (about 22 bits kept) and both halves go through the same
+//      dequantised weights; also A_down . h of the shared expert.
+//   4. k_mb_combine: y = sum_k w_k y_k + y_shared + down LoRA, in a fixed
 //      order (no atomics, deterministic), rounded to fp16.
+// The shared expert is grid row 0 of steps 2 and 3 (dispatched first, it has
+// the most tokens); a chunk holds at most 32 tokens.
 
 #include "gemv.h"
 #include "internal.h"
@@ -64,9 +69,6 @@ struct MbArgs {
   float* ax;             // [B][3*rmax] LoRA A products (gate, up, down)
   int rmax;
   float* H;              // [B][K+1][imax] SwiGLU outputs
-  uint16_t* hh;          // [B][K+1][imax] fp16 hi, pair-permuted
-  uint16_t* hl;
-  float* hexp;           // [B][K+1] power-of-two scale of hh/hl
   float* Y;              // [B][K+1][d] per-slot down outputs
   uint16_t* y;           // [B][d]
   int32_t* flags;
@@ -213,15 +215,8 @@ __global__ __launch_bounds__(256) void k_mb_prep(MbArgs a) {
 // Eight int4 weights of one word as exact fp16 integers, in the order
 // q0 q4 q1 q5 q2 q6 q3 q7 (matching the pair-permuted activations).
 __device__ __forceinline__ h8 q4_to_h8(uint32_t w) {
-  const uint32_t u = w ^ 0x88888888u;
-  const uint32_t v = u >> 8;
-  const f16x2 k1032 = {(f16)1032.0f, (f16)1032.0f};
-  const f16x2 k16 = {(f16)0.0625f, (f16)0.0625f};
-  const f16x2 k72 = {(f16)72.0f, (f16)72.0f};
-  const f16x2 p0 = as_h2((u & 0x000F000Fu) | 0x64006400u) - k1032;
-  const f16x2 p1 = as_h2((u & 0x00F000F0u) | 0x64006400u) * k16 - k72;
-  const f16x2 p2 = as_h2((v & 0x000F000Fu) | 0x64006400u) - k1032;
-  const f16x2 p3 = as_h2((v & 0x00F000F0u) | 0x64006400u) * k16 - k72;
+  f16x2 p0, p1, p2, p3;
+  q4_pairs(w, p0, p1, p2, p3);
   h8 r;
   r[0] = p0.x; r[1] = p0.y; r[2] = p1.x; r[3] = p1.y;
   r[4] = p2.x; r[5] = p2.y; r[6] = p3.x; r[7] = p3.y;
@@ -420,103 +415,19 @@ __global__ __launch_bounds__(512) void k_mb_gate_up(MbArgs a) {
   }
 }
 
-// One wave per (token, slot): fp16 hi/lo copies of the SwiGLU output under a
-// power-of-two scale; for the shared slot also A_down . h into ax.
-__global__ __launch_bounds__(64) void k_mb_hsplit(MbArgs a) {
-  const Dims& dm = a.dm;
-  const int K = dm.K;
-  const int imax = dm.I > dm.Is ? dm.I : dm.Is;
-  const int b = blockIdx.x / (K + 1), k = blockIdx.x % (K + 1);
-  const int n = k < K ? dm.I : dm.Is;
-  bool valid;
-  if (k < K) {
-    valid = resolve_entry(a.pool, dm.E, a.idx[b * K + k]) >= 0;
-  } else {
-    valid = a.sh.present != 0;
-  }
-  if (!valid) return;
-  const int lane = threadIdx.x;
-  const int64_t slot = (int64_t)b * (K + 1) + k;
-  const float* h = a.H + slot * imax;
-  float m = 0.0f;
-  for (int c = lane; c < n / 8; c += 64) {
-    const float4 v0 = *reinterpret_cast<const float4*>(h + 8 * c);
-    const float4 v1 = *reinterpret_cast<const float4*>(h + 8 * c + 4);
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))));
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(v1.x), fabsf(v1.y)), fmaxf(fabsf(v1.z), fabsf(v1.w))));
-  }
-  m = wave_max_rows(m);
-  const int e = hilo_exponent(m);
-  const float inv = ldexpf(1.0f, -e);
-  uint16_t* hh = a.hh + slot * imax;
-  uint16_t* hl = a.hl + slot * imax;
-  for (int c = lane; c < n / 8; c += 64) {
-    const float4 v0 = *reinterpret_cast<const float4*>(h + 8 * c);
-    const float4 v1 = *reinterpret_cast<const float4*>(h + 8 * c + 4);
-    const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    uint16_t hi[8], lo[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      f16 th, tl;
-      split_hilo(v[i], inv, th, tl);
-      hi[i] = __builtin_bit_cast(uint16_t, th);
-      lo[i] = __builtin_bit_cast(uint16_t, tl);
-    }
-    // pair-permuted order [0 4 1 5 2 6 3 7]
-    *reinterpret_cast<uint4*>(hh + 8 * c) =
-        make_uint4(hi[0] | ((uint32_t)hi[4] << 16), hi[1] | ((uint32_t)hi[5] << 16),
-                   hi[2] | ((uint32_t)hi[6] << 16), hi[3] | ((uint32_t)hi[7] << 16));
-    *reinterpret_cast<uint4*>(hl + 8 * c) =
-        make_uint4(lo[0] | ((uint32_t)lo[4] << 16), lo[1] | ((uint32_t)lo[5] << 16),
-                   lo[2] | ((uint32_t)lo[6] << 16), lo[3] | ((uint32_t)lo[7] << 16));
-  }
-  if (lane == 0) a.hexp[slot] = ldexpf(1.0f, e);
-  if (k == K && a.sh.ad) {
-    const int r = dm.r;
-    for (int q0 = 0; q0 < r; q0 += 16) {
-      float s[16];
-#pragma unroll
-      for (int q = 0; q < 16; ++q) s[q] = 0.0f;
-      for (int c = lane; c < n / 8; c += 64) {
-        const float4 v0 = *reinterpret_cast<const float4*>(h + 8 * c);
-        const float4 v1 = *reinterpret_cast<const float4*>(h + 8 * c + 4);
-        const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          if (q0 + q < r) {
-            const uint4 av =
-                ldg(reinterpret_cast<const uint4*>(a.sh.ad + (int64_t)(q0 + q) * n + 8 * c));
-            const uint32_t aw[4] = {av.x, av.y, av.z, av.w};
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-              const f16x2 ah = as_h2(aw[p]);
-              s[q] = fmaf((float)ah.x, v[2 * p], s[q]);
-              s[q] = fmaf((float)ah.y, v[2 * p + 1], s[q]);
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        if (q0 + q < r) {
-          const float t = wave_sum_rows(s[q]);
-          if (lane == 0) a.ax[(int64_t)b * 3 * a.rmax + 2 * a.rmax + q0 + q] = t;
-        }
-      }
-    }
-  }
-}
-
 // Down projection. A workgroup takes 128 output rows of one union member (or
 // the shared expert); its four waves take 32 rows each over all NG input
-// groups. The member's hi and lo activations (count tokens x NG*64 inputs)
-// are staged once in LDS; hi and lo then go through the same dequantised
-// weights.
+// groups. The member's fp32 SwiGLU outputs (count tokens x NG*64) are staged
+// once in LDS as fp16 hi + lo under a power-of-two scale per token (about 22
+// bits of each value kept); hi and lo then go through the same dequantised
+// weights. Workgroups of the shared expert also form A_down . h for the down
+// LoRA, two tokens each.
 constexpr int kDnPad = 8;  // fp16 padding per staged row (spreads LDS banks)
 
 template <int NG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_mb_down(MbArgs a) {
   extern __shared__ __align__(16) uint16_t hs[];  // [count][2][NG*64 + kDnPad]
+  __shared__ float hx[kCols];                      // per-token power-of-two scale
   constexpr int nin = NG * 64, stride = nin + kDnPad, wpr = NG * 8;
   const Dims& dm = a.dm;
   const int K = dm.K, d = dm.d;
@@ -552,15 +463,69 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
     for (int i = 0; i < NG; ++i) sc[i] = h2f(ldg(srow + i));
   }
-  // stage the activations: 16-byte pieces, [token][hi/lo][piece]
-  constexpr int ppr = nin / 8;
-  for (int p = threadIdx.x; p < count * 2 * ppr; p += blockDim.x) {
-    const int t = p / (2 * ppr), hl = (p / ppr) & 1, c = p % ppr;
+  // stage: wave w takes tokens w, w+4, ...; lane l the 8 values of chunk l
+  for (int t = wave; t < count; t += 4) {
     int b, k;
     entry_of(a, shared, start, t, b, k);
-    const uint16_t* src = (hl ? a.hl : a.hh) + ((int64_t)b * (K + 1) + k) * imax + 8 * c;
-    *reinterpret_cast<uint4*>(hs + (t * 2 + hl) * stride + 8 * c) =
-        *reinterpret_cast<const uint4*>(src);
+    const float* h = a.H + ((int64_t)b * (K + 1) + k) * imax + 8 * l;
+    float v[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    if (l < NG * 8) {
+      const float4 v0 = *reinterpret_cast<const float4*>(h);
+      const float4 v1 = *reinterpret_cast<const float4*>(h + 4);
+      v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
+      v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+    const int e = hilo_exponent(wave_max_rows(m));
+    const float inv = ldexpf(1.0f, -e);
+    if (l < NG * 8) {
+      uint16_t hi[8], lo[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        f16 th, tl;
+        split_hilo(v[i], inv, th, tl);
+        hi[i] = __builtin_bit_cast(uint16_t, th);
+        lo[i] = __builtin_bit_cast(uint16_t, tl);
+      }
+      // pair-permuted order [0 4 1 5 2 6 3 7]
+      *reinterpret_cast<uint4*>(hs + (t * 2) * stride + 8 * l) =
+          make_uint4(hi[0] | ((uint32_t)hi[4] << 16), hi[1] | ((uint32_t)hi[5] << 16),
+                     hi[2] | ((uint32_t)hi[6] << 16), hi[3] | ((uint32_t)hi[7] << 16));
+      *reinterpret_cast<uint4*>(hs + (t * 2 + 1) * stride + 8 * l) =
+          make_uint4(lo[0] | ((uint32_t)lo[4] << 16), lo[1] | ((uint32_t)lo[5] << 16),
+                     lo[2] | ((uint32_t)lo[6] << 16), lo[3] | ((uint32_t)lo[7] << 16));
+    }
+    if (l == 0) hx[t] = ldexpf(1.0f, e);
+  }
+  if (shared && a.sh.ad) {
+    // A_down . h_shared[t] for tokens t = blockIdx.x, blockIdx.x + gridDim.x, ...;
+    // wave w takes ranks q = w, w+4, ...
+    for (int t = blockIdx.x; t < count; t += gridDim.x) {
+      const float* h = a.H + ((int64_t)t * (K + 1) + K) * imax + 8 * l;
+      float v[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+      if (l < NG * 8) {
+        const float4 v0 = *reinterpret_cast<const float4*>(h);
+        const float4 v1 = *reinterpret_cast<const float4*>(h + 4);
+        v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
+        v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+      }
+      for (int q = wave; q < dm.r; q += 4) {
+        float sacc = 0.0f;
+        if (l < NG * 8) {
+          const uint4 av = ldg(reinterpret_cast<const uint4*>(a.sh.ad + (int64_t)q * nin + 8 * l));
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const f16x2 ah = as_h2(word(av, p));
+            sacc = fmaf((float)ah.x, v[2 * p], sacc);
+            sacc = fmaf((float)ah.y, v[2 * p + 1], sacc);
+          }
+        }
+        sacc = wave_sum_rows(sacc);
+        if (l == 0) a.ax[(int64_t)t * 3 * a.rmax + 2 * a.rmax + q] = sacc;
+      }
+    }
   }
   __syncthreads();
   if (!rows_ok) return;
@@ -581,7 +546,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       int b, k;
       entry_of(a, shared, start, t, b, k);
       const int64_t slot = (int64_t)b * (K + 1) + k;
-      a.Y[slot * d + m0 + n] = acc[r] * a.hexp[slot];
+      a.Y[slot * d + m0 + n] = acc[r] * hx[t];
     }
   }
 }
@@ -655,9 +620,6 @@ hipError_t launch_batched(const Dims& dm, const Pool& pool, const SharedW& sh, c
   a.ax = s.ax;
   a.rmax = dm.r > 1 ? dm.r : 1;
   a.H = s.gu;
-  a.hh = s.hh;
-  a.hl = s.hl;
-  a.hexp = s.hexp;
   a.Y = s.yk;
   a.y = y;
   a.flags = s.flags;
@@ -672,7 +634,6 @@ hipError_t launch_batched(const Dims& dm, const Pool& pool, const SharedW& sh, c
     case 6: launch_gate_up_ng<6>(a, gu_grid, st); break;
     default: launch_gate_up_ng<8>(a, gu_grid, st); break;
   }
-  hipLaunchKernelGGL(k_mb_hsplit, dim3(B * (dm.K + 1)), dim3(64), 0, st, a);
   const dim3 dn_grid(dm.d / 128, ny);
   switch (dm.I / dm.G) {
     case 2: launch_down_ng<2>(a, dn_grid, st); break;

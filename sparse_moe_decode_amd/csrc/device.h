@@ -35,27 +35,37 @@ __device__ __forceinline__ float dot2(f16x2 a, f16x2 b, float c) {
   return __builtin_amdgcn_fdot2(a, b, c, false);
 }
 
-// Eight int4 weights of one packed word against eight activations.
+// The eight int4 weights of one packed word as exact fp16 pairs.
 //
-// The word holds two's-complement nibbles n_0..n_7 (n_j at bits 4j). XOR with
-// 0x8 per nibble gives the offset-binary u_j = q_j + 8 in [0, 15]. OR-ing a
-// nibble into the mantissa of fp16 1024.0 (0x6400) yields 1024 + u exactly;
-// nibbles sitting 4 bits higher yield 1024 + 16u. One packed fp16 subtract
-// (or multiply-add by 1/16) then gives q exactly, two values per register:
+// The word holds two's-complement nibbles n_0..n_7 (n_j at bits 4j). With
+// 0x8 XOR-ed into a nibble it becomes the offset-binary u_j = q_j + 8 in
+// [0, 15]; placed in the mantissa of fp16 1024.0 (0x6400) it reads
+// 1024 + u exactly, and a nibble sitting 4 bits higher reads 1024 + 16u.
+// Both steps are one bitwise select per register: C ^ (w & M), with M the
+// nibble mask and C the 0x8 XOR bits inside M plus the 0x6400 exponent bits
+// outside it. One packed fp16 subtract (or multiply-add by 1/16) then gives
+// q exactly, two values per register:
 //   p0 = (q0, q4)   p1 = (q1, q5)   p2 = (q2, q6)   p3 = (q3, q7)
-// so the activations must be supplied pair-permuted as
+// so activations must be supplied pair-permuted as
 //   xp[0] = (x0, x4)  xp[1] = (x1, x5)  xp[2] = (x2, x6)  xp[3] = (x3, x7).
-// q and x are exact in fp16; v_dot2_f32_f16 accumulates the products in fp32.
-__device__ __forceinline__ float q4_dot8(uint32_t w, const f16x2* xp, float acc) {
-  const uint32_t u = w ^ 0x88888888u;
-  const uint32_t v = u >> 8;
+__device__ __forceinline__ void q4_pairs(uint32_t w, f16x2& p0, f16x2& p1, f16x2& p2,
+                                         f16x2& p3) {
+  const uint32_t v = w >> 8;
   const f16x2 k1032 = {(f16)1032.0f, (f16)1032.0f};
   const f16x2 k16 = {(f16)0.0625f, (f16)0.0625f};
   const f16x2 k72 = {(f16)72.0f, (f16)72.0f};
-  f16x2 p0 = as_h2((u & 0x000F000Fu) | 0x64006400u) - k1032;
-  f16x2 p1 = as_h2((u & 0x00F000F0u) | 0x64006400u) * k16 - k72;
-  f16x2 p2 = as_h2((v & 0x000F000Fu) | 0x64006400u) - k1032;
-  f16x2 p3 = as_h2((v & 0x00F000F0u) | 0x64006400u) * k16 - k72;
+  p0 = as_h2(0x64086408u ^ (w & 0x000F000Fu)) - k1032;
+  p1 = as_h2(0x64806480u ^ (w & 0x00F000F0u)) * k16 - k72;
+  p2 = as_h2(0x64086408u ^ (v & 0x000F000Fu)) - k1032;
+  p3 = as_h2(0x64806480u ^ (v & 0x00F000F0u)) * k16 - k72;
+}
+
+// Eight int4 weights of one packed word against eight pair-permuted
+// activations; q and x are exact in fp16, v_dot2_f32_f16 accumulates the
+// products in fp32.
+__device__ __forceinline__ float q4_dot8(uint32_t w, const f16x2* xp, float acc) {
+  f16x2 p0, p1, p2, p3;
+  q4_pairs(w, p0, p1, p2, p3);
   acc = dot2(p0, xp[0], acc);
   acc = dot2(p1, xp[1], acc);
   acc = dot2(p2, xp[2], acc);

@@ -47,15 +47,8 @@ __device__ __forceinline__ float q4_dot32(uint4 wv, const f16x2* xr) {
 // Same with an fp16 hi/lo activation pair (dequantises each word once).
 __device__ __forceinline__ float q4_dot8_hl(uint32_t w, const f16x2* xh, const f16x2* xl,
                                             float acc) {
-  const uint32_t u = w ^ 0x88888888u;
-  const uint32_t v = u >> 8;
-  const f16x2 k1032 = {(f16)1032.0f, (f16)1032.0f};
-  const f16x2 k16 = {(f16)0.0625f, (f16)0.0625f};
-  const f16x2 k72 = {(f16)72.0f, (f16)72.0f};
-  f16x2 p0 = as_h2((u & 0x000F000Fu) | 0x64006400u) - k1032;
-  f16x2 p1 = as_h2((u & 0x00F000F0u) | 0x64006400u) * k16 - k72;
-  f16x2 p2 = as_h2((v & 0x000F000Fu) | 0x64006400u) - k1032;
-  f16x2 p3 = as_h2((v & 0x00F000F0u) | 0x64006400u) * k16 - k72;
+  f16x2 p0, p1, p2, p3;
+  q4_pairs(w, p0, p1, p2, p3);
   acc = dot2(p0, xh[0], acc);
   acc = dot2(p1, xh[1], acc);
   acc = dot2(p2, xh[2], acc);
@@ -210,7 +203,6 @@ __device__ __forceinline__ void wave_lds_sync() {
 struct RouteScratch {
   float sel[kMaxE];  // sigmoid-group selection scores
   int keep[64];      // sigmoid-group: group kept
-  int ksel[8];       // selected ids, in selection order
 };
 
 // Routing of one token's fp32 logits by the tier's family [MW App. A]:
@@ -222,24 +214,23 @@ struct RouteScratch {
 //
 // One full wave (all 64 lanes active). Lane l holds candidates l + 64j as
 // 64-bit keys (order-preserving score bits, then the complemented id, so
-// the maximum key is the best score with the lowest id). Each of the K
-// rounds takes the lane-local best, the wave maximum (DPP inside rows,
-// four readlanes) and knocks the winner out. Lane 0 writes idx[K] / w[K].
-__device__ __forceinline__ void route_wave(const Dims& dm, const float* lg, const float* bias,
-                                           RouteScratch& rs, int32_t* out_idx, float* out_w,
-                                           int32_t* flags) {
+// the maximum key is the best score with the lowest id), sorted once per
+// lane. Each of the K rounds takes the wave maximum of the lanes' best keys
+// (DPP inside rows, four readlanes) and the winner's lane drops it. Lane k
+// keeps the k-th selection, computes its weight and writes idx[k] / w[k].
+template <int PER>
+__device__ __forceinline__ void route_wave_t(const Dims& dm, const float* lg, const float* bias,
+                                             RouteScratch& rs, int32_t* out_idx, float* out_w,
+                                             int32_t* flags) {
   const int lane = threadIdx.x & 63;
   const int E = dm.E, K = dm.K;
   const bool sg = dm.router_kind == E0_ROUTER_SIGMOID_GROUP;
-  constexpr int kPer = kMaxE / 64;
-  const int per = (E + 63) >> 6;
 
   if (sg) {
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
+    for (int j = 0; j < PER; ++j) {
       const int e = lane + 64 * j;
-      if (j < per && e < E)
-        rs.sel[e] = 1.0f / (1.0f + expf(-lg[e])) + (bias ? ldg(bias + e) : 0.0f);
+      if (e < E) rs.sel[e] = 1.0f / (1.0f + expf(-lg[e])) + (bias ? ldg(bias + e) : 0.0f);
     }
     wave_lds_sync();
     // group score: sum of the two best selection scores of the group
@@ -265,12 +256,16 @@ __device__ __forceinline__ void route_wave(const Dims& dm, const float* lg, cons
     wave_lds_sync();
   }
 
-  uint64_t key[kPer];
+  // Keys: order-preserving score bits over (inverted) id, so ties go to the
+  // lower id and every key is unique; 0 = no candidate. Each lane sorts its
+  // PER keys once; a round then takes the wave maximum of the lanes' heads
+  // and the winning lane shifts its list.
+  uint64_t key[PER];
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
+  for (int j = 0; j < PER; ++j) {
     key[j] = 0;
     const int e = lane + 64 * j;
-    if (j < per && e < E) {
+    if (e < E) {
       bool ok = true;
       float score = lg[e];
       if (sg) {
@@ -280,13 +275,19 @@ __device__ __forceinline__ void route_wave(const Dims& dm, const float* lg, cons
       if (ok) key[j] = ((uint64_t)f2key(score) << 32) | (0xFFFFFFFFu - (uint32_t)e);
     }
   }
+#pragma unroll
+  for (int i = 1; i < PER; ++i)
+#pragma unroll
+    for (int j = i; j > 0; --j) {
+      const uint64_t hi = key[j] > key[j - 1] ? key[j] : key[j - 1];
+      const uint64_t lo = key[j] > key[j - 1] ? key[j - 1] : key[j];
+      key[j - 1] = hi;
+      key[j] = lo;
+    }
+  int mine = -1;  // lane k < K: the k-th selection
   int first = 0;
   for (int k = 0; k < K; ++k) {
-    uint64_t b = 0;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j)
-      if (j < per) b = key[j] > b ? key[j] : b;
-    const uint64_t g = wave_max_u64_rows(b);
+    const uint64_t g = wave_max_u64_rows(key[0]);
     int e = 0;
     if (g == 0) {  // no candidate left (rejected shapes make this unreachable)
       if (lane == 0) atomicOr(&flags[FLAG_RANGE], 4);
@@ -294,10 +295,12 @@ __device__ __forceinline__ void route_wave(const Dims& dm, const float* lg, cons
       e = (int)(0xFFFFFFFFu - (uint32_t)g);
     }
     if (k == 0) first = e;
-    if (lane == 0) rs.ksel[k] = e;
+    if (lane == k) mine = e;
+    if (key[0] == g) {
 #pragma unroll
-    for (int j = 0; j < kPer; ++j)
-      if (j < per && key[j] == g) key[j] = 0;
+      for (int j = 0; j + 1 < PER; ++j) key[j] = key[j + 1];
+      key[PER - 1] = 0;
+    }
   }
   // softmax shift: the largest logit is the first selection
   const float mx = lg[first];
@@ -305,29 +308,34 @@ __device__ __forceinline__ void route_wave(const Dims& dm, const float* lg, cons
   if (!sg && !dm.norm_topk) {
     float z = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
+    for (int j = 0; j < PER; ++j) {
       const int e = lane + 64 * j;
-      if (j < per && e < E) z += expf(lg[e] - mx);
+      if (e < E) z += expf(lg[e] - mx);
     }
     full = wave_sum_rows(z);
   }
-  wave_lds_sync();
-  if (lane == 0) {
-    float wsel[8];
-    float denom = 0.0f;
-    for (int k = 0; k < K; ++k) {
-      const float l = lg[rs.ksel[k]];
-      wsel[k] = sg ? 1.0f / (1.0f + expf(-l)) : expf(l - mx);
-      denom += wsel[k];
-    }
-    if (sg) denom += 1e-20f;
-    else if (!dm.norm_topk) denom = full;
-    for (int k = 0; k < K; ++k) {
-      out_idx[k] = rs.ksel[k];
-      const float ww = wsel[k] / denom;
-      out_w[k] = sg ? dm.route_scale * ww : ww;
-    }
+  float wk = 0.0f;
+  if (lane < K) {
+    const float l = lg[mine];
+    wk = sg ? 1.0f / (1.0f + expf(-l)) : expf(l - mx);
   }
+  float denom = wave_sum_rows(wk);
+  if (sg) denom += 1e-20f;
+  else if (!dm.norm_topk) denom = full;
+  if (lane < K) {
+    out_idx[lane] = mine;
+    const float ww = wk / denom;
+    out_w[lane] = sg ? dm.route_scale * ww : ww;
+  }
+}
+
+__device__ __forceinline__ void route_wave(const Dims& dm, const float* lg, const float* bias,
+                                           RouteScratch& rs, int32_t* out_idx, float* out_w,
+                                           int32_t* flags) {
+  if (dm.E <= 256)
+    route_wave_t<4>(dm, lg, bias, rs, out_idx, out_w, flags);
+  else
+    route_wave_t<8>(dm, lg, bias, rs, out_idx, out_w, flags);
 }
 
 }  // namespace smd

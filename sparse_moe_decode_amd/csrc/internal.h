@@ -71,9 +71,6 @@ struct Scratch {
   int32_t* flags; // [N_FLAGS]
   // batched chunk (16..32 tokens)
   int32_t* grp;   // [1 + 4 B K]    experts of the chunk and their token runs
-  uint16_t* hh;   // [B][K+1][Imax] SwiGLU outputs, fp16 hi (pair-permuted)
-  uint16_t* hl;   // [B][K+1][Imax] fp16 lo
-  float* hexp;    // [B][K+1]       power-of-two scale of hh/hl
   float* yk;      // [B][K+1][d]    per-slot down outputs
 };
 

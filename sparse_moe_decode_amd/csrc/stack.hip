@@ -46,6 +46,7 @@ constexpr int kMaxL = 64;      // layers per launch (routing tables in LDS)
 constexpr int kNR = 4;         // fp16 rows per workgroup per block job (router, LoRA A)
 constexpr int kMaxExp = 9;     // experts per down row: K <= 8 routed + the shared expert
 constexpr int kRank = 16;      // LoRA rank of this kernel (or no LoRA at all)
+constexpr int kStackI = 512;   // expert intermediate width of this kernel
 constexpr int kHX = 4;         // head layers one workgroup keeps x / fc2 activations of
 constexpr int kF2R = 4;        // fc2 rounds (kGroups rows each) per workgroup
 constexpr int kCPF = 4;        // 16-byte chunks per lane of an fc2 row (P <= 512)
@@ -295,8 +296,8 @@ __device__ __forceinline__ bool gu_item(const LayerDev& Ly, const Dims& dm, cons
                                         const uint16_t*& us, int& row) {
   const bool routed = it < n_rt;
   if (routed) {
-    const int k = it / dm.I;
-    row = it % dm.I;
+    const int k = it / kStackI;
+    row = it % kStackI;
     const int64_t ent = ms.ent[k];
     const int64_t e = ent >= 0 ? ent : 0;
     gq = (const uint32_t*)entry_ptr(Ly.pool.gate.q, e, Ly.pool.stride_q);
@@ -325,7 +326,8 @@ __device__ __forceinline__ void gu_issue(GuRegs<CPL, IPG>& R, const LayerDev& Ly
     const uint16_t *gs, *us;
     int row;
     if (!gu_item(Ly, dm, ms, n_rt, it, gq, uq, gs, us, row)) continue;
-    const int wpr = dm.d / 8, spr = dm.d / dm.G;
+    const int gsh = __builtin_ctz(dm.G);  // G is a power of two
+    const int wpr = dm.d / 8, spr = dm.d >> gsh;
     const uint32_t* grow = gq + (int64_t)row * wpr;
     const uint32_t* urow = uq + (int64_t)row * wpr;
 #pragma unroll
@@ -333,8 +335,8 @@ __device__ __forceinline__ void gu_issue(GuRegs<CPL, IPG>& R, const LayerDev& Ly
       const int c = li + kLG * c2;
       R.wg[j][c2] = ldg(reinterpret_cast<const uint4*>(grow + 4 * c));
       R.wu[j][c2] = ldg(reinterpret_cast<const uint4*>(urow + 4 * c));
-      R.sg[j][c2] = ldg(gs + (int64_t)row * spr + (32 * c) / dm.G);
-      R.su[j][c2] = ldg(us + (int64_t)row * spr + (32 * c) / dm.G);
+      R.sg[j][c2] = ldg(gs + (int64_t)row * spr + ((32 * c) >> gsh));
+      R.su[j][c2] = ldg(us + (int64_t)row * spr + ((32 * c) >> gsh));
     }
   }
 }
@@ -349,7 +351,7 @@ __device__ __forceinline__ void gu_finish(const GuRegs<CPL, IPG>& R, const Dims&
     const int it = pl.ib + grp + kGroups * j;
     if (it >= pl.ie) continue;  // uniform over the lane group
     const bool routed = it < n_rt;
-    const bool ok = !routed || ms.ent[it / dm.I] >= 0;
+    const bool ok = !routed || ms.ent[it / kStackI] >= 0;
     float ag = 0.0f, au = 0.0f;
     if (ok) {
 #pragma unroll
@@ -429,7 +431,7 @@ struct PhaseA {
   F16Rows<kNR> router, ax;
   int n_router, n_ax;
   GuRegs<CPL, IPG> gu;
-  bool gu_loaded, b_loaded;
+  bool gu_loaded;
   uint4 attn;  // this thread's 8 elements of the attention update
   DownRegs<NX> D;
   LoraRegs LR;
@@ -442,7 +444,8 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
   constexpr int CPH = 4 * CPL_D;  // 16-byte chunks per lane of a d-wide fp16 head row
   extern __shared__ __align__(16) unsigned char smem[];
   const Dims& dm = a.dm;
-  const int d = dm.d, E = dm.E, K = dm.K, I = dm.I, P = dm.P, G = (int)gridDim.x;
+  constexpr int I = kStackI;
+  const int d = dm.d, E = dm.E, K = dm.K, P = dm.P, G = (int)gridDim.x;
   const int cu = (int)blockIdx.x;
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
@@ -519,14 +522,16 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
 
   // Phase B loads of a layer whose routed entries are in ms.ent: down rows
   // [drow] of every expert slot, LoRA B_down row, the shared-expert LoRA
-  // matrices.
+  // matrices. Issued once this workgroup's gate/up outputs are published, so
+  // that issuing them overlaps the wait for everyone else's.
   auto issue_b = [&](const LayerDev& Ly, PhaseA<CPL_D, IPG, NX>& A) {
     const bool has_sh = Ly.sh.present != 0;
     const int Is = has_sh ? dm.Is : 0;
     const bool lora_gu = has_sh && Ly.sh.ag != nullptr;
     const bool lora_d = has_sh && Ly.sh.ad != nullptr;
     if (drow < de) {
-      const int wpr = I / 8, spr = I / dm.G;
+      const int gsh = __builtin_ctz(dm.G);
+      const int wpr = I / 8, spr = I >> gsh;
 #pragma unroll
       for (int k = 0; k < NX; ++k) {
         A.D.w[k] = make_uint4(0, 0, 0, 0);
@@ -545,7 +550,7 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
         }
         if (!q) continue;
         A.D.w[k] = ldg(reinterpret_cast<const uint4*>(q + (int64_t)drow * wpr + 4 * li));
-        A.D.s[k] = ldg(sc + (int64_t)drow * spr + (32 * li) / dm.G);
+        A.D.s[k] = ldg(sc + (int64_t)drow * spr + ((32 * li) >> gsh));
       }
 #pragma unroll
       for (int c = 0; c < kRank / 8; ++c) {
@@ -566,10 +571,10 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
 #pragma unroll
     for (int q = 0; q < kRank; ++q)
       A.LR.ad[q] = lora_d ? ldg(reinterpret_cast<const uint32_t*>(Ly.sh.ad + q * Is + 2 * t)) : 0u;
-    A.b_loaded = true;
   };
 
-  // Issue every load of layer l that does not depend on its activations.
+  // Issue the loads of layer l that its gate/up step needs and that do not
+  // depend on its activations.
   auto issue_a = [&](int l, const LayerDev& Ly, PhaseA<CPL_D, IPG, NX>& A) {
     const bool has_sh = Ly.sh.present != 0;
     const int Is = has_sh ? dm.Is : 0;
@@ -593,7 +598,6 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
     A.attn = make_uint4(0, 0, 0, 0);
     if (Ly.attn && t < d / 8) A.attn = ldg(reinterpret_cast<const uint4*>(Ly.attn + 8 * t));
     A.gu_loaded = false;
-    A.b_loaded = false;
     if (!Ly.router) {
       // routing known: entries from the tables
       if (t < 16) ms.ent[t] = t < K ? ms.ent_all[(l - a.l0) * K + t] : 0;
@@ -602,7 +606,6 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
       split(K * I + Is, G, cu, pl.ib, pl.ie);
       gu_issue<CPL_D, IPG>(A.gu, Ly, dm, ms, K * I, pl, grp, li);
       A.gu_loaded = true;
-      issue_b(Ly, A);
     }
   };
 
@@ -753,8 +756,8 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
     }
     stamp(a, l, 4);
 
-    // ---- phase B loads (layers routed here): down rows, shared-expert LoRA --
-    if (!A.b_loaded) issue_b(Ly, A);
+    // ---- phase B loads: down rows, shared-expert LoRA -----------------------
+    issue_b(Ly, A);
     const DownRegs<NX>& D = A.D;
     const LoraRegs& LR = A.LR;
     stamp(a, l, 5);
@@ -1045,7 +1048,8 @@ int span(int per, int block) { return per <= 0 ? 0 : (per - 1) / block + 2; }
 }  // namespace
 
 bool stack_supported(const Dims& dm) {
-  if (dm.d % 512 || dm.I != 512 || dm.K > 8 || dm.E > kMaxE) return false;
+  if (dm.d % 512 || dm.I != kStackI || dm.K > 8 || dm.E > kMaxE) return false;
+  if (dm.G < 32 || (dm.G & (dm.G - 1)) || dm.d % dm.G) return false;
   if (dm.Is != 0 && dm.Is != dm.I) return false;
   if (dm.r != 0 && dm.r != kRank) return false;
   if (dm.P % 128 || dm.P > 128 * kCPF) return false;
