@@ -184,6 +184,49 @@ def run_chunk(args):
                       "warmup": args.warmup, "results": lines}))
 
 
+def host_link_probes(api, stager, host_pool, bundle, dm, n_layers, seed):
+    """Host-to-HBM rates on this machine: (1) a plain pinned-memory copy
+    (256 MiB, DMA engine), (2) stage_experts alone, every layer getting K
+    experts it does not hold (K bundles copied per layer, no compute)."""
+    import torch
+    from sparse_moe_decode_amd import synth
+    src = host_pool.view(-1)[: 256 << 20]
+    dst = torch.empty_like(src, device="cuda")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 8
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    memcpy = reps * src.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del dst
+    K, E = dm["K"], dm["E"]
+    rng = synth.rng_for(seed, 40_000)
+    rounds = 6
+    # disjoint K-sets per round for every layer: each staging copies K bundles
+    sets = [[torch.from_numpy(np.ascontiguousarray(rng.permutation(E)[: K * rounds]
+                                                   .reshape(rounds, K).astype(np.int32))).cuda()
+             for _ in range(n_layers)]]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(n_layers):  # prime: every slot table holds round 0
+            api.stage_experts(stager, i, sets[0][i][0], None, side_stream=side)
+        side.synchronize()
+        e0.record(side)
+        for r in range(1, rounds):
+            for i in range(n_layers):
+                api.stage_experts(stager, i, sets[0][i][r], sets[0][i][r - 1], side_stream=side)
+        e1.record(side)
+        side.synchronize()
+    nbytes = (rounds - 1) * n_layers * K * bundle
+    staging = nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    return {"pinned_memcpy_gb_per_s": round(memcpy, 1), "staging_only_gb_per_s": round(staging, 1)}
+
+
 def run_staged(args):
     """Host-staged 35B stack at batch 1 (StagedStack): routed experts of the
     predicted layers (7-38) live in a pinned host pool, 2K HBM slots per
@@ -226,6 +269,7 @@ def run_staged(args):
         print(f"[bench] staged workload: layer {l + 1}/{L} built", file=sys.stderr, flush=True)
     t_build = time.perf_counter() - t_build
     stager = api.Stager(ctx, host_pool, len(cons), n_slots, slots, slot_of, slot_expert)
+    link = host_link_probes(api, stager, host_pool, bundle, dm, len(cons), args.seed)
     model = api.Model(ctx, layers)
     state = api.State(dm, L, head_logits=False, x_trace=False)
     idx0, w0 = wl.initial_routing(tier, args.seed, L)
@@ -235,7 +279,8 @@ def run_staged(args):
     toks = wl.token_inputs(tier, args.seed, T, args.rho)
     h_all = torch.zeros((T, L + 1, dm["d"]), dtype=torch.float16, device="cuda")
     h_all[:, 0].copy_(torch.from_numpy(toks))
-    pipe = pipeline.StagedStack(ctx, model, state, stager, cons, L)
+    pipe = pipeline.StagedStack(ctx, model, state, stager, cons, L, reserve_cus=args.reserve_cus,
+                                group=args.group)
     main = pipe.main
     pipe.stage(0, after_token=False)
     sets = []
@@ -245,6 +290,7 @@ def run_staged(args):
     torch.cuda.synchronize()
     assert api.device_status(ctx) == 0
     print("[bench] staged workload: warmup done", file=sys.stderr, flush=True)
+    copies0 = stager.copies()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(main)
     for t in range(args.warmup, T):
@@ -253,22 +299,29 @@ def run_staged(args):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     assert api.device_status(ctx) == 0
+    # bundles copied for the timed tokens (the staging of the token after the
+    # last one is issued inside the timed loop as well)
+    copied = (stager.copies() - copies0) / args.steps
+    h2d = copied * bundle
     st = torch.stack(sets).cpu().numpy()[:, cons]          # [warmup, n_cons, K]
     new_ids = np.array([[len(set(st[t, i]) - set(st[t - 1, i])) for i in range(len(cons))]
                         for t in range(1, len(st))], np.float64)
     mean_new = float(new_ids.mean()) if new_ids.size else float("nan")
-    h2d = mean_new * len(cons) * bundle
     print(json.dumps({
         "workload": "35B-tier host-staged decode stack, batch 1: experts of the 32 predicted "
                     "layers streamed from pinned host memory into 2K HBM slots per layer by "
                     "stage_experts on a side stream; router layers resident",
         "steps": args.steps, "warmup": args.warmup, "rho": args.rho,
+        "reserved_cus_for_staging": args.reserve_cus, "layers_per_launch": args.group,
         "ms_per_token": round(ms, 4), "tokens_per_s": round(1000.0 / ms, 2),
         "adjacent_set_overlap": round(1.0 - mean_new / K, 3),
         "new_experts_per_layer_token": round(mean_new, 3),
+        "bundles_copied_per_token": round(copied, 2),
         "bundle_bytes": bundle,
-        "h2d_bytes_per_token_est": int(h2d),
-        "h2d_gb_per_s_est": round(h2d / (ms * 1e-3) / 1e9, 1),
+        "h2d_bytes_per_token": int(h2d),
+        "h2d_gb_per_s": round(h2d / (ms * 1e-3) / 1e9, 1),
+        "h2d_frac_of_staging_rate": round(h2d / (ms * 1e-3) / 1e9 / link["staging_only_gb_per_s"], 3),
+        "host_link": link,
         "pinned_pool_GB": round(host_pool.numel() / 1e9, 2), "build_s": round(t_build, 1)}))
     stager.close()
 
@@ -376,7 +429,9 @@ def main():
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=3)
-    ap.add_argument("--rho", type=float, default=0.5)
+    ap.add_argument("--rho", type=float, default=None,
+                    help="token correlation of the stack workloads (default: the calibrated "
+                         "value giving ~0.7 adjacent-token expert overlap)")
     ap.add_argument("--cpu-tokens", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0,
@@ -385,9 +440,16 @@ def main():
                     help="stack: the 40-layer resident decode (the bench line); chunk: the "
                          "B=32 batched chunk; staged: the host-staged stack; layer: single "
                          "layer-steps, warm and cold")
+    ap.add_argument("--reserve-cus", type=int, default=16,
+                    help="staged workload: compute units left to the staging copies")
+    ap.add_argument("--group", type=int, default=8,
+                    help="staged workload: predicted layers per launch")
     ap.add_argument("--chunk-k", type=int, default=0, choices=[0, 2, 4, 8],
                     help="chunk workload: only this top-K (0 = 2, 4 and 8)")
     args = ap.parse_args()
+    if args.rho is None:
+        from sparse_moe_decode_amd.workloads import RHO_STACK
+        args.rho = RHO_STACK
     if args.copy_probe:
         copy_probe(args.copy_probe)
         return
@@ -501,6 +563,7 @@ def main():
                         "6-38, own fp16 router on layers 0-6 and 39, attention replaced by a "
                         "fixed fp16 residual update",
             "tokens_timed": args.steps, "layers": L, "batch": 1,
+            "token_correlation_rho": args.rho,
             "weights_resident_GB": round(sum(
                 sum(v.numel() * v.element_size() for v in part.values())
                 if isinstance(part, dict) else 0

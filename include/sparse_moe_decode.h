@@ -218,6 +218,15 @@ void e0_model_destroy(e0_model* model);
 enum { E0_PATH_AUTO = 0, E0_PATH_PHASES = 1, E0_PATH_PERSISTENT = 2 };
 int e0_model_set_path(e0_model* model, int32_t path);
 
+/* Workgroups of the persistent kernel: one per compute unit by default (grid
+ * 0 restores that). A smaller grid leaves compute units free, so kernels on
+ * other streams (the staging copies of stage_experts) run concurrently with
+ * layer_step instead of between its launches; the work is spread over the
+ * grid either way. E0_ERR_ARG when grid exceeds the compute units (every
+ * workgroup must be resident at once), E0_ERR_SHAPE when the model's shapes do
+ * not fit the persistent kernel. The trace shape follows the grid. */
+int e0_model_set_grid(e0_model* model, int32_t grid);
+
 /* Phase tracing of the persistent kernel (observability; off by default).
  * trace: device uint64 [grid][rows][points] (shape from e0_model_trace_shape;
  * rows = L + 1), or NULL to turn tracing off. Thread 0 of each workgroup
@@ -298,9 +307,22 @@ void e0_stager_destroy(e0_stager* st);
  * stay resident. Runs the slot policy on the device and copies each missing
  * bundle from the host pool over PCIe into its slot, all on `side_stream`,
  * then records `done_event` (a hipEvent_t, may be NULL) on that stream.
- * Expert ids never travel to the host. */
+ * Expert ids never travel to the host. The copy kernel runs 16 workgroups,
+ * so it occupies at most 16 compute units; a persistent layer_step kernel
+ * sized to leave that many free (e0_model_set_grid) runs beside it. */
 int stage_experts(e0_stager* st, int32_t layer, const int32_t* new_idx,
                   const int32_t* in_use_idx, void* side_stream, void* done_event);
+
+/* stage_experts for the n_layers consecutive layers layer .. layer+n_layers-1
+ * in one pass (one policy launch, one copy launch): new_idx and in_use_idx
+ * (or NULL) are device int32 [n_layers][K], row i for layer layer+i. */
+int stage_experts_n(e0_stager* st, int32_t layer, int32_t n_layers, const int32_t* new_idx,
+                    const int32_t* in_use_idx, void* side_stream, void* done_event);
+
+/* Bundles copied by this stager's stage_experts calls since it was created
+ * (observability: host-link bytes = count x e0_bundle_bytes). Synchronises
+ * the device; E0_ERR_HIP if a copy fails. */
+int e0_stager_copies(e0_stager* st, int64_t* out);
 
 #ifdef __cplusplus
 }

@@ -84,6 +84,7 @@ _lib.prerouter_forward.argtypes = [_p, C.POINTER(e0_head), _p, _p, _p, _i32, _p,
 _lib.e0_model_create.argtypes = [_p, C.POINTER(e0_layer), _i32, C.POINTER(_p)]
 _lib.e0_model_destroy.argtypes = [_p]
 _lib.e0_model_set_path.argtypes = [_p, _i32]
+_lib.e0_model_set_grid.argtypes = [_p, _i32]
 _lib.e0_model_set_trace.argtypes = [_p, _p]
 _lib.e0_model_trace_shape.argtypes = [_p, C.POINTER(_i32), C.POINTER(_i32), C.POINTER(_i32)]
 _lib.layer_step.argtypes = [_p, _p, _i32, _i32, C.POINTER(e0_state), _i32, _p, _p]
@@ -92,11 +93,13 @@ _lib.e0_bundle_bytes.restype = _i64
 _lib.e0_stager_create.argtypes = [_p, _p, _i32, _i32, _p, _p, _p, C.POINTER(_p)]
 _lib.e0_stager_destroy.argtypes = [_p]
 _lib.stage_experts.argtypes = [_p, _i32, _p, _p, _p, _p]
+_lib.stage_experts_n.argtypes = [_p, _i32, _i32, _p, _p, _p, _p]
+_lib.e0_stager_copies.argtypes = [_p, C.POINTER(C.c_int64)]
 
 EXPORTS = ["e0_create", "e0_destroy", "e0_last_error", "e0_device_status", "moe_int4_decode",
            "lora_delta", "prerouter_forward", "e0_model_create", "e0_model_destroy",
            "layer_step", "e0_bundle_bytes", "e0_stager_create", "e0_stager_destroy",
-           "stage_experts", "e0_model_set_path", "e0_model_set_trace", "e0_model_trace_shape"]
+           "stage_experts", "stage_experts_n", "e0_stager_copies", "e0_model_set_path", "e0_model_set_grid", "e0_model_set_trace", "e0_model_trace_shape"]
 
 PATH_AUTO, PATH_PHASES, PATH_PERSISTENT = 0, 1, 2
 
@@ -277,6 +280,10 @@ class Model:
         """PATH_AUTO, PATH_PHASES (one kernel per phase) or PATH_PERSISTENT."""
         _check(_lib.e0_model_set_path(self.handle, path))
 
+    def set_grid(self, grid: int):
+        """Workgroups of the persistent kernel (0 = one per compute unit)."""
+        _check(_lib.e0_model_set_grid(self.handle, grid))
+
     def close(self):
         # at interpreter exit the module globals may already be gone
         if getattr(self, "handle", None) and _lib is not None:
@@ -355,6 +362,12 @@ class Stager:
         self.ctx = ctx
         self._keep = (host_pool, hbm_slots, slot_of, slot_expert)
 
+    def copies(self) -> int:
+        """Bundles copied since creation (synchronises the device)."""
+        n = C.c_int64(0)
+        _check(_lib.e0_stager_copies(self.handle, C.byref(n)))
+        return int(n.value)
+
     def close(self):
         # at interpreter exit the module globals may already be gone
         if getattr(self, "handle", None) and _lib is not None:
@@ -365,10 +378,33 @@ class Stager:
         self.close()
 
 
+def _event_handle(ev, stream):
+    """hipEvent_t of `ev` (a torch.cuda.Event or a raw handle). torch creates
+    the underlying event on its first record(), and a wait on an event never
+    created is a no-op; so a fresh torch event is recorded once on `stream`
+    to create it before the library records it."""
+    if ev is None:
+        return None
+    if not hasattr(ev, "cuda_event"):
+        return ev
+    if not ev.cuda_event:
+        ev.record(stream if stream is not None else torch.cuda.current_stream())
+    handle = ev.cuda_event
+    assert handle, "event has no HIP handle"
+    return handle
+
+
 def stage_experts(stager: Stager, layer: int, new_idx, in_use_idx=None, side_stream=None,
                   done_event=None):
-    ev = None
-    if done_event is not None:
-        ev = done_event.cuda_event if hasattr(done_event, "cuda_event") else done_event
+    ev = _event_handle(done_event, side_stream)
     _check(_lib.stage_experts(stager.handle, layer, _ptr(new_idx), _ptr(in_use_idx),
                               _stream(side_stream), ev))
+
+
+def stage_experts_n(stager: Stager, layer: int, n_layers: int, new_idx, in_use_idx=None,
+                    side_stream=None, done_event=None):
+    """stage_experts for layers [layer, layer + n_layers); new_idx / in_use_idx
+    device int32 [n_layers, K] (contiguous rows)."""
+    ev = _event_handle(done_event, side_stream)
+    _check(_lib.stage_experts_n(stager.handle, layer, n_layers, _ptr(new_idx), _ptr(in_use_idx),
+                                _stream(side_stream), ev))

@@ -59,7 +59,8 @@ struct e0_model {
   int32_t ng;
   uint32_t epoch;
   int32_t path;
-  int32_t grid;
+  int32_t grid;  // workgroups of the persistent kernel (one per compute unit)
+  int32_t cus;   // compute units of the device
   uint64_t* trace;
 };
 
@@ -441,6 +442,7 @@ int e0_model_create(e0_ctx* ctx, const e0_layer* layers, int32_t n_layers, e0_mo
     m->xa = w; w += wa;
     m->xl = w; w += wl;
     m->grid = cus;
+    m->cus = cus;
   }
   *out = m;
   return E0_OK;
@@ -464,6 +466,17 @@ int32_t e0_model_trace_shape(e0_model* model, int32_t* grid, int32_t* rows, int3
   if (grid) *grid = model->grid;
   if (rows) *rows = (int32_t)model->layers.size() + 1;
   if (points) *points = kTracePoints;
+  return E0_OK;
+}
+
+int e0_model_set_grid(e0_model* model, int32_t grid) {
+  if (!model || grid < 0) return fail(E0_ERR_ARG, "e0_model_set_grid: bad argument");
+  if (!model->dev_table)
+    return fail(E0_ERR_SHAPE, "e0_model_set_grid: shapes not supported by the persistent kernel");
+  if (grid > model->cus)
+    return fail(E0_ERR_ARG, "e0_model_set_grid: %d workgroups exceed the %d compute units", grid,
+                model->cus);
+  model->grid = grid == 0 ? model->cus : grid;
   return E0_OK;
 }
 
@@ -593,6 +606,7 @@ struct e0_stager {
   int64_t bundle;
   int32_t* copy_list;  // [L][2*8]
   int32_t* n_copies;   // [L]
+  unsigned long long* total;  // bundles copied since creation
 };
 
 extern "C" {
@@ -634,6 +648,8 @@ int e0_stager_create(e0_ctx* ctx, const void* host_pool, int32_t n_layers, int32
   s->bundle = e0_bundle_bytes(&ctx->spec);
   e = hipMalloc(&s->copy_list, (size_t)n_layers * 16 * sizeof(int32_t));
   if (e == hipSuccess) e = hipMalloc(&s->n_copies, (size_t)n_layers * sizeof(int32_t));
+  if (e == hipSuccess) e = hipMalloc(&s->total, sizeof(unsigned long long));
+  if (e == hipSuccess) e = hipMemset(s->total, 0, sizeof(unsigned long long));
   if (e == hipSuccess) e = hipMemset(slot_of, 0xFF, (size_t)n_layers * dm.E * sizeof(int32_t));
   if (e == hipSuccess)
     e = hipMemset(slot_expert, 0xFF, (size_t)n_layers * n_slots * sizeof(int32_t));
@@ -651,27 +667,46 @@ void e0_stager_destroy(e0_stager* st) {
   if (!st) return;
   if (st->copy_list) (void)hipFree(st->copy_list);
   if (st->n_copies) (void)hipFree(st->n_copies);
+  if (st->total) (void)hipFree(st->total);
   delete st;
 }
 
-int stage_experts(e0_stager* st, int32_t layer, const int32_t* new_idx,
-                  const int32_t* in_use_idx, void* side_stream, void* done_event) {
+int e0_stager_copies(e0_stager* st, int64_t* out) {
+  if (!st || !out) return fail(E0_ERR_ARG, "e0_stager_copies: null argument");
+  unsigned long long v = 0;
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(&v, st->total, sizeof(v), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "e0_stager_copies");
+  *out = (int64_t)v;
+  return E0_OK;
+}
+
+int stage_experts_n(e0_stager* st, int32_t layer, int32_t n_layers, const int32_t* new_idx,
+                    const int32_t* in_use_idx, void* side_stream, void* done_event) {
   if (!st || !new_idx) return fail(E0_ERR_ARG, "stage_experts: null argument");
-  if (layer < 0 || layer >= st->L) return fail(E0_ERR_ARG, "stage_experts: bad layer");
+  if (n_layers < 1 || layer < 0 || layer + n_layers > st->L)
+    return fail(E0_ERR_ARG, "stage_experts: layers [%d, %d) outside [0, %d)", layer,
+                layer + n_layers, st->L);
   const Dims& dm = st->ctx->dm;
   hipStream_t ss = (hipStream_t)side_stream;
   hipError_t e = launch_stage(
-      dm.E, st->n_slots, dm.K, st->slot_of + (int64_t)layer * dm.E,
+      dm.E, st->n_slots, dm.K, n_layers, st->slot_of + (int64_t)layer * dm.E,
       st->slot_expert + (int64_t)layer * st->n_slots, in_use_idx, new_idx,
-      st->copy_list + (int64_t)layer * 16, st->n_copies + layer,
-      st->host_dev + (int64_t)layer * dm.E * st->bundle,
-      st->hbm + (int64_t)layer * st->n_slots * st->bundle, st->bundle, st->ctx->s.flags, ss);
+      st->copy_list + (int64_t)layer * 16, st->n_copies + layer, st->total,
+      st->host_dev + (int64_t)layer * dm.E * st->bundle, (int64_t)dm.E * st->bundle,
+      st->hbm + (int64_t)layer * st->n_slots * st->bundle, (int64_t)st->n_slots * st->bundle,
+      st->bundle, st->ctx->s.flags, ss);
   if (e != hipSuccess) return hip_fail(e, "stage_experts");
   if (done_event) {
     e = hipEventRecord((hipEvent_t)done_event, ss);
     if (e != hipSuccess) return hip_fail(e, "stage_experts: event");
   }
   return E0_OK;
+}
+
+int stage_experts(e0_stager* st, int32_t layer, const int32_t* new_idx,
+                  const int32_t* in_use_idx, void* side_stream, void* done_event) {
+  return stage_experts_n(st, layer, 1, new_idx, in_use_idx, side_stream, done_event);
 }
 
 }  // extern "C"

@@ -153,9 +153,13 @@ hipError_t launch_stack(const StackArgs& a, int grid, hipStream_t st);
 
 // Staging: device-side slot policy for one layer, then a gather-copy of the
 // missing bundles from (device-mapped) pinned host memory into HBM slots.
-hipError_t launch_stage(int E, int n_slots, int K, int32_t* slot_of, int32_t* slot_expert,
-                        const int32_t* in_use, const int32_t* next, int32_t* copy_list,
-                        int32_t* n_copies, const char* host_layer, char* hbm_layer,
+hipError_t launch_stage(int E, int n_slots, int K, int n_layers, int32_t* slot_of,
+                        int32_t* slot_expert, const int32_t* in_use, const int32_t* next,
+                        int32_t* copy_list, int32_t* n_copies, unsigned long long* total,
+                        const char* host, int64_t host_stride, char* hbm, int64_t hbm_stride,
                         int64_t bundle, int32_t* flags, hipStream_t st);
+// Workgroups of the staging copy kernel (it occupies at most this many
+// compute units).
+constexpr int kCopyBlocks = 16;
 
 }  // namespace smd

@@ -15,17 +15,26 @@ namespace {
 
 constexpr int kMaxE = 512;
 constexpr int kMaxSlots = 64;
+constexpr int kCopyThreads = 1024;
 
-// Slot policy for one layer (single thread; E <= 512, K <= 8, slots <= 64):
-// ids of `next` with a slot keep it; misses in ascending id take, in
-// ascending slot order, the slots holding no id of in_use or next. Writes
-// (expert, slot) pairs to copy_list and the count to *n_copies.
+// Slot policy, one workgroup per layer of the call (single thread; E <= 512,
+// K <= 8, slots <= 64): ids of `next` with a slot keep it; misses in
+// ascending id take, in ascending slot order, the slots holding no id of
+// in_use or next. Writes (expert, slot) pairs to copy_list and the count to
+// n_copies, and adds the count to the stager's running total.
 __global__ __launch_bounds__(64) void k_slot_policy(int E, int n_slots, int K,
                                                     int32_t* slot_of, int32_t* slot_expert,
                                                     const int32_t* in_use, const int32_t* next,
                                                     int32_t* copy_list, int32_t* n_copies,
-                                                    int32_t* flags) {
+                                                    unsigned long long* total, int32_t* flags) {
   __shared__ uint32_t keep[kMaxE / 32];
+  const int l = blockIdx.x;
+  slot_of += (int64_t)l * E;
+  slot_expert += (int64_t)l * n_slots;
+  next += (int64_t)l * K;
+  if (in_use) in_use += (int64_t)l * K;
+  copy_list += (int64_t)l * 16;
+  n_copies += l;
   if (threadIdx.x < kMaxE / 32) keep[threadIdx.x] = 0;
   __syncthreads();
   if (threadIdx.x != 0) return;
@@ -75,47 +84,53 @@ __global__ __launch_bounds__(64) void k_slot_policy(int E, int n_slots, int K,
   }
   if (nc < nm) atomicOr(&flags[FLAG_RANGE], 2);  // pool too small for the set
   *n_copies = nc;
+  atomicAdd(total, (unsigned long long)nc);
 }
 
-// Gather-copy of the listed bundles: blockIdx.y = copy index, each thread
-// moves 16-byte units (4 per pass) from host-mapped memory into HBM.
-__global__ __launch_bounds__(256) void k_stage_copy(const char* host_layer, char* hbm_layer,
-                                                    int64_t bundle, const int32_t* copy_list,
-                                                    const int32_t* n_copies) {
-  const int j = blockIdx.y;
-  if (j >= *n_copies) return;
-  const int e = copy_list[2 * j], s = copy_list[2 * j + 1];
-  const uint4* src = reinterpret_cast<const uint4*>(host_layer + (int64_t)e * bundle);
-  uint4* dst = reinterpret_cast<uint4*>(hbm_layer + (int64_t)s * bundle);
+// Gather-copy of every listed bundle of the call's layers, host-mapped
+// memory -> HBM slots, in 16-byte units. A few large workgroups stride over
+// each bundle in turn (four loads in flight per thread): enough reads in
+// flight for the host link, while occupying at most kCopyBlocks compute
+// units so that a persistent kernel on the rest of the chip keeps running.
+__global__ __launch_bounds__(kCopyThreads) void k_stage_copy(
+    const char* host, int64_t host_stride, char* hbm, int64_t hbm_stride, int64_t bundle,
+    int n_layers, const int32_t* copy_list, const int32_t* n_copies) {
   const int64_t n16 = bundle / 16;
   const int64_t step = (int64_t)gridDim.x * blockDim.x;
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + 3 * step < n16; i += 4 * step) {
-    uint4 a = src[i], b = src[i + step], c = src[i + 2 * step], d = src[i + 3 * step];
-    dst[i] = a;
-    dst[i + step] = b;
-    dst[i + 2 * step] = c;
-    dst[i + 3 * step] = d;
+  for (int l = 0; l < n_layers; ++l) {
+    const int nc = n_copies[l];
+    for (int j = 0; j < nc; ++j) {
+      const int e = copy_list[16 * l + 2 * j], s = copy_list[16 * l + 2 * j + 1];
+      const uint4* src = reinterpret_cast<const uint4*>(host + l * host_stride + (int64_t)e * bundle);
+      uint4* dst = reinterpret_cast<uint4*>(hbm + l * hbm_stride + (int64_t)s * bundle);
+      int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+      for (; i + 3 * step < n16; i += 4 * step) {
+        uint4 a = src[i], b = src[i + step], c = src[i + 2 * step], d = src[i + 3 * step];
+        dst[i] = a;
+        dst[i + step] = b;
+        dst[i + 2 * step] = c;
+        dst[i + 3 * step] = d;
+      }
+      for (; i < n16; i += step) dst[i] = src[i];
+    }
   }
-  for (; i < n16; i += step) dst[i] = src[i];
 }
 
 }  // namespace
 
-hipError_t launch_stage(int E, int n_slots, int K, int32_t* slot_of, int32_t* slot_expert,
-                        const int32_t* in_use, const int32_t* next, int32_t* copy_list,
-                        int32_t* n_copies, const char* host_layer, char* hbm_layer,
+hipError_t launch_stage(int E, int n_slots, int K, int n_layers, int32_t* slot_of,
+                        int32_t* slot_expert, const int32_t* in_use, const int32_t* next,
+                        int32_t* copy_list, int32_t* n_copies, unsigned long long* total,
+                        const char* host, int64_t host_stride, char* hbm, int64_t hbm_stride,
                         int64_t bundle, int32_t* flags, hipStream_t st) {
-  if (E > kMaxE || n_slots > kMaxSlots || K > 8 || bundle % 16) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_slot_policy, dim3(1), dim3(64), 0, st, E, n_slots, K, slot_of,
-                     slot_expert, in_use, next, copy_list, n_copies, flags);
+  if (E > kMaxE || n_slots > kMaxSlots || K > 8 || bundle % 16 || n_layers < 1)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_slot_policy, dim3(n_layers), dim3(64), 0, st, E, n_slots, K, slot_of,
+                     slot_expert, in_use, next, copy_list, n_copies, total, flags);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // ~64 KiB per block-column keeps enough PCIe reads in flight per copy.
-  int gx = (int)((bundle + 65535) / 65536);
-  if (gx < 1) gx = 1;
-  hipLaunchKernelGGL(k_stage_copy, dim3(gx, K), dim3(256), 0, st, host_layer, hbm_layer, bundle,
-                     copy_list, n_copies);
+  hipLaunchKernelGGL(k_stage_copy, dim3(kCopyBlocks), dim3(kCopyThreads), 0, st, host,
+                     host_stride, hbm, hbm_stride, bundle, n_layers, copy_list, n_copies);
   return hipGetLastError();
 }
 

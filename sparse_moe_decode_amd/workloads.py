@@ -59,6 +59,17 @@ def initial_routing(tier: str, seed: int, n_layers: int):
     return idx, w
 
 
-def token_inputs(tier: str, seed: int, T: int, rho: float = 0.5) -> np.ndarray:
+# Token correlation of the AR(1) token inputs of the decode stacks. Written by
+# oracle/calibrate_rho.py (the fp64 oracle run free over the first 32 tokens
+# of the 35B stack, seed 3): mean adjacent-token overlap of the executed sets
+# on the predicted layers 7-38 is 0.670 at RHO_STACK (the pages' ~70% reuse
+# between consecutive tokens) and 0.264 at RHO_LOW_REUSE (their ~25% case).
+# With the random-init heads the sets follow x closely only when consecutive
+# tokens are nearly equal, hence rho so close to 1.
+RHO_STACK = 0.999988
+RHO_LOW_REUSE = 0.996
+
+
+def token_inputs(tier: str, seed: int, T: int, rho: float = RHO_STACK) -> np.ndarray:
     dm = synth.dims(tier)
     return synth.ar1_tokens(synth.rng_for(seed, 20_000), T, dm["d"], rho)

@@ -90,5 +90,49 @@ def test_stage_experts_matches_slot_policy(api, orc, tier, T):
             for s, e in enumerate(g_slot_exp[l]):
                 if e >= 0:
                     assert torch.equal(hbm[l, s], host_dev[l, e]), f"t={t} l={l} slot {s}"
+    assert st.copies() == copies, "bundle copies counted by the stager"
     print(f"{tier}: {T} tokens x {L} layers staged, {copies} bundle copies")
+    st.close()
+
+
+@pytest.mark.timeout(120)
+def test_stage_event_orders_the_decode(api, orc):
+    """The done event really orders work: the side stream is held back by a
+    bounded sleep kernel before staging, the main stream only waits on the
+    event, and the decode through the slots still sees the staged bundles."""
+    import torch
+    if not hasattr(torch.cuda, "_sleep"):
+        pytest.skip("torch.cuda._sleep unavailable")
+    dm = synth.dims("35b")
+    E, K = dm["E"], dm["K"]
+    n_slots = 2 * K
+    announce("stage_experts", "35b", "event ordering")
+    ctx = api.Context(dm, max_tokens=1)
+    bundle = ctx.bundle_bytes()
+    pool = synth.routed_pool(synth.rng_for(60), dm)
+    host_pool = torch.empty((1, E, bundle), dtype=torch.uint8, pin_memory=True)
+    host_pool[0].copy_(torch.from_numpy(api.pack_bundles(pool, dm)))
+    hbm = torch.zeros((1, n_slots, bundle), dtype=torch.uint8, device="cuda")
+    slot_of = torch.empty((1, E), dtype=torch.int32, device="cuda")
+    slot_expert = torch.empty((1, n_slots), dtype=torch.int32, device="cuda")
+    st = api.Stager(ctx, host_pool, 1, n_slots, hbm, slot_of, slot_expert)
+    side, main = torch.cuda.Stream(), torch.cuda.current_stream()
+    rng = np.random.default_rng(61)
+    new = synth.random_set(rng, E, K)
+    x = rng.normal(size=(1, dm["d"])).astype(np.float16)
+    w = synth.random_weights(rng, K)[None]
+    dnew, dx, dw, didx = dev(new), dev(x), dev(w), dev(new[None])
+    torch.cuda.synchronize()
+    ev = torch.cuda.Event()
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(40_000_000)  # ~20 ms of spinning, then it exits
+    api.stage_experts(st, 0, dnew, None, side_stream=side, done_event=ev)
+    main.wait_event(ev)
+    view = api.bundle_view(hbm[0].data_ptr(), dm)
+    y = api.moe_int4_decode(ctx, view, dx, didx, dw, slot_of=slot_of[0], count=n_slots,
+                            stride=bundle)
+    torch.cuda.synchronize()
+    assert api.device_status(ctx) == 0
+    ref = orc.moe_decode(dm, pool, None, x[0], new, w[0].astype(np.float64))
+    assert_out_close(f16_to_f64(y)[0], ref, "decode after the staging event")
     st.close()

@@ -37,8 +37,12 @@ ROLES = [dict(router=True, head=True), dict(router=False, head=True),
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("tier,T", [("35b", 5), ("8b", 4)])
-def test_staged_stack_matches_oracle(api, orc, tier, T):
+@pytest.mark.parametrize("tier,T,reserve,group", [("35b", 5, 0, 1), ("8b", 4, 0, 1),
+                                                  ("35b", 4, 16, 2), ("8b", 4, 8, 3)])
+def test_staged_stack_matches_oracle(api, orc, tier, T, reserve, group):
+    """reserve > 0 runs the persistent kernel on fewer workgroups than compute
+    units (staging copies then run beside the layers); group = predicted
+    layers per launch."""
     import torch
     from sparse_moe_decode_amd import pipeline
     from sparse_moe_decode_amd import workloads as wl
@@ -77,20 +81,22 @@ def test_staged_stack_matches_oracle(api, orc, tier, T):
     idx0, w0 = wl.initial_routing(tier, seed, L)
     state.route_idx[0].copy_(torch.from_numpy(idx0))
     state.route_w[0].copy_(torch.from_numpy(w0))
-    toks = wl.token_inputs(tier, seed, T)
+    toks = wl.token_inputs(tier, seed, T, rho=0.5)  # sets change between tokens: copies happen
     checker = StackChecker(orc, tier, seed, ROLES, list(range(L)), keep, zero_mean=True)
-    pipe = pipeline.StagedStack(ctx, model, state, stager, cons, L)
+    pipe = pipeline.StagedStack(ctx, model, state, stager, cons, L, reserve_cus=reserve,
+                                group=group)
 
     o_slot_of = np.full((len(cons), E), -1, np.int32)
     o_slot_exp = np.full((len(cons), n_slots), -1, np.int32)
+    copies = 0
     for i, l in enumerate(cons):
-        orc.slot_policy(E, n_slots, K, o_slot_of[i], o_slot_exp[i], None, idx0[l])
+        copies += len(orc.slot_policy(E, n_slots, K, o_slot_of[i], o_slot_exp[i], None, idx0[l]))
     pipe.stage(0, after_token=False)
     prev_exec = None
     h = torch.zeros((L + 1, dm["d"]), dtype=torch.float16, device="cuda")
-    copies = 0
     for t in range(T):
-        announce("staged layer_step", tier, f"L={L}", f"token {t}")
+        announce("staged layer_step", tier, f"L={L} reserve={reserve} group={group}",
+                 f"token {t}")
         h[0].copy_(torch.from_numpy(toks[t]))
         pipe.run_token(t, h)
         torch.cuda.synchronize()
@@ -116,8 +122,9 @@ def test_staged_stack_matches_oracle(api, orc, tier, T):
             for s, e in enumerate(g_slot_exp[i]):
                 if e >= 0:
                     assert torch.equal(hbm[i, s], host_dev[i, e]), f"t={t} l={l} slot {s}"
+    assert stager.copies() == copies, "bundle copies counted by the stager"
     print(f"{tier} staged L={L}: {checker.steps} layer-steps checked, worst error ratio "
-          f"{checker.worst:.3f}, {copies} bundle copies after the first token")
+          f"{checker.worst:.3f}, {copies} bundle copies")
     stager.close()
     model.close()
     ctx.close()
