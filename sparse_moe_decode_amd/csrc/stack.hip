@@ -163,9 +163,6 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 
 // Small per-layer values kept in LDS.
 struct Misc {
-  int32_t ridx[8];
-  float rw[8];
-  int64_t ent[16];
   // down-projection bases and combine weight of expert slot k (routed k < K,
   // shared k == K); null / 0 when the slot is unused or its id did not resolve
   const uint32_t* dq[kMaxExp];
@@ -290,7 +287,8 @@ struct GuPlan {
   int ib, ie;  // item range of this workgroup
 };
 
-__device__ __forceinline__ bool gu_item(const LayerDev& Ly, const Dims& dm, const Misc& ms,
+// ent: pool entries of the layer's K routed slots (LDS).
+__device__ __forceinline__ bool gu_item(const LayerDev& Ly, const Dims& dm, const int64_t* ent_k,
                                         int n_rt, int it, const uint32_t*& gq,
                                         const uint32_t*& uq, const uint16_t*& gs,
                                         const uint16_t*& us, int& row) {
@@ -298,7 +296,7 @@ __device__ __forceinline__ bool gu_item(const LayerDev& Ly, const Dims& dm, cons
   if (routed) {
     const int k = it / kStackI;
     row = it % kStackI;
-    const int64_t ent = ms.ent[k];
+    const int64_t ent = ent_k[k];
     const int64_t e = ent >= 0 ? ent : 0;
     gq = (const uint32_t*)entry_ptr(Ly.pool.gate.q, e, Ly.pool.stride_q);
     uq = (const uint32_t*)entry_ptr(Ly.pool.up.q, e, Ly.pool.stride_q);
@@ -316,8 +314,8 @@ __device__ __forceinline__ bool gu_item(const LayerDev& Ly, const Dims& dm, cons
 
 template <int CPL, int IPG>
 __device__ __forceinline__ void gu_issue(GuRegs<CPL, IPG>& R, const LayerDev& Ly, const Dims& dm,
-                                         const Misc& ms, int n_rt, const GuPlan& pl, int grp,
-                                         int li) {
+                                         const int64_t* ent_k, int n_rt, const GuPlan& pl,
+                                         int grp, int li) {
 #pragma unroll
   for (int j = 0; j < IPG; ++j) {
     const int it = pl.ib + grp + kGroups * j;
@@ -325,7 +323,7 @@ __device__ __forceinline__ void gu_issue(GuRegs<CPL, IPG>& R, const LayerDev& Ly
     const uint32_t *gq, *uq;
     const uint16_t *gs, *us;
     int row;
-    if (!gu_item(Ly, dm, ms, n_rt, it, gq, uq, gs, us, row)) continue;
+    if (!gu_item(Ly, dm, ent_k, n_rt, it, gq, uq, gs, us, row)) continue;
     const int gsh = __builtin_ctz(dm.G);  // G is a power of two
     const int wpr = dm.d / 8, spr = dm.d >> gsh;
     const uint32_t* grow = gq + (int64_t)row * wpr;
@@ -343,7 +341,7 @@ __device__ __forceinline__ void gu_issue(GuRegs<CPL, IPG>& R, const LayerDev& Ly
 
 template <int CPL, int IPG>
 __device__ __forceinline__ void gu_finish(const GuRegs<CPL, IPG>& R, const Dims& dm,
-                                          const Misc& ms, int n_rt, int Is, const GuPlan& pl,
+                                          const int64_t* ent_k, int n_rt, int Is, const GuPlan& pl,
                                           int grp, int li, const uint16_t* xperm, uint64_t* xg,
                                           uint32_t ep) {
 #pragma unroll
@@ -351,7 +349,7 @@ __device__ __forceinline__ void gu_finish(const GuRegs<CPL, IPG>& R, const Dims&
     const int it = pl.ib + grp + kGroups * j;
     if (it >= pl.ie) continue;  // uniform over the lane group
     const bool routed = it < n_rt;
-    const bool ok = !routed || ms.ent[it / kStackI] >= 0;
+    const bool ok = !routed || ent_k[it / kStackI] >= 0;
     float ag = 0.0f, au = 0.0f;
     if (ok) {
 #pragma unroll
@@ -520,11 +518,11 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
   }
   const int drow = db + grp;
 
-  // Phase B loads of a layer whose routed entries are in ms.ent: down rows
+  // Phase B loads of a layer whose routed entries are ent_k[0..K): down rows
   // [drow] of every expert slot, LoRA B_down row, the shared-expert LoRA
   // matrices. Issued once this workgroup's gate/up outputs are published, so
   // that issuing them overlaps the wait for everyone else's.
-  auto issue_b = [&](const LayerDev& Ly, PhaseA<CPL_D, IPG, NX>& A) {
+  auto issue_b = [&](const LayerDev& Ly, const int64_t* ent_k, PhaseA<CPL_D, IPG, NX>& A) {
     const bool has_sh = Ly.sh.present != 0;
     const int Is = has_sh ? dm.Is : 0;
     const bool lora_gu = has_sh && Ly.sh.ag != nullptr;
@@ -539,7 +537,7 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
         const uint32_t* q = nullptr;
         const uint16_t* sc = nullptr;
         if (k < K) {
-          const int64_t ent = ms.ent[k];
+          const int64_t ent = ent_k[k];
           if (ent >= 0) {
             q = (const uint32_t*)entry_ptr(Ly.pool.down.q, ent, Ly.pool.stride_q);
             sc = (const uint16_t*)entry_ptr(Ly.pool.down.s, ent, Ly.pool.stride_s);
@@ -600,11 +598,9 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
     A.gu_loaded = false;
     if (!Ly.router) {
       // routing known: entries from the tables
-      if (t < 16) ms.ent[t] = t < K ? ms.ent_all[(l - a.l0) * K + t] : 0;
-      __syncthreads();
       GuPlan pl;
       split(K * I + Is, G, cu, pl.ib, pl.ie);
-      gu_issue<CPL_D, IPG>(A.gu, Ly, dm, ms, K * I, pl, grp, li);
+      gu_issue<CPL_D, IPG>(A.gu, Ly, dm, &ms.ent_all[(l - a.l0) * K], K * I, pl, grp, li);
       A.gu_loaded = true;
     }
   };
@@ -693,40 +689,36 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
       ll_gather<2>(a.xr + (int64_t)l * E, E, ep, land, a.flags, &ms.abort);
       __syncthreads();
       stamp(a, l, 13);
-      if (wave == 0) route_wave(dm, (const float*)land, Ly.router_bias, ms.rs, ms.ridx, ms.rw, a.flags);
+      // the executed set (this layer's head reads it too) and its weights go
+      // straight into the launch's routing tables
+      if (wave == 0)
+        route_wave(dm, (const float*)land, Ly.router_bias, ms.rs, &ms.ridx_all[step * K],
+                   &ms.rw_all[step * K], a.flags);
       __syncthreads();
       stamp(a, l, 14);
-      if (t < 16) {
-        int64_t ent = 0;
-        if (t < K) {
-          ent = resolve_entry(Ly.pool, E, ms.ridx[t]);
-          ms.ridx_all[step * K + t] = ms.ridx[t];  // the executed set, for this layer's head
-        }
-        ms.ent[t] = ent;
+      if (t < K) {
+        const int64_t ent = resolve_entry(Ly.pool, E, ms.ridx_all[step * K + t]);
+        ms.ent_all[step * K + t] = ent;
         if (ent < 0 && cu == 0) atomicOr(&a.flags[FLAG_RANGE], 1);
       }
       __syncthreads();
-    } else {
-      if (t < K) {
-        ms.ridx[t] = ms.ridx_all[step * K + t];
-        ms.rw[t] = ms.rw_all[step * K + t];
-        if (ms.ent[t] < 0 && cu == 0) atomicOr(&a.flags[FLAG_RANGE], 1);
-      }
-      __syncthreads();
+    } else if (t < K && ms.ent_all[step * K + t] < 0 && cu == 0) {
+      atomicOr(&a.flags[FLAG_RANGE], 1);
     }
+    const int64_t* ent_k = &ms.ent_all[step * K];
     if (t < K && cu == 0) {
-      eidx[t] = ms.ridx[t];
-      ew[t] = ms.rw[t];
+      eidx[t] = ms.ridx_all[step * K + t];
+      ew[t] = ms.rw_all[step * K + t];
     }
     if (t < NX) {
       const uint32_t* q = nullptr;
       const uint16_t* sc = nullptr;
       float cf = 0.0f;
       if (t < K) {
-        if (ms.ent[t] >= 0) {
-          q = (const uint32_t*)entry_ptr(Ly.pool.down.q, ms.ent[t], Ly.pool.stride_q);
-          sc = (const uint16_t*)entry_ptr(Ly.pool.down.s, ms.ent[t], Ly.pool.stride_s);
-          cf = ms.rw[t];
+        if (ent_k[t] >= 0) {
+          q = (const uint32_t*)entry_ptr(Ly.pool.down.q, ent_k[t], Ly.pool.stride_q);
+          sc = (const uint16_t*)entry_ptr(Ly.pool.down.s, ent_k[t], Ly.pool.stride_s);
+          cf = ms.rw_all[step * K + t];
         }
       } else if (t == K && has_sh) {
         q = Ly.sh.down.q;
@@ -743,9 +735,9 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
     {
       GuPlan pl;
       split(n_rt + Is, G, cu, pl.ib, pl.ie);
-      if (!A.gu_loaded) gu_issue<CPL_D, IPG>(A.gu, Ly, dm, ms, n_rt, pl, grp, li);
+      if (!A.gu_loaded) gu_issue<CPL_D, IPG>(A.gu, Ly, dm, ent_k, n_rt, pl, grp, li);
       vm_drained();  // gate/up rows, router and LoRA A rows have arrived
-      gu_finish<CPL_D, IPG>(A.gu, dm, ms, n_rt, Is, pl, grp, li, xperm, xg, ep);
+      gu_finish<CPL_D, IPG>(A.gu, dm, ent_k, n_rt, Is, pl, grp, li, xperm, xg, ep);
       if (A.n_ax) {
         int b, e;
         split(r2, G, cu, b, e);
@@ -757,7 +749,7 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
     stamp(a, l, 4);
 
     // ---- phase B loads: down rows, shared-expert LoRA -----------------------
-    issue_b(Ly, A);
+    issue_b(Ly, ent_k, A);
     const DownRegs<NX>& D = A.D;
     const LoraRegs& LR = A.LR;
     stamp(a, l, 5);
