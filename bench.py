@@ -57,6 +57,34 @@ def measured_traffic():
     return int(m_b.group(1))
 
 
+def copy_bandwidth(nbytes: int = 1 << 30, reps: int = 5) -> float:
+    """Device-to-device copy rate (read + write bytes per second, GB/s) of a
+    plain torch copy of nbytes: the reference the algorithmic rate is also
+    compared against."""
+    import torch
+    src = torch.empty(nbytes // 2, dtype=torch.float16, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def copy_probe(nbytes: int):
     """A plain device copy of known size (calibrates the PMC byte counters)."""
     import torch
@@ -117,7 +145,8 @@ def cpu_baseline(tier: str, seed: int, roles, host_layers, toks, idx0, w0, n_tok
     dt = time.perf_counter() - t0
     return dict(value=n_tokens / dt, unit="tokens/s", cores=1, kind="oracle",
                 sample=f"first {n_tokens} decode tokens of the same 40-layer workload "
-                       f"({n_tokens * L} layer-steps, single thread, {dt:.1f} s)")
+                       f"({n_tokens * L} layer-steps, single thread, {dt:.1f} s, "
+                       f"{cpu_model()}, {os.cpu_count()} host threads available)")
 
 
 def run_chunk(args):
@@ -538,6 +567,7 @@ def main():
     ab = algorithmic_bytes(dm, roles)
     gbs = ab["total"] / (ms * 1e-3) / 1e9
     kgbs = ab["total"] / (kernel_ms * 1e-3) / 1e9
+    copy_gbs = copy_bandwidth()
     traffic = measured_traffic()
     tok_s = 1000.0 / ms
     cpu = None
@@ -572,6 +602,8 @@ def main():
         "layer_steps_per_s": round(tok_s * L, 1),
         "hbm_gb_per_s": round(gbs, 1),
         "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "device_copy_gb_per_s": round(copy_gbs, 1),
+        "hbm_frac_of_device_copy": round(gbs / copy_gbs, 4),
         "algorithmic_bytes_per_token": ab["total"],
         "roofline": {
             "bound": "hbm",
