@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+F16_PEAK_TFLOPS = 2500.0  # dense fp16 MFMA
 METRIC = "35B-tier decode layer-steps/s & tokens/s at B=1; HBM GB/s as % of MI355X peak"
 KERNEL_SOURCES = ["stack.hip", "gemv.h", "device.h", "internal.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_stack_35b_stack.md")
@@ -150,19 +151,20 @@ def cpu_baseline(tier: str, seed: int, roles, host_layers, toks, idx0, w0, n_tok
 
 
 def run_chunk(args):
-    """Batched chunk: B=32 independent N(0,1) fp16 tokens on one 35B-tier layer
-    (K in {2, 4, 8}), routed by the layer's fp16 router with softmax top-K,
-    then moe_int4_decode's grouped MFMA path. The routing runs on the GPU
-    through prerouter_forward with a head whose fc1 and fc2 are zero and whose
-    linear path is [router | 0 | 0] (its logits are the router's exactly);
-    it is input preparation, outside the timed loop. Weight bytes = the union
-    of the chunk's experts + the shared expert + its LoRA, each read once per
-    chunk."""
+    """Batched tokens on one 35B-tier layer (K in {2, 4, 8}): B independent
+    N(0,1) fp16 tokens (B = 32, a decode chunk, by default; prefill-sized
+    batches with --chunk-b, e.g. 3072 for the pages' ~3.1k-token prompt),
+    routed by the layer's fp16 router with softmax top-K, then
+    moe_int4_decode's grouped MFMA path. The routing runs on the GPU through
+    prerouter_forward with a head whose fc1 and fc2 are zero and whose linear
+    path is [router | 0 | 0] (its logits are the router's exactly); it is
+    input preparation, outside the timed loop. Weight bytes = the union of the
+    batch's experts + the shared expert + its LoRA, each read once; flops =
+    2 B (K+1) 3 I d (the int4 x fp16 products, LoRA not counted)."""
     import torch
     from sparse_moe_decode_amd import api, synth
     from sparse_moe_decode_amd import workloads as wl
     tier = "35b"
-    B = 32
     dm0 = synth.dims(tier)
     rng = synth.rng_for(args.seed, 70)
     pool = synth.routed_pool(rng, dm0)
@@ -175,41 +177,48 @@ def run_chunk(args):
                    lin=torch.cat([wl.to_dev(router),
                                   torch.zeros((E, 2 * E), dtype=torch.float16, device="cuda")],
                                  dim=1).contiguous())
-    x = synth.f16_normal(rng, (B, dm0["d"]))
     expert = 3 * (dm0["I"] * dm0["d"] // 2) + 3 * 2 * (dm0["I"] * dm0["d"] // dm0["G"])
     lora = 2 * (dm0["r"] * dm0["d"] + dm0["Is"] * dm0["r"]) * 2 + (dm0["r"] * dm0["Is"] + dm0["d"] * dm0["r"]) * 2
     lines = []
-    for K in ((2, 4, 8) if args.chunk_k == 0 else (args.chunk_k,)):
-        dm = synth.dims(tier, K=K)
-        ctx = api.Context(dm, max_tokens=B)
-        dx = torch.from_numpy(x).cuda()
-        krng = synth.rng_for(args.seed, 71, K)
-        cur = wl.to_dev(np.stack([synth.random_set(krng, E, K) for _ in range(B)]))
-        didx, dw = api.prerouter_forward(ctx, as_head, dx, cur)
-        torch.cuda.synchronize()
-        idx = didx.cpu().numpy()
-        y = torch.empty_like(dx)
-        for _ in range(args.warmup):
-            api.moe_int4_decode(ctx, dpool, dx, didx, dw, y=y, shared=dsh)
-        assert api.device_status(ctx) == 0
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(args.steps):
-            api.moe_int4_decode(ctx, dpool, dx, didx, dw, y=y, shared=dsh)
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / args.steps
-        union = int(len(np.unique(idx)))
-        nbytes = union * expert + expert + lora
-        flops = 2 * B * (K + 1) * 3 * dm0["I"] * dm0["d"]
-        lines.append({"K": K, "union_experts": union, "ms_per_chunk": round(ms, 5),
-                      "tokens_per_s": round(B / ms * 1e3, 1), "weight_bytes": nbytes,
-                      "hbm_gb_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
-                      "hbm_frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                      "tflops": round(flops / (ms * 1e-3) / 1e12, 2)})
-    print(json.dumps({"workload": "35B-tier batched chunk: B=32 tokens, one layer, grouped int4 "
-                                  "MFMA (moe_int4_decode, B>=16 path)", "steps": args.steps,
+    for B in args.chunk_b:
+        x = synth.f16_normal(synth.rng_for(args.seed, 72, B), (B, dm0["d"]))
+        for K in ((2, 4, 8) if args.chunk_k == 0 else (args.chunk_k,)):
+            dm = synth.dims(tier, K=K)
+            ctx = api.Context(dm, max_tokens=B)
+            dx = torch.from_numpy(x).cuda()
+            krng = synth.rng_for(args.seed, 71, K)
+            cur = wl.to_dev(np.stack([synth.random_set(krng, E, K) for _ in range(B)]))
+            didx, dw = api.prerouter_forward(ctx, as_head, dx, cur)
+            torch.cuda.synchronize()
+            idx = didx.cpu().numpy()
+            y = torch.empty_like(dx)
+            for _ in range(args.warmup):
+                api.moe_int4_decode(ctx, dpool, dx, didx, dw, y=y, shared=dsh)
+            assert api.device_status(ctx) == 0
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(args.steps):
+                api.moe_int4_decode(ctx, dpool, dx, didx, dw, y=y, shared=dsh)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / args.steps
+            counts = np.bincount(idx.ravel(), minlength=E)
+            union = int(np.count_nonzero(counts))
+            tiles = int(np.sum((counts + 31) // 32)) + (B + 31) // 32
+            nbytes = union * expert + expert + lora
+            flops = 2 * B * (K + 1) * 3 * dm0["I"] * dm0["d"]
+            lines.append({"B": B, "K": K, "union_experts": union, "tiles": tiles,
+                          "ms_per_call": round(ms, 5), "tokens_per_s": round(B / ms * 1e3, 1),
+                          "weight_bytes": nbytes,
+                          "hbm_gb_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                          "hbm_frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                          "mfma_frac_of_f16_peak": round(flops / (ms * 1e-3) / 1e12 / F16_PEAK_TFLOPS, 4)})
+            ctx.close()
+            print(json.dumps(lines[-1]), file=sys.stderr, flush=True)
+    print(json.dumps({"workload": "35B-tier batched tokens: one layer, grouped int4 MFMA "
+                                  "(moe_int4_decode, B>=16 path)", "steps": args.steps,
                       "warmup": args.warmup, "results": lines}))
 
 
@@ -467,7 +476,7 @@ def main():
                     help="only run a plain device copy of this many bytes (counter calibration)")
     ap.add_argument("--workload", choices=["stack", "chunk", "staged", "layer"], default="stack",
                     help="stack: the 40-layer resident decode (the bench line); chunk: the "
-                         "B=32 batched chunk; staged: the host-staged stack; layer: single "
+                         "batched path (B=32 chunk, or --chunk-b); staged: the host-staged stack; layer: single "
                          "layer-steps, warm and cold")
     ap.add_argument("--reserve-cus", type=int, default=16,
                     help="staged workload: compute units left to the staging copies")
@@ -475,6 +484,9 @@ def main():
                     help="staged workload: predicted layers per launch")
     ap.add_argument("--chunk-k", type=int, default=0, choices=[0, 2, 4, 8],
                     help="chunk workload: only this top-K (0 = 2, 4 and 8)")
+    ap.add_argument("--chunk-b", type=int, nargs="+", default=[32],
+                    help="chunk workload: batch sizes (32 = a decode chunk; 3072 = a "
+                         "prefill-sized batch)")
     args = ap.parse_args()
     if args.rho is None:
         from sparse_moe_decode_amd.workloads import RHO_STACK

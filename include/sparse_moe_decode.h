@@ -122,9 +122,10 @@ typedef struct e0_head {
 
 typedef struct e0_ctx e0_ctx;
 
-/* Create a context for one tier. Allocates the small device scratch the
- * entry points share (sized for up to `max_tokens` tokens per call) on the
- * current HIP device. Calls on one context must not overlap in time. */
+/* Create a context for one tier. Allocates the device scratch the entry
+ * points share, sized for up to `max_tokens` tokens per call (1..8192; a
+ * prefill batch of B tokens holds about B*(K+1)*(4d + 4I) bytes of it), on
+ * the current HIP device. Calls on one context must not overlap in time. */
 int e0_create(const e0_spec* spec, int32_t max_tokens, e0_ctx** out);
 void e0_destroy(e0_ctx* ctx);
 
@@ -150,10 +151,11 @@ int e0_device_status(e0_ctx* ctx, void* stream);
  *   y        fp16 [B, d] output (round-to-nearest-even of the fp32 sum).
  * B <= max_tokens. Internal sums are fp32; q*s is never rounded to fp16 and
  * the SwiGLU intermediate keeps fp32 precision. B < 16 runs one GEMV per
- * (token, expert); B >= 16 runs in chunks of up to 32 tokens grouped by
- * expert, each expert's weights read once per chunk by int4 x fp16 MFMA
- * tiles (fp32 group scales applied to fp32 partials) [MW §3.1 Executor
- * paths: batched chunks take the whole-layer path]. Both are deterministic. */
+ * (token, expert); B >= 16 groups the B*K entries by expert in one launch
+ * and runs int4 x fp16 MFMA tiles of up to 32 of an expert's tokens (fp32
+ * group scales applied to fp32 partials), each expert's weights read once per
+ * tile [MW §3.1 Executor paths: batched chunks and prefill take the
+ * whole-layer path]. Both are deterministic. */
 int moe_int4_decode(e0_ctx* ctx, const e0_experts* routed, const int32_t* slot_of,
                     const e0_shared* shared, const uint16_t* x, const int32_t* idx,
                     const float* w, int32_t n_tokens, uint16_t* y, void* stream);

@@ -74,7 +74,7 @@ int e0_create(const e0_spec* spec, int32_t max_tokens, e0_ctx** out) {
   const e0_spec& p = *spec;
   if (p.d_model <= 0 || p.n_experts <= 0 || p.top_k < 1 || p.top_k > 8 ||
       p.top_k > p.n_experts || p.inter <= 0 || p.group <= 0 || max_tokens < 1 ||
-      max_tokens > 256)
+      max_tokens > 8192)
     return fail(E0_ERR_ARG, "e0_create: bad dimensions");
   if (p.group % 32 || p.d_model % p.group || p.inter % p.group)
     return fail(E0_ERR_SHAPE, "e0_create: group %d must be a multiple of 32 dividing d and I",
@@ -119,11 +119,12 @@ int e0_create(const e0_spec* spec, int32_t max_tokens, e0_ctx** out) {
   const size_t n_p = (size_t)B * (dm.P > 0 ? dm.P : 1);
   const size_t n_e = (size_t)B * dm.E;
   auto up = [](size_t bytes) { return (bytes + 255) & ~(size_t)255; };
-  const size_t n_grp = 1 + 4 * (size_t)B * dm.K;
+  const size_t n_grp = 2 + 4 * (size_t)B * dm.K + 2 * (size_t)batched_max_tiles(B, dm.K, dm.E);
   const size_t n_slot = (size_t)B * (dm.K + 1);
+  const size_t n_axp = (size_t)kLoraSlices * B * 2 * rmax;
   const size_t bytes = up(n_gu * 4) + up(n_ax * 4) + up(n_d * 4) + up(n_d * 2) + up(n_p * 4) +
                        2 * up(n_e * 4) + 2 * up((size_t)B * dm.K * 4) + up(N_FLAGS * 4) +
-                       up(n_grp * 4) + up(n_slot * dm.d * 4);
+                       up(n_grp * 4) + up(n_axp * 4) + up(n_slot * dm.d * 4);
   hipError_t e = hipMalloc(&c->block, bytes);
   if (e != hipSuccess) {
     delete c;
@@ -149,6 +150,7 @@ int e0_create(const e0_spec* spec, int32_t max_tokens, e0_ctx** out) {
   s.sink_w = (float*)q; q += up((size_t)B * dm.K * 4);
   s.flags = (int32_t*)q; q += up(N_FLAGS * 4);
   s.grp = (int32_t*)q; q += up(n_grp * 4);
+  s.axp = (float*)q; q += up(n_axp * 4);
   s.yk = (float*)q;
   *out = c;
   return E0_OK;
@@ -272,14 +274,10 @@ int moe_int4_decode(e0_ctx* ctx, const e0_experts* routed, const int32_t* slot_o
   hipError_t e;
   const Dims& dm = ctx->dm;
   if (n_tokens >= kBatchedMin && batched_supported(dm)) {
-    // chunks of up to 32 tokens through the grouped MFMA path
-    for (int c0 = 0; c0 < n_tokens; c0 += 32) {
-      const int nb = n_tokens - c0 < 32 ? n_tokens - c0 : 32;
-      const uint16_t* xc = x + (int64_t)c0 * dm.d;
-      if ((e = launch_batched(dm, pool, sh, xc, idx + (int64_t)c0 * dm.K, w + (int64_t)c0 * dm.K,
-                              nb, y + (int64_t)c0 * dm.d, ctx->s, st)) != hipSuccess)
-        return hip_fail(e, "batched chunk");
-    }
+    // the whole batch through the grouped MFMA path: each expert's weights
+    // are read once for all of its tokens
+    if ((e = launch_batched(dm, pool, sh, x, idx, w, n_tokens, y, ctx->s, st)) != hipSuccess)
+      return hip_fail(e, "batched");
     return E0_OK;
   }
   if ((e = lora_a_x(ctx, sh, x, n_tokens, st)) != hipSuccess) return hip_fail(e, "lora A");

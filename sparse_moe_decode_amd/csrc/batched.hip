@@ -1,4 +1,5 @@
-// Batched decode chunk (16..32 tokens): grouped int4 GEMMs on MFMA.
+// Batched tokens (B >= 16, decode chunks up to prefill-sized batches):
+// grouped int4 GEMMs on MFMA.
 //
 // Source: "The Other Half of the Memory Wall" §3.1 Executor paths (batched
 // chunks take the whole-layer path: experts are grouped so each expert's
@@ -25,8 +26,11 @@
 //      dequantised weights; also A_down . h of the shared expert.
 //   4. k_mb_combine: y = sum_k w_k y_k + y_shared + down LoRA, in a fixed
 //      order (no atomics, deterministic), rounded to fp16.
-// The shared expert is grid row 0 of steps 2 and 3 (dispatched first, it has
-// the most tokens); a chunk holds at most 32 tokens.
+// Steps 2 and 3 run over a work list of tiles: one per 32 tokens of each
+// union member (the MFMA column block), the shared expert's tiles first
+// (dispatched first, they have the most tokens). A batch of any size B is
+// one launch of each step; each expert's weights are read once per 32 of its
+// tokens, so B = 32 reads every expert with routed tokens at most once.
 
 #include "gemv.h"
 #include "internal.h"
@@ -41,19 +45,25 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kCols = 32;  // tokens per MFMA column block
 constexpr int kMaxR = 32;  // largest LoRA rank of the shared expert
 
-// Grouping tables in s.grp (int32): [0] union size; then sorted entries
-// (b*K + k) [BK]; expert, first sorted position and run length per union
-// member [BK] each.
+__device__ __forceinline__ h8 as_h8(uint4 v) { return __builtin_bit_cast(h8, v); }
+
+// Grouping tables in s.grp (int32): [0] union size, [1] number of tiles;
+// then sorted entries (b*K + k) [BK]; expert, first sorted position and run
+// length per union member [BK] each; the work tiles as (member, tile) pairs
+// (member -1 = the shared expert, whose tokens are all B), one per up to 32
+// of a member's tokens.
 struct Groups {
   int32_t* n_union;
+  int32_t* n_tiles;
   int32_t* sorted;
   int32_t* uexp;
   int32_t* ustart;
   int32_t* ucount;
+  int32_t* tiles;
 };
 
 __host__ __device__ inline Groups groups(int32_t* g, int BK) {
-  return {g, g + 1, g + 1 + BK, g + 1 + 2 * BK, g + 1 + 3 * BK};
+  return {g, g + 1, g + 2, g + 2 + BK, g + 2 + 2 * BK, g + 2 + 3 * BK, g + 2 + 4 * BK};
 }
 
 struct MbArgs {
@@ -66,7 +76,9 @@ struct MbArgs {
   int32_t* grp;
   const int32_t* idx;    // [B][K]
   const float* w;        // [B][K]
-  float* ax;             // [B][3*rmax] LoRA A products (gate, up, down)
+  float* ax;             // [B][3*rmax] LoRA A products (down in slot 2)
+  float* axp;            // [n_sl][B][2*rmax] gate/up LoRA A products per input slice
+  int n_sl;              // input slices (divides d/64)
   int rmax;
   float* H;              // [B][K+1][imax] SwiGLU outputs
   float* Y;              // [B][K+1][d] per-slot down outputs
@@ -85,73 +97,122 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-// Block B of k_mb_prep: the chunk's B*K entries sorted by expert (ascending
-// expert id, then entry order), the union of experts and each member's run.
-// Integer counting only, so the result does not depend on thread timing.
+// Block B of k_mb_prep: the B*K entries sorted by expert (ascending expert
+// id, then entry order), the union of experts with each member's run, and
+// the work tiles. Integer counting only, so nothing depends on thread timing:
+// counts by LDS atomics, offsets by prefix sums, then a stable placement over
+// 256 entries per pass. Lanes of a wave that hold the same expert find each
+// other with one ballot per bit of the id; an entry's rank is the number of
+// its expert's entries in earlier waves of the pass (per-wave counts in LDS,
+// tagged with the pass) plus earlier lanes of its own wave, after the
+// expert's running cursor. kMaxE = 512 ids take nine bits.
 __device__ void group_entries(const MbArgs& a) {
   __shared__ int cnt[kMaxE];
-  __shared__ __align__(16) int sidx[256];
-  __shared__ int wtot[2][4];
+  __shared__ int cur[kMaxE];
+  __shared__ int wcnt[4][kMaxE];  // (pass tag << 16) | entries of the wave
+  __shared__ int wtot[3][4];
   const int E = a.dm.E, K = a.dm.K, BK = a.B * K;
   const Groups g = groups(a.grp, BK);
-  const int t = threadIdx.x;
-  for (int e = t; e < kMaxE; e += blockDim.x) cnt[e] = 0;
+  const int t = threadIdx.x, nt = blockDim.x;
+  for (int e = t; e < kMaxE; e += nt) cnt[e] = 0;
+  for (int e = t; e < 4 * kMaxE; e += nt) (&wcnt[0][0])[e] = 0;
   __syncthreads();
-  int e = -1;
-  if (t < BK) {
-    e = a.idx[t];
-    if (e < 0 || e >= E) {
-      atomicOr(&a.flags[FLAG_RANGE], 1);
-      e = -1;
-    } else {
-      atomicAdd(&cnt[e], 1);  // integer counts: order-independent
+  for (int i0 = t; i0 < BK; i0 += 4 * nt) {
+    int ev[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) ev[u] = i0 + u * nt < BK ? a.idx[i0 + u * nt] : -2;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (ev[u] == -2) continue;
+      if (ev[u] < 0 || ev[u] >= E)
+        atomicOr(&a.flags[FLAG_RANGE], 1);
+      else
+        atomicAdd(&cnt[ev[u]], 1);  // integer counts: order-independent
     }
-    sidx[t] = e;
   }
   __syncthreads();
-  // thread t owns experts 2t and 2t+1 (E <= 512)
+  // thread t owns experts 2t and 2t+1 (E <= 512): offsets, union positions
+  // and tile positions by prefix sums
   const int c0 = cnt[2 * t], c1 = cnt[2 * t + 1];
+  const int n0 = (c0 + kCols - 1) / kCols, n1 = (c1 + kCols - 1) / kCols;
   int ps = wave_incl_scan(c0 + c1);
   int pu = wave_incl_scan((c0 > 0) + (c1 > 0));
+  int pt = wave_incl_scan(n0 + n1);
   const int wv = t >> 6;
   if ((t & 63) == 63) {
     wtot[0][wv] = ps;
     wtot[1][wv] = pu;
+    wtot[2][wv] = pt;
   }
   __syncthreads();
   for (int v = 0; v < wv; ++v) {
     ps += wtot[0][v];
     pu += wtot[1][v];
+    pt += wtot[2][v];
   }
+  const int n_sh = a.sh.present ? (a.B + kCols - 1) / kCols : 0;
   const int off0 = ps - c0 - c1;
   int u = pu - (c0 > 0) - (c1 > 0);
+  int tp = n_sh + pt - n0 - n1;
   if (c0) {
     g.uexp[u] = 2 * t;
     g.ustart[u] = off0;
     g.ucount[u] = c0;
+    for (int j = 0; j < n0; ++j) {
+      g.tiles[2 * tp] = u;
+      g.tiles[2 * tp + 1] = j;
+      ++tp;
+    }
     ++u;
   }
   if (c1) {
     g.uexp[u] = 2 * t + 1;
     g.ustart[u] = off0 + c0;
     g.ucount[u] = c1;
-  }
-  if (t == blockDim.x - 1) *g.n_union = pu;
-  __syncthreads();
-  // cnt becomes the exclusive offsets
-  cnt[2 * t] = off0;
-  cnt[2 * t + 1] = off0 + c0;
-  __syncthreads();
-  if (e >= 0) {
-    int rank = 0;  // earlier entries routed to the same expert
-    const int4* s4 = reinterpret_cast<const int4*>(sidx);
-    int j = 0;
-    for (; j + 4 <= t; j += 4) {
-      const int4 v = s4[j >> 2];
-      rank += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
+    for (int j = 0; j < n1; ++j) {
+      g.tiles[2 * tp] = u;
+      g.tiles[2 * tp + 1] = j;
+      ++tp;
     }
-    for (; j < t; ++j) rank += sidx[j] == e;
-    g.sorted[cnt[e] + rank] = t;
+  }
+  for (int j = t; j < n_sh; j += blockDim.x) {
+    g.tiles[2 * j] = -1;
+    g.tiles[2 * j + 1] = j;
+  }
+  if (t == blockDim.x - 1) {
+    *g.n_union = pu;
+    *g.n_tiles = n_sh + pt;
+  }
+  cur[2 * t] = off0;
+  cur[2 * t + 1] = off0 + c0;
+  const uint64_t below = (1ull << (t & 63)) - 1;
+  int e_next = t < BK ? a.idx[t] : -1;
+  for (int p0 = 0, tag = 1; p0 < BK; p0 += nt, ++tag) {
+    const int i = p0 + t;
+    const int e = i < BK && e_next >= 0 && e_next < E ? e_next : -1;
+    e_next = i + nt < BK ? a.idx[i + nt] : -1;  // next pass, loaded early
+    uint64_t same = __ballot(e >= 0);
+#pragma unroll
+    for (int bit = 0; bit < 9; ++bit) {
+      const bool set = (e >> bit) & 1;
+      const uint64_t m = __ballot(set);
+      same &= set ? m : ~m;
+    }
+    const int rank = __popcll(same & below), n_same = __popcll(same);
+    const bool leader = e >= 0 && rank == 0;
+    if (leader) wcnt[wv][e] = (tag << 16) | n_same;
+    // also orders the previous pass's cursor updates before the reads below
+    __syncthreads();
+    if (e >= 0) {
+      int base = cur[e] + rank;
+      for (int v = 0; v < wv; ++v) {
+        const int c = wcnt[v][e];
+        if ((c >> 16) == tag) base += c & 0xFFFF;
+      }
+      g.sorted[base] = i;
+    }
+    __syncthreads();
+    if (leader) atomicAdd(&cur[e], n_same);  // integer sum: order-independent
   }
 }
 
@@ -174,34 +235,51 @@ __device__ void prep_token(const MbArgs& a, int b) {
   }
 }
 
-// LoRA blocks of k_mb_prep: each wave one output o of ax[b] = (A_gate x_b,
-// A_up x_b), o in [0, 2r).
+// LoRA blocks of k_mb_prep: partial (A_gate x_b, A_up x_b) over one slice of
+// the inputs for 32 tokens b0.. per block, on MFMA: tokens are operand A
+// (rows), the 2r LoRA rows operand B (columns, gate rows then up rows, 32 per
+// column block); the four waves take a quarter of the slice each and meet in
+// LDS (fixed order). The slices are summed in order by the gate/up step.
+// Products of fp16 values are exact; sums are fp32.
 __device__ void prep_lora(const MbArgs& a, int lb) {
-  const int d = a.dm.d, r = a.dm.r, per = (2 * r + 3) / 4;
-  const int b = lb / per, o = (lb % per) * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (b >= a.B || o >= 2 * r) return;
-  const uint16_t* xb = a.x + (int64_t)b * d;
-  {
-    const uint16_t* A = (o < r ? a.sh.ag : a.sh.au) + (int64_t)(o % r) * d;
-    float s = 0.0f;
-    for (int c = lane; c < d / 8; c += 64) {
-      const uint4 av = ldg(reinterpret_cast<const uint4*>(A + 8 * c));
-      const uint4 xv = ldg(reinterpret_cast<const uint4*>(xb + 8 * c));
-      const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, xw[4] = {xv.x, xv.y, xv.z, xv.w};
+  __shared__ float red[4][16][64];
+  const int d = a.dm.d, r = a.dm.r, b0 = (lb / a.n_sl) * kCols, sl = lb % a.n_sl;
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, n = l & 31, kh = l >> 5;
+  const int nb = min(kCols, a.B - b0);
+  const int q = d / a.n_sl / 4, k0 = sl * (d / a.n_sl) + wave * q;
+  float* out = a.axp + (int64_t)sl * a.B * 2 * a.rmax;
+  // token rows past the batch read a valid row (their outputs are not stored)
+  const uint16_t* xrow = a.x + (int64_t)(b0 + (n < nb ? n : nb - 1)) * d + k0 + 8 * kh;
+  for (int cb = 0; cb < 2 * r; cb += 32) {
+    const int o = cb + n;
+    const bool col_ok = o < 2 * r;
+    const uint16_t* arow =
+        (o < r ? a.sh.ag : a.sh.au) + (int64_t)((col_ok ? o : 0) % r) * d + k0 + 8 * kh;
+    f32x16 acc = {};
+#pragma unroll 4
+    for (int k = 0; k < q; k += 16) {
+      const uint4 xv = ldg(reinterpret_cast<const uint4*>(xrow + k));
+      const uint4 av = col_ok ? ldg(reinterpret_cast<const uint4*>(arow + k)) : make_uint4(0, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(xv), as_h8(av), acc, 0, 0, 0);
+    }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f16x2 ah = as_h2(aw[q]), xh = as_h2(xw[q]);
-        s = fmaf((float)ah.x, (float)xh.x, s);
-        s = fmaf((float)ah.y, (float)xh.y, s);
+    for (int i = 0; i < 16; ++i) red[wave][i][l] = acc[i];
+    __syncthreads();
+    // thread (register i, lane l) sums the four quarters in order
+    for (int e = threadIdx.x; e < 16 * 64; e += blockDim.x) {
+      const int i = e >> 6, ll = e & 63;
+      const int t = 8 * (i >> 2) + 4 * (ll >> 5) + (i & 3), oo = cb + (ll & 31);
+      if (t < nb && oo < 2 * r) {
+        const float v = (red[0][i][ll] + red[1][i][ll]) + (red[2][i][ll] + red[3][i][ll]);
+        out[(int64_t)(b0 + t) * 2 * a.rmax + oo] = v;
       }
     }
-    s = wave_sum_rows(s);
-    if (lane == 0) a.ax[(int64_t)b * 3 * a.rmax + (o < r ? 0 : a.rmax) + o % r] = s;
+    __syncthreads();
   }
 }
 
-// Grid: B token blocks, one grouping block, then B*ceil(2r/4) LoRA blocks
-// when the shared expert has LoRA.
+// Grid: B token blocks, one grouping block, then ceil(B/32) x n_sl LoRA
+// blocks when the shared expert has LoRA.
 __global__ __launch_bounds__(256) void k_mb_prep(MbArgs a) {
   const int bx = blockIdx.x;
   if (bx < a.B)
@@ -222,8 +300,6 @@ __device__ __forceinline__ h8 q4_to_h8(uint32_t w) {
   r[4] = p2.x; r[5] = p2.y; r[6] = p3.x; r[7] = p3.y;
   return r;
 }
-
-__device__ __forceinline__ h8 as_h8(uint4 v) { return __builtin_bit_cast(h8, v); }
 
 __device__ __forceinline__ uint32_t word(const uint4& v, int j) {
   return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
@@ -285,12 +361,13 @@ __device__ __forceinline__ f32x16 dn_mma(const uint4 (&wq)[NG], const float (&sc
   return acc;
 }
 
-// Token and output slot of token row t of a union member's run.
+// Token and output slot of token row t of a tile: the shared expert's tiles
+// run over tokens start.., a member's over its sorted entries start...
 __device__ __forceinline__ void entry_of(const MbArgs& a, bool shared, int start, int t, int& b,
                                          int& k) {
   const int K = a.dm.K;
   if (shared) {
-    b = t;
+    b = start + t;
     k = K;
   } else {
     const Groups g = groups(a.grp, a.B * K);
@@ -300,15 +377,24 @@ __device__ __forceinline__ void entry_of(const MbArgs& a, bool shared, int start
   }
 }
 
-// Member of a grid row: y = 0 is the shared expert (dispatched first, it has
-// the most tokens), y = 1..n_union the union members in ascending expert id.
-__device__ __forceinline__ bool member_of(const MbArgs& a, int y, bool& shared, int& u) {
-  const Groups gv = groups(a.grp, a.B * a.dm.K);
-  const int nu = *gv.n_union;
-  shared = y == 0;
-  u = y - 1;
-  if (shared) return a.sh.present != 0;
-  return u < nu;
+// Work tile y: the shared expert (dispatched first, it has the most tokens)
+// or union member u, with its first entry and token count (<= 32).
+__device__ __forceinline__ bool tile_of(const MbArgs& a, int y, bool& shared, int& u, int& start,
+                                        int& count) {
+  const Groups g = groups(a.grp, a.B * a.dm.K);
+  if (y >= *g.n_tiles) return false;
+  const int mem = g.tiles[2 * y], tile = g.tiles[2 * y + 1];
+  shared = mem < 0;
+  u = mem;
+  const int first = kCols * tile;
+  if (shared) {
+    start = first;
+    count = min(kCols, a.B - first);
+  } else {
+    start = g.ustart[mem] + first;
+    count = min(kCols, g.ucount[mem] - first);
+  }
+  return true;
 }
 
 // Gate/up of one union member (or the shared expert) for 32 rows. Eight
@@ -324,30 +410,30 @@ __global__ __launch_bounds__(512) void k_mb_gate_up(MbArgs a) {
   const int K = dm.K, d = dm.d;
   const int imax = dm.I > dm.Is ? dm.I : dm.Is;
   bool shared;
-  int u;
-  if (!member_of(a, blockIdx.y, shared, u)) return;
+  int u, start, count;
+  if (!tile_of(a, blockIdx.y, shared, u, start, count)) return;
   const int m0 = blockIdx.x * 32;
   if (m0 >= (shared ? dm.Is : dm.I)) return;
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, n = l & 31, kh = l >> 5;
   const int mat = wave >> 2, quarter = wave & 3;  // 0 gate, 1 up
   const uint32_t* wq;
   const uint16_t* ws;
-  int start = 0, count = a.B;
   const bool lora = shared && a.sh.ag;
   if (shared) {
     wq = mat ? a.sh.up.q : a.sh.gate.q;
     ws = mat ? a.sh.up.s : a.sh.gate.s;
-    if (lora) {
-      for (int i = threadIdx.x; i < a.B * 2 * dm.r; i += blockDim.x) {
-        const int b = i / (2 * dm.r), j = i % (2 * dm.r);
-        axs[b][j / dm.r][j % dm.r] = a.ax[(int64_t)b * 3 * a.rmax + (j / dm.r) * a.rmax + j % dm.r];
+    if (lora) {  // LoRA A products of this tile's tokens: the slices in order
+      for (int i = threadIdx.x; i < count * 2 * dm.r; i += blockDim.x) {
+        const int tt = i / (2 * dm.r), j = i % (2 * dm.r);
+        const float* p = a.axp + (int64_t)(start + tt) * 2 * a.rmax + j;
+        float v = 0.0f;
+        for (int sl = 0; sl < a.n_sl; ++sl) v += p[(int64_t)sl * a.B * 2 * a.rmax];
+        axs[tt][j / dm.r][j % dm.r] = v;
       }
     }
   } else {
     const Groups gv = groups(a.grp, a.B * K);
     const int e = gv.uexp[u];
-    start = gv.ustart[u];
-    count = gv.ucount[u];
     const int64_t ent = resolve_entry(a.pool, dm.E, e);
     if (ent < 0) {
       if (threadIdx.x == 0) atomicOr(&a.flags[FLAG_RANGE], 1);
@@ -402,10 +488,10 @@ __global__ __launch_bounds__(512) void k_mb_gate_up(MbArgs a) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           const f16x2 g2 = as_h2(word(bgv, p)), u2 = as_h2(word(buv, p));
-          lg = fmaf((float)g2.x, axs[b][0][q + 2 * p], lg);
-          lg = fmaf((float)g2.y, axs[b][0][q + 2 * p + 1], lg);
-          lu = fmaf((float)u2.x, axs[b][1][q + 2 * p], lu);
-          lu = fmaf((float)u2.y, axs[b][1][q + 2 * p + 1], lu);
+          lg = fmaf((float)g2.x, axs[t][0][q + 2 * p], lg);
+          lg = fmaf((float)g2.y, axs[t][0][q + 2 * p + 1], lg);
+          lu = fmaf((float)u2.x, axs[t][1][q + 2 * p], lu);
+          lu = fmaf((float)u2.y, axs[t][1][q + 2 * p + 1], lu);
         }
       }
       gg = fmaf(c, lg, gg);
@@ -433,18 +519,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int K = dm.K, d = dm.d;
   const int imax = dm.I > dm.Is ? dm.I : dm.Is;
   bool shared;
-  int u;
-  if (!member_of(a, blockIdx.y, shared, u)) return;
+  int u, start, count;
+  if (!tile_of(a, blockIdx.y, shared, u, start, count)) return;
   const uint32_t* dq;
   const uint16_t* ds;
-  int start = 0, count = a.B;
   if (shared) {
     dq = a.sh.down.q; ds = a.sh.down.s;
   } else {
     const Groups gv = groups(a.grp, a.B * K);
     const int e = gv.uexp[u];
-    start = gv.ustart[u];
-    count = gv.ucount[u];
     const int64_t ent = resolve_entry(a.pool, dm.E, e);
     if (ent < 0) return;  // flagged by the gate/up step
     dq = (const uint32_t*)entry_ptr(a.pool.down.q, ent, a.pool.stride_q);
@@ -503,7 +586,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     // A_down . h_shared[t] for tokens t = blockIdx.x, blockIdx.x + gridDim.x, ...;
     // wave w takes ranks q = w, w+4, ...
     for (int t = blockIdx.x; t < count; t += gridDim.x) {
-      const float* h = a.H + ((int64_t)t * (K + 1) + K) * imax + 8 * l;
+      const int b = start + t;
+      const float* h = a.H + ((int64_t)b * (K + 1) + K) * imax + 8 * l;
       float v[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
       if (l < NG * 8) {
         const float4 v0 = *reinterpret_cast<const float4*>(h);
@@ -523,7 +607,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
           }
         }
         sacc = wave_sum_rows(sacc);
-        if (l == 0) a.ax[(int64_t)t * 3 * a.rmax + 2 * a.rmax + q] = sacc;
+        if (l == 0) a.ax[(int64_t)b * 3 * a.rmax + 2 * a.rmax + q] = sacc;
       }
     }
   }
@@ -552,12 +636,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 }
 
 // y[b] = sum_k w_k y_k + y_shared + down LoRA, in a fixed order (no atomics),
-// rounded to fp16. Grid (B, ceil(d/256)).
+// rounded to fp16. Grid (B, ceil(d/256)); thread j reads its down-LoRA row
+// as 16-byte words.
 __global__ __launch_bounds__(256) void k_mb_combine(MbArgs a) {
   __shared__ int ok[8];
+  __shared__ float axd[kMaxR];
   const Dims& dm = a.dm;
   const int K = dm.K, d = dm.d, b = blockIdx.x;
   if (threadIdx.x < K) ok[threadIdx.x] = resolve_entry(a.pool, dm.E, a.idx[b * K + threadIdx.x]) >= 0;
+  const bool lora = a.sh.present && a.sh.bd;
+  if (lora && threadIdx.x < dm.r)
+    axd[threadIdx.x] = a.ax[(int64_t)b * 3 * a.rmax + 2 * a.rmax + threadIdx.x];
   __syncthreads();
   const int j = blockIdx.y * blockDim.x + threadIdx.x;
   if (j >= d) return;
@@ -569,10 +658,18 @@ __global__ __launch_bounds__(256) void k_mb_combine(MbArgs a) {
   }
   if (a.sh.present) {
     acc += a.Y[((int64_t)b * (K + 1) + K) * d + j];
-    if (a.sh.bd) {
-      const float* axb = a.ax + (int64_t)b * 3 * a.rmax + 2 * a.rmax;
+    if (lora) {
+      const uint16_t* brow = a.sh.bd + (int64_t)j * dm.r;
       float ls = 0.0f;
-      for (int q = 0; q < dm.r; ++q) ls = fmaf(h2f(ldg(a.sh.bd + (int64_t)j * dm.r + q)), axb[q], ls);
+      for (int q = 0; q < dm.r; q += 8) {
+        const uint4 v = ldg(reinterpret_cast<const uint4*>(brow + q));
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const f16x2 h = as_h2(word(v, p));
+          ls = fmaf((float)h.x, axd[q + 2 * p], ls);
+          ls = fmaf((float)h.y, axd[q + 2 * p + 1], ls);
+        }
+      }
       acc += c * ls;
     }
   }
@@ -597,7 +694,7 @@ void launch_gate_up_ng(const MbArgs& a, dim3 grid, hipStream_t st) {
 
 template <int NG>
 void launch_down_ng(const MbArgs& a, dim3 grid, hipStream_t st) {
-  const size_t lds = (size_t)a.B * 2 * (NG * 64 + kDnPad) * sizeof(uint16_t);
+  const size_t lds = (size_t)(a.B < kCols ? a.B : kCols) * 2 * (NG * 64 + kDnPad) * sizeof(uint16_t);
   hipLaunchKernelGGL(k_mb_down<NG>, grid, dim3(256), lds, st, a);
 }
 
@@ -606,7 +703,7 @@ void launch_down_ng(const MbArgs& a, dim3 grid, hipStream_t st) {
 hipError_t launch_batched(const Dims& dm, const Pool& pool, const SharedW& sh, const uint16_t* x,
                           const int32_t* idx, const float* w, int B, uint16_t* y,
                           const Scratch& s, hipStream_t st) {
-  if (B < 1 || B > kCols || !batched_supported(dm)) return hipErrorInvalidValue;
+  if (B < 1 || !batched_supported(dm)) return hipErrorInvalidValue;
   MbArgs a;
   a.dm = dm;
   a.pool = pool;
@@ -618,14 +715,17 @@ hipError_t launch_batched(const Dims& dm, const Pool& pool, const SharedW& sh, c
   a.idx = idx;
   a.w = w;
   a.ax = s.ax;
+  a.axp = s.axp;
   a.rmax = dm.r > 1 ? dm.r : 1;
+  a.n_sl = 1;  // largest slice count <= kLoraSlices with whole 16-input MFMA steps per wave
+  while (a.n_sl < kLoraSlices && (dm.d / 64) % (2 * a.n_sl) == 0) a.n_sl *= 2;
   a.H = s.gu;
   a.Y = s.yk;
   a.y = y;
   a.flags = s.flags;
-  const int ny = B * dm.K + 1;  // union members + the shared expert
+  const int ny = batched_max_tiles(B, dm.K, dm.E);  // tiles past n_tiles exit at once
   const int imax = dm.I > dm.Is ? dm.I : dm.Is;
-  const int lora_blocks = sh.present && sh.ag ? B * ((2 * dm.r + 3) / 4) : 0;
+  const int lora_blocks = sh.present && sh.ag ? (B + kCols - 1) / kCols * a.n_sl : 0;
   hipLaunchKernelGGL(k_mb_prep, dim3(B + 1 + lora_blocks), dim3(256), 0, st, a);
   const dim3 gu_grid(imax / 32, ny);
   switch (dm.d / dm.G / 4) {

@@ -69,10 +69,16 @@ struct Scratch {
   int32_t* sink_idx;  // [B][K]     prediction with no consumer layer
   float* sink_w;      // [B][K]
   int32_t* flags; // [N_FLAGS]
-  // batched chunk (16..32 tokens)
-  int32_t* grp;   // [1 + 4 B K]    experts of the chunk and their token runs
+  // batched path (B >= 16 tokens)
+  int32_t* grp;   // [2 + 4 B K + 2 T] experts of the batch, their token runs and
+                  //                work tiles (T = batched_max_tiles)
+  float* axp;     // [kLoraSlices][B][2 rmax] shared gate/up LoRA A products
+                  //                over slices of the inputs
   float* yk;      // [B][K+1][d]    per-slot down outputs
 };
+
+// Input slices of the batched path's LoRA A products (summed in order later).
+constexpr int kLoraSlices = 8;
 
 // ---- launchers (kernels.hip) ------------------------------------------------
 // All return hipSuccess or the launch error; shapes are validated by callers.
@@ -112,10 +118,18 @@ hipError_t launch_prep(const Dims& dm, const uint16_t* h, const uint16_t* attn, 
                        float* hattn, uint16_t* xn, const int32_t* cidx, const float* cw,
                        int32_t* eidx, float* ew, hipStream_t st);
 
-// Batched chunk of 1..32 tokens through grouped int4 GEMMs on MFMA
-// (batched.hip): y[b] = fp16(sum_k w[b,k] E_idx(x[b]) + S(x[b])). The LoRA A
-// products of the shared gate/up must already be in s.ax.
+// Batch of B tokens through grouped int4 GEMMs on MFMA (batched.hip):
+// y[b] = fp16(sum_k w[b,k] E_idx(x[b]) + S(x[b])). Work is split into tiles of
+// up to 32 tokens of one expert (the union of the batch's experts, plus the
+// shared expert over all B tokens).
 bool batched_supported(const Dims& dm);
+// Upper bound on the work tiles of a batch: sum over members of
+// ceil(count/32) <= B*K/32 + members, members <= min(B*K, E), plus the
+// shared expert's ceil(B/32).
+inline int batched_max_tiles(int B, int K, int E) {
+  const int BK = B * K;
+  return (B + 31) / 32 + (BK < E ? BK : E) + (BK + 31) / 32;
+}
 hipError_t launch_batched(const Dims& dm, const Pool& pool, const SharedW& sh, const uint16_t* x,
                           const int32_t* idx, const float* w, int B, uint16_t* y,
                           const Scratch& s, hipStream_t st);

@@ -1,11 +1,22 @@
-"""GPU parity of the batched chunk (16..32 tokens per chunk, grouped int4
-GEMMs on MFMA) against the fp64 oracle.
+"""GPU parity of the batched path (B >= 16 tokens, grouped int4 GEMMs on
+MFMA) against the fp64 oracle.
 
-moe_int4_decode with B >= 16 groups the tokens by expert and reads each
-expert's weights once per chunk of up to 32 tokens. Every token's output is
-compared with the oracle's moe_decode for its own routing: 35B shapes with
-top-K in {2, 4, 8} and 8B shapes, full chunks of 32, a partial chunk and two
-chunks; two runs are bitwise equal; an out-of-range id is flagged.
+moe_int4_decode with B >= 16 groups the batch's B*K entries by expert in one
+launch and runs tiles of up to 32 of an expert's tokens, each reading the
+expert's weights once. Decode chunks: every token's output is compared with
+the oracle's moe_decode for its own routing, 35B shapes with top-K in
+{2, 4, 8} and 8B shapes, B = 32, a partial tile (20) and two tiles (40); two
+runs are bitwise equal; an out-of-range id is flagged.
+
+Prefill-sized batches (the whole-layer path): B = 16 (the smallest batched
+call) and B = 64 checked token by token;
+B = 256 (8B tier, the union covers almost every expert), a skewed batch whose
+tokens share a few hot experts (members of several ragged tiles each) and
+B = 3072 (the pages' ~3.1k-token prompt) and B = 8192 (the largest context)
+checked against the oracle on sampled tokens, and on every token by a property that holds at any size: a token's
+output does not depend on the other tokens of its batch (tile rows are
+independent and every sum runs in a fixed order), so the batch equals the same
+tokens run in chunks of 32, bit for bit.
 """
 
 import numpy as np
@@ -91,3 +102,60 @@ def test_batched_bad_id_is_flagged(api, pools):
     idx[5, 1] = dm["E"] + 3
     api.moe_int4_decode(ctx, dev_tree(pool), dev(x), dev(idx), dev(w), shared=dev_tree(sh))
     assert api.device_status(ctx) == api.E0_ERR_RANGE
+
+
+def _chunks(B, c=32):
+    """Chunk bounds of about c tokens, none below the batched path's 16."""
+    bounds = list(range(0, B, c)) + [B]
+    if len(bounds) > 2 and bounds[-1] - bounds[-2] < 16:
+        del bounds[-2]
+    return list(zip(bounds[:-1], bounds[1:]))
+
+
+def _hot_tokens(rng, dm, B, n_hot):
+    """Tokens whose sets are drawn from n_hot hot experts only."""
+    x, _, w = _tokens(rng, dm, B)
+    hot = rng.choice(dm["E"], size=n_hot, replace=False)
+    idx = np.stack([rng.choice(hot, size=dm["K"], replace=False) for _ in range(B)])
+    return x, idx.astype(np.int32), w
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("tier,K,B,hot,n_check", [("35b", 4, 16, 0, 16), ("35b", 4, 64, 0, 64),
+                                                  ("8b", 8, 256, 0, 24),
+                                                  ("35b", 4, 200, 6, 24),
+                                                  ("35b", 8, 3072, 0, 16),
+                                                  ("35b", 8, 8192, 0, 8)])
+def test_batched_prefill_parity(api, orc, pools, tier, K, B, hot, n_check):
+    import torch
+    dm = synth.dims(tier, K=K)
+    pool, sh = pools[tier]
+    announce("batched prefill", tier, f"K={K} B={B} hot={hot}")
+    ctx = api.Context(dm, max_tokens=B)
+    dpool, dsh = dev_tree(pool), dev_tree(sh)
+    rng = np.random.default_rng(64 + K + B)
+    x, idx, w = _hot_tokens(rng, dm, B, hot) if hot else _tokens(rng, dm, B)
+    dx, didx, dw = dev(x), dev(idx), dev(w)
+    y = api.moe_int4_decode(ctx, dpool, dx, didx, dw, shared=dsh)
+    torch.cuda.synchronize()
+    assert api.device_status(ctx) == 0
+    # every token: the batch equals the same tokens in chunks of ~32
+    yb = host(y).view(np.uint16)
+    for c0, c1 in _chunks(B):
+        yc = api.moe_int4_decode(ctx, dpool, dx[c0:c1].contiguous(), didx[c0:c1].contiguous(),
+                                 dw[c0:c1].contiguous(), shared=dsh)
+        assert np.array_equal(host(yc).view(np.uint16), yb[c0:c1]), \
+            f"tokens {c0}..{c1} differ between the batch and a chunk"
+    assert api.device_status(ctx) == 0
+    # sampled tokens (always the first and the last) against the oracle
+    check = (np.arange(B) if n_check >= B else
+             np.unique(np.concatenate([[0, B - 1], rng.choice(B, size=n_check, replace=False)])))
+    yg = f16_to_f64(y)
+    worst = 0.0
+    for b in check:
+        ref = orc.moe_decode(dm, pool, sh, x[b], idx[b], w[b].astype(np.float64))
+        assert_out_close(yg[b], ref, f"{tier} K={K} B={B} token {b}")
+        worst = max(worst, out_err(yg[b], ref))
+    counts = np.bincount(idx.ravel(), minlength=dm["E"])
+    print(f"{tier} K={K} B={B}: worst error ratio {worst:.3f} over {len(check)} tokens, "
+          f"union {np.count_nonzero(counts)} experts, largest member {counts.max()} tokens")
