@@ -205,7 +205,9 @@ def run_chunk(args):
             ms = e0.elapsed_time(e1) / args.steps
             counts = np.bincount(idx.ravel(), minlength=E)
             union = int(np.count_nonzero(counts))
-            tiles = int(np.sum((counts + 31) // 32)) + (B + 31) // 32
+            # the library's prefill kernels (B*K >= 16 E) take 64-token tiles
+            tile = 64 if B * K >= 16 * E else 32
+            tiles = int(np.sum((counts + tile - 1) // tile)) + (B + tile - 1) // tile
             nbytes = union * expert + expert + lora
             flops = 2 * B * (K + 1) * 3 * dm0["I"] * dm0["d"]
             lines.append({"B": B, "K": K, "union_experts": union, "tiles": tiles,

@@ -74,6 +74,7 @@ struct MbArgs {
   const uint16_t* x;     // [B][d] input, natural order
   uint16_t* xp;          // [B][d] pair-permuted copy
   int32_t* grp;
+  int tile;              // tokens per work tile: 32 (chunk kernels) or 64 (prefill kernels)
   const int32_t* idx;    // [B][K]
   const float* w;        // [B][K]
   float* ax;             // [B][3*rmax] LoRA A products (down in slot 2)
@@ -134,7 +135,7 @@ __device__ void group_entries(const MbArgs& a) {
   // thread t owns experts 2t and 2t+1 (E <= 512): offsets, union positions
   // and tile positions by prefix sums
   const int c0 = cnt[2 * t], c1 = cnt[2 * t + 1];
-  const int n0 = (c0 + kCols - 1) / kCols, n1 = (c1 + kCols - 1) / kCols;
+  const int n0 = (c0 + a.tile - 1) / a.tile, n1 = (c1 + a.tile - 1) / a.tile;
   int ps = wave_incl_scan(c0 + c1);
   int pu = wave_incl_scan((c0 > 0) + (c1 > 0));
   int pt = wave_incl_scan(n0 + n1);
@@ -150,7 +151,7 @@ __device__ void group_entries(const MbArgs& a) {
     pu += wtot[1][v];
     pt += wtot[2][v];
   }
-  const int n_sh = a.sh.present ? (a.B + kCols - 1) / kCols : 0;
+  const int n_sh = a.sh.present ? (a.B + a.tile - 1) / a.tile : 0;
   const int off0 = ps - c0 - c1;
   int u = pu - (c0 > 0) - (c1 > 0);
   int tp = n_sh + pt - n0 - n1;
@@ -186,11 +187,16 @@ __device__ void group_entries(const MbArgs& a) {
   cur[2 * t] = off0;
   cur[2 * t + 1] = off0 + c0;
   const uint64_t below = (1ull << (t & 63)) - 1;
-  int e_next = t < BK ? a.idx[t] : -1;
+  // entries of the next four passes, loaded ahead
+  int e1 = t < BK ? a.idx[t] : -1, e2 = t + nt < BK ? a.idx[t + nt] : -1;
+  int e3 = t + 2 * nt < BK ? a.idx[t + 2 * nt] : -1, e4 = t + 3 * nt < BK ? a.idx[t + 3 * nt] : -1;
   for (int p0 = 0, tag = 1; p0 < BK; p0 += nt, ++tag) {
     const int i = p0 + t;
-    const int e = i < BK && e_next >= 0 && e_next < E ? e_next : -1;
-    e_next = i + nt < BK ? a.idx[i + nt] : -1;  // next pass, loaded early
+    const int e = i < BK && e1 >= 0 && e1 < E ? e1 : -1;
+    e1 = e2;
+    e2 = e3;
+    e3 = e4;
+    e4 = i + 4 * nt < BK ? a.idx[i + 4 * nt] : -1;
     uint64_t same = __ballot(e >= 0);
 #pragma unroll
     for (int bit = 0; bit < 9; ++bit) {
@@ -278,14 +284,15 @@ __device__ void prep_lora(const MbArgs& a, int lb) {
   }
 }
 
-// Grid: B token blocks, one grouping block, then ceil(B/32) x n_sl LoRA
-// blocks when the shared expert has LoRA.
+// Grid: the grouping block first (the longest, so it starts at once), B
+// token blocks, then ceil(B/32) x n_sl LoRA blocks when the shared expert has
+// LoRA.
 __global__ __launch_bounds__(256) void k_mb_prep(MbArgs a) {
   const int bx = blockIdx.x;
-  if (bx < a.B)
-    prep_token(a, bx);
-  else if (bx == a.B)
+  if (bx == 0)
     group_entries(a);
+  else if (bx <= a.B)
+    prep_token(a, bx - 1);
   else
     prep_lora(a, bx - a.B - 1);
 }
@@ -304,6 +311,11 @@ __device__ __forceinline__ h8 q4_to_h8(uint32_t w) {
 __device__ __forceinline__ uint32_t word(const uint4& v, int j) {
   return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
 }
+
+// Pins an accumulator in registers at this point: without it the compiler
+// sinks the per-group scale-adds into the conditional stores at the end and
+// keeps every group's partial alive until then.
+__device__ __forceinline__ void keep(f32x16& v) { asm volatile("" : "+v"(v)); }
 
 // MFMA 32x32x16 layout with the chunk's tokens as operand A and 32 weight rows
 // as operand B: lane l supplies token row l%32 and weight row l%32 over the
@@ -334,6 +346,7 @@ __device__ __forceinline__ f32x16 gu_mma(const uint4 (&wv)[NG], const float (&sv
       c = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(xv[i][j]), q4_to_h8(word(wv[i], j)), c,
                                                 0, 0, 0);
     scale_add<NR>(acc, c, sv[i]);
+    keep(acc);
   }
   return acc;
 }
@@ -357,6 +370,7 @@ __device__ __forceinline__ f32x16 dn_mma(const uint4 (&wq)[NG], const float (&sc
       c = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(lv), w8, c, 0, 0, 0);
     }
     scale_add<NR>(acc, c, sc[i]);
+    keep(acc);
   }
   return acc;
 }
@@ -378,7 +392,7 @@ __device__ __forceinline__ void entry_of(const MbArgs& a, bool shared, int start
 }
 
 // Work tile y: the shared expert (dispatched first, it has the most tokens)
-// or union member u, with its first entry and token count (<= 32).
+// or union member u, with its first entry and token count (<= a.tile).
 __device__ __forceinline__ bool tile_of(const MbArgs& a, int y, bool& shared, int& u, int& start,
                                         int& count) {
   const Groups g = groups(a.grp, a.B * a.dm.K);
@@ -386,15 +400,25 @@ __device__ __forceinline__ bool tile_of(const MbArgs& a, int y, bool& shared, in
   const int mem = g.tiles[2 * y], tile = g.tiles[2 * y + 1];
   shared = mem < 0;
   u = mem;
-  const int first = kCols * tile;
+  const int first = a.tile * tile;
   if (shared) {
     start = first;
-    count = min(kCols, a.B - first);
+    count = min(a.tile, a.B - first);
   } else {
     start = g.ustart[mem] + first;
-    count = min(kCols, g.ucount[mem] - first);
+    count = min(a.tile, g.ucount[mem] - first);
   }
   return true;
+}
+
+// Work item of this workgroup in the (row block, tile) grid. The natural
+// order is kept: renumbering so that one XCD takes all row blocks of a tile
+// (sharing its activations in that XCD's L2) measured slower, since the
+// shared expert's full tiles then crowd onto one XCD.
+__device__ __forceinline__ bool tile_block(const MbArgs& a, int& bx, bool& shared, int& u,
+                                           int& start, int& count) {
+  bx = blockIdx.x;
+  return tile_of(a, blockIdx.y, shared, u, start, count);
 }
 
 // Gate/up of one union member (or the shared expert) for 32 rows. Eight
@@ -411,8 +435,9 @@ __global__ __launch_bounds__(512) void k_mb_gate_up(MbArgs a) {
   const int imax = dm.I > dm.Is ? dm.I : dm.Is;
   bool shared;
   int u, start, count;
-  if (!tile_of(a, blockIdx.y, shared, u, start, count)) return;
-  const int m0 = blockIdx.x * 32;
+  int bx;
+  if (!tile_block(a, bx, shared, u, start, count)) return;
+  const int m0 = bx * 32;
   if (m0 >= (shared ? dm.Is : dm.I)) return;
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, n = l & 31, kh = l >> 5;
   const int mat = wave >> 2, quarter = wave & 3;  // 0 gate, 1 up
@@ -520,7 +545,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int imax = dm.I > dm.Is ? dm.I : dm.Is;
   bool shared;
   int u, start, count;
-  if (!tile_of(a, blockIdx.y, shared, u, start, count)) return;
+  int bx;
+  if (!tile_block(a, bx, shared, u, start, count)) return;
   const uint32_t* dq;
   const uint16_t* ds;
   if (shared) {
@@ -534,7 +560,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     ds = (const uint16_t*)entry_ptr(a.pool.down.s, ent, a.pool.stride_s);
   }
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, n = l & 31, kh = l >> 5;
-  const int m0 = (blockIdx.x * 4 + wave) * 32;
+  const int m0 = (bx * 4 + wave) * 32;
   const bool rows_ok = m0 < d;
   uint4 wq[NG];
   float sc[NG];
@@ -583,9 +609,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     if (l == 0) hx[t] = ldexpf(1.0f, e);
   }
   if (shared && a.sh.ad) {
-    // A_down . h_shared[t] for tokens t = blockIdx.x, blockIdx.x + gridDim.x, ...;
+    // A_down . h_shared[t] for tokens t = bx, bx + gridDim.x, ...;
     // wave w takes ranks q = w, w+4, ...
-    for (int t = blockIdx.x; t < count; t += gridDim.x) {
+    for (int t = bx; t < count; t += gridDim.x) {
       const int b = start + t;
       const float* h = a.H + ((int64_t)b * (K + 1) + K) * imax + 8 * l;
       float v[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
@@ -636,8 +662,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 }
 
 // y[b] = sum_k w_k y_k + y_shared + down LoRA, in a fixed order (no atomics),
-// rounded to fp16. Grid (B, ceil(d/256)); thread j reads its down-LoRA row
-// as 16-byte words.
+// rounded to fp16. Grid (B, ceil(d/1024)); thread j takes columns 4j..4j+3
+// (16-byte loads) and reads their down-LoRA rows as 16-byte words.
 __global__ __launch_bounds__(256) void k_mb_combine(MbArgs a) {
   __shared__ int ok[8];
   __shared__ float axd[kMaxR];
@@ -648,32 +674,397 @@ __global__ __launch_bounds__(256) void k_mb_combine(MbArgs a) {
   if (lora && threadIdx.x < dm.r)
     axd[threadIdx.x] = a.ax[(int64_t)b * 3 * a.rmax + 2 * a.rmax + threadIdx.x];
   __syncthreads();
-  const int j = blockIdx.y * blockDim.x + threadIdx.x;
-  if (j >= d) return;
+  const int j0 = 4 * (blockIdx.y * blockDim.x + threadIdx.x);
+  if (j0 >= d) return;  // d % 128 == 0: a thread's four columns are all in range
   const float c = dm.lora_scale;
-  float acc = 0.0f;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int k = 0; k < K; ++k) {
     if (!ok[k]) continue;
-    acc += a.w[b * K + k] * a.Y[((int64_t)b * (K + 1) + k) * d + j];
+    const float wk = a.w[b * K + k];
+    const float4 v = *reinterpret_cast<const float4*>(a.Y + ((int64_t)b * (K + 1) + k) * d + j0);
+    acc[0] += wk * v.x;
+    acc[1] += wk * v.y;
+    acc[2] += wk * v.z;
+    acc[3] += wk * v.w;
   }
   if (a.sh.present) {
-    acc += a.Y[((int64_t)b * (K + 1) + K) * d + j];
+    const float4 v = *reinterpret_cast<const float4*>(a.Y + ((int64_t)b * (K + 1) + K) * d + j0);
+    acc[0] += v.x;
+    acc[1] += v.y;
+    acc[2] += v.z;
+    acc[3] += v.w;
     if (lora) {
-      const uint16_t* brow = a.sh.bd + (int64_t)j * dm.r;
-      float ls = 0.0f;
-      for (int q = 0; q < dm.r; q += 8) {
-        const uint4 v = ldg(reinterpret_cast<const uint4*>(brow + q));
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const f16x2 h = as_h2(word(v, p));
-          ls = fmaf((float)h.x, axd[q + 2 * p], ls);
-          ls = fmaf((float)h.y, axd[q + 2 * p + 1], ls);
+      for (int jj = 0; jj < 4; ++jj) {
+        const uint16_t* brow = a.sh.bd + (int64_t)(j0 + jj) * dm.r;
+        float ls = 0.0f;
+        for (int q = 0; q < dm.r; q += 8) {
+          const uint4 bv = ldg(reinterpret_cast<const uint4*>(brow + q));
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const f16x2 h = as_h2(word(bv, p));
+            ls = fmaf((float)h.x, axd[q + 2 * p], ls);
+            ls = fmaf((float)h.y, axd[q + 2 * p + 1], ls);
+          }
         }
+        acc[jj] += c * ls;
       }
-      acc += c * ls;
     }
   }
-  a.y[(int64_t)b * d + j] = f2h(acc);
+  const uint32_t lo = (uint32_t)f2h(acc[0]) | ((uint32_t)f2h(acc[1]) << 16);
+  const uint32_t hi = (uint32_t)f2h(acc[2]) | ((uint32_t)f2h(acc[3]) << 16);
+  *reinterpret_cast<uint2*>(a.y + (int64_t)b * d + j0) = make_uint2(lo, hi);
+}
+
+// ---------------------------------------------------------------------------
+// Prefill-sized batches: 64-token tiles through GEMM-shaped kernels. A
+// workgroup keeps its tile's activations in LDS and streams the weight rows
+// it owns past them, so each dequantised weight word feeds the tile's two
+// 32-token MFMA column blocks.
+
+constexpr int kPfTok = 64;        // tokens per tile
+constexpr int kPfSG = 4;          // 64-input groups per LDS stage (gate/up)
+// Batches with at least this many entries per expert on average (B*K >= 16 E)
+// take the prefill kernels; measured on the 35B tier (K = 4), the chunk
+// kernels are faster up to about 900 tokens.
+constexpr int kPrefillPerExpert = 16;
+
+// LDS slot of token t's 16-byte chunk c. Rows of one chunk are padded by
+// one slot, so one token's chunks (written by a wave) spread over the banks
+// as one chunk of 32 tokens (an MFMA operand read) does, and a lane's read
+// address is its own base plus a constant offset per (group, step).
+constexpr int kPfRow = kPfTok + 1;
+__device__ __forceinline__ int pf_slot(int c, int t) { return c * kPfRow + t; }
+
+// Gate/up of one tile: eight waves, each the same 32 rows of I of both the
+// gate and the up matrix (256 rows per workgroup) over all d inputs, for the
+// tile's 64 tokens (four accumulators), so SwiGLU is formed in registers.
+// Activations are staged through LDS kPfSG groups at a time (double-buffered,
+// one barrier per stage); a wave reloads each weight word for the next stage
+// as soon as it has dequantised it. Each 64-input group is accumulated on
+// its own and scaled in fp32 by the row's group scale, as in the chunk
+// kernels. Two waves per SIMD overlap one wave's loads with the other's
+// MFMAs.
+constexpr int kPfGuRows = 256;  // rows of I per gate/up workgroup
+
+// SiLU through the hardware exp2 and reciprocal: relative error about 1e-6,
+// far below the fp16 rounding of the layer output.
+__device__ __forceinline__ float silu_fast(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
+__global__ __launch_bounds__(512) void k_pf_gate_up(MbArgs a) {
+  __shared__ __align__(16) uint4 xs[2][kPfSG * 8 * kPfRow];
+  __shared__ float axs[kPfTok][2][kMaxR];
+  __shared__ int tokb[kPfTok], tokk[kPfTok];
+  const Dims& dm = a.dm;
+  const int K = dm.K, d = dm.d;
+  const int imax = dm.I > dm.Is ? dm.I : dm.Is;
+  bool shared;
+  int u, start, count;
+  int bx;
+  if (!tile_block(a, bx, shared, u, start, count)) return;
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, n = l & 31, kh = l >> 5;
+  const int row = bx * kPfGuRows + wave * 32 + n;  // I % 256 == 0
+  const bool lora = shared && a.sh.ag;
+  const uint32_t *gq, *uq;
+  const uint16_t *gs, *us;
+  if (shared) {
+    gq = a.sh.gate.q; uq = a.sh.up.q; gs = a.sh.gate.s; us = a.sh.up.s;
+  } else {
+    const Groups gv = groups(a.grp, a.B * K);
+    const int64_t ent = resolve_entry(a.pool, dm.E, gv.uexp[u]);
+    if (ent < 0) {
+      if (threadIdx.x == 0) atomicOr(&a.flags[FLAG_RANGE], 1);
+      return;
+    }
+    gq = (const uint32_t*)entry_ptr(a.pool.gate.q, ent, a.pool.stride_q);
+    uq = (const uint32_t*)entry_ptr(a.pool.up.q, ent, a.pool.stride_q);
+    gs = (const uint16_t*)entry_ptr(a.pool.gate.s, ent, a.pool.stride_s);
+    us = (const uint16_t*)entry_ptr(a.pool.up.s, ent, a.pool.stride_s);
+  }
+  if (threadIdx.x < kPfTok) {
+    // rows past count repeat the last token (their outputs are never stored)
+    int b, k;
+    entry_of(a, shared, start, threadIdx.x < count ? threadIdx.x : count - 1, b, k);
+    tokb[threadIdx.x] = b;
+    tokk[threadIdx.x] = k;
+  }
+  if (lora) {  // LoRA A products of this tile's tokens: the slices in order
+    for (int i = threadIdx.x; i < count * 2 * dm.r; i += blockDim.x) {
+      const int tt = i / (2 * dm.r), j = i % (2 * dm.r);
+      const float* p = a.axp + (int64_t)(start + tt) * 2 * a.rmax + j;
+      float v = 0.0f;
+      for (int sl = 0; sl < a.n_sl; ++sl) v += p[(int64_t)sl * a.B * 2 * a.rmax];
+      axs[tt][j / dm.r][j % dm.r] = v;
+    }
+  }
+  __syncthreads();
+  const int wpr = d / 8, ngs = d / 64, ns = d / (64 * kPfSG);
+  const uint32_t* gro = gq + (int64_t)row * wpr + 4 * kh;
+  const uint32_t* uro = uq + (int64_t)row * wpr + 4 * kh;
+  const uint16_t* gsr = gs + (int64_t)row * ngs;
+  const uint16_t* usr = us + (int64_t)row * ngs;
+  constexpr int kXr = kPfSG * 8 * kPfTok / 512;  // 16-byte chunks per thread per stage
+  uint4 xr[kXr];
+  auto load_x = [&](int st) {
+#pragma unroll
+    for (int it = 0; it < kXr; ++it) {
+      const int flat = it * 512 + threadIdx.x, tt = flat / (kPfSG * 8), c = flat % (kPfSG * 8);
+      xr[it] = ldg(reinterpret_cast<const uint4*>(a.xp + (int64_t)tokb[tt] * d +
+                                                  64 * kPfSG * st + 8 * c));
+    }
+  };
+  auto store_x = [&](int buf) {
+#pragma unroll
+    for (int it = 0; it < kXr; ++it) {
+      const int flat = it * 512 + threadIdx.x, tt = flat / (kPfSG * 8), c = flat % (kPfSG * 8);
+      xs[buf][pf_slot(c, tt)] = xr[it];
+    }
+  };
+  uint4 wg[kPfSG], wu[kPfSG];
+  float sg[kPfSG], su[kPfSG];
+#pragma unroll
+  for (int i = 0; i < kPfSG; ++i) {
+    wg[i] = ldg(reinterpret_cast<const uint4*>(gro + 8 * i));
+    wu[i] = ldg(reinterpret_cast<const uint4*>(uro + 8 * i));
+    sg[i] = h2f(ldg(gsr + i));
+    su[i] = h2f(ldg(usr + i));
+  }
+  load_x(0);
+  store_x(0);
+  __syncthreads();
+  f32x16 ag0 = {}, ag1 = {}, au0 = {}, au1 = {};
+  for (int st = 0; st < ns; ++st) {
+    const bool more = st + 1 < ns;
+    if (more) load_x(st + 1);
+    const uint4* xb = xs[st & 1];
+#pragma unroll
+    for (int g = 0; g < kPfSG; ++g) {
+      __builtin_amdgcn_sched_barrier(0);  // one group's operands live at a time
+      const uint4 cwg = wg[g], cwu = wu[g];
+      const float csg = sg[g], csu = su[g];
+      if (more) {  // the same group of the next stage, into the freed registers
+        const int gn = kPfSG * (st + 1) + g;
+        wg[g] = ldg(reinterpret_cast<const uint4*>(gro + 8 * gn));
+        wu[g] = ldg(reinterpret_cast<const uint4*>(uro + 8 * gn));
+        sg[g] = h2f(ldg(gsr + gn));
+        su[g] = h2f(ldg(usr + gn));
+      }
+      f32x16 cg0 = {}, cg1 = {}, cu0 = {}, cu1 = {};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = 8 * g + 4 * kh + j;
+        const h8 x0 = as_h8(xb[pf_slot(c, n)]), x1 = as_h8(xb[pf_slot(c, 32 + n)]);
+        const h8 w_g = q4_to_h8(word(cwg, j)), w_u = q4_to_h8(word(cwu, j));
+        cg0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(x0, w_g, cg0, 0, 0, 0);
+        cg1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(x1, w_g, cg1, 0, 0, 0);
+        cu0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(x0, w_u, cu0, 0, 0, 0);
+        cu1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(x1, w_u, cu1, 0, 0, 0);
+      }
+      scale_add<16>(ag0, cg0, csg);
+      scale_add<16>(ag1, cg1, csg);
+      scale_add<16>(au0, cu0, csu);
+      scale_add<16>(au1, cu1, csu);
+      keep(ag0);
+      keep(ag1);
+      keep(au0);
+      keep(au1);
+    }
+    if (more) store_x((st + 1) & 1);
+    __syncthreads();
+  }
+  // epilogue: shared-expert LoRA B terms, SwiGLU, fp32 store
+  const float cl = dm.lora_scale;
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int t = 32 * tb + tok_row(r, kh);
+      if (t >= count) continue;
+      float gg = tb ? ag1[r] : ag0[r];
+      float uu = tb ? au1[r] : au0[r];
+      if (lora) {
+        float lg = 0.0f, lu = 0.0f;
+        for (int q = 0; q < dm.r; q += 8) {
+          const uint4 bgv = ldg(reinterpret_cast<const uint4*>(a.sh.bg + (int64_t)row * dm.r + q));
+          const uint4 buv = ldg(reinterpret_cast<const uint4*>(a.sh.bu + (int64_t)row * dm.r + q));
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const f16x2 g2 = as_h2(word(bgv, p)), u2 = as_h2(word(buv, p));
+            lg = fmaf((float)g2.x, axs[t][0][q + 2 * p], lg);
+            lg = fmaf((float)g2.y, axs[t][0][q + 2 * p + 1], lg);
+            lu = fmaf((float)u2.x, axs[t][1][q + 2 * p], lu);
+            lu = fmaf((float)u2.y, axs[t][1][q + 2 * p + 1], lu);
+          }
+        }
+        gg = fmaf(cl, lg, gg);
+        uu = fmaf(cl, lu, uu);
+      }
+      a.H[((int64_t)tokb[t] * (K + 1) + tokk[t]) * imax + row] = silu_fast(gg) * uu;
+    }
+  }
+}
+
+// Down projection of one tile: eight waves, 32 output rows each (256 per
+// workgroup) over all NG input groups. The tile's fp32 SwiGLU outputs
+// (64 tokens x NG*64) are staged once in LDS as fp16 hi + lo under a
+// power-of-two scale per token; each dequantised weight word feeds four
+// MFMAs (hi and lo of both 32-token blocks). Workgroups of the shared
+// expert's tiles also form A_down . h for the down LoRA.
+template <int NG>
+__global__ __launch_bounds__(512) void k_pf_down(MbArgs a) {
+  extern __shared__ __align__(16) uint4 hsp[];  // [NG*8 chunks][hi, lo] x kPfTok slots
+  __shared__ float hx[kPfTok];
+  __shared__ int tokb[kPfTok], tokk[kPfTok];
+  constexpr int nin = NG * 64, nch = NG * 8;
+  const Dims& dm = a.dm;
+  const int K = dm.K, d = dm.d;
+  const int imax = dm.I > dm.Is ? dm.I : dm.Is;
+  bool shared;
+  int u, start, count;
+  int bx;
+  if (!tile_block(a, bx, shared, u, start, count)) return;
+  const uint32_t* dq;
+  const uint16_t* ds;
+  if (shared) {
+    dq = a.sh.down.q;
+    ds = a.sh.down.s;
+  } else {
+    const Groups gv = groups(a.grp, a.B * K);
+    const int64_t ent = resolve_entry(a.pool, dm.E, gv.uexp[u]);
+    if (ent < 0) return;  // flagged by the gate/up step
+    dq = (const uint32_t*)entry_ptr(a.pool.down.q, ent, a.pool.stride_q);
+    ds = (const uint16_t*)entry_ptr(a.pool.down.s, ent, a.pool.stride_s);
+  }
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, n = l & 31, kh = l >> 5;
+  const int row = bx * 256 + wave * 32 + n;  // d % 256 == 0
+  uint4 wq[NG];
+  float sc[NG];
+  {
+    const uint32_t* qrow = dq + (int64_t)row * (nin / 8) + 4 * kh;
+    const uint16_t* srow = ds + (int64_t)row * NG;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) wq[i] = ldg(reinterpret_cast<const uint4*>(qrow + 8 * i));
+#pragma unroll
+    for (int i = 0; i < NG; ++i) sc[i] = h2f(ldg(srow + i));
+  }
+  if (threadIdx.x < kPfTok) {
+    int b = 0, k = 0;
+    if ((int)threadIdx.x < count) entry_of(a, shared, start, threadIdx.x, b, k);
+    tokb[threadIdx.x] = b;
+    tokk[threadIdx.x] = k;
+  }
+  __syncthreads();
+  // stage: wave w takes tokens w, w+8, ...; lane c the 8 values of chunk c.
+  // All of the wave's loads are issued before the first token is split.
+  constexpr int kTpw = kPfTok / 8, kCpl = (nch + 63) / 64;
+  float4 hv[kTpw][kCpl][2];
+#pragma unroll
+  for (int i = 0; i < kTpw; ++i) {
+    const int t = wave + 8 * i;
+    const float* h = a.H + ((int64_t)tokb[t] * (K + 1) + tokk[t]) * imax;
+#pragma unroll
+    for (int cc = 0; cc < kCpl; ++cc) {
+      const int c = l + 64 * cc;
+      hv[i][cc][0] = hv[i][cc][1] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (t < count && c < nch) {  // rows past count: zeros (never stored)
+        hv[i][cc][0] = *reinterpret_cast<const float4*>(h + 8 * c);
+        hv[i][cc][1] = *reinterpret_cast<const float4*>(h + 8 * c + 4);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kTpw; ++i) {
+    const int t = wave + 8 * i;
+    float v[kCpl][8];
+    float m = 0.0f;
+#pragma unroll
+    for (int cc = 0; cc < kCpl; ++cc) {
+      const float4 v0 = hv[i][cc][0], v1 = hv[i][cc][1];
+      v[cc][0] = v0.x; v[cc][1] = v0.y; v[cc][2] = v0.z; v[cc][3] = v0.w;
+      v[cc][4] = v1.x; v[cc][5] = v1.y; v[cc][6] = v1.z; v[cc][7] = v1.w;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(v[cc][q]));
+    }
+    const int e = hilo_exponent(wave_max_rows(m));
+    const float inv = ldexpf(1.0f, -e);
+#pragma unroll
+    for (int cc = 0; cc < kCpl; ++cc) {
+      const int c = l + 64 * cc;
+      if (c >= nch) continue;
+      uint16_t hi[8], lo[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        f16 th, tl;
+        split_hilo(v[cc][q], inv, th, tl);
+        hi[q] = __builtin_bit_cast(uint16_t, th);
+        lo[q] = __builtin_bit_cast(uint16_t, tl);
+      }
+      // pair-permuted order [0 4 1 5 2 6 3 7]
+      hsp[pf_slot(2 * c, t)] =
+          make_uint4(hi[0] | ((uint32_t)hi[4] << 16), hi[1] | ((uint32_t)hi[5] << 16),
+                     hi[2] | ((uint32_t)hi[6] << 16), hi[3] | ((uint32_t)hi[7] << 16));
+      hsp[pf_slot(2 * c + 1, t)] =
+          make_uint4(lo[0] | ((uint32_t)lo[4] << 16), lo[1] | ((uint32_t)lo[5] << 16),
+                     lo[2] | ((uint32_t)lo[6] << 16), lo[3] | ((uint32_t)lo[7] << 16));
+    }
+    if (l == 0) hx[t] = t < count ? ldexpf(1.0f, e) : 0.0f;
+  }
+  if (shared && a.sh.ad) {
+    // A_down . h_shared[t] for tokens t = bx, bx + gridDim.x, ...;
+    // wave w takes ranks q = w, w+8, ...
+    for (int t = bx; t < count; t += gridDim.x) {
+      const int b = start + t;
+      const float* h = a.H + ((int64_t)b * (K + 1) + K) * imax;
+      for (int q = wave; q < dm.r; q += 8) {
+        float sacc = 0.0f;
+        for (int c = l; c < nch; c += 64) {
+          const float4 v0 = *reinterpret_cast<const float4*>(h + 8 * c);
+          const float4 v1 = *reinterpret_cast<const float4*>(h + 8 * c + 4);
+          const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+          const uint4 av = ldg(reinterpret_cast<const uint4*>(a.sh.ad + (int64_t)q * nin + 8 * c));
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const f16x2 ah = as_h2(word(av, p));
+            sacc = fmaf((float)ah.x, v[2 * p], sacc);
+            sacc = fmaf((float)ah.y, v[2 * p + 1], sacc);
+          }
+        }
+        sacc = wave_sum_rows(sacc);
+        if (l == 0) a.ax[(int64_t)b * 3 * a.rmax + 2 * a.rmax + q] = sacc;
+      }
+    }
+  }
+  __syncthreads();
+  f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    __builtin_amdgcn_sched_barrier(0);  // one group's operands live at a time
+    f32x16 c0 = {}, c1 = {};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = 8 * g + 4 * kh + j;
+      const h8 w8 = q4_to_h8(word(wq[g], j));
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(hsp[pf_slot(2 * c, n)]), w8, c0, 0, 0, 0);
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(hsp[pf_slot(2 * c + 1, n)]), w8, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(hsp[pf_slot(2 * c, 32 + n)]), w8, c1, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(hsp[pf_slot(2 * c + 1, 32 + n)]), w8, c1, 0, 0, 0);
+    }
+    scale_add<16>(acc0, c0, sc[g]);
+    scale_add<16>(acc1, c1, sc[g]);
+    keep(acc0);
+    keep(acc1);
+  }
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int t = 32 * tb + tok_row(r, kh);
+      if (t < count)
+        a.Y[((int64_t)tokb[t] * (K + 1) + tokk[t]) * d + row] = (tb ? acc1[r] : acc0[r]) * hx[t];
+    }
+  }
 }
 
 }  // namespace
@@ -685,11 +1076,28 @@ bool batched_supported(const Dims& dm) {
          dm.E <= kMaxE && dm.r % 8 == 0 && dm.r <= kMaxR && (dm.Is == 0 || dm.Is == dm.I);
 }
 
+// Shapes the prefill kernels take: 256 rows of I per gate/up workgroup,
+// 256 output rows per down workgroup, whole LDS stages of kPfSG groups.
+static bool prefill_supported(const Dims& dm) {
+  return batched_supported(dm) && dm.I % kPfGuRows == 0 && dm.d % 256 == 0 &&
+         dm.d % (64 * kPfSG) == 0;
+}
+
 namespace {
 
 template <int NG>
 void launch_gate_up_ng(const MbArgs& a, dim3 grid, hipStream_t st) {
   hipLaunchKernelGGL(k_mb_gate_up<NG>, grid, dim3(512), 0, st, a);
+}
+
+template <int NG>
+hipError_t launch_pf_down_ng(const MbArgs& a, dim3 grid, hipStream_t st) {
+  const size_t lds = (size_t)NG * 8 * 2 * kPfRow * sizeof(uint4);
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)k_pf_down<NG>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(k_pf_down<NG>, grid, dim3(512), lds, st, a);
+  return hipSuccess;
 }
 
 template <int NG>
@@ -723,10 +1131,27 @@ hipError_t launch_batched(const Dims& dm, const Pool& pool, const SharedW& sh, c
   a.Y = s.yk;
   a.y = y;
   a.flags = s.flags;
-  const int ny = batched_max_tiles(B, dm.K, dm.E);  // tiles past n_tiles exit at once
+  const bool pf = (int64_t)B * dm.K >= (int64_t)kPrefillPerExpert * dm.E && prefill_supported(dm);
+  a.tile = pf ? kPfTok : kCols;
+  // an upper bound for either tile size; tiles past n_tiles exit at once
+  const int ny = batched_max_tiles(B, dm.K, dm.E);
   const int imax = dm.I > dm.Is ? dm.I : dm.Is;
   const int lora_blocks = sh.present && sh.ag ? (B + kCols - 1) / kCols * a.n_sl : 0;
   hipLaunchKernelGGL(k_mb_prep, dim3(B + 1 + lora_blocks), dim3(256), 0, st, a);
+  if (pf) {
+    hipLaunchKernelGGL(k_pf_gate_up, dim3(imax / kPfGuRows, ny), dim3(512), 0, st, a);
+    const dim3 grid(dm.d / 256, ny);
+    hipError_t e;
+    switch (dm.I / dm.G) {
+      case 2: e = launch_pf_down_ng<2>(a, grid, st); break;
+      case 4: e = launch_pf_down_ng<4>(a, grid, st); break;
+      case 6: e = launch_pf_down_ng<6>(a, grid, st); break;
+      default: e = launch_pf_down_ng<8>(a, grid, st); break;
+    }
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_mb_combine, dim3(B, (dm.d + 1023) / 1024), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
   const dim3 gu_grid(imax / 32, ny);
   switch (dm.d / dm.G / 4) {
     case 2: launch_gate_up_ng<2>(a, gu_grid, st); break;
@@ -741,7 +1166,7 @@ hipError_t launch_batched(const Dims& dm, const Pool& pool, const SharedW& sh, c
     case 6: launch_down_ng<6>(a, dn_grid, st); break;
     default: launch_down_ng<8>(a, dn_grid, st); break;
   }
-  hipLaunchKernelGGL(k_mb_combine, dim3(B, (dm.d + 255) / 256), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_mb_combine, dim3(B, (dm.d + 1023) / 1024), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

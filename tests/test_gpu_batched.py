@@ -8,15 +8,18 @@ the oracle's moe_decode for its own routing, 35B shapes with top-K in
 {2, 4, 8} and 8B shapes, B = 32, a partial tile (20) and two tiles (40); two
 runs are bitwise equal; an out-of-range id is flagged.
 
-Prefill-sized batches (the whole-layer path): B = 16 (the smallest batched
-call) and B = 64 checked token by token;
-B = 256 (8B tier, the union covers almost every expert), a skewed batch whose
-tokens share a few hot experts (members of several ragged tiles each) and
+Prefill-sized batches (the whole-layer path; from 16 entries per expert on
+average, B*K >= 16 E, they take the prefill kernels with 64-token tiles):
+B = 16 (the smallest batched call) and B = 64 checked token by token; B = 1023
+and 1024 either side of the switch at K = 4; B = 256 (8B tier, the union
+covers almost every expert), skewed batches of 200 and 1024 tokens whose sets
+share 6 hot experts (members of several ragged tiles each; the second on
+the prefill kernels) and
 B = 3072 (the pages' ~3.1k-token prompt) and B = 8192 (the largest context)
 checked against the oracle on sampled tokens, and on every token by a property that holds at any size: a token's
 output does not depend on the other tokens of its batch (tile rows are
 independent and every sum runs in a fixed order), so the batch equals the same
-tokens run in chunks of 32, bit for bit.
+tokens run in smaller batches that take the same kernels, bit for bit.
 """
 
 import numpy as np
@@ -104,12 +107,25 @@ def test_batched_bad_id_is_flagged(api, pools):
     assert api.device_status(ctx) == api.E0_ERR_RANGE
 
 
-def _chunks(B, c=32):
-    """Chunk bounds of about c tokens, none below the batched path's 16."""
-    bounds = list(range(0, B, c)) + [B]
-    if len(bounds) > 2 and bounds[-1] - bounds[-2] < 16:
-        del bounds[-2]
-    return list(zip(bounds[:-1], bounds[1:]))
+def _prefill_min(dm):
+    """Smallest batch that takes the prefill kernels (64-token tiles): at least
+    16 entries per expert on average, B*K >= 16 E; smaller batches take the
+    chunk kernels (32-token tiles)."""
+    return -(-16 * dm["E"] // dm["K"])
+
+
+def _windows(B, dm):
+    """Token windows that take the same kernels as the whole batch: chunks of
+    ~32 (none below 16) for the chunk kernels; windows of the prefill minimum,
+    the last one ending at B (windows may overlap), for the prefill kernels."""
+    PREFILL_MIN = _prefill_min(dm)
+    if B < PREFILL_MIN:
+        bounds = list(range(0, B, 32)) + [B]
+        if len(bounds) > 2 and bounds[-1] - bounds[-2] < 16:
+            del bounds[-2]
+        return list(zip(bounds[:-1], bounds[1:]))
+    starts = sorted(set(list(range(0, B - PREFILL_MIN + 1, PREFILL_MIN)) + [B - PREFILL_MIN]))
+    return [(c0, c0 + PREFILL_MIN) for c0 in starts]
 
 
 def _hot_tokens(rng, dm, B, n_hot):
@@ -122,8 +138,11 @@ def _hot_tokens(rng, dm, B, n_hot):
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("tier,K,B,hot,n_check", [("35b", 4, 16, 0, 16), ("35b", 4, 64, 0, 64),
+                                                  ("35b", 4, 1023, 0, 16),
+                                                  ("35b", 4, 1024, 0, 16),
                                                   ("8b", 8, 256, 0, 24),
                                                   ("35b", 4, 200, 6, 24),
+                                                  ("35b", 4, 1024, 6, 16),
                                                   ("35b", 8, 3072, 0, 16),
                                                   ("35b", 8, 8192, 0, 8)])
 def test_batched_prefill_parity(api, orc, pools, tier, K, B, hot, n_check):
@@ -139,14 +158,6 @@ def test_batched_prefill_parity(api, orc, pools, tier, K, B, hot, n_check):
     y = api.moe_int4_decode(ctx, dpool, dx, didx, dw, shared=dsh)
     torch.cuda.synchronize()
     assert api.device_status(ctx) == 0
-    # every token: the batch equals the same tokens in chunks of ~32
-    yb = host(y).view(np.uint16)
-    for c0, c1 in _chunks(B):
-        yc = api.moe_int4_decode(ctx, dpool, dx[c0:c1].contiguous(), didx[c0:c1].contiguous(),
-                                 dw[c0:c1].contiguous(), shared=dsh)
-        assert np.array_equal(host(yc).view(np.uint16), yb[c0:c1]), \
-            f"tokens {c0}..{c1} differ between the batch and a chunk"
-    assert api.device_status(ctx) == 0
     # sampled tokens (always the first and the last) against the oracle
     check = (np.arange(B) if n_check >= B else
              np.unique(np.concatenate([[0, B - 1], rng.choice(B, size=n_check, replace=False)])))
@@ -156,6 +167,15 @@ def test_batched_prefill_parity(api, orc, pools, tier, K, B, hot, n_check):
         ref = orc.moe_decode(dm, pool, sh, x[b], idx[b], w[b].astype(np.float64))
         assert_out_close(yg[b], ref, f"{tier} K={K} B={B} token {b}")
         worst = max(worst, out_err(yg[b], ref))
+    # every token: the batch equals the same tokens run in smaller batches
+    # that take the same kernels
+    yb = host(y).view(np.uint16)
+    for c0, c1 in _windows(B, dm):
+        yc = api.moe_int4_decode(ctx, dpool, dx[c0:c1].contiguous(), didx[c0:c1].contiguous(),
+                                 dw[c0:c1].contiguous(), shared=dsh)
+        assert np.array_equal(host(yc).view(np.uint16), yb[c0:c1]), \
+            f"tokens {c0}..{c1} differ between the batch and a smaller batch"
+    assert api.device_status(ctx) == 0
     counts = np.bincount(idx.ravel(), minlength=dm["E"])
     print(f"{tier} K={K} B={B}: worst error ratio {worst:.3f} over {len(check)} tokens, "
           f"union {np.count_nonzero(counts)} experts, largest member {counts.max()} tokens")
