@@ -224,6 +224,94 @@ def run_chunk(args):
                       "warmup": args.warmup, "results": lines}))
 
 
+def run_prefill(args):
+    """Prefill-sized batch through L layers whose routed experts live in a
+    pinned host pool, with layer-ahead whole-layer staging
+    (pipeline.PrefillStack over stage_layer): B tokens per layer (default
+    3072, the pages' ~3.1k-token prompt), 35B-tier layers, routing by each
+    layer's fp16 router with softmax top-K (input preparation, outside the
+    timed loop; see run_chunk). Timed: passes over the L layers, staged from
+    the host; the same layers with resident pools (compute alone); the copies
+    alone (host link). MoE work only: the attention stand-in is not part of
+    this path."""
+    import torch
+    from sparse_moe_decode_amd import api, pipeline, synth
+    from sparse_moe_decode_amd import workloads as wl
+    tier, B, L, K = "35b", args.prefill_b, args.prefill_layers, args.chunk_k or 4
+    dm = synth.dims(tier, K=K)
+    d, E, P = dm["d"], dm["E"], dm["P"]
+    ctx = api.Context(dm, max_tokens=B)
+    bundle = ctx.bundle_bytes()
+    host_pool = torch.empty((L, E * bundle), dtype=torch.uint8, pin_memory=True)
+    resident, shared, xs, idxs, ws = [], [], [], [], []
+    for l in range(L):
+        rng = synth.rng_for(args.seed, 80, l)
+        pool = synth.routed_pool(rng, dm)
+        sh = synth.shared_expert(rng, dm)
+        router, _ = synth.router(rng, dm)
+        host_pool[l].copy_(torch.from_numpy(api.pack_bundles(pool, dm).reshape(-1)))
+        resident.append(wl.tree_to_dev(pool))
+        shared.append(wl.tree_to_dev(sh))
+        head = dict(fc1=torch.zeros((P, d + 2 * E), dtype=torch.float16, device="cuda"),
+                    fc2=torch.zeros((E, P), dtype=torch.float16, device="cuda"),
+                    lin=torch.cat([wl.to_dev(router),
+                                   torch.zeros((E, 2 * E), dtype=torch.float16, device="cuda")],
+                                  dim=1).contiguous())
+        x = torch.from_numpy(synth.f16_normal(rng, (B, d))).cuda()
+        cur = wl.to_dev(np.stack([synth.random_set(rng, E, K) for _ in range(B)]))
+        didx, dw = api.prerouter_forward(ctx, head, x, cur)
+        xs.append(x)
+        idxs.append(didx)
+        ws.append(dw)
+        print(f"[bench] prefill layer {l + 1}/{L} ready", file=sys.stderr, flush=True)
+    X, IDX, W = torch.stack(xs), torch.stack(idxs), torch.stack(ws)
+    Y = torch.empty((L, B, d), dtype=torch.float16, device="cuda")
+    torch.cuda.synchronize()
+    pipe = pipeline.PrefillStack(ctx, host_pool, shared)
+
+    def timed(fn, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def resident_pass():
+        for l in range(L):
+            api.moe_int4_decode(ctx, resident[l], X[l], IDX[l], W[l], y=Y[l], shared=shared[l])
+
+    def copy_pass():
+        for l in range(L):
+            api.stage_layer(ctx, host_pool[l], pipe.hbm[l % 2])
+
+    for _ in range(args.warmup):
+        pipe.run(X, IDX, W, Y)
+        resident_pass()
+    assert api.device_status(ctx) == 0
+    ms_staged = timed(lambda: pipe.run(X, IDX, W, Y), args.steps)
+    ms_res = timed(resident_pass, args.steps)
+    ms_copy = timed(copy_pass, max(1, args.steps // 2))
+    assert api.device_status(ctx) == 0
+    layer_bytes = E * bundle
+    print(json.dumps({
+        "workload": f"35B-tier prefill batch through {L} layers with host-resident experts, "
+                    "layer-ahead whole-layer staging (stage_layer + moe_int4_decode)",
+        "B": B, "K": K, "layers": L, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_layer_staged": round(ms_staged / L, 4),
+        "ms_per_layer_resident": round(ms_res / L, 4),
+        "ms_per_layer_copy_alone": round(ms_copy / L, 4),
+        "tokens_per_s_per_layer_staged": round(B / (ms_staged / L * 1e-3), 1),
+        "tokens_per_s_per_layer_resident": round(B / (ms_res / L * 1e-3), 1),
+        "host_gb_per_s_staged": round(layer_bytes * L / (ms_staged * 1e-3) / 1e9, 2),
+        "host_gb_per_s_copy_alone": round(layer_bytes * L / (ms_copy * 1e-3) / 1e9, 2),
+        "layer_bytes": layer_bytes,
+        "note": "tokens/s are per layer (a B-token batch through one MoE layer); a 40-layer "
+                "MoE prefill takes 40x the per-layer time"}))
+
+
 def host_link_probes(api, stager, host_pool, bundle, dm, n_layers, seed):
     """Host-to-HBM rates on this machine: (1) a plain pinned-memory copy
     (256 MiB, DMA engine), (2) stage_experts alone, every layer getting K
@@ -476,9 +564,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
-    ap.add_argument("--workload", choices=["stack", "chunk", "staged", "layer"], default="stack",
+    ap.add_argument("--workload", choices=["stack", "chunk", "staged", "layer", "prefill"],
+                    default="stack",
                     help="stack: the 40-layer resident decode (the bench line); chunk: the "
-                         "batched path (B=32 chunk, or --chunk-b); staged: the host-staged stack; layer: single "
+                         "batched path (B=32 chunk, or --chunk-b); prefill: a B-token batch through "
+                         "host-resident layers with layer-ahead staging; staged: the host-staged stack; layer: single "
                          "layer-steps, warm and cold")
     ap.add_argument("--reserve-cus", type=int, default=16,
                     help="staged workload: compute units left to the staging copies")
@@ -486,6 +576,10 @@ def main():
                     help="staged workload: predicted layers per launch")
     ap.add_argument("--chunk-k", type=int, default=0, choices=[0, 2, 4, 8],
                     help="chunk workload: only this top-K (0 = 2, 4 and 8)")
+    ap.add_argument("--prefill-b", type=int, default=3072,
+                    help="prefill workload: tokens per batch")
+    ap.add_argument("--prefill-layers", type=int, default=8,
+                    help="prefill workload: host-resident layers")
     ap.add_argument("--chunk-b", type=int, nargs="+", default=[32],
                     help="chunk workload: batch sizes (32 = a decode chunk; 3072 = a "
                          "prefill-sized batch)")
@@ -500,7 +594,8 @@ def main():
         if args.gpus != 1:
             print("bench.py measures one GPU (run with --gpus 1)", file=sys.stderr)
             sys.exit(2)
-        dict(chunk=run_chunk, staged=run_staged, layer=run_layer)[args.workload](args)
+        dict(chunk=run_chunk, staged=run_staged, layer=run_layer,
+             prefill=run_prefill)[args.workload](args)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:

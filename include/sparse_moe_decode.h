@@ -321,6 +321,25 @@ int stage_experts(e0_stager* st, int32_t layer, const int32_t* new_idx,
 int stage_experts_n(e0_stager* st, int32_t layer, int32_t n_layers, const int32_t* new_idx,
                     const int32_t* in_use_idx, void* side_stream, void* done_event);
 
+/* ---------------------------------------------------------------------------
+ * stage_layer — whole-layer staging for prefill-sized batches [MW §3.1
+ * Executor paths, "whole-layer": a prefill loads every expert of a layer at
+ * once, and the load of the next layer overlaps the current layer's GPU
+ * work]. Copies one layer's E expert bundles as a single DMA transfer on
+ * `stream`, then records done_event (a hipEvent_t, may be NULL) there.
+ *   host_layer  HOST pointer, pinned (hipHostMalloc), E bundles in the bundle
+ *               layout above (E * e0_bundle_bytes bytes, contiguous, expert e
+ *               at e * bundle).
+ *   hbm_layer   device pointer, the same size. An e0_experts view of it with
+ *               stride_q = stride_s = bundle bytes (no slot table) feeds
+ *               moe_int4_decode.
+ * The caller owns both buffers and orders the copy against the kernels that
+ * read hbm_layer (events). Errors: E0_ERR_ARG for a null pointer or a host
+ * pointer that is not pinned, E0_ERR_ALIGN unless both are 16-byte aligned,
+ * E0_ERR_HIP if the copy cannot be queued. */
+int stage_layer(e0_ctx* ctx, const void* host_layer, void* hbm_layer, void* stream,
+                void* done_event);
+
 /* Bundles copied by this stager's stage_experts calls since it was created
  * (observability: host-link bytes = count x e0_bundle_bytes). Synchronises
  * the device; E0_ERR_HIP if a copy fails. */

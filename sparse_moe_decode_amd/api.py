@@ -94,12 +94,13 @@ _lib.e0_stager_create.argtypes = [_p, _p, _i32, _i32, _p, _p, _p, C.POINTER(_p)]
 _lib.e0_stager_destroy.argtypes = [_p]
 _lib.stage_experts.argtypes = [_p, _i32, _p, _p, _p, _p]
 _lib.stage_experts_n.argtypes = [_p, _i32, _i32, _p, _p, _p, _p]
+_lib.stage_layer.argtypes = [_p, _p, _p, _p, _p]
 _lib.e0_stager_copies.argtypes = [_p, C.POINTER(C.c_int64)]
 
 EXPORTS = ["e0_create", "e0_destroy", "e0_last_error", "e0_device_status", "moe_int4_decode",
            "lora_delta", "prerouter_forward", "e0_model_create", "e0_model_destroy",
            "layer_step", "e0_bundle_bytes", "e0_stager_create", "e0_stager_destroy",
-           "stage_experts", "stage_experts_n", "e0_stager_copies", "e0_model_set_path", "e0_model_set_grid", "e0_model_set_trace", "e0_model_trace_shape"]
+           "stage_experts", "stage_experts_n", "e0_stager_copies", "stage_layer", "e0_model_set_path", "e0_model_set_grid", "e0_model_set_trace", "e0_model_trace_shape"]
 
 PATH_AUTO, PATH_PHASES, PATH_PERSISTENT = 0, 1, 2
 
@@ -399,6 +400,13 @@ def stage_experts(stager: Stager, layer: int, new_idx, in_use_idx=None, side_str
     ev = _event_handle(done_event, side_stream)
     _check(_lib.stage_experts(stager.handle, layer, _ptr(new_idx), _ptr(in_use_idx),
                               _stream(side_stream), ev))
+
+
+def stage_layer(ctx: Context, host_layer, hbm_layer, stream=None, done_event=None):
+    """Copy one layer's E expert bundles (pinned host uint8 [E * bundle]) into
+    hbm_layer (device, same size) as one DMA transfer on `stream`."""
+    ev = _event_handle(done_event, stream)
+    _check(_lib.stage_layer(ctx.handle, _ptr(host_layer), _ptr(hbm_layer), _stream(stream), ev))
 
 
 def stage_experts_n(stager: Stager, layer: int, n_layers: int, new_idx, in_use_idx=None,

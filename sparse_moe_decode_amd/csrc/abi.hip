@@ -707,4 +707,26 @@ int stage_experts(e0_stager* st, int32_t layer, const int32_t* new_idx,
   return stage_experts_n(st, layer, 1, new_idx, in_use_idx, side_stream, done_event);
 }
 
+int stage_layer(e0_ctx* ctx, const void* host_layer, void* hbm_layer, void* stream,
+                void* done_event) {
+  if (!ctx || !host_layer || !hbm_layer) return fail(E0_ERR_ARG, "stage_layer: null argument");
+  if (!aligned(host_layer, 16) || !aligned(hbm_layer, 16))
+    return fail(E0_ERR_ALIGN, "stage_layer: pools must be 16-byte aligned");
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, host_layer);
+  if (e != hipSuccess || attr.type != hipMemoryTypeHost) {
+    (void)hipGetLastError();
+    return fail(E0_ERR_ARG, "stage_layer: host pool is not pinned host memory");
+  }
+  const size_t bytes = (size_t)ctx->dm.E * (size_t)e0_bundle_bytes(&ctx->spec);
+  hipStream_t st = (hipStream_t)stream;
+  e = hipMemcpyAsync(hbm_layer, host_layer, bytes, hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return hip_fail(e, "stage_layer: copy");
+  if (done_event) {
+    e = hipEventRecord((hipEvent_t)done_event, st);
+    if (e != hipSuccess) return hip_fail(e, "stage_layer: event");
+  }
+  return E0_OK;
+}
+
 }  // extern "C"

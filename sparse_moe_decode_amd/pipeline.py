@@ -109,3 +109,54 @@ class StagedStack:
         if c1 + 1 < self.L:
             api.layer_step(ctx, model, c1 + 1, self.L, st, t, h[c1 + 1:], main)
         self.stage(t + 1, after_token=True)
+
+
+class PrefillStack:
+    """Prefill-sized batches through layers whose routed experts live in a
+    pinned host pool, with layer-ahead whole-layer staging ("The Other Half of
+    the Memory Wall", §3.1 Executor paths, whole-layer: a prefill loads every
+    expert of a layer at once, and the load of the next layer overlaps the
+    current layer's GPU work).
+
+    Two HBM layer buffers alternate: while layer l runs moe_int4_decode on
+    buffer l % 2 (main stream), stage_layer copies layer l+1's bundles into
+    the other buffer (side stream, DMA), after the main stream has finished
+    with it (layer l-1). Events order every copy against the kernels that read
+    its buffer.
+
+    host_pool: pinned uint8 [L, E * bundle]; shared: per-layer shared-expert
+    dicts of device tensors (resident) or None."""
+
+    def __init__(self, ctx: api.Context, host_pool, shared: list,
+                 main: torch.cuda.Stream | None = None, side: torch.cuda.Stream | None = None):
+        self.ctx, self.host, self.shared = ctx, host_pool, shared
+        self.L = host_pool.shape[0]
+        self.bundle = ctx.bundle_bytes()
+        assert host_pool.shape[1] == ctx.dims["E"] * self.bundle and host_pool.is_pinned()
+        self.hbm = torch.empty((2, host_pool.shape[1]), dtype=torch.uint8, device="cuda")
+        self.views = [api.bundle_view(self.hbm[i].data_ptr(), ctx.dims) for i in range(2)]
+        self.main = main if main is not None else torch.cuda.current_stream()
+        self.side = side if side is not None else torch.cuda.Stream()
+        self.staged = [torch.cuda.Event() for _ in range(2)]
+        self.free = [torch.cuda.Event() for _ in range(2)]
+
+    def _stage(self, l: int):
+        buf = l % 2
+        self.side.wait_event(self.free[buf])
+        api.stage_layer(self.ctx, self.host[l], self.hbm[buf], stream=self.side,
+                        done_event=self.staged[buf])
+
+    def run(self, x, idx, w, y):
+        """Layer l maps x[l] (fp16 [B, d], normed) with routing idx[l], w[l]
+        ([B, K]) to y[l]; all on the GPU."""
+        for i in range(2):  # both buffers start free
+            self.free[i].record(self.main)
+        self._stage(0)
+        for l in range(self.L):
+            buf = l % 2
+            if l + 1 < self.L:
+                self._stage(l + 1)
+            self.main.wait_event(self.staged[buf])
+            api.moe_int4_decode(self.ctx, self.views[buf], x[l], idx[l], w[l], y=y[l],
+                                shared=self.shared[l], stride=self.bundle, stream=self.main)
+            self.free[buf].record(self.main)
