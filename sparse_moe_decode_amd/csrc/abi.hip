@@ -410,7 +410,9 @@ int e0_model_create(e0_ctx* ctx, const e0_layer* layers, int32_t n_layers, e0_mo
     t.attn = L.attn;
     const int Is = t.sh.present ? dm.Is : 0;
     const int r2 = (t.sh.present && t.sh.ag) ? 2 * dm.r : 0;
-    const int n = dm.K * dm.I + 2 * Is + r2;
+    // exchange words of a layer: routed SwiGLU outputs, shared SwiGLU
+    // outputs, the shared gate/up LoRA A products
+    const int n = dm.K * dm.I + Is + r2;
     if (n > ng) ng = n;
   }
   m->ng = ng;

@@ -9,10 +9,12 @@
 //   2. routing: the layer's own router (rows spread over the chip, logits
 //      exchanged, top-K recomputed identically everywhere) or the prediction
 //      the previous token's head wrote;
-//   3. gate/up rows of the routed experts and the shared expert, and the
-//      LoRA A products of the shared gate/up, spread over the chip;
-//   4. every workgroup gathers the SwiGLU outputs and finishes the shared
-//      expert (LoRA B of gate/up, SwiGLU, LoRA A of down) itself;
+//   3. gate/up rows of the routed experts and the shared expert spread over
+//      the chip; the LoRA A products of the shared gate/up (published right
+//      after the norm) let the owners of shared rows add the LoRA B terms, so
+//      every gate/up row leaves its owner as a finished SwiGLU output;
+//   4. every workgroup gathers the SwiGLU outputs and forms the shared
+//      expert's down-LoRA A product itself;
 //   5. down rows with the weighted combine, shared expert and down LoRA;
 //      h_{l+1} = fp16(h_a + y) is published.
 // The prerouter heads are not on this chain: a head's output is consumed by
@@ -170,6 +172,12 @@ struct Misc {
   float coef[16];
   float csc[kMaxExp][16];      // power-of-two scale of each 32-element hi/lo chunk
   float ad[kRank];             // A_down . h_shared
+  float axgu[2 * kRank];       // A_gate x then A_up x (rows of the shared expert)
+  // base addresses of a layer's experts (slot k < K routed, k == K shared;
+  // null when unused or unresolved): gate q, up q, down q, gate s, up s,
+  // down s. Two sets by layer parity: the next layer's is written while the
+  // current one is read.
+  const void* eptr[2][kMaxExp][6];
   float red16[kRank][kGroups];
   float hsc[kHX][16];          // scales of the fc2 activation chunks (per lane)
   float red[4 * kNR];
@@ -276,54 +284,65 @@ __device__ __forceinline__ void f16rows_finish(const F16Rows<NR>& R, int nr, int
   block_rows_reduce<NR>(p, nr, ms);
 }
 
+// Base addresses of expert slot k of a layer into ep[k] (see Misc::eptr);
+// ent: the slot's pool entry (routed slots, k < K).
+__device__ __forceinline__ void fill_slot(const void* (&ep)[6], const LayerDev& Ly, int K, int k,
+                                          int64_t ent) {
+  const void* p[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  if (k < K && ent >= 0) {
+    p[0] = entry_ptr(Ly.pool.gate.q, ent, Ly.pool.stride_q);
+    p[1] = entry_ptr(Ly.pool.up.q, ent, Ly.pool.stride_q);
+    p[2] = entry_ptr(Ly.pool.down.q, ent, Ly.pool.stride_q);
+    p[3] = entry_ptr(Ly.pool.gate.s, ent, Ly.pool.stride_s);
+    p[4] = entry_ptr(Ly.pool.up.s, ent, Ly.pool.stride_s);
+    p[5] = entry_ptr(Ly.pool.down.s, ent, Ly.pool.stride_s);
+  } else if (k == K && Ly.sh.present) {
+    p[0] = Ly.sh.gate.q;
+    p[1] = Ly.sh.up.q;
+    p[2] = Ly.sh.down.q;
+    p[3] = Ly.sh.gate.s;
+    p[4] = Ly.sh.up.s;
+    p[5] = Ly.sh.down.s;
+  }
+#pragma unroll
+  for (int i = 0; i < 6; ++i) ep[i] = p[i];
+}
+
 // ---- gate/up items of one lane group (IPG items per group) ---------------
 template <int CPL, int IPG>
 struct GuRegs {
   uint4 wg[IPG][CPL], wu[IPG][CPL];
   uint16_t sg[IPG][CPL], su[IPG][CPL];
+  uint16_t lbg[IPG], lbu[IPG];  // shared items: element li of the row of LoRA B_gate / B_up
 };
 
 struct GuPlan {
   int ib, ie;  // item range of this workgroup
 };
 
-// ent: pool entries of the layer's K routed slots (LDS).
-__device__ __forceinline__ bool gu_item(const LayerDev& Ly, const Dims& dm, const int64_t* ent_k,
-                                        int n_rt, int it, const uint32_t*& gq,
-                                        const uint32_t*& uq, const uint16_t*& gs,
-                                        const uint16_t*& us, int& row) {
-  const bool routed = it < n_rt;
-  if (routed) {
-    const int k = it / kStackI;
-    row = it % kStackI;
-    const int64_t ent = ent_k[k];
-    const int64_t e = ent >= 0 ? ent : 0;
-    gq = (const uint32_t*)entry_ptr(Ly.pool.gate.q, e, Ly.pool.stride_q);
-    uq = (const uint32_t*)entry_ptr(Ly.pool.up.q, e, Ly.pool.stride_q);
-    gs = (const uint16_t*)entry_ptr(Ly.pool.gate.s, e, Ly.pool.stride_s);
-    us = (const uint16_t*)entry_ptr(Ly.pool.up.s, e, Ly.pool.stride_s);
-    return ent >= 0;
-  }
-  row = it - n_rt;
-  gq = Ly.sh.gate.q;
-  uq = Ly.sh.up.q;
-  gs = Ly.sh.gate.s;
-  us = Ly.sh.up.s;
-  return true;
-}
-
+// Gate/up rows of the group's items, addressed through the layer's slot
+// table ep (LDS); items of unresolved routed slots are skipped.
 template <int CPL, int IPG>
 __device__ __forceinline__ void gu_issue(GuRegs<CPL, IPG>& R, const LayerDev& Ly, const Dims& dm,
-                                         const int64_t* ent_k, int n_rt, const GuPlan& pl,
+                                         const void* const (*ep)[6], int n_rt, const GuPlan& pl,
                                          int grp, int li) {
 #pragma unroll
   for (int j = 0; j < IPG; ++j) {
     const int it = pl.ib + grp + kGroups * j;
     if (it >= pl.ie) continue;
-    const uint32_t *gq, *uq;
-    const uint16_t *gs, *us;
-    int row;
-    if (!gu_item(Ly, dm, ent_k, n_rt, it, gq, uq, gs, us, row)) continue;
+    const bool routed = it < n_rt;
+    const int k = routed ? it / kStackI : dm.K;
+    const int row = routed ? it % kStackI : it - n_rt;
+    const uint32_t* gq = (const uint32_t*)ep[k][0];
+    if (!gq) continue;
+    const uint32_t* uq = (const uint32_t*)ep[k][1];
+    const uint16_t* gs = (const uint16_t*)ep[k][3];
+    const uint16_t* us = (const uint16_t*)ep[k][4];
+    R.lbg[j] = R.lbu[j] = 0;
+    if (!routed && Ly.sh.ag) {
+      R.lbg[j] = ldg(Ly.sh.bg + (int64_t)row * kRank + li);
+      R.lbu[j] = ldg(Ly.sh.bu + (int64_t)row * kRank + li);
+    }
     const int gsh = __builtin_ctz(dm.G);  // G is a power of two
     const int wpr = dm.d / 8, spr = dm.d >> gsh;
     const uint32_t* grow = gq + (int64_t)row * wpr;
@@ -339,11 +358,14 @@ __device__ __forceinline__ void gu_issue(GuRegs<CPL, IPG>& R, const LayerDev& Ly
   }
 }
 
+// Gate and up dot products of the group's items. Routed items publish
+// silu(g) u at once; a shared item's sums are returned in sg_out / su_out
+// for gu_finish_shared (its LoRA terms need the layer's A products).
 template <int CPL, int IPG>
-__device__ __forceinline__ void gu_finish(const GuRegs<CPL, IPG>& R, const Dims& dm,
-                                          const int64_t* ent_k, int n_rt, int Is, const GuPlan& pl,
-                                          int grp, int li, const uint16_t* xperm, uint64_t* xg,
-                                          uint32_t ep) {
+__device__ __forceinline__ void gu_finish(const GuRegs<CPL, IPG>& R, const int64_t* ent_k,
+                                          int n_rt, const GuPlan& pl, int grp, int li,
+                                          const uint16_t* xperm, uint64_t* xg, uint32_t ep,
+                                          float (&sg_out)[IPG], float (&su_out)[IPG]) {
 #pragma unroll
   for (int j = 0; j < IPG; ++j) {
     const int it = pl.ib + grp + kGroups * j;
@@ -362,14 +384,33 @@ __device__ __forceinline__ void gu_finish(const GuRegs<CPL, IPG>& R, const Dims&
     }
     ag = group_sum<kLG>(ag);
     au = group_sum<kLG>(au);
-    if (li == 0) {
-      if (routed) {
-        ll_put(xg + it, fbits(ok ? silu(ag) * au : 0.0f), ep);
-      } else {
-        ll_put(xg + n_rt + (it - n_rt), fbits(ag), ep);
-        ll_put(xg + n_rt + Is + (it - n_rt), fbits(au), ep);
-      }
+    sg_out[j] = ag;
+    su_out[j] = au;
+    if (routed && li == 0) ll_put(xg + it, fbits(ok ? silu(ag) * au : 0.0f), ep);
+  }
+}
+
+// Shared items: g += c B_gate[row] . (A_gate x), u likewise (lane li takes
+// rank li; axgu holds the r gate then r up A products, or null without
+// LoRA), then silu(g) u is published after the routed outputs.
+template <int CPL, int IPG>
+__device__ __forceinline__ void gu_finish_shared(const GuRegs<CPL, IPG>& R, float cl, int n_rt,
+                                                 const GuPlan& pl, int grp, int li,
+                                                 const float* axgu, const float (&sg_in)[IPG],
+                                                 const float (&su_in)[IPG], uint64_t* xg,
+                                                 uint32_t ep) {
+#pragma unroll
+  for (int j = 0; j < IPG; ++j) {
+    const int it = pl.ib + grp + kGroups * j;
+    if (it >= pl.ie || it < n_rt) continue;  // uniform over the lane group
+    float g = sg_in[j], u = su_in[j];
+    if (axgu) {
+      const float lg = group_sum<kLG>(h2f(R.lbg[j]) * axgu[li]);
+      const float lu = group_sum<kLG>(h2f(R.lbu[j]) * axgu[kRank + li]);
+      g = fmaf(cl, lg, g);
+      u = fmaf(cl, lu, u);
     }
+    if (li == 0) ll_put(xg + it, fbits(silu(g) * u), ep);
   }
 }
 
@@ -381,24 +422,10 @@ struct DownRegs {
   uint4 bd[kRank / 8];  // LoRA B of the down projection, row drow (lane 0 of the group)
 };
 
-// Shared-expert LoRA matrices, thread t's part: rows 2t and 2t+1 of B_gate
-// and B_up ([Is, r]), and columns 2t, 2t+1 of A_down ([r, Is]).
+// Shared-expert LoRA A_down ([r, Is]), thread t's part: columns 2t, 2t+1.
 struct LoraRegs {
-  uint4 bg[kRank / 4], bu[kRank / 4];
   uint32_t ad[kRank];
 };
-
-// B row (kRank fp16 in two 16-byte chunks) . a (kRank fp32 in LDS).
-__device__ __forceinline__ float lora_row(uint4 c0, uint4 c1, const float* a) {
-  const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-  float s = 0.0f;
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    s += h2f((uint16_t)(w[q] & 0xFFFF)) * a[2 * q];
-    s += h2f((uint16_t)(w[q] >> 16)) * a[2 * q + 1];
-  }
-  return s;
-}
 
 // Lane li of a 16-lane group holds elements 32c + 2li and 32c + 2li + 1 of an
 // I-vector. The group converts chunk c to fp16 hi + lo scaled by a power of
@@ -501,6 +528,9 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
     ms.ent_all[i] = ldg(&Ls->router) ? 0 : resolve_entry(ldg_struct(&Ls->pool), E, ms.ridx_all[i]);
   }
   __syncthreads();
+  // slot table of the first layer (a router layer fills its own once routed)
+  if (t <= K) fill_slot(ms.eptr[0][t], lay[0], K, t, t < K ? ms.ent_all[t] : 0);
+  __syncthreads();
   const int nH = ms.n_heads;
   // This workgroup's share of the heads' fc1 / linear rows (head-major), and
   // the heads whose x it keeps for them.
@@ -519,13 +549,12 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
   const int drow = db + grp;
 
   // Phase B loads of a layer whose routed entries are ent_k[0..K): down rows
-  // [drow] of every expert slot, LoRA B_down row, the shared-expert LoRA
-  // matrices. Issued once this workgroup's gate/up outputs are published, so
-  // that issuing them overlaps the wait for everyone else's.
-  auto issue_b = [&](const LayerDev& Ly, const int64_t* ent_k, PhaseA<CPL_D, IPG, NX>& A) {
+  // [drow] of every expert slot, LoRA B_down row, the shared expert's A_down.
+  // Issued once this workgroup's gate/up outputs are published, so that
+  // issuing them overlaps the wait for everyone else's.
+  auto issue_b = [&](const LayerDev& Ly, const void* const (*ep_k)[6], PhaseA<CPL_D, IPG, NX>& A) {
     const bool has_sh = Ly.sh.present != 0;
     const int Is = has_sh ? dm.Is : 0;
-    const bool lora_gu = has_sh && Ly.sh.ag != nullptr;
     const bool lora_d = has_sh && Ly.sh.ad != nullptr;
     if (drow < de) {
       const int gsh = __builtin_ctz(dm.G);
@@ -534,18 +563,9 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
       for (int k = 0; k < NX; ++k) {
         A.D.w[k] = make_uint4(0, 0, 0, 0);
         A.D.s[k] = 0;
-        const uint32_t* q = nullptr;
-        const uint16_t* sc = nullptr;
-        if (k < K) {
-          const int64_t ent = ent_k[k];
-          if (ent >= 0) {
-            q = (const uint32_t*)entry_ptr(Ly.pool.down.q, ent, Ly.pool.stride_q);
-            sc = (const uint16_t*)entry_ptr(Ly.pool.down.s, ent, Ly.pool.stride_s);
-          }
-        } else if (k == K && has_sh) {
-          q = Ly.sh.down.q;
-          sc = Ly.sh.down.s;
-        }
+        if (k > K) continue;
+        const uint32_t* q = (const uint32_t*)ep_k[k][2];
+        const uint16_t* sc = (const uint16_t*)ep_k[k][5];
         if (!q) continue;
         A.D.w[k] = ldg(reinterpret_cast<const uint4*>(q + (int64_t)drow * wpr + 4 * li));
         A.D.s[k] = ldg(sc + (int64_t)drow * spr + ((32 * li) >> gsh));
@@ -555,15 +575,6 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
         A.D.bd[c] = make_uint4(0, 0, 0, 0);
         if (lora_d && li == 0)
           A.D.bd[c] = ldg(reinterpret_cast<const uint4*>(Ly.sh.bd + (int64_t)drow * kRank + 8 * c));
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < kRank / 4; ++c) {
-      A.LR.bg[c] = make_uint4(0, 0, 0, 0);
-      A.LR.bu[c] = make_uint4(0, 0, 0, 0);
-      if (lora_gu) {
-        A.LR.bg[c] = ldg(reinterpret_cast<const uint4*>(Ly.sh.bg + 2 * t * kRank + 8 * c));
-        A.LR.bu[c] = ldg(reinterpret_cast<const uint4*>(Ly.sh.bu + 2 * t * kRank + 8 * c));
       }
     }
 #pragma unroll
@@ -600,7 +611,7 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
       // routing known: entries from the tables
       GuPlan pl;
       split(K * I + Is, G, cu, pl.ib, pl.ie);
-      gu_issue<CPL_D, IPG>(A.gu, Ly, dm, &ms.ent_all[(l - a.l0) * K], K * I, pl, grp, li);
+      gu_issue<CPL_D, IPG>(A.gu, Ly, dm, ms.eptr[(l - a.l0) & 1], K * I, pl, grp, li);
       A.gu_loaded = true;
     }
   };
@@ -674,6 +685,15 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
       }
     }
     __syncthreads();
+    // LoRA A products of the shared gate/up (rows spread over the chip),
+    // published now: the workgroups that own shared-expert rows need them at
+    // the end of step 3 for the LoRA B terms.
+    if (A.n_ax) {
+      int b, e;
+      split(r2, G, cu, b, e);
+      f16rows_finish<kNR>(A.ax, A.n_ax, d, xnat, ms);
+      if (t < A.n_ax) ll_put(xg + n_rt + Is + b + t, fbits(ms.rows[t]), ep);
+    }
     stamp(a, l, 2);
 
     // ---- 2. routing ----------------------------------------------------
@@ -699,6 +719,7 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
       if (t < K) {
         const int64_t ent = resolve_entry(Ly.pool, E, ms.ridx_all[step * K + t]);
         ms.ent_all[step * K + t] = ent;
+        fill_slot(ms.eptr[step & 1][t], Ly, K, t, ent);
         if (ent < 0 && cu == 0) atomicOr(&a.flags[FLAG_RANGE], 1);
       }
       __syncthreads();
@@ -711,23 +732,10 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
       ew[t] = ms.rw_all[step * K + t];
     }
     if (t < NX) {
-      const uint32_t* q = nullptr;
-      const uint16_t* sc = nullptr;
-      float cf = 0.0f;
-      if (t < K) {
-        if (ent_k[t] >= 0) {
-          q = (const uint32_t*)entry_ptr(Ly.pool.down.q, ent_k[t], Ly.pool.stride_q);
-          sc = (const uint16_t*)entry_ptr(Ly.pool.down.s, ent_k[t], Ly.pool.stride_s);
-          cf = ms.rw_all[step * K + t];
-        }
-      } else if (t == K && has_sh) {
-        q = Ly.sh.down.q;
-        sc = Ly.sh.down.s;
-        cf = 1.0f;
-      }
+      const uint32_t* q = t <= K ? (const uint32_t*)ms.eptr[step & 1][t][2] : nullptr;
       ms.dq[t] = q;
-      ms.dsc[t] = sc;
-      ms.coef[t] = cf;
+      ms.dsc[t] = t <= K ? (const uint16_t*)ms.eptr[step & 1][t][5] : nullptr;
+      ms.coef[t] = !q ? 0.0f : t < K ? ms.rw_all[step * K + t] : 1.0f;
     }
     stamp(a, l, 3);
 
@@ -735,27 +743,33 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
     {
       GuPlan pl;
       split(n_rt + Is, G, cu, pl.ib, pl.ie);
-      if (!A.gu_loaded) gu_issue<CPL_D, IPG>(A.gu, Ly, dm, ent_k, n_rt, pl, grp, li);
+      if (!A.gu_loaded) gu_issue<CPL_D, IPG>(A.gu, Ly, dm, ms.eptr[step & 1], n_rt, pl, grp, li);
       vm_drained();  // gate/up rows, router and LoRA A rows have arrived
-      gu_finish<CPL_D, IPG>(A.gu, dm, ent_k, n_rt, Is, pl, grp, li, xperm, xg, ep);
-      if (A.n_ax) {
-        int b, e;
-        split(r2, G, cu, b, e);
-        f16rows_finish<kNR>(A.ax, A.n_ax, d, xnat, ms);
-        if (t < A.n_ax) ll_put(xg + n_rt + 2 * Is + b + t, fbits(ms.rows[t]), ep);
+      float shg[IPG], shu[IPG];
+      gu_finish<CPL_D, IPG>(A.gu, ent_k, n_rt, pl, grp, li, xperm, xg, ep, shg, shu);
+      if (pl.ie > n_rt) {  // this workgroup owns rows of the shared expert
+        const float* axgu = nullptr;
+        if (r2) {
+          ll_gather<1>(xg + n_rt + Is, r2, ep, reinterpret_cast<uint32_t*>(ms.axgu), a.flags,
+                       &ms.abort);
+          __syncthreads();
+          axgu = ms.axgu;
+        }
+        gu_finish_shared<CPL_D, IPG>(A.gu, dm.lora_scale, n_rt, pl, grp, li, axgu, shg, shu, xg,
+                                     ep);
       }
       __syncthreads();  // the down-projection table of this layer is visible
     }
     stamp(a, l, 4);
 
     // ---- phase B loads: down rows, shared-expert LoRA -----------------------
-    issue_b(Ly, ent_k, A);
+    issue_b(Ly, ms.eptr[step & 1], A);
     const DownRegs<NX>& D = A.D;
     const LoraRegs& LR = A.LR;
     stamp(a, l, 5);
 
     // ---- 4. gather SwiGLU outputs; finish the shared expert ----------------
-    const int ng_l = n_rt + 2 * Is + r2;
+    const int ng_l = n_rt + Is;
     ll_gather<16>(xg, ng_l, ep, land, a.flags, &ms.abort);
     vm_drained();
     __syncthreads();
@@ -765,19 +779,9 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
       // lane group grp converts 32-element chunk grp (I / 32 == kGroups).
       const float* lf = (const float*)land;
       if (has_sh) {
-        const float cs = dm.lora_scale;
-        const float2 gb = *reinterpret_cast<const float2*>(lf + n_rt + 2 * t);
-        const float2 ub = *reinterpret_cast<const float2*>(lf + n_rt + Is + 2 * t);
-        float g0v = gb.x, g1v = gb.y, u0v = ub.x, u1v = ub.y;
-        if (r2) {
-          const float* axg = lf + n_rt + 2 * Is;
-          const float* axu = axg + kRank;
-          g0v += cs * lora_row(LR.bg[0], LR.bg[1], axg);
-          g1v += cs * lora_row(LR.bg[2], LR.bg[3], axg);
-          u0v += cs * lora_row(LR.bu[0], LR.bu[1], axu);
-          u1v += cs * lora_row(LR.bu[2], LR.bu[3], axu);
-        }
-        const float h0 = silu(g0v) * u0v, h1 = silu(g1v) * u1v;
+        // the shared expert's SwiGLU outputs, LoRA terms included
+        const float2 hb = *reinterpret_cast<const float2*>(lf + n_rt + 2 * t);
+        const float h0 = hb.x, h1 = hb.y;
         const float sc = hilo_pair(h0, h1, grp, li, hk + K * 2 * I, I);
         if (li == 0) ms.csc[K][grp] = sc;
         if (lora_d) {
@@ -789,11 +793,22 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
           }
         }
       }
-      for (int k = 0; k < K; ++k) {
-        if (!ms.dq[k]) continue;  // uniform: unresolved expert, contributes nothing
-        const float2 v = *reinterpret_cast<const float2*>(lf + k * I + 32 * grp + 2 * li);
-        const float sc = hilo_pair(v.x, v.y, grp, li, hk + k * 2 * I, I);
-        if (li == 0) ms.csc[k][grp] = sc;
+      // An unresolved expert's outputs are zeros (never used: its down rows
+      // are zero too). With K == NX - 1 the loop is unrolled without
+      // branches, so the experts' conversions interleave.
+      if (K == NX - 1) {
+#pragma unroll
+        for (int k = 0; k < NX - 1; ++k) {
+          const float2 v = *reinterpret_cast<const float2*>(lf + k * I + 32 * grp + 2 * li);
+          const float sc = hilo_pair(v.x, v.y, grp, li, hk + k * 2 * I, I);
+          if (li == 0) ms.csc[k][grp] = sc;
+        }
+      } else {
+        for (int k = 0; k < K; ++k) {
+          const float2 v = *reinterpret_cast<const float2*>(lf + k * I + 32 * grp + 2 * li);
+          const float sc = hilo_pair(v.x, v.y, grp, li, hk + k * 2 * I, I);
+          if (li == 0) ms.csc[k][grp] = sc;
+        }
       }
       __syncthreads();
       if (lora_d && t < kRank) {
@@ -808,14 +823,28 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
     // ---- 5. down rows: combine, shared expert, down LoRA, residual ---------
     if (drow < de) {
       float acc = 0.0f;
+      // Slots without an expert (unresolved ids, no shared expert, k > K)
+      // hold zero weights and a zero coefficient; with K == NX - 1 the loop
+      // runs without branches so that the slots' LDS reads interleave.
+      if (K == NX - 1 && has_sh) {
 #pragma unroll
-      for (int k = 0; k < NX; ++k) {
-        if (!ms.dq[k]) continue;
-        const uint16_t* hh = hk + (int64_t)k * 2 * I;
-        f16x2 xh[16], xl[16];
-        load_xchunk(hh, li, xh);
-        load_xchunk(hh + I, li, xl);
-        acc += (ms.coef[k] * ms.csc[k][li]) * (h2f(D.s[k]) * q4_dot32_hl(D.w[k], xh, xl));
+        for (int k = 0; k < NX; ++k) {
+          const uint16_t* hh = hk + (int64_t)k * 2 * I;
+          f16x2 xh[16], xl[16];
+          load_xchunk(hh, li, xh);
+          load_xchunk(hh + I, li, xl);
+          acc += (ms.coef[k] * ms.csc[k][li]) * (h2f(D.s[k]) * q4_dot32_hl(D.w[k], xh, xl));
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < NX; ++k) {
+          if (!ms.dq[k]) continue;
+          const uint16_t* hh = hk + (int64_t)k * 2 * I;
+          f16x2 xh[16], xl[16];
+          load_xchunk(hh, li, xh);
+          load_xchunk(hh + I, li, xl);
+          acc += (ms.coef[k] * ms.csc[k][li]) * (h2f(D.s[k]) * q4_dot32_hl(D.w[k], xh, xl));
+        }
       }
       if (lora_d && li == 0) {
         float lsum = 0.0f;
@@ -838,6 +867,11 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
         ms.hstage[drow - db] = hv;
       }
     }
+    // slot table of the next layer (its routing is known unless it is a
+    // router layer, which fills its own once routed)
+    if (step + 1 < nL && t <= K)
+      fill_slot(ms.eptr[(step + 1) & 1][t], lay[step + 1], K, t,
+                t < K ? ms.ent_all[(step + 1) * K + t] : 0);
     __syncthreads();
     for (int j = db / 2 + t; j < de / 2; j += kThreads) {
       const int r0 = 2 * j - db;
