@@ -312,7 +312,9 @@ __device__ __forceinline__ void fill_slot(const void* (&ep)[6], const LayerDev& 
 template <int CPL, int IPG>
 struct GuRegs {
   uint4 wg[IPG][CPL], wu[IPG][CPL];
-  uint16_t sg[IPG][CPL], su[IPG][CPL];
+  // group scales of the item's row, two per lane (lane li: scales 2li, 2li+1;
+  // a row has d/G <= 32 of them); a chunk's scale is fetched from its lane
+  uint32_t sg[IPG], su[IPG];
   uint16_t lbg[IPG], lbu[IPG];  // shared items: element li of the row of LoRA B_gate / B_up
 };
 
@@ -352,18 +354,28 @@ __device__ __forceinline__ void gu_issue(GuRegs<CPL, IPG>& R, const LayerDev& Ly
       const int c = li + kLG * c2;
       R.wg[j][c2] = ldg(reinterpret_cast<const uint4*>(grow + 4 * c));
       R.wu[j][c2] = ldg(reinterpret_cast<const uint4*>(urow + 4 * c));
-      R.sg[j][c2] = ldg(gs + (int64_t)row * spr + ((32 * c) >> gsh));
-      R.su[j][c2] = ldg(us + (int64_t)row * spr + ((32 * c) >> gsh));
     }
+    // spr is even and rows start 4-byte aligned: one 4-byte load per lane
+    R.sg[j] = 2 * li < spr ? ldg(reinterpret_cast<const uint32_t*>(gs + (int64_t)row * spr) + li) : 0u;
+    R.su[j] = 2 * li < spr ? ldg(reinterpret_cast<const uint32_t*>(us + (int64_t)row * spr) + li) : 0u;
   }
 }
 
 // Gate and up dot products of the group's items. Routed items publish
 // silu(g) u at once; a shared item's sums are returned in sg_out / su_out
 // for gu_finish_shared (its LoRA terms need the layer's A products).
+// Scale (32 c) >> gsh of a row whose scales the lane group holds two per
+// lane (the group's lanes are active together).
+__device__ __forceinline__ float row_scale(uint32_t packed, int c, int gsh) {
+  const int idx = (32 * c) >> gsh;
+  const int base = (int)(threadIdx.x & 63) & ~(kLG - 1);
+  const uint32_t v = (uint32_t)__shfl((int)packed, base + (idx >> 1));
+  return h2f((uint16_t)((idx & 1) ? v >> 16 : v & 0xFFFFu));
+}
+
 template <int CPL, int IPG>
 __device__ __forceinline__ void gu_finish(const GuRegs<CPL, IPG>& R, const int64_t* ent_k,
-                                          int n_rt, const GuPlan& pl, int grp, int li,
+                                          int n_rt, const GuPlan& pl, int grp, int li, int gsh,
                                           const uint16_t* xperm, uint64_t* xg, uint32_t ep,
                                           float (&sg_out)[IPG], float (&su_out)[IPG]) {
 #pragma unroll
@@ -378,8 +390,9 @@ __device__ __forceinline__ void gu_finish(const GuRegs<CPL, IPG>& R, const int64
       for (int c2 = 0; c2 < CPL; ++c2) {
         f16x2 xr[16];
         load_xchunk(xperm, li + kLG * c2, xr);
-        ag += h2f(R.sg[j][c2]) * q4_dot32(R.wg[j][c2], xr);
-        au += h2f(R.su[j][c2]) * q4_dot32(R.wu[j][c2], xr);
+        const int c = li + kLG * c2;
+        ag += row_scale(R.sg[j], c, gsh) * q4_dot32(R.wg[j][c2], xr);
+        au += row_scale(R.su[j], c, gsh) * q4_dot32(R.wu[j][c2], xr);
       }
     }
     ag = group_sum<kLG>(ag);
@@ -746,7 +759,8 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
       if (!A.gu_loaded) gu_issue<CPL_D, IPG>(A.gu, Ly, dm, ms.eptr[step & 1], n_rt, pl, grp, li);
       vm_drained();  // gate/up rows, router and LoRA A rows have arrived
       float shg[IPG], shu[IPG];
-      gu_finish<CPL_D, IPG>(A.gu, ent_k, n_rt, pl, grp, li, xperm, xg, ep, shg, shu);
+      gu_finish<CPL_D, IPG>(A.gu, ent_k, n_rt, pl, grp, li, __builtin_ctz(dm.G), xperm, xg, ep,
+                            shg, shu);
       if (pl.ie > n_rt) {  // this workgroup owns rows of the shared expert
         const float* axgu = nullptr;
         if (r2) {
@@ -1075,7 +1089,7 @@ int span(int per, int block) { return per <= 0 ? 0 : (per - 1) / block + 2; }
 
 bool stack_supported(const Dims& dm) {
   if (dm.d % 512 || dm.I != kStackI || dm.K > 8 || dm.E > kMaxE) return false;
-  if (dm.G < 32 || (dm.G & (dm.G - 1)) || dm.d % dm.G) return false;
+  if (dm.G < 32 || (dm.G & (dm.G - 1)) || dm.d % dm.G || dm.d / dm.G > 32) return false;
   if (dm.Is != 0 && dm.Is != dm.I) return false;
   if (dm.r != 0 && dm.r != kRank) return false;
   if (dm.P % 128 || dm.P > 128 * kCPF) return false;
