@@ -395,3 +395,53 @@ def slot_policy(E, n_slots, K, slot_of, slot_expert, in_use, nxt):
     if n < 0:
         raise ValueError("slot pool overflow or bad id")
     return list(zip(ce[:n].tolist(), cs[:n].tolist()))
+
+
+def cache_policy(E, C, slot_of, owner, stamp, layer0, new_sets, tick):
+    """Cross-layer hot-expert cache of C bundles in HBM ([MW] §3.1 Executor
+    paths, "hot": LRU-resident hot experts; Table 1: a shared LRU of expert
+    bundles across layers; "Inside Edge0-35B", The Streaming Subsystem: a hit
+    skips the read from the slower tier). The pages give no replacement
+    detail beyond LRU; this is the reading used:
+
+      * slot_of int32 [L, E]: cache entry of (layer, expert), or -1;
+        owner int32 [C]: layer * E + expert held by an entry, or -1 (empty);
+        stamp int32 [C]: the last tick at which the entry was staged for a
+        set (-1: never). All three are mutated in place.
+      * staging the sets of layers layer0 .. layer0 + len(new_sets) - 1 at
+        tick T (the sets of token T): every id already cached is a hit and
+        its entry's stamp becomes T; the misses, in ascending (layer, id)
+        order, take the entries that are empty or were last staged before
+        T - 1 (the running token T - 1 and the sets already staged for T
+        keep theirs), least recently staged first, ties to the lower entry
+        index. The previous owner of a taken entry loses it.
+
+    Returns the copies as (layer - layer0, expert, entry), in miss order.
+    Raises ValueError on an id outside [0, E) or when too few entries are
+    free (nothing is changed then beyond the hit stamps)."""
+    sets = [np.asarray(s).astype(np.int64).ravel() for s in new_sets]
+    for s in sets:
+        if np.any(s < 0) or np.any(s >= E):
+            raise ValueError("expert id out of range")
+    misses = []
+    for i, s in enumerate(sets):
+        l = layer0 + i
+        for e in sorted(set(int(v) for v in s)):
+            c = int(slot_of[l, e])
+            if c >= 0:
+                stamp[c] = tick
+            else:
+                misses.append((l, e))
+    free = [c for c in range(C) if owner[c] < 0 or stamp[c] < tick - 1]
+    free.sort(key=lambda c: (int(stamp[c]), c))
+    if len(free) < len(misses):
+        raise ValueError("cache too small for the staged sets")
+    copies = []
+    for (l, e), c in zip(misses, free):
+        if owner[c] >= 0:
+            slot_of[owner[c] // E, owner[c] % E] = -1
+        owner[c] = l * E + e
+        slot_of[l, e] = c
+        stamp[c] = tick
+        copies.append((l - layer0, e, c))
+    return copies
