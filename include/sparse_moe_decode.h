@@ -340,6 +340,52 @@ int stage_experts_n(e0_stager* st, int32_t layer, int32_t n_layers, const int32_
 int stage_layer(e0_ctx* ctx, const void* host_layer, void* hbm_layer, void* stream,
                 void* done_event);
 
+/* ---------------------------------------------------------------------------
+ * Cross-layer hot-expert cache [MW §3.1 Executor paths, "hot": LRU-resident
+ * hot experts; MW Table 1: a shared LRU of expert bundles across layers
+ * (64 -> 1024 bundles); IE "The Streaming Subsystem": a hit skips the read
+ * from the slower tier]. One HBM pool of n_entries bundles serves every
+ * layer of a pinned host pool: a layer's slot table maps its ids to cache
+ * entries, so a hit costs no copy and an id evicted from one layer's set can
+ * be refilled for another layer.
+ *   host_pool  HOST pointer, pinned (hipHostMalloc), [n_layers][E] bundles.
+ *   hbm_cache  device pointer, [n_entries] bundles; an e0_experts view of it
+ *              (stride_q = stride_s = bundle bytes, count = n_entries) with
+ *              slot_of = slot_of[l] is layer l's routed pool.
+ *   slot_of    device int32 [n_layers][E]: cache entry of (layer, id), -1;
+ *   owner      device int32 [n_entries]: layer * E + id held, -1 (empty);
+ *   stamp      device int32 [n_entries]: tick of the last staging, -1.
+ *              The cache initialises all three to -1 and owns their
+ *              contents afterwards; the caller owns the memory.
+ * Replacement (the pages say LRU and give no detail; this is the library's
+ * reading): staging the sets of token T (tick T), ids already cached are
+ * hits and their entries get stamp T; the misses, in ascending (layer, id),
+ * take the entries that are empty or were last staged before T - 1 (the
+ * running token T - 1 and the sets already staged for T keep theirs), least
+ * recently staged first, ties to the lower entry index. n_entries >= 2 K
+ * n_layers guarantees a free entry. n_entries <= 4096. */
+typedef struct e0_cache e0_cache;
+
+int e0_cache_create(e0_ctx* ctx, const void* host_pool, int32_t n_layers, int32_t n_entries,
+                    void* hbm_cache, int32_t* slot_of, int32_t* owner, int32_t* stamp,
+                    e0_cache** out);
+void e0_cache_destroy(e0_cache* c);
+
+/* stage_experts_cached — stage the sets new_idx (device int32 [n_layers][K],
+ * row i for layer layer+i, n_layers <= 64) at tick `tick` (the index of the
+ * token that will use them, >= 0): runs the replacement on the device, then
+ * copies each missing bundle from the host pool over PCIe into its entry,
+ * all on side_stream, then records done_event (may be NULL). Ids out of
+ * range: nothing is staged and device_status reports E0_ERR_RANGE; too few
+ * free entries: only the hit stamps change, also reported as E0_ERR_RANGE.
+ * The copy kernel occupies at most 16 compute units, as stage_experts. */
+int stage_experts_cached(e0_cache* c, int32_t layer, int32_t n_layers, const int32_t* new_idx,
+                         int32_t tick, void* side_stream, void* done_event);
+
+/* Bundles copied from the host pool since the cache was created (a
+ * synchronous device read; -1 on error). */
+int64_t e0_cache_copies(e0_cache* c);
+
 /* Bundles copied by this stager's stage_experts calls since it was created
  * (observability: host-link bytes = count x e0_bundle_bytes). Synchronises
  * the device; E0_ERR_HIP if a copy fails. */

@@ -95,12 +95,18 @@ _lib.e0_stager_destroy.argtypes = [_p]
 _lib.stage_experts.argtypes = [_p, _i32, _p, _p, _p, _p]
 _lib.stage_experts_n.argtypes = [_p, _i32, _i32, _p, _p, _p, _p]
 _lib.stage_layer.argtypes = [_p, _p, _p, _p, _p]
+_lib.e0_cache_create.argtypes = [_p, _p, _i32, _i32, _p, _p, _p, _p, C.POINTER(_p)]
+_lib.e0_cache_destroy.argtypes = [_p]
+_lib.e0_cache_copies.argtypes = [_p]
+_lib.e0_cache_copies.restype = _i64
+_lib.stage_experts_cached.argtypes = [_p, _i32, _i32, _p, _i32, _p, _p]
 _lib.e0_stager_copies.argtypes = [_p, C.POINTER(C.c_int64)]
 
 EXPORTS = ["e0_create", "e0_destroy", "e0_last_error", "e0_device_status", "moe_int4_decode",
            "lora_delta", "prerouter_forward", "e0_model_create", "e0_model_destroy",
            "layer_step", "e0_bundle_bytes", "e0_stager_create", "e0_stager_destroy",
-           "stage_experts", "stage_experts_n", "e0_stager_copies", "stage_layer", "e0_model_set_path", "e0_model_set_grid", "e0_model_set_trace", "e0_model_trace_shape"]
+           "stage_experts", "stage_experts_n", "e0_stager_copies", "stage_layer",
+           "e0_cache_create", "e0_cache_destroy", "e0_cache_copies", "stage_experts_cached", "e0_model_set_path", "e0_model_set_grid", "e0_model_set_trace", "e0_model_trace_shape"]
 
 PATH_AUTO, PATH_PHASES, PATH_PERSISTENT = 0, 1, 2
 
@@ -400,6 +406,39 @@ def stage_experts(stager: Stager, layer: int, new_idx, in_use_idx=None, side_str
     ev = _event_handle(done_event, side_stream)
     _check(_lib.stage_experts(stager.handle, layer, _ptr(new_idx), _ptr(in_use_idx),
                               _stream(side_stream), ev))
+
+
+class HotCache:
+    """e0_cache: pinned host pool of expert bundles -> one cross-layer HBM
+    pool of n_entries bundles with least-recently-staged replacement."""
+
+    def __init__(self, ctx: Context, host_pool, n_layers: int, n_entries: int, hbm_cache,
+                 slot_of, owner, stamp):
+        h = _p()
+        _check(_lib.e0_cache_create(ctx.handle, _ptr(host_pool), n_layers, n_entries,
+                                    _ptr(hbm_cache), _ptr(slot_of), _ptr(owner), _ptr(stamp),
+                                    C.byref(h)))
+        self.handle = h.value
+        self.ctx = ctx
+        self.n_entries = n_entries
+        self._keep = (host_pool, hbm_cache, slot_of, owner, stamp)
+
+    def copies(self) -> int:
+        return int(_lib.e0_cache_copies(self.handle))
+
+    def close(self):
+        if self.handle:
+            _lib.e0_cache_destroy(self.handle)
+            self.handle = None
+
+
+def stage_experts_cached(cache: HotCache, layer: int, n_layers: int, new_idx, tick: int,
+                         side_stream=None, done_event=None):
+    """Stage the sets new_idx (device int32 [n_layers, K]) of layers
+    [layer, layer + n_layers) for token `tick` through the hot cache."""
+    ev = _event_handle(done_event, side_stream)
+    _check(_lib.stage_experts_cached(cache.handle, layer, n_layers, _ptr(new_idx), tick,
+                                     _stream(side_stream), ev))
 
 
 def stage_layer(ctx: Context, host_layer, hbm_layer, stream=None, done_event=None):

@@ -709,6 +709,112 @@ int stage_experts(e0_stager* st, int32_t layer, const int32_t* new_idx,
   return stage_experts_n(st, layer, 1, new_idx, in_use_idx, side_stream, done_event);
 }
 
+}  // extern "C"
+
+struct e0_cache {
+  e0_ctx* ctx;
+  const char* host_dev;  // device-side address of the pinned host pool
+  int32_t L, C;
+  char* hbm;
+  int32_t* slot_of;
+  int32_t* owner;
+  int32_t* stamp;
+  int64_t bundle;
+  int32_t* copy_list;  // [L][2*8]
+  int32_t* n_copies;   // [L]
+  unsigned long long* total;
+};
+
+extern "C" {
+
+int e0_cache_create(e0_ctx* ctx, const void* host_pool, int32_t n_layers, int32_t n_entries,
+                    void* hbm_cache, int32_t* slot_of, int32_t* owner, int32_t* stamp,
+                    e0_cache** out) {
+  if (!ctx || !host_pool || !hbm_cache || !slot_of || !owner || !stamp || !out)
+    return fail(E0_ERR_ARG, "e0_cache_create: null argument");
+  *out = nullptr;
+  const Dims& dm = ctx->dm;
+  if (n_layers < 1 || n_entries < 1 || n_entries > kMaxCacheEntries)
+    return fail(E0_ERR_ARG, "e0_cache_create: need n_layers >= 1 and 1 <= n_entries <= %d",
+                kMaxCacheEntries);
+  if (!aligned(host_pool, 16) || !aligned(hbm_cache, 16))
+    return fail(E0_ERR_ALIGN, "e0_cache_create: pools must be 16-byte aligned");
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, host_pool);
+  if (e != hipSuccess || attr.type != hipMemoryTypeHost) {
+    (void)hipGetLastError();
+    return fail(E0_ERR_ARG, "e0_cache_create: host pool is not pinned host memory");
+  }
+  void* dev = nullptr;
+  e = hipHostGetDevicePointer(&dev, const_cast<void*>(host_pool), 0);
+  if (e != hipSuccess || !dev) return hip_fail(e, "e0_cache_create: device address of pool");
+  e0_cache* c = new e0_cache();
+  c->ctx = ctx;
+  c->host_dev = (const char*)dev;
+  c->L = n_layers;
+  c->C = n_entries;
+  c->hbm = (char*)hbm_cache;
+  c->slot_of = slot_of;
+  c->owner = owner;
+  c->stamp = stamp;
+  c->bundle = e0_bundle_bytes(&ctx->spec);
+  c->copy_list = nullptr;
+  c->n_copies = nullptr;
+  c->total = nullptr;
+  e = hipMalloc(&c->copy_list, (size_t)n_layers * 16 * sizeof(int32_t));
+  if (e == hipSuccess) e = hipMalloc(&c->n_copies, (size_t)n_layers * sizeof(int32_t));
+  if (e == hipSuccess) e = hipMalloc(&c->total, sizeof(unsigned long long));
+  if (e == hipSuccess) e = hipMemset(c->total, 0, sizeof(unsigned long long));
+  if (e == hipSuccess) e = hipMemset(slot_of, 0xFF, (size_t)n_layers * dm.E * sizeof(int32_t));
+  if (e == hipSuccess) e = hipMemset(owner, 0xFF, (size_t)n_entries * sizeof(int32_t));
+  if (e == hipSuccess) e = hipMemset(stamp, 0xFF, (size_t)n_entries * sizeof(int32_t));
+  if (e == hipSuccess) e = hipMemset(c->n_copies, 0, (size_t)n_layers * sizeof(int32_t));
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    e0_cache_destroy(c);
+    return hip_fail(e, "e0_cache_create");
+  }
+  *out = c;
+  return E0_OK;
+}
+
+void e0_cache_destroy(e0_cache* c) {
+  if (!c) return;
+  (void)hipFree(c->copy_list);
+  (void)hipFree(c->n_copies);
+  (void)hipFree(c->total);
+  delete c;
+}
+
+int64_t e0_cache_copies(e0_cache* c) {
+  if (!c) return -1;
+  unsigned long long v = 0;
+  if (hipMemcpy(&v, c->total, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return -1;
+  return (int64_t)v;
+}
+
+int stage_experts_cached(e0_cache* c, int32_t layer, int32_t n_layers, const int32_t* new_idx,
+                         int32_t tick, void* side_stream, void* done_event) {
+  if (!c || !new_idx) return fail(E0_ERR_ARG, "stage_experts_cached: null argument");
+  if (n_layers < 1 || n_layers > kMaxCacheLayers || layer < 0 || layer + n_layers > c->L)
+    return fail(E0_ERR_ARG, "stage_experts_cached: layers [%d, %d) outside [0, %d) or more than %d",
+                layer, layer + n_layers, c->L, kMaxCacheLayers);
+  if (tick < 0) return fail(E0_ERR_ARG, "stage_experts_cached: negative tick");
+  const Dims& dm = c->ctx->dm;
+  hipStream_t ss = (hipStream_t)side_stream;
+  hipError_t e = launch_cache_stage(
+      dm.E, c->C, dm.K, layer, n_layers, tick, c->slot_of, c->owner, c->stamp, new_idx,
+      c->copy_list + (int64_t)layer * 16, c->n_copies + layer, c->total,
+      c->host_dev + (int64_t)layer * dm.E * c->bundle, (int64_t)dm.E * c->bundle, c->hbm,
+      c->bundle, c->ctx->s.flags, ss);
+  if (e != hipSuccess) return hip_fail(e, "stage_experts_cached");
+  if (done_event) {
+    e = hipEventRecord((hipEvent_t)done_event, ss);
+    if (e != hipSuccess) return hip_fail(e, "stage_experts_cached: event");
+  }
+  return E0_OK;
+}
+
 int stage_layer(e0_ctx* ctx, const void* host_layer, void* hbm_layer, void* stream,
                 void* done_event) {
   if (!ctx || !host_layer || !hbm_layer) return fail(E0_ERR_ARG, "stage_layer: null argument");

@@ -167,6 +167,14 @@ hipError_t launch_stack(const StackArgs& a, int grid, hipStream_t st);
 
 // Staging: device-side slot policy for one layer, then a gather-copy of the
 // missing bundles from (device-mapped) pinned host memory into HBM slots.
+// Cross-layer hot-expert cache (stage.hip): largest cache and layers per call.
+constexpr int kMaxCacheEntries = 4096;
+constexpr int kMaxCacheLayers = 64;
+hipError_t launch_cache_stage(int E, int C, int K, int layer0, int n_layers, int tick,
+                              int32_t* slot_of, int32_t* owner, int32_t* stamp,
+                              const int32_t* next, int32_t* copy_list, int32_t* n_copies,
+                              unsigned long long* total, const char* host, int64_t host_stride,
+                              char* cache, int64_t bundle, int32_t* flags, hipStream_t st);
 hipError_t launch_stage(int E, int n_slots, int K, int n_layers, int32_t* slot_of,
                         int32_t* slot_expert, const int32_t* in_use, const int32_t* next,
                         int32_t* copy_list, int32_t* n_copies, unsigned long long* total,

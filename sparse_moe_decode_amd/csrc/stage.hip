@@ -116,7 +116,155 @@ __global__ __launch_bounds__(kCopyThreads) void k_stage_copy(
   }
 }
 
+constexpr int kCacheThreads = 1024;
+
+// Cross-layer hot-expert cache policy [MW §3.1 Executor paths, "hot":
+// LRU-resident experts; Table 1: a shared LRU of expert bundles across
+// layers; IE "The Streaming Subsystem": a hit skips the read], one workgroup
+// for all layers of the call. State: slot_of [L][E] (cache entry of
+// (layer, id), or -1), owner [C] (layer * E + id, or -1 for empty), stamp
+// [C] (tick of the entry's last staging, -1 never). Staging the sets of
+// layers layer0 .. layer0 + n_layers - 1 at tick T: ids already cached are
+// hits and their entries' stamp becomes T; the misses, in ascending
+// (layer, id), take the entries that are empty or were last staged before
+// T - 1 (the running token and the sets already staged for T keep theirs),
+// least recently staged first, ties to the lower index; the previous owner
+// loses the entry. The entry table is worked on in LDS (one bitonic sort of
+// the free entries by (stamp, index)) and written back at the end. Writes
+// the per-layer (id, entry) copy lists. With too few free entries nothing
+// but the hit stamps changes and the range flag gets bit 2.
+__global__ __launch_bounds__(kCacheThreads) void k_cache_policy(
+    int E, int C, int K, int layer0, int n_layers, int tick, int32_t* slot_of, int32_t* owner,
+    int32_t* stamp, const int32_t* next, int32_t* copy_list, int32_t* n_copies,
+    unsigned long long* total, int32_t* flags) {
+  __shared__ uint64_t key[kMaxCacheEntries];
+  __shared__ int32_t own_l[kMaxCacheEntries], stm_l[kMaxCacheEntries];
+  __shared__ int32_t mis[kMaxCacheLayers * 8];
+  __shared__ int32_t nmis[kMaxCacheLayers], moff[kMaxCacheLayers + 1];
+  __shared__ int bad;
+  const int t = threadIdx.x, nt = blockDim.x, nk = n_layers * K;
+  if (t == 0) bad = 0;
+  for (int c = t; c < C; c += nt) {
+    own_l[c] = owner[c];
+    stm_l[c] = stamp[c];
+  }
+  __syncthreads();
+  for (int i = t; i < nk; i += nt)
+    if (next[i] < 0 || next[i] >= E) bad = 1;
+  __syncthreads();
+  if (bad) {
+    if (t == 0) atomicOr(&flags[FLAG_RANGE], 1);
+    for (int l = t; l < n_layers; l += nt) n_copies[l] = 0;
+    return;
+  }
+  // hits: refresh the entry's stamp (every writer stores the same value)
+  for (int i = t; i < nk; i += nt) {
+    const int c = slot_of[(int64_t)(layer0 + i / K) * E + next[i]];
+    if (c >= 0) stm_l[c] = tick;
+  }
+  // misses of each layer, ascending and without repeats (a thread per layer)
+  if (t < n_layers) {
+    const int64_t row = (int64_t)(layer0 + t) * E;
+    int m[8];
+    int nm = 0;
+    for (int k = 0; k < K; ++k) {
+      const int e = next[t * K + k];
+      if (slot_of[row + e] >= 0) continue;
+      bool dup = false;
+      for (int i = 0; i < nm; ++i) dup |= (m[i] == e);
+      if (dup) continue;
+      int i = nm++;
+      while (i > 0 && m[i - 1] > e) {
+        m[i] = m[i - 1];
+        --i;
+      }
+      m[i] = e;
+    }
+    for (int i = 0; i < nm; ++i) mis[t * 8 + i] = m[i];
+    nmis[t] = nm;
+  }
+  __syncthreads();
+  if (t == 0) {
+    moff[0] = 0;
+    for (int l = 0; l < n_layers; ++l) moff[l + 1] = moff[l] + nmis[l];
+  }
+  // free entries keyed by (stamp, index) (stamp + 1 >= 0); others sort last
+  int P = 1;
+  while (P < C) P <<= 1;
+  for (int c = t; c < P; c += nt) {
+    uint64_t kk = ~0ull;
+    if (c < C && (own_l[c] < 0 || stm_l[c] < tick - 1))
+      kk = ((uint64_t)(uint32_t)(stm_l[c] + 1) << 32) | (uint32_t)c;
+    key[c] = kk;
+  }
+  __syncthreads();
+  for (int k = 2; k <= P; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = t; i < P; i += nt) {
+        const int x = i ^ j;
+        if (x > i) {
+          const uint64_t a = key[i], b = key[x];
+          if ((a > b) == ((i & k) == 0)) {
+            key[i] = b;
+            key[x] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  const int m_total = moff[n_layers];
+  const bool overflow = m_total > C || (m_total > 0 && key[m_total - 1] == ~0ull);
+  if (!overflow) {
+    for (int j = t; j < m_total; j += nt) {
+      int li = 0;
+      while (moff[li + 1] <= j) ++li;
+      const int r = j - moff[li], e = mis[li * 8 + r];
+      const int c = (int)(uint32_t)key[j];
+      const int old = own_l[c];
+      if (old >= 0) slot_of[old] = -1;  // old = layer * E + id
+      own_l[c] = (layer0 + li) * E + e;
+      stm_l[c] = tick;
+      slot_of[(int64_t)(layer0 + li) * E + e] = c;
+      copy_list[li * 16 + 2 * r] = e;
+      copy_list[li * 16 + 2 * r + 1] = c;
+    }
+  }
+  for (int l = t; l < n_layers; l += nt) n_copies[l] = overflow ? 0 : nmis[l];
+  if (t == 0) {
+    if (overflow)
+      atomicOr(&flags[FLAG_RANGE], 2);
+    else
+      atomicAdd(total, (unsigned long long)m_total);
+  }
+  __syncthreads();
+  for (int c = t; c < C; c += nt) {
+    owner[c] = own_l[c];
+    stamp[c] = stm_l[c];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_cache_stage(int E, int C, int K, int layer0, int n_layers, int tick,
+                              int32_t* slot_of, int32_t* owner, int32_t* stamp,
+                              const int32_t* next, int32_t* copy_list, int32_t* n_copies,
+                              unsigned long long* total, const char* host, int64_t host_stride,
+                              char* cache, int64_t bundle, int32_t* flags, hipStream_t st) {
+  if (E > kMaxE || C < 1 || C > kMaxCacheEntries || K > 8 || n_layers < 1 ||
+      n_layers > kMaxCacheLayers || bundle % 16)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_cache_policy, dim3(1), dim3(kCacheThreads), 0, st, E, C, K, layer0,
+                     n_layers, tick, slot_of, owner, stamp, next, copy_list, n_copies, total,
+                     flags);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // copies: host pool of the call's layers -> cache entries (one pool, no
+  // per-layer stride on the device side)
+  hipLaunchKernelGGL(k_stage_copy, dim3(kCopyBlocks), dim3(kCopyThreads), 0, st, host,
+                     host_stride, cache, (int64_t)0, bundle, n_layers, copy_list, n_copies);
+  return hipGetLastError();
+}
 
 hipError_t launch_stage(int E, int n_slots, int K, int n_layers, int32_t* slot_of,
                         int32_t* slot_expert, const int32_t* in_use, const int32_t* next,

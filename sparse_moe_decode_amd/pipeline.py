@@ -40,8 +40,10 @@ from . import api
 
 class StagedStack:
     """Layers `cons` (a contiguous range) read their routed experts through
-    slot pools filled by `stager` (stager layer i = cons[i]); the rest of
-    `model`'s layers are resident. `state` is the decode state of the stack.
+    slot pools filled by `stager` (stager layer i = cons[i]), or through the
+    entries of a cross-layer hot cache when `stager` is an api.HotCache; the
+    rest of `model`'s layers are resident. `state` is the decode state of the
+    stack.
 
     group: predicted layers per launch. Layer m's prediction comes from head
     m-1, so the staging of a group for token t+1 waits for the launch of token
@@ -86,9 +88,15 @@ class StagedStack:
         st = self.state
         if not after_token:
             self.side.wait_stream(self.main)
+        cached = isinstance(self.stager, api.HotCache)
         for j, (g0, g1) in enumerate(self.groups):
             if after_token:
                 self.side.wait_event(self._source(j))
+            if cached:  # the cache keeps the running token's entries by their stamps
+                api.stage_experts_cached(self.stager, g0 - self.cons[0], g1 - g0,
+                                         st.route_idx[t & 1][g0:g1], t, side_stream=self.side,
+                                         done_event=self.staged[j])
+                continue
             in_use = self.sets[(t - 1) & 1][g0:g1] if t > 0 else None
             api.stage_experts_n(self.stager, g0 - self.cons[0], g1 - g0, st.route_idx[t & 1][g0:g1],
                                 in_use, side_stream=self.side, done_event=self.staged[j])

@@ -128,3 +128,97 @@ def test_staged_stack_matches_oracle(api, orc, tier, T, reserve, group):
     stager.close()
     model.close()
     ctx.close()
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("tier,T,C,group", [("35b", 5, 24, 1), ("8b", 4, 64, 2)])
+def test_staged_stack_through_hot_cache(api, orc, tier, T, C, group):
+    """The predicted layers read their experts from one cross-layer hot cache
+    of C entries (C = 2K x 3 layers is the smallest that always fits at
+    35B). Per token: every layer-step matches the oracle; the cache's tables
+    equal the oracle's cache policy run on the same sets, groups and ticks;
+    every owned entry holds its bundle; the copy count matches."""
+    import torch
+    from sparse_moe_decode_amd import pipeline
+    from sparse_moe_decode_amd import workloads as wl
+    dm = synth.dims(tier)
+    E, K, L = dm["E"], dm["K"], len(ROLES)
+    seed = 43
+    cons = [l for l in range(L) if not ROLES[l]["router"]]
+    ci = {l: i for i, l in enumerate(cons)}
+    ctx = api.Context(dm, max_tokens=1)
+    bundle = ctx.bundle_bytes()
+    host_pool = torch.empty((len(cons), E, bundle), dtype=torch.uint8, pin_memory=True)
+    cache = torch.zeros((C, bundle), dtype=torch.uint8, device="cuda")
+    slot_of = torch.empty((len(cons), E), dtype=torch.int32, device="cuda")
+    owner = torch.empty(C, dtype=torch.int32, device="cuda")
+    stamp = torch.empty(C, dtype=torch.int32, device="cuda")
+    view = api.bundle_view(cache.data_ptr(), dm)
+    layers, keep = [], {}
+    for l, role in enumerate(ROLES):
+        announce("upload", tier, f"layer {l}/{L}")
+        lw = synth.layer(seed, l, dm, role, zero_mean=True)
+        keep[l] = lw
+        lay = dict(shared=wl.tree_to_dev(lw["shared"]), attn=dev(lw["attn"]),
+                   router=None if lw["router"] is None else dev(lw["router"]),
+                   router_bias=None if lw["router_bias"] is None else dev(lw["router_bias"]),
+                   head=wl.tree_to_dev(lw["head"]))
+        if l in ci:
+            host_pool[ci[l]].copy_(torch.from_numpy(api.pack_bundles(lw["routed"], dm)))
+            lay.update(routed=view, count=C, stride_q=bundle, stride_s=bundle,
+                       slot_of=slot_of[ci[l]])
+        else:
+            lay["routed"] = wl.tree_to_dev(lw["routed"])
+        layers.append(lay)
+    host_dev = host_pool.to("cuda")
+    hc = api.HotCache(ctx, host_pool, len(cons), C, cache, slot_of, owner, stamp)
+    model = api.Model(ctx, layers)
+    state = api.State(dm, L)
+    idx0, w0 = wl.initial_routing(tier, seed, L)
+    state.route_idx[0].copy_(torch.from_numpy(idx0))
+    state.route_w[0].copy_(torch.from_numpy(w0))
+    toks = wl.token_inputs(tier, seed, T, rho=0.5)
+    checker = StackChecker(orc, tier, seed, ROLES, list(range(L)), keep, zero_mean=True)
+    pipe = pipeline.StagedStack(ctx, model, state, hc, cons, L, group=group)
+    so = np.full((len(cons), E), -1, np.int32)
+    ow = np.full(C, -1, np.int32)
+    st = np.full(C, -1, np.int32)
+    copies = 0
+
+    def oracle_stage(routes, tick):
+        nonlocal copies
+        for g0, g1 in pipe.groups:
+            copies += len(orc.cache_policy(E, C, so, ow, st, g0 - cons[0],
+                                           [routes[l] for l in range(g0, g1)], tick))
+
+    oracle_stage(idx0, 0)
+    pipe.stage(0, after_token=False)
+    prev_exec = None
+    h = torch.zeros((L + 1, dm["d"]), dtype=torch.float16, device="cuda")
+    for t in range(T):
+        announce("cached layer_step", tier, f"C={C} group={group}", f"token {t}")
+        h[0].copy_(torch.from_numpy(toks[t]))
+        pipe.run_token(t, h)
+        torch.cuda.synchronize()
+        assert api.device_status(ctx) == 0
+        cur, nxt = t & 1, (t + 1) & 1
+        exec_idx = host(state.exec_idx[cur]).copy()
+        route_nxt = host(state.route_idx[nxt]).copy()
+        checker.check(t, host(h).copy(), host(state.x_trace).copy(), exec_idx,
+                      host(state.exec_w[cur]).copy(), prev_exec, host(state.route_idx[cur]).copy(),
+                      host(state.route_w[cur]).copy(), route_nxt,
+                      host(state.route_w[nxt]).copy(), host(state.head_logits).copy())
+        prev_exec = exec_idx
+        oracle_stage(route_nxt, t + 1)
+        assert np.array_equal(host(slot_of), so), f"slot_of after token {t}"
+        assert np.array_equal(host(owner), ow), f"owner after token {t}"
+        assert np.array_equal(host(stamp), st), f"stamp after token {t}"
+        for c in np.nonzero(ow >= 0)[0]:
+            i, e = divmod(int(ow[c]), E)
+            assert torch.equal(cache[c], host_dev[i, e]), f"t={t} entry {c}"
+    assert hc.copies() == copies
+    print(f"{tier} cached L={L} C={C}: {checker.steps} layer-steps checked, worst error ratio "
+          f"{checker.worst:.3f}, {copies} bundle copies")
+    hc.close()
+    model.close()
+    ctx.close()
