@@ -377,6 +377,12 @@ def run_staged(args):
     slots = torch.zeros((len(cons), n_slots, bundle), dtype=torch.uint8, device="cuda")
     slot_of = torch.empty((len(cons), E), dtype=torch.int32, device="cuda")
     slot_expert = torch.empty((len(cons), n_slots), dtype=torch.int32, device="cuda")
+    C = args.cache_entries
+    if C:  # one cross-layer hot cache instead of 2K slots per layer
+        cache = torch.zeros((C, bundle), dtype=torch.uint8, device="cuda")
+        c_slot_of = torch.empty((len(cons), E), dtype=torch.int32, device="cuda")
+        c_owner = torch.empty(C, dtype=torch.int32, device="cuda")
+        c_stamp = torch.empty(C, dtype=torch.int32, device="cuda")
     layers = []
     t_build = time.perf_counter()
     for l, role in enumerate(roles):
@@ -388,8 +394,12 @@ def run_staged(args):
                    head=wl.tree_to_dev(lw["head"]))
         if l in ci:
             host_pool[ci[l]].copy_(torch.from_numpy(api.pack_bundles(lw["routed"], dm)))
-            lay.update(routed=api.bundle_view(slots[ci[l]].data_ptr(), dm), count=n_slots,
-                       stride_q=bundle, stride_s=bundle, slot_of=slot_of[ci[l]])
+            if C:
+                lay.update(routed=api.bundle_view(cache.data_ptr(), dm), count=C,
+                           stride_q=bundle, stride_s=bundle, slot_of=c_slot_of[ci[l]])
+            else:
+                lay.update(routed=api.bundle_view(slots[ci[l]].data_ptr(), dm), count=n_slots,
+                           stride_q=bundle, stride_s=bundle, slot_of=slot_of[ci[l]])
         else:
             lay["routed"] = wl.tree_to_dev(lw["routed"])
         layers.append(lay)
@@ -398,6 +408,10 @@ def run_staged(args):
     t_build = time.perf_counter() - t_build
     stager = api.Stager(ctx, host_pool, len(cons), n_slots, slots, slot_of, slot_expert)
     link = host_link_probes(api, stager, host_pool, bundle, dm, len(cons), args.seed)
+    if C:  # the slot stager served the link probes only
+        stager.close()
+        del slots
+        stager = api.HotCache(ctx, host_pool, len(cons), C, cache, c_slot_of, c_owner, c_stamp)
     model = api.Model(ctx, layers)
     state = api.State(dm, L, head_logits=False, x_trace=False)
     idx0, w0 = wl.initial_routing(tier, args.seed, L)
@@ -436,9 +450,15 @@ def run_staged(args):
                         for t in range(1, len(st))], np.float64)
     mean_new = float(new_ids.mean()) if new_ids.size else float("nan")
     print(json.dumps({
-        "workload": "35B-tier host-staged decode stack, batch 1: experts of the 32 predicted "
-                    "layers streamed from pinned host memory into 2K HBM slots per layer by "
-                    "stage_experts on a side stream; router layers resident",
+        "workload": ("35B-tier host-staged decode stack, batch 1: experts of the 32 predicted "
+                     "layers streamed from pinned host memory " +
+                     (f"through one cross-layer HBM hot cache of {C} bundles "
+                      "(stage_experts_cached)" if C else
+                      "into 2K HBM slots per layer (stage_experts)") +
+                     " on a side stream; router layers resident"),
+        "cache_entries": C or None,
+        "staged_ids_per_token": len(cons) * K,
+        "cache_hit_rate": (round(1.0 - copied / (len(cons) * K), 4) if C else None),
         "steps": args.steps, "warmup": args.warmup, "rho": args.rho,
         "reserved_cus_for_staging": args.reserve_cus, "layers_per_launch": args.group,
         "ms_per_token": round(ms, 4), "tokens_per_s": round(1000.0 / ms, 2),
@@ -574,6 +594,9 @@ def main():
                     help="staged workload: compute units left to the staging copies")
     ap.add_argument("--group", type=int, default=8,
                     help="staged workload: predicted layers per launch")
+    ap.add_argument("--cache-entries", type=int, default=0,
+                    help="staged workload: stage through one cross-layer hot cache of this "
+                         "many bundles (0: 2K slots per layer)")
     ap.add_argument("--chunk-k", type=int, default=0, choices=[0, 2, 4, 8],
                     help="chunk workload: only this top-K (0 = 2, 4 and 8)")
     ap.add_argument("--prefill-b", type=int, default=3072,
