@@ -52,7 +52,8 @@ enum {
   E0_ERR_HIP = -4,    /* a HIP runtime call failed */
   E0_ERR_RANGE = -5,  /* an expert id read on the device was out of range */
   E0_ERR_SYNC = -6,   /* a device-side wait hit its spin limit */
-  E0_ERR_STATE = -7   /* object used in a state it does not allow */
+  E0_ERR_STATE = -7,  /* object used in a state it does not allow */
+  E0_ERR_IO = -8      /* a file could not be opened or read */
 };
 
 enum { E0_ROUTER_SOFTMAX_TOPK = 0, E0_ROUTER_SIGMOID_GROUP = 1 };
@@ -385,6 +386,35 @@ int stage_experts_cached(e0_cache* c, int32_t layer, int32_t n_layers, const int
 /* Bundles copied from the host pool since the cache was created (a
  * synchronous device read; -1 on error). */
 int64_t e0_cache_copies(e0_cache* c);
+
+/* ---------------------------------------------------------------------------
+ * Storage tier under the pinned pool [MW §3.1: expert weights stay on SSD
+ * as per-layer stacked files and stream on demand by byte range; §5.3:
+ * reads issued one token ahead move the load time off the critical path].
+ * Layer l's file (paths[l]) holds its E bundles back to back, bundle e at
+ * byte e * bundle_bytes (the bundle layout above). io_threads host threads
+ * serve the reads; direct != 0 opens the files with O_DIRECT (page cache
+ * bypassed: bundle_bytes and every destination 4096-byte aligned), so every
+ * read reaches the device. Host code only: no GPU call.
+ *   e0_store_read   queue one pread per id of `ids` (host int32 [n]) into
+ *                   dst[i] (host pointers, typically into a pinned pool);
+ *                   returns at once with a ticket.
+ *   e0_store_wait   block until the ticket's reads are done; blocked_s (may
+ *                   be NULL) gets the time this call waited, read_s the time
+ *                   from queueing to the last read's completion. E0_ERR_IO if
+ *                   any read failed; a ticket is waited on once.
+ *   e0_store_bytes  bytes read since opening.
+ * Errors: E0_ERR_ARG (bad argument), E0_ERR_ALIGN (O_DIRECT alignment),
+ * E0_ERR_RANGE (id outside [0, E)), E0_ERR_IO (open or read failed). */
+typedef struct e0_store e0_store;
+
+int e0_store_open(const char* const* paths, int32_t n_layers, int32_t n_experts,
+                  int64_t bundle_bytes, int32_t io_threads, int32_t direct, e0_store** out);
+void e0_store_close(e0_store* s);
+int e0_store_read(e0_store* s, int32_t layer, const int32_t* ids, int32_t n, void* const* dst,
+                  int64_t* ticket);
+int e0_store_wait(e0_store* s, int64_t ticket, double* blocked_s, double* read_s);
+int64_t e0_store_bytes(e0_store* s);
 
 /* Bundles copied by this stager's stage_experts calls since it was created
  * (observability: host-link bytes = count x e0_bundle_bytes). Synchronises

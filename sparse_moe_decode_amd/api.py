@@ -22,8 +22,11 @@ if not os.path.exists(LIB_PATH):
 _lib = C.CDLL(LIB_PATH)
 
 E0_OK = 0
+E0_ERR_ALIGN = -3
 E0_ERR_RANGE = -5
 E0_ERR_SYNC = -6
+E0_ERR_STATE = -7
+E0_ERR_IO = -8
 ROUTER_SOFTMAX_TOPK = 0
 ROUTER_SIGMOID_GROUP = 1
 
@@ -100,13 +103,20 @@ _lib.e0_cache_destroy.argtypes = [_p]
 _lib.e0_cache_copies.argtypes = [_p]
 _lib.e0_cache_copies.restype = _i64
 _lib.stage_experts_cached.argtypes = [_p, _i32, _i32, _p, _i32, _p, _p]
+_lib.e0_store_open.argtypes = [C.POINTER(C.c_char_p), _i32, _i32, _i64, _i32, _i32, C.POINTER(_p)]
+_lib.e0_store_close.argtypes = [_p]
+_lib.e0_store_read.argtypes = [_p, _i32, C.POINTER(_i32), _i32, C.POINTER(_p), C.POINTER(_i64)]
+_lib.e0_store_wait.argtypes = [_p, _i64, C.POINTER(C.c_double), C.POINTER(C.c_double)]
+_lib.e0_store_bytes.argtypes = [_p]
+_lib.e0_store_bytes.restype = _i64
 _lib.e0_stager_copies.argtypes = [_p, C.POINTER(C.c_int64)]
 
 EXPORTS = ["e0_create", "e0_destroy", "e0_last_error", "e0_device_status", "moe_int4_decode",
            "lora_delta", "prerouter_forward", "e0_model_create", "e0_model_destroy",
            "layer_step", "e0_bundle_bytes", "e0_stager_create", "e0_stager_destroy",
            "stage_experts", "stage_experts_n", "e0_stager_copies", "stage_layer",
-           "e0_cache_create", "e0_cache_destroy", "e0_cache_copies", "stage_experts_cached", "e0_model_set_path", "e0_model_set_grid", "e0_model_set_trace", "e0_model_trace_shape"]
+           "e0_cache_create", "e0_cache_destroy", "e0_cache_copies", "stage_experts_cached",
+           "e0_store_open", "e0_store_close", "e0_store_read", "e0_store_wait", "e0_store_bytes", "e0_model_set_path", "e0_model_set_grid", "e0_model_set_trace", "e0_model_trace_shape"]
 
 PATH_AUTO, PATH_PHASES, PATH_PERSISTENT = 0, 1, 2
 
@@ -439,6 +449,43 @@ def stage_experts_cached(cache: HotCache, layer: int, n_layers: int, new_idx, ti
     ev = _event_handle(done_event, side_stream)
     _check(_lib.stage_experts_cached(cache.handle, layer, n_layers, _ptr(new_idx), tick,
                                      _stream(side_stream), ev))
+
+
+class Store:
+    """e0_store: per-layer stacked bundle files read by byte range on a pool
+    of host I/O threads (host only, no GPU)."""
+
+    def __init__(self, paths: list[str], n_experts: int, bundle_bytes: int, io_threads: int = 16,
+                 direct: bool = True):
+        arr = (C.c_char_p * len(paths))(*[p.encode() for p in paths])
+        h = _p()
+        _check(_lib.e0_store_open(arr, len(paths), n_experts, bundle_bytes, io_threads,
+                                  1 if direct else 0, C.byref(h)))
+        self.handle = h.value
+
+    def read(self, layer: int, ids, dst_ptrs) -> int:
+        """Queue reads of bundles `ids` of `layer` into host addresses
+        dst_ptrs; returns a ticket."""
+        n = len(ids)
+        ida = (_i32 * max(n, 1))(*[int(i) for i in ids])
+        dsa = (_p * max(n, 1))(*[int(p) for p in dst_ptrs])
+        tk = _i64()
+        _check(_lib.e0_store_read(self.handle, layer, ida, n, dsa, C.byref(tk)))
+        return tk.value
+
+    def wait(self, ticket: int):
+        """Block until the ticket's reads are done; returns (blocked_s, read_s)."""
+        b, r = C.c_double(), C.c_double()
+        _check(_lib.e0_store_wait(self.handle, ticket, C.byref(b), C.byref(r)))
+        return b.value, r.value
+
+    def bytes_read(self) -> int:
+        return int(_lib.e0_store_bytes(self.handle))
+
+    def close(self):
+        if self.handle:
+            _lib.e0_store_close(self.handle)
+            self.handle = None
 
 
 def stage_layer(ctx: Context, host_layer, hbm_layer, stream=None, done_event=None):

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libsmd.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["abi.hip", "kernels.hip", "stage.hip", "stack.hip", "batched.hip"]
+SOURCES = ["abi.hip", "kernels.hip", "stage.hip", "stack.hip", "batched.hip", "store.cpp"]
 ARCH = os.environ.get("SMD_OFFLOAD_ARCH", "gfx950")
 
 # Packed-FP32 instructions are disabled for all device code.
@@ -49,7 +49,7 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = OUT + ".tmp"
-    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")

@@ -19,7 +19,7 @@ using namespace smd;
 namespace {
 
 // Token count from which moe_int4_decode groups tokens by expert and runs
-// grouped int4 GEMMs on MFMA (chunks of up to 32 tokens).
+// grouped int4 GEMMs on MFMA (tiles of up to 32 or 64 of an expert's tokens).
 constexpr int kBatchedMin = 16;
 
 thread_local std::string g_err = "no error";
@@ -37,6 +37,13 @@ int fail(int code, const char* fmt, ...) {
 int hip_fail(hipError_t e, const char* what) {
   return fail(E0_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
+
+}  // namespace
+
+// The error channel of e0_last_error for the other translation units.
+int smd_report(int code, const char* msg) { return fail(code, "%s", msg); }
+
+namespace {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
