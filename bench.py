@@ -474,6 +474,115 @@ def run_staged(args):
     stager.close()
 
 
+def run_storage(args):
+    """Host-staged 35B stack at batch 1 whose pinned pool is filled from
+    per-layer stacked files on local disk (pipeline.StorageStagedStack, the
+    pages' SSD tier): the routed experts of the 32 predicted layers are
+    written to one file per layer, the pool starts empty, and every bundle a
+    staged set needs that is neither in the previous token's set nor in the
+    RAM tier is read with O_DIRECT. Arms: prefetch (reads queued as soon as a
+    group's predictions exist, one token ahead) and ondemand (each group's
+    reads queued and waited for just before it runs; --group 1 for per-layer
+    loads). Reported: tokens/s, host time blocked on reads per token, disk
+    bytes and rate, and a least-squares fit of each load's read time against
+    its bundle count."""
+    import tempfile
+    import torch
+    from sparse_moe_decode_amd import api, pipeline, synth
+    from sparse_moe_decode_amd import workloads as wl
+    tier = "35b"
+    dm = synth.dims(tier)
+    roles = synth.stack_roles(tier)
+    L = len(roles)
+    K, E = dm["K"], dm["E"]
+    n_slots = 2 * K
+    cons = [l for l in range(L) if not roles[l]["router"]]
+    ci = {l: i for i, l in enumerate(cons)}
+    ctx = api.Context(dm, max_tokens=1)
+    bundle = ctx.bundle_bytes()
+    host_pool = torch.zeros((len(cons), E, bundle), dtype=torch.uint8, pin_memory=True)
+    slots = torch.zeros((len(cons), n_slots, bundle), dtype=torch.uint8, device="cuda")
+    slot_of = torch.empty((len(cons), E), dtype=torch.int32, device="cuda")
+    slot_expert = torch.empty((len(cons), n_slots), dtype=torch.int32, device="cuda")
+    tmpdir = tempfile.mkdtemp(prefix="smd_store_", dir=args.store_dir)
+    paths = [os.path.join(tmpdir, f"layer{i:02d}.bin") for i in range(len(cons))]
+    layers = []
+    t_build = time.perf_counter()
+    for l, role in enumerate(roles):
+        lw = synth.layer(args.seed, l, dm, role, zero_mean=True)
+        lay = dict(shared=wl.tree_to_dev(lw["shared"]), attn=wl.to_dev(lw["attn"]),
+                   router=None if lw["router"] is None else wl.to_dev(lw["router"]),
+                   router_bias=(None if lw["router_bias"] is None
+                                else wl.to_dev(lw["router_bias"])),
+                   head=wl.tree_to_dev(lw["head"]))
+        if l in ci:
+            with open(paths[ci[l]], "wb") as f:
+                api.pack_bundles(lw["routed"], dm).tofile(f)
+                f.flush()
+                os.fsync(f.fileno())
+            lay.update(routed=api.bundle_view(slots[ci[l]].data_ptr(), dm), count=n_slots,
+                       stride_q=bundle, stride_s=bundle, slot_of=slot_of[ci[l]])
+        else:
+            lay["routed"] = wl.tree_to_dev(lw["routed"])
+        layers.append(lay)
+        del lw
+        print(f"[bench] storage workload: layer {l + 1}/{L} built", file=sys.stderr, flush=True)
+    t_build = time.perf_counter() - t_build
+    store = api.Store(paths, E, bundle, io_threads=args.io_threads, direct=True)
+    stager = api.Stager(ctx, host_pool, len(cons), n_slots, slots, slot_of, slot_expert)
+    model = api.Model(ctx, layers)
+    state = api.State(dm, L, head_logits=False, x_trace=False)
+    idx0, w0 = wl.initial_routing(tier, args.seed, L)
+    state.route_idx[0].copy_(torch.from_numpy(idx0))
+    state.route_w[0].copy_(torch.from_numpy(w0))
+    T = args.warmup + args.steps
+    toks = wl.token_inputs(tier, args.seed, T, args.rho)
+    h_all = torch.zeros((T, L + 1, dm["d"]), dtype=torch.float16, device="cuda")
+    h_all[:, 0].copy_(torch.from_numpy(toks))
+    pipe = pipeline.StorageStagedStack(ctx, model, state, stager, cons, L, store, host_pool,
+                                       ram_bundles=args.ram_bundles, arm=args.arm,
+                                       reserve_cus=args.reserve_cus, group=args.group)
+    pipe.stage(0, after_token=False)
+    for t in range(args.warmup):
+        pipe.run_token(t, h_all[t])
+    torch.cuda.synchronize()
+    assert api.device_status(ctx) == 0
+    b0, bytes0, loads0 = pipe.blocked_s, store.bytes_read(), len(pipe.loads)
+    t0 = time.perf_counter()
+    for t in range(args.warmup, T):
+        pipe.run_token(t, h_all[t])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert api.device_status(ctx) == 0
+    ms = wall * 1e3 / args.steps
+    nbytes = (store.bytes_read() - bytes0) / args.steps
+    loads = np.array(pipe.loads[loads0:], np.float64)
+    fit = None
+    if len(loads) >= 3 and np.ptp(loads[:, 0]) > 0:
+        A = np.stack([np.ones(len(loads)), loads[:, 0]], axis=1)
+        coef, *_ = np.linalg.lstsq(A, loads[:, 1] * 1e3, rcond=None)
+        fit = {"ms_per_load": round(float(coef[0]), 3), "ms_per_bundle": round(float(coef[1]), 4),
+               "loads": int(len(loads)), "mean_bundles_per_load": round(float(loads[:, 0].mean()), 2)}
+    print(json.dumps({
+        "workload": "35B-tier decode stack, batch 1, experts of the 32 predicted layers read "
+                    "from per-layer stacked files (O_DIRECT) into the pinned pool, then staged "
+                    "into 2K HBM slots per layer",
+        "arm": args.arm, "group": args.group, "ram_bundles": args.ram_bundles,
+        "io_threads": args.io_threads, "rho": args.rho, "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_token": round(ms, 3), "tokens_per_s": round(1e3 / ms, 2),
+        "blocked_ms_per_token": round((pipe.blocked_s - b0) * 1e3 / args.steps, 3),
+        "disk_bytes_per_token": int(nbytes),
+        "bundles_read_per_token": round(nbytes / bundle, 2),
+        "disk_gb_per_s": round(nbytes / (ms * 1e-3) / 1e9, 2),
+        "load_cost_fit": fit, "bundle_bytes": bundle, "build_s": round(t_build, 1)}))
+    store.close()
+    stager.close()
+    for p in paths:
+        os.remove(p)
+    os.rmdir(tmpdir)
+
+
 def layer_step_bytes(dm: dict) -> int:
     """Algorithmic weight bytes of one predicted layer-step with a head: K
     routed experts + shared expert + LoRA + head (fc1/lin read over the d dense
@@ -584,7 +693,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
-    ap.add_argument("--workload", choices=["stack", "chunk", "staged", "layer", "prefill"],
+    ap.add_argument("--workload", choices=["stack", "chunk", "staged", "layer", "prefill",
+                                           "storage"],
                     default="stack",
                     help="stack: the 40-layer resident decode (the bench line); chunk: the "
                          "batched path (B=32 chunk, or --chunk-b); prefill: a B-token batch through "
@@ -594,6 +704,14 @@ def main():
                     help="staged workload: compute units left to the staging copies")
     ap.add_argument("--group", type=int, default=8,
                     help="staged workload: predicted layers per launch")
+    ap.add_argument("--arm", choices=["prefetch", "ondemand"], default="prefetch",
+                    help="storage workload: disk reads one token ahead, or just before use")
+    ap.add_argument("--ram-bundles", type=int, default=0,
+                    help="storage workload: bundles the RAM tier keeps (LRU)")
+    ap.add_argument("--io-threads", type=int, default=16,
+                    help="storage workload: host I/O threads")
+    ap.add_argument("--store-dir", default=None,
+                    help="storage workload: directory for the layer files (default: temp dir)")
     ap.add_argument("--cache-entries", type=int, default=0,
                     help="staged workload: stage through one cross-layer hot cache of this "
                          "many bundles (0: 2K slots per layer)")
@@ -617,8 +735,8 @@ def main():
         if args.gpus != 1:
             print("bench.py measures one GPU (run with --gpus 1)", file=sys.stderr)
             sys.exit(2)
-        dict(chunk=run_chunk, staged=run_staged, layer=run_layer,
-             prefill=run_prefill)[args.workload](args)
+        dict(chunk=run_chunk, staged=run_staged, layer=run_layer, prefill=run_prefill,
+             storage=run_storage)[args.workload](args)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:

@@ -394,8 +394,10 @@ int64_t e0_cache_copies(e0_cache* c);
  * Layer l's file (paths[l]) holds its E bundles back to back, bundle e at
  * byte e * bundle_bytes (the bundle layout above). io_threads host threads
  * serve the reads; direct != 0 opens the files with O_DIRECT (page cache
- * bypassed: bundle_bytes and every destination 4096-byte aligned), so every
- * read reaches the device. Host code only: no GPU call.
+ * bypassed; bundle_bytes a multiple of 4096), so every
+ * read reaches the device (each I/O thread reads into its own page-aligned
+ * buffer and copies the bundle to its destination, since the driver's
+ * pinned pages cannot take a direct read). Host code only: no GPU call.
  *   e0_store_read   queue one pread per id of `ids` (host int32 [n]) into
  *                   dst[i] (host pointers, typically into a pinned pool);
  *                   returns at once with a ticket.
@@ -404,7 +406,7 @@ int64_t e0_cache_copies(e0_cache* c);
  *                   from queueing to the last read's completion. E0_ERR_IO if
  *                   any read failed; a ticket is waited on once.
  *   e0_store_bytes  bytes read since opening.
- * Errors: E0_ERR_ARG (bad argument), E0_ERR_ALIGN (O_DIRECT alignment),
+ * Errors: E0_ERR_ARG (bad argument), E0_ERR_ALIGN (O_DIRECT bundle size),
  * E0_ERR_RANGE (id outside [0, E)), E0_ERR_IO (open or read failed). */
 typedef struct e0_store e0_store;
 

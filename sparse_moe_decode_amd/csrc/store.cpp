@@ -10,16 +10,21 @@
 // e * bundle, the bundle layout of the staging path). A pool of I/O threads
 // serves read requests: each bundle is one pread into a caller buffer
 // (pinned host memory, so the GPU's staging copy reads it directly). With
-// O_DIRECT the page cache is bypassed, so every read reaches the device.
+// O_DIRECT the page cache is bypassed, so every read reaches the device;
+// the driver's pinned pages cannot take a direct read, so each thread reads
+// into its own page-aligned bounce buffer and copies the bundle over.
 // Requests are grouped under tickets; e0_store_wait blocks until a ticket's
 // reads are done and reports how long it blocked.
 
 #include <fcntl.h>
 #include <unistd.h>
 
+#include <cerrno>
+
 #include <chrono>
 #include <condition_variable>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <deque>
 #include <mutex>
@@ -44,6 +49,7 @@ struct Req {
 struct Ticket {
   int pending = 0;
   int errors = 0;
+  int first_errno = 0;  // errno of the first failed read (0: short read)
   double t_first = 0.0;  // issue time, seconds
   double t_done = 0.0;   // completion of the last read
 };
@@ -69,30 +75,40 @@ struct e0_store {
   int64_t bytes_read = 0, reads = 0;
 
   void worker() {
+    char* bounce = nullptr;  // direct reads: page-aligned staging for one bundle
+    if (direct && posix_memalign(reinterpret_cast<void**>(&bounce), 4096, (size_t)bundle) != 0)
+      bounce = nullptr;
     for (;;) {
       Req r;
       {
         std::unique_lock<std::mutex> lk(mu);
         cv_work.wait(lk, [&] { return stop || !queue.empty(); });
-        if (queue.empty()) return;  // stop requested and nothing left
+        if (queue.empty()) {  // stop requested and nothing left
+          free(bounce);
+          return;
+        }
         r = queue.front();
         queue.pop_front();
       }
       int64_t done = 0;
-      bool ok = true;
-      while (done < r.bytes) {
-        const ssize_t n = pread(r.fd, r.dst + done, (size_t)(r.bytes - done), (off_t)(r.off + done));
+      bool ok = !direct || bounce != nullptr;
+      int err = ok ? 0 : ENOMEM;
+      char* into = direct ? bounce : r.dst;
+      while (ok && done < r.bytes) {
+        const ssize_t n = pread(r.fd, into + done, (size_t)(r.bytes - done), (off_t)(r.off + done));
         if (n <= 0) {
           ok = false;
+          err = n < 0 ? errno : 0;
           break;
         }
         done += n;
       }
+      if (ok && direct) memcpy(r.dst, bounce, (size_t)r.bytes);
       {
         std::lock_guard<std::mutex> lk(mu);
         Ticket& tk = tickets[r.ticket];
         tk.pending -= 1;
-        if (!ok) tk.errors += 1;
+        if (!ok && tk.errors++ == 0) tk.first_errno = err;
         tk.t_done = now_s();
         bytes_read += done;
         reads += 1;
@@ -152,8 +168,7 @@ int e0_store_read(e0_store* s, int32_t layer, const int32_t* ids, int32_t n, voi
     return smd_report(E0_ERR_ARG, "e0_store_read: layer out of range");
   for (int i = 0; i < n; ++i) {
     if (ids[i] < 0 || ids[i] >= s->E) return smd_report(E0_ERR_RANGE, "e0_store_read: bad id");
-    if (!dst[i] || (s->direct && ((uintptr_t)dst[i] % 4096)))
-      return smd_report(E0_ERR_ALIGN, "e0_store_read: destination null or not 4096-aligned");
+    if (!dst[i]) return smd_report(E0_ERR_ARG, "e0_store_read: null destination");
   }
   {
     std::lock_guard<std::mutex> lk(s->mu);
@@ -186,7 +201,11 @@ int e0_store_wait(e0_store* s, int64_t ticket, double* blocked_s, double* read_s
   lk.unlock();
   if (blocked_s) *blocked_s = now_s() - t0;
   if (read_s) *read_s = t.t_done - t.t_first;
-  if (t.errors) return smd_report(E0_ERR_IO, "e0_store_wait: a read failed");
+  if (t.errors)
+    return smd_report(E0_ERR_IO, (std::string("e0_store_wait: ") + std::to_string(t.errors) +
+                                  " read(s) failed: " +
+                                  (t.first_errno ? strerror(t.first_errno) : "short read"))
+                                     .c_str());
   return E0_OK;
 }
 

@@ -168,3 +168,134 @@ class PrefillStack:
             api.moe_int4_decode(self.ctx, self.views[buf], x[l], idx[l], w[l], y=y[l],
                                 shared=self.shared[l], stride=self.bundle, stream=self.main)
             self.free[buf].record(self.main)
+
+
+class StorageStagedStack(StagedStack):
+    """StagedStack whose pinned host pool is itself filled from per-layer
+    stacked files on disk (api.Store), the pages' weight tier ("The Other
+    Half of the Memory Wall", §3.1: experts stay on SSD and stream by byte
+    range; §5.3: reads issued one token ahead take the load time off the
+    critical path).
+
+    A bundle is read from disk when a staged set needs it and it is neither
+    in the previous token's set of its layer (then it holds an HBM slot) nor
+    in the RAM tier: an LRU of `ram_bundles` (layer, id) keys over the pinned
+    pool (0 keeps nothing beyond what is being staged). Reads land at the
+    bundle's own address in the pool, so a re-read rewrites the same bytes.
+
+    arm "prefetch": after token t's launches are queued, each group's
+    predicted sets for t+1 are read back as soon as the launch holding the
+    heads that predict it has run, and its disk reads are queued at once; the
+    GPU staging of each group then waits for its own reads.
+    arm "ondemand": no early reads: before each group of token t runs, its
+    sets are read back, its disk reads are queued and waited for, then it is
+    staged and launched (group = 1 gives per-layer loads, as on-demand
+    streaming does).
+
+    Per token, blocked_s sums the time the host waited on disk reads; loads
+    lists (bundles, seconds) per read ticket."""
+
+    def __init__(self, ctx, model, state, stager, cons, n_layers, store, host_pool,
+                 ram_bundles: int = 0, arm: str = "prefetch", **kw):
+        super().__init__(ctx, model, state, stager, cons, n_layers, **kw)
+        import collections
+        assert arm in ("prefetch", "ondemand")
+        self.store, self.host_pool, self.arm = store, host_pool, arm
+        self.E = ctx.dims["E"]
+        self.bundle = ctx.bundle_bytes()
+        self.base = host_pool.data_ptr()
+        self.ram = collections.OrderedDict()
+        self.ram_bundles = ram_bundles
+        self.prev = {}  # layer -> set of ids of the previous staged token
+        self.copy_stream = torch.cuda.Stream()
+        self.sets_host = torch.empty_like(state.route_idx[0], device="cpu").pin_memory()
+        self.blocked_s = 0.0
+        self.loads = []
+
+    def _read_group(self, t: int, g0: int, g1: int, after: torch.cuda.Event | None):
+        """Queue disk reads for token t's sets of layers [g0, g1); returns the
+        ticket list."""
+        st = self.state
+        with torch.cuda.stream(self.copy_stream):
+            if after is not None:
+                self.copy_stream.wait_event(after)
+            else:
+                self.copy_stream.wait_stream(self.main)
+            self.sets_host[g0:g1].copy_(st.route_idx[t & 1][g0:g1], non_blocking=True)
+        self.copy_stream.synchronize()
+        sets = self.sets_host[g0:g1].numpy()
+        tickets = []
+        for i, l in enumerate(range(g0, g1)):
+            ids = []
+            prev = self.prev.get(l, set())
+            for e in sorted(set(int(v) for v in sets[i])):
+                key = (l, e)
+                if key in self.ram:
+                    self.ram.move_to_end(key)
+                    continue
+                if e in prev:
+                    continue
+                ids.append(e)
+                self.ram[key] = True
+                while len(self.ram) > self.ram_bundles:
+                    self.ram.popitem(last=False)
+            self.prev[l] = set(int(v) for v in sets[i])
+            if ids:
+                li = l - self.cons[0]
+                dst = [self.base + (li * self.E + e) * self.bundle for e in ids]
+                tickets.append((len(ids), self.store.read(li, ids, dst)))
+        return tickets
+
+    def _wait(self, tickets):
+        for n, tk in tickets:
+            blocked, read = self.store.wait(tk)
+            self.blocked_s += blocked
+            self.loads.append((n, read))
+
+    def stage(self, t: int, after_token: bool):
+        if not after_token:  # initial staging: read everything first
+            for g0, g1 in self.groups:
+                self._wait(self._read_group(t, g0, g1, None))
+        super().stage(t, after_token)
+
+    def run_token(self, t: int, h):
+        if self.arm == "prefetch":
+            c0, c1 = self.cons[0], self.cons[-1]
+            ctx, model, st, main = self.ctx, self.model, self.state, self.main
+            with torch.cuda.stream(main):
+                self.sets[t & 1].copy_(st.route_idx[t & 1])
+            api.layer_step(ctx, model, 0, c0, st, t, h, main)
+            self.pre.record(main)
+            for j, (g0, g1) in enumerate(self.groups):
+                main.wait_event(self.staged[j])
+                api.layer_step(ctx, model, g0, g1, st, t, h[g0:], main)
+                self.launched[j].record(main)
+            if c1 + 1 < self.L:
+                api.layer_step(ctx, model, c1 + 1, self.L, st, t, h[c1 + 1:], main)
+            # predictions for t+1 become readable group by group
+            pending = [self._read_group(t + 1, g0, g1, self._source(j))
+                       for j, (g0, g1) in enumerate(self.groups)]
+            for j, (g0, g1) in enumerate(self.groups):
+                self._wait(pending[j])
+                self.side.wait_event(self._source(j))
+                in_use = self.sets[t & 1][g0:g1]
+                api.stage_experts_n(self.stager, g0 - c0, g1 - g0, st.route_idx[(t + 1) & 1][g0:g1],
+                                    in_use, side_stream=self.side, done_event=self.staged[j])
+            return
+        # on demand: each group's reads are queued and waited for just before it runs
+        c0, c1 = self.cons[0], self.cons[-1]
+        ctx, model, st, main = self.ctx, self.model, self.state, self.main
+        with torch.cuda.stream(main):
+            self.sets[t & 1].copy_(st.route_idx[t & 1])
+        api.layer_step(ctx, model, 0, c0, st, t, h, main)
+        for j, (g0, g1) in enumerate(self.groups):
+            if t > 0:
+                self._wait(self._read_group(t, g0, g1, None))
+                self.side.wait_stream(main)
+                api.stage_experts_n(self.stager, g0 - c0, g1 - g0, st.route_idx[t & 1][g0:g1],
+                                    self.sets[(t - 1) & 1][g0:g1], side_stream=self.side,
+                                    done_event=self.staged[j])
+            main.wait_event(self.staged[j])
+            api.layer_step(ctx, model, g0, g1, st, t, h[g0:], main)
+        if c1 + 1 < self.L:
+            api.layer_step(ctx, model, c1 + 1, self.L, st, t, h[c1 + 1:], main)
