@@ -445,3 +445,80 @@ def cache_policy(E, C, slot_of, owner, stamp, layer0, new_sets, tick):
         stamp[c] = tick
         copies.append((l - layer0, e, c))
     return copies
+
+
+# --------------------------------------------------------------- affine int4
+# The pages' own codec ([MW] §3.1: "int4 affine group-64", each projection
+# with its scales and biases; bf16 scales and biases in the MLX layout):
+# unsigned nibbles, w = s q + b. Plain numpy in fp64, written from that
+# definition; it shares nothing with the symmetric C++ path above.
+
+def bf16_decode(bits) -> np.ndarray:
+    """Exact value of bfloat16 bit patterns: sign, 8-bit biased exponent,
+    7-bit fraction (subnormals at exponent 0)."""
+    b = np.asarray(bits, np.uint16).astype(np.int64)
+    sign = np.where(b >> 15, -1.0, 1.0)
+    expo = (b >> 7) & 0xFF
+    frac = b & 0x7F
+    normal = np.ldexp((128 + frac).astype(np.float64), (expo - 134).astype(np.int64))
+    sub = np.ldexp(frac.astype(np.float64), -133)
+    val = np.where(expo == 0, sub, normal)
+    val = np.where(expo == 255, np.where(frac == 0, np.inf, np.nan), val)
+    return sign * val
+
+
+def q4_affine_dequant(q, s_bits, b_bits, rows, cols, group) -> np.ndarray:
+    """fp64 [rows, cols]: element i of row o is the unsigned nibble at bits
+    4 (i % 8) of word i / 8 of the row; w = s[o][i / G] * nibble + b[o][i / G]."""
+    words = np.asarray(q, np.uint32).reshape(rows, cols // 8).astype(np.int64)
+    nib = np.empty((rows, cols), np.float64)
+    for j in range(8):
+        nib[:, j::8] = (words >> (4 * j)) & 0xF
+    s = bf16_decode(s_bits).reshape(rows, cols // group)
+    b = bf16_decode(b_bits).reshape(rows, cols // group)
+    g = np.arange(cols) // group
+    return s[:, g] * nib + b[:, g]
+
+
+def _silu64(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def expert_affine(mats: dict, d, I, group, x) -> np.ndarray:
+    """down(silu(gate x) * up x) of one affine expert ([MW] §3.1 Math
+    contract); mats holds gate_q/_s/_b [I, ...], up_*, down_* [d, ...]."""
+    Wg = q4_affine_dequant(mats["gate_q"], mats["gate_s"], mats["gate_b"], I, d, group)
+    Wu = q4_affine_dequant(mats["up_q"], mats["up_s"], mats["up_b"], I, d, group)
+    Wd = q4_affine_dequant(mats["down_q"], mats["down_s"], mats["down_b"], d, I, group)
+    return Wd @ (_silu64(Wg @ x) * (Wu @ x))
+
+
+def moe_decode_affine(dims: dict, routed: dict, shared: dict | None, x16, idx, w) -> np.ndarray:
+    """sum_k w_k E_idx[k](x) + S(x) with affine experts; S carries the
+    unmerged LoRA deltas (alpha / r) B (A v) on its gate, up and down ([MW]
+    §3.3). x16: fp16 activations."""
+    d, I, G = dims["d"], dims["I"], dims["G"]
+    x = np.asarray(x16, np.float16).astype(np.float64)
+    y = np.zeros(d)
+    names = ("gate_q", "gate_s", "gate_b", "up_q", "up_s", "up_b", "down_q", "down_s", "down_b")
+    for k, e in enumerate(np.asarray(idx).ravel()):
+        mats = {n: routed[n][int(e)] for n in names}
+        y += float(w[k]) * expert_affine(mats, d, I, G, x)
+    if shared is not None:
+        Is, r = dims["Is"], dims.get("r", 0)
+        Wg = q4_affine_dequant(shared["gate_q"], shared["gate_s"], shared["gate_b"], Is, d, G)
+        Wu = q4_affine_dequant(shared["up_q"], shared["up_s"], shared["up_b"], Is, d, G)
+        Wd = q4_affine_dequant(shared["down_q"], shared["down_s"], shared["down_b"], d, Is, G)
+        g, u = Wg @ x, Wu @ x
+        lora = r > 0 and shared.get("a_gate") is not None
+        f = lambda a: np.asarray(a, np.float16).astype(np.float64)
+        c = dims.get("alpha", 0.0) / r if r else 0.0
+        if lora:
+            g = g + c * (f(shared["b_gate"]) @ (f(shared["a_gate"]) @ x))
+            u = u + c * (f(shared["b_up"]) @ (f(shared["a_up"]) @ x))
+        h = _silu64(g) * u
+        ys = Wd @ h
+        if lora:
+            ys = ys + c * (f(shared["b_down"]) @ (f(shared["a_down"]) @ h))
+        y += ys
+    return y

@@ -117,24 +117,57 @@ def q4_matrix(rng, rows, cols, G, lead=(), zero_mean=False):
     return q, group_scales(rng, (*lead, rows, cols // G))
 
 
+def bf16_bits(x) -> np.ndarray:
+    """fp32 values -> bfloat16 bit patterns (round to nearest, ties to even)."""
+    f = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    return ((f + 0x7FFF + ((f >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def q4_matrix_affine(rng, rows, cols, G, lead=()):
+    """Affine int4 matrix: (uint32 [*lead, rows, cols/8] of unsigned nibbles,
+    bf16 scales and bf16 biases [*lead, rows, cols/G] as uint16 bits). The
+    biases sit near -7.5 scales, so the weights s q + b are about zero-mean."""
+    assert cols % 8 == 0 and cols % G == 0
+    q = random_words(rng, (*lead, rows, cols // 8))
+    shape = (*lead, rows, cols // G)
+    s = np.abs(rng.normal(0.0, 0.02, size=shape)) + 1e-3
+    b = -7.5 * s + rng.normal(0.0, 0.002, size=shape)
+    return q, bf16_bits(s), bf16_bits(b)
+
+
+def _q4(rng, rows, cols, G, lead, zero_mean, affine):
+    if affine:
+        return q4_matrix_affine(rng, rows, cols, G, lead)
+    return (*q4_matrix(rng, rows, cols, G, lead, zero_mean), None)
+
+
 # ----------------------------------------------------------- layer parts --
 
 def routed_pool(rng, dm: dict, n: int | None = None, zero_mean: bool = False) -> dict:
-    """n experts (default E) stacked: gate/up [n, I, d/8], down [n, d, I/8]."""
+    """n experts (default E) stacked: gate/up [n, I, d/8], down [n, d, I/8].
+    With dm["quant"] == 1 (the affine codec) the scales are bf16 bits and
+    gate_b / up_b / down_b hold the bf16 biases."""
     n = dm["E"] if n is None else n
     d, I, G = dm["d"], dm["I"], dm["G"]
-    gq, gs = q4_matrix(rng, I, d, G, (n,), zero_mean)
-    uq, us = q4_matrix(rng, I, d, G, (n,), zero_mean)
-    dq, ds = q4_matrix(rng, d, I, G, (n,), zero_mean)
-    return dict(gate_q=gq, gate_s=gs, up_q=uq, up_s=us, down_q=dq, down_s=ds)
+    af = dm.get("quant", 0) == 1
+    gq, gs, gb = _q4(rng, I, d, G, (n,), zero_mean, af)
+    uq, us, ub = _q4(rng, I, d, G, (n,), zero_mean, af)
+    dq, ds, db = _q4(rng, d, I, G, (n,), zero_mean, af)
+    out = dict(gate_q=gq, gate_s=gs, up_q=uq, up_s=us, down_q=dq, down_s=ds)
+    if af:
+        out.update(gate_b=gb, up_b=ub, down_b=db)
+    return out
 
 
 def shared_expert(rng, dm: dict, lora: bool = True, zero_mean: bool = False) -> dict:
     d, Is, G, r = dm["d"], dm["Is"], dm["G"], dm["r"]
-    gq, gs = q4_matrix(rng, Is, d, G, zero_mean=zero_mean)
-    uq, us = q4_matrix(rng, Is, d, G, zero_mean=zero_mean)
-    dq, ds = q4_matrix(rng, d, Is, G, zero_mean=zero_mean)
+    af = dm.get("quant", 0) == 1
+    gq, gs, gb = _q4(rng, Is, d, G, (), zero_mean, af)
+    uq, us, ub = _q4(rng, Is, d, G, (), zero_mean, af)
+    dq, ds, db = _q4(rng, d, Is, G, (), zero_mean, af)
     out = dict(gate_q=gq, gate_s=gs, up_q=uq, up_s=us, down_q=dq, down_s=ds)
+    if af:
+        out.update(gate_b=gb, up_b=ub, down_b=db)
     if lora and r > 0:
         out.update(a_gate=f16_normal(rng, (r, d), 0.01), b_gate=f16_normal(rng, (Is, r), 0.01),
                    a_up=f16_normal(rng, (r, d), 0.01), b_up=f16_normal(rng, (Is, r), 0.01),
