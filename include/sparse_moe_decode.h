@@ -58,6 +58,14 @@ enum {
 
 enum { E0_ROUTER_SOFTMAX_TOPK = 0, E0_ROUTER_SIGMOID_GROUP = 1 };
 
+/* Int4 codec of the expert matrices. Symmetric: a two's-complement nibble q
+ * in [-8, 7] times an fp16 group scale, w = s q. Affine (the pages' MLX
+ * format [MW §3.1, "int4 affine group-64", every projection with its scales
+ * and biases]): an unsigned nibble q in [0, 15], with a bf16 group scale
+ * and bias, w = s q + b. Both pack element i of a row in word i/8 at bits
+ * 4 (i % 8). */
+enum { E0_QUANT_SYMMETRIC = 0, E0_QUANT_AFFINE = 1 };
+
 /* Model dimensions and routing family of one tier ([CB "A3B describes a model
  * that isn't the one serving"], MoESpec; [MW App. A]). */
 typedef struct e0_spec {
@@ -76,18 +84,21 @@ typedef struct e0_spec {
   int32_t topk_groups;  /* sigmoid-group: groups kept */
   float route_scale;    /* sigmoid-group: scale s on the weights */
   float rms_eps;        /* RMSNorm epsilon (gain is 1) */
+  int32_t quant;        /* E0_QUANT_SYMMETRIC or E0_QUANT_AFFINE */
 } e0_spec;
 
 typedef struct e0_q4 {
   const uint32_t* q; /* packed nibbles [rows, cols/8] */
-  const uint16_t* s; /* fp16 group scales [rows, cols/G] */
+  const uint16_t* s; /* group scales [rows, cols/G]: fp16 (symmetric), bf16 (affine) */
+  const uint16_t* b; /* affine: bf16 group biases [rows, cols/G]; symmetric: NULL */
 } e0_q4;
 
 /* A pool of `count` routed experts (or staged slots). Entry j's gate/up
  * matrices ([I, d]) start at gate.q + j*stride_q bytes (scales at
- * gate.s + j*stride_s), its down matrix ([d, I]) likewise. stride_q /
- * stride_s = 0 selects dense stacking ([count, I, d/8] u32 and
- * [count, I, d/G] fp16), i.e. I*d/2 and 2*I*d/G bytes. Entries are
+ * gate.s + j*stride_s, affine biases at gate.b + j*stride_s), its down
+ * matrix ([d, I]) likewise. stride_q / stride_s = 0 selects dense stacking
+ * ([count, I, d/8] u32 and [count, I, d/G] 16-bit), i.e. I*d/2 and 2*I*d/G
+ * bytes. Entries are
  * addressed by expert id, or through a slot table; ids and slots at or
  * beyond `count` are rejected on the device. */
 typedef struct e0_experts {
@@ -285,8 +296,10 @@ int layer_step(e0_ctx* ctx, e0_model* model, int32_t layer_begin, int32_t layer_
  * bundles is copied into an HBM slot pool, keyed by the predicted set, on a
  * side stream.
  * Bundle layout of one expert (bytes, in order): gate q [I, d/8] u32,
- * up q, down q [d, I/8] u32, gate s [I, d/G] fp16, up s, down s; bundle size
- * e0_bundle_bytes(spec). An e0_experts view of a pool of bundles has
+ * up q, down q [d, I/8] u32, gate s [I, d/G] 16-bit, up s, down s, and for
+ * the affine codec gate b, up b, down b (bf16, shaped as the scales);
+ * bundle size e0_bundle_bytes(spec) (35B shapes: 1,671,168 bytes symmetric,
+ * 1,769,472 affine, the pages' "1.77 MB" per expert). An e0_experts view of a pool of bundles has
  * stride_q = stride_s = bundle bytes.
  *   host_pool  HOST pointer, pinned (hipHostMalloc), [n_layers][E] bundles.
  *   hbm_slots  device pointer, [n_layers][n_slots] bundles.

@@ -41,11 +41,11 @@ class e0_spec(C.Structure):
                 ("shared_inter", _i32), ("head_hidden", _i32), ("group", _i32),
                 ("lora_rank", _i32), ("lora_alpha", _f), ("router_kind", _i32),
                 ("norm_topk", _i32), ("n_groups", _i32), ("topk_groups", _i32),
-                ("route_scale", _f), ("rms_eps", _f)]
+                ("route_scale", _f), ("rms_eps", _f), ("quant", _i32)]
 
 
 class e0_q4(C.Structure):
-    _fields_ = [("q", _p), ("s", _p)]
+    _fields_ = [("q", _p), ("s", _p), ("b", _p)]
 
 
 class e0_experts(C.Structure):
@@ -119,6 +119,7 @@ EXPORTS = ["e0_create", "e0_destroy", "e0_last_error", "e0_device_status", "moe_
            "e0_store_open", "e0_store_close", "e0_store_read", "e0_store_wait", "e0_store_bytes", "e0_model_set_path", "e0_model_set_grid", "e0_model_set_trace", "e0_model_trace_shape"]
 
 PATH_AUTO, PATH_PHASES, PATH_PERSISTENT = 0, 1, 2
+QUANT_SYMMETRIC, QUANT_AFFINE = 0, 1
 
 
 class E0Error(RuntimeError):
@@ -156,7 +157,13 @@ def make_spec(dims: dict) -> e0_spec:
     s.norm_topk = int(dims.get("norm_topk", 1))
     s.n_groups, s.topk_groups = dims.get("n_groups", 1), dims.get("topk_groups", 1)
     s.route_scale, s.rms_eps = dims.get("route_scale", 1.0), dims.get("eps", 1e-6)
+    s.quant = int(dims.get("quant", QUANT_SYMMETRIC))
     return s
+
+
+def bundle_bytes_of(dims: dict) -> int:
+    """e0_bundle_bytes of a tier (host only, no context)."""
+    return int(_lib.e0_bundle_bytes(C.byref(make_spec(dims))))
 
 
 class Context:
@@ -192,7 +199,8 @@ def experts_struct(pool: dict, count: int, stride_q: int = 0, stride_s: int = 0)
     """pool: tensors gate_q/gate_s/up_q/up_s/down_q/down_s (or ints = device addresses)."""
     ex = e0_experts()
     for name in ("gate", "up", "down"):
-        setattr(ex, name, e0_q4(_ptr(pool[f"{name}_q"]), _ptr(pool[f"{name}_s"])))
+        setattr(ex, name, e0_q4(_ptr(pool[f"{name}_q"]), _ptr(pool[f"{name}_s"]),
+                                _ptr(pool.get(f"{name}_b"))))
     ex.stride_q, ex.stride_s, ex.count = stride_q, stride_s, count
     return ex
 
@@ -202,7 +210,8 @@ def shared_struct(sh: dict | None) -> e0_shared | None:
         return None
     s = e0_shared()
     for name in ("gate", "up", "down"):
-        setattr(s, name, e0_q4(_ptr(sh[f"{name}_q"]), _ptr(sh[f"{name}_s"])))
+        setattr(s, name, e0_q4(_ptr(sh[f"{name}_q"]), _ptr(sh[f"{name}_s"]),
+                               _ptr(sh.get(f"{name}_b"))))
     for lname, key in (("lgate", "gate"), ("lup", "up"), ("ldown", "down")):
         setattr(s, lname, e0_lora(_ptr(sh.get(f"a_{key}")), _ptr(sh.get(f"b_{key}"))))
     return s
@@ -339,11 +348,15 @@ def layer_step(ctx: Context, model: Model, layer_begin: int, layer_end: int, sta
 
 def bundle_parts(dims: dict) -> list[tuple[str, int]]:
     """(name, bytes) of one expert bundle in the ABI's order: gate q, up q,
-    down q (packed u32), gate s, up s, down s (fp16)."""
+    down q (packed u32), gate s, up s, down s (16-bit), then for the affine
+    codec gate b, up b, down b (bf16)."""
     qb = dims["I"] * dims["d"] // 2
     sb = dims["I"] * dims["d"] // dims["G"] * 2
-    return [("gate_q", qb), ("up_q", qb), ("down_q", qb), ("gate_s", sb), ("up_s", sb),
-            ("down_s", sb)]
+    parts = [("gate_q", qb), ("up_q", qb), ("down_q", qb), ("gate_s", sb), ("up_s", sb),
+             ("down_s", sb)]
+    if dims.get("quant", 0) == 1:
+        parts += [("gate_b", sb), ("up_b", sb), ("down_b", sb)]
+    return parts
 
 
 def pack_bundles(pool: dict, dims: dict):

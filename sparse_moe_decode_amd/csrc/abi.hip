@@ -83,6 +83,8 @@ int e0_create(const e0_spec* spec, int32_t max_tokens, e0_ctx** out) {
       p.top_k > p.n_experts || p.inter <= 0 || p.group <= 0 || max_tokens < 1 ||
       max_tokens > 8192)
     return fail(E0_ERR_ARG, "e0_create: bad dimensions");
+  if (p.quant != E0_QUANT_SYMMETRIC && p.quant != E0_QUANT_AFFINE)
+    return fail(E0_ERR_ARG, "e0_create: unknown int4 codec %d", p.quant);
   if (p.group % 32 || p.d_model % p.group || p.inter % p.group)
     return fail(E0_ERR_SHAPE, "e0_create: group %d must be a multiple of 32 dividing d and I",
                 p.group);
@@ -112,6 +114,7 @@ int e0_create(const e0_spec* spec, int32_t max_tokens, e0_ctx** out) {
   dm.router_kind = p.router_kind; dm.norm_topk = p.norm_topk; dm.n_groups = p.n_groups;
   dm.topk_groups = p.topk_groups; dm.route_scale = p.route_scale;
   dm.eps = p.rms_eps > 0 ? p.rms_eps : 1e-6f;
+  dm.affine = p.quant == E0_QUANT_AFFINE;
   if (hipGetDevice(&c->device) != hipSuccess) {
     delete c;
     return fail(E0_ERR_HIP, "e0_create: no current HIP device");
@@ -188,9 +191,12 @@ int e0_device_status(e0_ctx* ctx, void* stream) {
 
 namespace {
 
-int check_q4(const e0_q4& m, const char* what) {
+int check_q4(const e0_q4& m, bool affine, const char* what) {
   if (!m.q || !m.s) return fail(E0_ERR_ARG, "%s: null int4 matrix", what);
-  if (!aligned(m.q, 16) || !aligned(m.s, 2))
+  if (affine != (m.b != nullptr))
+    return fail(E0_ERR_ARG, "%s: biases must be given for the affine codec and only for it",
+                what);
+  if (!aligned(m.q, 16) || !aligned(m.s, 2) || (m.b && !aligned(m.b, 2)))
     return fail(E0_ERR_ALIGN, "%s: packed words must be 16-byte aligned", what);
   return E0_OK;
 }
@@ -198,13 +204,14 @@ int check_q4(const e0_q4& m, const char* what) {
 int make_pool(const e0_ctx* ctx, const e0_experts* ex, const int32_t* slot_of, Pool& p) {
   if (!ex) return fail(E0_ERR_ARG, "routed pool is null");
   int rc;
-  if ((rc = check_q4(ex->gate, "routed gate")) || (rc = check_q4(ex->up, "routed up")) ||
-      (rc = check_q4(ex->down, "routed down")))
-    return rc;
   const Dims& dm = ctx->dm;
-  p.gate = {ex->gate.q, ex->gate.s};
-  p.up = {ex->up.q, ex->up.s};
-  p.down = {ex->down.q, ex->down.s};
+  const bool af = dm.affine != 0;
+  if ((rc = check_q4(ex->gate, af, "routed gate")) || (rc = check_q4(ex->up, af, "routed up")) ||
+      (rc = check_q4(ex->down, af, "routed down")))
+    return rc;
+  p.gate = {ex->gate.q, ex->gate.s, ex->gate.b};
+  p.up = {ex->up.q, ex->up.s, ex->up.b};
+  p.down = {ex->down.q, ex->down.s, ex->down.b};
   p.stride_q = ex->stride_q ? ex->stride_q : (int64_t)dm.I * dm.d / 2;
   p.stride_s = ex->stride_s ? ex->stride_s : (int64_t)2 * dm.I * (dm.d / dm.G);
   if (p.stride_q % 16 || p.stride_s % 2) return fail(E0_ERR_ALIGN, "pool strides misaligned");
@@ -219,12 +226,13 @@ int make_shared(const e0_ctx* ctx, const e0_shared* sh, SharedW& w) {
   if (!sh) return E0_OK;
   if (ctx->dm.Is == 0) return fail(E0_ERR_ARG, "shared expert given but shared_inter = 0");
   int rc;
-  if ((rc = check_q4(sh->gate, "shared gate")) || (rc = check_q4(sh->up, "shared up")) ||
-      (rc = check_q4(sh->down, "shared down")))
+  const bool af = ctx->dm.affine != 0;
+  if ((rc = check_q4(sh->gate, af, "shared gate")) || (rc = check_q4(sh->up, af, "shared up")) ||
+      (rc = check_q4(sh->down, af, "shared down")))
     return rc;
-  w.gate = {sh->gate.q, sh->gate.s};
-  w.up = {sh->up.q, sh->up.s};
-  w.down = {sh->down.q, sh->down.s};
+  w.gate = {sh->gate.q, sh->gate.s, sh->gate.b};
+  w.up = {sh->up.q, sh->up.s, sh->up.b};
+  w.down = {sh->down.q, sh->down.s, sh->down.b};
   const bool lg = sh->lgate.a && sh->lgate.b, lu = sh->lup.a && sh->lup.b,
              ld = sh->ldown.a && sh->ldown.b;
   if ((lg || lu || ld) && ctx->dm.r == 0) return fail(E0_ERR_ARG, "LoRA given but rank = 0");
@@ -621,7 +629,8 @@ extern "C" {
 int64_t e0_bundle_bytes(const e0_spec* spec) {
   if (!spec || spec->group <= 0) return -1;
   const int64_t Id = (int64_t)spec->inter * spec->d_model;
-  return 3 * (Id / 2) + 3 * 2 * (Id / spec->group);
+  const int64_t per_group = spec->quant == E0_QUANT_AFFINE ? 2 : 1;  // scale (+ bias)
+  return 3 * (Id / 2) + 3 * 2 * per_group * (Id / spec->group);
 }
 
 int e0_stager_create(e0_ctx* ctx, const void* host_pool, int32_t n_layers, int32_t n_slots,

@@ -1071,7 +1071,8 @@ __global__ __launch_bounds__(512) void k_pf_down(MbArgs a) {
 
 bool batched_supported(const Dims& dm) {
   const int gu_groups = dm.G > 0 ? dm.d / dm.G : 0, dn_groups = dm.G > 0 ? dm.I / dm.G : 0;
-  return dm.G == 64 && dm.d % 128 == 0 && dm.I % 64 == 0 && gu_groups % 8 == 0 &&
+  // the symmetric codec only: affine experts take the per-token GEMV path
+  return !dm.affine && dm.G == 64 && dm.d % 128 == 0 && dm.I % 64 == 0 && gu_groups % 8 == 0 &&
          gu_groups <= 32 && dn_groups % 2 == 0 && dn_groups <= 8 && dm.K <= 8 &&
          dm.E <= kMaxE && dm.r % 8 == 0 && dm.r <= kMaxR && (dm.Is == 0 || dm.Is == dm.I);
 }

@@ -48,24 +48,36 @@ __device__ __forceinline__ float dot2(f16x2 a, f16x2 b, float c) {
 //   p0 = (q0, q4)   p1 = (q1, q5)   p2 = (q2, q6)   p3 = (q3, q7)
 // so activations must be supplied pair-permuted as
 //   xp[0] = (x0, x4)  xp[1] = (x1, x5)  xp[2] = (x2, x6)  xp[3] = (x3, x7).
+// AFF (the affine codec): the nibbles are unsigned values q in [0, 15];
+// without the 0x8 XOR the mantissa reads 1024 + q (1024 + 16 q a nibble
+// higher), so the same two instructions per register subtract 1024 (or
+// scale by 1/16 and subtract 64).
+template <bool AFF = false>
 __device__ __forceinline__ void q4_pairs(uint32_t w, f16x2& p0, f16x2& p1, f16x2& p2,
                                          f16x2& p3) {
   const uint32_t v = w >> 8;
-  const f16x2 k1032 = {(f16)1032.0f, (f16)1032.0f};
+  const uint32_t c0 = AFF ? 0x64006400u : 0x64086408u, c1 = AFF ? 0x64006400u : 0x64806480u;
+  const f16x2 k0 = {(f16)(AFF ? 1024.0f : 1032.0f), (f16)(AFF ? 1024.0f : 1032.0f)};
   const f16x2 k16 = {(f16)0.0625f, (f16)0.0625f};
-  const f16x2 k72 = {(f16)72.0f, (f16)72.0f};
-  p0 = as_h2(0x64086408u ^ (w & 0x000F000Fu)) - k1032;
-  p1 = as_h2(0x64806480u ^ (w & 0x00F000F0u)) * k16 - k72;
-  p2 = as_h2(0x64086408u ^ (v & 0x000F000Fu)) - k1032;
-  p3 = as_h2(0x64806480u ^ (v & 0x00F000F0u)) * k16 - k72;
+  const f16x2 k1 = {(f16)(AFF ? 64.0f : 72.0f), (f16)(AFF ? 64.0f : 72.0f)};
+  p0 = as_h2(c0 ^ (w & 0x000F000Fu)) - k0;
+  p1 = as_h2(c1 ^ (w & 0x00F000F0u)) * k16 - k1;
+  p2 = as_h2(c0 ^ (v & 0x000F000Fu)) - k0;
+  p3 = as_h2(c1 ^ (v & 0x00F000F0u)) * k16 - k1;
+}
+
+// bf16 bit pattern to fp32 (exact).
+__device__ __forceinline__ float bf2f(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
 }
 
 // Eight int4 weights of one packed word against eight pair-permuted
 // activations; q and x are exact in fp16, v_dot2_f32_f16 accumulates the
 // products in fp32.
+template <bool AFF = false>
 __device__ __forceinline__ float q4_dot8(uint32_t w, const f16x2* xp, float acc) {
   f16x2 p0, p1, p2, p3;
-  q4_pairs(w, p0, p1, p2, p3);
+  q4_pairs<AFF>(w, p0, p1, p2, p3);
   acc = dot2(p0, xp[0], acc);
   acc = dot2(p1, xp[1], acc);
   acc = dot2(p2, xp[2], acc);

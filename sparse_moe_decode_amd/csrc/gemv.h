@@ -35,20 +35,22 @@ __device__ __forceinline__ void load_xchunk(const uint16_t* xs, int c, f16x2* xr
 }
 
 // One 16-byte chunk (32 int4 weights) against 32 activations.
+template <bool AFF = false>
 __device__ __forceinline__ float q4_dot32(uint4 wv, const f16x2* xr) {
   float p = 0.0f;
-  p = q4_dot8(wv.x, xr + 0, p);
-  p = q4_dot8(wv.y, xr + 4, p);
-  p = q4_dot8(wv.z, xr + 8, p);
-  p = q4_dot8(wv.w, xr + 12, p);
+  p = q4_dot8<AFF>(wv.x, xr + 0, p);
+  p = q4_dot8<AFF>(wv.y, xr + 4, p);
+  p = q4_dot8<AFF>(wv.z, xr + 8, p);
+  p = q4_dot8<AFF>(wv.w, xr + 12, p);
   return p;
 }
 
 // Same with an fp16 hi/lo activation pair (dequantises each word once).
+template <bool AFF = false>
 __device__ __forceinline__ float q4_dot8_hl(uint32_t w, const f16x2* xh, const f16x2* xl,
                                             float acc) {
   f16x2 p0, p1, p2, p3;
-  q4_pairs(w, p0, p1, p2, p3);
+  q4_pairs<AFF>(w, p0, p1, p2, p3);
   acc = dot2(p0, xh[0], acc);
   acc = dot2(p1, xh[1], acc);
   acc = dot2(p2, xh[2], acc);
@@ -60,12 +62,13 @@ __device__ __forceinline__ float q4_dot8_hl(uint32_t w, const f16x2* xh, const f
   return acc;
 }
 
+template <bool AFF = false>
 __device__ __forceinline__ float q4_dot32_hl(uint4 wv, const f16x2* xh, const f16x2* xl) {
   float p = 0.0f;
-  p = q4_dot8_hl(wv.x, xh + 0, xl + 0, p);
-  p = q4_dot8_hl(wv.y, xh + 4, xl + 4, p);
-  p = q4_dot8_hl(wv.z, xh + 8, xl + 8, p);
-  p = q4_dot8_hl(wv.w, xh + 12, xl + 12, p);
+  p = q4_dot8_hl<AFF>(wv.x, xh + 0, xl + 0, p);
+  p = q4_dot8_hl<AFF>(wv.y, xh + 4, xl + 4, p);
+  p = q4_dot8_hl<AFF>(wv.z, xh + 8, xl + 8, p);
+  p = q4_dot8_hl<AFF>(wv.w, xh + 12, xl + 12, p);
   return p;
 }
 
@@ -145,6 +148,66 @@ __device__ __forceinline__ float down_row_hl(const uint32_t* qrow, const uint16_
     load_xchunk(hh, li + LG * j, xh);
     load_xchunk(hl, li + LG * j, xl);
     part += h2f(sv[j]) * q4_dot32_hl(wv[j], xh, xl);
+  }
+  return part;
+}
+
+// Affine gate/up rows: w = s q + b with bf16 s, b per group and unsigned q.
+// A 32-element chunk c contributes s (q . x) + b xsum[c], xsum[c] the sum of
+// the chunk's activations (fp32, in LDS).
+template <int LG, int CPL>
+__device__ __forceinline__ void gateup_rowpair_aff(const uint32_t* grow, const uint32_t* urow,
+                                                   const uint16_t* gsr, const uint16_t* usr,
+                                                   const uint16_t* gbr, const uint16_t* ubr,
+                                                   int G, const uint16_t* xs, const float* xsum,
+                                                   int li, float& ag, float& au) {
+  uint4 wg[CPL], wu[CPL];
+  uint16_t sg[CPL], su[CPL], bg[CPL], bu[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = li + LG * j;
+    wg[j] = ldg(reinterpret_cast<const uint4*>(grow + 4 * c));
+    wu[j] = ldg(reinterpret_cast<const uint4*>(urow + 4 * c));
+    sg[j] = ldg(gsr + (32 * c) / G);
+    su[j] = ldg(usr + (32 * c) / G);
+    bg[j] = ldg(gbr + (32 * c) / G);
+    bu[j] = ldg(ubr + (32 * c) / G);
+  }
+  ag = 0.0f;
+  au = 0.0f;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = li + LG * j;
+    f16x2 xr[16];
+    load_xchunk(xs, c, xr);
+    ag += bf2f(sg[j]) * q4_dot32<true>(wg[j], xr) + bf2f(bg[j]) * xsum[c];
+    au += bf2f(su[j]) * q4_dot32<true>(wu[j], xr) + bf2f(bu[j]) * xsum[c];
+  }
+}
+
+// Affine down row against hi/lo activations; hsum[c] = sum of the chunk's
+// hi + lo values.
+template <int LG, int CPL>
+__device__ __forceinline__ float down_row_hl_aff(const uint32_t* qrow, const uint16_t* srow,
+                                                 const uint16_t* brow, int G, const uint16_t* hh,
+                                                 const uint16_t* hl, const float* hsum, int li) {
+  uint4 wv[CPL];
+  uint16_t sv[CPL], bv[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = li + LG * j;
+    wv[j] = ldg(reinterpret_cast<const uint4*>(qrow + 4 * c));
+    sv[j] = ldg(srow + (32 * c) / G);
+    bv[j] = ldg(brow + (32 * c) / G);
+  }
+  float part = 0.0f;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = li + LG * j;
+    f16x2 xh[16], xl[16];
+    load_xchunk(hh, c, xh);
+    load_xchunk(hl, c, xl);
+    part += bf2f(sv[j]) * q4_dot32_hl<true>(wv[j], xh, xl) + bf2f(bv[j]) * hsum[c];
   }
   return part;
 }

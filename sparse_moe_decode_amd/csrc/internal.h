@@ -8,10 +8,11 @@
 
 namespace smd {
 
-// Device view of one int4 matrix.
+// Device view of one int4 matrix (b: affine biases, null for symmetric).
 struct Q4 {
   const uint32_t* q;
   const uint16_t* s;
+  const uint16_t* b;
 };
 
 // Device view of a routed pool: entry j of projection p sits at
@@ -51,6 +52,7 @@ struct Dims {
   float lora_scale;  // alpha / r
   int32_t router_kind, norm_topk, n_groups, topk_groups;
   float route_scale, eps;
+  int32_t affine;  // E0_QUANT_AFFINE codec
 };
 
 // Flags the kernels raise (device int32 array).

@@ -40,9 +40,11 @@ struct GateUpArgs {
 // token: h[row] = silu(Wg[row] . x (+ LoRA)) * (Wu[row] . x (+ LoRA))
 // [MW §3.1 Math contract; IE "Architectural Deep Dive"]. grid = (row blocks,
 // K+1, B).
-template <int LG, int CPL>
+// AFF: affine codec (bf16 scale and bias per group, unsigned nibbles); the
+// bias terms use the sums of the activation's 32-element chunks (LDS).
+template <int LG, int CPL, bool AFF>
 __global__ __launch_bounds__(kBlock) void k_gate_up(GateUpArgs a) {
-  extern __shared__ uint16_t xs[];
+  extern __shared__ uint16_t xs[];  // [d] pair-permuted; affine: then xsum [d/32] fp32
   const Dims& dm = a.dm;
   const int b = blockIdx.z, k = blockIdx.y;
   const bool shared = (k == dm.K);
@@ -51,9 +53,10 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(GateUpArgs a) {
   const int d = dm.d;
 
   const uint32_t *gq, *uq;
-  const uint16_t *gs, *us;
+  const uint16_t *gs, *us, *gb = nullptr, *ub = nullptr;
   if (shared) {
     gq = a.sh.gate.q; gs = a.sh.gate.s; uq = a.sh.up.q; us = a.sh.up.s;
+    gb = a.sh.gate.b; ub = a.sh.up.b;
   } else {
     const int64_t ent = resolve_entry(a.pool, dm.E, a.idx[b * dm.K + k]);
     if (ent < 0) {
@@ -64,10 +67,22 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(GateUpArgs a) {
     uq = (const uint32_t*)entry_ptr(a.pool.up.q, ent, a.pool.stride_q);
     gs = (const uint16_t*)entry_ptr(a.pool.gate.s, ent, a.pool.stride_s);
     us = (const uint16_t*)entry_ptr(a.pool.up.s, ent, a.pool.stride_s);
+    if (AFF) {
+      gb = (const uint16_t*)entry_ptr(a.pool.gate.b, ent, a.pool.stride_s);
+      ub = (const uint16_t*)entry_ptr(a.pool.up.b, ent, a.pool.stride_s);
+    }
   }
 
   const uint16_t* xb = a.x + (int64_t)b * d;
   for (int i = threadIdx.x; i < d; i += blockDim.x) xs[perm8(i)] = xb[i];
+  float* xsum = reinterpret_cast<float*>(xs + d);
+  if (AFF) {
+    for (int c = threadIdx.x; c < d / 32; c += blockDim.x) {
+      float sum = 0.0f;
+      for (int i = 0; i < 32; ++i) sum += h2f(xb[32 * c + i]);
+      xsum[c] = sum;
+    }
+  }
   __syncthreads();
 
   constexpr int kRowsPerWave = 64 / LG;
@@ -83,7 +98,11 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(GateUpArgs a) {
   const uint16_t* usr = us + (int64_t)row * spr;
 
   float ag, au;
-  gateup_rowpair<LG, CPL>(grow, urow, gsr, usr, dm.G, xs, li, ag, au);
+  if (AFF)
+    gateup_rowpair_aff<LG, CPL>(grow, urow, gsr, usr, gb + (int64_t)row * spr,
+                                ub + (int64_t)row * spr, dm.G, xs, xsum, li, ag, au);
+  else
+    gateup_rowpair<LG, CPL>(grow, urow, gsr, usr, dm.G, xs, li, ag, au);
   if (shared && a.sh.bg) {
     const float* axb = a.ax + (int64_t)b * 3 * a.rmax;
     float lg = 0.0f, lu = 0.0f;
@@ -120,9 +139,10 @@ struct DownArgs {
 // y[row] = sum_k w_k Wd_k[row] . h_k + Wd_s[row] . h_s (+ down LoRA)
 // [MW §3.1 Math contract; CB "The mechanism" (shared_experts = 1)].
 // Output fp16(resid + y). grid = (row blocks of d, B).
-template <int LG, int CPL>
+template <int LG, int CPL, bool AFF>
 __global__ __launch_bounds__(kBlock) void k_down(DownArgs a) {
-  extern __shared__ uint16_t hs[];  // [nexp][2][I] pair-permuted hi / lo
+  extern __shared__ uint16_t hs[];  // [nexp][2][I] pair-permuted hi / lo; affine: then
+                                    // hsum [nexp][I/32] fp32 (chunk sums of hi + lo)
   __shared__ float coef[16];
   __shared__ int64_t ent_s[16];
   __shared__ float red[4];
@@ -156,6 +176,19 @@ __global__ __launch_bounds__(kBlock) void k_down(DownArgs a) {
     }
   }
   __syncthreads();
+  float* hsum = reinterpret_cast<float*>(hs + (int64_t)nexp * 2 * I);
+  if (AFF) {
+    // the pair permutation stays inside 8-element blocks, so positions
+    // 32c .. 32c+31 hold exactly chunk c
+    for (int j = threadIdx.x; j < nexp * (I / 32); j += blockDim.x) {
+      const int k = j / (I / 32), c = j % (I / 32);
+      const uint16_t* hh = hs + (int64_t)k * 2 * I + 32 * c;
+      float sum = 0.0f;
+      for (int i = 0; i < 32; ++i) sum += h2f(hh[i]) + h2f(hh[I + i]);
+      hsum[j] = sum;
+    }
+    __syncthreads();
+  }
 
   constexpr int kRowsPerWave = 64 / LG;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -168,17 +201,25 @@ __global__ __launch_bounds__(kBlock) void k_down(DownArgs a) {
   for (int k = 0; k < nexp; ++k) {
     if (k < dm.K && ent_s[k] < 0) continue;
     const uint32_t* q;
-    const uint16_t* s;
+    const uint16_t *s, *bq = nullptr;
     if (k < dm.K) {
       q = (const uint32_t*)entry_ptr(a.pool.down.q, ent_s[k], a.pool.stride_q);
       s = (const uint16_t*)entry_ptr(a.pool.down.s, ent_s[k], a.pool.stride_s);
+      if (AFF) bq = (const uint16_t*)entry_ptr(a.pool.down.b, ent_s[k], a.pool.stride_s);
     } else {
       q = a.sh.down.q;
       s = a.sh.down.s;
+      bq = a.sh.down.b;
     }
     const uint16_t* hh = hs + (int64_t)k * 2 * I;
-    const float part = down_row_hl<LG, CPL>(q + (int64_t)row * wpr, s + (int64_t)row * spr, dm.G,
-                                            hh, hh + I, li);
+    float part;
+    if (AFF)
+      part = down_row_hl_aff<LG, CPL>(q + (int64_t)row * wpr, s + (int64_t)row * spr,
+                                      bq + (int64_t)row * spr, dm.G, hh, hh + I,
+                                      hsum + (int64_t)k * (I / 32), li);
+    else
+      part = down_row_hl<LG, CPL>(q + (int64_t)row * wpr, s + (int64_t)row * spr, dm.G, hh,
+                                  hh + I, li);
     acc += coef[k] * part;
   }
   if (a.sh.present && a.sh.bd) {
@@ -404,14 +445,20 @@ static hipError_t q4_dispatch(int lg, int cpl, A&&... args) {
 template <int LG, int CPL>
 struct GateUpOp {
   static void run(dim3 grid, size_t lds, hipStream_t st, const GateUpArgs& a) {
-    k_gate_up<LG, CPL><<<grid, kBlock, lds, st>>>(a);
+    if (a.dm.affine)
+      k_gate_up<LG, CPL, true><<<grid, kBlock, lds, st>>>(a);
+    else
+      k_gate_up<LG, CPL, false><<<grid, kBlock, lds, st>>>(a);
   }
 };
 
 template <int LG, int CPL>
 struct DownOp {
   static void run(dim3 grid, size_t lds, hipStream_t st, const DownArgs& a) {
-    k_down<LG, CPL><<<grid, kBlock, lds, st>>>(a);
+    if (a.dm.affine)
+      k_down<LG, CPL, true><<<grid, kBlock, lds, st>>>(a);
+    else
+      k_down<LG, CPL, false><<<grid, kBlock, lds, st>>>(a);
   }
 };
 
@@ -427,7 +474,7 @@ hipError_t launch_gate_up(const Dims& dm, const Pool& pool, const SharedW& sh,
   const int rows = imax_of(dm);
   const int rpb = (kBlock / 64) * (64 / lg);
   dim3 grid((rows + rpb - 1) / rpb, dm.K + 1, B);
-  const size_t lds = (size_t)dm.d * sizeof(uint16_t);
+  const size_t lds = (size_t)dm.d * sizeof(uint16_t) + (dm.affine ? (size_t)dm.d / 32 * 4 : 0);
   return q4_dispatch<GateUpOp>(lg, cpl, grid, lds, st, a);
 }
 
@@ -440,7 +487,8 @@ hipError_t launch_down(const Dims& dm, const Pool& pool, const SharedW& sh,
   const int rpb = (kBlock / 64) * (64 / lg);
   dim3 grid((dm.d + rpb - 1) / rpb, B);
   const int nexp = dm.K + (sh.present ? 1 : 0);
-  const size_t lds = (size_t)nexp * 2 * dm.I * sizeof(uint16_t);
+  const size_t lds = (size_t)nexp * 2 * dm.I * sizeof(uint16_t) +
+                     (dm.affine ? (size_t)nexp * (dm.I / 32) * 4 : 0);
   return q4_dispatch<DownOp>(lg, cpl, grid, lds, st, a);
 }
 

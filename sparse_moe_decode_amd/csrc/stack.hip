@@ -1088,6 +1088,7 @@ int span(int per, int block) { return per <= 0 ? 0 : (per - 1) / block + 2; }
 }  // namespace
 
 bool stack_supported(const Dims& dm) {
+  if (dm.affine) return false;  // symmetric codec only; affine stacks run per phase
   if (dm.d % 512 || dm.I != kStackI || dm.K > 8 || dm.E > kMaxE) return false;
   if (dm.G < 32 || (dm.G & (dm.G - 1)) || dm.d % dm.G || dm.d / dm.G > 32) return false;
   if (dm.Is != 0 && dm.Is != dm.I) return false;
