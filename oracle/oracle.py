@@ -522,3 +522,45 @@ def moe_decode_affine(dims: dict, routed: dict, shared: dict | None, x16, idx, w
             ys = ys + c * (f(shared["b_down"]) @ (f(shared["a_down"]) @ h))
         y += ys
     return y
+
+
+class LayerOracleAffine:
+    """One layer-step with affine routed and shared experts, same interface
+    and outputs as LayerOracle.step. The codec changes only the experts'
+    weights ([MW] §3.1), so the step is the same sequence: h_attn = h + attn
+    stand-in, x = fp16(rmsnorm(h_attn)), routing from the layer's router
+    (or the consumed prediction), h_out = h_attn + moe_decode_affine(x), and
+    the head's logits and top-K on x (the helpers above)."""
+
+    def __init__(self, dims: dict, layer: dict):
+        self.dims = dims
+        self.layer = layer
+        self.has_head = layer.get("head") is not None
+        self.has_router = layer.get("router") is not None
+
+    def step(self, h16, route_idx=None, route_w=None, prev_idx=None, x16=None) -> dict:
+        dm, lw = self.dims, self.layer
+        d, E, K = dm["d"], dm["E"], dm["K"]
+        ha = f16_decode(h16)
+        if lw.get("attn") is not None:
+            ha = ha + f16_decode(lw["attn"])
+        own = f16_round(rmsnorm(ha, float(dm.get("eps", 1e-6))))
+        x = own if x16 is None else _u16(x16)
+        out = dict(x16=own, router_logits=np.full(E, np.nan), head_logits=np.full(E, np.nan),
+                   pred_idx=np.full(K, -1, np.int32), pred_w=np.full(K, np.nan))
+        if self.has_router:
+            lg = f16_decode(lw["router"]).reshape(E, d) @ f16_decode(x)
+            out["router_logits"] = lg
+            idx, w = route(dm, lg, lw.get("router_bias"))
+        else:
+            idx = np.asarray(route_idx, np.int32).copy()
+            w = np.asarray(route_w, np.float32).astype(np.float64)
+        out["exec_idx"], out["exec_w"] = idx, w
+        xf = f16_decode(x).astype(np.float16)
+        out["h_out"] = ha + moe_decode_affine(dm, lw["routed"], lw.get("shared"), xf, idx, w)
+        if self.has_head:
+            hd = lw["head"]
+            lg = head_logits(hd["fc1"], hd["fc2"], hd["lin"], d, E, dm["P"], K, x, idx, prev_idx)
+            out["head_logits"] = lg
+            out["pred_idx"], out["pred_w"] = route(dm, lg, hd.get("bias"))
+        return out

@@ -9,6 +9,7 @@ set, computes that one layer-step in fp64 and compares:
   * h_out within 2e-3 + 1e-2 |ref|;
   * head logits (2e-4 absolute) and the prediction for layer l+1 (near-tie
     rule, weights 1e-4).
+quant=1 checks layers with affine int4 experts against the affine layer oracle.
 """
 
 from __future__ import annotations
@@ -21,9 +22,10 @@ from sparse_moe_decode_amd import synth
 
 class StackChecker:
     def __init__(self, orc, tier: str, seed: int, roles: list[dict], layers: list[int],
-                 host_layers: dict | None = None, zero_mean: bool = False):
+                 host_layers: dict | None = None, zero_mean: bool = False, quant: int = 0):
         self.orc = orc
-        self.dm = synth.dims(tier)
+        self.dm = synth.dims(tier, quant=1) if quant == 1 else synth.dims(tier)
+        oracle_cls = orc.LayerOracleAffine if quant == 1 else orc.LayerOracle
         self.roles = roles
         self.L = len(roles)
         self.layers = layers
@@ -33,11 +35,11 @@ class StackChecker:
             if lw is None:
                 lw = synth.layer(seed, l, self.dm, roles[l], zero_mean=zero_mean)
             self.w[l] = lw
-            self.lo[l] = orc.LayerOracle(self.dm, lw)
+            self.lo[l] = oracle_cls(self.dm, lw)
             if lw["router"] is not None:
                 cons = dict(lw)
                 cons["router"] = None
-                self.lo_cons[l] = orc.LayerOracle(self.dm, cons)
+                self.lo_cons[l] = oracle_cls(self.dm, cons)
         self.worst = 0.0
         self.x_ulp_diffs = 0
         self.reanchored = 0

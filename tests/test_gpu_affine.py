@@ -5,12 +5,15 @@ moe_int4_decode on affine experts takes the per-token GEMV kernels for every
 batch size (the grouped MFMA path is symmetric-only): 35B shapes at B = 1, 4
 and 20, 8B and tiny shapes, the shared expert with its LoRA, an expert pool
 read through the bundle layout (scales then biases), and a bad id flagged.
+layer_step on affine layers runs one kernel per phase (the persistent kernel
+is symmetric-only and refuses them); every layer-step is checked against the
+affine layer oracle, re-anchored on the GPU's own inputs.
 """
 
 import numpy as np
 import pytest
 
-from gpu_util import announce, dev, dev_tree, f16_to_f64
+from gpu_util import announce, dev, dev_tree, f16_to_f64, host
 from helpers import assert_out_close, out_err
 from sparse_moe_decode_amd import synth
 
@@ -80,4 +83,54 @@ def test_affine_bad_id_is_flagged(api):
     idx[1, 0] = dm["E"] + 1
     api.moe_int4_decode(ctx, dev_tree(pool), dev(x), dev(idx), dev(w))
     assert api.device_status(ctx) == api.E0_ERR_RANGE
+    ctx.close()
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("tier,T", [("tiny", 8), ("8b", 3), ("35b", 3)])
+def test_affine_layer_step_matches_oracle(api, orc, tier, T):
+    import torch
+    from stack_check import StackChecker
+    from sparse_moe_decode_amd import workloads as wl
+    dm = synth.dims(tier, quant=1)
+    roles = [dict(router=True, head=True), dict(router=False, head=True)]
+    L, seed = len(roles), 33
+    layers, keep = [], {}
+    for l, role in enumerate(roles):
+        lw = synth.layer(seed, l, dm, role)
+        keep[l] = lw
+        layers.append(dict(routed=wl.tree_to_dev(lw["routed"]), shared=wl.tree_to_dev(lw["shared"]),
+                           attn=dev(lw["attn"]),
+                           router=None if lw["router"] is None else dev(lw["router"]),
+                           router_bias=(None if lw["router_bias"] is None
+                                        else dev(lw["router_bias"])),
+                           head=wl.tree_to_dev(lw["head"])))
+    ctx = api.Context(dm, max_tokens=1)
+    model = api.Model(ctx, layers)
+    with pytest.raises(RuntimeError):
+        model.set_path(api.PATH_PERSISTENT)
+    state = api.State(dm, L)
+    idx0, w0 = wl.initial_routing(tier, seed, L)
+    state.route_idx[0].copy_(torch.from_numpy(idx0))
+    state.route_w[0].copy_(torch.from_numpy(w0))
+    toks = wl.token_inputs(tier, seed, T, 0.5)
+    checker = StackChecker(orc, tier, seed, roles, [0, 1], keep, quant=1)
+    prev_exec = None
+    h = torch.empty((L + 1, dm["d"]), dtype=torch.float16, device="cuda")
+    for t in range(T):
+        announce("affine layer_step", tier, f"token {t}")
+        h[0].copy_(torch.from_numpy(toks[t]))
+        api.layer_step(ctx, model, 0, L, state, t, h)
+        assert api.device_status(ctx) == 0
+        cur, nxt = t & 1, (t + 1) & 1
+        exec_idx = host(state.exec_idx[cur]).copy()
+        checker.check(t, host(h).copy(), host(state.x_trace).copy(), exec_idx,
+                      host(state.exec_w[cur]).copy(), prev_exec,
+                      host(state.route_idx[cur]).copy(), host(state.route_w[cur]).copy(),
+                      host(state.route_idx[nxt]).copy(), host(state.route_w[nxt]).copy(),
+                      host(state.head_logits).copy())
+        prev_exec = exec_idx
+    print(f"affine {tier} layer_step: {checker.steps} layer-steps checked, worst error ratio "
+          f"{checker.worst:.3f}")
+    model.close()
     ctx.close()

@@ -37,16 +37,18 @@ ROLES = [dict(router=True, head=True), dict(router=False, head=True),
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("tier,T,reserve,group", [("35b", 5, 0, 1), ("8b", 4, 0, 1),
-                                                  ("35b", 4, 16, 2), ("8b", 4, 8, 3)])
-def test_staged_stack_matches_oracle(api, orc, tier, T, reserve, group):
+@pytest.mark.parametrize("tier,T,reserve,group,quant", [("35b", 5, 0, 1, 0), ("8b", 4, 0, 1, 0),
+                                                        ("35b", 4, 16, 2, 0), ("8b", 4, 8, 3, 0),
+                                                        ("35b", 3, 0, 2, 1)])
+def test_staged_stack_matches_oracle(api, orc, tier, T, reserve, group, quant):
     """reserve > 0 runs the persistent kernel on fewer workgroups than compute
     units (staging copies then run beside the layers); group = predicted
-    layers per launch."""
+    layers per launch; quant = 1 stages affine bundles (scales, then biases)
+    and runs the layers one kernel per phase."""
     import torch
     from sparse_moe_decode_amd import pipeline
     from sparse_moe_decode_amd import workloads as wl
-    dm = synth.dims(tier)
+    dm = synth.dims(tier, quant=1) if quant else synth.dims(tier)
     E, K, L = dm["E"], dm["K"], len(ROLES)
     n_slots = 2 * K
     seed = 41
@@ -82,7 +84,8 @@ def test_staged_stack_matches_oracle(api, orc, tier, T, reserve, group):
     state.route_idx[0].copy_(torch.from_numpy(idx0))
     state.route_w[0].copy_(torch.from_numpy(w0))
     toks = wl.token_inputs(tier, seed, T, rho=0.5)  # sets change between tokens: copies happen
-    checker = StackChecker(orc, tier, seed, ROLES, list(range(L)), keep, zero_mean=True)
+    checker = StackChecker(orc, tier, seed, ROLES, list(range(L)), keep, zero_mean=True,
+                           quant=quant)
     pipe = pipeline.StagedStack(ctx, model, state, stager, cons, L, reserve_cus=reserve,
                                 group=group)
 
@@ -95,7 +98,7 @@ def test_staged_stack_matches_oracle(api, orc, tier, T, reserve, group):
     prev_exec = None
     h = torch.zeros((L + 1, dm["d"]), dtype=torch.float16, device="cuda")
     for t in range(T):
-        announce("staged layer_step", tier, f"L={L} reserve={reserve} group={group}",
+        announce("staged layer_step", tier, f"L={L} reserve={reserve} group={group} quant={quant}",
                  f"token {t}")
         h[0].copy_(torch.from_numpy(toks[t]))
         pipe.run_token(t, h)

@@ -81,3 +81,36 @@ def test_pages_byte_counts():
     assert e35 == 3 * 512 * 2048 // 2 + (3 * 512 * 2048 // 64) * 2 * 2 == 1_769_472
     assert e35 * 256 == 452_984_832
     assert api.bundle_bytes_of(synth.dims("8b", quant=1)) == 1_327_104
+
+
+@pytest.mark.parametrize("tier", ["tiny", "8b"])
+def test_affine_layer_step_matches_symmetric_identity(orc, tier):
+    """The affine layer-step (routing, head and residual around the affine
+    MoE) equals the C++ symmetric layer-step on the same weights, on a router
+    layer with a head and on a predicted layer."""
+    dm = synth.dims(tier)
+    keys = ("gate", "up", "down")
+    for l, role in enumerate([dict(router=True, head=True), dict(router=False, head=True)]):
+        lw = synth.layer(23, l, dm, role)
+        lw["routed"] = {k: v[:dm["E"]] for k, v in lw["routed"].items()}
+        _bf16_exact_scales(lw["routed"], keys)
+        _bf16_exact_scales(lw["shared"], keys)
+        alw = dict(lw, routed=_as_affine(lw["routed"], keys), shared=_as_affine(lw["shared"], keys))
+        sym = orc.LayerOracle(dm, lw)
+        aff = orc.LayerOracleAffine(dict(dm, quant=1), alw)
+        rng = synth.rng_for(24, l)
+        h = rng.normal(size=dm["d"]).astype(np.float16)
+        ri = synth.random_set(rng, dm["E"], dm["K"])
+        rw = synth.random_weights(rng, dm["K"])
+        prev = synth.random_set(rng, dm["E"], dm["K"])
+        kw = {} if role["router"] else dict(route_idx=ri, route_w=rw)
+        a, s = aff.step(h, prev_idx=prev, **kw), sym.step(h, prev_idx=prev, **kw)
+        assert np.array_equal(a["x16"], s["x16"])
+        assert list(a["exec_idx"]) == list(s["exec_idx"])
+        np.testing.assert_allclose(a["exec_w"], s["exec_w"], rtol=1e-12)
+        np.testing.assert_allclose(a["h_out"], s["h_out"], rtol=1e-10, atol=1e-10)
+        np.testing.assert_allclose(a["head_logits"], s["head_logits"], rtol=1e-10, atol=1e-12)
+        assert list(a["pred_idx"]) == list(s["pred_idx"])
+        if role["router"]:
+            np.testing.assert_allclose(a["router_logits"], s["router_logits"], rtol=1e-10,
+                                       atol=1e-12)
