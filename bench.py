@@ -101,14 +101,16 @@ def copy_probe(nbytes: int):
 def algorithmic_bytes(dm: dict, roles: list[dict]) -> dict:
     """Weight bytes one decode token must read (activations, < 20 KB, ignored).
 
-    Routed: K experts x (gate + up + down) packed nibbles + fp16 scales.
-    Shared expert likewise, plus its LoRA A/B (fp16). Head: dense fc1/lin
-    columns over d, fc2, and only the 2K gathered one-hot columns of fc1 and
-    lin. Router: fp16 [E, d] on layers that run their own router.
+    Routed: K experts x (gate + up + down) packed nibbles + fp16 scales
+    (affine codec: bf16 scales and bf16 biases). Shared expert likewise, plus
+    its LoRA A/B (fp16). Head: dense fc1/lin columns over d, fc2, and only the
+    2K gathered one-hot columns of fc1 and lin. Router: fp16 [E, d] on layers
+    that run their own router.
     """
     d, E, K, I, Is, P, G, r = (dm[k] for k in ("d", "E", "K", "I", "Is", "P", "G", "r"))
-    expert = 3 * (I * d // 2) + 3 * 2 * (I * d // G)
-    shared = 3 * (Is * d // 2) + 3 * 2 * (Is * d // G)
+    per_group = 2 * (2 if dm.get("quant", 0) == 1 else 1)
+    expert = 3 * (I * d // 2) + 3 * per_group * (I * d // G)
+    shared = 3 * (Is * d // 2) + 3 * per_group * (Is * d // G)
     lora = 2 * (r * d + Is * r) * 2 + (r * Is + d * r) * 2
     head = 2 * (P * d + E * d + E * P) + 2 * (2 * K) * (P + E)
     router = 2 * E * d
@@ -121,13 +123,15 @@ def algorithmic_bytes(dm: dict, roles: list[dict]) -> dict:
     return parts
 
 
-def cpu_baseline(tier: str, seed: int, roles, host_layers, toks, idx0, w0, n_tokens: int):
+def cpu_baseline(tier: str, seed: int, roles, host_layers, toks, idx0, w0, n_tokens: int,
+                 quant: int = 0):
     """The fp64 oracle (single thread) on the first tokens of the same workload."""
     import oracle
     from sparse_moe_decode_amd import synth
-    dm = synth.dims(tier)
+    dm = synth.dims(tier, quant=1) if quant == 1 else synth.dims(tier)
     L = len(roles)
-    los = [oracle.LayerOracle(dm, host_layers[l]) for l in range(L)]
+    cls = oracle.LayerOracleAffine if quant == 1 else oracle.LayerOracle
+    los = [cls(dm, host_layers[l]) for l in range(L)]
     pred_idx = {l: idx0[l] for l in range(L)}
     pred_w = {l: w0[l].astype(np.float64) for l in range(L)}
     prev = [None] * L
@@ -715,6 +719,9 @@ def main():
     ap.add_argument("--cache-entries", type=int, default=0,
                     help="staged workload: stage through one cross-layer hot cache of this "
                          "many bundles (0: 2K slots per layer)")
+    ap.add_argument("--quant", choices=["symmetric", "affine"], default="symmetric",
+                    help="stack workload: int4 codec of the experts (affine: the pages' "
+                         "unsigned nibbles with bf16 scale and bias per group)")
     ap.add_argument("--chunk-k", type=int, default=0, choices=[0, 2, 4, 8],
                     help="chunk workload: only this top-K (0 = 2, 4 and 8)")
     ap.add_argument("--prefill-b", type=int, default=3072,
@@ -750,7 +757,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     tier = "35b"
-    dm = synth.dims(tier)
+    quant = 1 if args.quant == "affine" else 0
+    dm = synth.dims(tier, quant=1) if quant else synth.dims(tier)
     roles = synth.stack_roles(tier)
     L = len(roles)
     T = args.warmup + args.steps
@@ -818,11 +826,12 @@ def main():
     gbs = ab["total"] / (ms * 1e-3) / 1e9
     kgbs = ab["total"] / (kernel_ms * 1e-3) / 1e9
     copy_gbs = copy_bandwidth()
-    traffic = measured_traffic()
+    traffic = measured_traffic() if not quant else None  # counters taken on the symmetric run
     tok_s = 1000.0 / ms
     cpu = None
     if keep_host:
-        cpu = cpu_baseline(tier, args.seed, roles, host_layers, toks, idx0, w0, args.cpu_tokens)
+        cpu = cpu_baseline(tier, args.seed, roles, host_layers, toks, idx0, w0, args.cpu_tokens,
+                           quant)
 
     out = {
         "metric": METRIC,
@@ -835,13 +844,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 weights x fp16 activations, fp32 accumulate",
+        "dtype": ("int4 weights x fp16 activations, fp32 accumulate" if not quant else
+                  "affine int4 weights (bf16 scale and bias) x fp16 activations, fp32 accumulate"),
         "data": "synthetic (seeded; random-init weights of the 35B-tier shapes)",
         "config": {
             "workload": "35B-tier full decode stack, batch 1: 40 MoE layers (d=2048, E=256, "
                         "K=4, I=512, shared I=512 with LoRA r=16), prerouter heads on layers "
                         "6-38, own fp16 router on layers 0-6 and 39, attention replaced by a "
-                        "fixed fp16 residual update",
+                        "fixed fp16 residual update" + (
+                            "; experts in the affine int4 codec (unsigned nibbles, bf16 scale "
+                            "and bias per 64)" if quant else ""),
             "tokens_timed": args.steps, "layers": L, "batch": 1,
             "token_correlation_rho": args.rho,
             "weights_resident_GB": round(sum(

@@ -47,6 +47,7 @@ constexpr uint64_t kSpinLimit = 20000000ull;  // 0.2 s of the 100 MHz wall clock
 constexpr int kMaxL = 64;      // layers per launch (routing tables in LDS)
 constexpr int kNR = 4;         // fp16 rows per workgroup per block job (router, LoRA A)
 constexpr int kMaxExp = 9;     // experts per down row: K <= 8 routed + the shared expert
+constexpr int kEp = 9;         // base addresses per expert slot (q, s, b of gate, up, down)
 constexpr int kRank = 16;      // LoRA rank of this kernel (or no LoRA at all)
 constexpr int kStackI = 512;   // expert intermediate width of this kernel
 constexpr int kHX = 4;         // head layers one workgroup keeps x / fc2 activations of
@@ -175,9 +176,13 @@ struct Misc {
   float axgu[2 * kRank];       // A_gate x then A_up x (rows of the shared expert)
   // base addresses of a layer's experts (slot k < K routed, k == K shared;
   // null when unused or unresolved): gate q, up q, down q, gate s, up s,
-  // down s. Two sets by layer parity: the next layer's is written while the
-  // current one is read.
-  const void* eptr[2][kMaxExp][6];
+  // down s, then (affine codec) gate b, up b, down b. Two sets by layer
+  // parity: the next layer's is written while the current one is read.
+  const void* eptr[2][kMaxExp][kEp];
+  // affine codec: sums of the normed x over each 32-element chunk, and of
+  // each expert's hi + lo SwiGLU chunk (the bias terms b * sum)
+  float xsum[64];
+  float hsum[kMaxExp][16];
   float red16[kRank][kGroups];
   float hsc[kHX][16];          // scales of the fc2 activation chunks (per lane)
   float red[4 * kNR];
@@ -286,9 +291,11 @@ __device__ __forceinline__ void f16rows_finish(const F16Rows<NR>& R, int nr, int
 
 // Base addresses of expert slot k of a layer into ep[k] (see Misc::eptr);
 // ent: the slot's pool entry (routed slots, k < K).
-__device__ __forceinline__ void fill_slot(const void* (&ep)[6], const LayerDev& Ly, int K, int k,
+// Biases (affine codec) sit at the scales' entry offsets: stride_s apart.
+__device__ __forceinline__ void fill_slot(const void* (&ep)[kEp], const LayerDev& Ly, int K, int k,
                                           int64_t ent) {
-  const void* p[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  const void* p[kEp] = {nullptr, nullptr, nullptr, nullptr, nullptr,
+                        nullptr, nullptr, nullptr, nullptr};
   if (k < K && ent >= 0) {
     p[0] = entry_ptr(Ly.pool.gate.q, ent, Ly.pool.stride_q);
     p[1] = entry_ptr(Ly.pool.up.q, ent, Ly.pool.stride_q);
@@ -296,6 +303,11 @@ __device__ __forceinline__ void fill_slot(const void* (&ep)[6], const LayerDev& 
     p[3] = entry_ptr(Ly.pool.gate.s, ent, Ly.pool.stride_s);
     p[4] = entry_ptr(Ly.pool.up.s, ent, Ly.pool.stride_s);
     p[5] = entry_ptr(Ly.pool.down.s, ent, Ly.pool.stride_s);
+    if (Ly.pool.gate.b) {
+      p[6] = entry_ptr(Ly.pool.gate.b, ent, Ly.pool.stride_s);
+      p[7] = entry_ptr(Ly.pool.up.b, ent, Ly.pool.stride_s);
+      p[8] = entry_ptr(Ly.pool.down.b, ent, Ly.pool.stride_s);
+    }
   } else if (k == K && Ly.sh.present) {
     p[0] = Ly.sh.gate.q;
     p[1] = Ly.sh.up.q;
@@ -303,9 +315,12 @@ __device__ __forceinline__ void fill_slot(const void* (&ep)[6], const LayerDev& 
     p[3] = Ly.sh.gate.s;
     p[4] = Ly.sh.up.s;
     p[5] = Ly.sh.down.s;
+    p[6] = Ly.sh.gate.b;
+    p[7] = Ly.sh.up.b;
+    p[8] = Ly.sh.down.b;
   }
 #pragma unroll
-  for (int i = 0; i < 6; ++i) ep[i] = p[i];
+  for (int i = 0; i < kEp; ++i) ep[i] = p[i];
 }
 
 // ---- gate/up items of one lane group (IPG items per group) ---------------
@@ -315,6 +330,7 @@ struct GuRegs {
   // group scales of the item's row, two per lane (lane li: scales 2li, 2li+1;
   // a row has d/G <= 32 of them); a chunk's scale is fetched from its lane
   uint32_t sg[IPG], su[IPG];
+  uint32_t bg[IPG], bu[IPG];  // affine codec: the group biases, packed like the scales
   uint16_t lbg[IPG], lbu[IPG];  // shared items: element li of the row of LoRA B_gate / B_up
 };
 
@@ -324,9 +340,9 @@ struct GuPlan {
 
 // Gate/up rows of the group's items, addressed through the layer's slot
 // table ep (LDS); items of unresolved routed slots are skipped.
-template <int CPL, int IPG>
+template <int CPL, int IPG, bool AFF>
 __device__ __forceinline__ void gu_issue(GuRegs<CPL, IPG>& R, const LayerDev& Ly, const Dims& dm,
-                                         const void* const (*ep)[6], int n_rt, const GuPlan& pl,
+                                         const void* const (*ep)[kEp], int n_rt, const GuPlan& pl,
                                          int grp, int li) {
 #pragma unroll
   for (int j = 0; j < IPG; ++j) {
@@ -358,6 +374,12 @@ __device__ __forceinline__ void gu_issue(GuRegs<CPL, IPG>& R, const LayerDev& Ly
     // spr is even and rows start 4-byte aligned: one 4-byte load per lane
     R.sg[j] = 2 * li < spr ? ldg(reinterpret_cast<const uint32_t*>(gs + (int64_t)row * spr) + li) : 0u;
     R.su[j] = 2 * li < spr ? ldg(reinterpret_cast<const uint32_t*>(us + (int64_t)row * spr) + li) : 0u;
+    if (AFF) {
+      const uint16_t* gb = (const uint16_t*)ep[k][6];
+      const uint16_t* ub = (const uint16_t*)ep[k][7];
+      R.bg[j] = 2 * li < spr ? ldg(reinterpret_cast<const uint32_t*>(gb + (int64_t)row * spr) + li) : 0u;
+      R.bu[j] = 2 * li < spr ? ldg(reinterpret_cast<const uint32_t*>(ub + (int64_t)row * spr) + li) : 0u;
+    }
   }
 }
 
@@ -366,18 +388,22 @@ __device__ __forceinline__ void gu_issue(GuRegs<CPL, IPG>& R, const LayerDev& Ly
 // for gu_finish_shared (its LoRA terms need the layer's A products).
 // Scale (32 c) >> gsh of a row whose scales the lane group holds two per
 // lane (the group's lanes are active together).
+// BF16: the packed values are bf16 (affine codec) rather than fp16.
+template <bool BF16 = false>
 __device__ __forceinline__ float row_scale(uint32_t packed, int c, int gsh) {
   const int idx = (32 * c) >> gsh;
   const int base = (int)(threadIdx.x & 63) & ~(kLG - 1);
   const uint32_t v = (uint32_t)__shfl((int)packed, base + (idx >> 1));
-  return h2f((uint16_t)((idx & 1) ? v >> 16 : v & 0xFFFFu));
+  const uint16_t b = (uint16_t)((idx & 1) ? v >> 16 : v & 0xFFFFu);
+  return BF16 ? bf2f(b) : h2f(b);
 }
 
-template <int CPL, int IPG>
+// AFF: affine items add b * (sum of the chunk's x), xsum per 32 elements.
+template <int CPL, int IPG, bool AFF>
 __device__ __forceinline__ void gu_finish(const GuRegs<CPL, IPG>& R, const int64_t* ent_k,
                                           int n_rt, const GuPlan& pl, int grp, int li, int gsh,
-                                          const uint16_t* xperm, uint64_t* xg, uint32_t ep,
-                                          float (&sg_out)[IPG], float (&su_out)[IPG]) {
+                                          const uint16_t* xperm, const float* xsum, uint64_t* xg,
+                                          uint32_t ep, float (&sg_out)[IPG], float (&su_out)[IPG]) {
 #pragma unroll
   for (int j = 0; j < IPG; ++j) {
     const int it = pl.ib + grp + kGroups * j;
@@ -391,8 +417,16 @@ __device__ __forceinline__ void gu_finish(const GuRegs<CPL, IPG>& R, const int64
         f16x2 xr[16];
         load_xchunk(xperm, li + kLG * c2, xr);
         const int c = li + kLG * c2;
-        ag += row_scale(R.sg[j], c, gsh) * q4_dot32(R.wg[j][c2], xr);
-        au += row_scale(R.su[j], c, gsh) * q4_dot32(R.wu[j][c2], xr);
+        if (AFF) {
+          const float xs = xsum[c];
+          ag += row_scale<true>(R.sg[j], c, gsh) * q4_dot32<true>(R.wg[j][c2], xr) +
+                row_scale<true>(R.bg[j], c, gsh) * xs;
+          au += row_scale<true>(R.su[j], c, gsh) * q4_dot32<true>(R.wu[j][c2], xr) +
+                row_scale<true>(R.bu[j], c, gsh) * xs;
+        } else {
+          ag += row_scale(R.sg[j], c, gsh) * q4_dot32(R.wg[j][c2], xr);
+          au += row_scale(R.su[j], c, gsh) * q4_dot32(R.wu[j][c2], xr);
+        }
       }
     }
     ag = group_sum<kLG>(ag);
@@ -432,6 +466,7 @@ template <int NX>
 struct DownRegs {
   uint4 w[NX];
   uint16_t s[NX];
+  uint16_t b[NX];  // affine codec: the chunk's group bias
   uint4 bd[kRank / 8];  // LoRA B of the down projection, row drow (lane 0 of the group)
 };
 
@@ -443,9 +478,11 @@ struct LoraRegs {
 // Lane li of a 16-lane group holds elements 32c + 2li and 32c + 2li + 1 of an
 // I-vector. The group converts chunk c to fp16 hi + lo scaled by a power of
 // two 2^-e chosen from the chunk's max |v|, written pair-permuted to dst (hi
-// at dst[0, I), lo at dst[I, 2I)); returns 2^e. All 16 lanes must be active.
+// at dst[0, I), lo at dst[I, 2I)); returns 2^e. With hsum non-null, lane 0
+// writes there the chunk's sum of hi + lo (for the affine bias terms). All 16
+// lanes must be active.
 __device__ __forceinline__ float hilo_pair(float v0, float v1, int c, int li, uint16_t* dst,
-                                           int I) {
+                                           int I, float* hsum = nullptr) {
   const float m = group_max<kLG>(fmaxf(fabsf(v0), fabsf(v1)));
   const int e = hilo_exponent(m);
   const float inv = ldexpf(1.0f, -e);
@@ -458,6 +495,10 @@ __device__ __forceinline__ float hilo_pair(float v0, float v1, int c, int li, ui
   dst[p1] = __builtin_bit_cast(uint16_t, h1);
   dst[I + p0] = __builtin_bit_cast(uint16_t, l0);
   dst[I + p1] = __builtin_bit_cast(uint16_t, l1);
+  if (hsum) {
+    const float sum = group_sum<kLG>(((float)h0 + (float)l0) + ((float)h1 + (float)l1));
+    if (li == 0) *hsum = sum;
+  }
   return ldexpf(1.0f, e);
 }
 
@@ -476,8 +517,9 @@ struct PhaseA {
 };
 
 // CPL_D: 16-byte chunks per lane of a d-wide int4 row; IPG: gate/up items
-// per lane group; NX: expert slots per down row (K routed + shared).
-template <int CPL_D, int IPG, int NX>
+// per lane group; NX: expert slots per down row (K routed + shared); AFF:
+// the affine int4 codec (bf16 scales and biases, unsigned nibbles).
+template <int CPL_D, int IPG, int NX, bool AFF>
 __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
   constexpr int CPH = 4 * CPL_D;  // 16-byte chunks per lane of a d-wide fp16 head row
   extern __shared__ __align__(16) unsigned char smem[];
@@ -565,7 +607,7 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
   // [drow] of every expert slot, LoRA B_down row, the shared expert's A_down.
   // Issued once this workgroup's gate/up outputs are published, so that
   // issuing them overlaps the wait for everyone else's.
-  auto issue_b = [&](const LayerDev& Ly, const void* const (*ep_k)[6], PhaseA<CPL_D, IPG, NX>& A) {
+  auto issue_b = [&](const LayerDev& Ly, const void* const (*ep_k)[kEp], PhaseA<CPL_D, IPG, NX>& A) {
     const bool has_sh = Ly.sh.present != 0;
     const int Is = has_sh ? dm.Is : 0;
     const bool lora_d = has_sh && Ly.sh.ad != nullptr;
@@ -576,12 +618,15 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
       for (int k = 0; k < NX; ++k) {
         A.D.w[k] = make_uint4(0, 0, 0, 0);
         A.D.s[k] = 0;
+        A.D.b[k] = 0;
         if (k > K) continue;
         const uint32_t* q = (const uint32_t*)ep_k[k][2];
         const uint16_t* sc = (const uint16_t*)ep_k[k][5];
         if (!q) continue;
         A.D.w[k] = ldg(reinterpret_cast<const uint4*>(q + (int64_t)drow * wpr + 4 * li));
         A.D.s[k] = ldg(sc + (int64_t)drow * spr + ((32 * li) >> gsh));
+        if (AFF)
+          A.D.b[k] = ldg((const uint16_t*)ep_k[k][8] + (int64_t)drow * spr + ((32 * li) >> gsh));
       }
 #pragma unroll
       for (int c = 0; c < kRank / 8; ++c) {
@@ -624,7 +669,7 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
       // routing known: entries from the tables
       GuPlan pl;
       split(K * I + Is, G, cu, pl.ib, pl.ie);
-      gu_issue<CPL_D, IPG>(A.gu, Ly, dm, ms.eptr[(l - a.l0) & 1], K * I, pl, grp, li);
+      gu_issue<CPL_D, IPG, AFF>(A.gu, Ly, dm, ms.eptr[(l - a.l0) & 1], K * I, pl, grp, li);
       A.gu_loaded = true;
     }
   };
@@ -693,6 +738,16 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
                                      xv[2] | ((uint32_t)xv[6] << 16), xv[3] | ((uint32_t)xv[7] << 16));
         *reinterpret_cast<uint4*>(xnat + 8 * t) = nat;
         *reinterpret_cast<uint4*>(xperm + 8 * t) = per;
+        if (AFF) {
+          // chunk c (32 elements) is held by threads 4c .. 4c+3; d / 8 is a
+          // multiple of 64, so whole waves take this branch
+          float sx = 0.0f;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) sx += h2f(xv[q]);
+          sx += __shfl_xor(sx, 1);
+          sx += __shfl_xor(sx, 2);
+          if ((t & 3) == 0) ms.xsum[t >> 2] = sx;
+        }
         if (keep_x) *reinterpret_cast<uint4*>(hx + (hid - hx0) * d + 8 * t) = nat;
         if (cu == 0 && a.x_trace) *reinterpret_cast<uint4*>(a.x_trace + (int64_t)l * d + 8 * t) = nat;
       }
@@ -756,11 +811,12 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
     {
       GuPlan pl;
       split(n_rt + Is, G, cu, pl.ib, pl.ie);
-      if (!A.gu_loaded) gu_issue<CPL_D, IPG>(A.gu, Ly, dm, ms.eptr[step & 1], n_rt, pl, grp, li);
+      if (!A.gu_loaded)
+        gu_issue<CPL_D, IPG, AFF>(A.gu, Ly, dm, ms.eptr[step & 1], n_rt, pl, grp, li);
       vm_drained();  // gate/up rows, router and LoRA A rows have arrived
       float shg[IPG], shu[IPG];
-      gu_finish<CPL_D, IPG>(A.gu, ent_k, n_rt, pl, grp, li, __builtin_ctz(dm.G), xperm, xg, ep,
-                            shg, shu);
+      gu_finish<CPL_D, IPG, AFF>(A.gu, ent_k, n_rt, pl, grp, li, __builtin_ctz(dm.G), xperm,
+                                 ms.xsum, xg, ep, shg, shu);
       if (pl.ie > n_rt) {  // this workgroup owns rows of the shared expert
         const float* axgu = nullptr;
         if (r2) {
@@ -796,7 +852,8 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
         // the shared expert's SwiGLU outputs, LoRA terms included
         const float2 hb = *reinterpret_cast<const float2*>(lf + n_rt + 2 * t);
         const float h0 = hb.x, h1 = hb.y;
-        const float sc = hilo_pair(h0, h1, grp, li, hk + K * 2 * I, I);
+        const float sc = hilo_pair(h0, h1, grp, li, hk + K * 2 * I, I,
+                                   AFF ? &ms.hsum[K][grp] : nullptr);
         if (li == 0) ms.csc[K][grp] = sc;
         if (lora_d) {
 #pragma unroll
@@ -814,13 +871,15 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
 #pragma unroll
         for (int k = 0; k < NX - 1; ++k) {
           const float2 v = *reinterpret_cast<const float2*>(lf + k * I + 32 * grp + 2 * li);
-          const float sc = hilo_pair(v.x, v.y, grp, li, hk + k * 2 * I, I);
+          const float sc = hilo_pair(v.x, v.y, grp, li, hk + k * 2 * I, I,
+                                     AFF ? &ms.hsum[k][grp] : nullptr);
           if (li == 0) ms.csc[k][grp] = sc;
         }
       } else {
         for (int k = 0; k < K; ++k) {
           const float2 v = *reinterpret_cast<const float2*>(lf + k * I + 32 * grp + 2 * li);
-          const float sc = hilo_pair(v.x, v.y, grp, li, hk + k * 2 * I, I);
+          const float sc = hilo_pair(v.x, v.y, grp, li, hk + k * 2 * I, I,
+                                     AFF ? &ms.hsum[k][grp] : nullptr);
           if (li == 0) ms.csc[k][grp] = sc;
         }
       }
@@ -847,7 +906,11 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
           f16x2 xh[16], xl[16];
           load_xchunk(hh, li, xh);
           load_xchunk(hh + I, li, xl);
-          acc += (ms.coef[k] * ms.csc[k][li]) * (h2f(D.s[k]) * q4_dot32_hl(D.w[k], xh, xl));
+          if (AFF)
+            acc += (ms.coef[k] * ms.csc[k][li]) *
+                   (bf2f(D.s[k]) * q4_dot32_hl<true>(D.w[k], xh, xl) + bf2f(D.b[k]) * ms.hsum[k][li]);
+          else
+            acc += (ms.coef[k] * ms.csc[k][li]) * (h2f(D.s[k]) * q4_dot32_hl(D.w[k], xh, xl));
         }
       } else {
 #pragma unroll
@@ -857,7 +920,11 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
           f16x2 xh[16], xl[16];
           load_xchunk(hh, li, xh);
           load_xchunk(hh + I, li, xl);
-          acc += (ms.coef[k] * ms.csc[k][li]) * (h2f(D.s[k]) * q4_dot32_hl(D.w[k], xh, xl));
+          if (AFF)
+            acc += (ms.coef[k] * ms.csc[k][li]) *
+                   (bf2f(D.s[k]) * q4_dot32_hl<true>(D.w[k], xh, xl) + bf2f(D.b[k]) * ms.hsum[k][li]);
+          else
+            acc += (ms.coef[k] * ms.csc[k][li]) * (h2f(D.s[k]) * q4_dot32_hl(D.w[k], xh, xl));
         }
       }
       if (lora_d && li == 0) {
@@ -1067,18 +1134,24 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
   stamp(a, hrow, 4);
 }
 
-template <int CPL_D, int IPG, int NX>
+template <int CPL_D, int IPG, int NX, bool AFF>
 hipError_t launch_stack_t(const StackArgs& a, int grid, hipStream_t st) {
   const Lds lo = lds_layout(a.dm, a.ng, a.l1 - a.l0);
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute((const void*)k_stack<CPL_D, IPG, NX>,
+    (void)hipFuncSetAttribute((const void*)k_stack<CPL_D, IPG, NX, AFF>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     attr_set = true;
   }
-  hipLaunchKernelGGL((k_stack<CPL_D, IPG, NX>), dim3(grid), dim3(kThreads), (size_t)lo.bytes, st,
-                     a);
+  hipLaunchKernelGGL((k_stack<CPL_D, IPG, NX, AFF>), dim3(grid), dim3(kThreads), (size_t)lo.bytes,
+                     st, a);
   return hipGetLastError();
+}
+
+template <int CPL_D, int IPG, int NX>
+hipError_t launch_stack_c(const StackArgs& a, int grid, hipStream_t st) {
+  return a.dm.affine ? launch_stack_t<CPL_D, IPG, NX, true>(a, grid, st)
+                     : launch_stack_t<CPL_D, IPG, NX, false>(a, grid, st);
 }
 
 // Largest number of consecutive blocks of size `block` that a contiguous
@@ -1088,7 +1161,6 @@ int span(int per, int block) { return per <= 0 ? 0 : (per - 1) / block + 2; }
 }  // namespace
 
 bool stack_supported(const Dims& dm) {
-  if (dm.affine) return false;  // symmetric codec only; affine stacks run per phase
   if (dm.d % 512 || dm.I != kStackI || dm.K > 8 || dm.E > kMaxE) return false;
   if (dm.G < 32 || (dm.G & (dm.G - 1)) || dm.d % dm.G || dm.d / dm.G > 32) return false;
   if (dm.Is != 0 && dm.Is != dm.I) return false;
@@ -1128,11 +1200,11 @@ hipError_t launch_stack(const StackArgs& a, int grid, hipStream_t st) {
   // instantiated shapes: top-4 (5 expert slots) with one gate/up item per
   // lane group, top-8 (9 slots) with up to two
   if (dm.K <= 4 && ipg <= kGroups) {
-    if (cpl == 3) return launch_stack_t<3, 1, 5>(a, grid, st);
-    if (cpl == 4) return launch_stack_t<4, 1, 5>(a, grid, st);
+    if (cpl == 3) return launch_stack_c<3, 1, 5>(a, grid, st);
+    if (cpl == 4) return launch_stack_c<4, 1, 5>(a, grid, st);
   } else if (ipg <= 2 * kGroups) {
-    if (cpl == 3) return launch_stack_t<3, 2, 9>(a, grid, st);
-    if (cpl == 4) return launch_stack_t<4, 2, 9>(a, grid, st);
+    if (cpl == 3) return launch_stack_c<3, 2, 9>(a, grid, st);
+    if (cpl == 4) return launch_stack_c<4, 2, 9>(a, grid, st);
   }
   return hipErrorInvalidValue;
 }

@@ -34,3 +34,11 @@ def test_stack_token_bytes():
     assert parts["heads"] == 33 * 3_420_160
     assert parts["routers"] == 8 * 2 * 256 * 2048
     assert parts["total"] == 465_317_888
+
+
+def test_stack_token_bytes_affine():
+    # the affine codec adds a bf16 bias per scale: 1,769,472 B per expert
+    parts = bench.algorithmic_bytes(synth.dims("35b", quant=1), synth.stack_roles("35b"))
+    assert parts["routed"] == 40 * 4 * 1_769_472
+    assert parts["shared"] == 40 * 1_769_472
+    assert parts["total"] == 465_317_888 + 200 * (1_769_472 - 1_671_168)

@@ -5,9 +5,10 @@ moe_int4_decode on affine experts takes the per-token GEMV kernels for every
 batch size (the grouped MFMA path is symmetric-only): 35B shapes at B = 1, 4
 and 20, 8B and tiny shapes, the shared expert with its LoRA, an expert pool
 read through the bundle layout (scales then biases), and a bad id flagged.
-layer_step on affine layers runs one kernel per phase (the persistent kernel
-is symmetric-only and refuses them); every layer-step is checked against the
-affine layer oracle, re-anchored on the GPU's own inputs.
+layer_step on affine layers runs on the persistent kernel (its affine
+variant) and on the per-phase kernels; every layer-step is checked against
+the affine layer oracle, re-anchored on the GPU's own inputs, on two-layer
+stacks and on the full 35B stack.
 """
 
 import numpy as np
@@ -86,19 +87,18 @@ def test_affine_bad_id_is_flagged(api):
     ctx.close()
 
 
-@pytest.mark.timeout(600)
-@pytest.mark.parametrize("tier,T", [("tiny", 8), ("8b", 3), ("35b", 3)])
-def test_affine_layer_step_matches_oracle(api, orc, tier, T):
+def _affine_stack(api, orc, tier, roles, T, path, seed, zero_mean=False):
     import torch
     from stack_check import StackChecker
     from sparse_moe_decode_amd import workloads as wl
     dm = synth.dims(tier, quant=1)
-    roles = [dict(router=True, head=True), dict(router=False, head=True)]
-    L, seed = len(roles), 33
+    L = len(roles)
     layers, keep = [], {}
     for l, role in enumerate(roles):
-        lw = synth.layer(seed, l, dm, role)
+        lw = synth.layer(seed, l, dm, role, zero_mean=zero_mean)
         keep[l] = lw
+        if L > 2:
+            announce("upload", tier, f"layer {l}/{L}")
         layers.append(dict(routed=wl.tree_to_dev(lw["routed"]), shared=wl.tree_to_dev(lw["shared"]),
                            attn=dev(lw["attn"]),
                            router=None if lw["router"] is None else dev(lw["router"]),
@@ -107,18 +107,17 @@ def test_affine_layer_step_matches_oracle(api, orc, tier, T):
                            head=wl.tree_to_dev(lw["head"])))
     ctx = api.Context(dm, max_tokens=1)
     model = api.Model(ctx, layers)
-    with pytest.raises(RuntimeError):
-        model.set_path(api.PATH_PERSISTENT)
+    model.set_path(api.PATH_PERSISTENT if path == "persistent" else api.PATH_PHASES)
     state = api.State(dm, L)
     idx0, w0 = wl.initial_routing(tier, seed, L)
     state.route_idx[0].copy_(torch.from_numpy(idx0))
     state.route_w[0].copy_(torch.from_numpy(w0))
     toks = wl.token_inputs(tier, seed, T, 0.5)
-    checker = StackChecker(orc, tier, seed, roles, [0, 1], keep, quant=1)
+    checker = StackChecker(orc, tier, seed, roles, list(range(L)), keep, zero_mean, quant=1)
     prev_exec = None
     h = torch.empty((L + 1, dm["d"]), dtype=torch.float16, device="cuda")
     for t in range(T):
-        announce("affine layer_step", tier, f"token {t}")
+        announce("affine layer_step", tier, path, f"L={L}", f"token {t}")
         h[0].copy_(torch.from_numpy(toks[t]))
         api.layer_step(ctx, model, 0, L, state, t, h)
         assert api.device_status(ctx) == 0
@@ -130,7 +129,26 @@ def test_affine_layer_step_matches_oracle(api, orc, tier, T):
                       host(state.route_idx[nxt]).copy(), host(state.route_w[nxt]).copy(),
                       host(state.head_logits).copy())
         prev_exec = exec_idx
-    print(f"affine {tier} layer_step: {checker.steps} layer-steps checked, worst error ratio "
-          f"{checker.worst:.3f}")
+    print(f"affine {tier} {path} L={L}: {checker.steps} layer-steps checked, worst error ratio "
+          f"{checker.worst:.3f}, re-anchored router sets {checker.reanchored}")
     model.close()
     ctx.close()
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("tier,T,path", [("tiny", 8, "phases"), ("8b", 3, "phases"),
+                                         ("35b", 3, "phases"), ("8b", 3, "persistent"),
+                                         ("35b", 3, "persistent")])
+def test_affine_layer_step_matches_oracle(api, orc, tier, T, path):
+    """Layer 0 runs its router and owns a head predicting layer 1; layer 1
+    consumes that prediction and owns a head with no consumer."""
+    roles = [dict(router=True, head=True), dict(router=False, head=True)]
+    _affine_stack(api, orc, tier, roles, T, path, seed=33)
+
+
+@pytest.mark.timeout(900)
+def test_affine_stack_35b_persistent(api, orc):
+    """The full 35B stack (40 layers, heads on 6-38) with affine experts on
+    the persistent kernel, the benchmark's launch configuration."""
+    _affine_stack(api, orc, "35b", synth.stack_roles("35b"), 2, "persistent", seed=3,
+                  zero_mean=True)
