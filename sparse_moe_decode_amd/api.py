@@ -22,7 +22,10 @@ if not os.path.exists(LIB_PATH):
 _lib = C.CDLL(LIB_PATH)
 
 E0_OK = 0
+E0_ERR_ARG = -1
+E0_ERR_SHAPE = -2
 E0_ERR_ALIGN = -3
+E0_ERR_HIP = -4
 E0_ERR_RANGE = -5
 E0_ERR_SYNC = -6
 E0_ERR_STATE = -7
