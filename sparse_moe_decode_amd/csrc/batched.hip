@@ -98,54 +98,64 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-// Block B of k_mb_prep: the B*K entries sorted by expert (ascending expert
+// Block 0 of k_mb_prep: the B*K entries sorted by expert (ascending expert
 // id, then entry order), the union of experts with each member's run, and
-// the work tiles. Integer counting only, so nothing depends on thread timing:
-// counts by LDS atomics, offsets by prefix sums, then a stable placement over
-// 256 entries per pass. Lanes of a wave that hold the same expert find each
-// other with one ballot per bit of the id; an entry's rank is the number of
-// its expert's entries in earlier waves of the pass (per-wave counts in LDS,
-// tagged with the pass) plus earlier lanes of its own wave, after the
-// expert's running cursor. kMaxE = 512 ids take nine bits.
+// the work tiles. Integer counting only, so nothing depends on thread timing.
+// Each wave owns a contiguous quarter of the entries:
+//   1. it counts its quarter per expert (LDS atomics: order-independent);
+//   2. thread t takes experts 2t and 2t+1: offsets, union positions and tile
+//      positions by prefix sums, and each wave's cursor for them (the
+//      expert's offset plus its entries in earlier quarters);
+//   3. each wave walks its quarter 64 entries at a time, in order, with no
+//      block barrier: lanes that hold the same expert find each other with
+//      one ballot per bit of the id, an entry lands at the wave's cursor plus
+//      its rank among them, and their first lane advances the cursor.
+// kMaxE = 512 ids take nine bits. Each lane keeps kGrpDepth loads in flight.
+constexpr int kGrpDepth = 16;
+
 __device__ void group_entries(const MbArgs& a) {
-  __shared__ int cnt[kMaxE];
-  __shared__ int cur[kMaxE];
-  __shared__ int wcnt[4][kMaxE];  // (pass tag << 16) | entries of the wave
+  __shared__ int wcnt[4][kMaxE];  // counts of wave w's quarter, then its cursors
   __shared__ int wtot[3][4];
   const int E = a.dm.E, K = a.dm.K, BK = a.B * K;
   const Groups g = groups(a.grp, BK);
   const int t = threadIdx.x, nt = blockDim.x;
-  for (int e = t; e < kMaxE; e += nt) cnt[e] = 0;
+  const int wv = t >> 6, lane = t & 63;
+  const int cpw = ((BK + 63) / 64 + 3) / 4;  // 64-entry chunks per quarter
+  const int q0 = min(BK, wv * cpw * 64), q1 = min(BK, (wv + 1) * cpw * 64);
   for (int e = t; e < 4 * kMaxE; e += nt) (&wcnt[0][0])[e] = 0;
   __syncthreads();
-  for (int i0 = t; i0 < BK; i0 += 4 * nt) {
-    int ev[4];
+  for (int i0 = q0 + lane; i0 < q1; i0 += kGrpDepth * 64) {
+    int ev[kGrpDepth];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) ev[u] = i0 + u * nt < BK ? a.idx[i0 + u * nt] : -2;
+    for (int u = 0; u < kGrpDepth; ++u) ev[u] = i0 + 64 * u < q1 ? a.idx[i0 + 64 * u] : -2;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kGrpDepth; ++u) {
       if (ev[u] == -2) continue;
       if (ev[u] < 0 || ev[u] >= E)
         atomicOr(&a.flags[FLAG_RANGE], 1);
       else
-        atomicAdd(&cnt[ev[u]], 1);  // integer counts: order-independent
+        atomicAdd(&wcnt[wv][ev[u]], 1);
     }
   }
   __syncthreads();
-  // thread t owns experts 2t and 2t+1 (E <= 512): offsets, union positions
-  // and tile positions by prefix sums
-  const int c0 = cnt[2 * t], c1 = cnt[2 * t + 1];
+  int cw0[4], cw1[4], c0 = 0, c1 = 0;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    cw0[v] = wcnt[v][2 * t];
+    cw1[v] = wcnt[v][2 * t + 1];
+    c0 += cw0[v];
+    c1 += cw1[v];
+  }
   const int n0 = (c0 + a.tile - 1) / a.tile, n1 = (c1 + a.tile - 1) / a.tile;
   int ps = wave_incl_scan(c0 + c1);
   int pu = wave_incl_scan((c0 > 0) + (c1 > 0));
   int pt = wave_incl_scan(n0 + n1);
-  const int wv = t >> 6;
-  if ((t & 63) == 63) {
+  if (lane == 63) {
     wtot[0][wv] = ps;
     wtot[1][wv] = pu;
     wtot[2][wv] = pt;
   }
-  __syncthreads();
+  __syncthreads();  // also: every count has been read before it becomes a cursor
   for (int v = 0; v < wv; ++v) {
     ps += wtot[0][v];
     pu += wtot[1][v];
@@ -184,41 +194,43 @@ __device__ void group_entries(const MbArgs& a) {
     *g.n_union = pu;
     *g.n_tiles = n_sh + pt;
   }
-  cur[2 * t] = off0;
-  cur[2 * t + 1] = off0 + c0;
-  const uint64_t below = (1ull << (t & 63)) - 1;
-  // entries of the next four passes, loaded ahead
-  int e1 = t < BK ? a.idx[t] : -1, e2 = t + nt < BK ? a.idx[t + nt] : -1;
-  int e3 = t + 2 * nt < BK ? a.idx[t + 2 * nt] : -1, e4 = t + 3 * nt < BK ? a.idx[t + 3 * nt] : -1;
-  for (int p0 = 0, tag = 1; p0 < BK; p0 += nt, ++tag) {
-    const int i = p0 + t;
-    const int e = i < BK && e1 >= 0 && e1 < E ? e1 : -1;
-    e1 = e2;
-    e2 = e3;
-    e3 = e4;
-    e4 = i + 4 * nt < BK ? a.idx[i + 4 * nt] : -1;
-    uint64_t same = __ballot(e >= 0);
+  {
+    int o0 = off0, o1 = off0 + c0;
 #pragma unroll
-    for (int bit = 0; bit < 9; ++bit) {
-      const bool set = (e >> bit) & 1;
-      const uint64_t m = __ballot(set);
-      same &= set ? m : ~m;
+    for (int v = 0; v < 4; ++v) {
+      wcnt[v][2 * t] = o0;
+      wcnt[v][2 * t + 1] = o1;
+      o0 += cw0[v];
+      o1 += cw1[v];
     }
-    const int rank = __popcll(same & below), n_same = __popcll(same);
-    const bool leader = e >= 0 && rank == 0;
-    if (leader) wcnt[wv][e] = (tag << 16) | n_same;
-    // also orders the previous pass's cursor updates before the reads below
-    __syncthreads();
-    if (e >= 0) {
-      int base = cur[e] + rank;
-      for (int v = 0; v < wv; ++v) {
-        const int c = wcnt[v][e];
-        if ((c >> 16) == tag) base += c & 0xFFFF;
+  }
+  __syncthreads();
+  int* cur = wcnt[wv];
+  const uint64_t below = (1ull << lane) - 1;
+  for (int c = q0; c < q1; c += kGrpDepth * 64) {
+    int ev[kGrpDepth];
+#pragma unroll
+    for (int v = 0; v < kGrpDepth; ++v)
+      ev[v] = c + 64 * v + lane < q1 ? a.idx[c + 64 * v + lane] : -1;
+#pragma unroll
+    for (int v = 0; v < kGrpDepth; ++v) {
+      if (c + 64 * v >= q1) break;  // uniform over the wave
+      const int i = c + 64 * v + lane;
+      const int e = ev[v] >= 0 && ev[v] < E ? ev[v] : -1;
+      uint64_t same = __ballot(e >= 0);
+#pragma unroll
+      for (int bit = 0; bit < 9; ++bit) {
+        const bool set = (e >> bit) & 1;
+        const uint64_t m = __ballot(set);
+        same &= set ? m : ~m;
       }
-      g.sorted[base] = i;
+      const int rank = __popcll(same & below), n_same = __popcll(same);
+      if (e >= 0) g.sorted[cur[e] + rank] = i;
+      // every lane has read its cursor before the first lanes advance them
+      __builtin_amdgcn_wave_barrier();
+      if (e >= 0 && rank == 0) cur[e] += n_same;
+      __builtin_amdgcn_wave_barrier();
     }
-    __syncthreads();
-    if (leader) atomicAdd(&cur[e], n_same);  // integer sum: order-independent
   }
 }
 
