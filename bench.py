@@ -164,12 +164,14 @@ def run_chunk(args):
     path is [router | 0 | 0] (its logits are the router's exactly); it is
     input preparation, outside the timed loop. Weight bytes = the union of the
     batch's experts + the shared expert + its LoRA, each read once; flops =
-    2 B (K+1) 3 I d (the int4 x fp16 products, LoRA not counted)."""
+    2 B (K+1) 3 I d (the int4 x fp16 products, LoRA not counted). --quant
+    affine runs the experts in the affine codec (bf16 scales and biases)."""
     import torch
     from sparse_moe_decode_amd import api, synth
     from sparse_moe_decode_amd import workloads as wl
     tier = "35b"
-    dm0 = synth.dims(tier)
+    quant = 1 if args.quant == "affine" else 0
+    dm0 = synth.dims(tier, quant=1) if quant else synth.dims(tier)
     rng = synth.rng_for(args.seed, 70)
     pool = synth.routed_pool(rng, dm0)
     sh = synth.shared_expert(rng, dm0)
@@ -181,13 +183,13 @@ def run_chunk(args):
                    lin=torch.cat([wl.to_dev(router),
                                   torch.zeros((E, 2 * E), dtype=torch.float16, device="cuda")],
                                  dim=1).contiguous())
-    expert = 3 * (dm0["I"] * dm0["d"] // 2) + 3 * 2 * (dm0["I"] * dm0["d"] // dm0["G"])
+    expert = 3 * (dm0["I"] * dm0["d"] // 2) + 3 * 2 * (2 if quant else 1) * (dm0["I"] * dm0["d"] // dm0["G"])
     lora = 2 * (dm0["r"] * dm0["d"] + dm0["Is"] * dm0["r"]) * 2 + (dm0["r"] * dm0["Is"] + dm0["d"] * dm0["r"]) * 2
     lines = []
     for B in args.chunk_b:
         x = synth.f16_normal(synth.rng_for(args.seed, 72, B), (B, dm0["d"]))
         for K in ((2, 4, 8) if args.chunk_k == 0 else (args.chunk_k,)):
-            dm = synth.dims(tier, K=K)
+            dm = synth.dims(tier, K=K, quant=quant)
             ctx = api.Context(dm, max_tokens=B)
             dx = torch.from_numpy(x).cuda()
             krng = synth.rng_for(args.seed, 71, K)
@@ -224,7 +226,8 @@ def run_chunk(args):
             ctx.close()
             print(json.dumps(lines[-1]), file=sys.stderr, flush=True)
     print(json.dumps({"workload": "35B-tier batched tokens: one layer, grouped int4 MFMA "
-                                  "(moe_int4_decode, B>=16 path)", "steps": args.steps,
+                                  "(moe_int4_decode, B>=16 path)" +
+                                  (", affine int4 codec" if quant else ""), "steps": args.steps,
                       "warmup": args.warmup, "results": lines}))
 
 
@@ -720,8 +723,8 @@ def main():
                     help="staged workload: stage through one cross-layer hot cache of this "
                          "many bundles (0: 2K slots per layer)")
     ap.add_argument("--quant", choices=["symmetric", "affine"], default="symmetric",
-                    help="stack workload: int4 codec of the experts (affine: the pages' "
-                         "unsigned nibbles with bf16 scale and bias per group)")
+                    help="stack and chunk workloads: int4 codec of the experts (affine: the "
+                         "pages' unsigned nibbles with bf16 scale and bias per group)")
     ap.add_argument("--chunk-k", type=int, default=0, choices=[0, 2, 4, 8],
                     help="chunk workload: only this top-K (0 = 2, 4 and 8)")
     ap.add_argument("--prefill-b", type=int, default=3072,

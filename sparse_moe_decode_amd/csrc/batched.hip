@@ -83,6 +83,7 @@ struct MbArgs {
   int rmax;
   float* H;              // [B][K+1][imax] SwiGLU outputs
   float* Y;              // [B][K+1][d] per-slot down outputs
+  float* xsum;           // affine codec: [B][d/64] sums of each token's x per input group
   uint16_t* y;           // [B][d]
   int32_t* flags;
 };
@@ -234,22 +235,35 @@ __device__ void group_entries(const MbArgs& a) {
   }
 }
 
-// Blocks 0..B-1 of k_mb_prep: token b's pair-permuted x.
+// Blocks 0..B-1 of k_mb_prep: token b's pair-permuted x; for the affine
+// codec also its sum over each 64-input group (fp32 over the fp16 values:
+// chunk c of 8 values is thread c, and a group's 8 chunks are 8 adjacent
+// lanes).
 __device__ void prep_token(const MbArgs& a, int b) {
   const int d = a.dm.d;
   const uint16_t* xb = a.x + (int64_t)b * d;
-  for (int c = threadIdx.x; c < d / 8; c += blockDim.x) {
-    const uint4 v = ldg(reinterpret_cast<const uint4*>(xb + 8 * c));
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint16_t e[8];
+  for (int c0 = 0; c0 < d / 8; c0 += blockDim.x) {  // uniform over the block
+    const int c = c0 + threadIdx.x;
+    float sum = 0.0f;
+    if (c < d / 8) {
+      const uint4 v = ldg(reinterpret_cast<const uint4*>(xb + 8 * c));
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      uint16_t e[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      e[2 * q] = (uint16_t)(w[q] & 0xFFFF);
-      e[2 * q + 1] = (uint16_t)(w[q] >> 16);
+      for (int q = 0; q < 4; ++q) {
+        e[2 * q] = (uint16_t)(w[q] & 0xFFFF);
+        e[2 * q + 1] = (uint16_t)(w[q] >> 16);
+      }
+      *reinterpret_cast<uint4*>(a.xp + (int64_t)b * d + 8 * c) =
+          make_uint4(e[0] | ((uint32_t)e[4] << 16), e[1] | ((uint32_t)e[5] << 16),
+                     e[2] | ((uint32_t)e[6] << 16), e[3] | ((uint32_t)e[7] << 16));
+#pragma unroll
+      for (int q = 0; q < 8; ++q) sum += h2f(e[q]);
     }
-    *reinterpret_cast<uint4*>(a.xp + (int64_t)b * d + 8 * c) =
-        make_uint4(e[0] | ((uint32_t)e[4] << 16), e[1] | ((uint32_t)e[5] << 16),
-                   e[2] | ((uint32_t)e[6] << 16), e[3] | ((uint32_t)e[7] << 16));
+    if (a.dm.affine) {
+      sum = group_sum<8>(sum);
+      if (c < d / 8 && (c & 7) == 0) a.xsum[(int64_t)b * (d / 64) + (c >> 3)] = sum;
+    }
   }
 }
 
@@ -310,10 +324,12 @@ __global__ __launch_bounds__(256) void k_mb_prep(MbArgs a) {
 }
 
 // Eight int4 weights of one word as exact fp16 integers, in the order
-// q0 q4 q1 q5 q2 q6 q3 q7 (matching the pair-permuted activations).
+// q0 q4 q1 q5 q2 q6 q3 q7 (matching the pair-permuted activations); AFF:
+// unsigned nibbles (the affine codec) rather than two's complement.
+template <bool AFF = false>
 __device__ __forceinline__ h8 q4_to_h8(uint32_t w) {
   f16x2 p0, p1, p2, p3;
-  q4_pairs(w, p0, p1, p2, p3);
+  q4_pairs<AFF>(w, p0, p1, p2, p3);
   h8 r;
   r[0] = p0.x; r[1] = p0.y; r[2] = p1.x; r[3] = p1.y;
   r[4] = p2.x; r[5] = p2.y; r[6] = p3.x; r[7] = p3.y;
@@ -335,6 +351,10 @@ __device__ __forceinline__ void keep(f32x16& v) { asm volatile("" : "+v"(v)); }
 // tok_row(r, l/32) of weight row l%32.
 __device__ __forceinline__ int tok_row(int r, int kh) { return 8 * (r >> 2) + 4 * kh + (r & 3); }
 
+// A group scale or bias: fp16 (symmetric codec) or bf16 (affine codec).
+template <bool AFF>
+__device__ __forceinline__ float sb2f(uint16_t v) { return AFF ? bf2f(v) : h2f(v); }
+
 // acc[r] += s * c[r] for the NR registers that can hold a valid token: count
 // tokens occupy rows 0..count-1, i.e. registers r < NR = 4*ceil(count/8).
 template <int NR>
@@ -346,7 +366,7 @@ __device__ __forceinline__ void scale_add(f32x16& acc, const f32x16& c, float s)
 // Multiply-accumulate of one wave: NG groups of 64 inputs, weights wv (one
 // word per lane per MFMA), activations xv of the lane's token row
 // (pair-permuted fp16), group scales sv.
-template <int NG, int NR>
+template <int NG, int NR, bool AFF>
 __device__ __forceinline__ f32x16 gu_mma(const uint4 (&wv)[NG], const float (&sv)[NG],
                                          const uint4 (&xv)[NG][4]) {
   f32x16 acc = {};
@@ -355,8 +375,8 @@ __device__ __forceinline__ f32x16 gu_mma(const uint4 (&wv)[NG], const float (&sv
     f32x16 c = {};
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      c = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(xv[i][j]), q4_to_h8(word(wv[i], j)), c,
-                                                0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(xv[i][j]), q4_to_h8<AFF>(word(wv[i], j)),
+                                                c, 0, 0, 0);
     scale_add<NR>(acc, c, sv[i]);
     keep(acc);
   }
@@ -365,7 +385,7 @@ __device__ __forceinline__ f32x16 gu_mma(const uint4 (&wv)[NG], const float (&sv
 
 // Down multiply-accumulate: hi and lo activation rows (in LDS) through the
 // same dequantised weights.
-template <int NG, int NR>
+template <int NG, int NR, bool AFF>
 __device__ __forceinline__ f32x16 dn_mma(const uint4 (&wq)[NG], const float (&sc)[NG],
                                          const uint16_t* hrow, const uint16_t* lrow) {
   f32x16 acc = {};
@@ -377,7 +397,7 @@ __device__ __forceinline__ f32x16 dn_mma(const uint4 (&wq)[NG], const float (&sc
     for (int j = 0; j < 4; ++j) {
       const uint4 hv = *reinterpret_cast<const uint4*>(hrow + 64 * i + 8 * j);
       const uint4 lv = *reinterpret_cast<const uint4*>(lrow + 64 * i + 8 * j);
-      const h8 w8 = q4_to_h8(word(wq[i], j));
+      const h8 w8 = q4_to_h8<AFF>(word(wq[i], j));
       c = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(hv), w8, c, 0, 0, 0);
       c = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(lv), w8, c, 0, 0, 0);
     }
@@ -437,11 +457,13 @@ __device__ __forceinline__ bool tile_block(const MbArgs& a, int& bx, bool& share
 // waves: waves 0-3 the gate rows, 4-7 the up rows, each over a quarter of
 // the inputs (NG groups); partials meet in LDS. A wave issues all its loads
 // (weight words, scales, activations of its valid token rows) before the
-// first multiply.
-template <int NG>
+// first multiply. AFF (affine codec): each wave adds b * (the token's sum of
+// x over the group) for its groups, from sums staged in LDS.
+template <int NG, bool AFF>
 __global__ __launch_bounds__(512) void k_mb_gate_up(MbArgs a) {
   __shared__ float red[2][4][16][64];
   __shared__ float axs[kCols][2][kMaxR];
+  __shared__ float xss[AFF ? kCols : 1][32];  // [tile token][input group]
   const Dims& dm = a.dm;
   const int K = dm.K, d = dm.d;
   const int imax = dm.I > dm.Is ? dm.I : dm.Is;
@@ -455,10 +477,12 @@ __global__ __launch_bounds__(512) void k_mb_gate_up(MbArgs a) {
   const int mat = wave >> 2, quarter = wave & 3;  // 0 gate, 1 up
   const uint32_t* wq;
   const uint16_t* ws;
+  const uint16_t* wb = nullptr;
   const bool lora = shared && a.sh.ag;
   if (shared) {
     wq = mat ? a.sh.up.q : a.sh.gate.q;
     ws = mat ? a.sh.up.s : a.sh.gate.s;
+    if (AFF) wb = mat ? a.sh.up.b : a.sh.gate.b;
     if (lora) {  // LoRA A products of this tile's tokens: the slices in order
       for (int i = threadIdx.x; i < count * 2 * dm.r; i += blockDim.x) {
         const int tt = i / (2 * dm.r), j = i % (2 * dm.r);
@@ -479,8 +503,18 @@ __global__ __launch_bounds__(512) void k_mb_gate_up(MbArgs a) {
     const Q4& m = mat ? a.pool.up : a.pool.gate;
     wq = (const uint32_t*)entry_ptr(m.q, ent, a.pool.stride_q);
     ws = (const uint16_t*)entry_ptr(m.s, ent, a.pool.stride_s);
+    if (AFF) wb = (const uint16_t*)entry_ptr(m.b, ent, a.pool.stride_s);
   }
   const int ngs = d / dm.G, g0 = quarter * NG, wpr = d / 8;
+  if (AFF) {
+    for (int i = threadIdx.x; i < count * ngs; i += blockDim.x) {
+      const int tt = i / ngs, gg = i % ngs;
+      int b, k;
+      entry_of(a, shared, start, tt, b, k);
+      xss[tt][gg] = a.xsum[(int64_t)b * ngs + gg];
+    }
+    __syncthreads();
+  }
   const int nr = 4 * ((count + 7) >> 3);
   const uint32_t* qrow = wq + (int64_t)(m0 + n) * wpr + 4 * kh;
   const uint16_t* srow = ws + (int64_t)(m0 + n) * ngs;
@@ -490,11 +524,16 @@ __global__ __launch_bounds__(512) void k_mb_gate_up(MbArgs a) {
   entry_of(a, shared, start, n < count ? n : count - 1, bt, kt);
   const uint16_t* xrow = a.xp + (int64_t)bt * d + 32 * kh + 64 * g0;
   uint4 wv[NG];
-  float sv[NG];
+  float sv[NG], bv[NG];
 #pragma unroll
   for (int i = 0; i < NG; ++i) wv[i] = ldg(reinterpret_cast<const uint4*>(qrow + 8 * (g0 + i)));
 #pragma unroll
-  for (int i = 0; i < NG; ++i) sv[i] = h2f(ldg(srow + g0 + i));
+  for (int i = 0; i < NG; ++i) sv[i] = sb2f<AFF>(ldg(srow + g0 + i));
+  if (AFF) {
+    const uint16_t* brow = wb + (int64_t)(m0 + n) * ngs;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) bv[i] = bf2f(ldg(brow + g0 + i));
+  }
   uint4 xv[NG][4];
 #pragma unroll
   for (int i = 0; i < NG; ++i)
@@ -502,7 +541,17 @@ __global__ __launch_bounds__(512) void k_mb_gate_up(MbArgs a) {
     for (int j = 0; j < 4; ++j) xv[i][j] = ldg(reinterpret_cast<const uint4*>(xrow + 64 * i + 8 * j));
   // one variant for all counts: a second (fewer registers scaled) costs the
   // register allocator more than it saves
-  const f32x16 acc = gu_mma<NG, 16>(wv, sv, xv);
+  f32x16 acc = gu_mma<NG, 16, AFF>(wv, sv, xv);
+  if (AFF) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float* xsr = xss[tok_row(r, kh)] + g0;  // rows past count: never stored
+      float bsum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NG; ++i) bsum = fmaf(bv[i], xsr[i], bsum);
+      acc[r] += bsum;
+    }
+  }
 #pragma unroll
   for (int r = 0; r < 16; ++r)
     if (r < nr) red[mat][quarter][r][l] = acc[r];
@@ -544,13 +593,16 @@ __global__ __launch_bounds__(512) void k_mb_gate_up(MbArgs a) {
 // once in LDS as fp16 hi + lo under a power-of-two scale per token (about 22
 // bits of each value kept); hi and lo then go through the same dequantised
 // weights. Workgroups of the shared expert also form A_down . h for the down
-// LoRA, two tokens each.
+// LoRA, two tokens each. AFF (affine codec): the staging also forms each
+// token's sum of hi + lo over every input group, and the epilogue adds
+// b * that sum per group.
 constexpr int kDnPad = 8;  // fp16 padding per staged row (spreads LDS banks)
 
-template <int NG>
+template <int NG, bool AFF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_mb_down(MbArgs a) {
   extern __shared__ __align__(16) uint16_t hs[];  // [count][2][NG*64 + kDnPad]
   __shared__ float hx[kCols];                      // per-token power-of-two scale
+  __shared__ float hss[AFF ? kCols : 1][8];        // [token][input group] sums of hi + lo
   constexpr int nin = NG * 64, stride = nin + kDnPad, wpr = NG * 8;
   const Dims& dm = a.dm;
   const int K = dm.K, d = dm.d;
@@ -561,8 +613,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   if (!tile_block(a, bx, shared, u, start, count)) return;
   const uint32_t* dq;
   const uint16_t* ds;
+  const uint16_t* db = nullptr;
   if (shared) {
     dq = a.sh.down.q; ds = a.sh.down.s;
+    if (AFF) db = a.sh.down.b;
   } else {
     const Groups gv = groups(a.grp, a.B * K);
     const int e = gv.uexp[u];
@@ -570,19 +624,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     if (ent < 0) return;  // flagged by the gate/up step
     dq = (const uint32_t*)entry_ptr(a.pool.down.q, ent, a.pool.stride_q);
     ds = (const uint16_t*)entry_ptr(a.pool.down.s, ent, a.pool.stride_s);
+    if (AFF) db = (const uint16_t*)entry_ptr(a.pool.down.b, ent, a.pool.stride_s);
   }
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, n = l & 31, kh = l >> 5;
   const int m0 = (bx * 4 + wave) * 32;
   const bool rows_ok = m0 < d;
   uint4 wq[NG];
-  float sc[NG];
+  float sc[NG], bd[NG];
   if (rows_ok) {
     const uint32_t* qrow = dq + (int64_t)(m0 + n) * wpr + 4 * kh;
     const uint16_t* srow = ds + (int64_t)(m0 + n) * NG;
 #pragma unroll
     for (int i = 0; i < NG; ++i) wq[i] = ldg(reinterpret_cast<const uint4*>(qrow + 8 * i));
 #pragma unroll
-    for (int i = 0; i < NG; ++i) sc[i] = h2f(ldg(srow + i));
+    for (int i = 0; i < NG; ++i) sc[i] = sb2f<AFF>(ldg(srow + i));
+    if (AFF) {
+      const uint16_t* brow = db + (int64_t)(m0 + n) * NG;
+#pragma unroll
+      for (int i = 0; i < NG; ++i) bd[i] = bf2f(ldg(brow + i));
+    }
   }
   // stage: wave w takes tokens w, w+4, ...; lane l the 8 values of chunk l
   for (int t = wave; t < count; t += 4) {
@@ -601,6 +661,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
     const int e = hilo_exponent(wave_max_rows(m));
     const float inv = ldexpf(1.0f, -e);
+    float psum = 0.0f;
     if (l < NG * 8) {
       uint16_t hi[8], lo[8];
 #pragma unroll
@@ -609,6 +670,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         split_hilo(v[i], inv, th, tl);
         hi[i] = __builtin_bit_cast(uint16_t, th);
         lo[i] = __builtin_bit_cast(uint16_t, tl);
+        if (AFF) psum += (float)th + (float)tl;
       }
       // pair-permuted order [0 4 1 5 2 6 3 7]
       *reinterpret_cast<uint4*>(hs + (t * 2) * stride + 8 * l) =
@@ -617,6 +679,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       *reinterpret_cast<uint4*>(hs + (t * 2 + 1) * stride + 8 * l) =
           make_uint4(lo[0] | ((uint32_t)lo[4] << 16), lo[1] | ((uint32_t)lo[5] << 16),
                      lo[2] | ((uint32_t)lo[6] << 16), lo[3] | ((uint32_t)lo[7] << 16));
+    }
+    if (AFF) {
+      psum = group_sum<8>(psum);  // lanes 8g .. 8g+7 hold group g's chunks
+      if (l < NG * 8 && (l & 7) == 0) hss[t][l >> 3] = psum;
     }
     if (l == 0) hx[t] = ldexpf(1.0f, e);
   }
@@ -658,9 +724,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const uint16_t* lrow = hrow + stride;
   f32x16 acc;
   if (nr == 4)
-    acc = dn_mma<NG, 4>(wq, sc, hrow, lrow);
+    acc = dn_mma<NG, 4, AFF>(wq, sc, hrow, lrow);
   else
-    acc = dn_mma<NG, 16>(wq, sc, hrow, lrow);
+    acc = dn_mma<NG, 16, AFF>(wq, sc, hrow, lrow);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int t = tok_row(r, kh);
@@ -668,7 +734,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       int b, k;
       entry_of(a, shared, start, t, b, k);
       const int64_t slot = (int64_t)b * (K + 1) + k;
-      a.Y[slot * d + m0 + n] = acc[r] * hx[t];
+      float v = acc[r];
+      if (AFF) {
+#pragma unroll
+        for (int i = 0; i < NG; ++i) v = fmaf(bd[i], hss[t][i], v);
+      }
+      a.Y[slot * d + m0 + n] = v * hx[t];
     }
   }
 }
@@ -765,9 +836,13 @@ __device__ __forceinline__ float silu_fast(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
+// AFF (affine codec): the epilogue adds b * (the token's sum of x over the
+// group) for every group, from sums staged in LDS.
+template <bool AFF>
 __global__ __launch_bounds__(512) void k_pf_gate_up(MbArgs a) {
   __shared__ __align__(16) uint4 xs[2][kPfSG * 8 * kPfRow];
   __shared__ float axs[kPfTok][2][kMaxR];
+  __shared__ __align__(16) float xss[AFF ? 32 : 1][kPfTok];  // [input group][tile token]
   __shared__ int tokb[kPfTok], tokk[kPfTok];
   const Dims& dm = a.dm;
   const int K = dm.K, d = dm.d;
@@ -780,9 +855,13 @@ __global__ __launch_bounds__(512) void k_pf_gate_up(MbArgs a) {
   const int row = bx * kPfGuRows + wave * 32 + n;  // I % 256 == 0
   const bool lora = shared && a.sh.ag;
   const uint32_t *gq, *uq;
-  const uint16_t *gs, *us;
+  const uint16_t *gs, *us, *gb = nullptr, *ub = nullptr;
   if (shared) {
     gq = a.sh.gate.q; uq = a.sh.up.q; gs = a.sh.gate.s; us = a.sh.up.s;
+    if (AFF) {
+      gb = a.sh.gate.b;
+      ub = a.sh.up.b;
+    }
   } else {
     const Groups gv = groups(a.grp, a.B * K);
     const int64_t ent = resolve_entry(a.pool, dm.E, gv.uexp[u]);
@@ -794,6 +873,10 @@ __global__ __launch_bounds__(512) void k_pf_gate_up(MbArgs a) {
     uq = (const uint32_t*)entry_ptr(a.pool.up.q, ent, a.pool.stride_q);
     gs = (const uint16_t*)entry_ptr(a.pool.gate.s, ent, a.pool.stride_s);
     us = (const uint16_t*)entry_ptr(a.pool.up.s, ent, a.pool.stride_s);
+    if (AFF) {
+      gb = (const uint16_t*)entry_ptr(a.pool.gate.b, ent, a.pool.stride_s);
+      ub = (const uint16_t*)entry_ptr(a.pool.up.b, ent, a.pool.stride_s);
+    }
   }
   if (threadIdx.x < kPfTok) {
     // rows past count repeat the last token (their outputs are never stored)
@@ -840,10 +923,15 @@ __global__ __launch_bounds__(512) void k_pf_gate_up(MbArgs a) {
   for (int i = 0; i < kPfSG; ++i) {
     wg[i] = ldg(reinterpret_cast<const uint4*>(gro + 8 * i));
     wu[i] = ldg(reinterpret_cast<const uint4*>(uro + 8 * i));
-    sg[i] = h2f(ldg(gsr + i));
-    su[i] = h2f(ldg(usr + i));
+    sg[i] = sb2f<AFF>(ldg(gsr + i));
+    su[i] = sb2f<AFF>(ldg(usr + i));
   }
   load_x(0);
+  if (AFF)
+    for (int i = threadIdx.x; i < ngs * kPfTok; i += blockDim.x) {
+      const int gg = i / kPfTok, tt = i % kPfTok;
+      xss[gg][tt] = a.xsum[(int64_t)tokb[tt] * ngs + gg];
+    }
   store_x(0);
   __syncthreads();
   f32x16 ag0 = {}, ag1 = {}, au0 = {}, au1 = {};
@@ -860,15 +948,15 @@ __global__ __launch_bounds__(512) void k_pf_gate_up(MbArgs a) {
         const int gn = kPfSG * (st + 1) + g;
         wg[g] = ldg(reinterpret_cast<const uint4*>(gro + 8 * gn));
         wu[g] = ldg(reinterpret_cast<const uint4*>(uro + 8 * gn));
-        sg[g] = h2f(ldg(gsr + gn));
-        su[g] = h2f(ldg(usr + gn));
+        sg[g] = sb2f<AFF>(ldg(gsr + gn));
+        su[g] = sb2f<AFF>(ldg(usr + gn));
       }
       f32x16 cg0 = {}, cg1 = {}, cu0 = {}, cu1 = {};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int c = 8 * g + 4 * kh + j;
         const h8 x0 = as_h8(xb[pf_slot(c, n)]), x1 = as_h8(xb[pf_slot(c, 32 + n)]);
-        const h8 w_g = q4_to_h8(word(cwg, j)), w_u = q4_to_h8(word(cwu, j));
+        const h8 w_g = q4_to_h8<AFF>(word(cwg, j)), w_u = q4_to_h8<AFF>(word(cwu, j));
         cg0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(x0, w_g, cg0, 0, 0, 0);
         cg1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(x1, w_g, cg1, 0, 0, 0);
         cu0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(x0, w_u, cu0, 0, 0, 0);
@@ -885,6 +973,29 @@ __global__ __launch_bounds__(512) void k_pf_gate_up(MbArgs a) {
     }
     if (more) store_x((st + 1) & 1);
     __syncthreads();
+  }
+  if (AFF) {
+    // bias terms: the lane's row, every group; four consecutive tile tokens
+    // per 16-byte read of the sums
+    const uint16_t* gbr = gb + (int64_t)row * ngs;
+    const uint16_t* ubr = ub + (int64_t)row * ngs;
+#pragma unroll 4
+    for (int g = 0; g < ngs; ++g) {
+      const float bg = bf2f(ldg(gbr + g)), bu = bf2f(ldg(ubr + g));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 x0 = *reinterpret_cast<const float4*>(&xss[g][8 * j + 4 * kh]);
+        const float4 x1 = *reinterpret_cast<const float4*>(&xss[g][32 + 8 * j + 4 * kh]);
+        const float xa[4] = {x0.x, x0.y, x0.z, x0.w}, xb4[4] = {x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          ag0[4 * j + q] = fmaf(bg, xa[q], ag0[4 * j + q]);
+          au0[4 * j + q] = fmaf(bu, xa[q], au0[4 * j + q]);
+          ag1[4 * j + q] = fmaf(bg, xb4[q], ag1[4 * j + q]);
+          au1[4 * j + q] = fmaf(bu, xb4[q], au1[4 * j + q]);
+        }
+      }
+    }
   }
   // epilogue: shared-expert LoRA B terms, SwiGLU, fp32 store
   const float cl = dm.lora_scale;
@@ -923,11 +1034,14 @@ __global__ __launch_bounds__(512) void k_pf_gate_up(MbArgs a) {
 // (64 tokens x NG*64) are staged once in LDS as fp16 hi + lo under a
 // power-of-two scale per token; each dequantised weight word feeds four
 // MFMAs (hi and lo of both 32-token blocks). Workgroups of the shared
-// expert's tiles also form A_down . h for the down LoRA.
-template <int NG>
+// expert's tiles also form A_down . h for the down LoRA. AFF (affine
+// codec): the staging also forms each token's sum of hi + lo over every input
+// group, and the epilogue adds b * that sum per group.
+template <int NG, bool AFF>
 __global__ __launch_bounds__(512) void k_pf_down(MbArgs a) {
   extern __shared__ __align__(16) uint4 hsp[];  // [NG*8 chunks][hi, lo] x kPfTok slots
   __shared__ float hx[kPfTok];
+  __shared__ __align__(16) float hss[AFF ? NG : 1][kPfTok];  // [input group][tile token]
   __shared__ int tokb[kPfTok], tokk[kPfTok];
   constexpr int nin = NG * 64, nch = NG * 8;
   const Dims& dm = a.dm;
@@ -939,27 +1053,35 @@ __global__ __launch_bounds__(512) void k_pf_down(MbArgs a) {
   if (!tile_block(a, bx, shared, u, start, count)) return;
   const uint32_t* dq;
   const uint16_t* ds;
+  const uint16_t* db = nullptr;
   if (shared) {
     dq = a.sh.down.q;
     ds = a.sh.down.s;
+    if (AFF) db = a.sh.down.b;
   } else {
     const Groups gv = groups(a.grp, a.B * K);
     const int64_t ent = resolve_entry(a.pool, dm.E, gv.uexp[u]);
     if (ent < 0) return;  // flagged by the gate/up step
     dq = (const uint32_t*)entry_ptr(a.pool.down.q, ent, a.pool.stride_q);
     ds = (const uint16_t*)entry_ptr(a.pool.down.s, ent, a.pool.stride_s);
+    if (AFF) db = (const uint16_t*)entry_ptr(a.pool.down.b, ent, a.pool.stride_s);
   }
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, n = l & 31, kh = l >> 5;
   const int row = bx * 256 + wave * 32 + n;  // d % 256 == 0
   uint4 wq[NG];
-  float sc[NG];
+  float sc[NG], bd[NG];
   {
     const uint32_t* qrow = dq + (int64_t)row * (nin / 8) + 4 * kh;
     const uint16_t* srow = ds + (int64_t)row * NG;
 #pragma unroll
     for (int i = 0; i < NG; ++i) wq[i] = ldg(reinterpret_cast<const uint4*>(qrow + 8 * i));
 #pragma unroll
-    for (int i = 0; i < NG; ++i) sc[i] = h2f(ldg(srow + i));
+    for (int i = 0; i < NG; ++i) sc[i] = sb2f<AFF>(ldg(srow + i));
+    if (AFF) {
+      const uint16_t* brow = db + (int64_t)row * NG;
+#pragma unroll
+      for (int i = 0; i < NG; ++i) bd[i] = bf2f(ldg(brow + i));
+    }
   }
   if (threadIdx.x < kPfTok) {
     int b = 0, k = 0;
@@ -1004,7 +1126,7 @@ __global__ __launch_bounds__(512) void k_pf_down(MbArgs a) {
 #pragma unroll
     for (int cc = 0; cc < kCpl; ++cc) {
       const int c = l + 64 * cc;
-      if (c >= nch) continue;
+      float psum = 0.0f;
       uint16_t hi[8], lo[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
@@ -1012,7 +1134,15 @@ __global__ __launch_bounds__(512) void k_pf_down(MbArgs a) {
         split_hilo(v[cc][q], inv, th, tl);
         hi[q] = __builtin_bit_cast(uint16_t, th);
         lo[q] = __builtin_bit_cast(uint16_t, tl);
+        if (AFF) psum += (float)th + (float)tl;
       }
+      if (AFF) {
+        // lanes 8g .. 8g+7 hold group g's chunks (uniform over the wave;
+        // chunks past nch hold zeros)
+        psum = group_sum<8>(psum);
+        if (c < nch && (c & 7) == 0) hss[c >> 3][t] = psum;
+      }
+      if (c >= nch) continue;
       // pair-permuted order [0 4 1 5 2 6 3 7]
       hsp[pf_slot(2 * c, t)] =
           make_uint4(hi[0] | ((uint32_t)hi[4] << 16), hi[1] | ((uint32_t)hi[5] << 16),
@@ -1057,7 +1187,7 @@ __global__ __launch_bounds__(512) void k_pf_down(MbArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c = 8 * g + 4 * kh + j;
-      const h8 w8 = q4_to_h8(word(wq[g], j));
+      const h8 w8 = q4_to_h8<AFF>(word(wq[g], j));
       c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(hsp[pf_slot(2 * c, n)]), w8, c0, 0, 0, 0);
       c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(hsp[pf_slot(2 * c + 1, n)]), w8, c0, 0, 0, 0);
       c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(hsp[pf_slot(2 * c, 32 + n)]), w8, c1, 0, 0, 0);
@@ -1073,8 +1203,14 @@ __global__ __launch_bounds__(512) void k_pf_down(MbArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int t = 32 * tb + tok_row(r, kh);
-      if (t < count)
-        a.Y[((int64_t)tokb[t] * (K + 1) + tokk[t]) * d + row] = (tb ? acc1[r] : acc0[r]) * hx[t];
+      if (t < count) {
+        float v = tb ? acc1[r] : acc0[r];
+        if (AFF) {
+#pragma unroll
+          for (int i = 0; i < NG; ++i) v = fmaf(bd[i], hss[i][t], v);
+        }
+        a.Y[((int64_t)tokb[t] * (K + 1) + tokk[t]) * d + row] = v * hx[t];
+      }
     }
   }
 }
@@ -1083,8 +1219,7 @@ __global__ __launch_bounds__(512) void k_pf_down(MbArgs a) {
 
 bool batched_supported(const Dims& dm) {
   const int gu_groups = dm.G > 0 ? dm.d / dm.G : 0, dn_groups = dm.G > 0 ? dm.I / dm.G : 0;
-  // the symmetric codec only: affine experts take the per-token GEMV path
-  return !dm.affine && dm.G == 64 && dm.d % 128 == 0 && dm.I % 64 == 0 && gu_groups % 8 == 0 &&
+  return dm.G == 64 && dm.d % 128 == 0 && dm.I % 64 == 0 && gu_groups % 8 == 0 &&
          gu_groups <= 32 && dn_groups % 2 == 0 && dn_groups <= 8 && dm.K <= 8 &&
          dm.E <= kMaxE && dm.r % 8 == 0 && dm.r <= kMaxR && (dm.Is == 0 || dm.Is == dm.I);
 }
@@ -1100,23 +1235,35 @@ namespace {
 
 template <int NG>
 void launch_gate_up_ng(const MbArgs& a, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL(k_mb_gate_up<NG>, grid, dim3(512), 0, st, a);
+  if (a.dm.affine)
+    hipLaunchKernelGGL((k_mb_gate_up<NG, true>), grid, dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_mb_gate_up<NG, false>), grid, dim3(512), 0, st, a);
+}
+
+template <int NG, bool AFF>
+hipError_t launch_pf_down_t(const MbArgs& a, dim3 grid, hipStream_t st) {
+  const size_t lds = (size_t)NG * 8 * 2 * kPfRow * sizeof(uint4);
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)k_pf_down<NG, AFF>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((k_pf_down<NG, AFF>), grid, dim3(512), lds, st, a);
+  return hipSuccess;
 }
 
 template <int NG>
 hipError_t launch_pf_down_ng(const MbArgs& a, dim3 grid, hipStream_t st) {
-  const size_t lds = (size_t)NG * 8 * 2 * kPfRow * sizeof(uint4);
-  static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)k_pf_down<NG>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(k_pf_down<NG>, grid, dim3(512), lds, st, a);
-  return hipSuccess;
+  return a.dm.affine ? launch_pf_down_t<NG, true>(a, grid, st)
+                     : launch_pf_down_t<NG, false>(a, grid, st);
 }
 
 template <int NG>
 void launch_down_ng(const MbArgs& a, dim3 grid, hipStream_t st) {
   const size_t lds = (size_t)(a.B < kCols ? a.B : kCols) * 2 * (NG * 64 + kDnPad) * sizeof(uint16_t);
-  hipLaunchKernelGGL(k_mb_down<NG>, grid, dim3(256), lds, st, a);
+  if (a.dm.affine)
+    hipLaunchKernelGGL((k_mb_down<NG, true>), grid, dim3(256), lds, st, a);
+  else
+    hipLaunchKernelGGL((k_mb_down<NG, false>), grid, dim3(256), lds, st, a);
 }
 
 }  // namespace
@@ -1142,6 +1289,7 @@ hipError_t launch_batched(const Dims& dm, const Pool& pool, const SharedW& sh, c
   while (a.n_sl < kLoraSlices && (dm.d / 64) % (2 * a.n_sl) == 0) a.n_sl *= 2;
   a.H = s.gu;
   a.Y = s.yk;
+  a.xsum = s.hattn;  // unused by this path otherwise; [B][d] floats >= [B][d/64]
   a.y = y;
   a.flags = s.flags;
   const bool pf = (int64_t)B * dm.K >= (int64_t)kPrefillPerExpert * dm.E && prefill_supported(dm);
@@ -1152,7 +1300,10 @@ hipError_t launch_batched(const Dims& dm, const Pool& pool, const SharedW& sh, c
   const int lora_blocks = sh.present && sh.ag ? (B + kCols - 1) / kCols * a.n_sl : 0;
   hipLaunchKernelGGL(k_mb_prep, dim3(B + 1 + lora_blocks), dim3(256), 0, st, a);
   if (pf) {
-    hipLaunchKernelGGL(k_pf_gate_up, dim3(imax / kPfGuRows, ny), dim3(512), 0, st, a);
+    if (dm.affine)
+      hipLaunchKernelGGL(k_pf_gate_up<true>, dim3(imax / kPfGuRows, ny), dim3(512), 0, st, a);
+    else
+      hipLaunchKernelGGL(k_pf_gate_up<false>, dim3(imax / kPfGuRows, ny), dim3(512), 0, st, a);
     const dim3 grid(dm.d / 256, ny);
     hipError_t e;
     switch (dm.I / dm.G) {

@@ -63,7 +63,8 @@ struct Scratch {
   int32_t max_tokens;
   float* gu;      // [B][K+1][Imax] SwiGLU outputs (routed experts, then shared)
   float* ax;      // [B][3][rmax]   LoRA A products: gate, up, down
-  float* hattn;   // [B][d]         h + attention update (fp32)
+  float* hattn;   // [B][d]         h + attention update (fp32); the batched path's
+                  //                affine input sums [B][d/64]
   uint16_t* xn;   // [B][d]         fp16 RMS-normed activation
   float* hact;    // [B][P]         head hidden activation erf_gelu(fc1 f)
   float* hlin;    // [B][E]         head linear path lin f
