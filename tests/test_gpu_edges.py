@@ -7,7 +7,9 @@
   gets weight 1) against the oracle, on the per-token GEMV path (B = 1, 3)
   and on the grouped MFMA path (B = 16, 64) at the 35B shapes, and at the
   tiny shapes;
-* a batch of exactly max_tokens, and one above it.
+* a batch of exactly max_tokens, and one above it;
+* every expert selected (K = E): the head routes all of them in descending
+  score with the full softmax as weights, and the decode sums them all.
 """
 
 import ctypes as C
@@ -123,4 +125,39 @@ def test_top1_routing(api, orc, tier, B):
     for b in range(B):
         assert_out_close(yg[b], orc.moe_decode(dmn, pool, sh, x[b], idx[b], np.ones(1)),
                          f"{tier} K=1 token {b}")
+    ctx.close()
+
+
+def test_every_expert_selected(api, orc):
+    """K = E (the tiny tier's 8 experts, softmax routing): the head's routing
+    returns every expert in descending score with the full softmax as
+    weights, and the decode sums every expert."""
+    import torch
+    from gpu_util import host
+    from helpers import W_TOL
+    dm = synth.dims("tiny", K=8)
+    assert dm["K"] == dm["E"]
+    announce("edges", "tiny", "K = E")
+    rng = synth.rng_for(80)
+    pool, sh = synth.routed_pool(rng, dm), synth.shared_expert(rng, dm)
+    hd = synth.head(synth.rng_for(81), dm)
+    ctx = api.Context(dm, max_tokens=2)
+    x = rng.normal(size=(2, dm["d"])).astype(np.float16)
+    cur = np.stack([rng.permutation(8) for _ in range(2)]).astype(np.int32)
+    prev = np.stack([rng.permutation(8) for _ in range(2)]).astype(np.int32)
+    lg = torch.empty((2, dm["E"]), dtype=torch.float32, device="cuda")
+    oi, ow = api.prerouter_forward(ctx, dev_tree(hd), dev(x), dev(cur), dev(prev), logits=lg)
+    y = api.moe_int4_decode(ctx, dev_tree(pool), dev(x), oi, ow, shared=dev_tree(sh))
+    assert api.device_status(ctx) == 0
+    oi, ow, lg, yg = host(oi), host(ow), host(lg), f16_to_f64(y)
+    for b in range(2):
+        ref = orc.head_logits(hd["fc1"], hd["fc2"], hd["lin"], dm["d"], dm["E"], dm["P"], dm["K"],
+                              x[b], cur[b], prev[b], 1)
+        np.testing.assert_allclose(lg[b], ref, rtol=0, atol=2e-4)
+        assert sorted(oi[b].tolist()) == list(range(8))
+        assert np.all(np.diff(ref[oi[b]]) <= 2e-4), "selection not in descending score"
+        p = np.exp(ref - ref.max())
+        np.testing.assert_allclose(ow[b], p[oi[b]] / p.sum(), rtol=0, atol=W_TOL)
+        assert_out_close(yg[b], orc.moe_decode(dm, pool, sh, x[b], oi[b], ow[b].astype(np.float64)),
+                         f"K = E token {b}")
     ctx.close()
