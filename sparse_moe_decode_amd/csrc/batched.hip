@@ -812,12 +812,11 @@ constexpr int kPfSG = 4;          // 64-input groups per LDS stage (gate/up)
 // kernels are faster up to about 900 tokens.
 constexpr int kPrefillPerExpert = 16;
 
-// LDS slot of token t's 16-byte chunk c. Rows of one chunk are padded by
-// one slot, so one token's chunks (written by a wave) spread over the banks
-// as one chunk of 32 tokens (an MFMA operand read) does, and a lane's read
+// LDS layout of the staged activations: token t's 16-byte chunk c sits in
+// slot c * ROW + t, ROW = tokens + 1. Rows of one chunk are padded by one
+// slot, so one token's chunks (written by a wave) spread over the banks as
+// one chunk of 32 tokens (an MFMA operand read) does, and a lane's read
 // address is its own base plus a constant offset per (group, step).
-constexpr int kPfRow = kPfTok + 1;
-__device__ __forceinline__ int pf_slot(int c, int t) { return c * kPfRow + t; }
 
 // Gate/up of one tile: eight waves, each the same 32 rows of I of both the
 // gate and the up matrix (256 rows per workgroup) over all d inputs, for the
@@ -838,12 +837,16 @@ __device__ __forceinline__ float silu_fast(float z) {
 
 // AFF (affine codec): the epilogue adds b * (the token's sum of x over the
 // group) for every group, from sums staged in LDS.
-template <bool AFF>
-__global__ __launch_bounds__(512) void k_pf_gate_up(MbArgs a) {
-  __shared__ __align__(16) uint4 xs[2][kPfSG * 8 * kPfRow];
-  __shared__ float axs[kPfTok][2][kMaxR];
-  __shared__ __align__(16) float xss[AFF ? 32 : 1][kPfTok];  // [input group][tile token]
-  __shared__ int tokb[kPfTok], tokk[kPfTok];
+// TB: 32-token blocks per workgroup (grid z: the tile's 64 / (32 TB) parts);
+// with TB = 1 two workgroups share a compute unit.
+template <bool AFF, int TB>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4 / TB)))
+void k_pf_gate_up(MbArgs a) {
+  constexpr int TOK = 32 * TB, ROW = TOK + 1;  // tokens per part; LDS row (one pad slot)
+  __shared__ __align__(16) uint4 xs[2][kPfSG * 8 * ROW];
+  __shared__ float axs[TOK][2][kMaxR];
+  __shared__ __align__(16) float xss[AFF ? 32 : 1][TOK];  // [input group][part token]
+  __shared__ int tokb[TOK], tokk[TOK];
   const Dims& dm = a.dm;
   const int K = dm.K, d = dm.d;
   const int imax = dm.I > dm.Is ? dm.I : dm.Is;
@@ -851,6 +854,12 @@ __global__ __launch_bounds__(512) void k_pf_gate_up(MbArgs a) {
   int u, start, count;
   int bx;
   if (!tile_block(a, bx, shared, u, start, count)) return;
+  // this part's tokens: t0 .. t0 + count - 1 of the tile
+  const int t0 = TOK * (int)blockIdx.z;
+  count -= t0;
+  if (count <= 0) return;
+  if (count > TOK) count = TOK;
+  start += t0;  // tiles run over consecutive tokens (shared) or sorted entries
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, n = l & 31, kh = l >> 5;
   const int row = bx * kPfGuRows + wave * 32 + n;  // I % 256 == 0
   const bool lora = shared && a.sh.ag;
@@ -878,7 +887,7 @@ __global__ __launch_bounds__(512) void k_pf_gate_up(MbArgs a) {
       ub = (const uint16_t*)entry_ptr(a.pool.up.b, ent, a.pool.stride_s);
     }
   }
-  if (threadIdx.x < kPfTok) {
+  if (threadIdx.x < TOK) {
     // rows past count repeat the last token (their outputs are never stored)
     int b, k;
     entry_of(a, shared, start, threadIdx.x < count ? threadIdx.x : count - 1, b, k);
@@ -900,7 +909,7 @@ __global__ __launch_bounds__(512) void k_pf_gate_up(MbArgs a) {
   const uint32_t* uro = uq + (int64_t)row * wpr + 4 * kh;
   const uint16_t* gsr = gs + (int64_t)row * ngs;
   const uint16_t* usr = us + (int64_t)row * ngs;
-  constexpr int kXr = kPfSG * 8 * kPfTok / 512;  // 16-byte chunks per thread per stage
+  constexpr int kXr = kPfSG * 8 * TOK / 512;  // 16-byte chunks per thread per stage
   uint4 xr[kXr];
   auto load_x = [&](int st) {
 #pragma unroll
@@ -914,7 +923,7 @@ __global__ __launch_bounds__(512) void k_pf_gate_up(MbArgs a) {
 #pragma unroll
     for (int it = 0; it < kXr; ++it) {
       const int flat = it * 512 + threadIdx.x, tt = flat / (kPfSG * 8), c = flat % (kPfSG * 8);
-      xs[buf][pf_slot(c, tt)] = xr[it];
+      xs[buf][c * ROW + tt] = xr[it];
     }
   };
   uint4 wg[kPfSG], wu[kPfSG];
@@ -928,13 +937,15 @@ __global__ __launch_bounds__(512) void k_pf_gate_up(MbArgs a) {
   }
   load_x(0);
   if (AFF)
-    for (int i = threadIdx.x; i < ngs * kPfTok; i += blockDim.x) {
-      const int gg = i / kPfTok, tt = i % kPfTok;
+    for (int i = threadIdx.x; i < ngs * TOK; i += blockDim.x) {
+      const int gg = i / TOK, tt = i % TOK;
       xss[gg][tt] = a.xsum[(int64_t)tokb[tt] * ngs + gg];
     }
   store_x(0);
   __syncthreads();
-  f32x16 ag0 = {}, ag1 = {}, au0 = {}, au1 = {};
+  f32x16 ag[TB], au[TB];
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb) ag[tb] = au[tb] = f32x16{};
   for (int st = 0; st < ns; ++st) {
     const bool more = st + 1 < ns;
     if (more) load_x(st + 1);
@@ -951,25 +962,27 @@ __global__ __launch_bounds__(512) void k_pf_gate_up(MbArgs a) {
         sg[g] = sb2f<AFF>(ldg(gsr + gn));
         su[g] = sb2f<AFF>(ldg(usr + gn));
       }
-      f32x16 cg0 = {}, cg1 = {}, cu0 = {}, cu1 = {};
+      f32x16 cg[TB], cu[TB];
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) cg[tb] = cu[tb] = f32x16{};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int c = 8 * g + 4 * kh + j;
-        const h8 x0 = as_h8(xb[pf_slot(c, n)]), x1 = as_h8(xb[pf_slot(c, 32 + n)]);
         const h8 w_g = q4_to_h8<AFF>(word(cwg, j)), w_u = q4_to_h8<AFF>(word(cwu, j));
-        cg0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(x0, w_g, cg0, 0, 0, 0);
-        cg1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(x1, w_g, cg1, 0, 0, 0);
-        cu0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(x0, w_u, cu0, 0, 0, 0);
-        cu1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(x1, w_u, cu1, 0, 0, 0);
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+          const h8 xv = as_h8(xb[c * ROW + 32 * tb + n]);
+          cg[tb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xv, w_g, cg[tb], 0, 0, 0);
+          cu[tb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xv, w_u, cu[tb], 0, 0, 0);
+        }
       }
-      scale_add<16>(ag0, cg0, csg);
-      scale_add<16>(ag1, cg1, csg);
-      scale_add<16>(au0, cu0, csu);
-      scale_add<16>(au1, cu1, csu);
-      keep(ag0);
-      keep(ag1);
-      keep(au0);
-      keep(au1);
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        scale_add<16>(ag[tb], cg[tb], csg);
+        scale_add<16>(au[tb], cu[tb], csu);
+        keep(ag[tb]);
+        keep(au[tb]);
+      }
     }
     if (more) store_x((st + 1) & 1);
     __syncthreads();
@@ -983,30 +996,29 @@ __global__ __launch_bounds__(512) void k_pf_gate_up(MbArgs a) {
     for (int g = 0; g < ngs; ++g) {
       const float bg = bf2f(ldg(gbr + g)), bu = bf2f(ldg(ubr + g));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 x0 = *reinterpret_cast<const float4*>(&xss[g][8 * j + 4 * kh]);
-        const float4 x1 = *reinterpret_cast<const float4*>(&xss[g][32 + 8 * j + 4 * kh]);
-        const float xa[4] = {x0.x, x0.y, x0.z, x0.w}, xb4[4] = {x1.x, x1.y, x1.z, x1.w};
+      for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          ag0[4 * j + q] = fmaf(bg, xa[q], ag0[4 * j + q]);
-          au0[4 * j + q] = fmaf(bu, xa[q], au0[4 * j + q]);
-          ag1[4 * j + q] = fmaf(bg, xb4[q], ag1[4 * j + q]);
-          au1[4 * j + q] = fmaf(bu, xb4[q], au1[4 * j + q]);
+        for (int j = 0; j < 4; ++j) {
+          const float4 x4 = *reinterpret_cast<const float4*>(&xss[g][32 * tb + 8 * j + 4 * kh]);
+          const float xa[4] = {x4.x, x4.y, x4.z, x4.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            ag[tb][4 * j + q] = fmaf(bg, xa[q], ag[tb][4 * j + q]);
+            au[tb][4 * j + q] = fmaf(bu, xa[q], au[tb][4 * j + q]);
+          }
         }
-      }
     }
   }
   // epilogue: shared-expert LoRA B terms, SwiGLU, fp32 store
   const float cl = dm.lora_scale;
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb) {
+  for (int tb = 0; tb < TB; ++tb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int t = 32 * tb + tok_row(r, kh);
       if (t >= count) continue;
-      float gg = tb ? ag1[r] : ag0[r];
-      float uu = tb ? au1[r] : au0[r];
+      float gg = ag[tb][r];
+      float uu = au[tb][r];
       if (lora) {
         float lg = 0.0f, lu = 0.0f;
         for (int q = 0; q < dm.r; q += 8) {
@@ -1029,20 +1041,25 @@ __global__ __launch_bounds__(512) void k_pf_gate_up(MbArgs a) {
   }
 }
 
-// Down projection of one tile: eight waves, 32 output rows each (256 per
-// workgroup) over all NG input groups. The tile's fp32 SwiGLU outputs
-// (64 tokens x NG*64) are staged once in LDS as fp16 hi + lo under a
-// power-of-two scale per token; each dequantised weight word feeds four
-// MFMAs (hi and lo of both 32-token blocks). Workgroups of the shared
+// Down projection of TB 32-token blocks of a tile (grid z: the tile's
+// 64 / (32 TB) parts): eight waves, 32 output rows each (256 per workgroup)
+// over all NG input groups. The part's fp32 SwiGLU outputs (32 TB tokens x
+// NG*64) are staged once in LDS as fp16 hi + lo under a power-of-two scale
+// per token; each dequantised weight word feeds 2 TB MFMAs (hi and lo of each
+// 32-token block). With TB = 1 the staged part takes half the LDS, so two
+// workgroups share a compute unit and one's loads overlap the other's
+// MFMAs. Workgroups of the shared
 // expert's tiles also form A_down . h for the down LoRA. AFF (affine
 // codec): the staging also forms each token's sum of hi + lo over every input
 // group, and the epilogue adds b * that sum per group.
-template <int NG, bool AFF>
-__global__ __launch_bounds__(512) void k_pf_down(MbArgs a) {
-  extern __shared__ __align__(16) uint4 hsp[];  // [NG*8 chunks][hi, lo] x kPfTok slots
-  __shared__ float hx[kPfTok];
-  __shared__ __align__(16) float hss[AFF ? NG : 1][kPfTok];  // [input group][tile token]
-  __shared__ int tokb[kPfTok], tokk[kPfTok];
+template <int NG, bool AFF, int TB>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4 / TB)))
+void k_pf_down(MbArgs a) {
+  constexpr int TOK = 32 * TB, ROW = TOK + 1;  // tokens per part; LDS row (one pad slot)
+  extern __shared__ __align__(16) uint4 hsp[];  // [NG*8 chunks][hi, lo] x ROW slots
+  __shared__ float hx[TOK];
+  __shared__ __align__(16) float hss[AFF ? NG : 1][TOK];  // [input group][part token]
+  __shared__ int tokb[TOK], tokk[TOK];
   constexpr int nin = NG * 64, nch = NG * 8;
   const Dims& dm = a.dm;
   const int K = dm.K, d = dm.d;
@@ -1051,6 +1068,11 @@ __global__ __launch_bounds__(512) void k_pf_down(MbArgs a) {
   int u, start, count;
   int bx;
   if (!tile_block(a, bx, shared, u, start, count)) return;
+  // this part's tokens: t0 .. t0 + count - 1 of the tile
+  const int t0 = TOK * (int)blockIdx.z;
+  count -= t0;
+  if (count <= 0) return;
+  if (count > TOK) count = TOK;
   const uint32_t* dq;
   const uint16_t* ds;
   const uint16_t* db = nullptr;
@@ -1083,16 +1105,16 @@ __global__ __launch_bounds__(512) void k_pf_down(MbArgs a) {
       for (int i = 0; i < NG; ++i) bd[i] = bf2f(ldg(brow + i));
     }
   }
-  if (threadIdx.x < kPfTok) {
+  if (threadIdx.x < TOK) {
     int b = 0, k = 0;
-    if ((int)threadIdx.x < count) entry_of(a, shared, start, threadIdx.x, b, k);
+    if ((int)threadIdx.x < count) entry_of(a, shared, start, t0 + threadIdx.x, b, k);
     tokb[threadIdx.x] = b;
     tokk[threadIdx.x] = k;
   }
   __syncthreads();
   // stage: wave w takes tokens w, w+8, ...; lane c the 8 values of chunk c.
   // All of the wave's loads are issued before the first token is split.
-  constexpr int kTpw = kPfTok / 8, kCpl = (nch + 63) / 64;
+  constexpr int kTpw = TOK / 8, kCpl = (nch + 63) / 64;
   float4 hv[kTpw][kCpl][2];
 #pragma unroll
   for (int i = 0; i < kTpw; ++i) {
@@ -1144,20 +1166,20 @@ __global__ __launch_bounds__(512) void k_pf_down(MbArgs a) {
       }
       if (c >= nch) continue;
       // pair-permuted order [0 4 1 5 2 6 3 7]
-      hsp[pf_slot(2 * c, t)] =
+      hsp[(2 * c) * ROW + t] =
           make_uint4(hi[0] | ((uint32_t)hi[4] << 16), hi[1] | ((uint32_t)hi[5] << 16),
                      hi[2] | ((uint32_t)hi[6] << 16), hi[3] | ((uint32_t)hi[7] << 16));
-      hsp[pf_slot(2 * c + 1, t)] =
+      hsp[(2 * c + 1) * ROW + t] =
           make_uint4(lo[0] | ((uint32_t)lo[4] << 16), lo[1] | ((uint32_t)lo[5] << 16),
                      lo[2] | ((uint32_t)lo[6] << 16), lo[3] | ((uint32_t)lo[7] << 16));
     }
     if (l == 0) hx[t] = t < count ? ldexpf(1.0f, e) : 0.0f;
   }
   if (shared && a.sh.ad) {
-    // A_down . h_shared[t] for tokens t = bx, bx + gridDim.x, ...;
+    // A_down . h_shared[t] for the part's tokens t = bx, bx + gridDim.x, ...;
     // wave w takes ranks q = w, w+8, ...
     for (int t = bx; t < count; t += gridDim.x) {
-      const int b = start + t;
+      const int b = start + t0 + t;
       const float* h = a.H + ((int64_t)b * (K + 1) + K) * imax;
       for (int q = wave; q < dm.r; q += 8) {
         float sacc = 0.0f;
@@ -1179,32 +1201,40 @@ __global__ __launch_bounds__(512) void k_pf_down(MbArgs a) {
     }
   }
   __syncthreads();
-  f32x16 acc0 = {}, acc1 = {};
+  f32x16 acc[TB];
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb) acc[tb] = f32x16{};
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     __builtin_amdgcn_sched_barrier(0);  // one group's operands live at a time
-    f32x16 c0 = {}, c1 = {};
+    f32x16 cc[TB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) cc[tb] = f32x16{};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c = 8 * g + 4 * kh + j;
       const h8 w8 = q4_to_h8<AFF>(word(wq[g], j));
-      c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(hsp[pf_slot(2 * c, n)]), w8, c0, 0, 0, 0);
-      c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(hsp[pf_slot(2 * c + 1, n)]), w8, c0, 0, 0, 0);
-      c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(hsp[pf_slot(2 * c, 32 + n)]), w8, c1, 0, 0, 0);
-      c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(hsp[pf_slot(2 * c + 1, 32 + n)]), w8, c1, 0, 0, 0);
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        cc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(hsp[(2 * c) * ROW + 32 * tb + n]), w8,
+                                                        cc[tb], 0, 0, 0);
+        cc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(hsp[(2 * c + 1) * ROW + 32 * tb + n]),
+                                                        w8, cc[tb], 0, 0, 0);
+      }
     }
-    scale_add<16>(acc0, c0, sc[g]);
-    scale_add<16>(acc1, c1, sc[g]);
-    keep(acc0);
-    keep(acc1);
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      scale_add<16>(acc[tb], cc[tb], sc[g]);
+      keep(acc[tb]);
+    }
   }
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb) {
+  for (int tb = 0; tb < TB; ++tb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int t = 32 * tb + tok_row(r, kh);
       if (t < count) {
-        float v = tb ? acc1[r] : acc0[r];
+        float v = acc[tb][r];
         if (AFF) {
 #pragma unroll
           for (int i = 0; i < NG; ++i) v = fmaf(bd[i], hss[i][t], v);
@@ -1241,13 +1271,19 @@ void launch_gate_up_ng(const MbArgs& a, dim3 grid, hipStream_t st) {
     hipLaunchKernelGGL((k_mb_gate_up<NG, false>), grid, dim3(512), 0, st, a);
 }
 
+// 32-token blocks per prefill workgroup (1: two workgroups per compute unit).
+constexpr int kPfDownTB = 1;
+constexpr int kPfGuTB = 2;  // one part of 32 tokens needs over 128 registers (scratch spills)
+
 template <int NG, bool AFF>
 hipError_t launch_pf_down_t(const MbArgs& a, dim3 grid, hipStream_t st) {
-  const size_t lds = (size_t)NG * 8 * 2 * kPfRow * sizeof(uint4);
+  constexpr int TB = kPfDownTB;
+  const size_t lds = (size_t)NG * 8 * 2 * (32 * TB + 1) * sizeof(uint4);
   static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)k_pf_down<NG, AFF>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      (const void*)k_pf_down<NG, AFF, TB>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((k_pf_down<NG, AFF>), grid, dim3(512), lds, st, a);
+  grid.z = kPfTok / (32 * TB);
+  hipLaunchKernelGGL((k_pf_down<NG, AFF, TB>), grid, dim3(512), lds, st, a);
   return hipSuccess;
 }
 
@@ -1300,10 +1336,11 @@ hipError_t launch_batched(const Dims& dm, const Pool& pool, const SharedW& sh, c
   const int lora_blocks = sh.present && sh.ag ? (B + kCols - 1) / kCols * a.n_sl : 0;
   hipLaunchKernelGGL(k_mb_prep, dim3(B + 1 + lora_blocks), dim3(256), 0, st, a);
   if (pf) {
+    const dim3 gu_grid(imax / kPfGuRows, ny, kPfTok / (32 * kPfGuTB));
     if (dm.affine)
-      hipLaunchKernelGGL(k_pf_gate_up<true>, dim3(imax / kPfGuRows, ny), dim3(512), 0, st, a);
+      hipLaunchKernelGGL((k_pf_gate_up<true, kPfGuTB>), gu_grid, dim3(512), 0, st, a);
     else
-      hipLaunchKernelGGL(k_pf_gate_up<false>, dim3(imax / kPfGuRows, ny), dim3(512), 0, st, a);
+      hipLaunchKernelGGL((k_pf_gate_up<false, kPfGuTB>), gu_grid, dim3(512), 0, st, a);
     const dim3 grid(dm.d / 256, ny);
     hipError_t e;
     switch (dm.I / dm.G) {
