@@ -84,6 +84,7 @@ struct MbArgs {
   float* H;              // [B][K+1][imax] SwiGLU outputs
   float* Y;              // [B][K+1][d] per-slot down outputs
   float* xsum;           // affine codec: [B][d/64] sums of each token's x per input group
+  int ctok;              // tokens per combine workgroup
   uint16_t* y;           // [B][d]
   int32_t* flags;
 };
@@ -745,58 +746,82 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 }
 
 // y[b] = sum_k w_k y_k + y_shared + down LoRA, in a fixed order (no atomics),
-// rounded to fp16. Grid (B, ceil(d/1024)); thread j takes columns 4j..4j+3
-// (16-byte loads) and reads their down-LoRA rows as 16-byte words.
+// rounded to fp16. Grid (ceil(B / ctok), ceil(d / 1024)); thread j takes
+// columns 4j..4j+3 of ctok consecutive tokens (16-byte loads): it reads the
+// four columns' down-LoRA rows once (16-byte words) and then each token's
+// slot outputs. ctok = 1 for small batches (more workgroups), more for large
+// ones (fewer reads of the LoRA rows).
+constexpr int kCombTokMax = 4;
+
 __global__ __launch_bounds__(256) void k_mb_combine(MbArgs a) {
-  __shared__ int ok[8];
-  __shared__ float axd[kMaxR];
+  __shared__ int ok[kCombTokMax][8];
+  __shared__ float axd[kCombTokMax][kMaxR];
   const Dims& dm = a.dm;
-  const int K = dm.K, d = dm.d, b = blockIdx.x;
-  if (threadIdx.x < K) ok[threadIdx.x] = resolve_entry(a.pool, dm.E, a.idx[b * K + threadIdx.x]) >= 0;
+  const int K = dm.K, d = dm.d, b0 = blockIdx.x * a.ctok;
+  const int nb = min(a.ctok, a.B - b0);
   const bool lora = a.sh.present && a.sh.bd;
-  if (lora && threadIdx.x < dm.r)
-    axd[threadIdx.x] = a.ax[(int64_t)b * 3 * a.rmax + 2 * a.rmax + threadIdx.x];
+  for (int i = threadIdx.x; i < nb * K; i += blockDim.x) {
+    const int tb = i / K, k = i % K;
+    ok[tb][k] = resolve_entry(a.pool, dm.E, a.idx[(b0 + tb) * K + k]) >= 0;
+  }
+  if (lora)
+    for (int i = threadIdx.x; i < nb * dm.r; i += blockDim.x) {
+      const int tb = i / dm.r, q = i % dm.r;
+      axd[tb][q] = a.ax[(int64_t)(b0 + tb) * 3 * a.rmax + 2 * a.rmax + q];
+    }
   __syncthreads();
   const int j0 = 4 * (blockIdx.y * blockDim.x + threadIdx.x);
   if (j0 >= d) return;  // d % 128 == 0: a thread's four columns are all in range
   const float c = dm.lora_scale;
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int k = 0; k < K; ++k) {
-    if (!ok[k]) continue;
-    const float wk = a.w[b * K + k];
-    const float4 v = *reinterpret_cast<const float4*>(a.Y + ((int64_t)b * (K + 1) + k) * d + j0);
-    acc[0] += wk * v.x;
-    acc[1] += wk * v.y;
-    acc[2] += wk * v.z;
-    acc[3] += wk * v.w;
+  uint4 bv[4][kMaxR / 8];  // the four columns' down-LoRA rows (fp16, r <= kMaxR)
+  if (lora) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int q = 0; q < kMaxR / 8; ++q)
+        if (8 * q < dm.r)
+          bv[jj][q] = ldg(reinterpret_cast<const uint4*>(a.sh.bd + (int64_t)(j0 + jj) * dm.r + 8 * q));
   }
-  if (a.sh.present) {
-    const float4 v = *reinterpret_cast<const float4*>(a.Y + ((int64_t)b * (K + 1) + K) * d + j0);
-    acc[0] += v.x;
-    acc[1] += v.y;
-    acc[2] += v.z;
-    acc[3] += v.w;
-    if (lora) {
+  for (int tb = 0; tb < nb; ++tb) {
+    const int b = b0 + tb;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k = 0; k < K; ++k) {
+      if (!ok[tb][k]) continue;
+      const float wk = a.w[b * K + k];
+      const float4 v = *reinterpret_cast<const float4*>(a.Y + ((int64_t)b * (K + 1) + k) * d + j0);
+      acc[0] += wk * v.x;
+      acc[1] += wk * v.y;
+      acc[2] += wk * v.z;
+      acc[3] += wk * v.w;
+    }
+    if (a.sh.present) {
+      const float4 v = *reinterpret_cast<const float4*>(a.Y + ((int64_t)b * (K + 1) + K) * d + j0);
+      acc[0] += v.x;
+      acc[1] += v.y;
+      acc[2] += v.z;
+      acc[3] += v.w;
+      if (lora) {
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const uint16_t* brow = a.sh.bd + (int64_t)(j0 + jj) * dm.r;
-        float ls = 0.0f;
-        for (int q = 0; q < dm.r; q += 8) {
-          const uint4 bv = ldg(reinterpret_cast<const uint4*>(brow + q));
+        for (int jj = 0; jj < 4; ++jj) {
+          float ls = 0.0f;
 #pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const f16x2 h = as_h2(word(bv, p));
-            ls = fmaf((float)h.x, axd[q + 2 * p], ls);
-            ls = fmaf((float)h.y, axd[q + 2 * p + 1], ls);
+          for (int q = 0; q < kMaxR / 8; ++q) {
+            if (8 * q >= dm.r) break;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              const f16x2 h = as_h2(word(bv[jj][q], p));
+              ls = fmaf((float)h.x, axd[tb][8 * q + 2 * p], ls);
+              ls = fmaf((float)h.y, axd[tb][8 * q + 2 * p + 1], ls);
+            }
           }
+          acc[jj] += c * ls;
         }
-        acc[jj] += c * ls;
       }
     }
+    const uint32_t lo = (uint32_t)f2h(acc[0]) | ((uint32_t)f2h(acc[1]) << 16);
+    const uint32_t hi = (uint32_t)f2h(acc[2]) | ((uint32_t)f2h(acc[3]) << 16);
+    *reinterpret_cast<uint2*>(a.y + (int64_t)b * d + j0) = make_uint2(lo, hi);
   }
-  const uint32_t lo = (uint32_t)f2h(acc[0]) | ((uint32_t)f2h(acc[1]) << 16);
-  const uint32_t hi = (uint32_t)f2h(acc[2]) | ((uint32_t)f2h(acc[3]) << 16);
-  *reinterpret_cast<uint2*>(a.y + (int64_t)b * d + j0) = make_uint2(lo, hi);
 }
 
 // ---------------------------------------------------------------------------
@@ -1326,6 +1351,7 @@ hipError_t launch_batched(const Dims& dm, const Pool& pool, const SharedW& sh, c
   a.H = s.gu;
   a.Y = s.yk;
   a.xsum = s.hattn;  // unused by this path otherwise; [B][d] floats >= [B][d/64]
+  a.ctok = B >= 512 ? kCombTokMax : 1;
   a.y = y;
   a.flags = s.flags;
   const bool pf = (int64_t)B * dm.K >= (int64_t)kPrefillPerExpert * dm.E && prefill_supported(dm);
@@ -1350,7 +1376,8 @@ hipError_t launch_batched(const Dims& dm, const Pool& pool, const SharedW& sh, c
       default: e = launch_pf_down_ng<8>(a, grid, st); break;
     }
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_mb_combine, dim3(B, (dm.d + 1023) / 1024), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_mb_combine, dim3((B + a.ctok - 1) / a.ctok, (dm.d + 1023) / 1024),
+                       dim3(256), 0, st, a);
     return hipGetLastError();
   }
   const dim3 gu_grid(imax / 32, ny);
@@ -1367,7 +1394,8 @@ hipError_t launch_batched(const Dims& dm, const Pool& pool, const SharedW& sh, c
     case 6: launch_down_ng<6>(a, dn_grid, st); break;
     default: launch_down_ng<8>(a, dn_grid, st); break;
   }
-  hipLaunchKernelGGL(k_mb_combine, dim3(B, (dm.d + 1023) / 1024), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_mb_combine, dim3((B + a.ctok - 1) / a.ctok, (dm.d + 1023) / 1024),
+                       dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
