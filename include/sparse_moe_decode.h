@@ -164,10 +164,12 @@ int e0_device_status(e0_ctx* ctx, void* stream);
  * B <= max_tokens. Internal sums are fp32; q*s is never rounded to fp16 and
  * the SwiGLU intermediate keeps fp32 precision. B < 16 runs one GEMV per
  * (token, expert); B >= 16 groups the B*K entries by expert in one launch
- * and runs int4 x fp16 MFMA tiles of up to 32 of an expert's tokens (fp32
- * group scales applied to fp32 partials), each expert's weights read once per
- * tile [MW §3.1 Executor paths: batched chunks and prefill take the
- * whole-layer path]. Both are deterministic. */
+ * and runs int4 x fp16 MFMA tiles of up to 32 of an expert's tokens (64 from
+ * 16 entries per expert on average, B*K >= 16 E), fp32 group scales applied
+ * to fp32 partials, each expert's weights read once per tile [MW §3.1
+ * Executor paths: batched chunks and prefill take the whole-layer path].
+ * Either codec runs on both paths; the affine biases enter as b times the
+ * fp32 sum of the group's inputs. Both paths are deterministic. */
 int moe_int4_decode(e0_ctx* ctx, const e0_experts* routed, const int32_t* slot_of,
                     const e0_shared* shared, const uint16_t* x, const int32_t* idx,
                     const float* w, int32_t n_tokens, uint16_t* y, void* stream);

@@ -31,6 +31,10 @@
 // (dispatched first, they have the most tokens). A batch of any size B is
 // one launch of each step; each expert's weights are read once per 32 of its
 // tokens, so B = 32 reads every expert with routed tokens at most once.
+// From 16 entries per expert on average the prefill kernels take over
+// (k_pf_gate_up, k_pf_down: 64-token tiles, below). Every kernel has an
+// affine-codec variant (AFF): unsigned nibbles, bf16 scales, and the bias
+// added in fp32 as b times the token's sum over the group.
 
 #include "gemv.h"
 #include "internal.h"
