@@ -49,6 +49,7 @@ constexpr int kNR = 4;         // fp16 rows per workgroup per block job (router,
 constexpr int kMaxExp = 9;     // experts per down row: K <= 8 routed + the shared expert
 constexpr int kEp = 9;         // base addresses per expert slot (q, s, b of gate, up, down)
 constexpr int kRank = 16;      // LoRA rank of this kernel (or no LoRA at all)
+static_assert(kRank == 16, "one lane group per rank of the down LoRA A product");
 constexpr int kStackI = 512;   // expert intermediate width of this kernel
 constexpr int kHX = 4;         // head layers one workgroup keeps x / fc2 activations of
 constexpr int kF2R = 4;        // fc2 rounds (kGroups rows each) per workgroup
@@ -183,7 +184,6 @@ struct Misc {
   // each expert's hi + lo SwiGLU chunk (the bias terms b * sum)
   float xsum[64];
   float hsum[kMaxExp][16];
-  float red16[kRank][kGroups];
   float hsc[kHX][16];          // scales of the fc2 activation chunks (per lane)
   float red[4 * kNR];
   float rows[kNR];             // results of the block fp16 row jobs
@@ -470,9 +470,10 @@ struct DownRegs {
   uint4 bd[kRank / 8];  // LoRA B of the down projection, row drow (lane 0 of the group)
 };
 
-// Shared-expert LoRA A_down ([r, Is]), thread t's part: columns 2t, 2t+1.
+// Shared-expert LoRA A_down ([r, Is]): lane group g takes rank g (kRank ==
+// kGroups), lane li its columns 32 li .. 32 li + 31 (Is == 16 * 32).
 struct LoraRegs {
-  uint32_t ad[kRank];
+  uint4 ad[4];
 };
 
 // Lane li of a 16-lane group holds elements 32c + 2li and 32c + 2li + 1 of an
@@ -636,8 +637,10 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
       }
     }
 #pragma unroll
-    for (int q = 0; q < kRank; ++q)
-      A.LR.ad[q] = lora_d ? ldg(reinterpret_cast<const uint32_t*>(Ly.sh.ad + q * Is + 2 * t)) : 0u;
+    for (int c = 0; c < 4; ++c)
+      A.LR.ad[c] = lora_d ? ldg(reinterpret_cast<const uint4*>(Ly.sh.ad + (int64_t)grp * Is +
+                                                              32 * li + 8 * c))
+                          : make_uint4(0, 0, 0, 0);
   };
 
   // Issue the loads of layer l that its gate/up step needs and that do not
@@ -856,12 +859,22 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
                                    AFF ? &ms.hsum[K][grp] : nullptr);
         if (li == 0) ms.csc[K][grp] = sc;
         if (lora_d) {
+          // rank grp of A_down h: the lane's 32 columns, then the group's sum
+          const float4* hp = reinterpret_cast<const float4*>(lf + n_rt + 32 * li);
+          float p = 0.0f;
 #pragma unroll
-          for (int q = 0; q < kRank; ++q) {
-            float p = h2f((uint16_t)(LR.ad[q] & 0xFFFF)) * h0 + h2f((uint16_t)(LR.ad[q] >> 16)) * h1;
-            p = group_sum<kLG>(p);
-            if (li == 0) ms.red16[q][grp] = p;
+          for (int c = 0; c < 4; ++c) {
+            const float4 v0 = hp[2 * c], v1 = hp[2 * c + 1];
+            const float hv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            const uint32_t aw[4] = {LR.ad[c].x, LR.ad[c].y, LR.ad[c].z, LR.ad[c].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              p = fmaf(h2f((uint16_t)(aw[e] & 0xFFFF)), hv[2 * e], p);
+              p = fmaf(h2f((uint16_t)(aw[e] >> 16)), hv[2 * e + 1], p);
+            }
           }
+          p = group_sum<kLG>(p);
+          if (li == 0) ms.ad[grp] = p;
         }
       }
       // An unresolved expert's outputs are zeros (never used: its down rows
@@ -882,12 +895,6 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
                                      AFF ? &ms.hsum[k][grp] : nullptr);
           if (li == 0) ms.csc[k][grp] = sc;
         }
-      }
-      __syncthreads();
-      if (lora_d && t < kRank) {
-        float s = 0.0f;
-        for (int g = 0; g < kGroups; ++g) s += ms.red16[t][g];
-        ms.ad[t] = s;
       }
       __syncthreads();
     }
