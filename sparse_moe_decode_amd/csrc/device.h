@@ -142,29 +142,35 @@ __device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
 
-template <int CTRL>
-__device__ __forceinline__ void max_step_u64(uint32_t& hi, uint32_t& lo) {
-  const uint32_t oh = dpp_u<CTRL>(hi), ol = dpp_u<CTRL>(lo);
-  const bool gt = oh > hi || (oh == hi && ol > lo);
-  hi = gt ? oh : hi;
-  lo = gt ? ol : lo;
+__device__ __forceinline__ uint32_t umax32(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// Wave-wide maximum of a uint32 (DPP in each 16-lane row, then the four row
+// results); the whole wave must be active.
+__device__ __forceinline__ uint32_t wave_max_u32_rows(uint32_t v) {
+  v = umax32(v, dpp_u<0xB1>(v));
+  v = umax32(v, dpp_u<0x4E>(v));
+  v = umax32(v, dpp_u<0x141>(v));
+  v = umax32(v, dpp_u<0x140>(v));
+  return umax32(umax32((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
+                       (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+                umax32((uint32_t)__builtin_amdgcn_readlane((int)v, 32),
+                       (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
 }
 
-// Wave-wide maximum of a 64-bit key; the whole wave must be active.
-__device__ __forceinline__ uint64_t wave_max_u64_rows(uint64_t k) {
-  uint32_t hi = (uint32_t)(k >> 32), lo = (uint32_t)k;
-  max_step_u64<0xB1>(hi, lo);
-  max_step_u64<0x4E>(hi, lo);
-  max_step_u64<0x141>(hi, lo);
-  max_step_u64<0x140>(hi, lo);
-  uint64_t best = 0;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const uint64_t v = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, 16 * r) << 32) |
-                       (uint32_t)__builtin_amdgcn_readlane((int)lo, 16 * r);
-    best = v > best ? v : best;
-  }
-  return best;
+// Wave-wide maximum of 64-bit keys (score bits high, a distinct tag low):
+// the maximal high word, then, only when several lanes hold it, the largest
+// low word among them (the 64-bit maximum, found with 32-bit steps). The
+// whole wave must be active.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+  const uint32_t hi = (uint32_t)(k >> 32), lo = (uint32_t)k;
+  const uint32_t mh = wave_max_u32_rows(hi);
+  const uint64_t tied = __ballot(hi == mh);
+  uint32_t ml;
+  if (__popcll(tied) == 1)
+    ml = (uint32_t)__builtin_amdgcn_readlane((int)lo, __ffsll((unsigned long long)tied) - 1);
+  else
+    ml = wave_max_u32_rows(hi == mh ? lo : 0u);
+  return ((uint64_t)mh << 32) | ml;
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }

@@ -309,7 +309,7 @@ __device__ __forceinline__ void route_wave_t(const Dims& dm, const float* lg, co
     }
     bool kept = false;
     for (int r = 0; r < dm.topk_groups; ++r) {
-      const uint64_t g = wave_max_u64_rows(gkey);
+      const uint64_t g = wave_max_key(gkey);
       if (gkey == g && g != 0) {
         kept = true;
         gkey = 0;
@@ -350,7 +350,7 @@ __device__ __forceinline__ void route_wave_t(const Dims& dm, const float* lg, co
   int mine = -1;  // lane k < K: the k-th selection
   int first = 0;
   for (int k = 0; k < K; ++k) {
-    const uint64_t g = wave_max_u64_rows(key[0]);
+    const uint64_t g = wave_max_key(key[0]);
     int e = 0;
     if (g == 0) {  // no candidate left (rejected shapes make this unreachable)
       if (lane == 0) atomicOr(&flags[FLAG_RANGE], 4);
