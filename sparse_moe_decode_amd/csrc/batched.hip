@@ -371,21 +371,21 @@ __device__ __forceinline__ void scale_add(f32x16& acc, const f32x16& c, float s)
 // Multiply-accumulate of one wave: NG groups of 64 inputs, weights wv (one
 // word per lane per MFMA), activations xv of the lane's token row
 // (pair-permuted fp16), group scales sv.
-template <int NG, int NR, bool AFF>
-__device__ __forceinline__ f32x16 gu_mma(const uint4 (&wv)[NG], const float (&sv)[NG],
-                                         const uint4 (&xv)[NG][4]) {
-  f32x16 acc = {};
+// Groups i0 .. i0 + NH - 1 of the NG, accumulated into acc; the activations
+// xv of those NH groups only.
+template <int NG, int NH, int NR, bool AFF>
+__device__ __forceinline__ void gu_mma(f32x16& acc, const uint4 (&wv)[NG], const float (&sv)[NG],
+                                       const uint4 (&xv)[NH][4], int i0) {
 #pragma unroll
-  for (int i = 0; i < NG; ++i) {
+  for (int i = 0; i < NH; ++i) {
     f32x16 c = {};
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      c = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(xv[i][j]), q4_to_h8<AFF>(word(wv[i], j)),
-                                                c, 0, 0, 0);
-    scale_add<NR>(acc, c, sv[i]);
+      c = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(xv[i][j]),
+                                                q4_to_h8<AFF>(word(wv[i0 + i], j)), c, 0, 0, 0);
+    scale_add<NR>(acc, c, sv[i0 + i]);
     keep(acc);
   }
-  return acc;
 }
 
 // Down multiply-accumulate: hi and lo activation rows (in LDS) through the
@@ -464,8 +464,11 @@ __device__ __forceinline__ bool tile_block(const MbArgs& a, int& bx, bool& share
 // (weight words, scales, activations of its valid token rows) before the
 // first multiply. AFF (affine codec): each wave adds b * (the token's sum of
 // x over the group) for its groups, from sums staged in LDS.
+// (The affine variant's bias terms need more registers: it keeps one
+// workgroup per compute unit.)
 template <int NG, bool AFF>
-__global__ __launch_bounds__(512) void k_mb_gate_up(MbArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(AFF ? 2 : 4)))
+void k_mb_gate_up(MbArgs a) {
   __shared__ float red[2][4][16][64];
   __shared__ float axs[kCols][2][kMaxR];
   __shared__ float xss[AFF ? kCols : 1][32];  // [tile token][input group]
@@ -539,14 +542,23 @@ __global__ __launch_bounds__(512) void k_mb_gate_up(MbArgs a) {
 #pragma unroll
     for (int i = 0; i < NG; ++i) bv[i] = bf2f(ldg(brow + g0 + i));
   }
-  uint4 xv[NG][4];
+  // the activations in two halves of the quarter's groups (each half's loads
+  // together), which keeps a wave within 128 registers: two workgroups share
+  // a compute unit, so one's loads overlap the other's MFMAs and epilogue
+  constexpr int NH = NG / 2;
+  f32x16 acc = {};
 #pragma unroll
-  for (int i = 0; i < NG; ++i)
+  for (int h = 0; h < 2; ++h) {
+    uint4 xv[NH][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xv[i][j] = ldg(reinterpret_cast<const uint4*>(xrow + 64 * i + 8 * j));
-  // one variant for all counts: a second (fewer registers scaled) costs the
-  // register allocator more than it saves
-  f32x16 acc = gu_mma<NG, 16, AFF>(wv, sv, xv);
+    for (int i = 0; i < NH; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        xv[i][j] = ldg(reinterpret_cast<const uint4*>(xrow + 64 * (NH * h + i) + 8 * j));
+    // one variant for all counts: a second (fewer registers scaled) costs
+    // the register allocator more than it saves
+    gu_mma<NG, NH, 16, AFF>(acc, wv, sv, xv, NH * h);
+  }
   if (AFF) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
