@@ -604,19 +604,22 @@ void k_mb_gate_up(MbArgs a) {
   }
 }
 
-// Down projection. A workgroup takes 128 output rows of one union member (or
-// the shared expert); its four waves take 32 rows each over all NG input
-// groups. The member's fp32 SwiGLU outputs (count tokens x NG*64) are staged
+// Down projection. A workgroup takes kDnWaves * 32 output rows of one union
+// member (or the shared expert); its waves take 32 rows each over all NG
+// input groups (eight waves: the staging below is shared by twice the rows,
+// and at up to 128 registers two workgroups still share a compute unit). The member's fp32 SwiGLU outputs (count tokens x NG*64) are staged
 // once in LDS as fp16 hi + lo under a power-of-two scale per token (about 22
 // bits of each value kept); hi and lo then go through the same dequantised
 // weights. Workgroups of the shared expert also form A_down . h for the down
 // LoRA, two tokens each. AFF (affine codec): the staging also forms each
 // token's sum of hi + lo over every input group, and the epilogue adds
 // b * that sum per group.
-constexpr int kDnPad = 8;  // fp16 padding per staged row (spreads LDS banks)
+constexpr int kDnPad = 8;    // fp16 padding per staged row (spreads LDS banks)
+constexpr int kDnWaves = 8;  // waves (32 output rows each) per workgroup
 
 template <int NG, bool AFF>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_mb_down(MbArgs a) {
+__global__ __launch_bounds__(64 * kDnWaves) __attribute__((amdgpu_waves_per_eu(AFF ? 2 : 4)))
+void k_mb_down(MbArgs a) {
   extern __shared__ __align__(16) uint16_t hs[];  // [count][2][NG*64 + kDnPad]
   __shared__ float hx[kCols];                      // per-token power-of-two scale
   __shared__ float hss[AFF ? kCols : 1][8];        // [token][input group] sums of hi + lo
@@ -644,7 +647,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     if (AFF) db = (const uint16_t*)entry_ptr(a.pool.down.b, ent, a.pool.stride_s);
   }
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, n = l & 31, kh = l >> 5;
-  const int m0 = (bx * 4 + wave) * 32;
+  const int m0 = (bx * kDnWaves + wave) * 32;
   const bool rows_ok = m0 < d;
   uint4 wq[NG];
   float sc[NG], bd[NG];
@@ -662,7 +665,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
   }
   // stage: wave w takes tokens w, w+4, ...; lane l the 8 values of chunk l
-  for (int t = wave; t < count; t += 4) {
+  for (int t = wave; t < count; t += kDnWaves) {
     int b, k;
     entry_of(a, shared, start, t, b, k);
     const float* h = a.H + ((int64_t)b * (K + 1) + k) * imax + 8 * l;
@@ -716,7 +719,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
         v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
       }
-      for (int q = wave; q < dm.r; q += 4) {
+      for (int q = wave; q < dm.r; q += kDnWaves) {
         float sacc = 0.0f;
         if (l < NG * 8) {
           const uint4 av = ldg(reinterpret_cast<const uint4*>(a.sh.ad + (int64_t)q * nin + 8 * l));
@@ -1338,9 +1341,9 @@ template <int NG>
 void launch_down_ng(const MbArgs& a, dim3 grid, hipStream_t st) {
   const size_t lds = (size_t)(a.B < kCols ? a.B : kCols) * 2 * (NG * 64 + kDnPad) * sizeof(uint16_t);
   if (a.dm.affine)
-    hipLaunchKernelGGL((k_mb_down<NG, true>), grid, dim3(256), lds, st, a);
+    hipLaunchKernelGGL((k_mb_down<NG, true>), grid, dim3(64 * kDnWaves), lds, st, a);
   else
-    hipLaunchKernelGGL((k_mb_down<NG, false>), grid, dim3(256), lds, st, a);
+    hipLaunchKernelGGL((k_mb_down<NG, false>), grid, dim3(64 * kDnWaves), lds, st, a);
 }
 
 }  // namespace
@@ -1403,7 +1406,7 @@ hipError_t launch_batched(const Dims& dm, const Pool& pool, const SharedW& sh, c
     case 6: launch_gate_up_ng<6>(a, gu_grid, st); break;
     default: launch_gate_up_ng<8>(a, gu_grid, st); break;
   }
-  const dim3 dn_grid(dm.d / 128, ny);
+  const dim3 dn_grid((dm.d + 32 * kDnWaves - 1) / (32 * kDnWaves), ny);
   switch (dm.I / dm.G) {
     case 2: launch_down_ng<2>(a, dn_grid, st); break;
     case 4: launch_down_ng<4>(a, dn_grid, st); break;
