@@ -705,8 +705,10 @@ def main():
                     default="stack",
                     help="stack: the 40-layer resident decode (the bench line); chunk: the "
                          "batched path (B=32 chunk, or --chunk-b); prefill: a B-token batch through "
-                         "host-resident layers with layer-ahead staging; staged: the host-staged stack; layer: single "
-                         "layer-steps, warm and cold")
+                         "host-resident layers with layer-ahead staging; staged: the host-staged "
+                         "stack (--cache-entries: through the HBM hot cache); storage: the stack "
+                         "with experts read from per-layer files; layer: single layer-steps, warm "
+                         "and cold")
     ap.add_argument("--reserve-cus", type=int, default=16,
                     help="staged workload: compute units left to the staging copies")
     ap.add_argument("--group", type=int, default=8,
