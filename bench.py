@@ -709,9 +709,9 @@ def main():
                          "stack (--cache-entries: through the HBM hot cache); storage: the stack "
                          "with experts read from per-layer files; layer: single layer-steps, warm "
                          "and cold")
-    ap.add_argument("--reserve-cus", type=int, default=16,
+    ap.add_argument("--reserve-cus", type=int, default=32,
                     help="staged workload: compute units left to the staging copies")
-    ap.add_argument("--group", type=int, default=8,
+    ap.add_argument("--group", type=int, default=16,
                     help="staged workload: predicted layers per launch")
     ap.add_argument("--arm", choices=["prefetch", "ondemand"], default="prefetch",
                     help="storage workload: disk reads one token ahead, or just before use")
