@@ -22,9 +22,13 @@ from sparse_moe_decode_amd import synth
 
 class StackChecker:
     def __init__(self, orc, tier: str, seed: int, roles: list[dict], layers: list[int],
-                 host_layers: dict | None = None, zero_mean: bool = False, quant: int = 0):
+                 host_layers: dict | None = None, zero_mean: bool = False, quant: int = 0,
+                 dims: dict | None = None):
         self.orc = orc
-        self.dm = synth.dims(tier, quant=1) if quant == 1 else synth.dims(tier)
+        if dims is not None:  # the tier's shapes with overrides (e.g. fewer experts)
+            self.dm = dims
+        else:
+            self.dm = synth.dims(tier, quant=1) if quant == 1 else synth.dims(tier)
         oracle_cls = orc.LayerOracleAffine if quant == 1 else orc.LayerOracle
         self.roles = roles
         self.L = len(roles)

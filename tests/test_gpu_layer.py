@@ -103,3 +103,84 @@ def test_layer_step_stack_8b(api, orc, path):
     roles = synth.stack_roles("8b")
     _run_and_check(api, orc, "8b", roles, seed=5, T=3, check_layers=list(range(24)),
                    zero_mean=True, path=path)
+
+
+def _long_stack(api, n_layers, E, seed):
+    import torch
+    from sparse_moe_decode_amd import workloads as wl
+    dm = synth.dims("8b", E=E)
+    roles = ([dict(router=True, head=True)] +
+             [dict(router=False, head=True) for _ in range(n_layers - 2)] +
+             [dict(router=True, head=False)])
+    layers, keep = [], {}
+    for l, role in enumerate(roles):
+        lw = synth.layer(seed, l, dm, role, zero_mean=True)
+        keep[l] = lw
+        if l % 8 == 0:
+            announce("upload", "8b", f"E={E}", f"layer {l}/{n_layers}")
+        layers.append(dict(routed=wl.tree_to_dev(lw["routed"]), shared=wl.tree_to_dev(lw["shared"]),
+                           attn=dev(lw["attn"]),
+                           router=None if lw["router"] is None else dev(lw["router"]),
+                           router_bias=(None if lw["router_bias"] is None
+                                        else dev(lw["router_bias"])),
+                           head=wl.tree_to_dev(lw["head"])))
+    rng = synth.rng_for(seed, 10_000)
+    idx0 = np.stack([synth.random_set(rng, E, dm["K"]) for _ in range(n_layers)])
+    w0 = np.stack([synth.random_weights(rng, dm["K"]) for _ in range(n_layers)])
+    state = api.State(dm, n_layers)
+    state.route_idx[0].copy_(torch.from_numpy(idx0))
+    state.route_w[0].copy_(torch.from_numpy(w0))
+    return dm, roles, layers, keep, state
+
+
+@pytest.mark.timeout(900)
+def test_layer_step_64_layers_persistent(api, orc):
+    """The largest launch of the persistent kernel: 64 layers (8B shapes, 32
+    experts), routers on the first and last layer, heads on all but the
+    last; every layer-step of two tokens against the oracle. A 65-layer range
+    cannot be forced onto the persistent kernel (E0_ERR_SHAPE) and runs per
+    phase on the automatic path."""
+    import torch
+    from sparse_moe_decode_amd import workloads as wl
+    L, seed = 64, 17
+    dm, roles, layers, keep, state = _long_stack(api, L, 32, seed)
+    ctx = api.Context(dm, max_tokens=1)
+    model = api.Model(ctx, layers)
+    model.set_path(api.PATH_PERSISTENT)
+    toks = wl.token_inputs("8b", seed, 2, 0.5)
+    checker = StackChecker(orc, "8b", seed, roles, list(range(L)), keep, zero_mean=True, dims=dm)
+    prev_exec = None
+    h = torch.empty((L + 1, dm["d"]), dtype=torch.float16, device="cuda")
+    for t in range(2):
+        announce("layer_step", "8b", "persistent", f"L={L}", f"token {t}")
+        h[0].copy_(torch.from_numpy(toks[t]))
+        api.layer_step(ctx, model, 0, L, state, t, h)
+        assert api.device_status(ctx) == 0
+        cur, nxt = t & 1, (t + 1) & 1
+        exec_idx = host(state.exec_idx[cur]).copy()
+        checker.check(t, host(h).copy(), host(state.x_trace).copy(), exec_idx,
+                      host(state.exec_w[cur]).copy(), prev_exec, host(state.route_idx[cur]).copy(),
+                      host(state.route_w[cur]).copy(), host(state.route_idx[nxt]).copy(),
+                      host(state.route_w[nxt]).copy(), host(state.head_logits).copy())
+        prev_exec = exec_idx
+    print(f"8b E=32 persistent L={L}: {checker.steps} layer-steps checked, worst error ratio "
+          f"{checker.worst:.3f}")
+    model.close()
+
+    L2 = L + 1
+    dm2, roles2, layers2, keep2, state2 = _long_stack(api, L2, 32, seed + 1)
+    model2 = api.Model(ctx, layers2)
+    model2.set_path(api.PATH_PERSISTENT)
+    h2 = torch.zeros((L2 + 1, dm["d"]), dtype=torch.float16, device="cuda")
+    announce("layer_step", "8b", "persistent refused", f"L={L2}")
+    with pytest.raises(api.E0Error) as err:
+        api.layer_step(ctx, model2, 0, L2, state2, 0, h2)
+    assert err.value.code == api.E0_ERR_SHAPE
+    model2.set_path(api.PATH_AUTO)
+    h2[0].copy_(torch.from_numpy(toks[0]))
+    api.layer_step(ctx, model2, 0, L2, state2, 0, h2)
+    torch.cuda.synchronize()
+    assert api.device_status(ctx) == 0
+    assert bool(torch.isfinite(h2.float()).all())
+    model2.close()
+    ctx.close()
