@@ -226,34 +226,51 @@ typedef struct e0_model e0_model;
 int e0_model_create(e0_ctx* ctx, const e0_layer* layers, int32_t n_layers, e0_model** out);
 void e0_model_destroy(e0_model* model);
 
-/* How layer_step executes: E0_PATH_AUTO (default) uses the persistent
- * whole-token kernel when the shapes allow it (d a multiple of 512 up to
- * 2048, I = 512), else one kernel per phase; E0_PATH_PHASES and
- * E0_PATH_PERSISTENT force one (the latter fails with E0_ERR_SHAPE when the
- * shapes are not supported). Both compute the same step. */
-enum { E0_PATH_AUTO = 0, E0_PATH_PHASES = 1, E0_PATH_PERSISTENT = 2 };
+/* How layer_step executes. E0_PATH_AUTO (default) takes the first of these
+ * that the shapes and the layer range allow: the wave-specialised streaming
+ * kernel (E0_PATH_FLOW: symmetric int4, d 1536 or 2048, I = 512, group 64,
+ * K <= 8, E <= 256, rank 0 or 16, at most 64 layers per launch), the
+ * persistent whole-token kernel (E0_PATH_PERSISTENT: d a multiple of 512 up
+ * to 2048, I = 512; both int4 codecs), one kernel per phase (E0_PATH_PHASES,
+ * any shape). Forcing FLOW or PERSISTENT fails with E0_ERR_SHAPE when the
+ * shapes or the range do not fit it. All compute the same step. */
+enum { E0_PATH_AUTO = 0, E0_PATH_PHASES = 1, E0_PATH_PERSISTENT = 2, E0_PATH_FLOW = 3 };
 int e0_model_set_path(e0_model* model, int32_t path);
 
-/* Workgroups of the persistent kernel: one per compute unit by default (grid
+/* Workgroups of the persistent kernels: one per compute unit by default (grid
  * 0 restores that). A smaller grid leaves compute units free, so kernels on
  * other streams (the staging copies of stage_experts) run concurrently with
  * layer_step instead of between its launches; the work is spread over the
  * grid either way. E0_ERR_ARG when grid exceeds the compute units (every
  * workgroup must be resident at once), E0_ERR_SHAPE when the model's shapes do
- * not fit the persistent kernel. The trace shape follows the grid. */
+ * not fit a persistent kernel. The trace shape follows the grid; a trace
+ * buffer set for a smaller grid is dropped. */
 int e0_model_set_grid(e0_model* model, int32_t grid);
 
-/* Phase tracing of the persistent kernel (observability; off by default).
+/* Split of the FLOW kernel's grid: n_gate_up workgroups own the SwiGLU items
+ * and the head's fc1 / linear rows, n_down the output rows and the head's fc2
+ * rows; n_gate_up + n_down must equal the grid. 0, 0 (default) picks the
+ * split from the shapes. E0_ERR_SHAPE when the split does not fit the
+ * kernel's per-workgroup limits. */
+int e0_model_set_roles(e0_model* model, int32_t n_gate_up, int32_t n_down);
+
+/* Phase tracing of the persistent kernels (observability; off by default).
  * trace: device uint64 [grid][rows][points] (shape from e0_model_trace_shape;
- * rows = L + 1), or NULL to turn tracing off. Thread 0 of each workgroup
- * writes the 100 MHz wall clock at each phase boundary. Row l < L (a layer),
- * point: 0 layer start, 9 activation-independent loads issued, 1 h gathered,
- * 2 x normed, 3 routed, 4 gate/up published, 5 down and LoRA loads issued,
- * 6 SwiGLU outputs gathered, 7 shared expert and hi/lo copies done, 8 h_out
- * published; a layer with its own router also 10 logits reduced, 11 logits
- * published, 13 logits gathered, 14 routed. Row L (the heads, after the last
- * layer): 0 start, 1 fc1/linear rows published, 2 activations gathered, 3 fc2
- * rows published, 4 head routing done. */
+ * rows = L + 1), or NULL to turn tracing off. It serves launches on at most
+ * the grid it was set for. Thread 0 of each workgroup writes the 100 MHz wall
+ * clock at phase boundaries of row l < L (a layer):
+ *   PERSISTENT: 0 layer start, 9 activation-independent loads issued, 1 h
+ *     gathered, 2 x normed, 3 routed, 4 gate/up published, 5 down and LoRA
+ *     loads issued, 6 SwiGLU outputs gathered, 7 shared expert and hi/lo
+ *     copies done, 8 h_out published; a layer with its own router also 10
+ *     logits reduced, 11 logits published, 13 logits gathered, 14 routed. Row
+ *     L (the heads, after the last layer): 0 start, 1 fc1/linear rows
+ *     published, 2 activations gathered, 3 fc2 rows published, 4 head routing.
+ *   FLOW, gate/up workgroups: 0 layer start, 1 h gathered, 2 x normed, 3
+ *     routed, 4 SwiGLU items published, 5 head rows published. Down
+ *     workgroups: 0 layer start, 1 SwiGLU outputs gathered, 2 hi/lo copies, 3
+ *     h_out published, 4 previous head's fc2 published, 5 ranking of the head
+ *     before done; row L point 0: end of the launch. */
 int e0_model_set_trace(e0_model* model, uint64_t* trace);
 int32_t e0_model_trace_shape(e0_model* model, int32_t* grid, int32_t* rows, int32_t* points);
 
@@ -267,7 +284,9 @@ int32_t e0_model_trace_shape(e0_model* model, int32_t* grid, int32_t* rows, int3
  *        head's "previous token" input.
  *   head_logits          fp32 [L][E] or NULL: logits of each layer's head.
  *   x_trace              fp16 [L][d] or NULL: each layer's normed activation
- *        x (the input of its experts and head) at the last token. */
+ *        x (the input of its experts and head) at the last token.
+ *   n_layers             L, the layer count the buffers were sized for; it
+ *        must equal the model's (E0_ERR_ARG otherwise). */
 typedef struct e0_state {
   int32_t* route_idx;
   float* route_w;
@@ -275,6 +294,7 @@ typedef struct e0_state {
   float* exec_w;
   float* head_logits;
   uint16_t* x_trace;
+  int32_t n_layers;
 } e0_state;
 
 /* ---------------------------------------------------------------------------

@@ -76,7 +76,7 @@ class e0_layer(C.Structure):
 
 class e0_state(C.Structure):
     _fields_ = [("route_idx", _p), ("route_w", _p), ("exec_idx", _p), ("exec_w", _p),
-                ("head_logits", _p), ("x_trace", _p)]
+                ("head_logits", _p), ("x_trace", _p), ("n_layers", _i32)]
 
 
 _lib.e0_create.argtypes = [C.POINTER(e0_spec), _i32, C.POINTER(_p)]
@@ -91,6 +91,7 @@ _lib.e0_model_create.argtypes = [_p, C.POINTER(e0_layer), _i32, C.POINTER(_p)]
 _lib.e0_model_destroy.argtypes = [_p]
 _lib.e0_model_set_path.argtypes = [_p, _i32]
 _lib.e0_model_set_grid.argtypes = [_p, _i32]
+_lib.e0_model_set_roles.argtypes = [_p, _i32, _i32]
 _lib.e0_model_set_trace.argtypes = [_p, _p]
 _lib.e0_model_trace_shape.argtypes = [_p, C.POINTER(_i32), C.POINTER(_i32), C.POINTER(_i32)]
 _lib.layer_step.argtypes = [_p, _p, _i32, _i32, C.POINTER(e0_state), _i32, _p, _p]
@@ -119,9 +120,10 @@ EXPORTS = ["e0_create", "e0_destroy", "e0_last_error", "e0_device_status", "moe_
            "layer_step", "e0_bundle_bytes", "e0_stager_create", "e0_stager_destroy",
            "stage_experts", "stage_experts_n", "e0_stager_copies", "stage_layer",
            "e0_cache_create", "e0_cache_destroy", "e0_cache_copies", "stage_experts_cached",
-           "e0_store_open", "e0_store_close", "e0_store_read", "e0_store_wait", "e0_store_bytes", "e0_model_set_path", "e0_model_set_grid", "e0_model_set_trace", "e0_model_trace_shape"]
+           "e0_store_open", "e0_store_close", "e0_store_read", "e0_store_wait", "e0_store_bytes", "e0_model_set_path", "e0_model_set_grid", "e0_model_set_trace", "e0_model_trace_shape",
+           "e0_model_set_roles"]
 
-PATH_AUTO, PATH_PHASES, PATH_PERSISTENT = 0, 1, 2
+PATH_AUTO, PATH_PHASES, PATH_PERSISTENT, PATH_FLOW = 0, 1, 2, 3
 QUANT_SYMMETRIC, QUANT_AFFINE = 0, 1
 
 
@@ -306,12 +308,17 @@ class Model:
         return self.trace
 
     def set_path(self, path: int):
-        """PATH_AUTO, PATH_PHASES (one kernel per phase) or PATH_PERSISTENT."""
+        """PATH_AUTO, PATH_PHASES (one kernel per phase), PATH_PERSISTENT (the
+        whole-token kernel) or PATH_FLOW (the wave-specialised streaming kernel)."""
         _check(_lib.e0_model_set_path(self.handle, path))
 
     def set_grid(self, grid: int):
-        """Workgroups of the persistent kernel (0 = one per compute unit)."""
+        """Workgroups of the persistent kernels (0 = one per compute unit)."""
         _check(_lib.e0_model_set_grid(self.handle, grid))
+
+    def set_roles(self, n_gate_up: int, n_down: int):
+        """Split of the streaming kernel's grid (0, 0 = automatic)."""
+        _check(_lib.e0_model_set_roles(self.handle, n_gate_up, n_down))
 
     def close(self):
         # at interpreter exit the module globals may already be gone
@@ -337,13 +344,24 @@ class State:
                             if head_logits else None)
         self.x_trace = (torch.zeros((n_layers, dims["d"]), dtype=torch.float16, device=device)
                         if x_trace else None)
+        self.n_layers = n_layers
+        self.dims = dims
         self.struct = e0_state(_ptr(self.route_idx), _ptr(self.route_w), _ptr(self.exec_idx),
-                               _ptr(self.exec_w), _ptr(self.head_logits), _ptr(self.x_trace))
+                               _ptr(self.exec_w), _ptr(self.head_logits), _ptr(self.x_trace),
+                               n_layers)
 
 
 def layer_step(ctx: Context, model: Model, layer_begin: int, layer_end: int, state: State,
                token: int, h, stream=None):
     """One token through layers [layer_begin, layer_end); h fp16 [n+1, d] (h[0] input)."""
+    if state.n_layers != model.n_layers:
+        raise ValueError(f"state sized for {state.n_layers} layers, the model has {model.n_layers}")
+    n = layer_end - layer_begin
+    d = ctx.dims["d"]
+    if (h.dtype != torch.float16 or not h.is_cuda or not h.is_contiguous()
+            or h.numel() < (n + 1) * d):
+        raise ValueError("h must be a contiguous fp16 CUDA tensor of at least "
+                         f"{n + 1} x {d} elements")
     _check(_lib.layer_step(ctx.handle, model.handle, layer_begin, layer_end,
                            C.byref(state.struct), token, _ptr(h), _stream(stream)))
     return h

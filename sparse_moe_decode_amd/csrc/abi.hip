@@ -66,10 +66,51 @@ struct e0_model {
   int32_t ng;
   uint32_t epoch;
   int32_t path;
-  int32_t grid;  // workgroups of the persistent kernel (one per compute unit)
+  int32_t grid;  // workgroups of the persistent kernels (one per compute unit)
   int32_t cus;   // compute units of the device
   uint64_t* trace;
+  int32_t trace_grid;  // grid the trace buffer was sized for
+  // streaming kernel: exchange words [L][xlayer] and the role split
+  uint64_t* fxbuf;
+  int64_t fxwords;
+  int32_t fng, fnd;  // explicit split (0, 0: automatic)
 };
+
+namespace {
+
+// Gate/up and down workgroups of the streaming kernel for a launch of nL
+// layers on the model's grid; false when it does not fit.
+bool flow_roles(const e0_model* m, int nL, int& ng, int& nd) {
+  const Dims& dm = m->ctx->dm;
+  if (!flow_supported(dm) || m->grid < 2) return false;
+  if (m->fng > 0 && m->fnd > 0) {
+    if (m->fng + m->fnd != m->grid) return false;
+    ng = m->fng;
+    nd = m->fnd;
+    return flow_plan(dm, ng, nd, nL).ok != 0;
+  }
+  return flow_default_roles(dm, m->grid, nL, ng, nd);
+}
+
+// Size the streaming kernel's exchange words for the current split.
+hipError_t flow_alloc(e0_model* m) {
+  int ng, nd;
+  const int L = (int)m->layers.size();
+  if (!flow_roles(m, L < 64 ? L : 64, ng, nd)) return hipSuccess;
+  const FlowPlan p = flow_plan(m->ctx->dm, ng, nd, L < 64 ? L : 64);
+  const int64_t need = (int64_t)L * p.xlayer;
+  if (need <= m->fxwords) return hipSuccess;
+  if (m->fxbuf) (void)hipFree(m->fxbuf);
+  m->fxbuf = nullptr;
+  m->fxwords = 0;
+  hipError_t e = hipMalloc(&m->fxbuf, need * 8);
+  if (e == hipSuccess) e = hipMemset(m->fxbuf, 0, need * 8);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e == hipSuccess) m->fxwords = need;
+  return e;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -409,6 +450,10 @@ int e0_model_create(e0_ctx* ctx, const e0_layer* layers, int32_t n_layers, e0_mo
   m->path = E0_PATH_AUTO;
   m->grid = 0;
   m->trace = nullptr;
+  m->trace_grid = 0;
+  m->fxbuf = nullptr;
+  m->fxwords = 0;
+  m->fng = m->fnd = 0;
   const Dims& dm = ctx->dm;
   // Device table of the layers for the persistent kernel.
   std::vector<LayerDev> table(n_layers);
@@ -458,6 +503,10 @@ int e0_model_create(e0_ctx* ctx, const e0_layer* layers, int32_t n_layers, e0_mo
     m->xl = w; w += wl;
     m->grid = cus;
     m->cus = cus;
+    if ((e = flow_alloc(m)) != hipSuccess) {
+      e0_model_destroy(m);
+      return hip_fail(e, "e0_model_create: streaming-kernel buffers");
+    }
   }
   *out = m;
   return E0_OK;
@@ -467,12 +516,14 @@ void e0_model_destroy(e0_model* model) {
   if (!model) return;
   if (model->dev_table) (void)hipFree(model->dev_table);
   if (model->xbuf) (void)hipFree(model->xbuf);
+  if (model->fxbuf) (void)hipFree(model->fxbuf);
   delete model;
 }
 
 int e0_model_set_trace(e0_model* model, uint64_t* trace) {
   if (!model) return fail(E0_ERR_ARG, "e0_model_set_trace: null model");
   model->trace = trace;
+  model->trace_grid = trace ? model->grid : 0;
   return E0_OK;
 }
 
@@ -492,14 +543,44 @@ int e0_model_set_grid(e0_model* model, int32_t grid) {
     return fail(E0_ERR_ARG, "e0_model_set_grid: %d workgroups exceed the %d compute units", grid,
                 model->cus);
   model->grid = grid == 0 ? model->cus : grid;
+  if (model->trace && model->grid > model->trace_grid) {
+    model->trace = nullptr;  // sized for a smaller grid: dropped
+    model->trace_grid = 0;
+  }
+  if (model->fng + model->fnd != model->grid) model->fng = model->fnd = 0;
+  const hipError_t e = flow_alloc(model);
+  if (e != hipSuccess) return hip_fail(e, "e0_model_set_grid: streaming-kernel buffers");
+  return E0_OK;
+}
+
+int e0_model_set_roles(e0_model* model, int32_t n_gate_up, int32_t n_down) {
+  if (!model || n_gate_up < 0 || n_down < 0)
+    return fail(E0_ERR_ARG, "e0_model_set_roles: bad argument");
+  if (!model->dev_table || !flow_supported(model->ctx->dm))
+    return fail(E0_ERR_SHAPE, "e0_model_set_roles: shapes not supported by the streaming kernel");
+  if ((n_gate_up == 0) != (n_down == 0))
+    return fail(E0_ERR_ARG, "e0_model_set_roles: give both counts or neither");
+  if (n_gate_up && n_gate_up + n_down != model->grid)
+    return fail(E0_ERR_ARG, "e0_model_set_roles: %d + %d workgroups differ from the grid %d",
+                n_gate_up, n_down, model->grid);
+  const int L = (int)model->layers.size();
+  if (n_gate_up && !flow_plan(model->ctx->dm, n_gate_up, n_down, L < 64 ? L : 64).ok)
+    return fail(E0_ERR_SHAPE, "e0_model_set_roles: split %d + %d does not fit the kernel",
+                n_gate_up, n_down);
+  model->fng = n_gate_up;
+  model->fnd = n_down;
+  const hipError_t e = flow_alloc(model);
+  if (e != hipSuccess) return hip_fail(e, "e0_model_set_roles: streaming-kernel buffers");
   return E0_OK;
 }
 
 int e0_model_set_path(e0_model* model, int32_t path) {
-  if (!model || path < E0_PATH_AUTO || path > E0_PATH_PERSISTENT)
+  if (!model || path < E0_PATH_AUTO || path > E0_PATH_FLOW)
     return fail(E0_ERR_ARG, "e0_model_set_path: bad argument");
   if (path == E0_PATH_PERSISTENT && !model->dev_table)
     return fail(E0_ERR_SHAPE, "e0_model_set_path: shapes not supported by the persistent kernel");
+  if (path == E0_PATH_FLOW && (!model->dev_table || !flow_supported(model->ctx->dm)))
+    return fail(E0_ERR_SHAPE, "e0_model_set_path: shapes not supported by the streaming kernel");
   model->path = path;
   return E0_OK;
 }
@@ -512,6 +593,9 @@ int layer_step(e0_ctx* ctx, e0_model* model, int32_t layer_begin, int32_t layer_
     return fail(E0_ERR_ARG, "layer_step: bad layer range or token");
   if (!state->route_idx || !state->route_w || !state->exec_idx || !state->exec_w)
     return fail(E0_ERR_ARG, "layer_step: state buffers are null");
+  if (state->n_layers != L)
+    return fail(E0_ERR_ARG, "layer_step: state sized for %d layers, the model has %d",
+                state->n_layers, L);
   if (!aligned(h, 16) || (ctx->dm.d * 2) % 16)
     return fail(E0_ERR_ALIGN, "layer_step: h must be 16-byte aligned");
   const Dims& dm = ctx->dm;
@@ -519,6 +603,45 @@ int layer_step(e0_ctx* ctx, e0_model* model, int32_t layer_begin, int32_t layer_
   hipStream_t st = (hipStream_t)stream;
   const int K = dm.K;
   const int cur = token & 1, nxt = (token + 1) & 1;
+  if (model->trace && model->grid > model->trace_grid)
+    return fail(E0_ERR_ARG, "layer_step: the trace buffer is sized for a smaller grid");
+  const int nL = layer_end - layer_begin;
+  if ((model->path == E0_PATH_AUTO || model->path == E0_PATH_FLOW) && model->dev_table) {
+    int ng = 0, nd = 0;
+    FlowArgs a;
+    bool ok = flow_roles(model, nL, ng, nd);
+    if (ok) {
+      a.pl = flow_plan(dm, ng, nd, nL);
+      ok = a.pl.ok && (int64_t)L * a.pl.xlayer <= model->fxwords;
+    }
+    if (ok) {
+      a.dm = dm;
+      a.layers = model->dev_table;
+      a.L = L;
+      a.l0 = layer_begin;
+      a.l1 = layer_end;
+      a.token = token;
+      a.epoch = ++model->epoch;
+      if (a.epoch == 0) a.epoch = ++model->epoch;  // 0 marks never-written words
+      a.route_idx = state->route_idx;
+      a.route_w = state->route_w;
+      a.exec_idx = state->exec_idx;
+      a.exec_w = state->exec_w;
+      a.head_logits = state->head_logits;
+      a.x_trace = state->x_trace;
+      a.h = h;
+      a.sink_idx = s.sink_idx;
+      a.sink_w = s.sink_w;
+      a.flags = s.flags;
+      a.xbuf = model->fxbuf;
+      a.trace = model->trace;
+      hipError_t e = launch_flow(a, st);
+      if (e != hipSuccess) return hip_fail(e, "layer_step (streaming kernel)");
+      return E0_OK;
+    }
+    if (model->path == E0_PATH_FLOW)
+      return fail(E0_ERR_SHAPE, "layer_step: this layer range does not fit the streaming kernel");
+  }
   if (model->path != E0_PATH_PHASES && model->dev_table) {
     StackArgs a;
     a.n_heads = 0;

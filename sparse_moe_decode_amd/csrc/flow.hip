@@ -1,0 +1,1194 @@
+// Wave-specialised persistent decode kernel: one launch runs one token through
+// a range of layers, with the weight stream decoupled from the dependent chain.
+//
+// What one layer computes ("The Other Half of the Memory Wall" §3.1 Math
+// contract, §3.2 Motivation / Head / Prediction-as-routing, §3.3; head
+// layout as listed in "I counted the bytes it can't stream"):
+//   x = fp16(RMSNorm(h + a)); routing (own router, or the previous token's
+//   prediction); SwiGLU of the K routed experts and the shared expert (with
+//   its unmerged LoRA); weighted down projections; h' = fp16(h + a + y); and,
+//   on head layers, the prerouter head over [x; onehot(S_cur); onehot(S_prev)]
+//   whose top-K becomes the next token's routing of the next layer.
+//
+// Layout of the work on the chip:
+//   * gate/up CUs [0, ng): gather h_l, norm it (every one of them), own a
+//     contiguous range of (expert, row) SwiGLU items and publish their
+//     outputs; the first E/4 also own four router rows each, the next 2r one
+//     LoRA A row each (the shared expert's gate/up A products); in the wait
+//     for the next layer they compute their share of the head's fc1 and
+//     linear-path rows;
+//   * down CUs [ng, ng + nd): gather all SwiGLU outputs, own a contiguous
+//     range of output row pairs (every expert slot, the down LoRA, the
+//     residual) and publish h_{l+1}; in the wait for the next layer they
+//     compute their share of the previous head's fc2 rows, and one of them
+//     ranks the head before that into the next token's prediction.
+// Every CU runs four compute waves and three loader waves. The loaders
+// stream a layer's rows into one of two LDS layer slots with direct-to-LDS
+// loads (their own vector memory counters, no registers), a layer ahead of
+// the compute; the third streams router and head rows into their own
+// buffers. Routed rows of a predicted layer are known at launch; on a router
+// layer they are issued as soon as the CU has ranked its own logits.
+// Loaders and compute waves meet only through LDS flags; the compute waves
+// synchronise among themselves with an LDS counter.
+//
+// Cross-CU data moves as 8-byte words (32-bit payload, 32-bit launch epoch)
+// stored and polled with agent-scope relaxed atomics (single-copy atomic, so
+// a word with the current epoch carries this launch's payload). Each
+// producer owns whole 64-byte blocks (no line is written by two CUs), and
+// consumers poll with 16-byte coherent loads. Every wait is bounded by the
+// wall clock; on expiry the kernel raises FLAG_SYNC and runs to completion.
+
+#include "gemv.h"
+#include "internal.h"
+
+namespace smd {
+
+namespace {
+
+constexpr int kFC = 256;                  // compute threads (four waves)
+constexpr int kFW = kFC / 64;
+constexpr int kFL = 3;                    // loader waves
+constexpr int kFThreads = kFC + 64 * kFL;
+constexpr int kGL = 16;                   // lanes per group
+constexpr int kGN = kFC / kGL;            // groups
+constexpr int kFRank = 16;
+constexpr int kFI = 512;
+constexpr int kFMaxL = 64;
+constexpr uint64_t kFSpin = 20000000ull;  // 0.2 s of the 100 MHz wall clock
+constexpr int kRouterRows = 4;
+constexpr int kBlk = 8;                   // words of a small exchange block
+
+// LDS flag words (loader <-> compute handshakes, compute barrier).
+enum {
+  FL_READY = 0,    // [2] layer slot landed (step + 1)
+  FL_PRE = 2,      // [2] the part of the slot that needs no routing landed
+  FL_FREED = 4,    // [2][4] slot released by compute wave w (step + 1)
+  FL_ROUTE = 12,   // routing of this step known (step + 1)
+  FL_RREADY = 13,  // router rows landed (step + 1)
+  FL_RFREED = 14,  // [4] router rows consumed by wave w (step + 1)
+  FL_HREADY = 18,  // head rows / fc2 rows landed (step + 1)
+  FL_HFREED = 19,  // [4] consumed by wave w (step + 1)
+  FL_CBAR = 23,
+  FL_ABORT = 24,
+  FL_N = 32
+};
+
+// per-step layer flags
+enum { LF_ROUTER = 1, LF_HEAD = 2, LF_SHARED = 4, LF_LORA = 8, LF_LORAD = 16, LF_ATTN = 32 };
+
+__shared__ __align__(16) unsigned char s_mem[kFlowLds];
+__shared__ int s_fl[FL_N];
+
+typedef __attribute__((address_space(3))) void lds_v;
+typedef __attribute__((address_space(1))) void glb_v;
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int fl_ld(int i) {
+  return __hip_atomic_load(&s_fl[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void fl_st(int i, int v) {
+  __hip_atomic_store(&s_fl[i], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+struct Waiter {
+  uint64_t t0;
+  uint32_t polls;
+};
+
+// A wait gives up once this CU has given up, any CU raised the sync flag, or
+// 0.2 s passed (then it raises the flag itself).
+__device__ __forceinline__ bool expired(Waiter& w, int32_t* gflags) {
+  if (fl_ld(FL_ABORT)) return true;
+  if ((++w.polls & 63u) == 0 &&
+      __hip_atomic_load(&gflags[FLAG_SYNC], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+    fl_st(FL_ABORT, 1);
+    return true;
+  }
+  if (wall_clock64() - w.t0 > kFSpin) {
+    atomicOr(&gflags[FLAG_SYNC], 1);
+    fl_st(FL_ABORT, 1);
+    return true;
+  }
+  return false;
+}
+
+// Wait until flag i reaches v.
+__device__ __forceinline__ void fl_wait(int i, int v, int32_t* gflags) {
+  if (fl_ld(i) >= v) return;
+  Waiter w{(uint64_t)wall_clock64(), 0};
+  while (fl_ld(i) < v) {
+    if (expired(w, gflags)) return;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// Wait until flags i .. i+n-1 all reach v.
+__device__ __forceinline__ void fl_wait_all(int i, int n, int v, int32_t* gflags) {
+  for (int q = 0; q < n; ++q) fl_wait(i + q, v, gflags);
+}
+
+// Barrier of the compute waves (the loader waves never join it).
+__device__ __forceinline__ void cbar(int& phase, int32_t* gflags) {
+  phase += kFW;
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+  asm volatile("" ::: "memory");
+  if ((threadIdx.x & 63) == 0)
+    __hip_atomic_fetch_add(&s_fl[FL_CBAR], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  fl_wait(FL_CBAR, phase, gflags);
+  asm volatile("" ::: "memory");
+}
+
+// Release a flag after this wave's LDS reads of the resource completed.
+__device__ __forceinline__ void release(int i, int v) {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("" ::: "memory");
+  if ((threadIdx.x & 63) == 0) fl_st(i, v);
+}
+
+// Loader: all direct-to-LDS loads of this wave have landed.
+__device__ __forceinline__ void dma_drain() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void xput(uint64_t* p, uint32_t v, uint32_t ep) {
+  __hip_atomic_store(p, ((uint64_t)ep << 32) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t fbits(float v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ float bitsf(uint32_t v) { return __builtin_bit_cast(float, v); }
+
+// Threads [0, nthr) poll words [0, n) of an exchange region (n even, region
+// 16-byte aligned) with 16-byte coherent loads until every word carries the
+// epoch; sink(word, payload) then sees each word once.
+template <int U, typename Sink>
+__device__ __forceinline__ void xgather(const uint64_t* base, int n, uint32_t ep, int tid, int nthr,
+                                        int32_t* gflags, Sink&& sink) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, n * 8, 0x00020000);
+  const int np = n >> 1;
+  for (int b0 = 0; b0 < np; b0 += U * nthr) {
+    u32x4v v[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int p = b0 + j * nthr + tid;
+      v[j] = p < np ? __builtin_amdgcn_raw_buffer_load_b128(rs, p * 16, 0, 16)
+                    : (u32x4v){0u, ep, 0u, ep};
+    }
+    Waiter w{0, 0};
+    bool started = false;
+    for (;;) {
+      bool ok = true;
+#pragma unroll
+      for (int j = 0; j < U; ++j) ok = ok && v[j].y == ep && v[j].w == ep;
+      if (ok) break;
+      if (!started) {
+        w.t0 = wall_clock64();
+        started = true;
+      }
+      if (expired(w, gflags)) break;
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        const int p = b0 + j * nthr + tid;
+        if (p < np && (v[j].y != ep || v[j].w != ep))
+          v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, p * 16, 0, 16);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int p = b0 + j * nthr + tid;
+      if (p < np) {
+        sink(2 * p, v[j].x);
+        sink(2 * p + 1, v[j].z);
+      }
+    }
+  }
+}
+
+template <typename Sink>
+__device__ __forceinline__ void xgather_any(const uint64_t* base, int n, uint32_t ep, int tid,
+                                            int nthr, int32_t* gflags, Sink&& sink) {
+  const int per = (n / 2 + nthr - 1) / nthr;  // pairs per thread
+  if (per <= 2) xgather<2>(base, n, ep, tid, nthr, gflags, sink);
+  else if (per <= 4) xgather<4>(base, n, ep, tid, nthr, gflags, sink);
+  else if (per <= 8) xgather<8>(base, n, ep, tid, nthr, gflags, sink);
+  else xgather<16>(base, n, ep, tid, nthr, gflags, sink);
+}
+
+// Loader: npieces 16-byte pieces into LDS dst (piece q at dst + 16 q) from
+// addr(q); lanes whose piece is invalid (ok(q) false) or past the end load
+// nothing.
+template <typename Addr, typename Ok>
+__device__ __forceinline__ void dma16(unsigned char* dst, int npieces, Addr&& addr, Ok&& ok) {
+  const int lane = threadIdx.x & 63;
+  for (int i = 0; i < npieces; i += 64) {
+    const int q = i + lane;
+    if (q < npieces && ok(q))
+      __builtin_amdgcn_global_load_lds((glb_v*)addr(q), (lds_v*)(dst + 16 * i), 16, 0, 0);
+  }
+}
+
+template <typename Addr>
+__device__ __forceinline__ void dma4(unsigned char* dst, int npieces, Addr&& addr) {
+  const int lane = threadIdx.x & 63;
+  for (int i = 0; i < npieces; i += 64) {
+    const int q = i + lane;
+    if (q < npieces)
+      __builtin_amdgcn_global_load_lds((glb_v*)addr(q), (lds_v*)(dst + 4 * i), 4, 0, 0);
+  }
+}
+
+__device__ __forceinline__ const char* cptr(const void* p) { return (const char*)p; }
+
+// Contiguous share [beg, end) of n items for part c of G.
+__device__ __forceinline__ int share_b(int n, int G, int c) {
+  return (int)((int64_t)n * c / G);
+}
+
+__device__ __forceinline__ void stamp(const FlowArgs& a, int row, int k) {
+  if (a.trace && threadIdx.x == 0)
+    a.trace[((int64_t)blockIdx.x * (a.L + 1) + row) * kTracePoints + k] = wall_clock64();
+}
+
+__device__ __forceinline__ float dot8_h(uint4 w, uint4 x, float acc) {
+  acc = dot2(as_h2(w.x), as_h2(x.x), acc);
+  acc = dot2(as_h2(w.y), as_h2(x.y), acc);
+  acc = dot2(as_h2(w.z), as_h2(x.z), acc);
+  acc = dot2(as_h2(w.w), as_h2(x.w), acc);
+  return acc;
+}
+
+template <typename T>
+__device__ __forceinline__ T* lds_at(int off) {
+  return reinterpret_cast<T*>(s_mem + off);
+}
+
+// Routing tables of the launch in LDS: [nL][K] each.
+struct RT {
+  int32_t* idx;
+  float* w;
+  int32_t* prev;
+  int32_t* ent;
+  int32_t* lf;
+};
+
+__device__ __forceinline__ RT rt_at(int off, int nL, int K) {
+  RT t;
+  t.idx = lds_at<int32_t>(off);
+  t.w = lds_at<float>(off + nL * K * 4);
+  t.prev = lds_at<int32_t>(off + 2 * nL * K * 4);
+  t.ent = lds_at<int32_t>(off + 3 * nL * K * 4);
+  t.lf = lds_at<int32_t>(off + 4 * nL * K * 4);
+  return t;
+}
+
+// Dot of a wave's fp16 row (LDS, natural order, d columns) with x (LDS,
+// natural fp16): lane takes 8-element chunks lane + 64 m.
+template <int CPL>
+__device__ __forceinline__ float wave_row_dot(const uint16_t* row, const uint16_t* x) {
+  const int lane = threadIdx.x & 63;
+  float acc = 0.0f;
+#pragma unroll
+  for (int m = 0; m < CPL; ++m) {
+    const int c = lane + 64 * m;
+    acc = dot8_h(*reinterpret_cast<const uint4*>(row + 8 * c),
+                 *reinterpret_cast<const uint4*>(x + 8 * c), acc);
+  }
+  return acc;
+}
+
+// ============================================================ gate/up CUs ==
+
+template <int CPL, int KM>
+__device__ void gu_loader(const FlowArgs& a, int lw) {
+  const FlowPlan& p = a.pl;
+  constexpr int d = 512 * CPL;
+  const int K = a.dm.K, E = a.dm.E, r = a.dm.r, I = kFI;
+  const int nL = a.l1 - a.l0;
+  const int cu = blockIdx.x;
+  const RT rt = rt_at(p.g_rt, nL, K);
+  const int ib = share_b(p.items, p.ng, cu), ie = share_b(p.items, p.ng, cu + 1);
+  const int ipc = ie - ib;
+  const int KI = K * I;
+  const int js0 = ib >= KI ? 0 : (ie > KI ? KI - ib : ipc);  // first shared item (local)
+  const int aq = (cu >= p.ca0 && cu < p.ca0 + 2 * r) ? cu - p.ca0 : -1;
+  const int srow0 = (ib > KI ? ib : KI) - KI, srow1 = ie - KI;
+  const int adw = js0 < ipc ? ((srow1 + 1) >> 1) - (srow0 >> 1) : 0;
+  int32_t* gf = a.flags;
+  if (lw < 2) {
+    for (int step = lw; step < nL; step += 2) {
+      const int slot = lw;
+      const int l = a.l0 + step;
+      if (step >= 2) fl_wait_all(FL_FREED + 4 * slot, kFW, step - 1, gf);
+      const LayerDev& Ly = a.layers[l];
+      const int lf = rt.lf[step];
+      unsigned char* S = s_mem + slot * p.g_slot;
+      if (lf & LF_ATTN)
+        dma16(S + p.g_at, d / 8, [&](int q) { return cptr(Ly.attn) + 16 * q; },
+              [](int) { return true; });
+      if (aq >= 0 && (lf & LF_LORA)) {
+        const uint16_t* A = (aq < r ? Ly.sh.ag : Ly.sh.au) + (int64_t)(aq % r) * d;
+        dma16(S + p.g_ar, d / 8, [&](int q) { return cptr(A) + 16 * q; }, [](int) { return true; });
+      }
+      // items: gate/up rows (d/32 pieces each), then their scales (d/512 each)
+      const int pr = d / 32, ps = d / 512;
+      auto item_dma = [&](int j0, int j1) {
+        if (j1 <= j0) return;
+        auto base = [&](int jj, int pj, bool sc) -> const char* {
+          const int it = ib + jj;
+          const int k = it / I, row = it % I;
+          if (k < K) {
+            const int ent = rt.ent[step * K + k];
+            const Q4& q4 = pj ? Ly.pool.up : Ly.pool.gate;
+            return sc ? cptr(q4.s) + ent * Ly.pool.stride_s + (int64_t)row * (d / 32)
+                      : cptr(q4.q) + ent * Ly.pool.stride_q + (int64_t)row * (d / 2);
+          }
+          const Q4& q4 = pj ? Ly.sh.up : Ly.sh.gate;
+          return sc ? cptr(q4.s) + (int64_t)row * (d / 32) : cptr(q4.q) + (int64_t)row * (d / 2);
+        };
+        auto valid = [&](int jj) {
+          const int k = (ib + jj) / I;
+          return k < K ? rt.ent[step * K + k] >= 0 : (lf & LF_SHARED) != 0;
+        };
+        dma16(S + p.g_gq + 16 * (j0 * 2 * pr), (j1 - j0) * 2 * pr,
+              [&](int q) {
+                const int jj = j0 + q / (2 * pr), rem = q % (2 * pr);
+                return base(jj, rem / pr, false) + 16 * (rem % pr);
+              },
+              [&](int q) { return valid(j0 + q / (2 * pr)); });
+        dma16(S + p.g_gs + 16 * (j0 * 2 * ps), (j1 - j0) * 2 * ps,
+              [&](int q) {
+                const int jj = j0 + q / (2 * ps), rem = q % (2 * ps);
+                return base(jj, rem / ps, true) + 16 * (rem % ps);
+              },
+              [&](int q) { return valid(j0 + q / (2 * ps)); });
+      };
+      if (js0 < ipc && (lf & LF_SHARED)) {
+        item_dma(js0, ipc);
+        if (lf & LF_LORA)  // LoRA B rows of gate and up (r fp16 = 2 pieces each)
+          dma16(S + p.g_lb + 16 * (js0 * 4), (ipc - js0) * 4,
+                [&](int q) {
+                  const int jj = js0 + q / 4, pj = (q / 2) % 2, row = ib + jj - KI;
+                  return cptr(pj ? Ly.sh.bu : Ly.sh.bg) + (int64_t)row * r * 2 + 16 * (q % 2);
+                },
+                [](int) { return true; });
+        if (lf & LF_LORAD)  // A_down columns of the CU's shared rows, as 4-byte words
+          dma4(S + p.g_ad, r * adw, [&](int q) {
+            const int t = q / adw, w = q % adw;
+            return cptr(Ly.sh.ad) + ((int64_t)t * a.dm.Is + (srow0 & ~1) + 2 * w) * 2;
+          });
+      }
+      const bool routed_known = !(lf & LF_ROUTER);
+      if (routed_known) item_dma(0, js0);
+      dma_drain();
+      fl_st(FL_PRE + slot, step + 1);
+      if (!routed_known && js0 > 0) {
+        fl_wait(FL_ROUTE, step + 1, gf);
+        item_dma(0, js0);
+        dma_drain();
+      }
+      fl_st(FL_READY + slot, step + 1);
+    }
+    return;
+  }
+  // router rows and head rows
+  const bool rcu = cu < p.nrc;
+  const int r0 = kRouterRows * cu, r1 = min(r0 + kRouterRows, E);
+  const int hb = share_b(p.hrn, p.ng, cu), he = share_b(p.hrn, p.ng, cu + 1);
+  const int P = a.dm.P, F = d + 2 * E;
+  int prev_r = 0, prev_h = 0;
+  for (int step = 0; step < nL; ++step) {
+    const int l = a.l0 + step;
+    const int lf = rt.lf[step];
+    const LayerDev& Ly = a.layers[l];
+    if ((lf & LF_ROUTER) && rcu && r1 > r0) {
+      fl_wait_all(FL_RFREED, kFW, prev_r, gf);
+      dma16(s_mem + p.g_rb, (r1 - r0) * (d / 8),
+            [&](int q) { return cptr(Ly.router) + ((int64_t)(r0 + q / (d / 8)) * d) * 2 + 16 * (q % (d / 8)); },
+            [](int) { return true; });
+      dma_drain();
+      fl_st(FL_RREADY, step + 1);
+      prev_r = step + 1;
+    }
+    if (lf & LF_HEAD) {
+      fl_wait_all(FL_HFREED, kFW, prev_h, gf);
+      auto hrow = [&](int hr) -> const char* {
+        return hr < P ? cptr(Ly.head.fc1) + (int64_t)hr * F * 2 : cptr(Ly.head.lin) + (int64_t)(hr - P) * F * 2;
+      };
+      if (he > hb) {
+        dma16(s_mem + p.g_hb, (he - hb) * (d / 8),
+              [&](int q) { return hrow(hb + q / (d / 8)) + 16 * (q % (d / 8)); },
+              [](int) { return true; });
+        if (lf & LF_ROUTER) fl_wait(FL_ROUTE, step + 1, gf);
+        dma4(s_mem + p.g_hc, (he - hb) * 2 * K, [&](int q) {
+          const int rr = q / (2 * K), kk = q % (2 * K);
+          const int e = kk < K ? rt.idx[step * K + kk] : rt.prev[step * K + kk - K];
+          const int col = (e >= 0 && e < E) ? (kk < K ? d + e : d + E + e) : d;
+          return hrow(hb + rr) + (col & ~1) * 2;
+        });
+      }
+      dma_drain();
+      fl_st(FL_HREADY, step + 1);
+      prev_h = step + 1;
+    }
+  }
+}
+
+template <int CPL, int KM>
+__device__ void gu_compute(const FlowArgs& a) {
+  const FlowPlan& p = a.pl;
+  constexpr int d = 512 * CPL;
+  const Dims& dm = a.dm;
+  const int K = dm.K, E = dm.E, r = dm.r, I = kFI, P = dm.P;
+  const int nL = a.l1 - a.l0;
+  const int cu = blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int li = t % kGL, grp = t / kGL;
+  const uint32_t ep = a.epoch;
+  const int cur = a.token & 1;
+  int32_t* gf = a.flags;
+  const RT rt = rt_at(p.g_rt, nL, K);
+  const int ib = share_b(p.items, p.ng, cu), ie = share_b(p.items, p.ng, cu + 1);
+  const int ipc = ie - ib;
+  const int KI = K * I;
+  const int js0 = ib >= KI ? 0 : (ie > KI ? KI - ib : ipc);
+  const int aq = (cu >= p.ca0 && cu < p.ca0 + 2 * r) ? cu - p.ca0 : -1;
+  const int srow0 = (ib > KI ? ib : KI) - KI, srow1 = ie - KI;
+  const int adw = js0 < ipc ? ((srow1 + 1) >> 1) - (srow0 >> 1) : 0;
+  const bool rcu = cu < p.nrc;
+  const int r0 = kRouterRows * cu, r1 = min(r0 + kRouterRows, E);
+  const int hb = share_b(p.hrn, p.ng, cu), he = share_b(p.hrn, p.ng, cu + 1);
+  uint16_t* hbuf = lds_at<uint16_t>(p.g_h);
+  uint16_t* xn = lds_at<uint16_t>(p.g_xn);
+  uint16_t* xp = lds_at<uint16_t>(p.g_xp);
+  float* lg = lds_at<float>(p.g_lg);
+  RouteScratch& rs = *lds_at<RouteScratch>(p.g_rs);
+  float* axw = lds_at<float>(p.g_ax) + wave * 2 * kFRank;
+  float* pp = lds_at<float>(p.g_pp);
+  int phase = 0;
+
+  for (int step = 0; step < nL; ++step) {
+    const int l = a.l0 + step;
+    const int slot = step & 1;
+    const int lf = rt.lf[step];
+    const unsigned char* S = s_mem + slot * p.g_slot;
+    uint64_t* X = a.xbuf + (int64_t)l * p.xlayer;
+    const LayerDev& Ly = a.layers[l];
+    stamp(a, l, 0);
+    fl_wait(FL_PRE + slot, step + 1, gf);
+
+    // ---- h_l ---------------------------------------------------------------
+    if (step == 0) {
+      if (t < d / 8)
+        *reinterpret_cast<uint4*>(hbuf + 8 * t) = ldg(reinterpret_cast<const uint4*>(a.h + 8 * t));
+    } else {
+      const uint64_t* XA = a.xbuf + (int64_t)(l - 1) * p.xlayer + p.o_xa;
+      uint32_t* h32 = reinterpret_cast<uint32_t*>(hbuf);
+      xgather_any(XA, p.nd * p.ba, ep, t, kFC, gf, [&](int wi, uint32_t v) {
+        const int jd = wi / p.ba, o = wi % p.ba;
+        const int pb = share_b(d / 2, p.nd, jd), pe = share_b(d / 2, p.nd, jd + 1);
+        if (o < pe - pb) h32[pb + o] = v;
+      });
+    }
+    cbar(phase, gf);
+    stamp(a, l, 1);
+
+    // ---- RMSNorm: every wave sums the squares itself -------------------------
+    {
+      const uint16_t* at = reinterpret_cast<const uint16_t*>(S + p.g_at);
+      const bool att = (lf & LF_ATTN) != 0;
+      float ss = 0.0f;
+#pragma unroll
+      for (int m = 0; m < CPL; ++m) {
+        const int c = lane + 64 * m;
+        const uint4 hv = *reinterpret_cast<const uint4*>(hbuf + 8 * c);
+        const uint4 av = att ? *reinterpret_cast<const uint4*>(at + 8 * c) : make_uint4(0, 0, 0, 0);
+        const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w}, aw[4] = {av.x, av.y, av.z, av.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float v0 = h2f((uint16_t)(hw[q] & 0xFFFF)) + h2f((uint16_t)(aw[q] & 0xFFFF));
+          const float v1 = h2f((uint16_t)(hw[q] >> 16)) + h2f((uint16_t)(aw[q] >> 16));
+          ss = fmaf(v0, v0, ss);
+          ss = fmaf(v1, v1, ss);
+        }
+      }
+      const float tot = wave_sum_rows(ss);
+      const float inv = 1.0f / sqrtf(tot / d + dm.eps);
+      if (t < d / 8) {
+        const uint4 hv = *reinterpret_cast<const uint4*>(hbuf + 8 * t);
+        const uint4 av = att ? *reinterpret_cast<const uint4*>(at + 8 * t) : make_uint4(0, 0, 0, 0);
+        const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w}, aw[4] = {av.x, av.y, av.z, av.w};
+        uint16_t xv[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          xv[2 * q] = f2h((h2f((uint16_t)(hw[q] & 0xFFFF)) + h2f((uint16_t)(aw[q] & 0xFFFF))) * inv);
+          xv[2 * q + 1] = f2h((h2f((uint16_t)(hw[q] >> 16)) + h2f((uint16_t)(aw[q] >> 16))) * inv);
+        }
+        const uint4 nat = make_uint4(xv[0] | ((uint32_t)xv[1] << 16), xv[2] | ((uint32_t)xv[3] << 16),
+                                     xv[4] | ((uint32_t)xv[5] << 16), xv[6] | ((uint32_t)xv[7] << 16));
+        const uint4 per = make_uint4(xv[0] | ((uint32_t)xv[4] << 16), xv[1] | ((uint32_t)xv[5] << 16),
+                                     xv[2] | ((uint32_t)xv[6] << 16), xv[3] | ((uint32_t)xv[7] << 16));
+        *reinterpret_cast<uint4*>(xn + 8 * t) = nat;
+        *reinterpret_cast<uint4*>(xp + 8 * t) = per;
+        if (cu == 0 && a.x_trace) *reinterpret_cast<uint4*>(a.x_trace + (int64_t)l * d + 8 * t) = nat;
+      }
+    }
+    cbar(phase, gf);
+    stamp(a, l, 2);
+
+    // ---- LoRA A row (shared gate/up) and router rows --------------------------
+    if (aq >= 0 && wave == 0) {
+      float v = 0.0f;
+      if (lf & LF_LORA) v = wave_sum_rows(wave_row_dot<CPL>(reinterpret_cast<const uint16_t*>(S + p.g_ar), xn));
+      if (lane < kBlk) xput(X + p.o_xl + aq * kBlk + lane, lane == 0 ? fbits(v) : 0u, ep);
+    }
+    if ((lf & LF_ROUTER) && rcu) {
+      fl_wait(FL_RREADY, step + 1, gf);
+      const int nr = r1 - r0;
+      if (wave < nr) {
+        const float v = wave_sum_rows(wave_row_dot<CPL>(lds_at<uint16_t>(p.g_rb) + wave * d, xn));
+        if (lane == 0) xput(X + p.o_xr + cu * kBlk + wave, fbits(v), ep);
+      }
+      if (wave == 0 && lane >= nr && lane < kBlk) xput(X + p.o_xr + cu * kBlk + lane, 0u, ep);
+      release(FL_RFREED + wave, step + 1);
+    }
+
+    // ---- routing -----------------------------------------------------------
+    if (lf & LF_ROUTER) {
+      if (wave == 0) {
+        xgather_any(X + p.o_xr, p.nrc * kBlk, ep, lane, 64, gf, [&](int wi, uint32_t v) {
+          const int c = wi / kBlk, o = wi % kBlk, e = kRouterRows * c + o;
+          if (o < kRouterRows && e < E) lg[e] = bitsf(v);
+        });
+        wave_lds_sync();
+        route_wave(dm, lg, Ly.router_bias, rs, rt.idx + step * K, rt.w + step * K, gf);
+        wave_lds_sync();
+        if (lane < K) {
+          const int64_t ent = resolve_entry(Ly.pool, E, rt.idx[step * K + lane]);
+          rt.ent[step * K + lane] = (int32_t)ent;
+          if (ent < 0 && cu == 0) atomicOr(&gf[FLAG_RANGE], 1);
+        }
+        release(FL_ROUTE, step + 1);
+      } else {
+        fl_wait(FL_ROUTE, step + 1, gf);
+      }
+    } else if (cu == 0 && wave == 0 && lane < K && rt.ent[step * K + lane] < 0) {
+      atomicOr(&gf[FLAG_RANGE], 1);
+    }
+    if (cu == 0 && wave == 0 && lane < K) {
+      a.exec_idx[((int64_t)cur * a.L + l) * K + lane] = rt.idx[step * K + lane];
+      a.exec_w[((int64_t)cur * a.L + l) * K + lane] = rt.w[step * K + lane];
+    }
+    stamp(a, l, 3);
+
+    // ---- gate/up items ---------------------------------------------------------
+    fl_wait(FL_READY + slot, step + 1, gf);
+    {
+      // the lane's activation chunks li + 16 m (pair-permuted fp16)
+      f16x2 xr[CPL][16];
+#pragma unroll
+      for (int m = 0; m < CPL; ++m) load_xchunk(xp, li + kGL * m, xr[m]);
+      // LoRA A products for shared items, gathered once per wave
+      // does any group of this wave own a shared item? (wave-uniform)
+      const bool mine_sh = (grp >= js0 && grp < ipc) || (grp + kGN >= js0 && grp + kGN < ipc);
+      const bool wave_sh = (lf & LF_SHARED) && (lf & LF_LORA) && __ballot(mine_sh) != 0;
+      if (wave_sh) {
+        xgather_any(X + p.o_xl, 2 * r * kBlk, ep, lane, 64, gf, [&](int wi, uint32_t v) {
+          if (wi % kBlk == 0) axw[wi / kBlk] = bitsf(v);
+        });
+        wave_lds_sync();
+      }
+      float pacc = 0.0f;  // A_down partial of rank li over this group's shared items
+      const float lc = dm.lora_scale;
+#pragma unroll
+      for (int j2 = 0; j2 < 2; ++j2) {
+        const int jj = grp + kGN * j2;
+        if (jj >= ipc) continue;  // uniform over the group
+        const int it = ib + jj;
+        const int k = it / I, row = it % I;
+        const bool shared = k >= K;
+        const bool ok = shared ? (lf & LF_SHARED) != 0 : rt.ent[step * K + k] >= 0;
+        float ag = 0.0f, au = 0.0f;
+        if (ok) {
+          const uint4* gq = reinterpret_cast<const uint4*>(S + p.g_gq + (2 * jj) * (d / 2));
+          const uint4* uq = reinterpret_cast<const uint4*>(S + p.g_gq + (2 * jj + 1) * (d / 2));
+          const uint16_t* gs = reinterpret_cast<const uint16_t*>(S + p.g_gs + (2 * jj) * (d / 32));
+          const uint16_t* us = reinterpret_cast<const uint16_t*>(S + p.g_gs + (2 * jj + 1) * (d / 32));
+#pragma unroll
+          for (int m = 0; m < CPL; ++m) {
+            const int c = li + kGL * m;
+            ag += h2f(gs[c >> 1]) * q4_dot32(gq[c], xr[m]);
+            au += h2f(us[c >> 1]) * q4_dot32(uq[c], xr[m]);
+          }
+        }
+        ag = group_sum<kGL>(ag);
+        au = group_sum<kGL>(au);
+        float out = 0.0f;
+        if (ok) {
+          if (shared && (lf & LF_LORA)) {
+            const uint16_t* bg = reinterpret_cast<const uint16_t*>(S + p.g_lb) + (2 * jj) * r;
+            const uint16_t* bu = bg + r;
+            ag = fmaf(lc, group_sum<kGL>(h2f(bg[li]) * axw[li]), ag);
+            au = fmaf(lc, group_sum<kGL>(h2f(bu[li]) * axw[r + li]), au);
+          }
+          out = silu(ag) * au;
+        }
+        if (shared && (lf & LF_LORAD)) {
+          const int srow = row, wdx = (srow >> 1) - (srow0 >> 1);
+          const uint16_t* adc = reinterpret_cast<const uint16_t*>(S + p.g_ad);
+          pacc = fmaf(h2f(adc[2 * (li * adw + wdx) + (srow & 1)]), out, pacc);
+        }
+        if (li == 0) xput(X + p.o_xb + cu * p.bi + jj, fbits(out), ep);
+      }
+      if (t >= ipc && t < p.bi) xput(X + p.o_xb + cu * p.bi + t, 0u, ep);
+      release(FL_FREED + 4 * slot + wave, step + 1);
+      // A_down partial of the CU's shared rows: one block per shared-owner CU
+      if (js0 < ipc && p.pbw) {
+        pp[grp * kFRank + li] = pacc;
+        cbar(phase, gf);
+        if (wave == 0 && lane < p.pbw) {
+          float v = 0.0f;
+          if (lane < r)
+            for (int g = 0; g < kGN; ++g) v += pp[g * kFRank + lane];
+          xput(X + p.o_xb + p.ng * p.bi + (cu - p.cs0) * p.pbw + lane, fbits(v), ep);
+        }
+      }
+    }
+    stamp(a, l, 4);
+
+    // ---- head: fc1 and linear-path rows --------------------------------------------
+    if (lf & LF_HEAD) {
+      fl_wait(FL_HREADY, step + 1, gf);
+      const int nh = he - hb;
+      for (int rr = wave; rr < nh; rr += kFW) {
+        const int hr = hb + rr;
+        float acc = wave_row_dot<CPL>(lds_at<uint16_t>(p.g_hb) + rr * d, xn);
+        if (lane < 2 * K) {
+          const int e = lane < K ? rt.idx[step * K + lane] : rt.prev[step * K + lane - K];
+          if (e >= 0 && e < E) {
+            const int col = lane < K ? d + e : d + E + e;
+            const uint32_t wv = lds_at<uint32_t>(p.g_hc)[rr * 2 * K + lane];
+            acc += h2f((uint16_t)((col & 1) ? wv >> 16 : wv & 0xFFFF));
+          }
+        }
+        acc = wave_sum_rows(acc);
+        if (lane == 0) xput(X + p.o_xh1 + cu * kBlk + rr, fbits(hr < P ? gelu_erf(acc) : acc), ep);
+      }
+      if (wave == 0 && lane >= nh && lane < kBlk) xput(X + p.o_xh1 + cu * kBlk + lane, 0u, ep);
+      release(FL_HFREED + wave, step + 1);
+    }
+    stamp(a, l, 5);
+  }
+}
+
+// ============================================================== down CUs ==
+
+template <int CPL, int KM>
+__device__ void dn_loader(const FlowArgs& a, int lw) {
+  const FlowPlan& p = a.pl;
+  constexpr int d = 512 * CPL;
+  const int K = a.dm.K, E = a.dm.E, r = a.dm.r, I = kFI, P = a.dm.P;
+  const int nL = a.l1 - a.l0;
+  const int j = blockIdx.x - p.ng;
+  const RT rt = rt_at(p.d_rt, nL, K);
+  const int pb = share_b(d / 2, p.nd, j), pe = share_b(d / 2, p.nd, j + 1);
+  const int rpc = 2 * (pe - pb);
+  const int KX = p.KX;
+  int32_t* gf = a.flags;
+  if (lw < 2) {
+    for (int step = lw; step < nL; step += 2) {
+      const int slot = lw;
+      const int l = a.l0 + step;
+      if (step >= 2) fl_wait_all(FL_FREED + 4 * slot, kFW, step - 1, gf);
+      const LayerDev& Ly = a.layers[l];
+      const int lf = rt.lf[step];
+      unsigned char* S = s_mem + slot * p.d_slot;
+      if (lf & LF_ATTN) dma4(S + p.d_at, rpc / 2, [&](int q) { return cptr(Ly.attn) + (int64_t)(pb + q) * 4; });
+      // rows of expert slot k: [k][rr][I/2 bytes], scales [k][rr][16 bytes]
+      auto exp_dma = [&](int k0, int k1) {
+        if (k1 <= k0) return;
+        auto qbase = [&](int k, int rr, bool sc) -> const char* {
+          const int row = 2 * pb + rr;
+          if (k < K) {
+            const int ent = rt.ent[step * K + k];
+            return sc ? cptr(Ly.pool.down.s) + ent * Ly.pool.stride_s + (int64_t)row * 16
+                      : cptr(Ly.pool.down.q) + ent * Ly.pool.stride_q + (int64_t)row * (I / 2);
+          }
+          return sc ? cptr(Ly.sh.down.s) + (int64_t)row * 16 : cptr(Ly.sh.down.q) + (int64_t)row * (I / 2);
+        };
+        auto valid = [&](int k) { return k < K ? rt.ent[step * K + k] >= 0 : (lf & LF_SHARED) != 0; };
+        constexpr int pq = kFI / 32;  // pieces of a row
+        dma16(S + p.d_dq + 16 * (k0 * rpc * pq), (k1 - k0) * rpc * pq,
+              [&](int q) {
+                const int k = k0 + q / (rpc * pq), rem = q % (rpc * pq);
+                return qbase(k, rem / pq, false) + 16 * (rem % pq);
+              },
+              [&](int q) { return valid(k0 + q / (rpc * pq)); });
+        dma16(S + p.d_ds + 16 * (k0 * rpc), (k1 - k0) * rpc,
+              [&](int q) { return qbase(k0 + q / rpc, q % rpc, true); },
+              [&](int q) { return valid(k0 + q / rpc); });
+      };
+      if (KX > K) {
+        exp_dma(K, KX);
+        if (lf & LF_LORAD)
+          dma16(S + p.d_bd, rpc * 2,
+                [&](int q) { return cptr(Ly.sh.bd) + ((int64_t)(2 * pb + q / 2) * r) * 2 + 16 * (q % 2); },
+                [](int) { return true; });
+      }
+      const bool routed_known = !(lf & LF_ROUTER);
+      if (routed_known) exp_dma(0, K);
+      dma_drain();
+      fl_st(FL_PRE + slot, step + 1);
+      if (!routed_known) {
+        fl_wait(FL_ROUTE, step + 1, gf);
+        exp_dma(0, K);
+        dma_drain();
+      }
+      fl_st(FL_READY + slot, step + 1);
+    }
+    return;
+  }
+  // fc2 rows of each head
+  const int fb = share_b(E, p.nd, j), fe = share_b(E, p.nd, j + 1);
+  int prev = 0;
+  for (int step = 0; step < nL; ++step) {
+    const int lf = rt.lf[step];
+    if (!(lf & LF_HEAD)) continue;
+    const LayerDev& Ly = a.layers[a.l0 + step];
+    fl_wait_all(FL_HFREED, kFW, prev, gf);
+    const int pr = P / 8;
+    dma16(s_mem + p.d_f2, (fe - fb) * pr,
+          [&](int q) { return cptr(Ly.head.fc2) + ((int64_t)(fb + q / pr) * P) * 2 + 16 * (q % pr); },
+          [](int) { return true; });
+    dma_drain();
+    fl_st(FL_HREADY, step + 1);
+    prev = step + 1;
+  }
+}
+
+// fc2 rows of the head on layer lh (head step hs), after the last layer or
+// in the wait of a later one.
+template <int CPL, int KM>
+__device__ void dn_head_fc2(const FlowArgs& a, int hs, int& phase) {
+  const FlowPlan& p = a.pl;
+  const Dims& dm = a.dm;
+  const int E = dm.E, P = dm.P;
+  const int lh = a.l0 + hs;
+  const int j = blockIdx.x - p.ng;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const uint32_t ep = a.epoch;
+  int32_t* gf = a.flags;
+  uint64_t* X = a.xbuf + (int64_t)lh * p.xlayer;
+  float* ab = lds_at<float>(p.d_ab);
+  xgather_any(X + p.o_xh1, p.ng * kBlk, ep, t, kFC, gf, [&](int wi, uint32_t v) {
+    const int c = wi / kBlk, o = wi % kBlk;
+    const int hb = share_b(p.hrn, p.ng, c), he = share_b(p.hrn, p.ng, c + 1);
+    if (o < he - hb) ab[hb + o] = bitsf(v);
+  });
+  cbar(phase, gf);
+  fl_wait(FL_HREADY, hs + 1, gf);
+  const int fb = share_b(E, p.nd, j), fe = share_b(E, p.nd, j + 1);
+  const uint16_t* f2 = lds_at<uint16_t>(p.d_f2);
+  for (int rr = wave; rr < fe - fb; rr += kFW) {
+    const int e = fb + rr;
+    float acc = 0.0f;
+    if (8 * lane < P) {
+      const uint4 wv = *reinterpret_cast<const uint4*>(f2 + rr * P + 8 * lane);
+      const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+      const float4 a0 = *reinterpret_cast<const float4*>(ab + 8 * lane);
+      const float4 a1 = *reinterpret_cast<const float4*>(ab + 8 * lane + 4);
+      const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc = fmaf(h2f((uint16_t)(ww[q] & 0xFFFF)), av[2 * q], acc);
+        acc = fmaf(h2f((uint16_t)(ww[q] >> 16)), av[2 * q + 1], acc);
+      }
+    }
+    acc = wave_sum_rows(acc);
+    const float logit = acc + ab[P + e];
+    if (lane == 0) {
+      xput(X + p.o_xh2 + j * kBlk + rr, fbits(logit), ep);
+      if (a.head_logits) a.head_logits[(int64_t)lh * E + e] = logit;
+    }
+  }
+  if (wave == 0 && lane >= fe - fb && lane < kBlk) xput(X + p.o_xh2 + j * kBlk + lane, 0u, ep);
+  release(FL_HFREED + wave, hs + 1);
+}
+
+// Ranking of the head on layer lh into the next token's routing of layer lh+1
+// (wave 0 of the designated down CU).
+template <int CPL, int KM>
+__device__ void dn_head_topk(const FlowArgs& a, int lh) {
+  const FlowPlan& p = a.pl;
+  const Dims& dm = a.dm;
+  const int E = dm.E, K = dm.K;
+  const int nxt = (a.token + 1) & 1;
+  const uint32_t ep = a.epoch;
+  int32_t* gf = a.flags;
+  const int lane = threadIdx.x & 63;
+  uint64_t* X = a.xbuf + (int64_t)lh * p.xlayer;
+  float* lg = lds_at<float>(p.d_lg);
+  RouteScratch& rs = *lds_at<RouteScratch>(p.d_rs);
+  xgather_any(X + p.o_xh2, p.nd * kBlk, ep, lane, 64, gf, [&](int wi, uint32_t v) {
+    const int jd = wi / kBlk, o = wi % kBlk;
+    const int fb = share_b(E, p.nd, jd), fe = share_b(E, p.nd, jd + 1);
+    if (o < fe - fb) lg[fb + o] = bitsf(v);
+  });
+  wave_lds_sync();
+  int32_t* pidx = lh + 1 < a.L ? a.route_idx + ((int64_t)nxt * a.L + lh + 1) * K : a.sink_idx;
+  float* pw = lh + 1 < a.L ? a.route_w + ((int64_t)nxt * a.L + lh + 1) * K : a.sink_w;
+  route_wave(dm, lg, a.layers[lh].head.bias, rs, pidx, pw, gf);
+}
+
+template <int CPL, int KM>
+__device__ void dn_compute(const FlowArgs& a) {
+  const FlowPlan& p = a.pl;
+  constexpr int d = 512 * CPL;
+  const Dims& dm = a.dm;
+  const int K = dm.K, E = dm.E, r = dm.r, I = kFI;
+  const int nL = a.l1 - a.l0;
+  const int j = blockIdx.x - p.ng;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int li = t % kGL, grp = t / kGL;
+  const uint32_t ep = a.epoch;
+  int32_t* gf = a.flags;
+  const RT rt = rt_at(p.d_rt, nL, K);
+  const int pb = share_b(d / 2, p.nd, j), pe = share_b(d / 2, p.nd, j + 1);
+  const int npairs = pe - pb, rpc = 2 * npairs;
+  const int KX = p.KX;
+  float* sb = lds_at<float>(p.d_sb);
+  uint16_t* hk = lds_at<uint16_t>(p.d_hk);
+  float* csc = lds_at<float>(p.d_cs);
+  float* pv = lds_at<float>(p.d_pv);
+  float* vv = lds_at<float>(p.d_v);
+  float* coef = lds_at<float>(p.d_co);
+  uint16_t* ho = lds_at<uint16_t>(p.d_ho);
+  float* lg = lds_at<float>(p.d_lg);
+  RouteScratch& rs = *lds_at<RouteScratch>(p.d_rs);
+  int phase = 0;
+
+  if (t < rpc) ho[t] = ldg(a.h + 2 * pb + t);
+
+  for (int step = 0; step < nL; ++step) {
+    const int l = a.l0 + step;
+    const int slot = step & 1;
+    const int lf = rt.lf[step];
+    const unsigned char* S = s_mem + slot * p.d_slot;
+    uint64_t* X = a.xbuf + (int64_t)l * p.xlayer;
+    const LayerDev& Ly = a.layers[l];
+    stamp(a, l, 0);
+
+    // ---- routing of a router layer: ranked here as well -----------------------
+    if (lf & LF_ROUTER) {
+      if (wave == 0) {
+        xgather_any(X + p.o_xr, p.nrc * kBlk, ep, lane, 64, gf, [&](int wi, uint32_t v) {
+          const int c = wi / kBlk, o = wi % kBlk, e = kRouterRows * c + o;
+          if (o < kRouterRows && e < E) lg[e] = bitsf(v);
+        });
+        wave_lds_sync();
+        route_wave(dm, lg, Ly.router_bias, rs, rt.idx + step * K, rt.w + step * K, gf);
+        wave_lds_sync();
+        if (lane < K) rt.ent[step * K + lane] = (int32_t)resolve_entry(Ly.pool, E, rt.idx[step * K + lane]);
+        release(FL_ROUTE, step + 1);
+      }
+    }
+    if (wave == 0 && lane < KX) {
+      float cv = 0.0f;
+      if (lane < K) cv = rt.ent[step * K + lane] >= 0 ? rt.w[step * K + lane] : 0.0f;
+      else cv = (lf & LF_SHARED) ? 1.0f : 0.0f;
+      coef[lane] = cv;
+    }
+
+    // ---- SwiGLU outputs and A_down partials ------------------------------------
+    {
+      const int nitem = p.ng * p.bi;
+      xgather_any(X + p.o_xb, nitem + p.n_sho * p.pbw, ep, t, kFC, gf, [&](int wi, uint32_t v) {
+        if (wi < nitem) {
+          const int c = wi / p.bi, o = wi % p.bi;
+          const int b = share_b(p.items, p.ng, c), e = share_b(p.items, p.ng, c + 1);
+          if (o < e - b) sb[b + o] = bitsf(v);
+        } else {
+          const int o2 = wi - nitem, sh = o2 / p.pbw, q = o2 % p.pbw;
+          if (q < r) pv[sh * r + q] = bitsf(v);
+        }
+      });
+    }
+    cbar(phase, gf);
+    stamp(a, l, 1);
+    // fp16 hi + lo copies (pair-permuted) with a power-of-two scale per 32 elements
+#pragma unroll
+    for (int k = 0; k < KM + 1; ++k) {
+      if (k >= KX) break;
+      const float2 v = *reinterpret_cast<const float2*>(sb + k * I + 32 * grp + 2 * li);
+      const float sc = hilo_pair(v.x, v.y, grp, li, hk + k * 2 * I, I);
+      if (li == 0) csc[k * (I / 32) + grp] = sc;
+    }
+    if (wave == 1 && lane < r) {
+      float s = 0.0f;
+      if (lf & LF_LORAD)
+        for (int sh = 0; sh < p.n_sho; ++sh) s += pv[sh * r + lane];
+      vv[lane] = s;
+    }
+    cbar(phase, gf);
+    stamp(a, l, 2);
+
+    // ---- down rows: every expert slot, down LoRA, residual -----------------------
+    fl_wait(FL_READY + slot, step + 1, gf);
+    if (grp < npairs) {
+      const int rr0 = 2 * grp;
+      float acc0 = 0.0f, acc1 = 0.0f;
+      constexpr int pq = kFI / 32;
+#pragma unroll
+      for (int k = 0; k < KM + 1; ++k) {
+        if (k >= KX) break;
+        const float cf = coef[k];
+        if (cf == 0.0f) continue;  // unresolved expert or no shared expert: uniform
+        f16x2 xh[16], xl[16];
+        load_xchunk(hk + k * 2 * I, li, xh);
+        load_xchunk(hk + k * 2 * I + I, li, xl);
+        const float f = cf * csc[k * (I / 32) + li];
+        const uint4* dq = reinterpret_cast<const uint4*>(S + p.d_dq) + (k * rpc + rr0) * pq;
+        const uint16_t* ds = reinterpret_cast<const uint16_t*>(S + p.d_ds + 16 * (k * rpc + rr0));
+        acc0 = fmaf(f, h2f(ds[li >> 1]) * q4_dot32_hl(dq[li], xh, xl), acc0);
+        acc1 = fmaf(f, h2f(ds[8 + (li >> 1)]) * q4_dot32_hl(dq[pq + li], xh, xl), acc1);
+      }
+      if ((lf & LF_LORAD) && KX > K) {
+        const uint16_t* bd = reinterpret_cast<const uint16_t*>(S + p.d_bd) + rr0 * r;
+        acc0 = fmaf(dm.lora_scale, h2f(bd[li]) * vv[li], acc0);
+        acc1 = fmaf(dm.lora_scale, h2f(bd[r + li]) * vv[li], acc1);
+      }
+      acc0 = group_sum<kGL>(acc0);
+      acc1 = group_sum<kGL>(acc1);
+      if (li == 0) {
+        float a0 = 0.0f, a1 = 0.0f;
+        if (lf & LF_ATTN) {
+          const uint32_t aw = reinterpret_cast<const uint32_t*>(S + p.d_at)[grp];
+          a0 = h2f((uint16_t)(aw & 0xFFFF));
+          a1 = h2f((uint16_t)(aw >> 16));
+        }
+        const uint16_t o0 = f2h((h2f(ho[rr0]) + a0) + acc0);
+        const uint16_t o1 = f2h((h2f(ho[rr0 + 1]) + a1) + acc1);
+        ho[rr0] = o0;
+        ho[rr0 + 1] = o1;
+        const int row = 2 * (pb + grp);
+        *reinterpret_cast<uint32_t*>(a.h + (int64_t)(step + 1) * d + row) = o0 | ((uint32_t)o1 << 16);
+        xput(X + p.o_xa + j * p.ba + grp, o0 | ((uint32_t)o1 << 16), ep);
+      }
+    }
+    if (t >= npairs && t < p.ba) xput(X + p.o_xa + j * p.ba + t, 0u, ep);
+    release(FL_FREED + 4 * slot + wave, step + 1);
+    stamp(a, l, 3);
+
+    // ---- heads in the wait for the next layer ----------------------------------
+    if (step >= 1 && (rt.lf[step - 1] & LF_HEAD)) dn_head_fc2<CPL, KM>(a, step - 1, phase);
+    stamp(a, l, 4);
+    if (step >= 2 && (rt.lf[step - 2] & LF_HEAD) && (l - 2) % p.nd == j && wave == 0)
+      dn_head_topk<CPL, KM>(a, l - 2);
+    stamp(a, l, 5);
+  }
+  if (nL >= 1 && (rt.lf[nL - 1] & LF_HEAD)) dn_head_fc2<CPL, KM>(a, nL - 1, phase);
+  for (int hs = (nL >= 2 ? nL - 2 : 0); hs < nL; ++hs)
+    if ((rt.lf[hs] & LF_HEAD) && (a.l0 + hs) % p.nd == j && wave == 0)
+      dn_head_topk<CPL, KM>(a, a.l0 + hs);
+  stamp(a, a.L, 0);
+}
+
+template <int CPL, int KM>
+__global__ __launch_bounds__(kFThreads) void k_flow(FlowArgs a) {
+  const FlowPlan& p = a.pl;
+  const int K = a.dm.K, E = a.dm.E;
+  const int nL = a.l1 - a.l0;
+  const bool gu = (int)blockIdx.x < p.ng;
+  const int cur = a.token & 1, nxt = (a.token + 1) & 1;
+  const int t = threadIdx.x;
+  if (t < FL_N) s_fl[t] = 0;
+  // routing tables of the launch and per-step layer flags
+  const RT rt = rt_at(gu ? p.g_rt : p.d_rt, nL, K);
+  for (int i = t; i < nL * K; i += kFThreads) {
+    const int l = a.l0 + i / K, k = i % K;
+    const LayerDev& Ly = a.layers[l];
+    const int e = a.route_idx[((int64_t)cur * a.L + l) * K + k];
+    rt.idx[i] = e;
+    rt.w[i] = a.route_w[((int64_t)cur * a.L + l) * K + k];
+    rt.prev[i] = a.token > 0 ? a.exec_idx[((int64_t)nxt * a.L + l) * K + k] : -1;
+    rt.ent[i] = Ly.router ? -1 : (int32_t)resolve_entry(Ly.pool, E, e);
+  }
+  for (int s = t; s < nL; s += kFThreads) {
+    const LayerDev& Ly = a.layers[a.l0 + s];
+    int lf = 0;
+    if (Ly.router) lf |= LF_ROUTER;
+    if (Ly.head.fc1) lf |= LF_HEAD;
+    if (Ly.sh.present) lf |= LF_SHARED;
+    if (Ly.sh.present && Ly.sh.ag) lf |= LF_LORA;
+    if (Ly.sh.present && Ly.sh.ad) lf |= LF_LORAD;
+    if (Ly.attn) lf |= LF_ATTN;
+    rt.lf[s] = lf;
+  }
+  __syncthreads();
+  const int w = t >> 6;
+  if (w >= kFW) {
+    if (gu) gu_loader<CPL, KM>(a, w - kFW);
+    else dn_loader<CPL, KM>(a, w - kFW);
+    dma_drain();
+    return;
+  }
+  if (gu) gu_compute<CPL, KM>(a);
+  else dn_compute<CPL, KM>(a);
+}
+
+template <int CPL, int KM>
+hipError_t launch_flow_t(const FlowArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((k_flow<CPL, KM>), dim3(a.pl.ng + a.pl.nd), dim3(kFThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ plan --
+
+static int rup8(int x) { return (x + 7) & ~7; }
+static int rup16(int x) { return (x + 15) & ~15; }
+static int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+bool flow_supported(const Dims& dm) {
+  if (dm.affine) return false;
+  if (dm.d != 1536 && dm.d != 2048) return false;
+  if (dm.I != kFI || dm.G != 64 || dm.K < 1 || dm.K > 8 || dm.E > 256 || dm.E < dm.K) return false;
+  if (dm.Is != 0 && dm.Is != kFI) return false;
+  if (dm.r != 0 && dm.r != kFRank) return false;
+  if (dm.P < 64 || dm.P > 512 || dm.P % 64) return false;
+  return true;
+}
+
+FlowPlan flow_plan(const Dims& dm, int ng, int nd, int nL) {
+  FlowPlan p{};
+  p.ok = 0;
+  if (!flow_supported(dm) || ng < 1 || nd < 1 || nL < 1 || nL > kFMaxL) return p;
+  const int d = dm.d, K = dm.K, E = dm.E, I = dm.I, r = dm.r, P = dm.P;
+  p.ng = ng;
+  p.nd = nd;
+  p.KX = K + (dm.Is ? 1 : 0);
+  p.items = K * I + dm.Is;
+  p.ipc_max = cdiv(p.items, ng);
+  p.bi = rup8(p.ipc_max);
+  const int KI = K * I;
+  p.cs0 = ng;
+  if (dm.Is) {
+    // first CU whose item range reaches past the routed items
+    const int64_t c1 = ((int64_t)(KI + 1) * ng + p.items - 1) / p.items;
+    p.cs0 = (int)c1 - 1;
+    if (p.cs0 < 0) p.cs0 = 0;
+    while (p.cs0 > 0 && (int64_t)p.items * p.cs0 / ng > KI) --p.cs0;
+    while ((int64_t)p.items * (p.cs0 + 1) / ng <= KI) ++p.cs0;
+  }
+  p.n_sho = dm.Is ? ng - p.cs0 : 0;
+  p.pbw = (dm.Is && r) ? rup8(r) : 0;
+  p.pairs_max = cdiv(d / 2, nd);
+  p.ba = rup8(p.pairs_max);
+  p.nrc = cdiv(E, kRouterRows);
+  p.ca0 = p.nrc;
+  p.hrn = P + E;
+  p.hr_max = cdiv(p.hrn, ng);
+  p.f2_max = cdiv(E, nd);
+  if (p.ipc_max > 2 * kGN || p.pairs_max > kGN || p.hr_max > kBlk || p.f2_max > kBlk) return p;
+  if (ng < p.nrc + 2 * r) return p;
+  // exchange words of a layer (every region starts on a 128-byte line)
+  int o = 0;
+  auto region = [&](int n) {
+    const int at = o;
+    o += (n + 15) & ~15;
+    return at;
+  };
+  p.o_xa = region(nd * p.ba);
+  p.o_xb = region(ng * p.bi + p.n_sho * p.pbw);
+  p.o_xr = region(p.nrc * kBlk);
+  p.o_xl = region(2 * r * kBlk);
+  p.o_xh1 = region(ng * kBlk);
+  p.o_xh2 = region(nd * kBlk);
+  p.xlayer = o;
+  // gate/up CU LDS
+  const int rtb = nL * K * 16 + nL * 4;
+  {
+    const int ipc = p.ipc_max;
+    int s = 0;
+    p.g_at = s; s = rup16(s + d * 2);
+    p.g_gq = s; s = rup16(s + ipc * 2 * (d / 2));
+    p.g_gs = s; s = rup16(s + ipc * 2 * (d / 32));
+    p.g_lb = s; s = rup16(s + ipc * 2 * r * 2);
+    p.g_ad = s; s = rup16(s + r * (ipc / 2 + 2) * 4);
+    p.g_ar = s; s = rup16(s + d * 2);
+    p.g_slot = s;
+    int off = 2 * s;
+    p.g_rb = off; off = rup16(off + kRouterRows * d * 2);
+    p.g_hb = off; off = rup16(off + p.hr_max * d * 2);
+    p.g_hc = off; off = rup16(off + p.hr_max * 2 * K * 4);
+    p.g_h = off; off = rup16(off + d * 2);
+    p.g_xn = off; off = rup16(off + d * 2);
+    p.g_xp = off; off = rup16(off + d * 2);
+    p.g_lg = off; off = rup16(off + E * 4);
+    p.g_rs = off; off = rup16(off + (int)sizeof(RouteScratch));
+    p.g_ax = off; off = rup16(off + kFW * 2 * kFRank * 4);
+    p.g_pp = off; off = rup16(off + kGN * kFRank * 4);
+    p.g_rt = off; off = rup16(off + rtb);
+    p.g_end = off;
+  }
+  // down CU LDS
+  {
+    const int rpc = 2 * p.pairs_max, KX = p.KX;
+    int s = 0;
+    p.d_dq = s; s = rup16(s + KX * rpc * (I / 2));
+    p.d_ds = s; s = rup16(s + KX * rpc * 16);
+    p.d_bd = s; s = rup16(s + rpc * r * 2);
+    p.d_at = s; s = rup16(s + p.pairs_max * 4);
+    p.d_slot = s;
+    int off = 2 * s;
+    p.d_f2 = off; off = rup16(off + p.f2_max * P * 2);
+    p.d_sb = off; off = rup16(off + KX * I * 4);
+    p.d_hk = off; off = rup16(off + KX * 2 * I * 2);
+    p.d_cs = off; off = rup16(off + KX * (I / 32) * 4);
+    p.d_pv = off; off = rup16(off + (p.n_sho > 0 ? p.n_sho : 1) * (r > 0 ? r : 1) * 4);
+    p.d_v = off; off = rup16(off + kFRank * 4);
+    p.d_co = off; off = rup16(off + 16 * 4);
+    p.d_ho = off; off = rup16(off + rpc * 2);
+    p.d_ab = off; off = rup16(off + (P + E) * 4);
+    p.d_lg = off; off = rup16(off + E * 4);
+    p.d_rs = off; off = rup16(off + (int)sizeof(RouteScratch));
+    p.d_rt = off; off = rup16(off + rtb);
+    p.d_end = off;
+  }
+  if (p.g_end > kFlowLds || p.d_end > kFlowLds) return p;
+  p.ok = 1;
+  return p;
+}
+
+// Default split of `grid` CUs: as many down CUs as it takes to give each at
+// most 16 row pairs and a layer slot that fits, the rest gate/up.
+bool flow_default_roles(const Dims& dm, int grid, int nL, int& ng, int& nd) {
+  if (!flow_supported(dm)) return false;
+  const int pairs = dm.d / 2;
+  for (int cand_nd = cdiv(pairs, kGN); cand_nd < grid; ++cand_nd) {
+    const int cand_ng = grid - cand_nd;
+    const FlowPlan p = flow_plan(dm, cand_ng, cand_nd, nL);
+    if (p.ok) {
+      ng = cand_ng;
+      nd = cand_nd;
+      return true;
+    }
+  }
+  return false;
+}
+
+hipError_t launch_flow(const FlowArgs& a, hipStream_t st) {
+  if (!a.pl.ok) return hipErrorInvalidValue;
+  const int cpl = a.dm.d / 512;
+  if (a.dm.K <= 4) {
+    if (cpl == 4) return launch_flow_t<4, 4>(a, st);
+    if (cpl == 3) return launch_flow_t<3, 4>(a, st);
+  } else {
+    if (cpl == 4) return launch_flow_t<4, 8>(a, st);
+    if (cpl == 3) return launch_flow_t<3, 8>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace smd

@@ -168,6 +168,47 @@ bool stack_launchable(const StackArgs& a, int grid);
 int stack_lds_bytes(const Dims& dm, int ng, int n_layers);
 hipError_t launch_stack(const StackArgs& a, int grid, hipStream_t st);
 
+
+// Wave-specialised persistent kernel (flow.hip): gate/up CUs [0, ng) and down
+// CUs [ng, ng + nd), four compute and three loader waves each. The plan holds
+// the work split, the exchange layout of a layer (8-byte words) and the LDS
+// layout of both roles (byte offsets); host and kernel read the same plan.
+constexpr int kFlowLds = 156 * 1024;
+struct FlowPlan {
+  int32_t ok, ng, nd, KX, items, ipc_max, bi, cs0, n_sho, pbw, pairs_max, ba, nrc, ca0, hrn,
+      hr_max, f2_max;
+  int32_t o_xa, o_xb, o_xr, o_xl, o_xh1, o_xh2, xlayer;
+  int32_t g_at, g_gq, g_gs, g_lb, g_ad, g_ar, g_slot, g_rb, g_hb, g_hc, g_h, g_xn, g_xp, g_lg, g_rs,
+      g_ax, g_pp, g_rt, g_end;
+  int32_t d_dq, d_ds, d_bd, d_at, d_slot, d_f2, d_sb, d_hk, d_cs, d_pv, d_v, d_co, d_ho, d_ab, d_lg,
+      d_rs, d_rt, d_end;
+};
+struct FlowArgs {
+  Dims dm;
+  FlowPlan pl;
+  const LayerDev* layers;
+  int32_t L, l0, l1, token;
+  uint32_t epoch;
+  int32_t* route_idx;
+  float* route_w;
+  int32_t* exec_idx;
+  float* exec_w;
+  float* head_logits;
+  uint16_t* x_trace;
+  uint16_t* h;
+  int32_t* sink_idx;
+  float* sink_w;
+  int32_t* flags;
+  uint64_t* xbuf;   // [L][pl.xlayer] exchange words
+  uint64_t* trace;  // optional [grid][L+1][kTracePoints] wall-clock stamps
+};
+bool flow_supported(const Dims& dm);
+// Plan of one launch over nL layers on ng + nd workgroups (ok == 0: does not fit).
+FlowPlan flow_plan(const Dims& dm, int ng, int nd, int nL);
+// Default split of grid workgroups into gate/up and down CUs.
+bool flow_default_roles(const Dims& dm, int grid, int nL, int& ng, int& nd);
+hipError_t launch_flow(const FlowArgs& a, hipStream_t st);
+
 // Staging: device-side slot policy for one layer, then a gather-copy of the
 // missing bundles from (device-mapped) pinned host memory into HBM slots.
 // Cross-layer hot-expert cache (stage.hip): largest cache and layers per call.

@@ -476,33 +476,6 @@ struct LoraRegs {
   uint4 ad[4];
 };
 
-// Lane li of a 16-lane group holds elements 32c + 2li and 32c + 2li + 1 of an
-// I-vector. The group converts chunk c to fp16 hi + lo scaled by a power of
-// two 2^-e chosen from the chunk's max |v|, written pair-permuted to dst (hi
-// at dst[0, I), lo at dst[I, 2I)); returns 2^e. With hsum non-null, lane 0
-// writes there the chunk's sum of hi + lo (for the affine bias terms). All 16
-// lanes must be active.
-__device__ __forceinline__ float hilo_pair(float v0, float v1, int c, int li, uint16_t* dst,
-                                           int I, float* hsum = nullptr) {
-  const float m = group_max<kLG>(fmaxf(fabsf(v0), fabsf(v1)));
-  const int e = hilo_exponent(m);
-  const float inv = ldexpf(1.0f, -e);
-  f16 h0, l0, h1, l1;
-  split_hilo(v0, inv, h0, l0);
-  split_hilo(v1, inv, h1, l1);
-  const int i0 = 32 * c + 2 * li;
-  const int p0 = perm8(i0), p1 = perm8(i0 + 1);
-  dst[p0] = __builtin_bit_cast(uint16_t, h0);
-  dst[p1] = __builtin_bit_cast(uint16_t, h1);
-  dst[I + p0] = __builtin_bit_cast(uint16_t, l0);
-  dst[I + p1] = __builtin_bit_cast(uint16_t, l1);
-  if (hsum) {
-    const float sum = group_sum<kLG>(((float)h0 + (float)l0) + ((float)h1 + (float)l1));
-    if (li == 0) *hsum = sum;
-  }
-  return ldexpf(1.0f, e);
-}
-
 // Loads of a layer issued ahead of its activations: router and LoRA A rows,
 // attention update, and, once the routing is known, gate/up rows (phase A)
 // and down rows with the shared-expert LoRA matrices (phase B).

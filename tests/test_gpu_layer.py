@@ -46,7 +46,7 @@ def _run_and_check(api, orc, tier, roles, seed, T, check_layers, rho=0.5, zero_m
     ctx = api.Context(dm, max_tokens=4)
     model = api.Model(ctx, layers)
     model.set_path({"auto": api.PATH_AUTO, "phases": api.PATH_PHASES,
-                    "persistent": api.PATH_PERSISTENT}[path])
+                    "persistent": api.PATH_PERSISTENT, "flow": api.PATH_FLOW}[path])
     state = api.State(dm, L)
     idx0, w0 = wl.initial_routing(tier, seed, L)
     state.route_idx[0].copy_(torch.from_numpy(idx0))
@@ -79,7 +79,8 @@ def _run_and_check(api, orc, tier, roles, seed, T, check_layers, rho=0.5, zero_m
 
 @pytest.mark.parametrize("tier,T,path", [("tiny", 24, "phases"), ("8b", 5, "phases"),
                                          ("35b", 5, "phases"), ("8b", 5, "persistent"),
-                                         ("35b", 5, "persistent")])
+                                         ("35b", 5, "persistent"), ("8b", 5, "flow"),
+                                         ("35b", 5, "flow")])
 def test_layer_step_two_layers(api, orc, tier, T, path):
     """Layer 0 runs its router and owns a head predicting layer 1; layer 1
     consumes that prediction and owns a head with no consumer."""
@@ -88,7 +89,7 @@ def test_layer_step_two_layers(api, orc, tier, T, path):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("path", ["persistent", "phases"])
+@pytest.mark.parametrize("path", ["flow", "persistent", "phases"])
 def test_layer_step_stack_35b(api, orc, path):
     """Full 35B stack (40 layers, heads on 6-38) in the benchmark's launch
     configuration; every layer-step of the first tokens is checked."""
@@ -98,7 +99,7 @@ def test_layer_step_stack_35b(api, orc, path):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("path", ["persistent", "phases"])
+@pytest.mark.parametrize("path", ["flow", "persistent", "phases"])
 def test_layer_step_stack_8b(api, orc, path):
     roles = synth.stack_roles("8b")
     _run_and_check(api, orc, "8b", roles, seed=5, T=3, check_layers=list(range(24)),
@@ -131,6 +132,40 @@ def _long_stack(api, n_layers, E, seed):
     state.route_idx[0].copy_(torch.from_numpy(idx0))
     state.route_w[0].copy_(torch.from_numpy(w0))
     return dm, roles, layers, keep, state
+
+
+@pytest.mark.timeout(900)
+def test_layer_step_64_layers_flow(api, orc):
+    """The largest launch of the streaming kernel: 64 layers (8B shapes, 32
+    experts), routers on the first and last layer, heads on all but the
+    last; every layer-step of two tokens against the oracle."""
+    import torch
+    from sparse_moe_decode_amd import workloads as wl
+    L, seed = 64, 19
+    dm, roles, layers, keep, state = _long_stack(api, L, 32, seed)
+    ctx = api.Context(dm, max_tokens=1)
+    model = api.Model(ctx, layers)
+    model.set_path(api.PATH_FLOW)
+    toks = wl.token_inputs("8b", seed, 2, 0.5)
+    checker = StackChecker(orc, "8b", seed, roles, list(range(L)), keep, zero_mean=True, dims=dm)
+    prev_exec = None
+    h = torch.empty((L + 1, dm["d"]), dtype=torch.float16, device="cuda")
+    for t in range(2):
+        announce("layer_step", "8b", "flow", f"L={L}", f"token {t}")
+        h[0].copy_(torch.from_numpy(toks[t]))
+        api.layer_step(ctx, model, 0, L, state, t, h)
+        assert api.device_status(ctx) == 0
+        cur, nxt = t & 1, (t + 1) & 1
+        exec_idx = host(state.exec_idx[cur]).copy()
+        checker.check(t, host(h).copy(), host(state.x_trace).copy(), exec_idx,
+                      host(state.exec_w[cur]).copy(), prev_exec, host(state.route_idx[cur]).copy(),
+                      host(state.route_w[cur]).copy(), host(state.route_idx[nxt]).copy(),
+                      host(state.route_w[nxt]).copy(), host(state.head_logits).copy())
+        prev_exec = exec_idx
+    print(f"8b E=32 flow L={L}: {checker.steps} layer-steps checked, worst error ratio "
+          f"{checker.worst:.3f}")
+    model.close()
+    ctx.close()
 
 
 @pytest.mark.timeout(900)
