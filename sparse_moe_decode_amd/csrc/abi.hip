@@ -606,7 +606,10 @@ int layer_step(e0_ctx* ctx, e0_model* model, int32_t layer_begin, int32_t layer_
   if (model->trace && model->grid > model->trace_grid)
     return fail(E0_ERR_ARG, "layer_step: the trace buffer is sized for a smaller grid");
   const int nL = layer_end - layer_begin;
-  if ((model->path == E0_PATH_AUTO || model->path == E0_PATH_FLOW) && model->dev_table) {
+  // The streaming kernel, when the layer range fits it: sets `launched`.
+  auto run_flow = [&](bool& launched) -> int {
+    launched = false;
+    if (!model->dev_table) return E0_OK;
     int ng = 0, nd = 0;
     FlowArgs a;
     bool ok = flow_roles(model, nL, ng, nd);
@@ -614,33 +617,37 @@ int layer_step(e0_ctx* ctx, e0_model* model, int32_t layer_begin, int32_t layer_
       a.pl = flow_plan(dm, ng, nd, nL);
       ok = a.pl.ok && (int64_t)L * a.pl.xlayer <= model->fxwords;
     }
-    if (ok) {
-      a.dm = dm;
-      a.layers = model->dev_table;
-      a.L = L;
-      a.l0 = layer_begin;
-      a.l1 = layer_end;
-      a.token = token;
-      a.epoch = ++model->epoch;
-      if (a.epoch == 0) a.epoch = ++model->epoch;  // 0 marks never-written words
-      a.route_idx = state->route_idx;
-      a.route_w = state->route_w;
-      a.exec_idx = state->exec_idx;
-      a.exec_w = state->exec_w;
-      a.head_logits = state->head_logits;
-      a.x_trace = state->x_trace;
-      a.h = h;
-      a.sink_idx = s.sink_idx;
-      a.sink_w = s.sink_w;
-      a.flags = s.flags;
-      a.xbuf = model->fxbuf;
-      a.trace = model->trace;
-      hipError_t e = launch_flow(a, st);
-      if (e != hipSuccess) return hip_fail(e, "layer_step (streaming kernel)");
-      return E0_OK;
-    }
-    if (model->path == E0_PATH_FLOW)
-      return fail(E0_ERR_SHAPE, "layer_step: this layer range does not fit the streaming kernel");
+    if (!ok) return E0_OK;
+    a.dm = dm;
+    a.layers = model->dev_table;
+    a.L = L;
+    a.l0 = layer_begin;
+    a.l1 = layer_end;
+    a.token = token;
+    a.epoch = ++model->epoch;
+    if (a.epoch == 0) a.epoch = ++model->epoch;  // 0 marks never-written words
+    a.route_idx = state->route_idx;
+    a.route_w = state->route_w;
+    a.exec_idx = state->exec_idx;
+    a.exec_w = state->exec_w;
+    a.head_logits = state->head_logits;
+    a.x_trace = state->x_trace;
+    a.h = h;
+    a.sink_idx = s.sink_idx;
+    a.sink_w = s.sink_w;
+    a.flags = s.flags;
+    a.xbuf = model->fxbuf;
+    a.trace = model->trace;
+    launched = true;
+    hipError_t e = launch_flow(a, st);
+    if (e != hipSuccess) return hip_fail(e, "layer_step (streaming kernel)");
+    return E0_OK;
+  };
+  if (model->path == E0_PATH_FLOW) {
+    bool launched;
+    const int rc = run_flow(launched);
+    if (!launched) return fail(E0_ERR_SHAPE, "layer_step: this layer range does not fit the streaming kernel");
+    return rc;
   }
   if (model->path != E0_PATH_PHASES && model->dev_table) {
     StackArgs a;
@@ -679,6 +686,11 @@ int layer_step(e0_ctx* ctx, e0_model* model, int32_t layer_begin, int32_t layer_
     }
     if (model->path == E0_PATH_PERSISTENT)
       return fail(E0_ERR_SHAPE, "layer_step: this layer range does not fit the persistent kernel");
+  }
+  if (model->path == E0_PATH_AUTO) {
+    bool launched;
+    const int rc = run_flow(launched);
+    if (launched) return rc;
   }
   for (int l = layer_begin; l < layer_end; ++l) {
     const e0_layer& Ly = model->layers[l];

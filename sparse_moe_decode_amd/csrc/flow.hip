@@ -208,11 +208,7 @@ __device__ __forceinline__ void xgather(const uint64_t* base, int n, uint32_t ep
 template <typename Sink>
 __device__ __forceinline__ void xgather_any(const uint64_t* base, int n, uint32_t ep, int tid,
                                             int nthr, int32_t* gflags, Sink&& sink) {
-  const int per = (n / 2 + nthr - 1) / nthr;  // pairs per thread
-  if (per <= 2) xgather<2>(base, n, ep, tid, nthr, gflags, sink);
-  else if (per <= 4) xgather<4>(base, n, ep, tid, nthr, gflags, sink);
-  else if (per <= 8) xgather<8>(base, n, ep, tid, nthr, gflags, sink);
-  else xgather<16>(base, n, ep, tid, nthr, gflags, sink);
+  xgather<8>(base, n, ep, tid, nthr, gflags, sink);
 }
 
 // Loader: npieces 16-byte pieces into LDS dst (piece q at dst + 16 q) from
@@ -240,12 +236,37 @@ __device__ __forceinline__ void dma4(unsigned char* dst, int npieces, Addr&& add
 
 __device__ __forceinline__ const char* cptr(const void* p) { return (const char*)p; }
 
-// Contiguous share [beg, end) of n items for part c of G.
-__device__ __forceinline__ int share_b(int n, int G, int c) {
-  return (int)((int64_t)n * c / G);
+// The launch's arguments, read in place from the kernel-argument segment
+// with scalar loads. The role functions below are separate functions: a
+// reference parameter would make the compiler copy the arguments to scratch,
+// and the segment pointer is only defined in the kernel itself, so the
+// kernel passes its address and the callee makes it wave-uniform again.
+typedef const __attribute__((address_space(4))) FlowArgs KA;
+typedef const __attribute__((address_space(4))) FlowPlan KP;
+typedef const __attribute__((address_space(4))) Dims KD;
+__device__ __forceinline__ KA& args_at(uint64_t p) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
+  return *(KA*)((((uint64_t)hi) << 32) | lo);
+}
+// A private copy of the dimensions (for helpers taking an ordinary reference).
+__device__ __forceinline__ Dims dims_of(KD& k) {
+  Dims d;
+  d.d = k.d; d.E = k.E; d.K = k.K; d.I = k.I; d.Is = k.Is; d.P = k.P; d.G = k.G; d.r = k.r;
+  d.lora_scale = k.lora_scale;
+  d.router_kind = k.router_kind; d.norm_topk = k.norm_topk; d.n_groups = k.n_groups;
+  d.topk_groups = k.topk_groups;
+  d.route_scale = k.route_scale; d.eps = k.eps;
+  d.affine = k.affine;
+  return d;
 }
 
-__device__ __forceinline__ void stamp(const FlowArgs& a, int row, int k) {
+// Contiguous share [beg, end) of n items for part c of G.
+__device__ __forceinline__ int share_b(int n, int G, int c) {
+  return (int)((uint32_t)n * (uint32_t)c / (uint32_t)G);  // n * c < 2^32
+}
+
+__device__ __forceinline__ void stamp(KA& a, int row, int k) {
   if (a.trace && threadIdx.x == 0)
     a.trace[((int64_t)blockIdx.x * (a.L + 1) + row) * kTracePoints + k] = wall_clock64();
 }
@@ -263,22 +284,33 @@ __device__ __forceinline__ T* lds_at(int off) {
   return reinterpret_cast<T*>(s_mem + off);
 }
 
-// Routing tables of the launch in LDS: [nL][K] each.
+// Routing tables of the launch in LDS ([nL][K] each), per-step layer flags,
+// and the work split: first routed item of routed CU c (ibr[c], c <= ngr),
+// first shared row of shared CU c (ibs[c], c <= ng - ngr), first row pair of
+// down CU j (pb[j], j <= nd), first head row of gate/up CU c (hb[c],
+// c <= ng), first fc2 row of down CU j (fb[j]).
 struct RT {
   int32_t* idx;
   float* w;
   int32_t* prev;
   int32_t* ent;
   int32_t* lf;
+  int32_t *ibr, *ibs, *pb, *hb, *fb;
 };
 
-__device__ __forceinline__ RT rt_at(int off, int nL, int K) {
+template <typename P>
+__device__ __forceinline__ RT rt_at(int off, int nL, int K, P& p) {
   RT t;
   t.idx = lds_at<int32_t>(off);
   t.w = lds_at<float>(off + nL * K * 4);
   t.prev = lds_at<int32_t>(off + 2 * nL * K * 4);
   t.ent = lds_at<int32_t>(off + 3 * nL * K * 4);
   t.lf = lds_at<int32_t>(off + 4 * nL * K * 4);
+  t.ibr = t.lf + nL;
+  t.ibs = t.ibr + p.ngr + 1;
+  t.pb = t.ibs + (p.ng - p.ngr) + 1;
+  t.hb = t.pb + p.nd + 1;
+  t.fb = t.hb + p.ng + 1;
   return t;
 }
 
@@ -287,39 +319,72 @@ __device__ __forceinline__ RT rt_at(int off, int nL, int K) {
 template <int CPL>
 __device__ __forceinline__ float wave_row_dot(const uint16_t* row, const uint16_t* x) {
   const int lane = threadIdx.x & 63;
-  float acc = 0.0f;
+  float pm[CPL];
 #pragma unroll
   for (int m = 0; m < CPL; ++m) {
     const int c = lane + 64 * m;
-    acc = dot8_h(*reinterpret_cast<const uint4*>(row + 8 * c),
-                 *reinterpret_cast<const uint4*>(x + 8 * c), acc);
+    pm[m] = dot8_h(*reinterpret_cast<const uint4*>(row + 8 * c),
+                   *reinterpret_cast<const uint4*>(x + 8 * c), 0.0f);
   }
+  float acc = 0.0f;
+#pragma unroll
+  for (int m = 0; m < CPL; ++m) acc += pm[m];
   return acc;
+}
+
+// fp16 bits of v, saturated to the largest finite fp16 (NaN stays NaN).
+__device__ __forceinline__ uint16_t f2h_sat(float v) {
+  return f2h(v == v ? fminf(fmaxf(v, -65504.0f), 65504.0f) : v);
+}
+
+// Loader waves stamp trace points from their first lane.
+__device__ __forceinline__ void lstamp(KA& a, int row, int k) {
+  if (a.trace && (threadIdx.x & 63) == 0)
+    a.trace[((int64_t)blockIdx.x * (a.L + 1) + row) * kTracePoints + k] = wall_clock64();
+}
+
+// Item range of gate/up CU cu: routed CUs own routed items (global index
+// it = k*I + row), shared CUs rows of the shared expert.
+struct Items {
+  bool shared;
+  int b, e;  // routed: item indices; shared: shared-expert rows
+};
+
+template <typename P>
+__device__ __forceinline__ Items items_of(const RT& rt, P& p, int cu) {
+  Items r;
+  r.shared = cu >= p.ngr;
+  if (r.shared) {
+    r.b = rt.ibs[cu - p.ngr];
+    r.e = rt.ibs[cu - p.ngr + 1];
+  } else {
+    r.b = rt.ibr[cu];
+    r.e = rt.ibr[cu + 1];
+  }
+  return r;
 }
 
 // ============================================================ gate/up CUs ==
 
 template <int CPL, int KM>
-__device__ void gu_loader(const FlowArgs& a, int lw) {
-  const FlowPlan& p = a.pl;
+__device__ __attribute__((noinline)) void gu_loader(uint64_t kap, int lw) {
+  KA& a = args_at(kap);
+  KP& p = a.pl;
   constexpr int d = 512 * CPL;
   const int K = a.dm.K, E = a.dm.E, r = a.dm.r, I = kFI;
   const int nL = a.l1 - a.l0;
   const int cu = blockIdx.x;
-  const RT rt = rt_at(p.g_rt, nL, K);
-  const int ib = share_b(p.items, p.ng, cu), ie = share_b(p.items, p.ng, cu + 1);
-  const int ipc = ie - ib;
-  const int KI = K * I;
-  const int js0 = ib >= KI ? 0 : (ie > KI ? KI - ib : ipc);  // first shared item (local)
+  const RT rt = rt_at(p.g_rt, nL, K, p);
+  const Items it = items_of(rt, p, cu);
+  const int ipc = it.e - it.b;
   const int aq = (cu >= p.ca0 && cu < p.ca0 + 2 * r) ? cu - p.ca0 : -1;
-  const int srow0 = (ib > KI ? ib : KI) - KI, srow1 = ie - KI;
-  const int adw = js0 < ipc ? ((srow1 + 1) >> 1) - (srow0 >> 1) : 0;
   int32_t* gf = a.flags;
   if (lw < 2) {
     for (int step = lw; step < nL; step += 2) {
       const int slot = lw;
       const int l = a.l0 + step;
       if (step >= 2) fl_wait_all(FL_FREED + 4 * slot, kFW, step - 1, gf);
+      lstamp(a, l, 10 + slot);
       const LayerDev& Ly = a.layers[l];
       const int lf = rt.lf[step];
       unsigned char* S = s_mem + slot * p.g_slot;
@@ -332,69 +397,54 @@ __device__ void gu_loader(const FlowArgs& a, int lw) {
       }
       // items: gate/up rows (d/32 pieces each), then their scales (d/512 each)
       const int pr = d / 32, ps = d / 512;
-      auto item_dma = [&](int j0, int j1) {
-        if (j1 <= j0) return;
+      auto item_dma = [&]() {
         auto base = [&](int jj, int pj, bool sc) -> const char* {
-          const int it = ib + jj;
-          const int k = it / I, row = it % I;
-          if (k < K) {
-            const int ent = rt.ent[step * K + k];
-            const Q4& q4 = pj ? Ly.pool.up : Ly.pool.gate;
-            return sc ? cptr(q4.s) + ent * Ly.pool.stride_s + (int64_t)row * (d / 32)
-                      : cptr(q4.q) + ent * Ly.pool.stride_q + (int64_t)row * (d / 2);
+          if (it.shared) {
+            const int row = it.b + jj;
+            const Q4& q4 = pj ? Ly.sh.up : Ly.sh.gate;
+            return sc ? cptr(q4.s) + (int64_t)row * (d / 32) : cptr(q4.q) + (int64_t)row * (d / 2);
           }
-          const Q4& q4 = pj ? Ly.sh.up : Ly.sh.gate;
-          return sc ? cptr(q4.s) + (int64_t)row * (d / 32) : cptr(q4.q) + (int64_t)row * (d / 2);
+          const int gi = it.b + jj, k = gi / I, row = gi % I;
+          const int ent = rt.ent[step * K + k];
+          const Q4& q4 = pj ? Ly.pool.up : Ly.pool.gate;
+          return sc ? cptr(q4.s) + ent * Ly.pool.stride_s + (int64_t)row * (d / 32)
+                    : cptr(q4.q) + ent * Ly.pool.stride_q + (int64_t)row * (d / 2);
         };
         auto valid = [&](int jj) {
-          const int k = (ib + jj) / I;
-          return k < K ? rt.ent[step * K + k] >= 0 : (lf & LF_SHARED) != 0;
+          return it.shared ? (lf & LF_SHARED) != 0 : rt.ent[step * K + (it.b + jj) / I] >= 0;
         };
-        dma16(S + p.g_gq + 16 * (j0 * 2 * pr), (j1 - j0) * 2 * pr,
+        dma16(S + p.g_gq, ipc * 2 * pr,
               [&](int q) {
-                const int jj = j0 + q / (2 * pr), rem = q % (2 * pr);
+                const int jj = q / (2 * pr), rem = q % (2 * pr);
                 return base(jj, rem / pr, false) + 16 * (rem % pr);
               },
-              [&](int q) { return valid(j0 + q / (2 * pr)); });
-        dma16(S + p.g_gs + 16 * (j0 * 2 * ps), (j1 - j0) * 2 * ps,
+              [&](int q) { return valid(q / (2 * pr)); });
+        dma16(S + p.g_gs, ipc * 2 * ps,
               [&](int q) {
-                const int jj = j0 + q / (2 * ps), rem = q % (2 * ps);
+                const int jj = q / (2 * ps), rem = q % (2 * ps);
                 return base(jj, rem / ps, true) + 16 * (rem % ps);
               },
-              [&](int q) { return valid(j0 + q / (2 * ps)); });
+              [&](int q) { return valid(q / (2 * ps)); });
       };
-      if (js0 < ipc && (lf & LF_SHARED)) {
-        item_dma(js0, ipc);
-        if (lf & LF_LORA)  // LoRA B rows of gate and up (r fp16 = 2 pieces each)
-          dma16(S + p.g_lb + 16 * (js0 * 4), (ipc - js0) * 4,
-                [&](int q) {
-                  const int jj = js0 + q / 4, pj = (q / 2) % 2, row = ib + jj - KI;
-                  return cptr(pj ? Ly.sh.bu : Ly.sh.bg) + (int64_t)row * r * 2 + 16 * (q % 2);
-                },
-                [](int) { return true; });
-        if (lf & LF_LORAD)  // A_down columns of the CU's shared rows, as 4-byte words
-          dma4(S + p.g_ad, r * adw, [&](int q) {
-            const int t = q / adw, w = q % adw;
-            return cptr(Ly.sh.ad) + ((int64_t)t * a.dm.Is + (srow0 & ~1) + 2 * w) * 2;
-          });
-      }
-      const bool routed_known = !(lf & LF_ROUTER);
-      if (routed_known) item_dma(0, js0);
+      const bool known = it.shared || !(lf & LF_ROUTER);
+      if (known) item_dma();
       dma_drain();
       fl_st(FL_PRE + slot, step + 1);
-      if (!routed_known && js0 > 0) {
+      if (!known) {
         fl_wait(FL_ROUTE, step + 1, gf);
-        item_dma(0, js0);
+        lstamp(a, l, 12);
+        item_dma();
         dma_drain();
       }
       fl_st(FL_READY + slot, step + 1);
+      lstamp(a, l, 13);
     }
     return;
   }
   // router rows and head rows
   const bool rcu = cu < p.nrc;
   const int r0 = kRouterRows * cu, r1 = min(r0 + kRouterRows, E);
-  const int hb = share_b(p.hrn, p.ng, cu), he = share_b(p.hrn, p.ng, cu + 1);
+  const int hb = rt.hb[cu], he = rt.hb[cu + 1];
   const int P = a.dm.P, F = d + 2 * E;
   int prev_r = 0, prev_h = 0;
   for (int step = 0; step < nL; ++step) {
@@ -435,10 +485,11 @@ __device__ void gu_loader(const FlowArgs& a, int lw) {
 }
 
 template <int CPL, int KM>
-__device__ void gu_compute(const FlowArgs& a) {
-  const FlowPlan& p = a.pl;
+__device__ __attribute__((noinline)) void gu_compute(uint64_t kap) {
+  KA& a = args_at(kap);
+  KP& p = a.pl;
   constexpr int d = 512 * CPL;
-  const Dims& dm = a.dm;
+  const Dims dm = dims_of(a.dm);
   const int K = dm.K, E = dm.E, r = dm.r, I = kFI, P = dm.P;
   const int nL = a.l1 - a.l0;
   const int cu = blockIdx.x;
@@ -447,24 +498,19 @@ __device__ void gu_compute(const FlowArgs& a) {
   const uint32_t ep = a.epoch;
   const int cur = a.token & 1;
   int32_t* gf = a.flags;
-  const RT rt = rt_at(p.g_rt, nL, K);
-  const int ib = share_b(p.items, p.ng, cu), ie = share_b(p.items, p.ng, cu + 1);
-  const int ipc = ie - ib;
-  const int KI = K * I;
-  const int js0 = ib >= KI ? 0 : (ie > KI ? KI - ib : ipc);
+  const RT rt = rt_at(p.g_rt, nL, K, p);
+  const Items it = items_of(rt, p, cu);
+  const int ipc = it.e - it.b;
   const int aq = (cu >= p.ca0 && cu < p.ca0 + 2 * r) ? cu - p.ca0 : -1;
-  const int srow0 = (ib > KI ? ib : KI) - KI, srow1 = ie - KI;
-  const int adw = js0 < ipc ? ((srow1 + 1) >> 1) - (srow0 >> 1) : 0;
   const bool rcu = cu < p.nrc;
   const int r0 = kRouterRows * cu, r1 = min(r0 + kRouterRows, E);
-  const int hb = share_b(p.hrn, p.ng, cu), he = share_b(p.hrn, p.ng, cu + 1);
+  const int hb = rt.hb[cu], he = rt.hb[cu + 1];
+  const int bir = 1 << p.lbr, hs = 1 << p.lhs;
   uint16_t* hbuf = lds_at<uint16_t>(p.g_h);
   uint16_t* xn = lds_at<uint16_t>(p.g_xn);
   uint16_t* xp = lds_at<uint16_t>(p.g_xp);
   float* lg = lds_at<float>(p.g_lg);
   RouteScratch& rs = *lds_at<RouteScratch>(p.g_rs);
-  float* axw = lds_at<float>(p.g_ax) + wave * 2 * kFRank;
-  float* pp = lds_at<float>(p.g_pp);
   int phase = 0;
 
   for (int step = 0; step < nL; ++step) {
@@ -473,6 +519,7 @@ __device__ void gu_compute(const FlowArgs& a) {
     const int lf = rt.lf[step];
     const unsigned char* S = s_mem + slot * p.g_slot;
     uint64_t* X = a.xbuf + (int64_t)l * p.xlayer;
+    uint64_t* XB = X + p.o_xb;
     const LayerDev& Ly = a.layers[l];
     stamp(a, l, 0);
     fl_wait(FL_PRE + slot, step + 1, gf);
@@ -484,10 +531,11 @@ __device__ void gu_compute(const FlowArgs& a) {
     } else {
       const uint64_t* XA = a.xbuf + (int64_t)(l - 1) * p.xlayer + p.o_xa;
       uint32_t* h32 = reinterpret_cast<uint32_t*>(hbuf);
-      xgather_any(XA, p.nd * p.ba, ep, t, kFC, gf, [&](int wi, uint32_t v) {
-        const int jd = wi / p.ba, o = wi % p.ba;
-        const int pb = share_b(d / 2, p.nd, jd), pe = share_b(d / 2, p.nd, jd + 1);
-        if (o < pe - pb) h32[pb + o] = v;
+      const int lba = p.lba;
+      xgather_any(XA, p.nd << lba, ep, t, kFC, gf, [&](int wi, uint32_t v) {
+        const int jd = wi >> lba, o = wi & ((1 << lba) - 1);
+        const int pb = rt.pb[jd];
+        if (o < rt.pb[jd + 1] - pb) h32[pb + o] = v;
       });
     }
     cbar(phase, gf);
@@ -497,7 +545,7 @@ __device__ void gu_compute(const FlowArgs& a) {
     {
       const uint16_t* at = reinterpret_cast<const uint16_t*>(S + p.g_at);
       const bool att = (lf & LF_ATTN) != 0;
-      float ss = 0.0f;
+      float ssq[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int m = 0; m < CPL; ++m) {
         const int c = lane + 64 * m;
@@ -508,11 +556,11 @@ __device__ void gu_compute(const FlowArgs& a) {
         for (int q = 0; q < 4; ++q) {
           const float v0 = h2f((uint16_t)(hw[q] & 0xFFFF)) + h2f((uint16_t)(aw[q] & 0xFFFF));
           const float v1 = h2f((uint16_t)(hw[q] >> 16)) + h2f((uint16_t)(aw[q] >> 16));
-          ss = fmaf(v0, v0, ss);
-          ss = fmaf(v1, v1, ss);
+          ssq[q] = fmaf(v0, v0, ssq[q]);
+          ssq[q] = fmaf(v1, v1, ssq[q]);
         }
       }
-      const float tot = wave_sum_rows(ss);
+      const float tot = wave_sum_rows((ssq[0] + ssq[1]) + (ssq[2] + ssq[3]));
       const float inv = 1.0f / sqrtf(tot / d + dm.eps);
       if (t < d / 8) {
         const uint4 hv = *reinterpret_cast<const uint4*>(hbuf + 8 * t);
@@ -536,11 +584,11 @@ __device__ void gu_compute(const FlowArgs& a) {
     cbar(phase, gf);
     stamp(a, l, 2);
 
-    // ---- LoRA A row (shared gate/up) and router rows --------------------------
+    // ---- LoRA A row of the shared gate/up, router rows --------------------------
     if (aq >= 0 && wave == 0) {
       float v = 0.0f;
       if (lf & LF_LORA) v = wave_sum_rows(wave_row_dot<CPL>(reinterpret_cast<const uint16_t*>(S + p.g_ar), xn));
-      if (lane < kBlk) xput(X + p.o_xl + aq * kBlk + lane, lane == 0 ? fbits(v) : 0u, ep);
+      if (lane < kBlk) xput(XB + p.xb_a + aq * kBlk + lane, lane == 0 ? fbits(v) : 0u, ep);
     }
     if ((lf & LF_ROUTER) && rcu) {
       fl_wait(FL_RREADY, step + 1, gf);
@@ -557,7 +605,7 @@ __device__ void gu_compute(const FlowArgs& a) {
     if (lf & LF_ROUTER) {
       if (wave == 0) {
         xgather_any(X + p.o_xr, p.nrc * kBlk, ep, lane, 64, gf, [&](int wi, uint32_t v) {
-          const int c = wi / kBlk, o = wi % kBlk, e = kRouterRows * c + o;
+          const int c = wi >> 3, o = wi & 7, e = kRouterRows * c + o;
           if (o < kRouterRows && e < E) lg[e] = bitsf(v);
         });
         wave_lds_sync();
@@ -583,76 +631,62 @@ __device__ void gu_compute(const FlowArgs& a) {
 
     // ---- gate/up items ---------------------------------------------------------
     fl_wait(FL_READY + slot, step + 1, gf);
+    stamp(a, l, 6);
     {
       // the lane's activation chunks li + 16 m (pair-permuted fp16)
       f16x2 xr[CPL][16];
 #pragma unroll
       for (int m = 0; m < CPL; ++m) load_xchunk(xp, li + kGL * m, xr[m]);
-      // LoRA A products for shared items, gathered once per wave
-      // does any group of this wave own a shared item? (wave-uniform)
-      const bool mine_sh = (grp >= js0 && grp < ipc) || (grp + kGN >= js0 && grp + kGN < ipc);
-      const bool wave_sh = (lf & LF_SHARED) && (lf & LF_LORA) && __ballot(mine_sh) != 0;
-      if (wave_sh) {
-        xgather_any(X + p.o_xl, 2 * r * kBlk, ep, lane, 64, gf, [&](int wi, uint32_t v) {
-          if (wi % kBlk == 0) axw[wi / kBlk] = bitsf(v);
-        });
-        wave_lds_sync();
-      }
-      float pacc = 0.0f;  // A_down partial of rank li over this group's shared items
-      const float lc = dm.lora_scale;
+      stamp(a, l, 7);
 #pragma unroll
       for (int j2 = 0; j2 < 2; ++j2) {
         const int jj = grp + kGN * j2;
-        if (jj >= ipc) continue;  // uniform over the group
-        const int it = ib + jj;
-        const int k = it / I, row = it % I;
-        const bool shared = k >= K;
-        const bool ok = shared ? (lf & LF_SHARED) != 0 : rt.ent[step * K + k] >= 0;
+        bool ok = jj < ipc;  // uniform over the group
+        if (ok) ok = it.shared ? (lf & LF_SHARED) != 0 : rt.ent[step * K + (it.b + jj) / I] >= 0;
         float ag = 0.0f, au = 0.0f;
         if (ok) {
           const uint4* gq = reinterpret_cast<const uint4*>(S + p.g_gq + (2 * jj) * (d / 2));
           const uint4* uq = reinterpret_cast<const uint4*>(S + p.g_gq + (2 * jj + 1) * (d / 2));
           const uint16_t* gs = reinterpret_cast<const uint16_t*>(S + p.g_gs + (2 * jj) * (d / 32));
           const uint16_t* us = reinterpret_cast<const uint16_t*>(S + p.g_gs + (2 * jj + 1) * (d / 32));
+          float pg[CPL], pu[CPL];
 #pragma unroll
           for (int m = 0; m < CPL; ++m) {
             const int c = li + kGL * m;
-            ag += h2f(gs[c >> 1]) * q4_dot32(gq[c], xr[m]);
-            au += h2f(us[c >> 1]) * q4_dot32(uq[c], xr[m]);
+            pg[m] = h2f(gs[c >> 1]) * q4_dot32_ilp(gq[c], xr[m]);
+            pu[m] = h2f(us[c >> 1]) * q4_dot32_ilp(uq[c], xr[m]);
+          }
+#pragma unroll
+          for (int m = 0; m < CPL; ++m) {
+            ag += pg[m];
+            au += pu[m];
           }
         }
         ag = group_sum<kGL>(ag);
         au = group_sum<kGL>(au);
-        float out = 0.0f;
-        if (ok) {
-          if (shared && (lf & LF_LORA)) {
-            const uint16_t* bg = reinterpret_cast<const uint16_t*>(S + p.g_lb) + (2 * jj) * r;
-            const uint16_t* bu = bg + r;
-            ag = fmaf(lc, group_sum<kGL>(h2f(bg[li]) * axw[li]), ag);
-            au = fmaf(lc, group_sum<kGL>(h2f(bu[li]) * axw[r + li]), au);
+        if (li == 0 && jj < ipc) {
+          if (it.shared) {
+            // the shared expert's sums go out as they are: the down CUs add
+            // the LoRA terms and take the SwiGLU
+            const int cs = cu - p.ngr;
+            xput(XB + p.xb_s + (cs << (p.lhs + 1)) + jj, fbits(ag), ep);
+            xput(XB + p.xb_s + (cs << (p.lhs + 1)) + hs + jj, fbits(au), ep);
+          } else {
+            xput(XB + (cu << p.lbr) + jj, fbits(ok ? silu(ag) * au : 0.0f), ep);
           }
-          out = silu(ag) * au;
         }
-        if (shared && (lf & LF_LORAD)) {
-          const int srow = row, wdx = (srow >> 1) - (srow0 >> 1);
-          const uint16_t* adc = reinterpret_cast<const uint16_t*>(S + p.g_ad);
-          pacc = fmaf(h2f(adc[2 * (li * adw + wdx) + (srow & 1)]), out, pacc);
-        }
-        if (li == 0) xput(X + p.o_xb + cu * p.bi + jj, fbits(out), ep);
       }
-      if (t >= ipc && t < p.bi) xput(X + p.o_xb + cu * p.bi + t, 0u, ep);
+      stamp(a, l, 8);
+      if (it.shared) {
+        const int cs = cu - p.ngr;
+        if (t >= ipc && t < hs) {
+          xput(XB + p.xb_s + (cs << (p.lhs + 1)) + t, 0u, ep);
+          xput(XB + p.xb_s + (cs << (p.lhs + 1)) + hs + t, 0u, ep);
+        }
+      } else if (t >= ipc && t < bir) {
+        xput(XB + (cu << p.lbr) + t, 0u, ep);
+      }
       release(FL_FREED + 4 * slot + wave, step + 1);
-      // A_down partial of the CU's shared rows: one block per shared-owner CU
-      if (js0 < ipc && p.pbw) {
-        pp[grp * kFRank + li] = pacc;
-        cbar(phase, gf);
-        if (wave == 0 && lane < p.pbw) {
-          float v = 0.0f;
-          if (lane < r)
-            for (int g = 0; g < kGN; ++g) v += pp[g * kFRank + lane];
-          xput(X + p.o_xb + p.ng * p.bi + (cu - p.cs0) * p.pbw + lane, fbits(v), ep);
-        }
-      }
     }
     stamp(a, l, 4);
 
@@ -684,14 +718,15 @@ __device__ void gu_compute(const FlowArgs& a) {
 // ============================================================== down CUs ==
 
 template <int CPL, int KM>
-__device__ void dn_loader(const FlowArgs& a, int lw) {
-  const FlowPlan& p = a.pl;
-  constexpr int d = 512 * CPL;
-  const int K = a.dm.K, E = a.dm.E, r = a.dm.r, I = kFI, P = a.dm.P;
+__device__ __attribute__((noinline)) void dn_loader(uint64_t kap, int lw) {
+  KA& a = args_at(kap);
+  KP& p = a.pl;
+  (void)CPL;
+  const int K = a.dm.K, r = a.dm.r, I = kFI, P = a.dm.P;
   const int nL = a.l1 - a.l0;
   const int j = blockIdx.x - p.ng;
-  const RT rt = rt_at(p.d_rt, nL, K);
-  const int pb = share_b(d / 2, p.nd, j), pe = share_b(d / 2, p.nd, j + 1);
+  const RT rt = rt_at(p.d_rt, nL, K, p);
+  const int pb = rt.pb[j], pe = rt.pb[j + 1];
   const int rpc = 2 * (pe - pb);
   const int KX = p.KX;
   int32_t* gf = a.flags;
@@ -700,6 +735,7 @@ __device__ void dn_loader(const FlowArgs& a, int lw) {
       const int slot = lw;
       const int l = a.l0 + step;
       if (step >= 2) fl_wait_all(FL_FREED + 4 * slot, kFW, step - 1, gf);
+      lstamp(a, l, 10 + slot);
       const LayerDev& Ly = a.layers[l];
       const int lf = rt.lf[step];
       unsigned char* S = s_mem + slot * p.d_slot;
@@ -741,15 +777,17 @@ __device__ void dn_loader(const FlowArgs& a, int lw) {
       fl_st(FL_PRE + slot, step + 1);
       if (!routed_known) {
         fl_wait(FL_ROUTE, step + 1, gf);
+        lstamp(a, l, 12);
         exp_dma(0, K);
         dma_drain();
       }
       fl_st(FL_READY + slot, step + 1);
+      lstamp(a, l, 13);
     }
     return;
   }
   // fc2 rows of each head
-  const int fb = share_b(E, p.nd, j), fe = share_b(E, p.nd, j + 1);
+  const int fb = rt.fb[j], fe = rt.fb[j + 1];
   int prev = 0;
   for (int step = 0; step < nL; ++step) {
     const int lf = rt.lf[step];
@@ -766,12 +804,13 @@ __device__ void dn_loader(const FlowArgs& a, int lw) {
   }
 }
 
-// fc2 rows of the head on layer lh (head step hs), after the last layer or
-// in the wait of a later one.
+// fc2 rows of the head on layer a.l0 + hs, in the wait for a later layer or
+// after the last one.
 template <int CPL, int KM>
-__device__ void dn_head_fc2(const FlowArgs& a, int hs, int& phase) {
-  const FlowPlan& p = a.pl;
-  const Dims& dm = a.dm;
+__device__ __attribute__((noinline)) int dn_head_fc2(uint64_t kap, int hs, int phase) {
+  KA& a = args_at(kap);
+  KP& p = a.pl;
+  const Dims dm = dims_of(a.dm);
   const int E = dm.E, P = dm.P;
   const int lh = a.l0 + hs;
   const int j = blockIdx.x - p.ng;
@@ -780,14 +819,15 @@ __device__ void dn_head_fc2(const FlowArgs& a, int hs, int& phase) {
   int32_t* gf = a.flags;
   uint64_t* X = a.xbuf + (int64_t)lh * p.xlayer;
   float* ab = lds_at<float>(p.d_ab);
+  const RT rt = rt_at(p.d_rt, a.l1 - a.l0, dm.K, p);
   xgather_any(X + p.o_xh1, p.ng * kBlk, ep, t, kFC, gf, [&](int wi, uint32_t v) {
-    const int c = wi / kBlk, o = wi % kBlk;
-    const int hb = share_b(p.hrn, p.ng, c), he = share_b(p.hrn, p.ng, c + 1);
-    if (o < he - hb) ab[hb + o] = bitsf(v);
+    const int c = wi >> 3, o = wi & 7;
+    const int hb = rt.hb[c];
+    if (o < rt.hb[c + 1] - hb) ab[hb + o] = bitsf(v);
   });
   cbar(phase, gf);
   fl_wait(FL_HREADY, hs + 1, gf);
-  const int fb = share_b(E, p.nd, j), fe = share_b(E, p.nd, j + 1);
+  const int fb = rt.fb[j], fe = rt.fb[j + 1];
   const uint16_t* f2 = lds_at<uint16_t>(p.d_f2);
   for (int rr = wave; rr < fe - fb; rr += kFW) {
     const int e = fb + rr;
@@ -798,11 +838,13 @@ __device__ void dn_head_fc2(const FlowArgs& a, int hs, int& phase) {
       const float4 a0 = *reinterpret_cast<const float4*>(ab + 8 * lane);
       const float4 a1 = *reinterpret_cast<const float4*>(ab + 8 * lane + 4);
       const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      float a2 = 0.0f;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         acc = fmaf(h2f((uint16_t)(ww[q] & 0xFFFF)), av[2 * q], acc);
-        acc = fmaf(h2f((uint16_t)(ww[q] >> 16)), av[2 * q + 1], acc);
+        a2 = fmaf(h2f((uint16_t)(ww[q] >> 16)), av[2 * q + 1], a2);
       }
+      acc += a2;
     }
     acc = wave_sum_rows(acc);
     const float logit = acc + ab[P + e];
@@ -813,15 +855,17 @@ __device__ void dn_head_fc2(const FlowArgs& a, int hs, int& phase) {
   }
   if (wave == 0 && lane >= fe - fb && lane < kBlk) xput(X + p.o_xh2 + j * kBlk + lane, 0u, ep);
   release(FL_HFREED + wave, hs + 1);
+  return phase;
 }
 
-// Ranking of the head on layer lh into the next token's routing of layer lh+1
-// (wave 0 of the designated down CU).
+// Ranking of the head on layer lh into the next token's routing of layer
+// lh+1 (wave 0 of the designated down CU).
 template <int CPL, int KM>
-__device__ void dn_head_topk(const FlowArgs& a, int lh) {
-  const FlowPlan& p = a.pl;
-  const Dims& dm = a.dm;
-  const int E = dm.E, K = dm.K;
+__device__ __attribute__((noinline)) void dn_head_topk(uint64_t kap, int lh) {
+  KA& a = args_at(kap);
+  KP& p = a.pl;
+  const Dims dm = dims_of(a.dm);
+  const int K = dm.K;
   const int nxt = (a.token + 1) & 1;
   const uint32_t ep = a.epoch;
   int32_t* gf = a.flags;
@@ -829,10 +873,11 @@ __device__ void dn_head_topk(const FlowArgs& a, int lh) {
   uint64_t* X = a.xbuf + (int64_t)lh * p.xlayer;
   float* lg = lds_at<float>(p.d_lg);
   RouteScratch& rs = *lds_at<RouteScratch>(p.d_rs);
+  const RT rt = rt_at(p.d_rt, a.l1 - a.l0, K, p);
   xgather_any(X + p.o_xh2, p.nd * kBlk, ep, lane, 64, gf, [&](int wi, uint32_t v) {
-    const int jd = wi / kBlk, o = wi % kBlk;
-    const int fb = share_b(E, p.nd, jd), fe = share_b(E, p.nd, jd + 1);
-    if (o < fe - fb) lg[fb + o] = bitsf(v);
+    const int jd = wi >> 3, o = wi & 7;
+    const int fb = rt.fb[jd];
+    if (o < rt.fb[jd + 1] - fb) lg[fb + o] = bitsf(v);
   });
   wave_lds_sync();
   int32_t* pidx = lh + 1 < a.L ? a.route_idx + ((int64_t)nxt * a.L + lh + 1) * K : a.sink_idx;
@@ -841,10 +886,11 @@ __device__ void dn_head_topk(const FlowArgs& a, int lh) {
 }
 
 template <int CPL, int KM>
-__device__ void dn_compute(const FlowArgs& a) {
-  const FlowPlan& p = a.pl;
+__device__ __attribute__((noinline)) void dn_compute(uint64_t kap) {
+  KA& a = args_at(kap);
+  KP& p = a.pl;
   constexpr int d = 512 * CPL;
-  const Dims& dm = a.dm;
+  const Dims dm = dims_of(a.dm);
   const int K = dm.K, E = dm.E, r = dm.r, I = kFI;
   const int nL = a.l1 - a.l0;
   const int j = blockIdx.x - p.ng;
@@ -852,14 +898,17 @@ __device__ void dn_compute(const FlowArgs& a) {
   const int li = t % kGL, grp = t / kGL;
   const uint32_t ep = a.epoch;
   int32_t* gf = a.flags;
-  const RT rt = rt_at(p.d_rt, nL, K);
-  const int pb = share_b(d / 2, p.nd, j), pe = share_b(d / 2, p.nd, j + 1);
+  const RT rt = rt_at(p.d_rt, nL, K, p);
+  const int pb = rt.pb[j], pe = rt.pb[j + 1];
   const int npairs = pe - pb, rpc = 2 * npairs;
-  const int KX = p.KX;
-  float* sb = lds_at<float>(p.d_sb);
+  const int KX = p.KX, KI = K * I;
+  const int Is = KX > K ? I : 0;
+  const int ngs = p.ng - p.ngr;
+  float* sb = lds_at<float>(p.d_sb);   // SwiGLU outputs [KX][I]; the shared slot first holds raw g
+  float* su = lds_at<float>(p.d_su);   // the shared expert's raw u [I]
+  float* ax = lds_at<float>(p.d_ax);   // LoRA A products: A_gate x, then A_up x
   uint16_t* hk = lds_at<uint16_t>(p.d_hk);
   float* csc = lds_at<float>(p.d_cs);
-  float* pv = lds_at<float>(p.d_pv);
   float* vv = lds_at<float>(p.d_v);
   float* coef = lds_at<float>(p.d_co);
   uint16_t* ho = lds_at<uint16_t>(p.d_ho);
@@ -878,19 +927,38 @@ __device__ void dn_compute(const FlowArgs& a) {
     const LayerDev& Ly = a.layers[l];
     stamp(a, l, 0);
 
+    // LoRA matrices of the shared expert, fetched ahead into registers:
+    // rows t and t + 256 of B_gate and B_up, and rank t/16's A_down columns
+    // 32 (t%16) .. 32 (t%16) + 31
+    const bool lora = (lf & LF_SHARED) && (lf & LF_LORA) && Is;
+    const bool lorad = (lf & LF_SHARED) && (lf & LF_LORAD) && Is;
+    uint4 bgr[2][2], bur[2][2], adr[4];
+    if (lora) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          bgr[q][h] = ldg(reinterpret_cast<const uint4*>(Ly.sh.bg + (int64_t)(t + 256 * q) * r + 8 * h));
+          bur[q][h] = ldg(reinterpret_cast<const uint4*>(Ly.sh.bu + (int64_t)(t + 256 * q) * r + 8 * h));
+        }
+    }
+    if (lorad) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        adr[c] = ldg(reinterpret_cast<const uint4*>(Ly.sh.ad + (int64_t)(t >> 4) * I + 32 * (t & 15) + 8 * c));
+    }
+
     // ---- routing of a router layer: ranked here as well -----------------------
-    if (lf & LF_ROUTER) {
-      if (wave == 0) {
-        xgather_any(X + p.o_xr, p.nrc * kBlk, ep, lane, 64, gf, [&](int wi, uint32_t v) {
-          const int c = wi / kBlk, o = wi % kBlk, e = kRouterRows * c + o;
-          if (o < kRouterRows && e < E) lg[e] = bitsf(v);
-        });
-        wave_lds_sync();
-        route_wave(dm, lg, Ly.router_bias, rs, rt.idx + step * K, rt.w + step * K, gf);
-        wave_lds_sync();
-        if (lane < K) rt.ent[step * K + lane] = (int32_t)resolve_entry(Ly.pool, E, rt.idx[step * K + lane]);
-        release(FL_ROUTE, step + 1);
-      }
+    if ((lf & LF_ROUTER) && wave == 0) {
+      xgather_any(X + p.o_xr, p.nrc * kBlk, ep, lane, 64, gf, [&](int wi, uint32_t v) {
+        const int c = wi >> 3, o = wi & 7, e = kRouterRows * c + o;
+        if (o < kRouterRows && e < E) lg[e] = bitsf(v);
+      });
+      wave_lds_sync();
+      route_wave(dm, lg, Ly.router_bias, rs, rt.idx + step * K, rt.w + step * K, gf);
+      wave_lds_sync();
+      if (lane < K) rt.ent[step * K + lane] = (int32_t)resolve_entry(Ly.pool, E, rt.idx[step * K + lane]);
+      release(FL_ROUTE, step + 1);
     }
     if (wave == 0 && lane < KX) {
       float cv = 0.0f;
@@ -899,60 +967,125 @@ __device__ void dn_compute(const FlowArgs& a) {
       coef[lane] = cv;
     }
 
-    // ---- SwiGLU outputs and A_down partials ------------------------------------
+    // ---- SwiGLU outputs, the shared expert's sums, LoRA A products -------------
     {
-      const int nitem = p.ng * p.bi;
-      xgather_any(X + p.o_xb, nitem + p.n_sho * p.pbw, ep, t, kFC, gf, [&](int wi, uint32_t v) {
-        if (wi < nitem) {
-          const int c = wi / p.bi, o = wi % p.bi;
-          const int b = share_b(p.items, p.ng, c), e = share_b(p.items, p.ng, c + 1);
-          if (o < e - b) sb[b + o] = bitsf(v);
+      const int lbr = p.lbr, lhs = p.lhs, hsz = 1 << lhs;
+      xgather_any(X + p.o_xb, p.xb_n, ep, t, kFC, gf, [&](int wi, uint32_t v) {
+        if (wi < p.xb_s) {
+          const int c = wi >> lbr, o = wi & ((1 << lbr) - 1);
+          const int b = rt.ibr[c];
+          if (o < rt.ibr[c + 1] - b) sb[b + o] = bitsf(v);
+        } else if (wi < p.xb_a) {
+          const int w2 = wi - p.xb_s, c = w2 >> (lhs + 1), o = w2 & (2 * hsz - 1);
+          const int oo = o & (hsz - 1);
+          const int b = rt.ibs[c];
+          if (c < ngs && oo < rt.ibs[c + 1] - b) {
+            if (o < hsz) sb[KI + b + oo] = bitsf(v);
+            else su[b + oo] = bitsf(v);
+          }
         } else {
-          const int o2 = wi - nitem, sh = o2 / p.pbw, q = o2 % p.pbw;
-          if (q < r) pv[sh * r + q] = bitsf(v);
+          const int w3 = wi - p.xb_a;
+          if ((w3 & 7) == 0) ax[w3 >> 3] = bitsf(v);
         }
       });
     }
     cbar(phase, gf);
     stamp(a, l, 1);
+    // the shared expert: LoRA B terms, then the SwiGLU
+    if (Is && (lf & LF_SHARED)) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int i = t + 256 * q;
+        float g = sb[KI + i], u = su[i];
+        if (lora) {
+          float lg2 = 0.0f, lu2 = 0.0f;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t gw[4] = {bgr[q][h].x, bgr[q][h].y, bgr[q][h].z, bgr[q][h].w};
+            const uint32_t uw[4] = {bur[q][h].x, bur[q][h].y, bur[q][h].z, bur[q][h].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              lg2 = fmaf(h2f((uint16_t)(gw[e] & 0xFFFF)), ax[8 * h + 2 * e], lg2);
+              lg2 = fmaf(h2f((uint16_t)(gw[e] >> 16)), ax[8 * h + 2 * e + 1], lg2);
+              lu2 = fmaf(h2f((uint16_t)(uw[e] & 0xFFFF)), ax[r + 8 * h + 2 * e], lu2);
+              lu2 = fmaf(h2f((uint16_t)(uw[e] >> 16)), ax[r + 8 * h + 2 * e + 1], lu2);
+            }
+          }
+          g = fmaf(dm.lora_scale, lg2, g);
+          u = fmaf(dm.lora_scale, lu2, u);
+        }
+        sb[KI + i] = silu(g) * u;
+      }
+    }
+    cbar(phase, gf);
     // fp16 hi + lo copies (pair-permuted) with a power-of-two scale per 32 elements
 #pragma unroll
     for (int k = 0; k < KM + 1; ++k) {
-      if (k >= KX) break;
-      const float2 v = *reinterpret_cast<const float2*>(sb + k * I + 32 * grp + 2 * li);
-      const float sc = hilo_pair(v.x, v.y, grp, li, hk + k * 2 * I, I);
-      if (li == 0) csc[k * (I / 32) + grp] = sc;
+      if (k < KX) {
+        const float2 v = *reinterpret_cast<const float2*>(sb + k * I + 32 * grp + 2 * li);
+        const float sc = hilo_pair(v.x, v.y, grp, li, hk + k * 2 * I, I);
+        if (li == 0) csc[k * (I / 32) + grp] = sc;
+      }
     }
-    if (wave == 1 && lane < r) {
-      float s = 0.0f;
-      if (lf & LF_LORAD)
-        for (int sh = 0; sh < p.n_sho; ++sh) s += pv[sh * r + lane];
-      vv[lane] = s;
+    // A_down . h_shared: group g takes rank g, lane li its 32 columns
+    {
+      float part = 0.0f;
+      if (lorad) {
+        const float* hsv = sb + KI + 32 * li;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t aw[4] = {adr[c].x, adr[c].y, adr[c].z, adr[c].w};
+          const float4 h0 = *reinterpret_cast<const float4*>(hsv + 8 * c);
+          const float4 h1 = *reinterpret_cast<const float4*>(hsv + 8 * c + 4);
+          float p2 = 0.0f;
+          part = fmaf(h2f((uint16_t)(aw[0] & 0xFFFF)), h0.x, part);
+          p2 = fmaf(h2f((uint16_t)(aw[0] >> 16)), h0.y, p2);
+          part = fmaf(h2f((uint16_t)(aw[1] & 0xFFFF)), h0.z, part);
+          p2 = fmaf(h2f((uint16_t)(aw[1] >> 16)), h0.w, p2);
+          part = fmaf(h2f((uint16_t)(aw[2] & 0xFFFF)), h1.x, part);
+          p2 = fmaf(h2f((uint16_t)(aw[2] >> 16)), h1.y, p2);
+          part = fmaf(h2f((uint16_t)(aw[3] & 0xFFFF)), h1.z, part);
+          p2 = fmaf(h2f((uint16_t)(aw[3] >> 16)), h1.w, p2);
+          part += p2;
+        }
+      }
+      part = group_sum<kGL>(part);
+      if (li == 0) vv[grp] = part;
     }
     cbar(phase, gf);
     stamp(a, l, 2);
 
     // ---- down rows: every expert slot, down LoRA, residual -----------------------
     fl_wait(FL_READY + slot, step + 1, gf);
+    stamp(a, l, 6);
     if (grp < npairs) {
       const int rr0 = 2 * grp;
-      float acc0 = 0.0f, acc1 = 0.0f;
       constexpr int pq = kFI / 32;
+      float p0[KM + 1], p1[KM + 1];
 #pragma unroll
       for (int k = 0; k < KM + 1; ++k) {
-        if (k >= KX) break;
-        const float cf = coef[k];
-        if (cf == 0.0f) continue;  // unresolved expert or no shared expert: uniform
-        f16x2 xh[16], xl[16];
-        load_xchunk(hk + k * 2 * I, li, xh);
-        load_xchunk(hk + k * 2 * I + I, li, xl);
-        const float f = cf * csc[k * (I / 32) + li];
-        const uint4* dq = reinterpret_cast<const uint4*>(S + p.d_dq) + (k * rpc + rr0) * pq;
-        const uint16_t* ds = reinterpret_cast<const uint16_t*>(S + p.d_ds + 16 * (k * rpc + rr0));
-        acc0 = fmaf(f, h2f(ds[li >> 1]) * q4_dot32_hl(dq[li], xh, xl), acc0);
-        acc1 = fmaf(f, h2f(ds[8 + (li >> 1)]) * q4_dot32_hl(dq[pq + li], xh, xl), acc1);
+        p0[k] = p1[k] = 0.0f;
+        // slots past KX, unresolved experts and a missing shared expert carry
+        // a zero coefficient (uniform over the CU)
+        if (k < KX && coef[k] != 0.0f) {
+          f16x2 xh[16], xl[16];
+          load_xchunk(hk + k * 2 * I, li, xh);
+          load_xchunk(hk + k * 2 * I + I, li, xl);
+          const float f = coef[k] * csc[k * (I / 32) + li];
+          const uint4* dq = reinterpret_cast<const uint4*>(S + p.d_dq) + (k * rpc + rr0) * pq;
+          const uint16_t* ds = reinterpret_cast<const uint16_t*>(S + p.d_ds + 16 * (k * rpc + rr0));
+          p0[k] = f * (h2f(ds[li >> 1]) * q4_dot32_hl_ilp(dq[li], xh, xl));
+          p1[k] = f * (h2f(ds[8 + (li >> 1)]) * q4_dot32_hl_ilp(dq[pq + li], xh, xl));
+        }
       }
-      if ((lf & LF_LORAD) && KX > K) {
+      float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+      for (int k = 0; k < KM + 1; ++k) {
+        acc0 += p0[k];
+        acc1 += p1[k];
+      }
+      stamp(a, l, 7);
+      if (lorad) {
         const uint16_t* bd = reinterpret_cast<const uint16_t*>(S + p.d_bd) + rr0 * r;
         acc0 = fmaf(dm.lora_scale, h2f(bd[li]) * vv[li], acc0);
         acc1 = fmaf(dm.lora_scale, h2f(bd[r + li]) * vv[li], acc1);
@@ -972,24 +1105,25 @@ __device__ void dn_compute(const FlowArgs& a) {
         ho[rr0 + 1] = o1;
         const int row = 2 * (pb + grp);
         *reinterpret_cast<uint32_t*>(a.h + (int64_t)(step + 1) * d + row) = o0 | ((uint32_t)o1 << 16);
-        xput(X + p.o_xa + j * p.ba + grp, o0 | ((uint32_t)o1 << 16), ep);
+        xput(X + p.o_xa + (j << p.lba) + grp, o0 | ((uint32_t)o1 << 16), ep);
       }
     }
-    if (t >= npairs && t < p.ba) xput(X + p.o_xa + j * p.ba + t, 0u, ep);
+    stamp(a, l, 8);
+    if (t >= npairs && t < (1 << p.lba)) xput(X + p.o_xa + (j << p.lba) + t, 0u, ep);
     release(FL_FREED + 4 * slot + wave, step + 1);
     stamp(a, l, 3);
 
     // ---- heads in the wait for the next layer ----------------------------------
-    if (step >= 1 && (rt.lf[step - 1] & LF_HEAD)) dn_head_fc2<CPL, KM>(a, step - 1, phase);
+    if (step >= 1 && (rt.lf[step - 1] & LF_HEAD)) phase = dn_head_fc2<CPL, KM>(kap, step - 1, phase);
     stamp(a, l, 4);
     if (step >= 2 && (rt.lf[step - 2] & LF_HEAD) && (l - 2) % p.nd == j && wave == 0)
-      dn_head_topk<CPL, KM>(a, l - 2);
+      dn_head_topk<CPL, KM>(kap, l - 2);
     stamp(a, l, 5);
   }
-  if (nL >= 1 && (rt.lf[nL - 1] & LF_HEAD)) dn_head_fc2<CPL, KM>(a, nL - 1, phase);
+  if (nL >= 1 && (rt.lf[nL - 1] & LF_HEAD)) phase = dn_head_fc2<CPL, KM>(kap, nL - 1, phase);
   for (int hs = (nL >= 2 ? nL - 2 : 0); hs < nL; ++hs)
     if ((rt.lf[hs] & LF_HEAD) && (a.l0 + hs) % p.nd == j && wave == 0)
-      dn_head_topk<CPL, KM>(a, a.l0 + hs);
+      dn_head_topk<CPL, KM>(kap, a.l0 + hs);
   stamp(a, a.L, 0);
 }
 
@@ -1002,8 +1136,8 @@ __global__ __launch_bounds__(kFThreads) void k_flow(FlowArgs a) {
   const int cur = a.token & 1, nxt = (a.token + 1) & 1;
   const int t = threadIdx.x;
   if (t < FL_N) s_fl[t] = 0;
-  // routing tables of the launch and per-step layer flags
-  const RT rt = rt_at(gu ? p.g_rt : p.d_rt, nL, K);
+  // routing tables of the launch, per-step layer flags, the work split
+  const RT rt = rt_at(gu ? p.g_rt : p.d_rt, nL, K, p);
   for (int i = t; i < nL * K; i += kFThreads) {
     const int l = a.l0 + i / K, k = i % K;
     const LayerDev& Ly = a.layers[l];
@@ -1012,6 +1146,14 @@ __global__ __launch_bounds__(kFThreads) void k_flow(FlowArgs a) {
     rt.w[i] = a.route_w[((int64_t)cur * a.L + l) * K + k];
     rt.prev[i] = a.token > 0 ? a.exec_idx[((int64_t)nxt * a.L + l) * K + k] : -1;
     rt.ent[i] = Ly.router ? -1 : (int32_t)resolve_entry(Ly.pool, E, e);
+  }
+  const int ngs = p.ng - p.ngr;
+  for (int i = t; i <= p.ngr; i += kFThreads) rt.ibr[i] = share_b(K * kFI, p.ngr, i);
+  for (int i = t; i <= ngs; i += kFThreads) rt.ibs[i] = ngs ? share_b(a.dm.Is, ngs, i) : 0;
+  for (int i = t; i <= p.ng; i += kFThreads) rt.hb[i] = share_b(p.hrn, p.ng, i);
+  for (int i = t; i <= p.nd; i += kFThreads) {
+    rt.pb[i] = share_b(a.dm.d / 2, p.nd, i);
+    rt.fb[i] = share_b(E, p.nd, i);
   }
   for (int s = t; s < nL; s += kFThreads) {
     const LayerDev& Ly = a.layers[a.l0 + s];
@@ -1026,14 +1168,15 @@ __global__ __launch_bounds__(kFThreads) void k_flow(FlowArgs a) {
   }
   __syncthreads();
   const int w = t >> 6;
+  const uint64_t kap = (uint64_t)__builtin_amdgcn_kernarg_segment_ptr();
   if (w >= kFW) {
-    if (gu) gu_loader<CPL, KM>(a, w - kFW);
-    else dn_loader<CPL, KM>(a, w - kFW);
+    if (gu) gu_loader<CPL, KM>(kap, w - kFW);
+    else dn_loader<CPL, KM>(kap, w - kFW);
     dma_drain();
     return;
   }
-  if (gu) gu_compute<CPL, KM>(a);
-  else dn_compute<CPL, KM>(a);
+  if (gu) gu_compute<CPL, KM>(kap);
+  else dn_compute<CPL, KM>(kap);
 }
 
 template <int CPL, int KM>
@@ -1046,9 +1189,13 @@ hipError_t launch_flow_t(const FlowArgs& a, hipStream_t st) {
 
 // ------------------------------------------------------------------ plan --
 
-static int rup8(int x) { return (x + 7) & ~7; }
 static int rup16(int x) { return (x + 15) & ~15; }
 static int cdiv(int a, int b) { return (a + b - 1) / b; }
+static int log2ceil(int x, int lo) {
+  int l = lo;
+  while ((1 << l) < x) ++l;
+  return l;
+}
 
 bool flow_supported(const Dims& dm) {
   if (dm.affine) return false;
@@ -1063,35 +1210,34 @@ bool flow_supported(const Dims& dm) {
 FlowPlan flow_plan(const Dims& dm, int ng, int nd, int nL) {
   FlowPlan p{};
   p.ok = 0;
-  if (!flow_supported(dm) || ng < 1 || nd < 1 || nL < 1 || nL > kFMaxL) return p;
-  const int d = dm.d, K = dm.K, E = dm.E, I = dm.I, r = dm.r, P = dm.P;
+  if (!flow_supported(dm) || ng < 2 || nd < 1 || nL < 1 || nL > kFMaxL) return p;
+  const int d = dm.d, K = dm.K, E = dm.E, I = dm.I, r = dm.r, P = dm.P, Is = dm.Is;
+  const int KI = K * I;
   p.ng = ng;
   p.nd = nd;
-  p.KX = K + (dm.Is ? 1 : 0);
-  p.items = K * I + dm.Is;
-  p.ipc_max = cdiv(p.items, ng);
-  p.bi = rup8(p.ipc_max);
-  const int KI = K * I;
-  p.cs0 = ng;
-  if (dm.Is) {
-    // first CU whose item range reaches past the routed items
-    const int64_t c1 = ((int64_t)(KI + 1) * ng + p.items - 1) / p.items;
-    p.cs0 = (int)c1 - 1;
-    if (p.cs0 < 0) p.cs0 = 0;
-    while (p.cs0 > 0 && (int64_t)p.items * p.cs0 / ng > KI) --p.cs0;
-    while ((int64_t)p.items * (p.cs0 + 1) / ng <= KI) ++p.cs0;
+  p.KX = K + (Is ? 1 : 0);
+  // routed and shared gate/up CUs in proportion to their items
+  p.ngr = ng;
+  if (Is) {
+    p.ngr = (int)(((int64_t)ng * KI + (KI + Is) / 2) / (KI + Is));
+    if (p.ngr > ng - 1) p.ngr = ng - 1;
+    if (p.ngr < 1) p.ngr = 1;
   }
-  p.n_sho = dm.Is ? ng - p.cs0 : 0;
-  p.pbw = (dm.Is && r) ? rup8(r) : 0;
+  const int ngs = ng - p.ngr;
+  p.ipr_max = cdiv(KI, p.ngr);
+  p.ips_max = Is ? cdiv(Is, ngs) : 0;
+  p.ipc_max = p.ipr_max > p.ips_max ? p.ipr_max : p.ips_max;
+  p.lbr = log2ceil(p.ipr_max, 3);
+  p.lhs = log2ceil(p.ips_max, 2);
   p.pairs_max = cdiv(d / 2, nd);
-  p.ba = rup8(p.pairs_max);
+  p.lba = log2ceil(p.pairs_max, 3);
   p.nrc = cdiv(E, kRouterRows);
   p.ca0 = p.nrc;
   p.hrn = P + E;
   p.hr_max = cdiv(p.hrn, ng);
   p.f2_max = cdiv(E, nd);
   if (p.ipc_max > 2 * kGN || p.pairs_max > kGN || p.hr_max > kBlk || p.f2_max > kBlk) return p;
-  if (ng < p.nrc + 2 * r) return p;
+  if (p.ngr < p.nrc + 2 * r || ng < p.nrc) return p;
   // exchange words of a layer (every region starts on a 128-byte line)
   int o = 0;
   auto region = [&](int n) {
@@ -1099,23 +1245,24 @@ FlowPlan flow_plan(const Dims& dm, int ng, int nd, int nL) {
     o += (n + 15) & ~15;
     return at;
   };
-  p.o_xa = region(nd * p.ba);
-  p.o_xb = region(ng * p.bi + p.n_sho * p.pbw);
+  p.o_xa = region(nd << p.lba);
+  p.xb_s = p.ngr << p.lbr;
+  p.xb_a = p.xb_s + (Is ? ngs << (p.lhs + 1) : 0);
+  p.xb_n = p.xb_a + 2 * r * kBlk;
+  p.o_xb = region(p.xb_n);
   p.o_xr = region(p.nrc * kBlk);
-  p.o_xl = region(2 * r * kBlk);
   p.o_xh1 = region(ng * kBlk);
   p.o_xh2 = region(nd * kBlk);
   p.xlayer = o;
+  // routing tables, layer flags and split tables
+  const int rtb = nL * K * 16 + nL * 4 + (p.ngr + 1 + ngs + 1 + nd + 1 + ng + 1 + nd + 1) * 4;
   // gate/up CU LDS
-  const int rtb = nL * K * 16 + nL * 4;
   {
     const int ipc = p.ipc_max;
     int s = 0;
     p.g_at = s; s = rup16(s + d * 2);
     p.g_gq = s; s = rup16(s + ipc * 2 * (d / 2));
     p.g_gs = s; s = rup16(s + ipc * 2 * (d / 32));
-    p.g_lb = s; s = rup16(s + ipc * 2 * r * 2);
-    p.g_ad = s; s = rup16(s + r * (ipc / 2 + 2) * 4);
     p.g_ar = s; s = rup16(s + d * 2);
     p.g_slot = s;
     int off = 2 * s;
@@ -1127,8 +1274,6 @@ FlowPlan flow_plan(const Dims& dm, int ng, int nd, int nL) {
     p.g_xp = off; off = rup16(off + d * 2);
     p.g_lg = off; off = rup16(off + E * 4);
     p.g_rs = off; off = rup16(off + (int)sizeof(RouteScratch));
-    p.g_ax = off; off = rup16(off + kFW * 2 * kFRank * 4);
-    p.g_pp = off; off = rup16(off + kGN * kFRank * 4);
     p.g_rt = off; off = rup16(off + rtb);
     p.g_end = off;
   }
@@ -1144,10 +1289,11 @@ FlowPlan flow_plan(const Dims& dm, int ng, int nd, int nL) {
     int off = 2 * s;
     p.d_f2 = off; off = rup16(off + p.f2_max * P * 2);
     p.d_sb = off; off = rup16(off + KX * I * 4);
+    p.d_su = off; off = rup16(off + I * 4);
+    p.d_ax = off; off = rup16(off + 2 * kFRank * 4);
     p.d_hk = off; off = rup16(off + KX * 2 * I * 2);
     p.d_cs = off; off = rup16(off + KX * (I / 32) * 4);
-    p.d_pv = off; off = rup16(off + (p.n_sho > 0 ? p.n_sho : 1) * (r > 0 ? r : 1) * 4);
-    p.d_v = off; off = rup16(off + kFRank * 4);
+    p.d_v = off; off = rup16(off + kGN * 4);
     p.d_co = off; off = rup16(off + 16 * 4);
     p.d_ho = off; off = rup16(off + rpc * 2);
     p.d_ab = off; off = rup16(off + (P + E) * 4);

@@ -72,6 +72,34 @@ __device__ __forceinline__ float q4_dot32_hl(uint4 wv, const f16x2* xh, const f1
   return p;
 }
 
+// The same sums with independent partial sums per packed word (and per hi /
+// lo half), so that a single wave's dependent v_dot2 chains are four (eight)
+// times shorter; the partials are added in a fixed tree.
+__device__ __forceinline__ float q4_dot32_ilp(uint4 wv, const f16x2* xr) {
+  const float p0 = q4_dot8(wv.x, xr + 0, 0.0f), p1 = q4_dot8(wv.y, xr + 4, 0.0f);
+  const float p2 = q4_dot8(wv.z, xr + 8, 0.0f), p3 = q4_dot8(wv.w, xr + 12, 0.0f);
+  return (p0 + p1) + (p2 + p3);
+}
+
+__device__ __forceinline__ float q4_dot8_split(uint32_t w, const f16x2* xh, const f16x2* xl) {
+  f16x2 p0, p1, p2, p3;
+  q4_pairs(w, p0, p1, p2, p3);
+  float h = dot2(p0, xh[0], 0.0f), l = dot2(p0, xl[0], 0.0f);
+  h = dot2(p1, xh[1], h);
+  l = dot2(p1, xl[1], l);
+  h = dot2(p2, xh[2], h);
+  l = dot2(p2, xl[2], l);
+  h = dot2(p3, xh[3], h);
+  l = dot2(p3, xl[3], l);
+  return h + l;
+}
+
+__device__ __forceinline__ float q4_dot32_hl_ilp(uint4 wv, const f16x2* xh, const f16x2* xl) {
+  const float p0 = q4_dot8_split(wv.x, xh + 0, xl + 0), p1 = q4_dot8_split(wv.y, xh + 4, xl + 4);
+  const float p2 = q4_dot8_split(wv.z, xh + 8, xl + 8), p3 = q4_dot8_split(wv.w, xh + 12, xl + 12);
+  return (p0 + p1) + (p2 + p3);
+}
+
 // Block-wide max of |v| over a strided range (kBlock threads).
 __device__ __forceinline__ float block_absmax(const float* v, int n, float* red) {
   float m = 0.0f;

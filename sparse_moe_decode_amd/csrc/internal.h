@@ -175,13 +175,24 @@ hipError_t launch_stack(const StackArgs& a, int grid, hipStream_t st);
 // layout of both roles (byte offsets); host and kernel read the same plan.
 constexpr int kFlowLds = 156 * 1024;
 struct FlowPlan {
-  int32_t ok, ng, nd, KX, items, ipc_max, bi, cs0, n_sho, pbw, pairs_max, ba, nrc, ca0, hrn,
-      hr_max, f2_max;
-  int32_t o_xa, o_xb, o_xr, o_xl, o_xh1, o_xh2, xlayer;
-  int32_t g_at, g_gq, g_gs, g_lb, g_ad, g_ar, g_slot, g_rb, g_hb, g_hc, g_h, g_xn, g_xp, g_lg, g_rs,
-      g_ax, g_pp, g_rt, g_end;
-  int32_t d_dq, d_ds, d_bd, d_at, d_slot, d_f2, d_sb, d_hk, d_cs, d_pv, d_v, d_co, d_ho, d_ab, d_lg,
-      d_rs, d_rt, d_end;
+  int32_t ok, ng, nd, KX;
+  // gate/up CUs [0, ngr) own the routed items (K*I, ipr_max at most each),
+  // [ngr, ng) the shared expert's rows (ips_max at most each)
+  int32_t ngr, ipr_max, ips_max, ipc_max;
+  int32_t lbr, lhs;  // routed block 1 << lbr words; shared block 2 << lhs (g, then u)
+  int32_t pairs_max, lba, nrc, ca0, hrn, hr_max, f2_max;
+  // exchange words of a layer: h_out, SwiGLU outputs (routed blocks, shared
+  // blocks, LoRA A-product blocks: one region), router logits, head hidden
+  // and linear path, head logits
+  int32_t o_xa, o_xb, xb_n, xb_s, xb_a, o_xr, o_xh1, o_xh2, xlayer;
+  // gate/up CU LDS (bytes): layer slot (attention update, item rows, scales,
+  // LoRA A row), router rows, head rows, head one-hot words, work
+  int32_t g_at, g_gq, g_gs, g_ar, g_slot, g_rb, g_hb, g_hc, g_h, g_xn, g_xp, g_lg, g_rs, g_rt,
+      g_end;
+  // down CU LDS: layer slot (down rows, scales, LoRA B_down rows, attention
+  // pairs), fc2 rows, work
+  int32_t d_dq, d_ds, d_bd, d_at, d_slot, d_f2, d_sb, d_su, d_ax, d_hk, d_cs, d_v, d_co, d_ho,
+      d_ab, d_lg, d_rs, d_rt, d_end;
 };
 struct FlowArgs {
   Dims dm;
