@@ -175,6 +175,29 @@ int moe_int4_decode(e0_ctx* ctx, const e0_experts* routed, const int32_t* slot_o
                     const float* w, int32_t n_tokens, uint16_t* y, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * moe_int4_decode_static — moe_int4_decode for callers that cannot allocate
+ * device memory at call time (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc). Same arguments and result as
+ * moe_int4_decode, with the tier given by its spec instead of a context, and
+ * no allocation, free or allocating library call of any kind: the kernels'
+ * workspace is a library-owned static device array of 16 MiB per GPU, held
+ * until the process ends, whose address is looked up (not allocated) on the
+ * first call on each device.
+ *   spec     the tier (validated as in e0_create).
+ *   flags    device int32 [4] or NULL: the kernels OR error bits into
+ *            flags[0] (an expert id out of range, as e0_device_status
+ *            reports them for moe_int4_decode); the library never clears it.
+ * E0_ERR_SHAPE when n_tokens tokens of this tier need more than the 16 MiB
+ * (35B shapes with K = 4: up to about 240 tokens; K = 8: about 150).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (two streams, two host threads) race and must be serialised by the
+ * caller. Each call rewrites all of the workspace it reads. */
+int moe_int4_decode_static(const e0_spec* spec, const e0_experts* routed, const int32_t* slot_of,
+                           const e0_shared* shared, const uint16_t* x, const int32_t* idx,
+                           const float* w, int32_t n_tokens, uint16_t* y, int32_t* flags,
+                           void* stream);
+
+/* ---------------------------------------------------------------------------
  * lora_delta — y_acc[b] += scale * B (A x[b]) for B tokens [MW §3.3; RG
  * "Unmerged Adapter Execution"]. A fp16 [rank, in], Bm fp16 [out, rank],
  * x fp16 [B, in], y_acc fp32 [B, out] (read-modify-write). rank <= 64. */

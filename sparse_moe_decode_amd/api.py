@@ -85,6 +85,8 @@ _lib.e0_last_error.restype = C.c_char_p
 _lib.e0_device_status.argtypes = [_p, _p]
 _lib.moe_int4_decode.argtypes = [_p, C.POINTER(e0_experts), _p, C.POINTER(e0_shared), _p, _p,
                                  _p, _i32, _p, _p]
+_lib.moe_int4_decode_static.argtypes = [C.POINTER(e0_spec), C.POINTER(e0_experts), _p,
+                                        C.POINTER(e0_shared), _p, _p, _p, _i32, _p, _p, _p]
 _lib.lora_delta.argtypes = [_p, _p, _p, _i32, _i32, _i32, _f, _p, _p, _i32, _p]
 _lib.prerouter_forward.argtypes = [_p, C.POINTER(e0_head), _p, _p, _p, _i32, _p, _p, _p, _p]
 _lib.e0_model_create.argtypes = [_p, C.POINTER(e0_layer), _i32, C.POINTER(_p)]
@@ -121,7 +123,7 @@ EXPORTS = ["e0_create", "e0_destroy", "e0_last_error", "e0_device_status", "moe_
            "stage_experts", "stage_experts_n", "e0_stager_copies", "stage_layer",
            "e0_cache_create", "e0_cache_destroy", "e0_cache_copies", "stage_experts_cached",
            "e0_store_open", "e0_store_close", "e0_store_read", "e0_store_wait", "e0_store_bytes", "e0_model_set_path", "e0_model_set_grid", "e0_model_set_trace", "e0_model_trace_shape",
-           "e0_model_set_roles"]
+           "e0_model_set_roles", "moe_int4_decode_static"]
 
 PATH_AUTO, PATH_PHASES, PATH_PERSISTENT, PATH_FLOW = 0, 1, 2, 3
 QUANT_SYMMETRIC, QUANT_AFFINE = 0, 1
@@ -242,6 +244,24 @@ def moe_int4_decode(ctx: Context, routed: dict, x, idx, w, y=None, shared: dict 
     _check(_lib.moe_int4_decode(ctx.handle, C.byref(ex), _ptr(slot_of),
                                 C.byref(sh) if sh is not None else None, _ptr(x), _ptr(idx),
                                 _ptr(w), B, _ptr(y), _stream(stream)))
+    return y
+
+
+def moe_int4_decode_static(dims: dict, routed: dict, x, idx, w, y=None,
+                           shared: dict | None = None, slot_of=None, count=None, stride: int = 0,
+                           flags=None, stream=None):
+    """moe_int4_decode on the library's static workspace (no context, no
+    allocation inside the call). flags: device int32 [4] receiving error bits."""
+    B = x.shape[0]
+    if y is None:
+        y = torch.empty_like(x)
+    spec = make_spec(dims)
+    ex = experts_struct(routed, count if count is not None else dims["E"], stride, stride)
+    sh = shared_struct(shared)
+    _check(_lib.moe_int4_decode_static(C.byref(spec), C.byref(ex), _ptr(slot_of),
+                                       C.byref(sh) if sh is not None else None, _ptr(x),
+                                       _ptr(idx), _ptr(w), B, _ptr(y), _ptr(flags),
+                                       _stream(stream)))
     return y
 
 

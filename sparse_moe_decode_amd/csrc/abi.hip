@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -110,6 +111,89 @@ hipError_t flow_alloc(e0_model* m) {
   return e;
 }
 
+// Validates a tier description and fills the kernels' dimensions.
+int spec_dims(const e0_spec& p, Dims& dm) {
+  if (p.d_model <= 0 || p.n_experts <= 0 || p.top_k < 1 || p.top_k > 8 ||
+      p.top_k > p.n_experts || p.inter <= 0 || p.group <= 0)
+    return fail(E0_ERR_ARG, "spec: bad dimensions");
+  if (p.quant != E0_QUANT_SYMMETRIC && p.quant != E0_QUANT_AFFINE)
+    return fail(E0_ERR_ARG, "spec: unknown int4 codec %d", p.quant);
+  if (p.group % 32 || p.d_model % p.group || p.inter % p.group)
+    return fail(E0_ERR_SHAPE, "spec: group %d must be a multiple of 32 dividing d and I",
+                p.group);
+  if (!q4_shape_ok(p.d_model) || !q4_shape_ok(p.inter))
+    return fail(E0_ERR_SHAPE, "spec: d=%d or I=%d not supported by the int4 kernels",
+                p.d_model, p.inter);
+  if (p.shared_inter != 0 && p.shared_inter != p.inter)
+    return fail(E0_ERR_SHAPE, "spec: shared_inter must be 0 or equal to inter");
+  if (p.lora_rank < 0 || p.lora_rank > 64) return fail(E0_ERR_SHAPE, "spec: rank > 64");
+  if (p.n_experts > 512) return fail(E0_ERR_SHAPE, "spec: more than 512 experts");
+  if (p.head_hidden < 0 || p.head_hidden % 8 || (p.d_model + 2 * p.n_experts) % 8)
+    return fail(E0_ERR_SHAPE, "spec: head dims must be multiples of 8");
+  if (p.router_kind == E0_ROUTER_SIGMOID_GROUP) {
+    if (p.n_groups < 1 || p.n_groups > 64 || p.n_experts % p.n_groups ||
+        p.n_experts / p.n_groups < 2 || p.topk_groups < 1 || p.topk_groups > p.n_groups ||
+        p.top_k > p.topk_groups * (p.n_experts / p.n_groups))
+      return fail(E0_ERR_SHAPE, "spec: bad sigmoid-group parameters");
+  } else if (p.router_kind != E0_ROUTER_SOFTMAX_TOPK) {
+    return fail(E0_ERR_ARG, "spec: unknown router kind");
+  }
+  dm = Dims{};
+  dm.d = p.d_model; dm.E = p.n_experts; dm.K = p.top_k; dm.I = p.inter; dm.Is = p.shared_inter;
+  dm.P = p.head_hidden; dm.G = p.group; dm.r = p.lora_rank;
+  dm.lora_scale = p.lora_rank > 0 ? p.lora_alpha / (float)p.lora_rank : 0.0f;
+  dm.router_kind = p.router_kind; dm.norm_topk = p.norm_topk; dm.n_groups = p.n_groups;
+  dm.topk_groups = p.topk_groups; dm.route_scale = p.route_scale;
+  dm.eps = p.rms_eps > 0 ? p.rms_eps : 1e-6f;
+  dm.affine = p.quant == E0_QUANT_AFFINE;
+  return E0_OK;
+}
+
+// Byte size of the scratch for B tokens; with base != nullptr also carves
+// the buffers of *s out of [base, base + size) (every buffer 256-byte aligned).
+size_t scratch_layout(const Dims& dm, int B, char* base, Scratch* s) {
+  const int imax = dm.I > dm.Is ? dm.I : dm.Is;
+  const int rmax = dm.r > 1 ? dm.r : 1;
+  const size_t n_gu = (size_t)B * (dm.K + 1) * imax;
+  const size_t n_ax = (size_t)B * 3 * rmax;
+  const size_t n_d = (size_t)B * dm.d;
+  const size_t n_p = (size_t)B * (dm.P > 0 ? dm.P : 1);
+  const size_t n_e = (size_t)B * dm.E;
+  const size_t n_grp = 2 + 4 * (size_t)B * dm.K + 2 * (size_t)batched_max_tiles(B, dm.K, dm.E);
+  const size_t n_slot = (size_t)B * (dm.K + 1);
+  const size_t n_axp = (size_t)kLoraSlices * B * 2 * rmax;
+  auto up = [](size_t bytes) { return (bytes + 255) & ~(size_t)255; };
+  const size_t sizes[] = {up(n_gu * 4), up(n_ax * 4), up(n_d * 4), up(n_d * 2), up(n_p * 4),
+                          up(n_e * 4), up(n_e * 4), up((size_t)B * dm.K * 4),
+                          up((size_t)B * dm.K * 4), up(N_FLAGS * 4), up(n_grp * 4),
+                          up(n_axp * 4), up(n_slot * dm.d * 4)};
+  size_t total = 0;
+  for (size_t z : sizes) total += z;
+  if (base) {
+    char* q = base;
+    void* ptrs[13];
+    for (int i = 0; i < 13; ++i) {
+      ptrs[i] = q;
+      q += sizes[i];
+    }
+    s->max_tokens = B;
+    s->gu = (float*)ptrs[0];
+    s->ax = (float*)ptrs[1];
+    s->hattn = (float*)ptrs[2];
+    s->xn = (uint16_t*)ptrs[3];
+    s->hact = (float*)ptrs[4];
+    s->hlin = (float*)ptrs[5];
+    s->logits = (float*)ptrs[6];
+    s->sink_idx = (int32_t*)ptrs[7];
+    s->sink_w = (float*)ptrs[8];
+    s->flags = (int32_t*)ptrs[9];
+    s->grp = (int32_t*)ptrs[10];
+    s->axp = (float*)ptrs[11];
+    s->yk = (float*)ptrs[12];
+  }
+  return total;
+}
+
 }  // namespace
 
 extern "C" {
@@ -119,63 +203,19 @@ const char* e0_last_error(void) { return g_err.c_str(); }
 int e0_create(const e0_spec* spec, int32_t max_tokens, e0_ctx** out) {
   if (!spec || !out) return fail(E0_ERR_ARG, "e0_create: null argument");
   *out = nullptr;
-  const e0_spec& p = *spec;
-  if (p.d_model <= 0 || p.n_experts <= 0 || p.top_k < 1 || p.top_k > 8 ||
-      p.top_k > p.n_experts || p.inter <= 0 || p.group <= 0 || max_tokens < 1 ||
-      max_tokens > 8192)
-    return fail(E0_ERR_ARG, "e0_create: bad dimensions");
-  if (p.quant != E0_QUANT_SYMMETRIC && p.quant != E0_QUANT_AFFINE)
-    return fail(E0_ERR_ARG, "e0_create: unknown int4 codec %d", p.quant);
-  if (p.group % 32 || p.d_model % p.group || p.inter % p.group)
-    return fail(E0_ERR_SHAPE, "e0_create: group %d must be a multiple of 32 dividing d and I",
-                p.group);
-  if (!q4_shape_ok(p.d_model) || !q4_shape_ok(p.inter))
-    return fail(E0_ERR_SHAPE, "e0_create: d=%d or I=%d not supported by the int4 kernels",
-                p.d_model, p.inter);
-  if (p.shared_inter != 0 && p.shared_inter != p.inter)
-    return fail(E0_ERR_SHAPE, "e0_create: shared_inter must be 0 or equal to inter");
-  if (p.lora_rank < 0 || p.lora_rank > 64) return fail(E0_ERR_SHAPE, "e0_create: rank > 64");
-  if (p.n_experts > 512) return fail(E0_ERR_SHAPE, "e0_create: more than 512 experts");
-  if (p.head_hidden < 0 || p.head_hidden % 8 || (p.d_model + 2 * p.n_experts) % 8)
-    return fail(E0_ERR_SHAPE, "e0_create: head dims must be multiples of 8");
-  if (p.router_kind == E0_ROUTER_SIGMOID_GROUP) {
-    if (p.n_groups < 1 || p.n_groups > 64 || p.n_experts % p.n_groups ||
-        p.n_experts / p.n_groups < 2 || p.topk_groups < 1 || p.topk_groups > p.n_groups ||
-        p.top_k > p.topk_groups * (p.n_experts / p.n_groups))
-      return fail(E0_ERR_SHAPE, "e0_create: bad sigmoid-group parameters");
-  } else if (p.router_kind != E0_ROUTER_SOFTMAX_TOPK) {
-    return fail(E0_ERR_ARG, "e0_create: unknown router kind");
-  }
+  if (max_tokens < 1 || max_tokens > 8192)
+    return fail(E0_ERR_ARG, "e0_create: max_tokens %d outside [1, 8192]", max_tokens);
+  Dims dm;
+  int rc;
+  if ((rc = spec_dims(*spec, dm))) return rc;
   e0_ctx* c = new e0_ctx();
-  c->spec = p;
-  Dims& dm = c->dm;
-  dm.d = p.d_model; dm.E = p.n_experts; dm.K = p.top_k; dm.I = p.inter; dm.Is = p.shared_inter;
-  dm.P = p.head_hidden; dm.G = p.group; dm.r = p.lora_rank;
-  dm.lora_scale = p.lora_rank > 0 ? p.lora_alpha / (float)p.lora_rank : 0.0f;
-  dm.router_kind = p.router_kind; dm.norm_topk = p.norm_topk; dm.n_groups = p.n_groups;
-  dm.topk_groups = p.topk_groups; dm.route_scale = p.route_scale;
-  dm.eps = p.rms_eps > 0 ? p.rms_eps : 1e-6f;
-  dm.affine = p.quant == E0_QUANT_AFFINE;
+  c->spec = *spec;
+  c->dm = dm;
   if (hipGetDevice(&c->device) != hipSuccess) {
     delete c;
     return fail(E0_ERR_HIP, "e0_create: no current HIP device");
   }
-
-  const int B = max_tokens;
-  const int imax = dm.I > dm.Is ? dm.I : dm.Is;
-  const int rmax = dm.r > 1 ? dm.r : 1;
-  const size_t n_gu = (size_t)B * (dm.K + 1) * imax;
-  const size_t n_ax = (size_t)B * 3 * rmax;
-  const size_t n_d = (size_t)B * dm.d;
-  const size_t n_p = (size_t)B * (dm.P > 0 ? dm.P : 1);
-  const size_t n_e = (size_t)B * dm.E;
-  auto up = [](size_t bytes) { return (bytes + 255) & ~(size_t)255; };
-  const size_t n_grp = 2 + 4 * (size_t)B * dm.K + 2 * (size_t)batched_max_tiles(B, dm.K, dm.E);
-  const size_t n_slot = (size_t)B * (dm.K + 1);
-  const size_t n_axp = (size_t)kLoraSlices * B * 2 * rmax;
-  const size_t bytes = up(n_gu * 4) + up(n_ax * 4) + up(n_d * 4) + up(n_d * 2) + up(n_p * 4) +
-                       2 * up(n_e * 4) + 2 * up((size_t)B * dm.K * 4) + up(N_FLAGS * 4) +
-                       up(n_grp * 4) + up(n_axp * 4) + up(n_slot * dm.d * 4);
+  const size_t bytes = scratch_layout(dm, max_tokens, nullptr, nullptr);
   hipError_t e = hipMalloc(&c->block, bytes);
   if (e != hipSuccess) {
     delete c;
@@ -187,22 +227,7 @@ int e0_create(const e0_spec* spec, int32_t max_tokens, e0_ctx** out) {
     delete c;
     return hip_fail(e, "e0_create: hipMemset");
   }
-  char* q = (char*)c->block;
-  Scratch& s = c->s;
-  s.max_tokens = B;
-  s.gu = (float*)q; q += up(n_gu * 4);
-  s.ax = (float*)q; q += up(n_ax * 4);
-  s.hattn = (float*)q; q += up(n_d * 4);
-  s.xn = (uint16_t*)q; q += up(n_d * 2);
-  s.hact = (float*)q; q += up(n_p * 4);
-  s.hlin = (float*)q; q += up(n_e * 4);
-  s.logits = (float*)q; q += up(n_e * 4);
-  s.sink_idx = (int32_t*)q; q += up((size_t)B * dm.K * 4);
-  s.sink_w = (float*)q; q += up((size_t)B * dm.K * 4);
-  s.flags = (int32_t*)q; q += up(N_FLAGS * 4);
-  s.grp = (int32_t*)q; q += up(n_grp * 4);
-  s.axp = (float*)q; q += up(n_axp * 4);
-  s.yk = (float*)q;
+  scratch_layout(dm, max_tokens, (char*)c->block, &c->s);
   *out = c;
   return E0_OK;
 }
@@ -242,10 +267,9 @@ int check_q4(const e0_q4& m, bool affine, const char* what) {
   return E0_OK;
 }
 
-int make_pool(const e0_ctx* ctx, const e0_experts* ex, const int32_t* slot_of, Pool& p) {
+int make_pool(const Dims& dm, const e0_experts* ex, const int32_t* slot_of, Pool& p) {
   if (!ex) return fail(E0_ERR_ARG, "routed pool is null");
   int rc;
-  const Dims& dm = ctx->dm;
   const bool af = dm.affine != 0;
   if ((rc = check_q4(ex->gate, af, "routed gate")) || (rc = check_q4(ex->up, af, "routed up")) ||
       (rc = check_q4(ex->down, af, "routed down")))
@@ -262,12 +286,12 @@ int make_pool(const e0_ctx* ctx, const e0_experts* ex, const int32_t* slot_of, P
   return E0_OK;
 }
 
-int make_shared(const e0_ctx* ctx, const e0_shared* sh, SharedW& w) {
+int make_shared(const Dims& dm, const e0_shared* sh, SharedW& w) {
   std::memset(&w, 0, sizeof(w));
   if (!sh) return E0_OK;
-  if (ctx->dm.Is == 0) return fail(E0_ERR_ARG, "shared expert given but shared_inter = 0");
+  if (dm.Is == 0) return fail(E0_ERR_ARG, "shared expert given but shared_inter = 0");
   int rc;
-  const bool af = ctx->dm.affine != 0;
+  const bool af = dm.affine != 0;
   if ((rc = check_q4(sh->gate, af, "shared gate")) || (rc = check_q4(sh->up, af, "shared up")) ||
       (rc = check_q4(sh->down, af, "shared down")))
     return rc;
@@ -276,7 +300,7 @@ int make_shared(const e0_ctx* ctx, const e0_shared* sh, SharedW& w) {
   w.down = {sh->down.q, sh->down.s, sh->down.b};
   const bool lg = sh->lgate.a && sh->lgate.b, lu = sh->lup.a && sh->lup.b,
              ld = sh->ldown.a && sh->ldown.b;
-  if ((lg || lu || ld) && ctx->dm.r == 0) return fail(E0_ERR_ARG, "LoRA given but rank = 0");
+  if ((lg || lu || ld) && dm.r == 0) return fail(E0_ERR_ARG, "LoRA given but rank = 0");
   if (lg != lu) return fail(E0_ERR_ARG, "gate and up LoRA must be given together");
   for (const uint16_t* a : {sh->lgate.a, sh->lup.a, sh->ldown.a})
     if (a && !aligned(a, 16)) return fail(E0_ERR_ALIGN, "LoRA A must be 16-byte aligned");
@@ -287,26 +311,51 @@ int make_shared(const e0_ctx* ctx, const e0_shared* sh, SharedW& w) {
 }
 
 // Shared-expert LoRA A products for the gate/up (input x fp16).
-hipError_t lora_a_x(const e0_ctx* ctx, const SharedW& sh, const uint16_t* x, int B,
-                    hipStream_t st) {
+hipError_t lora_a_x(const Dims& dm, const Scratch& s, const SharedW& sh, const uint16_t* x,
+                    int B, hipStream_t st) {
   if (!sh.present || !sh.ag) return hipSuccess;
-  const int rmax = ctx->dm.r > 1 ? ctx->dm.r : 1;
+  const int rmax = dm.r > 1 ? dm.r : 1;
   const uint16_t* A[2] = {sh.ag, sh.au};
   const int slots[2] = {0, rmax};
-  return launch_lora_a(2, A, slots, ctx->dm.d, ctx->dm.r, x, nullptr, ctx->dm.d, B, ctx->s.ax,
-                       3 * rmax, st);
+  return launch_lora_a(2, A, slots, dm.d, dm.r, x, nullptr, dm.d, B, s.ax, 3 * rmax, st);
 }
 
 // Down LoRA A product on the shared expert's fp32 SwiGLU output.
-hipError_t lora_a_down(const e0_ctx* ctx, const SharedW& sh, int B, hipStream_t st) {
+hipError_t lora_a_down(const Dims& dm, const Scratch& s, const SharedW& sh, int B,
+                       hipStream_t st) {
   if (!sh.present || !sh.ad) return hipSuccess;
-  const Dims& dm = ctx->dm;
   const int rmax = dm.r > 1 ? dm.r : 1;
   const int imax = dm.I > dm.Is ? dm.I : dm.Is;
   const uint16_t* A[1] = {sh.ad};
   const int slots[1] = {2 * rmax};
-  return launch_lora_a(1, A, slots, dm.Is, dm.r, nullptr, ctx->s.gu + (int64_t)dm.K * imax,
-                       (int64_t)(dm.K + 1) * imax, B, ctx->s.ax, 3 * rmax, st);
+  return launch_lora_a(1, A, slots, dm.Is, dm.r, nullptr, s.gu + (int64_t)dm.K * imax,
+                       (int64_t)(dm.K + 1) * imax, B, s.ax, 3 * rmax, st);
+}
+
+// The routed experts and the shared expert of n_tokens tokens on scratch s
+// (sized for at least n_tokens).
+int moe_run(const Dims& dm, const Scratch& s, const e0_experts* routed, const int32_t* slot_of,
+            const e0_shared* shared, const uint16_t* x, const int32_t* idx, const float* w,
+            int n_tokens, uint16_t* y, hipStream_t st) {
+  Pool pool;
+  SharedW sh;
+  int rc;
+  if ((rc = make_pool(dm, routed, slot_of, pool)) || (rc = make_shared(dm, shared, sh))) return rc;
+  hipError_t e;
+  if (n_tokens >= kBatchedMin && batched_supported(dm)) {
+    // the whole batch through the grouped MFMA path: each expert's weights
+    // are read once for all of its tokens
+    if ((e = launch_batched(dm, pool, sh, x, idx, w, n_tokens, y, s, st)) != hipSuccess)
+      return hip_fail(e, "batched");
+    return E0_OK;
+  }
+  if ((e = lora_a_x(dm, s, sh, x, n_tokens, st)) != hipSuccess) return hip_fail(e, "lora A");
+  if ((e = launch_gate_up(dm, pool, sh, x, idx, n_tokens, s, st)) != hipSuccess)
+    return hip_fail(e, "gate/up");
+  if ((e = lora_a_down(dm, s, sh, n_tokens, st)) != hipSuccess) return hip_fail(e, "lora A down");
+  if ((e = launch_down(dm, pool, sh, idx, w, n_tokens, nullptr, y, s, st)) != hipSuccess)
+    return hip_fail(e, "down");
+  return E0_OK;
 }
 
 }  // namespace
@@ -321,29 +370,8 @@ int moe_int4_decode(e0_ctx* ctx, const e0_experts* routed, const int32_t* slot_o
   if (n_tokens < 0 || n_tokens > ctx->s.max_tokens)
     return fail(E0_ERR_ARG, "moe_int4_decode: n_tokens %d outside [0, %d]", n_tokens,
                 ctx->s.max_tokens);
-  Pool pool;
-  SharedW sh;
-  int rc;
-  if ((rc = make_pool(ctx, routed, slot_of, pool)) || (rc = make_shared(ctx, shared, sh)))
-    return rc;
-  hipStream_t st = (hipStream_t)stream;
-  hipError_t e;
-  const Dims& dm = ctx->dm;
-  if (n_tokens >= kBatchedMin && batched_supported(dm)) {
-    // the whole batch through the grouped MFMA path: each expert's weights
-    // are read once for all of its tokens
-    if ((e = launch_batched(dm, pool, sh, x, idx, w, n_tokens, y, ctx->s, st)) != hipSuccess)
-      return hip_fail(e, "batched");
-    return E0_OK;
-  }
-  if ((e = lora_a_x(ctx, sh, x, n_tokens, st)) != hipSuccess) return hip_fail(e, "lora A");
-  if ((e = launch_gate_up(ctx->dm, pool, sh, x, idx, n_tokens, ctx->s, st)) != hipSuccess)
-    return hip_fail(e, "gate/up");
-  if ((e = lora_a_down(ctx, sh, n_tokens, st)) != hipSuccess) return hip_fail(e, "lora A down");
-  if ((e = launch_down(ctx->dm, pool, sh, idx, w, n_tokens, nullptr, y, ctx->s, st)) !=
-      hipSuccess)
-    return hip_fail(e, "down");
-  return E0_OK;
+  return moe_run(ctx->dm, ctx->s, routed, slot_of, shared, x, idx, w, n_tokens, y,
+                 (hipStream_t)stream);
 }
 
 int lora_delta(e0_ctx* ctx, const uint16_t* A, const uint16_t* Bm, int32_t in_dim,
@@ -432,8 +460,8 @@ int e0_model_create(e0_ctx* ctx, const e0_layer* layers, int32_t n_layers, e0_mo
     Pool p;
     SharedW sw;
     int rc;
-    if ((rc = make_pool(ctx, &L.experts, L.slot_of, p)) ||
-        (rc = make_shared(ctx, L.shared.gate.q ? &L.shared : nullptr, sw)))
+    if ((rc = make_pool(ctx->dm, &L.experts, L.slot_of, p)) ||
+        (rc = make_shared(ctx->dm, L.shared.gate.q ? &L.shared : nullptr, sw)))
       return fail(rc, "layer %d: %s", l, g_err.c_str());
     if (L.head.fc1 && (rc = check_head(ctx, &L.head)))
       return fail(rc, "layer %d: %s", l, g_err.c_str());
@@ -461,8 +489,8 @@ int e0_model_create(e0_ctx* ctx, const e0_layer* layers, int32_t n_layers, e0_mo
   for (int l = 0; l < n_layers; ++l) {
     const e0_layer& L = layers[l];
     LayerDev& t = table[l];
-    make_pool(ctx, &L.experts, L.slot_of, t.pool);
-    make_shared(ctx, L.shared.gate.q ? &L.shared : nullptr, t.sh);
+    make_pool(ctx->dm, &L.experts, L.slot_of, t.pool);
+    make_shared(ctx->dm, L.shared.gate.q ? &L.shared : nullptr, t.sh);
     t.router = L.router;
     t.router_bias = L.router_bias;
     t.head = HeadW{L.head.fc1, L.head.fc2, L.head.lin, L.head.bias};
@@ -696,8 +724,8 @@ int layer_step(e0_ctx* ctx, e0_model* model, int32_t layer_begin, int32_t layer_
     const e0_layer& Ly = model->layers[l];
     Pool pool;
     SharedW sh;
-    make_pool(ctx, &Ly.experts, Ly.slot_of, pool);
-    make_shared(ctx, Ly.shared.gate.q ? &Ly.shared : nullptr, sh);
+    make_pool(ctx->dm, &Ly.experts, Ly.slot_of, pool);
+    make_shared(ctx->dm, Ly.shared.gate.q ? &Ly.shared : nullptr, sh);
     const uint16_t* hin = h + (int64_t)(l - layer_begin) * dm.d;
     uint16_t* hout = h + (int64_t)(l - layer_begin + 1) * dm.d;
     int32_t* eidx = state->exec_idx + ((int64_t)cur * L + l) * K;
@@ -716,10 +744,10 @@ int layer_step(e0_ctx* ctx, e0_model* model, int32_t layer_begin, int32_t layer_
       if (e == hipSuccess) e = launch_route(dm, s.logits, Ly.router_bias, 1, eidx, ew, s.flags, st);
       if (e != hipSuccess) return hip_fail(e, "layer_step router");
     }
-    if ((e = lora_a_x(ctx, sh, xn, 1, st)) != hipSuccess) return hip_fail(e, "lora A");
+    if ((e = lora_a_x(ctx->dm, ctx->s, sh, xn, 1, st)) != hipSuccess) return hip_fail(e, "lora A");
     if ((e = launch_gate_up(dm, pool, sh, xn, eidx, 1, s, st)) != hipSuccess)
       return hip_fail(e, "gate/up");
-    if ((e = lora_a_down(ctx, sh, 1, st)) != hipSuccess) return hip_fail(e, "lora A down");
+    if ((e = lora_a_down(ctx->dm, ctx->s, sh, 1, st)) != hipSuccess) return hip_fail(e, "lora A down");
     if ((e = launch_down(dm, pool, sh, eidx, ew, 1, s.hattn, hout, s, st)) != hipSuccess)
       return hip_fail(e, "down");
     if (Ly.head.fc1) {
@@ -986,6 +1014,69 @@ int stage_layer(e0_ctx* ctx, const void* host_layer, void* hbm_layer, void* stre
     if (e != hipSuccess) return hip_fail(e, "stage_layer: event");
   }
   return E0_OK;
+}
+
+}  // extern "C"
+
+// ---- moe_int4_decode_static: the same step on a workspace the library
+// never allocates ------------------------------------------------------------
+
+namespace {
+
+// Workspace of moe_int4_decode_static. Each GPU the library runs on holds its
+// own copy until the process ends; in host code `scratch` names a host-side
+// stand-in, so only the address from hipGetSymbolAddress reaches kernels.
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_static_mu;
+char* g_static_ptr[kMaxDevices];
+
+// Device address of the current device's copy (looked up once per device).
+int static_scratch(int dev, char** out) {
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (!g_static_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "moe_int4_decode_static: hipGetSymbolAddress");
+    g_static_ptr[dev] = (char*)ptr;
+  }
+  *out = g_static_ptr[dev];
+  return E0_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_int4_decode_static(const e0_spec* spec, const e0_experts* routed, const int32_t* slot_of,
+                           const e0_shared* shared, const uint16_t* x, const int32_t* idx,
+                           const float* w, int32_t n_tokens, uint16_t* y, int32_t* flags,
+                           void* stream) {
+  if (!spec || !x || !idx || !w || !y)
+    return fail(E0_ERR_ARG, "moe_int4_decode_static: null argument");
+  if (n_tokens < 0) return fail(E0_ERR_ARG, "moe_int4_decode_static: n_tokens %d < 0", n_tokens);
+  if (n_tokens == 0) return E0_OK;
+  Dims dm;
+  int rc;
+  if ((rc = spec_dims(*spec, dm))) return rc;
+  const size_t need = scratch_layout(dm, n_tokens, nullptr, nullptr);
+  if (need > kStaticScratchBytes)
+    return fail(E0_ERR_SHAPE,
+                "moe_int4_decode_static: %d tokens of this tier need %zu bytes of workspace; "
+                "the static workspace holds %zu",
+                n_tokens, need, kStaticScratchBytes);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(E0_ERR_HIP, "moe_int4_decode_static: no device");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(E0_ERR_ARG, "moe_int4_decode_static: device %d beyond %d", dev, kMaxDevices);
+  char* base = nullptr;
+  if ((rc = static_scratch(dev, &base))) return rc;
+  Scratch s;
+  scratch_layout(dm, n_tokens, base, &s);
+  if (flags) s.flags = flags;
+  return moe_run(dm, s, routed, slot_of, shared, x, idx, w, n_tokens, y, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -67,3 +67,25 @@ def test_host_validation_rejects_bad_specs():
     assert lib.e0_create(None, 4, C.byref(h)) == -1
     assert lib.e0_bundle_bytes(C.byref(api.make_spec(synth.dims("35b")))) == 1671168
     assert lib.e0_bundle_bytes(C.byref(api.make_spec(synth.dims("8b")))) == 1253376
+
+
+def test_static_entry_point_checks_its_workspace_size_first():
+    """moe_int4_decode_static validates the spec and the workspace it needs
+    before any device call (the pointers below are never dereferenced)."""
+    from sparse_moe_decode_amd import api, synth
+    lib = api._lib
+    ex = api.e0_experts()
+    p = C.c_void_p(4096)
+    spec = api.make_spec(synth.dims("35b"))
+    assert lib.moe_int4_decode_static(C.byref(spec), C.byref(ex), None, None, p, p, p, 4000, p,
+                                      None, None) == -2
+    assert b"static workspace" in lib.e0_last_error()
+    assert lib.moe_int4_decode_static(C.byref(spec), C.byref(ex), None, None, p, p, p, -1, p,
+                                      None, None) == -1
+    bad = api.make_spec(dict(synth.dims("35b"), K=9))
+    assert lib.moe_int4_decode_static(C.byref(bad), C.byref(ex), None, None, p, p, p, 1, p,
+                                      None, None) == -1
+    assert lib.moe_int4_decode_static(None, C.byref(ex), None, None, p, p, p, 1, p, None,
+                                      None) == -1
+    assert lib.moe_int4_decode_static(C.byref(spec), C.byref(ex), None, None, p, p, p, 0, p,
+                                      None, None) == 0
