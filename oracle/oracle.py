@@ -329,6 +329,37 @@ def route(dims: dict, logits, bias=None):
     return idx, w
 
 
+def route_scores(dims: dict, logits, bias=None) -> np.ndarray:
+    """The score the tier's routing ranks experts by [MW App. A]: the logit for
+    softmax-top-K (softmax is monotone in it), the biased sigmoid sigma + bias
+    for sigmoid-group."""
+    lg = np.asarray(logits, np.float64)
+    if dims.get("router_kind", ROUTER_SOFTMAX_TOPK) == ROUTER_SOFTMAX_TOPK:
+        return lg.copy()
+    sig = 1.0 / (1.0 + np.exp(-lg))
+    return sig + (0.0 if bias is None else np.asarray(bias, np.float64))
+
+
+def route_set_weights(dims: dict, logits, idx, bias=None) -> np.ndarray:
+    """Routing weights [MW App. A] that the tier's routing function gives a
+    set `idx` (in its order), whichever set that is: softmax-top-K takes the
+    softmax over all E logits and, when normalised, renormalises it over the
+    set; sigmoid-group takes scale * sigma / (sum of sigma over the set +
+    1e-20) on the raw sigmoid (the selection bias only ranks). Used to hold a
+    set that differs from the oracle's own under a near tie to the weights
+    the routing function assigns that set."""
+    lg = np.asarray(logits, np.float64)
+    idx = np.asarray(idx, np.int64)
+    if dims.get("router_kind", ROUTER_SOFTMAX_TOPK) == ROUTER_SOFTMAX_TOPK:
+        g = np.exp(lg - lg.max())
+        g = g / g.sum()
+        sel = g[idx]
+        return sel / sel.sum() if dims.get("norm_topk", 1) else sel
+    sig = 1.0 / (1.0 + np.exp(-lg))
+    sel = sig[idx]
+    return float(dims.get("route_scale", 1.0)) * sel / (sel.sum() + 1e-20)
+
+
 class LayerOracle:
     """One MoE layer for the oracle: weights are held as numpy arrays.
 

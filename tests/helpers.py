@@ -7,6 +7,8 @@ operations, independently of both the oracle and the HIP library.
 
 from __future__ import annotations
 
+import itertools
+
 import numpy as np
 
 # Output tolerance for fp16 results against the fp64 oracle:
@@ -82,10 +84,12 @@ def routing_set_ok(dims: dict, logits: np.ndarray, got: np.ndarray, bias=None,
                    gap=TIE_GAP) -> bool:
     """Near-tie acceptance for a routed set, given the oracle's fp64 logits.
 
-    Softmax-top-K: a top-K of the logits up to `gap`. Sigmoid-group: the
-    groups the set touches must be among the top groups up to `gap` on the
-    group score, and the set must be a top-K of the biased score up to `gap`
-    within the union of the oracle's kept groups and the touched groups.
+    Softmax-top-K: a top-K of the logits up to `gap`. Sigmoid-group: there
+    must be a choice S of topk_groups groups that holds every group the set
+    touches and is a top-topk_groups of the group scores up to `gap` (its
+    lowest score at least the highest score outside S minus `gap`), such that
+    the set is a top-K of the biased scores within S up to `gap`. Every such
+    S is tried (C(8, 4) = 70 at most for the tiers here).
     """
     K, E = dims["K"], dims["E"]
     if dims["router_kind"] == 0:
@@ -95,14 +99,18 @@ def routing_set_ok(dims: dict, logits: np.ndarray, got: np.ndarray, bias=None,
     sig = 1.0 / (1.0 + np.exp(-np.asarray(logits, np.float64)))
     sel = sig + (0.0 if bias is None else np.asarray(bias, np.float64))
     gs = np.sort(sel.reshape(n, per), axis=1)[:, -2:].sum(axis=1)
-    touched = np.unique(np.asarray(got) // per)
-    if touched.size > Gk:
+    touched = sorted(set((np.asarray(got) // per).tolist()))
+    if len(touched) > Gk:
         return False
-    gth = np.sort(gs)[::-1][Gk - 1]
-    if gs[touched].min() < gth - gap:
-        return False
-    kept = set(np.argsort(-gs, kind="stable")[:Gk].tolist()) | set(touched.tolist())
-    allowed = np.zeros(E, bool)
-    for g in kept:
-        allowed[g * per:(g + 1) * per] = True
-    return topk_set_ok(sel, got, K, allowed=allowed, gap=gap)
+    others = [g for g in range(n) if g not in touched]
+    for extra in itertools.combinations(others, Gk - len(touched)):
+        S = set(touched) | set(extra)
+        outside = [g for g in range(n) if g not in S]
+        if outside and gs[list(S)].min() < gs[outside].max() - gap:
+            continue
+        allowed = np.zeros(E, bool)
+        for g in S:
+            allowed[g * per:(g + 1) * per] = True
+        if topk_set_ok(sel, got, K, allowed=allowed, gap=gap):
+            return True
+    return False

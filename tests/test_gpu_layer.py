@@ -25,7 +25,9 @@ def api():
 
 
 def _run_and_check(api, orc, tier, roles, seed, T, check_layers, rho=0.5, zero_mean=False,
-                   path="auto"):
+                   path="auto", mutate=None):
+    """mutate(l, lw) -> lw, if given, reshapes each layer's host weights
+    before upload (the checker sees the same weights)."""
     import torch
     from sparse_moe_decode_amd import workloads as wl
     dm = synth.dims(tier)
@@ -33,6 +35,8 @@ def _run_and_check(api, orc, tier, roles, seed, T, check_layers, rho=0.5, zero_m
     layers, keep = [], {}
     for l, role in enumerate(roles):
         lw = synth.layer(seed, l, dm, role, zero_mean=zero_mean)
+        if mutate is not None:
+            lw = mutate(l, lw)
         if l in check_layers:
             keep[l] = lw
         if L > 2:
@@ -70,8 +74,8 @@ def _run_and_check(api, orc, tier, roles, seed, T, check_layers, rho=0.5, zero_m
                       host(state.head_logits).copy())
         prev_exec = exec_idx
     print(f"{tier} {path} L={L}: {checker.steps} layer-steps checked, worst error ratio "
-          f"{checker.worst:.3f}, re-anchored router sets {checker.reanchored}, "
-          f"x elements one ulp off {checker.x_ulp_diffs}")
+          f"{checker.worst:.3f}, re-anchored router sets {checker.reanchored}, predictions "
+          f"{checker.pred_reanchored}, x elements one ulp off {checker.x_ulp_diffs}")
     model.close()
     ctx.close()
     return checker
@@ -218,4 +222,58 @@ def test_layer_step_64_layers_persistent(api, orc):
     assert api.device_status(ctx) == 0
     assert bool(torch.isfinite(h2.float()).all())
     model2.close()
+    ctx.close()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("path", ["flow", "persistent", "phases"])
+def test_layer_step_bitwise_deterministic(api, path):
+    """Two runs of the 35B stack (40 layers, three tokens) from the same
+    state give the same bits: every layer's residual, executed set and
+    weights, head logits and prediction. The cross-workgroup exchanges are
+    where run-to-run variation would enter."""
+    import torch
+    from sparse_moe_decode_amd import workloads as wl
+    tier, seed, T = "35b", 47, 3
+    dm = synth.dims(tier)
+    roles = synth.stack_roles(tier)
+    L = len(roles)
+    layers = []
+    for l, role in enumerate(roles):
+        if l % 8 == 0:
+            announce("upload", tier, f"layer {l}/{L}")
+        lw = synth.layer(seed, l, dm, role, zero_mean=True)
+        layers.append(dict(routed=wl.tree_to_dev(lw["routed"]), shared=wl.tree_to_dev(lw["shared"]),
+                           attn=dev(lw["attn"]),
+                           router=None if lw["router"] is None else dev(lw["router"]),
+                           router_bias=None, head=wl.tree_to_dev(lw["head"])))
+    ctx = api.Context(dm, max_tokens=1)
+    model = api.Model(ctx, layers)
+    model.set_path({"persistent": api.PATH_PERSISTENT, "flow": api.PATH_FLOW,
+                    "phases": api.PATH_PHASES}[path])
+    idx0, w0 = wl.initial_routing(tier, seed, L)
+    toks = wl.token_inputs(tier, seed, T)
+    runs = []
+    for run in range(2):
+        state = api.State(dm, L)
+        state.route_idx[0].copy_(torch.from_numpy(idx0))
+        state.route_w[0].copy_(torch.from_numpy(w0))
+        h = torch.zeros((T, L + 1, dm["d"]), dtype=torch.float16, device="cuda")
+        got = []
+        for t in range(T):
+            announce("layer_step determinism", tier, path, f"run {run} token {t}")
+            h[t, 0].copy_(torch.from_numpy(toks[t]))
+            api.layer_step(ctx, model, 0, L, state, t, h[t])
+            torch.cuda.synchronize()
+            assert api.device_status(ctx) == 0
+            cur, nxt = t & 1, (t + 1) & 1
+            got.append([host(x).copy() for x in (state.exec_idx[cur], state.exec_w[cur],
+                                                  state.route_idx[nxt], state.route_w[nxt],
+                                                  state.head_logits, state.x_trace)])
+        got.append([host(h).view(np.uint16).copy()])
+        runs.append(got)
+    for a, b in zip(runs[0], runs[1]):
+        for x, y in zip(a, b):
+            assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), f"{path}: runs differ"
+    model.close()
     ctx.close()

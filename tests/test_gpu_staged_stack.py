@@ -45,14 +45,30 @@ def test_staged_stack_matches_oracle(api, orc, tier, T, reserve, group, quant):
     units (staging copies then run beside the layers); group = predicted
     layers per launch; quant = 1 stages affine bundles (scales, then biases)
     and runs the layers one kernel per phase."""
+    dm = synth.dims(tier, quant=1) if quant else synth.dims(tier)
+    _staged_run(api, orc, tier, ROLES, dm, T, reserve, group, quant)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("path", ["persistent", "flow"])
+def test_staged_stack_bench_shape(api, orc, path):
+    """The benchmark's staged configuration: the 35B stack's 40 layers (own
+    routers on 0-6 and 39, 32 predicted layers staged through slots),
+    16 predicted layers per launch and 32 compute units left to the copies,
+    with each layer kernel forced; 32 experts per layer instead of 256 keep
+    the host pool small, every other shape is the 35B tier's. Every
+    layer-step of three tokens against the oracle."""
+    dm = synth.dims("35b", E=32)
+    _staged_run(api, orc, "35b", synth.stack_roles("35b"), dm, 3, 32, 16, 0, seed=45, path=path)
+
+
+def _staged_run(api, orc, tier, roles, dm, T, reserve, group, quant, seed=41, path="auto"):
     import torch
     from sparse_moe_decode_amd import pipeline
     from sparse_moe_decode_amd import workloads as wl
-    dm = synth.dims(tier, quant=1) if quant else synth.dims(tier)
-    E, K, L = dm["E"], dm["K"], len(ROLES)
+    E, K, L = dm["E"], dm["K"], len(roles)
     n_slots = 2 * K
-    seed = 41
-    cons = [l for l in range(L) if not ROLES[l]["router"]]
+    cons = [l for l in range(L) if not roles[l]["router"]]
     ci = {l: i for i, l in enumerate(cons)}
     ctx = api.Context(dm, max_tokens=1)
     bundle = ctx.bundle_bytes()
@@ -61,8 +77,9 @@ def test_staged_stack_matches_oracle(api, orc, tier, T, reserve, group, quant):
     slot_of = torch.empty((len(cons), E), dtype=torch.int32, device="cuda")
     slot_expert = torch.empty((len(cons), n_slots), dtype=torch.int32, device="cuda")
     layers, keep = [], {}
-    for l, role in enumerate(ROLES):
-        announce("upload", tier, f"layer {l}/{L}")
+    for l, role in enumerate(roles):
+        if l % 8 == 0 or L < 8:
+            announce("upload", tier, f"E={E}", f"layer {l}/{L}")
         lw = synth.layer(seed, l, dm, role, zero_mean=True)
         keep[l] = lw
         lay = dict(shared=wl.tree_to_dev(lw["shared"]), attn=dev(lw["attn"]),
@@ -79,13 +96,17 @@ def test_staged_stack_matches_oracle(api, orc, tier, T, reserve, group, quant):
     host_dev = host_pool.to("cuda")
     stager = api.Stager(ctx, host_pool, len(cons), n_slots, hbm, slot_of, slot_expert)
     model = api.Model(ctx, layers)
+    model.set_path({"auto": api.PATH_AUTO, "persistent": api.PATH_PERSISTENT,
+                    "flow": api.PATH_FLOW}[path])
     state = api.State(dm, L)
-    idx0, w0 = wl.initial_routing(tier, seed, L)
+    rng = synth.rng_for(seed, 10_000)
+    idx0 = np.stack([synth.random_set(rng, E, K) for _ in range(L)])
+    w0 = np.stack([synth.random_weights(rng, K) for _ in range(L)])
     state.route_idx[0].copy_(torch.from_numpy(idx0))
     state.route_w[0].copy_(torch.from_numpy(w0))
     toks = wl.token_inputs(tier, seed, T, rho=0.5)  # sets change between tokens: copies happen
-    checker = StackChecker(orc, tier, seed, ROLES, list(range(L)), keep, zero_mean=True,
-                           quant=quant)
+    checker = StackChecker(orc, tier, seed, roles, list(range(L)), keep, zero_mean=True,
+                           quant=quant, dims=dm)
     pipe = pipeline.StagedStack(ctx, model, state, stager, cons, L, reserve_cus=reserve,
                                 group=group)
 
@@ -98,8 +119,8 @@ def test_staged_stack_matches_oracle(api, orc, tier, T, reserve, group, quant):
     prev_exec = None
     h = torch.zeros((L + 1, dm["d"]), dtype=torch.float16, device="cuda")
     for t in range(T):
-        announce("staged layer_step", tier, f"L={L} reserve={reserve} group={group} quant={quant}",
-                 f"token {t}")
+        announce("staged layer_step", tier, path,
+                 f"L={L} E={E} reserve={reserve} group={group} quant={quant}", f"token {t}")
         h[0].copy_(torch.from_numpy(toks[t]))
         pipe.run_token(t, h)
         torch.cuda.synchronize()
@@ -126,8 +147,8 @@ def test_staged_stack_matches_oracle(api, orc, tier, T, reserve, group, quant):
                 if e >= 0:
                     assert torch.equal(hbm[i, s], host_dev[i, e]), f"t={t} l={l} slot {s}"
     assert stager.copies() == copies, "bundle copies counted by the stager"
-    print(f"{tier} staged L={L}: {checker.steps} layer-steps checked, worst error ratio "
-          f"{checker.worst:.3f}, {copies} bundle copies")
+    print(f"{tier} staged {path} L={L} E={E}: {checker.steps} layer-steps checked, worst error "
+          f"ratio {checker.worst:.3f}, {copies} bundle copies, re-anchored {checker.reanchored}")
     stager.close()
     model.close()
     ctx.close()

@@ -124,3 +124,36 @@ def test_routing_dispatch_by_tier(orc):
                                              dm["topk_groups"], dm["route_scale"])
         assert idx.tolist() == i2.tolist()
         np.testing.assert_allclose(w, w2, rtol=1e-15)
+
+
+def test_set_weights_match_the_routing_function_on_its_own_set(orc):
+    """route_set_weights (numpy) on the set route() picks reproduces route()'s
+    weights (the C++ routine) on every tier and both normalisations."""
+    from sparse_moe_decode_amd import synth
+    rng = np.random.default_rng(15)
+    for tier in ("tiny", "8b", "35b"):
+        for norm in (1, 0):
+            dm = dict(synth.dims(tier), norm_topk=norm)
+            for _ in range(10):
+                lg = rng.normal(0, 1.5, dm["E"])
+                bias = rng.normal(0, 0.02, dm["E"]).astype(np.float32)
+                b = bias if dm["router_kind"] else None
+                idx, w = orc.route(dm, lg, b)
+                np.testing.assert_allclose(orc.route_set_weights(dm, lg, idx, b), w, rtol=1e-13)
+
+
+def test_set_weights_closed_forms(orc):
+    """Any set, not only the top-K: library softmax and sigmoid."""
+    lg = np.array([0.3, -1.2, 2.0, 0.7, -0.1, 1.1])
+    soft = dict(router_kind=0, norm_topk=1)
+    w = orc.route_set_weights(soft, lg, [4, 1])
+    np.testing.assert_allclose(w, [sp.expit(lg[4] - lg[1]), sp.expit(lg[1] - lg[4])], rtol=1e-13)
+    w = orc.route_set_weights(dict(soft, norm_topk=0), lg, [4, 1])
+    np.testing.assert_allclose(w, sp.softmax(lg)[[4, 1]], rtol=1e-13)
+    grp = dict(router_kind=1, route_scale=2.5)
+    w = orc.route_set_weights(grp, lg, [5, 0, 3], bias=np.full(6, 7.0))
+    s = sp.expit(lg[[5, 0, 3]])
+    np.testing.assert_allclose(w, 2.5 * s / s.sum(), rtol=1e-13)
+    np.testing.assert_allclose(orc.route_scores(soft, lg), lg, rtol=0)
+    bias = np.linspace(-0.1, 0.1, 6)
+    np.testing.assert_allclose(orc.route_scores(grp, lg, bias), sp.expit(lg) + bias, rtol=1e-15)
