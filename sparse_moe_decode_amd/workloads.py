@@ -60,7 +60,7 @@ def initial_routing(tier: str, seed: int, n_layers: int):
 
 
 # Token correlation of the AR(1) token inputs of the decode stacks. Written by
-# oracle/calibrate_rho.py (the fp64 oracle run free over the first 32 tokens
+# tests/golden/calibrate_rho.py (the fp64 oracle run free over the first 32 tokens
 # of the 35B stack, seed 3): mean adjacent-token overlap of the executed sets
 # on the predicted layers 7-38 is 0.670 at RHO_STACK (the pages' ~70% reuse
 # between consecutive tokens) and 0.264 at RHO_LOW_REUSE (their ~25% case).

@@ -10,7 +10,7 @@ the oracle free (its own routing and predictions, fp64) over the first tokens
 for a list of rho values and prints the mean adjacent-token set overlap
 |S_t & S_{t-1}| / K over the predicted layers.
 
-    python oracle/calibrate_rho.py --tokens 32 --rho 0.5 0.9 0.99
+    python tests/golden/calibrate_rho.py --tokens 32 --rho 0.5 0.9 0.99
 
 The workload constants it fixes (the rho giving about 0.7 overlap and the one
 giving about 0.25) are stored in sparse_moe_decode_amd/workloads.py.
@@ -27,7 +27,7 @@ import time
 
 import numpy as np
 
-sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__)))))
 
 import oracle  # noqa: E402
 from sparse_moe_decode_amd import synth  # noqa: E402
