@@ -31,29 +31,39 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 F16_PEAK_TFLOPS = 2500.0  # dense fp16 MFMA
 METRIC = "35B-tier decode layer-steps/s & tokens/s at B=1; HBM GB/s as % of MI355X peak"
-KERNEL_SOURCES = ["stack.hip", "gemv.h", "device.h", "internal.h"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_stack_35b_stack.md")
+# layer_step kernel of each --path: its name, the sources it is built from
+# (the counter summaries record their hash) and its traffic summary
+PATH_KERNELS = {
+    "persistent": ("k_stack", "persistent layer_step kernel",
+                   ["stack.hip", "gemv.h", "device.h", "internal.h"]),
+    "flow": ("k_flow", "wave-specialised streaming layer_step kernel",
+             ["flow.hip", "gemv.h", "device.h", "internal.h"]),
+}
 
 
-def kernel_source_hash() -> str:
+def traffic_file(kernel: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{kernel}_35b_stack.md")
+
+
+def kernel_source_hash(path: str = "persistent") -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in PATH_KERNELS[path][2]:
         with open(os.path.join(ROOT, "sparse_moe_decode_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch of the persistent kernel from the committed
+def measured_traffic(path: str = "persistent"):
+    """HBM bytes per launch of the path's layer_step kernel from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if it was taken on the current
     kernel sources (else None)."""
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(traffic_file(PATH_KERNELS[path][0])).read()
     except OSError:
         return None
     m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
     m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9]+)", text)
-    if not m_hash or not m_b or m_hash.group(1) != kernel_source_hash():
+    if not m_hash or not m_b or m_hash.group(1) != kernel_source_hash(path):
         return None
     return int(m_b.group(1))
 
@@ -709,6 +719,9 @@ def main():
                          "stack (--cache-entries: through the HBM hot cache); storage: the stack "
                          "with experts read from per-layer files; layer: single layer-steps, warm "
                          "and cold")
+    ap.add_argument("--path", choices=["persistent", "flow"], default="persistent",
+                    help="stack workload: layer_step kernel (persistent whole-token kernel, or "
+                         "the wave-specialised streaming kernel)")
     ap.add_argument("--reserve-cus", type=int, default=32,
                     help="staged workload: compute units left to the staging copies")
     ap.add_argument("--group", type=int, default=16,
@@ -785,6 +798,7 @@ def main():
 
     ctx = api.Context(dm, max_tokens=1)
     model = api.Model(ctx, layers)
+    model.set_path(api.PATH_PERSISTENT if args.path == "persistent" else api.PATH_FLOW)
     state = api.State(dm, L, head_logits=False)
     idx0, w0 = wl.initial_routing(tier, args.seed, L)
     state.route_idx[0].copy_(torch.from_numpy(idx0))
@@ -801,8 +815,10 @@ def main():
         exec_hist[t].copy_(state.exec_idx[t & 1])
     rc = api.device_status(ctx)
     assert rc == 0, f"device status {rc}"
+    # the decode state at the start of the timed region, for the replay below
+    snap = [x.clone() for x in (state.route_idx, state.route_w, state.exec_idx, state.exec_w)]
 
-    # Timed region: one persistent-kernel launch per token on `stream`; events
+    # Timed region: one layer_step kernel launch per token on `stream`; events
     # on that stream bracket the whole region and each launch.
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -820,18 +836,29 @@ def main():
     rc = api.device_status(ctx)
     assert rc == 0, f"device status {rc}"
 
-    # Adjacent-token overlap of the executed sets on predicted layers (warmup tokens).
-    eh = exec_hist[: args.warmup].cpu().numpy()
+    # Adjacent-token overlap of the executed sets on the predicted layers over
+    # the timed tokens. Their sets are not kept by the timed loop (a copy per
+    # token would sit in the timed region): the timed tokens are replayed
+    # after it from the saved state, and layer_step is bitwise deterministic,
+    # so the replay executes the same sets.
+    for x, y in zip((state.route_idx, state.route_w, state.exec_idx, state.exec_w), snap):
+        x.copy_(y)
+    for t in range(args.warmup, T):
+        api.layer_step(ctx, model, 0, L, state, t, h_all[t], stream)
+        exec_hist[t].copy_(state.exec_idx[t & 1])
+    torch.cuda.synchronize()
+    eh = exec_hist.cpu().numpy()
     cons = [l for l, r in enumerate(roles) if not r["router"]]
     ov = [len(set(eh[t, l]) & set(eh[t - 1, l])) / dm["K"]
-          for t in range(1, args.warmup) for l in cons]
+          for t in range(args.warmup + 1, T) for l in cons]
     overlap = float(np.mean(ov)) if ov else None
 
     ab = algorithmic_bytes(dm, roles)
     gbs = ab["total"] / (ms * 1e-3) / 1e9
     kgbs = ab["total"] / (kernel_ms * 1e-3) / 1e9
     copy_gbs = copy_bandwidth()
-    traffic = measured_traffic() if not quant else None  # counters taken on the symmetric run
+    # counters taken on the symmetric run
+    traffic = measured_traffic(args.path) if not quant else None
     tok_s = 1000.0 / ms
     cpu = None
     if keep_host:
@@ -874,7 +901,8 @@ def main():
         "algorithmic_bytes_per_token": ab["total"],
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_stack (persistent layer_step kernel: one decode token, 40 layers)",
+            "kernel": f"{PATH_KERNELS[args.path][0]} ({PATH_KERNELS[args.path][1]}: one decode "
+                      f"token, 40 layers)",
             "achieved": round(kgbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -884,6 +912,7 @@ def main():
             "algorithmic_bytes_per_launch": ab["total"],
         },
         "adjacent_set_overlap": None if overlap is None else round(overlap, 3),
+        "adjacent_set_overlap_tokens": "the timed tokens (replayed), predicted layers 7-38",
         "cpu_baseline": cpu,
         "build_s": round(t_build, 1),
     }

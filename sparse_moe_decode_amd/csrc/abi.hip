@@ -74,6 +74,7 @@ struct e0_model {
   // streaming kernel: exchange words [L][xlayer] and the role split
   uint64_t* fxbuf;
   int64_t fxwords;
+  uint32_t fx_clean;  // every exchange word is zero or was written after this epoch
   int32_t fng, fnd;  // explicit split (0, 0: automatic)
 };
 
@@ -107,7 +108,10 @@ hipError_t flow_alloc(e0_model* m) {
   hipError_t e = hipMalloc(&m->fxbuf, need * 8);
   if (e == hipSuccess) e = hipMemset(m->fxbuf, 0, need * 8);
   if (e == hipSuccess) e = hipDeviceSynchronize();
-  if (e == hipSuccess) m->fxwords = need;
+  if (e == hipSuccess) {
+    m->fxwords = need;
+    m->fx_clean = m->epoch;
+  }
   return e;
 }
 
@@ -482,6 +486,7 @@ int e0_model_create(e0_ctx* ctx, const e0_layer* layers, int32_t n_layers, e0_mo
   m->fxbuf = nullptr;
   m->fxwords = 0;
   m->fng = m->fnd = 0;
+  m->fx_clean = 0;
   const Dims& dm = ctx->dm;
   // Device table of the layers for the persistent kernel.
   std::vector<LayerDev> table(n_layers);
@@ -667,6 +672,12 @@ int layer_step(e0_ctx* ctx, e0_model* model, int32_t layer_begin, int32_t layer_
     a.xbuf = model->fxbuf;
     a.trace = model->trace;
     launched = true;
+    // packed words carry the epoch mod 255: clear them before a tag repeats
+    if (a.epoch - model->fx_clean >= 255u) {
+      hipError_t e = launch_flow_clear(model->fxbuf, model->fxwords, st);
+      if (e != hipSuccess) return hip_fail(e, "layer_step (exchange clear)");
+      model->fx_clean = a.epoch - 1;
+    }
     hipError_t e = launch_flow(a, st);
     if (e != hipSuccess) return hip_fail(e, "layer_step (streaming kernel)");
     return E0_OK;

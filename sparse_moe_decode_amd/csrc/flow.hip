@@ -205,6 +205,67 @@ __device__ __forceinline__ void xgather(const uint64_t* base, int n, uint32_t ep
   }
 }
 
+// Packed exchange words: two floats rounded to 28 bits (sign, exponent and
+// 19 mantissa bits, round half away from zero on the magnitude) under an
+// 8-bit tag: bits 0-27 the first, 28-55 the second, 56-63 the tag. The tag is
+// the launch epoch mod 255, plus 1; the host clears the words before a tag
+// could come round again (every 255 launches), so a word with the current
+// tag was written by this launch.
+__device__ __forceinline__ uint32_t pk_tag(uint32_t epoch) { return epoch % 255u + 1u; }
+__device__ __forceinline__ uint64_t q28(float v) { return (uint64_t)((fbits(v) + 8u) >> 4); }
+__device__ __forceinline__ void xput2(uint64_t* p, float v0, float v1, uint32_t tag) {
+  const uint64_t w = ((uint64_t)tag << 56) | (q28(v1) << 28) | q28(v0);
+  __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Gather of n packed words (n even; 16-byte polls, U in flight per thread):
+// sink(word index, first value, second value) once per word.
+template <int U, typename Sink>
+__device__ __forceinline__ void xgather2(const uint64_t* base, int n, uint32_t tag, int tid,
+                                         int nthr, int32_t* gflags, Sink&& sink) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, n * 8, 0x00020000);
+  const int np = n >> 1;
+  const uint32_t want = tag << 24;
+  for (int b0 = 0; b0 < np; b0 += U * nthr) {
+    u32x4v v[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int p = b0 + j * nthr + tid;
+      v[j] = p < np ? __builtin_amdgcn_raw_buffer_load_b128(rs, p * 16, 0, 16)
+                    : (u32x4v){0u, want, 0u, want};
+    }
+    Waiter w{0, 0};
+    bool started = false;
+    for (;;) {
+      bool ok = true;
+#pragma unroll
+      for (int j = 0; j < U; ++j)
+        ok = ok && (v[j].y & 0xFF000000u) == want && (v[j].w & 0xFF000000u) == want;
+      if (ok) break;
+      if (!started) {
+        w.t0 = wall_clock64();
+        started = true;
+      }
+      if (expired(w, gflags)) break;
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        const int p = b0 + j * nthr + tid;
+        if (p < np && ((v[j].y & 0xFF000000u) != want || (v[j].w & 0xFF000000u) != want))
+          v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, p * 16, 0, 16);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int p = b0 + j * nthr + tid;
+      if (p < np) {
+        sink(2 * p, bitsf(v[j].x << 4), bitsf(((v[j].y << 8) | (v[j].x >> 24)) & 0xFFFFFFF0u));
+        sink(2 * p + 1, bitsf(v[j].z << 4), bitsf(((v[j].w << 8) | (v[j].z >> 24)) & 0xFFFFFFF0u));
+      }
+    }
+  }
+}
+
 template <typename Sink>
 __device__ __forceinline__ void xgather_any(const uint64_t* base, int n, uint32_t ep, int tid,
                                             int nthr, int32_t* gflags, Sink&& sink) {
@@ -312,6 +373,11 @@ __device__ __forceinline__ RT rt_at(int off, int nL, int K, P& p) {
   t.hb = t.pb + p.nd + 1;
   t.fb = t.hb + p.ng + 1;
   return t;
+}
+
+// A wave-uniform float in a scalar register.
+__device__ __forceinline__ float uniform_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
 }
 
 // Dot of a wave's fp16 row (LDS, natural order, d columns) with x (LDS,
@@ -506,6 +572,7 @@ __device__ __attribute__((noinline)) void gu_compute(uint64_t kap) {
   const int r0 = kRouterRows * cu, r1 = min(r0 + kRouterRows, E);
   const int hb = rt.hb[cu], he = rt.hb[cu + 1];
   const int bir = 1 << p.lbr, hs = 1 << p.lhs;
+  const uint32_t tag = pk_tag(ep);
   uint16_t* hbuf = lds_at<uint16_t>(p.g_h);
   uint16_t* xn = lds_at<uint16_t>(p.g_xn);
   uint16_t* xp = lds_at<uint16_t>(p.g_xp);
@@ -532,11 +599,15 @@ __device__ __attribute__((noinline)) void gu_compute(uint64_t kap) {
       const uint64_t* XA = a.xbuf + (int64_t)(l - 1) * p.xlayer + p.o_xa;
       uint32_t* h32 = reinterpret_cast<uint32_t*>(hbuf);
       const int lba = p.lba;
-      xgather_any(XA, p.nd << lba, ep, t, kFC, gf, [&](int wi, uint32_t v) {
-        const int jd = wi >> lba, o = wi & ((1 << lba) - 1);
-        const int pb = rt.pb[jd];
-        if (o < rt.pb[jd + 1] - pb) h32[pb + o] = v;
-      });
+      if (p.direct & 4) {  // every down CU owns 1 << lba row pairs: word w is pair w
+        xgather_any(XA, p.nd << lba, ep, t, kFC, gf, [&](int wi, uint32_t v) { h32[wi] = v; });
+      } else {
+        xgather_any(XA, p.nd << lba, ep, t, kFC, gf, [&](int wi, uint32_t v) {
+          const int jd = wi >> lba, o = wi & ((1 << lba) - 1);
+          const int pb = rt.pb[jd];
+          if (o < rt.pb[jd + 1] - pb) h32[pb + o] = v;
+        });
+      }
     }
     cbar(phase, gf);
     stamp(a, l, 1);
@@ -588,7 +659,7 @@ __device__ __attribute__((noinline)) void gu_compute(uint64_t kap) {
     if (aq >= 0 && wave == 0) {
       float v = 0.0f;
       if (lf & LF_LORA) v = wave_sum_rows(wave_row_dot<CPL>(reinterpret_cast<const uint16_t*>(S + p.g_ar), xn));
-      if (lane < kBlk) xput(XB + p.xb_a + aq * kBlk + lane, lane == 0 ? fbits(v) : 0u, ep);
+      if (lane < kBlk) xput2(XB + p.xb_a + aq * kBlk + lane, lane == 0 ? v : 0.0f, 0.0f, tag);
     }
     if ((lf & LF_ROUTER) && rcu) {
       fl_wait(FL_RREADY, step + 1, gf);
@@ -664,27 +735,23 @@ __device__ __attribute__((noinline)) void gu_compute(uint64_t kap) {
         }
         ag = group_sum<kGL>(ag);
         au = group_sum<kGL>(au);
-        if (li == 0 && jj < ipc) {
-          if (it.shared) {
-            // the shared expert's sums go out as they are: the down CUs add
-            // the LoRA terms and take the SwiGLU
-            const int cs = cu - p.ngr;
-            xput(XB + p.xb_s + (cs << (p.lhs + 1)) + jj, fbits(ag), ep);
-            xput(XB + p.xb_s + (cs << (p.lhs + 1)) + hs + jj, fbits(au), ep);
-          } else {
-            xput(XB + (cu << p.lbr) + jj, fbits(ok ? silu(ag) * au : 0.0f), ep);
-          }
+        if (it.shared) {
+          // the shared expert's raw sums, (g, u) in one word: the down CUs
+          // add the LoRA terms and take the SwiGLU
+          if (li == 0 && jj < ipc) xput2(XB + p.xb_s + ((cu - p.ngr) << p.lhs) + jj, ag, au, tag);
+        } else {
+          // items 2o and 2o + 1 share word o: the odd group hands its value to
+          // the even one 16 lanes below
+          const float sv = ok ? silu(ag) * au : 0.0f;
+          const float sn = __shfl_xor(sv, kGL, 64);
+          if (li == 0 && (grp & 1) == 0 && jj < ipc) xput2(XB + (cu << p.lbr) + (jj >> 1), sv, sn, tag);
         }
       }
       stamp(a, l, 8);
       if (it.shared) {
-        const int cs = cu - p.ngr;
-        if (t >= ipc && t < hs) {
-          xput(XB + p.xb_s + (cs << (p.lhs + 1)) + t, 0u, ep);
-          xput(XB + p.xb_s + (cs << (p.lhs + 1)) + hs + t, 0u, ep);
-        }
-      } else if (t >= ipc && t < bir) {
-        xput(XB + (cu << p.lbr) + t, 0u, ep);
+        if (t >= ipc && t < hs) xput2(XB + p.xb_s + ((cu - p.ngr) << p.lhs) + t, 0.0f, 0.0f, tag);
+      } else if (t >= (ipc + 1) / 2 && t < bir) {
+        xput2(XB + (cu << p.lbr) + t, 0.0f, 0.0f, tag);
       }
       release(FL_FREED + 4 * slot + wave, step + 1);
     }
@@ -969,30 +1036,61 @@ __device__ __attribute__((noinline)) void dn_compute(uint64_t kap) {
 
     // ---- SwiGLU outputs, the shared expert's sums, LoRA A products -------------
     {
-      const int lbr = p.lbr, lhs = p.lhs, hsz = 1 << lhs;
-      xgather_any(X + p.o_xb, p.xb_n, ep, t, kFC, gf, [&](int wi, uint32_t v) {
-        if (wi < p.xb_s) {
-          const int c = wi >> lbr, o = wi & ((1 << lbr) - 1);
-          const int b = rt.ibr[c];
-          if (o < rt.ibr[c + 1] - b) sb[b + o] = bitsf(v);
-        } else if (wi < p.xb_a) {
-          const int w2 = wi - p.xb_s, c = w2 >> (lhs + 1), o = w2 & (2 * hsz - 1);
-          const int oo = o & (hsz - 1);
-          const int b = rt.ibs[c];
-          if (c < ngs && oo < rt.ibs[c + 1] - b) {
-            if (o < hsz) sb[KI + b + oo] = bitsf(v);
-            else su[b + oo] = bitsf(v);
+      const int lbr = p.lbr, lhs = p.lhs;
+      if ((p.direct & 3) == 3) {
+        // whole blocks everywhere: routed word w holds items 2w, 2w + 1, shared
+        // word w row w
+        xgather2<8>(X + p.o_xb, p.xb_n, pk_tag(ep), t, kFC, gf, [&](int wi, float v0, float v1) {
+          if (wi < p.xb_s) {
+            sb[2 * wi] = v0;
+            sb[2 * wi + 1] = v1;
+          } else if (wi < p.xb_a) {
+            sb[KI + wi - p.xb_s] = v0;
+            su[wi - p.xb_s] = v1;
+          } else if (((wi - p.xb_a) & 7) == 0) {
+            ax[(wi - p.xb_a) >> 3] = v0;
           }
-        } else {
-          const int w3 = wi - p.xb_a;
-          if ((w3 & 7) == 0) ax[w3 >> 3] = bitsf(v);
-        }
-      });
+        });
+      } else {
+        xgather2<8>(X + p.o_xb, p.xb_n, pk_tag(ep), t, kFC, gf, [&](int wi, float v0, float v1) {
+          if (wi < p.xb_s) {
+            // SwiGLU outputs of items 2o and 2o + 1 of routed CU c
+            const int c = wi >> lbr, o = wi & ((1 << lbr) - 1);
+            const int b = rt.ibr[c], n = rt.ibr[c + 1] - b;
+            if (2 * o < n) sb[b + 2 * o] = v0;
+            if (2 * o + 1 < n) sb[b + 2 * o + 1] = v1;
+          } else if (wi < p.xb_a) {
+            // the shared expert's raw g and u of row o of shared CU c
+            const int w2 = wi - p.xb_s, c = w2 >> lhs, o = w2 & ((1 << lhs) - 1);
+            const int b = rt.ibs[c];
+            if (c < ngs && o < rt.ibs[c + 1] - b) {
+              sb[KI + b + o] = v0;
+              su[b + o] = v1;
+            }
+          } else {
+            const int w3 = wi - p.xb_a;
+            if ((w3 & 7) == 0) ax[w3 >> 3] = v0;
+          }
+        });
+      }
     }
     cbar(phase, gf);
     stamp(a, l, 1);
     // the shared expert: LoRA B terms, then the SwiGLU
     if (Is && (lf & LF_SHARED)) {
+      // the A products are the same for every lane: one vector read of all
+      // of them, then scalar registers, so the B terms wait on no LDS read
+      float axs[2 * kFRank];
+      if (lora) {
+#pragma unroll
+        for (int c = 0; c < 2 * kFRank / 4; ++c) {
+          const float4 v = reinterpret_cast<const float4*>(ax)[c];
+          axs[4 * c] = v.x;
+          axs[4 * c + 1] = v.y;
+          axs[4 * c + 2] = v.z;
+          axs[4 * c + 3] = v.w;
+        }
+      }
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int i = t + 256 * q;
@@ -1005,10 +1103,10 @@ __device__ __attribute__((noinline)) void dn_compute(uint64_t kap) {
             const uint32_t uw[4] = {bur[q][h].x, bur[q][h].y, bur[q][h].z, bur[q][h].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              lg2 = fmaf(h2f((uint16_t)(gw[e] & 0xFFFF)), ax[8 * h + 2 * e], lg2);
-              lg2 = fmaf(h2f((uint16_t)(gw[e] >> 16)), ax[8 * h + 2 * e + 1], lg2);
-              lu2 = fmaf(h2f((uint16_t)(uw[e] & 0xFFFF)), ax[r + 8 * h + 2 * e], lu2);
-              lu2 = fmaf(h2f((uint16_t)(uw[e] >> 16)), ax[r + 8 * h + 2 * e + 1], lu2);
+              lg2 = fmaf(h2f((uint16_t)(gw[e] & 0xFFFF)), axs[8 * h + 2 * e], lg2);
+              lg2 = fmaf(h2f((uint16_t)(gw[e] >> 16)), axs[8 * h + 2 * e + 1], lg2);
+              lu2 = fmaf(h2f((uint16_t)(uw[e] & 0xFFFF)), axs[kFRank + 8 * h + 2 * e], lu2);
+              lu2 = fmaf(h2f((uint16_t)(uw[e] >> 16)), axs[kFRank + 8 * h + 2 * e + 1], lu2);
             }
           }
           g = fmaf(dm.lora_scale, lg2, g);
@@ -1018,6 +1116,7 @@ __device__ __attribute__((noinline)) void dn_compute(uint64_t kap) {
       }
     }
     cbar(phase, gf);
+    stamp(a, l, 14);
     // fp16 hi + lo copies (pair-permuted) with a power-of-two scale per 32 elements
 #pragma unroll
     for (int k = 0; k < KM + 1; ++k) {
@@ -1027,6 +1126,7 @@ __device__ __attribute__((noinline)) void dn_compute(uint64_t kap) {
         if (li == 0) csc[k * (I / 32) + grp] = sc;
       }
     }
+    stamp(a, l, 15);
     // A_down . h_shared: group g takes rank g, lane li its 32 columns
     {
       float part = 0.0f;
@@ -1207,7 +1307,7 @@ bool flow_supported(const Dims& dm) {
   return true;
 }
 
-FlowPlan flow_plan(const Dims& dm, int ng, int nd, int nL) {
+static FlowPlan flow_plan_t(const Dims& dm, int ng, int nd, int nL, bool snap) {
   FlowPlan p{};
   p.ok = 0;
   if (!flow_supported(dm) || ng < 2 || nd < 1 || nL < 1 || nL > kFMaxL) return p;
@@ -1223,21 +1323,34 @@ FlowPlan flow_plan(const Dims& dm, int ng, int nd, int nL) {
     if (p.ngr > ng - 1) p.ngr = ng - 1;
     if (p.ngr < 1) p.ngr = 1;
   }
+  {
+    // a power-of-two share of routed items per CU (16 or more: whole 64-byte
+    // blocks of two items a word) lets the down CUs store the exchange
+    // words straight into place; taken when it keeps at least 80% of the CUs
+    int ipr = 2;
+    while (ipr * p.ngr < KI) ipr *= 2;
+    if (snap && ipr >= 16 && KI % ipr == 0 && 5 * (KI / ipr) >= 4 * p.ngr) p.ngr = KI / ipr;
+  }
   const int ngs = ng - p.ngr;
   p.ipr_max = cdiv(KI, p.ngr);
   p.ips_max = Is ? cdiv(Is, ngs) : 0;
   p.ipc_max = p.ipr_max > p.ips_max ? p.ipr_max : p.ips_max;
-  p.lbr = log2ceil(p.ipr_max, 3);
-  p.lhs = log2ceil(p.ips_max, 2);
+  p.lbr = log2ceil(cdiv(p.ipr_max, 2), 3);  // two items a word
+  p.lhs = log2ceil(p.ips_max, 3);            // (g, u) of one row a word
   p.pairs_max = cdiv(d / 2, nd);
   p.lba = log2ceil(p.pairs_max, 3);
   p.nrc = cdiv(E, kRouterRows);
-  p.ca0 = p.nrc;
+  // the LoRA A rows go to the shared CUs when there are enough of them
+  p.ca0 = (Is && ngs >= 2 * r) ? p.ngr : p.nrc;
   p.hrn = P + E;
   p.hr_max = cdiv(p.hrn, ng);
   p.f2_max = cdiv(E, nd);
   if (p.ipc_max > 2 * kGN || p.pairs_max > kGN || p.hr_max > kBlk || p.f2_max > kBlk) return p;
-  if (p.ngr < p.nrc + 2 * r || ng < p.nrc) return p;
+  if (p.ngr < p.nrc || (p.ca0 == p.nrc && p.ngr < p.nrc + 2 * r)) return p;
+  p.direct = 0;
+  if (p.ipr_max == (2 << p.lbr) && KI == p.ngr * p.ipr_max) p.direct |= 1;
+  if (!Is || Is == (ngs << p.lhs)) p.direct |= 2;
+  if (d / 2 == (nd << p.lba)) p.direct |= 4;
   // exchange words of a layer (every region starts on a 128-byte line)
   int o = 0;
   auto region = [&](int n) {
@@ -1247,7 +1360,7 @@ FlowPlan flow_plan(const Dims& dm, int ng, int nd, int nL) {
   };
   p.o_xa = region(nd << p.lba);
   p.xb_s = p.ngr << p.lbr;
-  p.xb_a = p.xb_s + (Is ? ngs << (p.lhs + 1) : 0);
+  p.xb_a = p.xb_s + (Is ? ngs << p.lhs : 0);
   p.xb_n = p.xb_a + 2 * r * kBlk;
   p.o_xb = region(p.xb_n);
   p.o_xr = region(p.nrc * kBlk);
@@ -1307,6 +1420,11 @@ FlowPlan flow_plan(const Dims& dm, int ng, int nd, int nL) {
   return p;
 }
 
+FlowPlan flow_plan(const Dims& dm, int ng, int nd, int nL) {
+  const FlowPlan p = flow_plan_t(dm, ng, nd, nL, true);
+  return p.ok ? p : flow_plan_t(dm, ng, nd, nL, false);
+}
+
 // Default split of `grid` CUs: as many down CUs as it takes to give each at
 // most 16 row pairs and a layer slot that fits, the rest gate/up.
 bool flow_default_roles(const Dims& dm, int grid, int nL, int& ng, int& nd) {
@@ -1322,6 +1440,22 @@ bool flow_default_roles(const Dims& dm, int grid, int nL, int& ng, int& nd) {
     }
   }
   return false;
+}
+
+namespace {
+__global__ __launch_bounds__(256) void k_fill0(uint64_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = 0;
+}
+}  // namespace
+
+// Zero n exchange words (a plain kernel, so a captured stream records no memset).
+hipError_t launch_flow_clear(uint64_t* words, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(k_fill0, dim3((unsigned)blocks), dim3(256), 0, st, words, n);
+  return hipGetLastError();
 }
 
 hipError_t launch_flow(const FlowArgs& a, hipStream_t st) {

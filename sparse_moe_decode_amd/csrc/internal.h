@@ -176,6 +176,7 @@ hipError_t launch_stack(const StackArgs& a, int grid, hipStream_t st);
 constexpr int kFlowLds = 156 * 1024;
 struct FlowPlan {
   int32_t ok, ng, nd, KX;
+  int32_t direct;  // exchange words map to LDS without tables: 1 routed, 2 shared, 4 h
   // gate/up CUs [0, ngr) own the routed items (K*I, ipr_max at most each),
   // [ngr, ng) the shared expert's rows (ips_max at most each)
   int32_t ngr, ipr_max, ips_max, ipc_max;
@@ -219,6 +220,9 @@ FlowPlan flow_plan(const Dims& dm, int ng, int nd, int nL);
 // Default split of grid workgroups into gate/up and down CUs.
 bool flow_default_roles(const Dims& dm, int grid, int nL, int& ng, int& nd);
 hipError_t launch_flow(const FlowArgs& a, hipStream_t st);
+// Zero the streaming kernel's exchange words (its packed words carry an
+// 8-bit tag that comes round every 255 launches).
+hipError_t launch_flow_clear(uint64_t* words, int64_t n, hipStream_t st);
 
 // Staging: device-side slot policy for one layer, then a gather-copy of the
 // missing bundles from (device-mapped) pinned host memory into HBM slots.
