@@ -643,6 +643,7 @@ def run_layer(args):
                                     else (v.clone() if v is not None else None))
                                 for k, v in base.items()} for _ in range(copies - 1)]
             model = api.Model(ctx, layers)
+            model.set_path(api.PATH_PERSISTENT if args.path == "persistent" else api.PATH_FLOW)
             n = copies
             # per-step private routing / exec blocks [T+1][2][n][K]
             ri = np.zeros((T + 1, 2, n, K), np.int32)
@@ -659,7 +660,7 @@ def run_layer(args):
             dri, drw, dei, dew = (torch.from_numpy(a).cuda() for a in (ri, rw, ei, ew))
             states = [types.SimpleNamespace(struct=api.e0_state(
                 dri[t].data_ptr(), drw[t].data_ptr(), dei[t].data_ptr(), dew[t].data_ptr(),
-                None, None)) for t in range(T + 1)]
+                None, None, n), n_layers=n) for t in range(T + 1)]
             h = torch.zeros((T + 1, 2, d), dtype=torch.float16, device="cuda")
             h[:, 0].copy_(torch.from_numpy(toks))
             main = torch.cuda.current_stream()
@@ -694,6 +695,7 @@ def run_layer(args):
         torch.cuda.empty_cache()
     print(json.dumps({"workload": "single predicted layer-step with head, batch 1, one "
                                   "layer_step launch per step (8B and 35B tiers)",
+                      "layer_kernel": PATH_KERNELS[args.path][0],
                       "steps": T, "repeats": R, "results": results}))
 
 
@@ -720,8 +722,8 @@ def main():
                          "with experts read from per-layer files; layer: single layer-steps, warm "
                          "and cold")
     ap.add_argument("--path", choices=["persistent", "flow"], default="persistent",
-                    help="stack workload: layer_step kernel (persistent whole-token kernel, or "
-                         "the wave-specialised streaming kernel)")
+                    help="stack and layer workloads: layer_step kernel (persistent whole-token "
+                         "kernel, or the wave-specialised streaming kernel)")
     ap.add_argument("--reserve-cus", type=int, default=32,
                     help="staged workload: compute units left to the staging copies")
     ap.add_argument("--group", type=int, default=16,
