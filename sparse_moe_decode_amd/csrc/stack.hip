@@ -122,6 +122,55 @@ __device__ __forceinline__ void ll_gather(const uint64_t* src, int n, uint32_t e
   }
 }
 
+// ll_gather with 16-byte polls: two words per load, U loads per thread in
+// flight (agent-scope buffer loads, so a poll is one request for both
+// words). src 16-byte aligned and n even; otherwise the 8-byte gather.
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+template <int U>
+__device__ __forceinline__ void ll_gather2(const uint64_t* src, int n, uint32_t ep, uint32_t* dst,
+                                           int32_t* flags, int* abort_lds) {
+  if ((n & 1) || (reinterpret_cast<uintptr_t>(src) & 15)) {
+    ll_gather<2 * U>(src, n, ep, dst, flags, abort_lds);
+    return;
+  }
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, n * 8, 0x00020000);
+  const uint64_t t0 = wall_clock64();
+  uint32_t polls = 0;
+  const int np = n >> 1;
+  for (int b0 = 0; b0 < np; b0 += U * kThreads) {
+    u32x4v v[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int p = b0 + j * kThreads + (int)threadIdx.x;
+      v[j] = p < np ? __builtin_amdgcn_raw_buffer_load_b128(rs, p * 16, 0, 16)
+                    : (u32x4v){0u, ep, 0u, ep};
+    }
+    for (;;) {
+      bool ok = true;
+#pragma unroll
+      for (int j = 0; j < U; ++j) ok = ok && v[j].y == ep && v[j].w == ep;
+      if (ok) break;
+      if (wait_expired(t0, flags, abort_lds, polls)) break;
+      __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        const int p = b0 + j * kThreads + (int)threadIdx.x;
+        if (p < np && (v[j].y != ep || v[j].w != ep))
+          v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, p * 16, 0, 16);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int p = b0 + j * kThreads + (int)threadIdx.x;
+      if (p < np) {
+        dst[2 * p] = v[j].x;
+        dst[2 * p + 1] = v[j].z;
+      }
+    }
+  }
+}
+
 // Phase timestamp of this workgroup (thread 0) when tracing is on. Rows
 // 0..L-1 are layers, row L the head phase after the last layer.
 __device__ __forceinline__ void stamp(const StackArgs& a, int row, int k) {
@@ -670,7 +719,7 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
     // ---- 1. h_l, attention stand-in, RMSNorm ---------------------------
     stamp(a, l, 9);
     if (step > 0) {
-      ll_gather<4>(a.xh + (int64_t)(l - 1) * (d / 2), d / 2, ep, land, a.flags, &ms.abort);
+      ll_gather2<2>(a.xh + (int64_t)(l - 1) * (d / 2), d / 2, ep, land, a.flags, &ms.abort);
     }
     vm_drained();
     __syncthreads();
@@ -750,7 +799,7 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
       stamp(a, l, 10);
       if (t < A.n_router) ll_put(a.xr + (int64_t)l * E + rb + t, fbits(ms.rows[t]), ep);
       stamp(a, l, 11);
-      ll_gather<2>(a.xr + (int64_t)l * E, E, ep, land, a.flags, &ms.abort);
+      ll_gather2<1>(a.xr + (int64_t)l * E, E, ep, land, a.flags, &ms.abort);
       __syncthreads();
       stamp(a, l, 13);
       // the executed set (this layer's head reads it too) and its weights go
@@ -796,8 +845,8 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
       if (pl.ie > n_rt) {  // this workgroup owns rows of the shared expert
         const float* axgu = nullptr;
         if (r2) {
-          ll_gather<1>(xg + n_rt + Is, r2, ep, reinterpret_cast<uint32_t*>(ms.axgu), a.flags,
-                       &ms.abort);
+          ll_gather2<1>(xg + n_rt + Is, r2, ep, reinterpret_cast<uint32_t*>(ms.axgu), a.flags,
+                        &ms.abort);
           __syncthreads();
           axgu = ms.axgu;
         }
@@ -816,7 +865,7 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
 
     // ---- 4. gather SwiGLU outputs; finish the shared expert ----------------
     const int ng_l = n_rt + Is;
-    ll_gather<16>(xg, ng_l, ep, land, a.flags, &ms.abort);
+    ll_gather2<8>(xg, ng_l, ep, land, a.flags, &ms.abort);
     vm_drained();
     __syncthreads();
     stamp(a, l, 6);
@@ -1036,8 +1085,8 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
   // fc2 rows, as fp16 hi + lo with a power-of-two scale per lane chunk.
   const int hf0 = nf > 0 ? f0 / E : 0, hf1 = nf > 0 ? (f1 - 1) / E : -1;
   for (int h = hf0; h <= hf1; ++h)
-    ll_gather<4>(a.xa + (int64_t)ms.hl_list[h] * PE, PE, ep, land + (h - hf0) * PE, a.flags,
-                 &ms.abort);
+    ll_gather2<2>(a.xa + (int64_t)ms.hl_list[h] * PE, PE, ep, land + (h - hf0) * PE, a.flags,
+                  &ms.abort);
   __syncthreads();
   stamp(a, hrow, 2);
   if (t < (hf1 - hf0 + 1) * kLG) {
@@ -1104,7 +1153,7 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
   // routing of each head's logits: the next token's prediction
   for (int h = cu; h < nH; h += G) {
     const int l = ms.hl_list[h];
-    ll_gather<2>(a.xl + (int64_t)l * E, E, ep, land, a.flags, &ms.abort);
+    ll_gather2<1>(a.xl + (int64_t)l * E, E, ep, land, a.flags, &ms.abort);
     __syncthreads();
     int32_t* pidx = l + 1 < a.L ? a.route_idx + ((int64_t)nxt * a.L + l + 1) * K : a.sink_idx;
     float* pw = l + 1 < a.L ? a.route_w + ((int64_t)nxt * a.L + l + 1) * K : a.sink_w;
