@@ -55,6 +55,32 @@ constexpr int kHX = 4;         // head layers one workgroup keeps x / fc2 activa
 constexpr int kF2R = 4;        // fc2 rounds (kGroups rows each) per workgroup
 constexpr int kCPF = 4;        // 16-byte chunks per lane of an fc2 row (P <= 512)
 
+// Stand-in row for loads whose row does not exist (an unresolved expert, an
+// item past the workgroup's share, a layer without that matrix): every load of
+// the layer loop is issued unconditionally, from its row or from here, so that
+// each lands in the register it is consumed from. A conditional load merged
+// with a default value makes the compiler copy the register at the merge,
+// which waits for the load there instead of where the value is used. Never
+// written; 8 KB covers every such load (offsets < d * 2 bytes, d <= 2048).
+__device__ __align__(16) uint32_t g_zrow[2048];
+
+// The row's address is made opaque to the compiler, which could otherwise
+// fold the loads to zeros and turn them back into conditional loads.
+__device__ __forceinline__ const void* zrow() {
+  const void* p = g_zrow;
+  asm("" : "+s"(p));
+  return p;
+}
+
+// p when v, else the zero row. The choice is hidden from the compiler too, so
+// that it cannot split the load into two conditional ones.
+template <typename T>
+__device__ __forceinline__ const T* pick(bool v, const T* p) {
+  const T* q = v ? p : (const T*)zrow();
+  asm("" : "+v"(q));
+  return q;
+}
+
 __device__ __forceinline__ uint64_t ld64(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -294,8 +320,7 @@ __device__ __forceinline__ void f16rows_issue(F16Rows<NR>& R, const uint16_t* co
   const int t = threadIdx.x;
 #pragma unroll
   for (int j = 0; j < NR; ++j) {
-    R.w[j] = make_uint4(0, 0, 0, 0);
-    if (j < nr && t < cols / 8) R.w[j] = ldg(reinterpret_cast<const uint4*>(rp[j] + 8 * t));
+    R.w[j] = ldg(pick(j < nr && t < cols / 8, reinterpret_cast<const uint4*>(rp[j] + 8 * t)));
   }
 }
 
@@ -392,42 +417,39 @@ struct GuPlan {
 template <int CPL, int IPG, bool AFF>
 __device__ __forceinline__ void gu_issue(GuRegs<CPL, IPG>& R, const LayerDev& Ly, const Dims& dm,
                                          const void* const (*ep)[kEp], int n_rt, const GuPlan& pl,
-                                         int grp, int li) {
+                                         int grp, int li, bool known) {
 #pragma unroll
   for (int j = 0; j < IPG; ++j) {
+    // every load is issued; a missing row reads the zero row (see zrow)
     const int it = pl.ib + grp + kGroups * j;
-    if (it >= pl.ie) continue;
     const bool routed = it < n_rt;
-    const int k = routed ? it / kStackI : dm.K;
-    const int row = routed ? it % kStackI : it - n_rt;
+    const int k = it >= pl.ie ? 0 : routed ? it / kStackI : dm.K;
+    const int row = it >= pl.ie ? 0 : routed ? it % kStackI : it - n_rt;
     const uint32_t* gq = (const uint32_t*)ep[k][0];
-    if (!gq) continue;
+    const bool v = known && it < pl.ie && gq != nullptr;
     const uint32_t* uq = (const uint32_t*)ep[k][1];
     const uint16_t* gs = (const uint16_t*)ep[k][3];
     const uint16_t* us = (const uint16_t*)ep[k][4];
-    R.lbg[j] = R.lbu[j] = 0;
-    if (!routed && Ly.sh.ag) {
-      R.lbg[j] = ldg(Ly.sh.bg + (int64_t)row * kRank + li);
-      R.lbu[j] = ldg(Ly.sh.bu + (int64_t)row * kRank + li);
-    }
+    const bool lb = v && !routed && Ly.sh.ag != nullptr;
+    R.lbg[j] = ldg(pick(lb, Ly.sh.bg + (int64_t)row * kRank + li));
+    R.lbu[j] = ldg(pick(lb, Ly.sh.bu + (int64_t)row * kRank + li));
     const int gsh = __builtin_ctz(dm.G);  // G is a power of two
     const int wpr = dm.d / 8, spr = dm.d >> gsh;
-    const uint32_t* grow = gq + (int64_t)row * wpr;
-    const uint32_t* urow = uq + (int64_t)row * wpr;
 #pragma unroll
     for (int c2 = 0; c2 < CPL; ++c2) {
       const int c = li + kLG * c2;
-      R.wg[j][c2] = ldg(reinterpret_cast<const uint4*>(grow + 4 * c));
-      R.wu[j][c2] = ldg(reinterpret_cast<const uint4*>(urow + 4 * c));
+      R.wg[j][c2] = ldg(pick(v, reinterpret_cast<const uint4*>(gq + (int64_t)row * wpr + 4 * c)));
+      R.wu[j][c2] = ldg(pick(v, reinterpret_cast<const uint4*>(uq + (int64_t)row * wpr + 4 * c)));
     }
     // spr is even and rows start 4-byte aligned: one 4-byte load per lane
-    R.sg[j] = 2 * li < spr ? ldg(reinterpret_cast<const uint32_t*>(gs + (int64_t)row * spr) + li) : 0u;
-    R.su[j] = 2 * li < spr ? ldg(reinterpret_cast<const uint32_t*>(us + (int64_t)row * spr) + li) : 0u;
+    const bool vs = v && 2 * li < spr;
+    R.sg[j] = ldg(pick(vs, reinterpret_cast<const uint32_t*>(gs + (int64_t)row * spr) + li));
+    R.su[j] = ldg(pick(vs, reinterpret_cast<const uint32_t*>(us + (int64_t)row * spr) + li));
     if (AFF) {
       const uint16_t* gb = (const uint16_t*)ep[k][6];
       const uint16_t* ub = (const uint16_t*)ep[k][7];
-      R.bg[j] = 2 * li < spr ? ldg(reinterpret_cast<const uint32_t*>(gb + (int64_t)row * spr) + li) : 0u;
-      R.bu[j] = 2 * li < spr ? ldg(reinterpret_cast<const uint32_t*>(ub + (int64_t)row * spr) + li) : 0u;
+      R.bg[j] = ldg(pick(vs, reinterpret_cast<const uint32_t*>(gb + (int64_t)row * spr) + li));
+      R.bu[j] = ldg(pick(vs, reinterpret_cast<const uint32_t*>(ub + (int64_t)row * spr) + li));
     }
   }
 }
@@ -634,35 +656,34 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
     const bool has_sh = Ly.sh.present != 0;
     const int Is = has_sh ? dm.Is : 0;
     const bool lora_d = has_sh && Ly.sh.ad != nullptr;
-    if (drow < de) {
-      const int gsh = __builtin_ctz(dm.G);
-      const int wpr = I / 8, spr = I >> gsh;
+    // every load is issued; a missing row reads the zero row (see zrow)
+    const bool rv = drow < de;
+    const int gsh = __builtin_ctz(dm.G);
+    const int wpr = I / 8, spr = I >> gsh;
+    const uint32_t* q[NX];
+    const uint16_t* sc[NX];
+    const uint16_t* bb[NX];
 #pragma unroll
-      for (int k = 0; k < NX; ++k) {
-        A.D.w[k] = make_uint4(0, 0, 0, 0);
-        A.D.s[k] = 0;
-        A.D.b[k] = 0;
-        if (k > K) continue;
-        const uint32_t* q = (const uint32_t*)ep_k[k][2];
-        const uint16_t* sc = (const uint16_t*)ep_k[k][5];
-        if (!q) continue;
-        A.D.w[k] = ldg(reinterpret_cast<const uint4*>(q + (int64_t)drow * wpr + 4 * li));
-        A.D.s[k] = ldg(sc + (int64_t)drow * spr + ((32 * li) >> gsh));
-        if (AFF)
-          A.D.b[k] = ldg((const uint16_t*)ep_k[k][8] + (int64_t)drow * spr + ((32 * li) >> gsh));
-      }
-#pragma unroll
-      for (int c = 0; c < kRank / 8; ++c) {
-        A.D.bd[c] = make_uint4(0, 0, 0, 0);
-        if (lora_d && li == 0)
-          A.D.bd[c] = ldg(reinterpret_cast<const uint4*>(Ly.sh.bd + (int64_t)drow * kRank + 8 * c));
-      }
+    for (int k = 0; k < NX; ++k) {
+      q[k] = k <= K ? (const uint32_t*)ep_k[k][2] : nullptr;
+      sc[k] = k <= K ? (const uint16_t*)ep_k[k][5] : nullptr;
+      bb[k] = AFF && k <= K ? (const uint16_t*)ep_k[k][8] : nullptr;
     }
 #pragma unroll
+    for (int k = 0; k < NX; ++k) {
+      const bool v = rv && q[k] != nullptr;
+      A.D.w[k] = ldg(pick(v, reinterpret_cast<const uint4*>(q[k] + (int64_t)drow * wpr + 4 * li)));
+      A.D.s[k] = ldg(pick(v, sc[k] + (int64_t)drow * spr + ((32 * li) >> gsh)));
+      if (AFF) A.D.b[k] = ldg(pick(v, bb[k] + (int64_t)drow * spr + ((32 * li) >> gsh)));
+    }
+    const bool vb = rv && lora_d && li == 0;
+#pragma unroll
+    for (int c = 0; c < kRank / 8; ++c)
+      A.D.bd[c] = ldg(pick(vb, reinterpret_cast<const uint4*>(Ly.sh.bd + (int64_t)drow * kRank + 8 * c)));
+#pragma unroll
     for (int c = 0; c < 4; ++c)
-      A.LR.ad[c] = lora_d ? ldg(reinterpret_cast<const uint4*>(Ly.sh.ad + (int64_t)grp * Is +
-                                                              32 * li + 8 * c))
-                          : make_uint4(0, 0, 0, 0);
+      A.LR.ad[c] = ldg(pick(lora_d, reinterpret_cast<const uint4*>(Ly.sh.ad + (int64_t)grp * Is +
+                                                                   32 * li + 8 * c)));
   };
 
   // Issue the loads of layer l that its gate/up step needs and that do not
@@ -671,32 +692,28 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
     const bool has_sh = Ly.sh.present != 0;
     const int Is = has_sh ? dm.Is : 0;
     const int r2 = (has_sh && Ly.sh.ag) ? 2 * kRank : 0;
+    // straight-line: every load is issued, missing rows from the zero row
+    // (see zrow), so that no load result is merged at a branch
     const uint16_t* rp[kNR];
     int b, e;
-    A.n_router = 0;
-    if (Ly.router) {
-      split(E, G, cu, b, e);
-      A.n_router = e - b;
-      for (int j = 0; j < kNR; ++j) rp[j] = Ly.router + (int64_t)(b + (j < A.n_router ? j : 0)) * d;
-      f16rows_issue<kNR>(A.router, rp, A.n_router, d);
-    }
+    split(E, G, cu, b, e);
+    A.n_router = Ly.router ? e - b : 0;
+    for (int j = 0; j < kNR; ++j) rp[j] = Ly.router + (int64_t)(b + (j < A.n_router ? j : 0)) * d;
+    f16rows_issue<kNR>(A.router, rp, A.n_router, d);
     split(r2, G, cu, b, e);
     A.n_ax = e - b;
     for (int j = 0; j < kNR; ++j) {
       const int tt = b + (j < A.n_ax ? j : 0);
       rp[j] = (tt < kRank ? Ly.sh.ag : Ly.sh.au) + (int64_t)(tt % kRank) * d;
     }
-    if (A.n_ax) f16rows_issue<kNR>(A.ax, rp, A.n_ax, d);
-    A.attn = make_uint4(0, 0, 0, 0);
-    if (Ly.attn && t < d / 8) A.attn = ldg(reinterpret_cast<const uint4*>(Ly.attn + 8 * t));
-    A.gu_loaded = false;
-    if (!Ly.router) {
-      // routing known: entries from the tables
-      GuPlan pl;
-      split(K * I + Is, G, cu, pl.ib, pl.ie);
-      gu_issue<CPL_D, IPG, AFF>(A.gu, Ly, dm, ms.eptr[(l - a.l0) & 1], K * I, pl, grp, li);
-      A.gu_loaded = true;
-    }
+    f16rows_issue<kNR>(A.ax, rp, A.n_ax, d);
+    A.attn = ldg(pick(Ly.attn != nullptr && t < d / 8, reinterpret_cast<const uint4*>(Ly.attn + 8 * t)));
+    // routing known unless this is a router layer: entries from the tables
+    A.gu_loaded = !Ly.router;
+    GuPlan pl;
+    split(K * I + Is, G, cu, pl.ib, pl.ie);
+    gu_issue<CPL_D, IPG, AFF>(A.gu, Ly, dm, ms.eptr[(l - a.l0) & 1], K * I, pl, grp, li,
+                              A.gu_loaded);
   };
 
   for (int l = a.l0; l < a.l1; ++l) {
@@ -837,7 +854,7 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
       GuPlan pl;
       split(n_rt + Is, G, cu, pl.ib, pl.ie);
       if (!A.gu_loaded)
-        gu_issue<CPL_D, IPG, AFF>(A.gu, Ly, dm, ms.eptr[step & 1], n_rt, pl, grp, li);
+        gu_issue<CPL_D, IPG, AFF>(A.gu, Ly, dm, ms.eptr[step & 1], n_rt, pl, grp, li, true);
       vm_drained();  // gate/up rows, router and LoRA A rows have arrived
       float shg[IPG], shu[IPG];
       gu_finish<CPL_D, IPG, AFF>(A.gu, ent_k, n_rt, pl, grp, li, __builtin_ctz(dm.G), xperm,
