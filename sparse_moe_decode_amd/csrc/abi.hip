@@ -163,7 +163,7 @@ size_t scratch_layout(const Dims& dm, int B, char* base, Scratch* s) {
   const size_t n_d = (size_t)B * dm.d;
   const size_t n_p = (size_t)B * (dm.P > 0 ? dm.P : 1);
   const size_t n_e = (size_t)B * dm.E;
-  const size_t n_grp = 2 + 4 * (size_t)B * dm.K + 2 * (size_t)batched_max_tiles(B, dm.K, dm.E);
+  const size_t n_grp = batched_grp_ints(B, dm.K, dm.E);
   const size_t n_slot = (size_t)B * (dm.K + 1);
   const size_t n_axp = (size_t)kLoraSlices * B * 2 * rmax;
   auto up = [](size_t bytes) { return (bytes + 255) & ~(size_t)255; };

@@ -70,6 +70,16 @@ __host__ __device__ inline Groups groups(int32_t* g, int BK) {
   return {g, g + 1, g + 2, g + 2 + BK, g + 2 + 2 * BK, g + 2 + 3 * BK, g + 2 + 4 * BK};
 }
 
+// Work tile descriptors after the tables above (16-byte aligned), one int4
+// per tile of the launch grids (ny of them): member (-1 the shared expert),
+// first entry, token count (0: no tile), and the member's pool entry (-1
+// when its id does not resolve). k_mb_prep writes them where it forms the
+// tiles, so a gate/up or down workgroup reads everything it needs before
+// its weight loads in one load.
+__host__ __device__ inline int4* tile_descs(int32_t* g, int BK, int ny) {
+  return reinterpret_cast<int4*>(g + batched_desc_offset(BK, ny));
+}
+
 struct MbArgs {
   Dims dm;
   Pool pool;
@@ -79,6 +89,7 @@ struct MbArgs {
   uint16_t* xp;          // [B][d] pair-permuted copy
   int32_t* grp;
   int tile;              // tokens per work tile: 32 (chunk kernels) or 64 (prefill kernels)
+  int ny;                // work tiles the launch grids cover (an upper bound on the tiles)
   const int32_t* idx;    // [B][K]
   const float* w;        // [B][K]
   float* ax;             // [B][3*rmax] LoRA A products (down in slot 2)
@@ -171,13 +182,16 @@ __device__ void group_entries(const MbArgs& a) {
   const int off0 = ps - c0 - c1;
   int u = pu - (c0 > 0) - (c1 > 0);
   int tp = n_sh + pt - n0 - n1;
+  int4* td = tile_descs(a.grp, BK, a.ny);
   if (c0) {
     g.uexp[u] = 2 * t;
     g.ustart[u] = off0;
     g.ucount[u] = c0;
+    const int ent = (int)resolve_entry(a.pool, E, 2 * t);
     for (int j = 0; j < n0; ++j) {
       g.tiles[2 * tp] = u;
       g.tiles[2 * tp + 1] = j;
+      td[tp] = make_int4(u, off0 + a.tile * j, min(a.tile, c0 - a.tile * j), ent);
       ++tp;
     }
     ++u;
@@ -186,16 +200,23 @@ __device__ void group_entries(const MbArgs& a) {
     g.uexp[u] = 2 * t + 1;
     g.ustart[u] = off0 + c0;
     g.ucount[u] = c1;
+    const int ent = (int)resolve_entry(a.pool, E, 2 * t + 1);
     for (int j = 0; j < n1; ++j) {
       g.tiles[2 * tp] = u;
       g.tiles[2 * tp + 1] = j;
+      td[tp] = make_int4(u, off0 + c0 + a.tile * j, min(a.tile, c1 - a.tile * j), ent);
       ++tp;
     }
   }
   for (int j = t; j < n_sh; j += blockDim.x) {
     g.tiles[2 * j] = -1;
     g.tiles[2 * j + 1] = j;
+    td[j] = make_int4(-1, a.tile * j, min(a.tile, a.B - a.tile * j), 0);
   }
+  // tiles of the grids past the last one: no work
+  for (int y = n_sh + (wtot[2][0] + wtot[2][1]) + (wtot[2][2] + wtot[2][3]) + t; y < a.ny;
+       y += blockDim.x)
+    td[y] = make_int4(0, 0, 0, -1);
   if (t == blockDim.x - 1) {
     *g.n_union = pu;
     *g.n_tiles = n_sh + pt;
@@ -429,22 +450,17 @@ __device__ __forceinline__ void entry_of(const MbArgs& a, bool shared, int start
 }
 
 // Work tile y: the shared expert (dispatched first, it has the most tokens)
-// or union member u, with its first entry and token count (<= a.tile).
+// or a union member, with its first entry and token count (<= a.tile).
+// u: the member's pool entry (-1 when its id did not resolve; 0 for the
+// shared expert). One 16-byte read of the tile's descriptor.
 __device__ __forceinline__ bool tile_of(const MbArgs& a, int y, bool& shared, int& u, int& start,
                                         int& count) {
-  const Groups g = groups(a.grp, a.B * a.dm.K);
-  if (y >= *g.n_tiles) return false;
-  const int mem = g.tiles[2 * y], tile = g.tiles[2 * y + 1];
-  shared = mem < 0;
-  u = mem;
-  const int first = a.tile * tile;
-  if (shared) {
-    start = first;
-    count = min(a.tile, a.B - first);
-  } else {
-    start = g.ustart[mem] + first;
-    count = min(a.tile, g.ucount[mem] - first);
-  }
+  const uint4 v = ldg(reinterpret_cast<const uint4*>(tile_descs(a.grp, a.B * a.dm.K, a.ny) + y));
+  if ((int)v.z <= 0) return false;
+  shared = (int)v.x < 0;
+  start = (int)v.y;
+  count = (int)v.z;
+  u = (int)v.w;
   return true;
 }
 
@@ -501,9 +517,7 @@ void k_mb_gate_up(MbArgs a) {
       }
     }
   } else {
-    const Groups gv = groups(a.grp, a.B * K);
-    const int e = gv.uexp[u];
-    const int64_t ent = resolve_entry(a.pool, dm.E, e);
+    const int64_t ent = u;
     if (ent < 0) {
       if (threadIdx.x == 0) atomicOr(&a.flags[FLAG_RANGE], 1);
       return;
@@ -638,9 +652,7 @@ void k_mb_down(MbArgs a) {
     dq = a.sh.down.q; ds = a.sh.down.s;
     if (AFF) db = a.sh.down.b;
   } else {
-    const Groups gv = groups(a.grp, a.B * K);
-    const int e = gv.uexp[u];
-    const int64_t ent = resolve_entry(a.pool, dm.E, e);
+    const int64_t ent = u;
     if (ent < 0) return;  // flagged by the gate/up step
     dq = (const uint32_t*)entry_ptr(a.pool.down.q, ent, a.pool.stride_q);
     ds = (const uint16_t*)entry_ptr(a.pool.down.s, ent, a.pool.stride_s);
@@ -916,8 +928,7 @@ void k_pf_gate_up(MbArgs a) {
       ub = a.sh.up.b;
     }
   } else {
-    const Groups gv = groups(a.grp, a.B * K);
-    const int64_t ent = resolve_entry(a.pool, dm.E, gv.uexp[u]);
+    const int64_t ent = u;
     if (ent < 0) {
       if (threadIdx.x == 0) atomicOr(&a.flags[FLAG_RANGE], 1);
       return;
@@ -1125,8 +1136,7 @@ void k_pf_down(MbArgs a) {
     ds = a.sh.down.s;
     if (AFF) db = a.sh.down.b;
   } else {
-    const Groups gv = groups(a.grp, a.B * K);
-    const int64_t ent = resolve_entry(a.pool, dm.E, gv.uexp[u]);
+    const int64_t ent = u;
     if (ent < 0) return;  // flagged by the gate/up step
     dq = (const uint32_t*)entry_ptr(a.pool.down.q, ent, a.pool.stride_q);
     ds = (const uint16_t*)entry_ptr(a.pool.down.s, ent, a.pool.stride_s);
@@ -1377,6 +1387,7 @@ hipError_t launch_batched(const Dims& dm, const Pool& pool, const SharedW& sh, c
   a.tile = pf ? kPfTok : kCols;
   // an upper bound for either tile size; tiles past n_tiles exit at once
   const int ny = batched_max_tiles(B, dm.K, dm.E);
+  a.ny = ny;
   const int imax = dm.I > dm.Is ? dm.I : dm.Is;
   const int lora_blocks = sh.present && sh.ag ? (B + kCols - 1) / kCols * a.n_sl : 0;
   hipLaunchKernelGGL(k_mb_prep, dim3(B + 1 + lora_blocks), dim3(256), 0, st, a);

@@ -73,8 +73,8 @@ struct Scratch {
   float* sink_w;      // [B][K]
   int32_t* flags; // [N_FLAGS]
   // batched path (B >= 16 tokens)
-  int32_t* grp;   // [2 + 4 B K + 2 T] experts of the batch, their token runs and
-                  //                work tiles (T = batched_max_tiles)
+  int32_t* grp;   // [batched_grp_ints] experts of the batch, their token runs,
+                  //                work tiles and tile descriptors (T = batched_max_tiles)
   float* axp;     // [kLoraSlices][B][2 rmax] shared gate/up LoRA A products
                   //                over slices of the inputs
   float* yk;      // [B][K+1][d]    per-slot down outputs
@@ -132,6 +132,14 @@ bool batched_supported(const Dims& dm);
 inline int batched_max_tiles(int B, int K, int E) {
   const int BK = B * K;
   return (B + 31) / 32 + (BK < E ? BK : E) + (BK + 31) / 32;
+}
+// The grouping tables (int32): counts, sorted entries, union members and
+// their runs [2 + 4 B K], the tiles [2 T]; then, from this 16-byte aligned
+// offset, one int4 descriptor per tile [4 T].
+__host__ __device__ inline int batched_desc_offset(int BK, int ny) { return (2 + 4 * BK + 2 * ny + 3) & ~3; }
+inline size_t batched_grp_ints(int B, int K, int E) {
+  const int ny = batched_max_tiles(B, K, E);
+  return (size_t)batched_desc_offset(B * K, ny) + 4 * (size_t)ny;
 }
 hipError_t launch_batched(const Dims& dm, const Pool& pool, const SharedW& sh, const uint16_t* x,
                           const int32_t* idx, const float* w, int B, uint16_t* y,
