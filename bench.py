@@ -34,6 +34,8 @@ METRIC = "35B-tier decode layer-steps/s & tokens/s at B=1; HBM GB/s as % of MI35
 # layer_step kernel of each --path: its name, the sources it is built from
 # (the counter summaries record their hash) and its traffic summary
 PATH_KERNELS = {
+    "chain": ("k_chain", "persistent layer_step kernel with a layer-ahead weight slot",
+              ["chain.hip", "gemv.h", "device.h", "internal.h"]),
     "persistent": ("k_stack", "persistent layer_step kernel",
                    ["stack.hip", "gemv.h", "device.h", "internal.h"]),
     "flow": ("k_flow", "wave-specialised streaming layer_step kernel",
@@ -643,7 +645,8 @@ def run_layer(args):
                                     else (v.clone() if v is not None else None))
                                 for k, v in base.items()} for _ in range(copies - 1)]
             model = api.Model(ctx, layers)
-            model.set_path(api.PATH_PERSISTENT if args.path == "persistent" else api.PATH_FLOW)
+            model.set_path({"chain": api.PATH_CHAIN, "persistent": api.PATH_PERSISTENT,
+                        "flow": api.PATH_FLOW}[args.path])
             n = copies
             # per-step private routing / exec blocks [T+1][2][n][K]
             ri = np.zeros((T + 1, 2, n, K), np.int32)
@@ -721,9 +724,10 @@ def main():
                          "stack (--cache-entries: through the HBM hot cache); storage: the stack "
                          "with experts read from per-layer files; layer: single layer-steps, warm "
                          "and cold")
-    ap.add_argument("--path", choices=["persistent", "flow"], default="persistent",
-                    help="stack and layer workloads: layer_step kernel (persistent whole-token "
-                         "kernel, or the wave-specialised streaming kernel)")
+    ap.add_argument("--path", choices=["chain", "persistent", "flow"], default="persistent",
+                    help="stack and layer workloads: layer_step kernel (persistent kernel with a "
+                         "layer-ahead weight slot, persistent whole-token kernel, or the "
+                         "wave-specialised streaming kernel)")
     ap.add_argument("--reserve-cus", type=int, default=32,
                     help="staged workload: compute units left to the staging copies")
     ap.add_argument("--group", type=int, default=16,
@@ -800,7 +804,8 @@ def main():
 
     ctx = api.Context(dm, max_tokens=1)
     model = api.Model(ctx, layers)
-    model.set_path(api.PATH_PERSISTENT if args.path == "persistent" else api.PATH_FLOW)
+    model.set_path({"chain": api.PATH_CHAIN, "persistent": api.PATH_PERSISTENT,
+                        "flow": api.PATH_FLOW}[args.path])
     state = api.State(dm, L, head_logits=False)
     idx0, w0 = wl.initial_routing(tier, args.seed, L)
     state.route_idx[0].copy_(torch.from_numpy(idx0))

@@ -253,12 +253,18 @@ void e0_model_destroy(e0_model* model);
  * that the shapes and the layer range allow: the persistent whole-token
  * kernel (E0_PATH_PERSISTENT: d a multiple of 512 up to 2048, I = 512; both
  * int4 codecs), the wave-specialised streaming kernel (E0_PATH_FLOW:
- * symmetric int4, d 1536 or 2048, I = 512, group 64, K <= 8, E <= 256, rank
- * 0 or 16, at most 64 layers per launch), one kernel per phase
- * (E0_PATH_PHASES, any shape). Forcing FLOW or PERSISTENT fails with
- * E0_ERR_SHAPE when the shapes or the range do not fit it. All compute the
- * same step. */
-enum { E0_PATH_AUTO = 0, E0_PATH_PHASES = 1, E0_PATH_PERSISTENT = 2, E0_PATH_FLOW = 3 };
+ * symmetric int4, d 1536 or 2048, I = 512, group 64, K <= 8, E <= 256, rank 0
+ * or 16, at most 64 layers per launch), one kernel per phase
+ * (E0_PATH_PHASES, any shape). E0_PATH_CHAIN, taken only when asked for, is
+ * a persistent kernel that loads the next layer's weights while the current
+ * layer's exchanges run (symmetric int4, d 1536 or 2048, I = 512, group 64,
+ * K <= 8, E <= 512 and even, rank 0 or 16, at most 64 layers per launch, and
+ * per-workgroup shares that fit its plans); its exchange words carry the
+ * SwiGLU outputs rounded to 28 bits. Forcing CHAIN, FLOW or PERSISTENT fails
+ * with E0_ERR_SHAPE when the shapes or the range do not fit it. All compute
+ * the same step. */
+enum { E0_PATH_AUTO = 0, E0_PATH_PHASES = 1, E0_PATH_PERSISTENT = 2, E0_PATH_FLOW = 3,
+       E0_PATH_CHAIN = 4 };
 int e0_model_set_path(e0_model* model, int32_t path);
 
 /* Workgroups of the persistent kernels: one per compute unit by default (grid

@@ -125,7 +125,7 @@ EXPORTS = ["e0_create", "e0_destroy", "e0_last_error", "e0_device_status", "moe_
            "e0_store_open", "e0_store_close", "e0_store_read", "e0_store_wait", "e0_store_bytes", "e0_model_set_path", "e0_model_set_grid", "e0_model_set_trace", "e0_model_trace_shape",
            "e0_model_set_roles", "moe_int4_decode_static"]
 
-PATH_AUTO, PATH_PHASES, PATH_PERSISTENT, PATH_FLOW = 0, 1, 2, 3
+PATH_AUTO, PATH_PHASES, PATH_PERSISTENT, PATH_FLOW, PATH_CHAIN = 0, 1, 2, 3, 4
 QUANT_SYMMETRIC, QUANT_AFFINE = 0, 1
 
 
@@ -328,7 +328,8 @@ class Model:
         return self.trace
 
     def set_path(self, path: int):
-        """PATH_AUTO, PATH_PHASES (one kernel per phase), PATH_PERSISTENT (the
+        """PATH_AUTO, PATH_PHASES (one kernel per phase), PATH_CHAIN (the
+        persistent kernel with a layer-ahead weight slot), PATH_PERSISTENT (the
         whole-token kernel) or PATH_FLOW (the wave-specialised streaming kernel)."""
         _check(_lib.e0_model_set_path(self.handle, path))
 

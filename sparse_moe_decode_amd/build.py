@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libsmd.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["abi.hip", "kernels.hip", "stage.hip", "stack.hip", "flow.hip", "batched.hip", "store.cpp"]
+SOURCES = ["abi.hip", "kernels.hip", "stage.hip", "stack.hip", "chain.hip", "flow.hip", "batched.hip", "store.cpp"]
 ARCH = os.environ.get("SMD_OFFLOAD_ARCH", "gfx950")
 
 # Packed-FP32 instructions are disabled for all device code.

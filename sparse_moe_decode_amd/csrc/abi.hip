@@ -75,6 +75,7 @@ struct e0_model {
   uint64_t* fxbuf;
   int64_t fxwords;
   uint32_t fx_clean;  // every exchange word is zero or was written after this epoch
+  uint32_t cx_clean;  // the same for the packed words of the layer-ahead slot kernel (in xg)
   int32_t fng, fnd;  // explicit split (0, 0: automatic)
 };
 
@@ -487,6 +488,7 @@ int e0_model_create(e0_ctx* ctx, const e0_layer* layers, int32_t n_layers, e0_mo
   m->fxwords = 0;
   m->fng = m->fnd = 0;
   m->fx_clean = 0;
+  m->cx_clean = 0;
   const Dims& dm = ctx->dm;
   // Device table of the layers for the persistent kernel.
   std::vector<LayerDev> table(n_layers);
@@ -504,8 +506,10 @@ int e0_model_create(e0_ctx* ctx, const e0_layer* layers, int32_t n_layers, e0_mo
     const int Is = t.sh.present ? dm.Is : 0;
     const int r2 = (t.sh.present && t.sh.ag) ? 2 * dm.r : 0;
     // exchange words of a layer: routed SwiGLU outputs, shared SwiGLU
-    // outputs, the shared gate/up LoRA A products
-    const int n = dm.K * dm.I + Is + r2;
+    // outputs, (layer-ahead slot kernel, down LoRA) partial A_down products,
+    // the shared gate/up LoRA A products
+    const int n_ad = (t.sh.present && t.sh.ad) ? 16 * kChainSO : 0;
+    const int n = dm.K * dm.I + Is + n_ad + r2;
     if (n > ng) ng = n;
   }
   m->ng = ng;
@@ -608,9 +612,9 @@ int e0_model_set_roles(e0_model* model, int32_t n_gate_up, int32_t n_down) {
 }
 
 int e0_model_set_path(e0_model* model, int32_t path) {
-  if (!model || path < E0_PATH_AUTO || path > E0_PATH_FLOW)
+  if (!model || path < E0_PATH_AUTO || path > E0_PATH_CHAIN)
     return fail(E0_ERR_ARG, "e0_model_set_path: bad argument");
-  if (path == E0_PATH_PERSISTENT && !model->dev_table)
+  if ((path == E0_PATH_PERSISTENT || path == E0_PATH_CHAIN) && !model->dev_table)
     return fail(E0_ERR_SHAPE, "e0_model_set_path: shapes not supported by the persistent kernel");
   if (path == E0_PATH_FLOW && (!model->dev_table || !flow_supported(model->ctx->dm)))
     return fail(E0_ERR_SHAPE, "e0_model_set_path: shapes not supported by the streaming kernel");
@@ -718,6 +722,20 @@ int layer_step(e0_ctx* ctx, e0_model* model, int32_t layer_begin, int32_t layer_
     a.sink_w = s.sink_w;
     a.flags = s.flags;
     a.trace = model->trace;
+    if (model->path == E0_PATH_CHAIN && chain_launchable(a, model->grid)) {
+      // its packed exchange words carry the epoch mod 255: clear them before
+      // a tag can recur
+      if (a.epoch - model->cx_clean >= 255u) {
+        hipError_t e = launch_flow_clear(model->xg, (int64_t)L * model->ng, st);
+        if (e != hipSuccess) return hip_fail(e, "layer_step (exchange clear)");
+        model->cx_clean = a.epoch - 1;
+      }
+      hipError_t e = launch_chain(a, model->grid, st);
+      if (e != hipSuccess) return hip_fail(e, "layer_step (layer-ahead slot kernel)");
+      return E0_OK;
+    }
+    if (model->path == E0_PATH_CHAIN)
+      return fail(E0_ERR_SHAPE, "layer_step: this layer range does not fit the layer-ahead slot kernel");
     if (stack_launchable(a, model->grid)) {
       hipError_t e = launch_stack(a, model->grid, st);
       if (e != hipSuccess) return hip_fail(e, "layer_step (persistent kernel)");

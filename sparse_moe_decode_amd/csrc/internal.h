@@ -175,6 +175,15 @@ bool stack_supported(const Dims& dm);
 bool stack_launchable(const StackArgs& a, int grid);
 int stack_lds_bytes(const Dims& dm, int ng, int n_layers);
 hipError_t launch_stack(const StackArgs& a, int grid, hipStream_t st);
+// Persistent kernel with a layer-ahead weight slot (chain.hip): the same
+// arguments and exchange buffers; whether [l0, l1) on `grid` workgroups fits
+// its plans. Its SwiGLU exchange of a layer with a down LoRA also carries 16
+// partial A_down products from each of at most kChainSO workgroups (the ones
+// owning shared-expert rows), after the shared expert's words; the LoRA A
+// products of the gate/up follow them.
+constexpr int kChainSO = 64;
+bool chain_launchable(const StackArgs& a, int grid);
+hipError_t launch_chain(const StackArgs& a, int grid, hipStream_t st);
 
 
 // Wave-specialised persistent kernel (flow.hip): gate/up CUs [0, ng) and down

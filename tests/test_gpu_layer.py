@@ -49,7 +49,7 @@ def _run_and_check(api, orc, tier, roles, seed, T, check_layers, rho=0.5, zero_m
                            head=wl.tree_to_dev(lw["head"])))
     ctx = api.Context(dm, max_tokens=4)
     model = api.Model(ctx, layers)
-    model.set_path({"auto": api.PATH_AUTO, "phases": api.PATH_PHASES,
+    model.set_path({"auto": api.PATH_AUTO, "phases": api.PATH_PHASES, "chain": api.PATH_CHAIN,
                     "persistent": api.PATH_PERSISTENT, "flow": api.PATH_FLOW}[path])
     state = api.State(dm, L)
     idx0, w0 = wl.initial_routing(tier, seed, L)
@@ -82,7 +82,8 @@ def _run_and_check(api, orc, tier, roles, seed, T, check_layers, rho=0.5, zero_m
 
 
 @pytest.mark.parametrize("tier,T,path", [("tiny", 24, "phases"), ("8b", 5, "phases"),
-                                         ("35b", 5, "phases"), ("8b", 5, "persistent"),
+                                         ("35b", 5, "phases"), ("8b", 5, "chain"),
+                                         ("35b", 5, "chain"), ("8b", 5, "persistent"),
                                          ("35b", 5, "persistent"), ("8b", 5, "flow"),
                                          ("35b", 5, "flow")])
 def test_layer_step_two_layers(api, orc, tier, T, path):
@@ -93,7 +94,7 @@ def test_layer_step_two_layers(api, orc, tier, T, path):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("path", ["flow", "persistent", "phases"])
+@pytest.mark.parametrize("path", ["chain", "flow", "persistent", "phases"])
 def test_layer_step_stack_35b(api, orc, path):
     """Full 35B stack (40 layers, heads on 6-38) in the benchmark's launch
     configuration; every layer-step of the first tokens is checked."""
@@ -103,7 +104,7 @@ def test_layer_step_stack_35b(api, orc, path):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("path", ["flow", "persistent", "phases"])
+@pytest.mark.parametrize("path", ["chain", "flow", "persistent", "phases"])
 def test_layer_step_stack_8b(api, orc, path):
     roles = synth.stack_roles("8b")
     _run_and_check(api, orc, "8b", roles, seed=5, T=3, check_layers=list(range(24)),
@@ -173,25 +174,27 @@ def test_layer_step_64_layers_flow(api, orc):
 
 
 @pytest.mark.timeout(900)
-def test_layer_step_64_layers_persistent(api, orc):
-    """The largest launch of the persistent kernel: 64 layers (8B shapes, 32
+@pytest.mark.parametrize("path", ["chain", "persistent"])
+def test_layer_step_64_layers_persistent(api, orc, path):
+    """The largest launch of the persistent kernels: 64 layers (8B shapes, 32
     experts), routers on the first and last layer, heads on all but the
     last; every layer-step of two tokens against the oracle. A 65-layer range
-    cannot be forced onto the persistent kernel (E0_ERR_SHAPE) and runs per
-    phase on the automatic path."""
+    cannot be forced onto either kernel (E0_ERR_SHAPE) and runs per phase on
+    the automatic path."""
     import torch
     from sparse_moe_decode_amd import workloads as wl
     L, seed = 64, 17
     dm, roles, layers, keep, state = _long_stack(api, L, 32, seed)
     ctx = api.Context(dm, max_tokens=1)
     model = api.Model(ctx, layers)
-    model.set_path(api.PATH_PERSISTENT)
+    pid = {"chain": api.PATH_CHAIN, "persistent": api.PATH_PERSISTENT}[path]
+    model.set_path(pid)
     toks = wl.token_inputs("8b", seed, 2, 0.5)
     checker = StackChecker(orc, "8b", seed, roles, list(range(L)), keep, zero_mean=True, dims=dm)
     prev_exec = None
     h = torch.empty((L + 1, dm["d"]), dtype=torch.float16, device="cuda")
     for t in range(2):
-        announce("layer_step", "8b", "persistent", f"L={L}", f"token {t}")
+        announce("layer_step", "8b", path, f"L={L}", f"token {t}")
         h[0].copy_(torch.from_numpy(toks[t]))
         api.layer_step(ctx, model, 0, L, state, t, h)
         assert api.device_status(ctx) == 0
@@ -202,16 +205,16 @@ def test_layer_step_64_layers_persistent(api, orc):
                       host(state.route_w[cur]).copy(), host(state.route_idx[nxt]).copy(),
                       host(state.route_w[nxt]).copy(), host(state.head_logits).copy())
         prev_exec = exec_idx
-    print(f"8b E=32 persistent L={L}: {checker.steps} layer-steps checked, worst error ratio "
+    print(f"8b E=32 {path} L={L}: {checker.steps} layer-steps checked, worst error ratio "
           f"{checker.worst:.3f}")
     model.close()
 
     L2 = L + 1
     dm2, roles2, layers2, keep2, state2 = _long_stack(api, L2, 32, seed + 1)
     model2 = api.Model(ctx, layers2)
-    model2.set_path(api.PATH_PERSISTENT)
+    model2.set_path(pid)
     h2 = torch.zeros((L2 + 1, dm["d"]), dtype=torch.float16, device="cuda")
-    announce("layer_step", "8b", "persistent refused", f"L={L2}")
+    announce("layer_step", "8b", f"{path} refused", f"L={L2}")
     with pytest.raises(api.E0Error) as err:
         api.layer_step(ctx, model2, 0, L2, state2, 0, h2)
     assert err.value.code == api.E0_ERR_SHAPE
@@ -226,7 +229,7 @@ def test_layer_step_64_layers_persistent(api, orc):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("path", ["flow", "persistent", "phases"])
+@pytest.mark.parametrize("path", ["chain", "flow", "persistent", "phases"])
 def test_layer_step_bitwise_deterministic(api, path):
     """Two runs of the 35B stack (40 layers, three tokens) from the same
     state give the same bits: every layer's residual, executed set and
@@ -249,8 +252,8 @@ def test_layer_step_bitwise_deterministic(api, path):
                            router_bias=None, head=wl.tree_to_dev(lw["head"])))
     ctx = api.Context(dm, max_tokens=1)
     model = api.Model(ctx, layers)
-    model.set_path({"persistent": api.PATH_PERSISTENT, "flow": api.PATH_FLOW,
-                    "phases": api.PATH_PHASES}[path])
+    model.set_path({"chain": api.PATH_CHAIN, "persistent": api.PATH_PERSISTENT,
+                    "flow": api.PATH_FLOW, "phases": api.PATH_PHASES}[path])
     idx0, w0 = wl.initial_routing(tier, seed, L)
     toks = wl.token_inputs(tier, seed, T)
     runs = []

@@ -50,7 +50,7 @@ def test_staged_stack_matches_oracle(api, orc, tier, T, reserve, group, quant):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("path", ["persistent", "flow"])
+@pytest.mark.parametrize("path", ["chain", "persistent", "flow"])
 def test_staged_stack_bench_shape(api, orc, path):
     """The benchmark's staged configuration: the 35B stack's 40 layers (own
     routers on 0-6 and 39, 32 predicted layers staged through slots),
@@ -96,8 +96,8 @@ def _staged_run(api, orc, tier, roles, dm, T, reserve, group, quant, seed=41, pa
     host_dev = host_pool.to("cuda")
     stager = api.Stager(ctx, host_pool, len(cons), n_slots, hbm, slot_of, slot_expert)
     model = api.Model(ctx, layers)
-    model.set_path({"auto": api.PATH_AUTO, "persistent": api.PATH_PERSISTENT,
-                    "flow": api.PATH_FLOW}[path])
+    model.set_path({"auto": api.PATH_AUTO, "chain": api.PATH_CHAIN,
+                    "persistent": api.PATH_PERSISTENT, "flow": api.PATH_FLOW}[path])
     state = api.State(dm, L)
     rng = synth.rng_for(seed, 10_000)
     idx0 = np.stack([synth.random_set(rng, E, K) for _ in range(L)])

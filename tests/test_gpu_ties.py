@@ -95,7 +95,7 @@ def test_prerouter_exact_ties(api, orc, tier):
 
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("tier", ["35b", "8b"])
-@pytest.mark.parametrize("path", ["flow", "persistent", "phases"])
+@pytest.mark.parametrize("path", ["chain", "flow", "persistent", "phases"])
 def test_layer_step_exact_ties(api, orc, tier, path):
     """A router layer with paired rows and heads with integer logits: every
     router set and prediction must equal the oracle's, no re-anchoring."""
@@ -116,7 +116,7 @@ def test_layer_step_exact_ties(api, orc, tier, path):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("path", ["flow", "persistent", "phases"])
+@pytest.mark.parametrize("path", ["chain", "flow", "persistent", "phases"])
 def test_layer_step_near_tie_reanchors(api, orc, path):
     from sparse_moe_decode_amd import workloads as wl
     tier, seed = "35b", 44
