@@ -205,4 +205,24 @@ __device__ __forceinline__ void split_hilo(float v, float inv_scale, f16& hi, f1
   lo = (f16)(t - (float)hi);
 }
 
+// Packed exchange words: two fp32 values rounded to 28 bits (19 stored
+// mantissa bits, round to nearest even; relative error <= 2^-20) under an
+// 8-bit launch tag in the top byte. The tag is 1 + epoch % 255; the host
+// clears the buffer before a tag can recur.
+__device__ __forceinline__ uint32_t round28(float v) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  return (b + 0x7u + ((b >> 4) & 1u)) >> 4;
+}
+__device__ __forceinline__ void put2(uint64_t* p, float v0, float v1, uint32_t tag) {
+  const uint64_t w = ((uint64_t)tag << 56) | ((uint64_t)(round28(v0) & 0xFFFFFFFu) << 28) |
+                     (uint64_t)(round28(v1) & 0xFFFFFFFu);
+  __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// The two values of a packed word given as its low and high 32-bit halves.
+__device__ __forceinline__ float2 unpack2(uint32_t lo, uint32_t hi) {
+  const uint32_t r0 = ((hi & 0x00FFFFFFu) << 4) | (lo >> 28);
+  const uint32_t r1 = lo & 0x0FFFFFFFu;
+  return make_float2(__builtin_bit_cast(float, r0 << 4), __builtin_bit_cast(float, r1 << 4));
+}
+
 }  // namespace smd
