@@ -482,12 +482,18 @@ __device__ __forceinline__ bool tile_block(const MbArgs& a, int& bx, bool& share
 // x over the group) for its groups, from sums staged in LDS.
 // (The affine variant's bias terms need more registers: it keeps one
 // workgroup per compute unit.)
+constexpr int kXsTok = 8;            // tiles of up to this many tokens stage x in LDS
+typedef __attribute__((address_space(3))) void lptr_v;
+typedef __attribute__((address_space(1))) void gptr_v;
+constexpr int kXsRow = 2048 + 8;     // staged row stride (fp16; 16-byte pad against bank conflicts)
+
 template <int NG, bool AFF>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(AFF ? 2 : 4)))
 void k_mb_gate_up(MbArgs a) {
   __shared__ float red[2][4][16][64];
   __shared__ float axs[kCols][2][kMaxR];
   __shared__ float xss[AFF ? kCols : 1][32];  // [tile token][input group]
+  __shared__ uint16_t xsl[kXsTok * kXsRow];  // the tile's activations (count <= kXsTok)
   const Dims& dm = a.dm;
   const int K = dm.K, d = dm.d;
   const int imax = dm.I > dm.Is ? dm.I : dm.Is;
@@ -540,11 +546,15 @@ void k_mb_gate_up(MbArgs a) {
   const int nr = 4 * ((count + 7) >> 3);
   const uint32_t* qrow = wq + (int64_t)(m0 + n) * wpr + 4 * kh;
   const uint16_t* srow = ws + (int64_t)(m0 + n) * ngs;
+  // Small tiles (most of a decode chunk's) stage their token rows in LDS
+  // once (direct-to-LDS loads, issued after the weight loads), so the eight
+  // waves read their activations there instead of each loading them.
+  const bool xlds = count <= kXsTok && d + 8 <= kXsRow && d % 512 == 0;
   // Token rows past count read a valid row (the last one): their outputs
   // land in accumulator rows that are never stored.
   int bt, kt;
-  entry_of(a, shared, start, n < count ? n : count - 1, bt, kt);
-  const uint16_t* xrow = a.xp + (int64_t)bt * d + 32 * kh + 64 * g0;
+  if (!xlds) entry_of(a, shared, start, n < count ? n : count - 1, bt, kt);
+  const uint16_t* xrow = xlds ? nullptr : a.xp + (int64_t)bt * d + 32 * kh + 64 * g0;
   uint4 wv[NG];
   float sv[NG], bv[NG];
 #pragma unroll
@@ -561,17 +571,44 @@ void k_mb_gate_up(MbArgs a) {
   // a compute unit, so one's loads overlap the other's MFMAs and epilogue
   constexpr int NH = NG / 2;
   f32x16 acc = {};
+  if (xlds) {
+    // 1 KB pieces (512 inputs of one token row), one per wave instruction:
+    // piece q of the tile is row q / (d / 512), part q % (d / 512)
+    const int ppr = d / 512;
+    for (int q = wave; q < count * ppr; q += 8) {
+      const int tt = q / ppr, c = q - tt * ppr;
+      int b, k;
+      entry_of(a, shared, start, tt, b, k);
+      __builtin_amdgcn_global_load_lds(
+          (gptr_v*)(a.xp + (int64_t)b * d + 512 * c + 8 * l),
+          (lptr_v*)(xsl + tt * kXsRow + 512 * c), 16, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the staged rows (and the weights) are in
+    __syncthreads();
+    const uint16_t* xl = xsl + (n < count ? n : count - 1) * kXsRow + 32 * kh + 64 * g0;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    uint4 xv[NH][4];
+    for (int h = 0; h < 2; ++h) {
+      uint4 xv[NH][4];
 #pragma unroll
-    for (int i = 0; i < NH; ++i)
+      for (int i = 0; i < NH; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        xv[i][j] = ldg(reinterpret_cast<const uint4*>(xrow + 64 * (NH * h + i) + 8 * j));
-    // one variant for all counts: a second (fewer registers scaled) costs
-    // the register allocator more than it saves
-    gu_mma<NG, NH, 16, AFF>(acc, wv, sv, xv, NH * h);
+        for (int j = 0; j < 4; ++j)
+          xv[i][j] = *reinterpret_cast<const uint4*>(xl + 64 * (NH * h + i) + 8 * j);
+      gu_mma<NG, NH, 16, AFF>(acc, wv, sv, xv, NH * h);
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint4 xv[NH][4];
+#pragma unroll
+      for (int i = 0; i < NH; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          xv[i][j] = ldg(reinterpret_cast<const uint4*>(xrow + 64 * (NH * h + i) + 8 * j));
+      // one variant for all counts: a second (fewer registers scaled) costs
+      // the register allocator more than it saves
+      gu_mma<NG, NH, 16, AFF>(acc, wv, sv, xv, NH * h);
+    }
   }
   if (AFF) {
 #pragma unroll
