@@ -547,9 +547,9 @@ void k_mb_gate_up(MbArgs a) {
   const uint32_t* qrow = wq + (int64_t)(m0 + n) * wpr + 4 * kh;
   const uint16_t* srow = ws + (int64_t)(m0 + n) * ngs;
   // Small tiles (most of a decode chunk's) stage their token rows in LDS
-  // once (direct-to-LDS loads, issued after the weight loads), so the eight
-  // waves read their activations there instead of each loading them.
-  const bool xlds = count <= kXsTok && d + 8 <= kXsRow && d % 512 == 0;
+  // (direct-to-LDS loads, issued after the weight loads), so a wave reads
+  // its activations there instead of loading them per lane.
+  const bool xlds = count <= kXsTok && d + 8 <= kXsRow;
   // Token rows past count read a valid row (the last one): their outputs
   // land in accumulator rows that are never stored.
   int bt, kt;
@@ -572,19 +572,18 @@ void k_mb_gate_up(MbArgs a) {
   constexpr int NH = NG / 2;
   f32x16 acc = {};
   if (xlds) {
-    // 1 KB pieces (512 inputs of one token row), one per wave instruction:
-    // piece q of the tile is row q / (d / 512), part q % (d / 512)
-    const int ppr = d / 512;
-    for (int q = wave; q < count * ppr; q += 8) {
-      const int tt = q / ppr, c = q - tt * ppr;
+    // each wave stages its own quarter of every token row (the gate and the
+    // up wave of a quarter write the same bytes), so a wave waits only for
+    // its own loads: one instruction per row, 16 bytes a lane
+    const int qw = 64 * NG;  // inputs of a quarter
+    for (int tt = 0; tt < count; ++tt) {
       int b, k;
       entry_of(a, shared, start, tt, b, k);
-      __builtin_amdgcn_global_load_lds(
-          (gptr_v*)(a.xp + (int64_t)b * d + 512 * c + 8 * l),
-          (lptr_v*)(xsl + tt * kXsRow + 512 * c), 16, 0, 0);
+      if (8 * l < qw)
+        __builtin_amdgcn_global_load_lds((gptr_v*)(a.xp + (int64_t)b * d + qw * quarter + 8 * l),
+                                         (lptr_v*)(xsl + tt * kXsRow + qw * quarter), 16, 0, 0);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the staged rows (and the weights) are in
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's rows (and weights) are in
     const uint16_t* xl = xsl + (n < count ? n : count - 1) * kXsRow + 32 * kh + 64 * g0;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
