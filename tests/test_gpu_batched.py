@@ -5,8 +5,10 @@ moe_int4_decode with B >= 16 groups the batch's B*K entries by expert in one
 launch and runs tiles of up to 32 of an expert's tokens, each reading the
 expert's weights once. Decode chunks: every token's output is compared with
 the oracle's moe_decode for its own routing, 35B shapes with top-K in
-{2, 4, 8} and 8B shapes, B = 32, a partial tile (20) and two tiles (40); two
-runs are bitwise equal; an out-of-range id is flagged.
+{2, 4, 8} and 8B shapes, B = 32, a partial tile (20) and two tiles (40);
+routed tiles of exactly 1, 8, 9 and 32 tokens (either side of the gate/up
+kernel's LDS staging bound); two runs are bitwise equal; an out-of-range id
+is flagged.
 
 Prefill-sized batches (the whole-layer path; from 16 entries per expert on
 average, B*K >= 16 E, they take the prefill kernels with 64-token tiles):
@@ -93,6 +95,44 @@ def test_batched_chunk_parity(api, orc, pools, tier, K, B):
     union = len(np.unique(idx))
     print(f"{tier} K={K} B={B}: worst error ratio {worst:.3f}, union {union} experts, "
           f"{ev0.elapsed_time(ev1) / 10 * 1e3:.1f} us per call")
+
+
+@pytest.mark.parametrize("n_a,n_b", [(8, 9), (1, 32)])
+def test_batched_chunk_tile_sizes(api, orc, pools, n_a, n_b):
+    """Routed tiles of exactly n_a and n_b tokens (K = 2, B = 32): 8 and 9
+    straddle the gate/up kernel's switch from activations staged in LDS (up
+    to 8 tokens) to activations loaded per lane; 1 and 32 are a one-token
+    tile and a full routed tile. Every token against the oracle, and two runs
+    bitwise equal."""
+    dm = synth.dims("35b", K=2)
+    pool, sh = pools["35b"]
+    announce("batched chunk tile sizes", f"{n_a}/{n_b}")
+    ctx = api.Context(dm, max_tokens=32)
+    B, E = 32, dm["E"]
+    rng = np.random.default_rng(64 + n_a)
+    a_id, b_id = 17, 200
+    others = np.array([e for e in range(E) if e not in (a_id, b_id)])
+    idx = np.zeros((B, 2), np.int32)
+    for b in range(B):
+        if n_b == B:  # expert b_id in every token, a_id in the first n_a
+            idx[b] = [b_id, a_id if b < n_a else rng.choice(others)]
+        else:  # a_id in tokens [0, n_a), b_id in [n_a, n_a + n_b)
+            first = a_id if b < n_a else (b_id if b < n_a + n_b else rng.choice(others))
+            second = rng.choice(others)
+            idx[b] = [first, second]
+    assert (idx == a_id).sum() == n_a and (idx == b_id).sum() == n_b
+    x = rng.normal(size=(B, dm["d"]))
+    x = (x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + 1e-6)).astype(np.float16)
+    w = np.stack([synth.random_weights(rng, 2) for _ in range(B)]).astype(np.float32)
+    dpool, dsh, dx, didx, dw = dev_tree(pool), dev_tree(sh), dev(x), dev(idx), dev(w)
+    y = api.moe_int4_decode(ctx, dpool, dx, didx, dw, shared=dsh)
+    y2 = api.moe_int4_decode(ctx, dpool, dx, didx, dw, shared=dsh)
+    assert api.device_status(ctx) == 0
+    assert np.array_equal(host(y).view(np.uint16), host(y2).view(np.uint16)), "not deterministic"
+    yg = f16_to_f64(y)
+    for b in range(B):
+        ref = orc.moe_decode(dm, pool, sh, x[b], idx[b], w[b].astype(np.float64))
+        assert_out_close(yg[b], ref, f"tiles {n_a}/{n_b} token {b}")
 
 
 def test_batched_bad_id_is_flagged(api, pools):
