@@ -100,6 +100,30 @@ __device__ __forceinline__ float q4_dot32_hl_ilp(uint4 wv, const f16x2* xh, cons
   return (p0 + p1) + (p2 + p3);
 }
 
+// 32 int4 weights of one 16-byte chunk against 32 fp32 activations (natural
+// order, 16-byte aligned in LDS): each product q * s is formed and
+// accumulated in fp32 (v_fma_mix takes the exact fp16 q).
+__device__ __forceinline__ float q4_dot32_f32(uint4 wv, const float* s) {
+  const uint32_t w4[4] = {wv.x, wv.y, wv.z, wv.w};
+  float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    f16x2 p0, p1, p2, p3;
+    q4_pairs(w4[m], p0, p1, p2, p3);
+    const float4 x0 = *reinterpret_cast<const float4*>(s + 8 * m);
+    const float4 x1 = *reinterpret_cast<const float4*>(s + 8 * m + 4);
+    a0 = fmaf((float)p0.x, x0.x, a0);
+    a1 = fmaf((float)p0.y, x1.x, a1);
+    a0 = fmaf((float)p1.x, x0.y, a0);
+    a1 = fmaf((float)p1.y, x1.y, a1);
+    a0 = fmaf((float)p2.x, x0.z, a0);
+    a1 = fmaf((float)p2.y, x1.z, a1);
+    a0 = fmaf((float)p3.x, x0.w, a0);
+    a1 = fmaf((float)p3.y, x1.w, a1);
+  }
+  return a0 + a1;
+}
+
 // Block-wide max of |v| over a strided range (kBlock threads).
 __device__ __forceinline__ float block_absmax(const float* v, int n, float* red) {
   float m = 0.0f;

@@ -152,10 +152,14 @@ __device__ __forceinline__ void ll_gather(const uint64_t* src, int n, uint32_t e
 // flight (agent-scope buffer loads, so a poll is one request for both
 // words). src 16-byte aligned and n even; otherwise the 8-byte gather.
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
-template <int U>
+// PAD: word i goes to dst[pad32(i)] (four words of padding after every 32),
+// so 16-lane groups reading 32 consecutive words per lane hit distinct banks.
+__device__ __forceinline__ int pad32(int i) { return i + 4 * (i >> 5); }
+
+template <int U, bool PAD = false>
 __device__ __forceinline__ void ll_gather2(const uint64_t* src, int n, uint32_t ep, uint32_t* dst,
                                            int32_t* flags, int* abort_lds) {
-  if ((n & 1) || (reinterpret_cast<uintptr_t>(src) & 15)) {
+  if (!PAD && ((n & 1) || (reinterpret_cast<uintptr_t>(src) & 15))) {
     ll_gather<2 * U>(src, n, ep, dst, flags, abort_lds);
     return;
   }
@@ -190,8 +194,9 @@ __device__ __forceinline__ void ll_gather2(const uint64_t* src, int n, uint32_t 
     for (int j = 0; j < U; ++j) {
       const int p = b0 + j * kThreads + (int)threadIdx.x;
       if (p < np) {
-        dst[2 * p] = v[j].x;
-        dst[2 * p + 1] = v[j].z;
+        const int i = PAD ? pad32(2 * p) : 2 * p;
+        dst[i] = v[j].x;
+        dst[i + 1] = v[j].z;
       }
     }
   }
@@ -294,7 +299,7 @@ __host__ __device__ inline Lds lds_layout(const Dims& dm, int ng, int nl) {
   o.hattn = off; off += up(dm.d * 4);
   o.xperm = off; off += up(dm.d * 2);
   o.xnat = off; off += up(dm.d * 2);
-  int land = ng;
+  int land = ng + ng / 8;  // the SwiGLU outputs land padded (pad32)
   if (dm.d / 2 > land) land = dm.d / 2;
   if (dm.E > land) land = dm.E;
   if (kHX * (dm.P + dm.E) > land) land = kHX * (dm.P + dm.E);
@@ -882,7 +887,7 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
 
     // ---- 4. gather SwiGLU outputs; finish the shared expert ----------------
     const int ng_l = n_rt + Is;
-    ll_gather2<8>(xg, ng_l, ep, land, a.flags, &ms.abort);
+    ll_gather2<8, true>(xg, ng_l, ep, land, a.flags, &ms.abort);
     vm_drained();
     __syncthreads();
     stamp(a, l, 6);
@@ -892,14 +897,14 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
       const float* lf = (const float*)land;
       if (has_sh) {
         // the shared expert's SwiGLU outputs, LoRA terms included
-        const float2 hb = *reinterpret_cast<const float2*>(lf + n_rt + 2 * t);
-        const float h0 = hb.x, h1 = hb.y;
-        const float sc = hilo_pair(h0, h1, grp, li, hk + K * 2 * I, I,
-                                   AFF ? &ms.hsum[K][grp] : nullptr);
-        if (li == 0) ms.csc[K][grp] = sc;
+        if (AFF) {
+          const float2 hb = *reinterpret_cast<const float2*>(lf + pad32(n_rt + 2 * t));
+          const float sc = hilo_pair(hb.x, hb.y, grp, li, hk + K * 2 * I, I, &ms.hsum[K][grp]);
+          if (li == 0) ms.csc[K][grp] = sc;
+        }
         if (lora_d) {
           // rank grp of A_down h: the lane's 32 columns, then the group's sum
-          const float4* hp = reinterpret_cast<const float4*>(lf + n_rt + 32 * li);
+          const float4* hp = reinterpret_cast<const float4*>(lf + pad32(n_rt + 32 * li));
           float p = 0.0f;
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
@@ -916,23 +921,25 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
           if (li == 0) ms.ad[grp] = p;
         }
       }
-      // An unresolved expert's outputs are zeros (never used: its down rows
-      // are zero too). With K == NX - 1 the loop is unrolled without
-      // branches, so the experts' conversions interleave.
-      if (K == NX - 1) {
+      // Affine codec: fp16 hi + lo copies (the bias terms take each chunk's
+      // sum of hi + lo). The symmetric codec's down rows read the fp32
+      // outputs in place. An unresolved expert's outputs are zeros (never
+      // used: its down rows are zero too). With K == NX - 1 the loop is
+      // unrolled without branches, so the experts' conversions interleave.
+      if (AFF) {
+        if (K == NX - 1) {
 #pragma unroll
-        for (int k = 0; k < NX - 1; ++k) {
-          const float2 v = *reinterpret_cast<const float2*>(lf + k * I + 32 * grp + 2 * li);
-          const float sc = hilo_pair(v.x, v.y, grp, li, hk + k * 2 * I, I,
-                                     AFF ? &ms.hsum[k][grp] : nullptr);
-          if (li == 0) ms.csc[k][grp] = sc;
-        }
-      } else {
-        for (int k = 0; k < K; ++k) {
-          const float2 v = *reinterpret_cast<const float2*>(lf + k * I + 32 * grp + 2 * li);
-          const float sc = hilo_pair(v.x, v.y, grp, li, hk + k * 2 * I, I,
-                                     AFF ? &ms.hsum[k][grp] : nullptr);
-          if (li == 0) ms.csc[k][grp] = sc;
+          for (int k = 0; k < NX - 1; ++k) {
+            const float2 v = *reinterpret_cast<const float2*>(lf + pad32(k * I + 32 * grp + 2 * li));
+            const float sc = hilo_pair(v.x, v.y, grp, li, hk + k * 2 * I, I, &ms.hsum[k][grp]);
+            if (li == 0) ms.csc[k][grp] = sc;
+          }
+        } else {
+          for (int k = 0; k < K; ++k) {
+            const float2 v = *reinterpret_cast<const float2*>(lf + pad32(k * I + 32 * grp + 2 * li));
+            const float sc = hilo_pair(v.x, v.y, grp, li, hk + k * 2 * I, I, &ms.hsum[k][grp]);
+            if (li == 0) ms.csc[k][grp] = sc;
+          }
         }
       }
       __syncthreads();
@@ -945,32 +952,35 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
       // Slots without an expert (unresolved ids, no shared expert, k > K)
       // hold zero weights and a zero coefficient; with K == NX - 1 the loop
       // runs without branches so that the slots' LDS reads interleave.
+      const float* lf = (const float*)land;
       if (K == NX - 1 && has_sh) {
 #pragma unroll
         for (int k = 0; k < NX; ++k) {
-          const uint16_t* hh = hk + (int64_t)k * 2 * I;
-          f16x2 xh[16], xl[16];
-          load_xchunk(hh, li, xh);
-          load_xchunk(hh + I, li, xl);
-          if (AFF)
+          if (AFF) {
+            const uint16_t* hh = hk + (int64_t)k * 2 * I;
+            f16x2 xh[16], xl[16];
+            load_xchunk(hh, li, xh);
+            load_xchunk(hh + I, li, xl);
             acc += (ms.coef[k] * ms.csc[k][li]) *
                    (bf2f(D.s[k]) * q4_dot32_hl<true>(D.w[k], xh, xl) + bf2f(D.b[k]) * ms.hsum[k][li]);
-          else
-            acc += (ms.coef[k] * ms.csc[k][li]) * (h2f(D.s[k]) * q4_dot32_hl(D.w[k], xh, xl));
+          } else {
+            acc += ms.coef[k] * (h2f(D.s[k]) * q4_dot32_f32(D.w[k], lf + pad32(k * I + 32 * li)));
+          }
         }
       } else {
 #pragma unroll
         for (int k = 0; k < NX; ++k) {
           if (!ms.dq[k]) continue;
-          const uint16_t* hh = hk + (int64_t)k * 2 * I;
-          f16x2 xh[16], xl[16];
-          load_xchunk(hh, li, xh);
-          load_xchunk(hh + I, li, xl);
-          if (AFF)
+          if (AFF) {
+            const uint16_t* hh = hk + (int64_t)k * 2 * I;
+            f16x2 xh[16], xl[16];
+            load_xchunk(hh, li, xh);
+            load_xchunk(hh + I, li, xl);
             acc += (ms.coef[k] * ms.csc[k][li]) *
                    (bf2f(D.s[k]) * q4_dot32_hl<true>(D.w[k], xh, xl) + bf2f(D.b[k]) * ms.hsum[k][li]);
-          else
-            acc += (ms.coef[k] * ms.csc[k][li]) * (h2f(D.s[k]) * q4_dot32_hl(D.w[k], xh, xl));
+          } else {
+            acc += ms.coef[k] * (h2f(D.s[k]) * q4_dot32_f32(D.w[k], lf + pad32(k * I + 32 * li)));
+          }
         }
       }
       if (lora_d && li == 0) {
