@@ -103,13 +103,16 @@ __device__ __forceinline__ float q4_dot32_hl_ilp(uint4 wv, const f16x2* xh, cons
 // 32 int4 weights of one 16-byte chunk against 32 fp32 activations (natural
 // order, 16-byte aligned in LDS): each product q * s is formed and
 // accumulated in fp32 (v_fma_mix takes the exact fp16 q).
-__device__ __forceinline__ float q4_dot32_f32(uint4 wv, const float* s) {
+// AFF: unsigned nibbles (the affine codec); with xsum non-null the sum of
+// the 32 activations is written there as well (the bias term's factor).
+template <bool AFF = false>
+__device__ __forceinline__ float q4_dot32_f32(uint4 wv, const float* s, float* xsum = nullptr) {
   const uint32_t w4[4] = {wv.x, wv.y, wv.z, wv.w};
-  float a0 = 0.0f, a1 = 0.0f;
+  float a0 = 0.0f, a1 = 0.0f, sx = 0.0f;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     f16x2 p0, p1, p2, p3;
-    q4_pairs(w4[m], p0, p1, p2, p3);
+    q4_pairs<AFF>(w4[m], p0, p1, p2, p3);
     const float4 x0 = *reinterpret_cast<const float4*>(s + 8 * m);
     const float4 x1 = *reinterpret_cast<const float4*>(s + 8 * m + 4);
     a0 = fmaf((float)p0.x, x0.x, a0);
@@ -120,7 +123,9 @@ __device__ __forceinline__ float q4_dot32_f32(uint4 wv, const float* s) {
     a1 = fmaf((float)p2.y, x1.z, a1);
     a0 = fmaf((float)p3.x, x0.w, a0);
     a1 = fmaf((float)p3.y, x1.w, a1);
+    if (xsum) sx += ((x0.x + x0.y) + (x0.z + x0.w)) + ((x1.x + x1.y) + (x1.z + x1.w));
   }
+  if (xsum) *xsum = sx;
   return a0 + a1;
 }
 

@@ -252,7 +252,6 @@ struct Misc {
   const uint32_t* dq[kMaxExp];
   const uint16_t* dsc[kMaxExp];
   float coef[16];
-  float csc[kMaxExp][16];      // power-of-two scale of each 32-element hi/lo chunk
   float ad[kRank];             // A_down . h_shared
   float axgu[2 * kRank];       // A_gate x then A_up x (rows of the shared expert)
   // base addresses of a layer's experts (slot k < K routed, k == K shared;
@@ -260,10 +259,9 @@ struct Misc {
   // down s, then (affine codec) gate b, up b, down b. Two sets by layer
   // parity: the next layer's is written while the current one is read.
   const void* eptr[2][kMaxExp][kEp];
-  // affine codec: sums of the normed x over each 32-element chunk, and of
-  // each expert's hi + lo SwiGLU chunk (the bias terms b * sum)
+  // affine codec: sums of the normed x over each 32-element chunk (the
+  // gate/up bias terms b * sum)
   float xsum[64];
-  float hsum[kMaxExp][16];
   float hsc[kHX][16];          // scales of the fc2 activation chunks (per lane)
   float red[4 * kNR];
   float rows[kNR];             // results of the block fp16 row jobs
@@ -285,7 +283,7 @@ struct Misc {
 
 struct Lds {
   // byte offsets into dynamic LDS
-  int hattn, xperm, xnat, land, hk, ha, hx, misc, lay;
+  int hattn, xperm, xnat, land, ha, hx, misc, lay;
   int bytes;
 };
 
@@ -304,7 +302,6 @@ __host__ __device__ inline Lds lds_layout(const Dims& dm, int ng, int nl) {
   if (dm.E > land) land = dm.E;
   if (kHX * (dm.P + dm.E) > land) land = kHX * (dm.P + dm.E);
   o.land = off; off += up(land * 4);
-  o.hk = off; off += up((dm.K + 1) * 2 * dm.I * 2);
   o.ha = off; off += up(kHX * 2 * dm.P * 2);
   o.hx = off; off += up(kHX * dm.d * 2);
   o.misc = off; off += up((int)sizeof(Misc));
@@ -588,7 +585,6 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
   uint16_t* xperm = (uint16_t*)(smem + lo.xperm);
   uint16_t* xnat = (uint16_t*)(smem + lo.xnat);
   uint32_t* land = (uint32_t*)(smem + lo.land);
-  uint16_t* hk = (uint16_t*)(smem + lo.hk);
   uint16_t* ha = (uint16_t*)(smem + lo.ha);
   uint16_t* hx = (uint16_t*)(smem + lo.hx);
   Misc& ms = *(Misc*)(smem + lo.misc);
@@ -892,16 +888,9 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
     __syncthreads();
     stamp(a, l, 6);
     {
-      // fp16 hi/lo copies of every expert's SwiGLU output for the down GEMVs:
-      // lane group grp converts 32-element chunk grp (I / 32 == kGroups).
       const float* lf = (const float*)land;
       if (has_sh) {
         // the shared expert's SwiGLU outputs, LoRA terms included
-        if (AFF) {
-          const float2 hb = *reinterpret_cast<const float2*>(lf + pad32(n_rt + 2 * t));
-          const float sc = hilo_pair(hb.x, hb.y, grp, li, hk + K * 2 * I, I, &ms.hsum[K][grp]);
-          if (li == 0) ms.csc[K][grp] = sc;
-        }
         if (lora_d) {
           // rank grp of A_down h: the lane's 32 columns, then the group's sum
           const float4* hp = reinterpret_cast<const float4*>(lf + pad32(n_rt + 32 * li));
@@ -921,27 +910,8 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
           if (li == 0) ms.ad[grp] = p;
         }
       }
-      // Affine codec: fp16 hi + lo copies (the bias terms take each chunk's
-      // sum of hi + lo). The symmetric codec's down rows read the fp32
-      // outputs in place. An unresolved expert's outputs are zeros (never
-      // used: its down rows are zero too). With K == NX - 1 the loop is
-      // unrolled without branches, so the experts' conversions interleave.
-      if (AFF) {
-        if (K == NX - 1) {
-#pragma unroll
-          for (int k = 0; k < NX - 1; ++k) {
-            const float2 v = *reinterpret_cast<const float2*>(lf + pad32(k * I + 32 * grp + 2 * li));
-            const float sc = hilo_pair(v.x, v.y, grp, li, hk + k * 2 * I, I, &ms.hsum[k][grp]);
-            if (li == 0) ms.csc[k][grp] = sc;
-          }
-        } else {
-          for (int k = 0; k < K; ++k) {
-            const float2 v = *reinterpret_cast<const float2*>(lf + pad32(k * I + 32 * grp + 2 * li));
-            const float sc = hilo_pair(v.x, v.y, grp, li, hk + k * 2 * I, I, &ms.hsum[k][grp]);
-            if (li == 0) ms.csc[k][grp] = sc;
-          }
-        }
-      }
+      // The down rows read the fp32 outputs in place (unresolved experts'
+      // outputs are zeros, never used: their down rows are zero too).
       __syncthreads();
     }
     stamp(a, l, 7);
@@ -957,12 +927,9 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
 #pragma unroll
         for (int k = 0; k < NX; ++k) {
           if (AFF) {
-            const uint16_t* hh = hk + (int64_t)k * 2 * I;
-            f16x2 xh[16], xl[16];
-            load_xchunk(hh, li, xh);
-            load_xchunk(hh + I, li, xl);
-            acc += (ms.coef[k] * ms.csc[k][li]) *
-                   (bf2f(D.s[k]) * q4_dot32_hl<true>(D.w[k], xh, xl) + bf2f(D.b[k]) * ms.hsum[k][li]);
+            float xs;
+            const float dq = q4_dot32_f32<true>(D.w[k], lf + pad32(k * I + 32 * li), &xs);
+            acc += ms.coef[k] * (bf2f(D.s[k]) * dq + bf2f(D.b[k]) * xs);
           } else {
             acc += ms.coef[k] * (h2f(D.s[k]) * q4_dot32_f32(D.w[k], lf + pad32(k * I + 32 * li)));
           }
@@ -972,12 +939,9 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
         for (int k = 0; k < NX; ++k) {
           if (!ms.dq[k]) continue;
           if (AFF) {
-            const uint16_t* hh = hk + (int64_t)k * 2 * I;
-            f16x2 xh[16], xl[16];
-            load_xchunk(hh, li, xh);
-            load_xchunk(hh + I, li, xl);
-            acc += (ms.coef[k] * ms.csc[k][li]) *
-                   (bf2f(D.s[k]) * q4_dot32_hl<true>(D.w[k], xh, xl) + bf2f(D.b[k]) * ms.hsum[k][li]);
+            float xs;
+            const float dq = q4_dot32_f32<true>(D.w[k], lf + pad32(k * I + 32 * li), &xs);
+            acc += ms.coef[k] * (bf2f(D.s[k]) * dq + bf2f(D.b[k]) * xs);
           } else {
             acc += ms.coef[k] * (h2f(D.s[k]) * q4_dot32_f32(D.w[k], lf + pad32(k * I + 32 * li)));
           }
