@@ -881,6 +881,13 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
     const LoraRegs& LR = A.LR;
     stamp(a, l, 5);
 
+    // slot table of the next layer (its routing is known unless it is a
+    // router layer, which fills its own once routed), written while this
+    // layer's SwiGLU outputs are still in flight
+    if (step + 1 < nL && t <= K)
+      fill_slot(ms.eptr[(step + 1) & 1][t], lay[step + 1], K, t,
+                t < K ? ms.ent_all[(step + 1) * K + t] : 0);
+
     // ---- 4. gather SwiGLU outputs; finish the shared expert ----------------
     const int ng_l = n_rt + Is;
     ll_gather2<8, true>(xg, ng_l, ep, land, a.flags, &ms.abort);
@@ -968,11 +975,6 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
         ms.hstage[drow - db] = hv;
       }
     }
-    // slot table of the next layer (its routing is known unless it is a
-    // router layer, which fills its own once routed)
-    if (step + 1 < nL && t <= K)
-      fill_slot(ms.eptr[(step + 1) & 1][t], lay[step + 1], K, t,
-                t < K ? ms.ent_all[(step + 1) * K + t] : 0);
     __syncthreads();
     for (int j = db / 2 + t; j < de / 2; j += kThreads) {
       const int r0 = 2 * j - db;
