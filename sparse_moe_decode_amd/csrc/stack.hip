@@ -842,12 +842,6 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
       eidx[t] = ms.ridx_all[step * K + t];
       ew[t] = ms.rw_all[step * K + t];
     }
-    if (t < NX) {
-      const uint32_t* q = t <= K ? (const uint32_t*)ms.eptr[step & 1][t][2] : nullptr;
-      ms.dq[t] = q;
-      ms.dsc[t] = t <= K ? (const uint16_t*)ms.eptr[step & 1][t][5] : nullptr;
-      ms.coef[t] = !q ? 0.0f : t < K ? ms.rw_all[step * K + t] : 1.0f;
-    }
     stamp(a, l, 3);
 
     // ---- 3. gate/up rows, shared bases, LoRA A of gate/up ----------------
@@ -887,6 +881,13 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
     if (step + 1 < nL && t <= K)
       fill_slot(ms.eptr[(step + 1) & 1][t], lay[step + 1], K, t,
                 t < K ? ms.ent_all[(step + 1) * K + t] : 0);
+    // this layer's down bases and combine weights (read after the gather)
+    if (t < NX) {
+      const uint32_t* q = t <= K ? (const uint32_t*)ms.eptr[step & 1][t][2] : nullptr;
+      ms.dq[t] = q;
+      ms.dsc[t] = t <= K ? (const uint16_t*)ms.eptr[step & 1][t][5] : nullptr;
+      ms.coef[t] = !q ? 0.0f : t < K ? ms.rw_all[step * K + t] : 1.0f;
+    }
 
     // ---- 4. gather SwiGLU outputs; finish the shared expert ----------------
     const int ng_l = n_rt + Is;
