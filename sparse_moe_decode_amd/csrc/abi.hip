@@ -512,7 +512,7 @@ int e0_model_create(e0_ctx* ctx, const e0_layer* layers, int32_t n_layers, e0_mo
     const int n = dm.K * dm.I + Is + n_ad + r2;
     if (n > ng) ng = n;
   }
-  m->ng = ng;
+  m->ng = (ng + 1) & ~1;  // layer rows of xg stay 16-byte aligned (16-byte polls)
   if (stack_supported(dm)) {
     hipError_t e = hipMalloc(&m->dev_table, sizeof(LayerDev) * n_layers);
     if (e == hipSuccess)
