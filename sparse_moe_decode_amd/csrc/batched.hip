@@ -547,7 +547,7 @@ void k_mb_gate_up(MbArgs a) {
   const uint32_t* qrow = wq + (int64_t)(m0 + n) * wpr + 4 * kh;
   const uint16_t* srow = ws + (int64_t)(m0 + n) * ngs;
   // Small tiles (most of a decode chunk's) stage their token rows in LDS
-  // (direct-to-LDS loads, issued after the weight loads), so a wave reads
+  // (direct-to-LDS loads, issued before the weight loads), so a wave reads
   // its activations there instead of loading them per lane.
   const bool xlds = count <= kXsTok && d + 8 <= kXsRow;
   // Token rows past count read a valid row (the last one): their outputs
@@ -555,6 +555,21 @@ void k_mb_gate_up(MbArgs a) {
   int bt, kt;
   if (!xlds) entry_of(a, shared, start, n < count ? n : count - 1, bt, kt);
   const uint16_t* xrow = xlds ? nullptr : a.xp + (int64_t)bt * d + 32 * kh + 64 * g0;
+  if (xlds) {
+    // each wave stages its own quarter of every token row (the gate and the
+    // up wave of a quarter write the same bytes), so a wave waits only for
+    // its own loads: one instruction per row, 16 bytes a lane, issued before
+    // the weight words
+    const int qw = 64 * NG;  // inputs of a quarter
+    for (int tt = 0; tt < count; ++tt) {
+      int b, k;
+      entry_of(a, shared, start, tt, b, k);
+      if (8 * l < qw)
+        __builtin_amdgcn_global_load_lds((gptr_v*)(a.xp + (int64_t)b * d + qw * quarter + 8 * l),
+                                         (lptr_v*)(xsl + tt * kXsRow + qw * quarter), 16, 0, 0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
   uint4 wv[NG];
   float sv[NG], bv[NG];
 #pragma unroll
@@ -572,18 +587,9 @@ void k_mb_gate_up(MbArgs a) {
   constexpr int NH = NG / 2;
   f32x16 acc = {};
   if (xlds) {
-    // each wave stages its own quarter of every token row (the gate and the
-    // up wave of a quarter write the same bytes), so a wave waits only for
-    // its own loads: one instruction per row, 16 bytes a lane
-    const int qw = 64 * NG;  // inputs of a quarter
-    for (int tt = 0; tt < count; ++tt) {
-      int b, k;
-      entry_of(a, shared, start, tt, b, k);
-      if (8 * l < qw)
-        __builtin_amdgcn_global_load_lds((gptr_v*)(a.xp + (int64_t)b * d + qw * quarter + 8 * l),
-                                         (lptr_v*)(xsl + tt * kXsRow + qw * quarter), 16, 0, 0);
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's rows (and weights) are in
+    // the staged rows are in once at most NG loads (the weight words issued
+    // after them) are outstanding; the MFMAs then wait for each group's word
+    __builtin_amdgcn_s_waitcnt(0x0F70 | NG);
     const uint16_t* xl = xsl + (n < count ? n : count - 1) * kXsRow + 32 * kh + 64 * g0;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
