@@ -608,9 +608,9 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
     ms.pidx_all[i] = a.token > 0 ? a.exec_idx[((int64_t)nxt * a.L + l) * K + k] : -1;
   }
   __syncthreads();
+  // (the layer table is in LDS now: no further global reads of it)
   if (wave == 0) {  // head list (nL <= 64: one lane per layer)
-    const LayerDev* Lm = a.layers + a.l0 + (lane < nL ? lane : 0);
-    const HeadW hw = ldg_struct(&Lm->head);
+    const HeadW hw = lay[lane < nL ? lane : 0].head;
     const bool has = lane < nL && hw.fc1 != nullptr;
     const uint64_t m = __ballot(has);
     const int before = __popcll(m & ((1ull << lane) - 1ull));
@@ -625,8 +625,8 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
     if (lane == 0) ms.n_heads = __popcll(m);
   }
   for (int i = t; i < nL * K; i += kThreads) {
-    const LayerDev* Ls = a.layers + a.l0 + i / K;
-    ms.ent_all[i] = ldg(&Ls->router) ? 0 : resolve_entry(ldg_struct(&Ls->pool), E, ms.ridx_all[i]);
+    const LayerDev& Ls = lay[i / K];
+    ms.ent_all[i] = Ls.router ? 0 : resolve_entry(Ls.pool, E, ms.ridx_all[i]);
   }
   __syncthreads();
   // slot table of the first layer (a router layer fills its own once routed)
