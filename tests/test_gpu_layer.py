@@ -1,4 +1,5 @@
-"""GPU parity of layer_step: single layers of every tier and the full stacks.
+"""GPU parity of layer_step: single layers of every tier and the full stacks,
+64-layer launches, and top-K below the kernels' expert slots.
 
 Runs tokens through layer_step exactly as the benchmark does (one call per
 token over the layer range) and checks every (token, layer) step against the
@@ -111,10 +112,10 @@ def test_layer_step_stack_8b(api, orc, path):
                    zero_mean=True, path=path)
 
 
-def _long_stack(api, n_layers, E, seed):
+def _long_stack(api, n_layers, E, seed, tier="8b", K=None):
     import torch
     from sparse_moe_decode_amd import workloads as wl
-    dm = synth.dims("8b", E=E)
+    dm = synth.dims(tier, E=E) if K is None else synth.dims(tier, E=E, K=K)
     roles = ([dict(router=True, head=True)] +
              [dict(router=False, head=True) for _ in range(n_layers - 2)] +
              [dict(router=True, head=False)])
@@ -123,7 +124,7 @@ def _long_stack(api, n_layers, E, seed):
         lw = synth.layer(seed, l, dm, role, zero_mean=True)
         keep[l] = lw
         if l % 8 == 0:
-            announce("upload", "8b", f"E={E}", f"layer {l}/{n_layers}")
+            announce("upload", tier, f"E={E}", f"layer {l}/{n_layers}")
         layers.append(dict(routed=wl.tree_to_dev(lw["routed"]), shared=wl.tree_to_dev(lw["shared"]),
                            attn=dev(lw["attn"]),
                            router=None if lw["router"] is None else dev(lw["router"]),
@@ -278,5 +279,45 @@ def test_layer_step_bitwise_deterministic(api, path):
     for a, b in zip(runs[0], runs[1]):
         for x, y in zip(a, b):
             assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), f"{path}: runs differ"
+    model.close()
+    ctx.close()
+
+
+@pytest.mark.parametrize("tier,K,path", [("35b", 2, "persistent"), ("35b", 3, "persistent"),
+                                         ("8b", 6, "persistent"), ("35b", 3, "chain"),
+                                         ("8b", 6, "chain"), ("35b", 3, "flow")])
+def test_layer_step_top_k_below_slots(api, orc, tier, K, path):
+    """Top-K below the kernels' expert slots (K = 2 and 3 on the five-slot
+    instantiation, 6 on the nine-slot one): the slots past K hold no expert
+    and the down rows skip them. Four layers (routers first and last, 32
+    experts), every layer-step of three tokens against the oracle. (The
+    layer-ahead slot kernel takes at most 64 shared-expert owners, so not
+    K = 2 on 256 workgroups.)"""
+    import torch
+    from sparse_moe_decode_amd import workloads as wl
+    L, seed = 4, 23 + K
+    dm, roles, layers, keep, state = _long_stack(api, L, 32, seed, tier=tier, K=K)
+    ctx = api.Context(dm, max_tokens=1)
+    model = api.Model(ctx, layers)
+    model.set_path({"chain": api.PATH_CHAIN, "persistent": api.PATH_PERSISTENT,
+                    "flow": api.PATH_FLOW}[path])
+    toks = wl.token_inputs(tier, seed, 3, 0.5)
+    checker = StackChecker(orc, tier, seed, roles, list(range(L)), keep, zero_mean=True, dims=dm)
+    prev_exec = None
+    h = torch.empty((L + 1, dm["d"]), dtype=torch.float16, device="cuda")
+    for t in range(3):
+        announce("layer_step", tier, path, f"K={K}", f"token {t}")
+        h[0].copy_(torch.from_numpy(toks[t]))
+        api.layer_step(ctx, model, 0, L, state, t, h)
+        assert api.device_status(ctx) == 0
+        cur, nxt = t & 1, (t + 1) & 1
+        exec_idx = host(state.exec_idx[cur]).copy()
+        checker.check(t, host(h).copy(), host(state.x_trace).copy(), exec_idx,
+                      host(state.exec_w[cur]).copy(), prev_exec, host(state.route_idx[cur]).copy(),
+                      host(state.route_w[cur]).copy(), host(state.route_idx[nxt]).copy(),
+                      host(state.route_w[nxt]).copy(), host(state.head_logits).copy())
+        prev_exec = exec_idx
+    print(f"{tier} K={K} {path}: {checker.steps} layer-steps checked, worst error ratio "
+          f"{checker.worst:.3f}")
     model.close()
     ctx.close()
