@@ -236,6 +236,18 @@ __device__ __forceinline__ void split(int n, int G, int c, int& beg, int& end) {
   end = (int)((uint32_t)n * (uint32_t)(c + 1) / (uint32_t)G);
 }
 
+// LoRA A rows of workgroup c: one each on the first r2 workgroups (whose
+// SwiGLU items are routed ones, so no shared-expert owner computes them), or
+// spread over all G when G < r2.
+__device__ __forceinline__ void ax_share(int r2, int G, int c, int& beg, int& end) {
+  if (G >= r2) {
+    beg = c < r2 ? c : r2;
+    end = c < r2 ? c + 1 : r2;
+  } else {
+    split(r2, G, c, beg, end);
+  }
+}
+
 // Block-wide sum (all threads return the total).
 __device__ __forceinline__ float block_sum(float v, float* red) {
   v = wave_sum_rows(v);
@@ -701,7 +713,7 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
     A.n_router = Ly.router ? e - b : 0;
     for (int j = 0; j < kNR; ++j) rp[j] = Ly.router + (int64_t)(b + (j < A.n_router ? j : 0)) * d;
     f16rows_issue<kNR>(A.router, rp, A.n_router, d);
-    split(r2, G, cu, b, e);
+    ax_share(r2, G, cu, b, e);
     A.n_ax = e - b;
     for (int j = 0; j < kNR; ++j) {
       const int tt = b + (j < A.n_ax ? j : 0);
@@ -801,7 +813,7 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
     // the end of step 3 for the LoRA B terms.
     if (A.n_ax) {
       int b, e;
-      split(r2, G, cu, b, e);
+      ax_share(r2, G, cu, b, e);
       f16rows_finish<kNR>(A.ax, A.n_ax, d, xnat, ms);
       if (t < A.n_ax) ll_put(xg + n_rt + Is + b + t, fbits(ms.rows[t]), ep);
     }
