@@ -154,6 +154,8 @@ __device__ __forceinline__ void ll_gather(const uint64_t* src, int n, uint32_t e
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 // PAD: word i goes to dst[pad32(i)] (four words of padding after every 32),
 // so 16-lane groups reading 32 consecutive words per lane hit distinct banks.
+// The padded gather has no 8-byte fallback: its callers pass an even n and a
+// 16-byte aligned src (the SwiGLU outputs: I == 512, even exchange rows).
 __device__ __forceinline__ int pad32(int i) { return i + 4 * (i >> 5); }
 
 template <int U, bool PAD = false>
