@@ -250,6 +250,16 @@ __device__ __forceinline__ void ax_share(int r2, int G, int c, int& beg, int& en
   }
 }
 
+// Router rows of workgroup c: kNR each on the first E / kNR workgroups, so
+// the logits exchange waits on fewer producers (stack_launchable requires
+// E <= kNR * G).
+__device__ __forceinline__ void router_share(int E, int G, int c, int& beg, int& end) {
+  const int np = (E + kNR - 1) / kNR;
+  beg = c < np ? kNR * c : E;
+  end = c < np ? min(kNR * c + kNR, E) : E;
+  if (np > G) split(E, G, c, beg, end);
+}
+
 // Block-wide sum (all threads return the total).
 __device__ __forceinline__ float block_sum(float v, float* red) {
   v = wave_sum_rows(v);
@@ -703,6 +713,8 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
 
   // Issue the loads of layer l that its gate/up step needs and that do not
   // depend on its activations.
+  int rt0, rt1;  // this workgroup's router rows (the same on every router layer)
+  router_share(E, G, cu, rt0, rt1);
   auto issue_a = [&](int l, const LayerDev& Ly, PhaseA<CPL_D, IPG, NX>& A) {
     const bool has_sh = Ly.sh.present != 0;
     const int Is = has_sh ? dm.Is : 0;
@@ -711,7 +723,8 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
     // (see zrow), so that no load result is merged at a branch
     const uint16_t* rp[kNR];
     int b, e;
-    split(E, G, cu, b, e);
+    b = rt0;
+    e = rt1;
     A.n_router = Ly.router ? e - b : 0;
     for (int j = 0; j < kNR; ++j) rp[j] = Ly.router + (int64_t)(b + (j < A.n_router ? j : 0)) * d;
     f16rows_issue<kNR>(A.router, rp, A.n_router, d);
@@ -825,8 +838,7 @@ __global__ __launch_bounds__(kThreads) void k_stack(StackArgs a) {
     int32_t* eidx = a.exec_idx + ((int64_t)cur * a.L + l) * K;
     float* ew = a.exec_w + ((int64_t)cur * a.L + l) * K;
     if (Ly.router) {
-      int rb, re;
-      split(E, G, cu, rb, re);
+      const int rb = rt0;
       f16rows_finish<kNR>(A.router, A.n_router, d, xnat, ms);
       stamp(a, l, 10);
       if (t < A.n_router) ll_put(a.xr + (int64_t)l * E + rb + t, fbits(ms.rows[t]), ep);
