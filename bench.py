@@ -711,7 +711,7 @@ def main():
     ap.add_argument("--rho", type=float, default=None,
                     help="token correlation of the stack workloads (default: the calibrated "
                          "value giving ~0.7 adjacent-token expert overlap)")
-    ap.add_argument("--cpu-tokens", type=int, default=2)
+    ap.add_argument("--cpu-tokens", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
@@ -869,8 +869,8 @@ def main():
     tok_s = 1000.0 / ms
     cpu = None
     if keep_host:
-        cpu = cpu_baseline(tier, args.seed, roles, host_layers, toks, idx0, w0, args.cpu_tokens,
-                           quant)
+        cpu = cpu_baseline(tier, args.seed, roles, host_layers, toks, idx0, w0,
+                           min(args.cpu_tokens, len(toks)), quant)
 
     out = {
         "metric": METRIC,
