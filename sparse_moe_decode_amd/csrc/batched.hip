@@ -825,14 +825,54 @@ void k_mb_down(MbArgs a) {
 // slot outputs. ctok = 1 for small batches (more workgroups), more for large
 // ones (fewer reads of the LoRA rows).
 constexpr int kCombTokMax = 4;
+constexpr int kCombK = 8;  // routed slots a token's loads cover (K <= 8)
+
+// Token b's routed slot outputs (four columns from j0), its shared slot's and
+// its K weights, all issued together with no condition, so one memory latency
+// covers them. Slots k >= K read the shared slot's row and weights k >= K the
+// last one: in bounds (Y holds K + 1 rows per token, w K), never used.
+struct CombRow {
+  float4 y[kCombK];
+  float4 ysh;
+  float w[kCombK];
+};
+
+__device__ __forceinline__ void comb_load(const MbArgs& a, int b, int j0, CombRow& r) {
+  const int K = a.dm.K, d = a.dm.d;
+  const float* yb = a.Y + (int64_t)b * (K + 1) * d + j0;
+#pragma unroll
+  for (int k = 0; k < kCombK; ++k)
+    r.y[k] = *reinterpret_cast<const float4*>(yb + (int64_t)(k < K ? k : K) * d);
+  r.ysh = *reinterpret_cast<const float4*>(yb + (int64_t)K * d);
+#pragma unroll
+  for (int k = 0; k < kCombK; ++k) r.w[k] = a.w[b * K + (k < K ? k : K - 1)];
+}
 
 __global__ __launch_bounds__(256) void k_mb_combine(MbArgs a) {
-  __shared__ int ok[kCombTokMax][8];
+  __shared__ int ok[kCombTokMax][kCombK];
   __shared__ float axd[kCombTokMax][kMaxR];
   const Dims& dm = a.dm;
   const int K = dm.K, d = dm.d, b0 = blockIdx.x * a.ctok;
   const int nb = min(a.ctok, a.B - b0);
   const bool lora = a.sh.present && a.sh.bd;
+  const int j0 = 4 * (blockIdx.y * blockDim.x + threadIdx.x);
+  // d % 128 == 0: a thread's four columns are all in range or all out; the
+  // loads of out-of-range threads read column 0 and are dropped
+  const bool act = j0 < d;
+  const int jl = act ? j0 : 0;
+  // the first token's rows and the LoRA rows do not depend on the tables
+  // below: issued first, so their latency overlaps the table lookups
+  CombRow row;
+  comb_load(a, b0, jl, row);
+  uint4 bv[4][kMaxR / 8];  // the four columns' down-LoRA rows (fp16, r <= kMaxR)
+  if (lora) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int q = 0; q < kMaxR / 8; ++q)
+        if (8 * q < dm.r)
+          bv[jj][q] = ldg(reinterpret_cast<const uint4*>(a.sh.bd + (int64_t)(jl + jj) * dm.r + 8 * q));
+  }
   for (int i = threadIdx.x; i < nb * K; i += blockDim.x) {
     const int tb = i / K, k = i % K;
     ok[tb][k] = resolve_entry(a.pool, dm.E, a.idx[(b0 + tb) * K + k]) >= 0;
@@ -843,32 +883,24 @@ __global__ __launch_bounds__(256) void k_mb_combine(MbArgs a) {
       axd[tb][q] = a.ax[(int64_t)(b0 + tb) * 3 * a.rmax + 2 * a.rmax + q];
     }
   __syncthreads();
-  const int j0 = 4 * (blockIdx.y * blockDim.x + threadIdx.x);
-  if (j0 >= d) return;  // d % 128 == 0: a thread's four columns are all in range
+  if (!act) return;
   const float c = dm.lora_scale;
-  uint4 bv[4][kMaxR / 8];  // the four columns' down-LoRA rows (fp16, r <= kMaxR)
-  if (lora) {
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-      for (int q = 0; q < kMaxR / 8; ++q)
-        if (8 * q < dm.r)
-          bv[jj][q] = ldg(reinterpret_cast<const uint4*>(a.sh.bd + (int64_t)(j0 + jj) * dm.r + 8 * q));
-  }
   for (int tb = 0; tb < nb; ++tb) {
     const int b = b0 + tb;
+    if (tb > 0) comb_load(a, b, j0, row);
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int k = 0; k < K; ++k) {
-      if (!ok[tb][k]) continue;
-      const float wk = a.w[b * K + k];
-      const float4 v = *reinterpret_cast<const float4*>(a.Y + ((int64_t)b * (K + 1) + k) * d + j0);
+#pragma unroll
+    for (int k = 0; k < kCombK; ++k) {
+      if (k >= K || !ok[tb][k]) continue;
+      const float wk = row.w[k];
+      const float4 v = row.y[k];
       acc[0] += wk * v.x;
       acc[1] += wk * v.y;
       acc[2] += wk * v.z;
       acc[3] += wk * v.w;
     }
     if (a.sh.present) {
-      const float4 v = *reinterpret_cast<const float4*>(a.Y + ((int64_t)b * (K + 1) + K) * d + j0);
+      const float4 v = row.ysh;
       acc[0] += v.x;
       acc[1] += v.y;
       acc[2] += v.z;
